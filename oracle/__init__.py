@@ -1,0 +1,135 @@
+"""fp64 CPU oracle for the gated delta rule -- TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product package
+(``gated_delta_rule_44_amd``) never imports it, and the two share no code.
+
+The arithmetic lives in ``gdr_oracle.c`` (plain C, fp64, one token at a time,
+built with gcc).  This module only builds/loads that library and marshals
+arrays: it widens the *stored* input values (bf16 or fp32) to float32, which
+is exact, and hands them over.
+
+Source of the method: "Super Apriel: One Checkpoint, Many Speeds"
+(arXiv 2604.19877).  Its gist.science technical summary, section 2a, lists
+Kimi Delta Attention as recurrent with a per-channel gate and Gated DeltaNet
+as recurrent with a scalar gate; the recurrence itself is the standard gated
+delta rule stated in ``gdr_oracle.c``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gdr_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(src: str = _SRC, out: str = _LIB, extra_flags=()) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP) into a shared library."""
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-fopenmp",
+           *extra_flags, src, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def _bind(lib):
+    f = lib.gdr_oracle_forward
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                  ctypes.c_int, ctypes.c_int, ctypes.c_double,
+                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+    lib.gdr_oracle_max_threads.restype = ctypes.c_int
+    return lib
+
+
+def load(path: str | None = None):
+    """Load (building first if absent) the oracle library."""
+    global _lib
+    if path is not None:
+        return _bind(ctypes.CDLL(path))
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        _lib = _bind(ctypes.CDLL(_LIB))
+    return _lib
+
+
+def _f32(x) -> np.ndarray:
+    """Stored values -> contiguous float32 ndarray (exact for bf16/fp32)."""
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            x = x.detach().to("cpu")
+            if x.dtype != torch.float32:
+                x = x.to(torch.float32)
+            return np.ascontiguousarray(x.numpy())
+    except ImportError:  # pragma: no cover
+        pass
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def forward(q, k, v, g, beta, h0=None, cu_seqlens=None, scale: float = 1.0,
+            threads: int | None = None, lib=None):
+    """Gated delta rule over a batch, token by token in fp64.
+
+    Layouts (row-major):
+      fixed batch : q,k [B,T,H,Dk]  v [B,T,H,Dv]  g [B,T,H] or [B,T,H,Dk]
+                    beta [B,T,H]    h0 [B,H,Dv,Dk] or None
+      packed      : (cu_seqlens given, int [N+1]) q,k [T_tot,H,Dk] ...,
+                    h0 [N,H,Dv,Dk] or None
+    A gate with as many dims as q is a per-channel gate; one dim fewer is a
+    scalar (per token and head) gate.  Returns (o, ht) as float64 arrays with
+    o shaped like v and ht [N,H,Dv,Dk].
+    """
+    lib = lib or load()
+    qf, kf, vf, gf, bf = (_f32(x) for x in (q, k, v, g, beta))
+    channel = gf.ndim == qf.ndim
+    if cu_seqlens is None:
+        B, T, H, Dk = qf.shape
+        cu = np.arange(B + 1, dtype=np.int64) * T
+    else:
+        cu = np.ascontiguousarray(np.asarray(
+            cu_seqlens.cpu() if hasattr(cu_seqlens, "cpu") else cu_seqlens,
+            dtype=np.int64))
+        _, H, Dk = qf.shape
+    Dv = vf.shape[-1]
+    N = len(cu) - 1
+    hf = None if h0 is None else _f32(h0)
+    o = np.zeros(vf.shape, dtype=np.float64)
+    ht = np.zeros((N, H, Dv, Dk), dtype=np.float64)
+    rc = lib.gdr_oracle_forward(
+        N, _ptr(cu), H, Dk, Dv, int(channel), float(scale),
+        _ptr(qf), _ptr(kf), _ptr(vf), _ptr(gf), _ptr(bf), _ptr(hf),
+        _ptr(o), _ptr(ht), int(threads or 0))
+    if rc != 0:
+        raise RuntimeError("gdr_oracle_forward failed with code %d" % rc)
+    return o, ht
+
+
+def decode(q, k, v, g, beta, state, scale: float = 1.0, threads=None, lib=None):
+    """One decode step per (b, h): q,k [B,H,Dk], v [B,H,Dv], g [B,H] or
+    [B,H,Dk], beta [B,H], state [B,H,Dv,Dk].  Returns (o [B,H,Dv], new state),
+    both float64.  This is the same recurrence over a length-1 sequence."""
+    qf = _f32(q)
+    B, H, Dk = qf.shape
+    add_t = lambda x: _f32(x)[:, None]  # noqa: E731  [B,1,...]
+    o, ht = forward(add_t(q), add_t(k), add_t(v), add_t(g), add_t(beta),
+                    h0=state, scale=scale, threads=threads, lib=lib)
+    return o[:, 0], ht
+
+
+def max_threads(lib=None) -> int:
+    return (lib or load()).gdr_oracle_max_threads()

@@ -1,0 +1,189 @@
+/*
+ * gdr_oracle.c -- fp64 CPU oracle for the gated delta rule.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only tests/, __graft_entry__.smoke() and the
+ * cpu_baseline leg of bench.py may load this library.  The product path
+ * (gated_delta_rule_44_amd) never links, imports or calls it, and it shares
+ * no code, header, table or helper with the HIP kernels.
+ *
+ * What it computes.  "Super Apriel: One Checkpoint, Many Speeds" (arXiv
+ * 2604.19877; the gist.science technical summary, section 2a "supernet
+ * architecture") names two recurrent O(n) mixers: Kimi Delta Attention,
+ * gated per key channel, and Gated DeltaNet, gated by one scalar per head.
+ * The pages give no formula; the plain reading used here is the standard
+ * gated delta rule, per (sequence, head):
+ *
+ *     S_t = S_{t-1} Diag(a_t) (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+ *     o_t = scale * S_t q_t                       (state AFTER the update)
+ *
+ * with S in R^{Dv x Dk} (row = value index i, column = key index j), the
+ * gate supplied as its logarithm g = ln a <= 0, a_t = exp(g_t) either one
+ * value per (token, head) [scalar gate, GDN] or Dk values [channel gate,
+ * KDA].  Expanding the product,
+ *     S' = S_{t-1} Diag(a_t);   S_t = S' + beta_t (v_t - S' k_t) k_t^T,
+ * which is the form evaluated below, one token at a time, in fp64.
+ *
+ * Inputs are float32 (bf16 and fp32 values are exactly representable) and
+ * are widened to double before any arithmetic.  Nothing is chunked, fused
+ * or reordered.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/*
+ * Run the recurrence over one (sequence, head) pair.
+ *   q,k : token-major rows, row t at  q + t*qk_stride,  Dk values each
+ *   v   : row t at v + t*v_stride, Dv values
+ *   g   : channel gate: row t at g + t*g_stride, Dk values
+ *         scalar gate : value at g[t*g_stride]
+ *   beta: value at beta[t*b_stride]
+ *   S   : Dv*Dk doubles, holds the initial state on entry and the final
+ *         state on exit (row-major, S[i*Dk + j])
+ *   o   : row t at o + t*o_stride, Dv doubles
+ */
+static void recur_one(int T, int Dk, int Dv, int channel_gate, double scale,
+                      const float *q, const float *k, const float *v,
+                      const float *g, const float *beta,
+                      size_t qk_stride, size_t v_stride, size_t g_stride,
+                      size_t b_stride, size_t o_stride,
+                      double *S, double *o, double *a, double *kt, double *qt)
+{
+    for (int t = 0; t < T; ++t) {
+        const float *qrow = q + (size_t)t * qk_stride;
+        const float *krow = k + (size_t)t * qk_stride;
+        const float *vrow = v + (size_t)t * v_stride;
+        const double bt = (double)beta[(size_t)t * b_stride];
+
+        for (int j = 0; j < Dk; ++j) {
+            kt[j] = (double)krow[j];
+            qt[j] = (double)qrow[j];
+            a[j] = channel_gate ? exp((double)g[(size_t)t * g_stride + j])
+                                : exp((double)g[(size_t)t * g_stride]);
+        }
+
+        for (int i = 0; i < Dv; ++i) {
+            double *Si = S + (size_t)i * Dk;
+            /* S' = S Diag(a): column j scaled by a_j */
+            for (int j = 0; j < Dk; ++j)
+                Si[j] *= a[j];
+            /* (S' k)_i */
+            double y = 0.0;
+            for (int j = 0; j < Dk; ++j)
+                y += Si[j] * kt[j];
+            /* S_i += beta (v_i - (S'k)_i) k^T */
+            const double u = bt * ((double)vrow[i] - y);
+            for (int j = 0; j < Dk; ++j)
+                Si[j] += u * kt[j];
+            /* o_i = scale * (S_t q)_i with the updated row */
+            double oi = 0.0;
+            for (int j = 0; j < Dk; ++j)
+                oi += Si[j] * qt[j];
+            o[(size_t)t * o_stride + i] = scale * oi;
+        }
+    }
+}
+
+/*
+ * Packed-batch entry point.
+ *
+ *   N            number of sequences
+ *   cu_seqlens   N+1 non-decreasing offsets into the packed token axis;
+ *                sequence n owns tokens [cu_seqlens[n], cu_seqlens[n+1])
+ *   H, Dk, Dv    heads, key width, value width
+ *   channel_gate 1: g is [T_total, H, Dk];  0: g is [T_total, H]
+ *   q, k         [T_total, H, Dk] float32
+ *   v            [T_total, H, Dv] float32
+ *   beta         [T_total, H] float32
+ *   h0           [N, H, Dv, Dk] float32, or NULL for zero initial states
+ *   o            [T_total, H, Dv] double (written)
+ *   ht           [N, H, Dv, Dk] double (written), or NULL
+ *   num_threads  OpenMP threads (<= 0: library default)
+ *
+ * Returns 0 on success, -1 on bad arguments, -2 if scratch allocation
+ * failed.  The state is reset to h0[n] at every sequence start, so nothing
+ * crosses a cu_seqlens boundary.
+ */
+int gdr_oracle_forward(int N, const int64_t *cu_seqlens, int H, int Dk, int Dv,
+                       int channel_gate, double scale,
+                       const float *q, const float *k, const float *v,
+                       const float *g, const float *beta, const float *h0,
+                       double *o, double *ht, int num_threads)
+{
+    if (N < 0 || H <= 0 || Dk <= 0 || Dv <= 0 || !cu_seqlens)
+        return -1;
+    for (int n = 0; n < N; ++n)
+        if (cu_seqlens[n + 1] < cu_seqlens[n])
+            return -1;
+
+    const size_t qk_stride = (size_t)H * Dk;
+    const size_t v_stride = (size_t)H * Dv;
+    const size_t g_stride = channel_gate ? (size_t)H * Dk : (size_t)H;
+    const size_t b_stride = (size_t)H;
+    const size_t o_stride = (size_t)H * Dv;
+    const size_t SS = (size_t)Dv * Dk;
+    const long pairs = (long)N * H;
+    int failed = 0;
+
+#ifdef _OPENMP
+    if (num_threads > 0)
+        omp_set_num_threads(num_threads);
+#else
+    (void)num_threads;
+#endif
+
+#pragma omp parallel
+    {
+        double *S = (double *)malloc(sizeof(double) * SS);
+        double *a = (double *)malloc(sizeof(double) * (size_t)Dk);
+        double *kt = (double *)malloc(sizeof(double) * (size_t)Dk);
+        double *qt = (double *)malloc(sizeof(double) * (size_t)Dk);
+        if (!S || !a || !kt || !qt) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (long p = 0; p < pairs; ++p) {
+                const int n = (int)(p / H);
+                const int h = (int)(p % H);
+                const int64_t t0 = cu_seqlens[n];
+                const int T = (int)(cu_seqlens[n + 1] - t0);
+                const float *h0p = h0 ? h0 + ((size_t)n * H + h) * SS : NULL;
+                for (size_t e = 0; e < SS; ++e)
+                    S[e] = h0p ? (double)h0p[e] : 0.0;
+                recur_one(T, Dk, Dv, channel_gate, scale,
+                          q + (size_t)t0 * qk_stride + (size_t)h * Dk,
+                          k + (size_t)t0 * qk_stride + (size_t)h * Dk,
+                          v + (size_t)t0 * v_stride + (size_t)h * Dv,
+                          channel_gate ? g + (size_t)t0 * g_stride + (size_t)h * Dk
+                                       : g + (size_t)t0 * g_stride + h,
+                          beta + (size_t)t0 * b_stride + h,
+                          qk_stride, v_stride, g_stride, b_stride, o_stride,
+                          S, o + (size_t)t0 * o_stride + (size_t)h * Dv, a, kt, qt);
+                if (ht)
+                    memcpy(ht + ((size_t)n * H + h) * SS, S, sizeof(double) * SS);
+            }
+        }
+        free(S);
+        free(a);
+        free(kt);
+        free(qt);
+    }
+    return failed ? -2 : 0;
+}
+
+/* Number of OpenMP threads a parallel region would use (1 without OpenMP). */
+int gdr_oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
