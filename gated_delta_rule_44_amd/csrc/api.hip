@@ -1,0 +1,256 @@
+// api.hip -- the C ABI declared in include/gdr.h: host-side argument checks,
+// dispatch over dtype x gate x width, and launches on the caller's stream.
+// Every check runs before the first HIP call, so a rejected call has no side
+// effects.  No C++ exception crosses the interface.
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "../../include/gdr.h"
+#include "gdr_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+gdr_status fail(gdr_status code, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+bool debug_sync() {
+    static const int on = [] {
+        const char *e = getenv("GDR_DEBUG");
+        return (e && e[0] && e[0] != '0') ? 1 : 0;
+    }();
+    return on != 0;
+}
+
+gdr_status finish(hipError_t launch, hipStream_t s, const char *what) {
+    if (launch != hipSuccess)
+        return fail(GDR_EHIP, "%s: launch failed: %s", what, hipGetErrorString(launch));
+    if (debug_sync()) {
+        hipError_t e = hipStreamSynchronize(s);
+        if (e == hipSuccess) e = hipGetLastError();
+        if (e != hipSuccess)
+            return fail(GDR_EHIP, "%s: execution failed: %s", what, hipGetErrorString(e));
+    }
+    return GDR_OK;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+gdr_status check_common(int dt, int gk, int Dk, int Dv, const char *what) {
+    if (dt != GDR_F32 && dt != GDR_BF16)
+        return fail(GDR_EINVAL, "%s: dtype %d is not GDR_F32 or GDR_BF16", what, dt);
+    if (gk != GDR_GATE_SCALAR && gk != GDR_GATE_CHANNEL)
+        return fail(GDR_EINVAL, "%s: gate kind %d is not scalar or channel", what, gk);
+    if (Dk != Dv)
+        return fail(GDR_EUNSUPPORTED, "%s: Dk (%d) != Dv (%d) is not supported", what, Dk, Dv);
+    if (Dk != 64 && Dk != 128)
+        return fail(GDR_EUNSUPPORTED, "%s: Dk = %d; supported widths are 64 and 128", what, Dk);
+    return GDR_OK;
+}
+
+#define REQUIRE_PTR(p, name)                                                        \
+    do {                                                                            \
+        if (!(p)) return fail(GDR_EINVAL, "%s: %s is NULL", what, name);            \
+        if (!aligned16(p)) return fail(GDR_EINVAL, "%s: %s is not 16-byte aligned", \
+                                       what, name);                                 \
+    } while (0)
+#define REQUIRE_ALIGNED_OR_NULL(p, name)                                            \
+    do {                                                                            \
+        if ((p) && !aligned16(p)) return fail(GDR_EINVAL,                           \
+                                              "%s: %s is not 16-byte aligned",      \
+                                              what, name);                          \
+    } while (0)
+
+gdr_status check_prefill_ptrs(const char *what, const void *q, const void *k, const void *v,
+                              const float *g, const float *beta, const float *h0,
+                              const void *o, const float *ht, long long tokens) {
+    if (tokens > 0) {
+        REQUIRE_PTR(q, "q");
+        REQUIRE_PTR(k, "k");
+        REQUIRE_PTR(v, "v");
+        REQUIRE_PTR(g, "g");
+        if (!beta) return fail(GDR_EINVAL, "%s: beta is NULL", what);
+        REQUIRE_PTR(o, "o");
+    }
+    REQUIRE_ALIGNED_OR_NULL(h0, "h0");
+    REQUIRE_ALIGNED_OR_NULL(ht, "ht");
+    return GDR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *gdr_last_error(void) { return g_err; }
+
+const char *gdr_version(void) { return "gdr 0.1.0 (gfx950)"; }
+
+size_t gdr_prefill_workspace_bytes(int N) {
+    if (N <= 0) return 0;
+    return (((size_t)N * sizeof(int32_t)) + 255) / 256 * 256;
+}
+
+gdr_status gdr_prefill_chunked(enum gdr_dtype dt, enum gdr_gate gk, int B, int T, int H,
+                               int Dk, int Dv, int chunk, float scale, const void *q,
+                               const void *k, const void *v, const float *g,
+                               const float *beta, const float *h0, void *o, float *ht,
+                               void *stream) {
+    const char *what = "gdr_prefill_chunked";
+    gdr_status st = check_common(dt, gk, Dk, Dv, what);
+    if (st != GDR_OK) return st;
+    if (chunk != 64) return fail(GDR_EUNSUPPORTED, "%s: chunk = %d; only 64 is supported", what, chunk);
+    if (B < 0 || T < 0 || H <= 0)
+        return fail(GDR_EINVAL, "%s: bad sizes B=%d T=%d H=%d", what, B, T, H);
+    if ((long long)B * T * H * Dk >= (1LL << 40))
+        return fail(GDR_EUNSUPPORTED, "%s: problem too large", what);
+    st = check_prefill_ptrs(what, q, k, v, g, beta, h0, o, ht, (long long)B * T);
+    if (st != GDR_OK) return st;
+    if (h0 && ht && h0 != ht) {
+        const size_t bytes = (size_t)B * H * Dv * Dk * sizeof(float);
+        const char *a0 = (const char *)h0, *a1 = (const char *)ht;
+        if (a0 < a1 + bytes && a1 < a0 + bytes)
+            return fail(GDR_EINVAL, "%s: h0 and ht overlap without being equal", what);
+    }
+    if (B == 0) return GDR_OK;
+    gdr::PrefillArgs a{};
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.h0 = h0; a.o = o; a.ht = ht;
+    a.cu_seqlens = nullptr; a.order = nullptr;
+    a.N = B; a.T = T; a.H = H; a.scale = scale; a.channel_gate = gk == GDR_GATE_CHANNEL;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = dt == GDR_BF16 ? gdr::launch_prefill_chunked(Dk, a, s)
+                                  : gdr::launch_prefill_recurrent(false, Dk, a, s);
+    return finish(e, s, what);
+}
+
+gdr_status gdr_prefill_chunked_varlen(enum gdr_dtype dt, enum gdr_gate gk, int N, int T_total,
+                                      int H, int Dk, int Dv, int chunk, float scale,
+                                      const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
+                                      const void *q, const void *k, const void *v,
+                                      const float *g, const float *beta, const float *h0,
+                                      void *o, float *ht, void *workspace, size_t ws_bytes,
+                                      void *stream) {
+    const char *what = "gdr_prefill_chunked_varlen";
+    gdr_status st = check_common(dt, gk, Dk, Dv, what);
+    if (st != GDR_OK) return st;
+    if (chunk != 64) return fail(GDR_EUNSUPPORTED, "%s: chunk = %d; only 64 is supported", what, chunk);
+    if (N < 0 || T_total < 0 || H <= 0)
+        return fail(GDR_EINVAL, "%s: bad sizes N=%d T_total=%d H=%d", what, N, T_total, H);
+    if ((long long)T_total * H * Dk >= (1LL << 40))
+        return fail(GDR_EUNSUPPORTED, "%s: problem too large", what);
+    if (N == 0) return GDR_OK;
+    if (!cu_seqlens) return fail(GDR_EINVAL, "%s: cu_seqlens is NULL", what);
+    if (cu_seqlens_host) {
+        if (cu_seqlens_host[0] != 0)
+            return fail(GDR_EINVAL, "%s: cu_seqlens[0] = %d, expected 0", what, cu_seqlens_host[0]);
+        for (int i = 0; i < N; ++i)
+            if (cu_seqlens_host[i + 1] < cu_seqlens_host[i])
+                return fail(GDR_EINVAL, "%s: cu_seqlens decreases at %d", what, i);
+        if (cu_seqlens_host[N] != T_total)
+            return fail(GDR_EINVAL, "%s: cu_seqlens[N] = %d but T_total = %d", what,
+                        cu_seqlens_host[N], T_total);
+    }
+    st = check_prefill_ptrs(what, q, k, v, g, beta, h0, o, ht, T_total);
+    if (st != GDR_OK) return st;
+    if (h0 && ht && h0 != ht) {
+        const size_t bytes = (size_t)N * H * Dv * Dk * sizeof(float);
+        const char *a0 = (const char *)h0, *a1 = (const char *)ht;
+        if (a0 < a1 + bytes && a1 < a0 + bytes)
+            return fail(GDR_EINVAL, "%s: h0 and ht overlap without being equal", what);
+    }
+    const size_t need = gdr_prefill_workspace_bytes(N);
+    if (!workspace || ws_bytes < need)
+        return fail(GDR_EINVAL, "%s: workspace of %zu bytes needed, %zu given", what, need,
+                    workspace ? ws_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fail(GDR_EINVAL, "%s: workspace is not 16-byte aligned", what);
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int32_t *order = static_cast<int32_t *>(workspace);
+    hipError_t e = gdr::launch_varlen_schedule(cu_seqlens, N, order, s);
+    if (e != hipSuccess) return finish(e, s, what);
+    gdr::PrefillArgs a{};
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.h0 = h0; a.o = o; a.ht = ht;
+    a.cu_seqlens = cu_seqlens; a.order = order;
+    a.N = N; a.T = 0; a.H = H; a.scale = scale; a.channel_gate = gk == GDR_GATE_CHANNEL;
+    e = dt == GDR_BF16 ? gdr::launch_prefill_chunked(Dk, a, s)
+                       : gdr::launch_prefill_recurrent(false, Dk, a, s);
+    return finish(e, s, what);
+}
+
+gdr_status gdr_decode_step(enum gdr_dtype dt, enum gdr_gate gk, int B, int H, int Dk, int Dv,
+                           float scale, const void *q, const void *k, const void *v,
+                           const float *g, const float *beta, float *state, void *o,
+                           void *stream) {
+    const char *what = "gdr_decode_step";
+    gdr_status st = check_common(dt, gk, Dk, Dv, what);
+    if (st != GDR_OK) return st;
+    if (B < 0 || H <= 0) return fail(GDR_EINVAL, "%s: bad sizes B=%d H=%d", what, B, H);
+    if ((long long)B * H >= (1LL << 31))
+        return fail(GDR_EUNSUPPORTED, "%s: B*H too large", what);
+    if (B == 0) return GDR_OK;
+    REQUIRE_PTR(q, "q");
+    REQUIRE_PTR(k, "k");
+    REQUIRE_PTR(v, "v");
+    REQUIRE_PTR(g, "g");
+    if (!beta) return fail(GDR_EINVAL, "%s: beta is NULL", what);
+    REQUIRE_PTR(state, "state");
+    if (!o) return fail(GDR_EINVAL, "%s: o is NULL", what);
+    gdr::DecodeArgs a{};
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.state = state; a.o = o;
+    a.B = B; a.H = H; a.scale = scale;
+    a.g_bh = gk == GDR_GATE_CHANNEL ? Dk : 1;
+    a.g_layer = 0;
+    gdr::DecodeLayers layers;
+    layers.n = 1;
+    layers.code[0] = (uint16_t)(gk == GDR_GATE_CHANNEL ? 1 : 0);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return finish(gdr::launch_decode(dt == GDR_BF16, Dk, a, layers, s), s, what);
+}
+
+gdr_status gdr_decode_placement(const uint8_t *placement, int L, enum gdr_dtype dt, int B,
+                                int H, int Dk, int Dv, float scale, const void *q,
+                                const void *k, const void *v, const float *g,
+                                const float *beta, float *state_pool, void *o, void *stream) {
+    const char *what = "gdr_decode_placement";
+    gdr_status st = check_common(dt, GDR_GATE_CHANNEL, Dk, Dv, what);
+    if (st != GDR_OK) return st;
+    if (!placement) return fail(GDR_EINVAL, "%s: placement is NULL", what);
+    if (L <= 0 || L > gdr::kMaxLayers)
+        return fail(GDR_EINVAL, "%s: L = %d outside 1..%d", what, L, gdr::kMaxLayers);
+    if (B < 0 || H <= 0) return fail(GDR_EINVAL, "%s: bad sizes B=%d H=%d", what, B, H);
+    gdr::DecodeLayers layers;
+    layers.n = 0;
+    for (int l = 0; l < L; ++l) {
+        const int c = placement[l];
+        if (c > GDR_KDA)
+            return fail(GDR_EINVAL, "%s: placement[%d] = %d is not a mixer code 0..3", what, l, c);
+        if (c == GDR_GDN || c == GDR_KDA)
+            layers.code[layers.n++] = (uint16_t)((l << 1) | (c == GDR_KDA ? 1 : 0));
+    }
+    if ((long long)layers.n * B * H >= (1LL << 31))
+        return fail(GDR_EUNSUPPORTED, "%s: too many (layer, b, h) slots", what);
+    if (B == 0 || layers.n == 0) return GDR_OK;
+    REQUIRE_PTR(q, "q");
+    REQUIRE_PTR(k, "k");
+    REQUIRE_PTR(v, "v");
+    REQUIRE_PTR(g, "g");
+    if (!beta) return fail(GDR_EINVAL, "%s: beta is NULL", what);
+    REQUIRE_PTR(state_pool, "state_pool");
+    if (!o) return fail(GDR_EINVAL, "%s: o is NULL", what);
+    gdr::DecodeArgs a{};
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.state = state_pool; a.o = o;
+    a.B = B; a.H = H; a.scale = scale;
+    a.g_bh = Dk;
+    a.g_layer = (long long)B * H * Dk;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return finish(gdr::launch_decode(dt == GDR_BF16, Dk, a, layers, s), s, what);
+}
+
+}  // extern "C"

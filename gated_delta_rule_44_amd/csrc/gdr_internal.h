@@ -1,0 +1,81 @@
+// gdr_internal.h -- shared declarations of libgdr's HIP kernels (gfx950).
+// Internal to the library: the public interface is include/gdr.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdr {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kMaxLayers = 1024;
+
+// Element loads/stores for the two input dtypes (bf16 <-> fp32 conversions
+// are exact one way and round-to-nearest-even the other).
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+    __device__ static inline float load(const float *p) { return *p; }
+    __device__ static inline void store(float *p, float x) { *p = x; }
+    // four consecutive values starting at p (16-byte aligned for fp32)
+    __device__ static inline f32x4 load4(const float *p) {
+        return *reinterpret_cast<const f32x4 *>(p);
+    }
+};
+template <> struct Elem<bf16> {
+    __device__ static inline float load(const bf16 *p) { return (float)*p; }
+    __device__ static inline void store(bf16 *p, float x) { *p = (bf16)x; }
+    __device__ static inline f32x4 load4(const bf16 *p) {
+        bf16x4 h = *reinterpret_cast<const bf16x4 *>(p);
+        return f32x4{(float)h.x, (float)h.y, (float)h.z, (float)h.w};
+    }
+};
+
+// One recurrent layer slot for the decode kernel: layer index and gate kind.
+struct DecodeLayers {
+    int n;                        // number of layers to step
+    uint16_t code[kMaxLayers];    // (layer << 1) | channel_gate
+};
+
+struct DecodeArgs {
+    const void *q, *k, *v;        // [L, B, H, D] dt
+    const float *g;               // gate logs, see g_bh / g_layer
+    const float *beta;            // [L, B, H]
+    float *state;                 // [L, B, H, D, D]
+    void *o;                      // [L, B, H, D] dt
+    int B, H;
+    float scale;
+    long long g_bh;               // stride of g between (b,h) pairs (D or 1)
+    long long g_layer;            // stride of g between layers
+};
+
+hipError_t launch_decode(bool bf16_io, int D, const DecodeArgs &a,
+                         const DecodeLayers &layers, hipStream_t s);
+
+// Fixed-length (cu_seqlens == nullptr, T = seq_len) or packed batches.
+struct PrefillArgs {
+    const void *q, *k, *v;        // [tokens, H, D] dt
+    const float *g;               // [tokens, H] or [tokens, H, D]
+    const float *beta;            // [tokens, H]
+    const float *h0;              // [N, H, D, D] or nullptr
+    void *o;                      // [tokens, H, D] dt
+    float *ht;                    // [N, H, D, D] or nullptr
+    const int32_t *cu_seqlens;    // [N+1] or nullptr (fixed length)
+    const int32_t *order;         // schedule [N] or nullptr (identity)
+    int N, T, H;                  // T used only when cu_seqlens == nullptr
+    float scale;
+    int channel_gate;
+};
+
+hipError_t launch_prefill_recurrent(bool bf16_io, int D, const PrefillArgs &a,
+                                    hipStream_t s);
+hipError_t launch_prefill_chunked(int D, const PrefillArgs &a, hipStream_t s);
+hipError_t launch_varlen_schedule(const int32_t *cu_seqlens, int N,
+                                  int32_t *order, hipStream_t s);
+
+}  // namespace gdr

@@ -1,0 +1,241 @@
+// recurrent.hip -- fused single-token state update (decode) and the
+// token-by-token prefill that repeats it, for gfx950.
+//
+// Per (sequence, head) and token, with the gate given as g = ln a:
+//     S' = S Diag(a);   u = beta (v - S' k);   S <- S' + u k^T;
+//     o  = scale * S q = scale * (S' q + u (k.q))
+// which is the gated delta rule S_t = S_{t-1} Diag(a_t)(I - beta k k^T)
+// + beta v k^T, o_t = S_t q_t, multiplied out (Kimi Delta Attention: a per
+// key channel; Gated DeltaNet: one scalar a per head -- "Super Apriel: One
+// Checkpoint, Many Speeds", gist.science summary, section 2a).
+//
+// Layout.  A 256-thread workgroup (4 waves) owns one Dv x Dk fp32 state.  A
+// state row is D floats = D/4 lanes of float4, so each wave covers 64/(D/4)
+// rows per load and every load instruction of the workgroup reads one
+// contiguous block of rows: the state streams from HBM with dwordx4
+// accesses, once in and once out.  Thread (wave w, lane l) holds rows
+//     row(m) = m * RPI + w * RPW + l / LPR,   m < M
+// at columns 4 * (l % LPR) .. +3.  The two row dot products S'k and S'q are
+// reduced together by a recursive-halving exchange (reduce-scatter) across
+// the LPR lanes of a row, which leaves one finished dot product per lane.
+#include "gdr_internal.h"
+
+namespace gdr {
+namespace {
+
+template <int D> struct Geom {
+    static constexpr int LPR = D / 4;          // lanes per state row
+    static constexpr int RPW = 64 / LPR;       // rows per wave per load
+    static constexpr int NW = 4;               // waves per workgroup
+    static constexpr int RPI = RPW * NW;       // rows per workgroup load
+    static constexpr int M = D / RPI;          // rows held per thread
+    static constexpr int NV = 2 * M;           // dot products per thread
+    static constexpr int LOG_LPR = D == 128 ? 5 : 4;
+    static constexpr int LOG_NV = D == 128 ? 5 : 3;
+    static constexpr int SHIFT = LOG_LPR - LOG_NV;   // lanes sharing a result
+    static_assert(LPR >= NV, "reduce-scatter needs one lane per result");
+};
+
+__device__ inline float dot4(f32x4 a, f32x4 b) {
+    return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
+}
+
+// One token's update of the state slice S held by this thread.  qp, kp, vp
+// point at the head's D-vector for this token, gp at its gate logs (D values
+// for a channel gate, one for a scalar gate).  The output is written to op.
+template <typename T, int D>
+__device__ inline void head_step(f32x4 (&S)[Geom<D>::M], const T *qp, const T *kp,
+                                 const T *vp, const float *gp, bool channel,
+                                 float beta, float scale, T *op, int lane, int w) {
+    using G = Geom<D>;
+    const int c0 = (lane % G::LPR) * 4;
+    const int sub = lane / G::LPR;
+    const f32x4 kv = Elem<T>::load4(kp + c0);
+    const f32x4 qv = Elem<T>::load4(qp + c0);
+    f32x4 lg;
+    if (channel) {
+        lg = *reinterpret_cast<const f32x4 *>(gp + c0);
+    } else {
+        const float s = gp[0];
+        lg = f32x4{s, s, s, s};
+    }
+    constexpr float kLog2e = 1.4426950408889634f;
+    const f32x4 a = f32x4{__builtin_amdgcn_exp2f(lg.x * kLog2e),
+                          __builtin_amdgcn_exp2f(lg.y * kLog2e),
+                          __builtin_amdgcn_exp2f(lg.z * kLog2e),
+                          __builtin_amdgcn_exp2f(lg.w * kLog2e)};
+    const f32x4 ak = a * kv;
+    const f32x4 aq = a * qv;
+
+    // k.q over the full row: all-reduce across the LPR lanes of the row
+    float kq = dot4(kv, qv);
+#pragma unroll
+    for (int mask = G::LPR / 2; mask >= 1; mask >>= 1)
+        kq += __shfl_xor(kq, mask);
+
+    // partial (S'k)_row and (S'q)_row over this thread's 4 columns
+    float val[G::NV];
+#pragma unroll
+    for (int m = 0; m < G::M; ++m) {
+        val[m] = dot4(S[m], ak);
+        val[G::M + m] = dot4(S[m], aq);
+    }
+    // recursive halving: after step with mask b the lane keeps the half of
+    // the list selected by its lane bit b, summed with the partner's copy
+    int n = G::NV;
+#pragma unroll
+    for (int mask = G::LPR / 2; mask >= 1; mask >>= 1) {
+        if (n > 1) {
+            const int half = n / 2;
+            const bool upper = (lane & mask) != 0;
+#pragma unroll
+            for (int i = 0; i < half; ++i) {
+                const float keep = upper ? val[half + i] : val[i];
+                const float give = upper ? val[i] : val[half + i];
+                val[i] = keep + __shfl_xor(give, mask);
+            }
+            n = half;
+        } else {
+            val[0] += __shfl_xor(val[0], mask);
+        }
+    }
+    // this lane now holds result index idx: which = idx / M, row slot idx % M
+    const int idx = (lane % G::LPR) >> G::SHIFT;
+    const bool is_q = idx >= G::M;
+    const int mrow = idx % G::M;
+    const int row = mrow * G::RPI + w * G::RPW + sub;
+
+    const float vrow = Elem<T>::load(vp + row);
+    const float u = beta * (vrow - val[0]);              // valid where !is_q
+    const float u_pair = __shfl_xor(u, G::M << G::SHIFT);   // for is_q lanes
+    if (is_q && (lane & ((1 << G::SHIFT) - 1)) == 0)
+        Elem<T>::store(op + row, scale * (val[0] + u_pair * kq));
+
+    // rank-1 update: every lane needs u for each of its M rows
+#pragma unroll
+    for (int m = 0; m < G::M; ++m) {
+        const float um = __shfl(u, sub * G::LPR + (m << G::SHIFT));
+        S[m] = S[m] * a + um * kv;
+    }
+}
+
+template <int D>
+__device__ inline const float *state_row(const float *st, int m, int lane, int w) {
+    using G = Geom<D>;
+    const int row = m * G::RPI + w * G::RPW + lane / G::LPR;
+    return st + (size_t)row * D + (lane % G::LPR) * 4;
+}
+
+// ---------------------------------------------------------------------------
+// Decode: one workgroup per (recurrent layer, b, h).
+template <typename T, int D>
+__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a, DecodeLayers L) {
+    using G = Geom<D>;
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    const int bh_count = a.B * a.H;
+    const int rec = blockIdx.x / bh_count;
+    const int bh = blockIdx.x - rec * bh_count;
+    const int code = L.code[rec];
+    const int layer = code >> 1;
+    const bool channel = (code & 1) != 0;
+    const size_t slot = (size_t)layer * bh_count + bh;
+
+    float *st = a.state + slot * D * D;
+    f32x4 S[G::M];
+#pragma unroll
+    for (int m = 0; m < G::M; ++m)
+        S[m] = __builtin_nontemporal_load(
+            reinterpret_cast<const f32x4 *>(state_row<D>(st, m, lane, w)));
+
+    head_step<T, D>(S, static_cast<const T *>(a.q) + slot * D,
+                    static_cast<const T *>(a.k) + slot * D,
+                    static_cast<const T *>(a.v) + slot * D,
+                    a.g + layer * a.g_layer + (long long)bh * a.g_bh, channel,
+                    a.beta[slot], a.scale, static_cast<T *>(a.o) + slot * D, lane, w);
+
+#pragma unroll
+    for (int m = 0; m < G::M; ++m)
+        __builtin_nontemporal_store(
+            S[m], reinterpret_cast<f32x4 *>(const_cast<float *>(state_row<D>(st, m, lane, w))));
+}
+
+// ---------------------------------------------------------------------------
+// Prefill in the recurrent form: one workgroup per (sequence, head) walks
+// its tokens in order with the state resident in registers.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void prefill_recurrent_kernel(PrefillArgs a) {
+    using G = Geom<D>;
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    const int rank = blockIdx.x / a.H;
+    const int h = blockIdx.x - rank * a.H;
+    const int n = a.order ? a.order[rank] : rank;
+    long long t0, t1;
+    if (a.cu_seqlens) {
+        t0 = a.cu_seqlens[n];
+        t1 = a.cu_seqlens[n + 1];
+    } else {
+        t0 = (long long)n * a.T;
+        t1 = t0 + a.T;
+    }
+    const size_t sslot = ((size_t)n * a.H + h) * D * D;
+
+    f32x4 S[G::M];
+#pragma unroll
+    for (int m = 0; m < G::M; ++m)
+        S[m] = a.h0 ? *reinterpret_cast<const f32x4 *>(state_row<D>(a.h0 + sslot, m, lane, w))
+                    : f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const size_t tok = (size_t)a.H * D;                 // q/k/v/o token stride
+    const size_t gtok = a.channel_gate ? tok : (size_t)a.H;
+    const size_t goff = a.channel_gate ? (size_t)h * D : (size_t)h;
+    const T *q = static_cast<const T *>(a.q) + h * D;
+    const T *k = static_cast<const T *>(a.k) + h * D;
+    const T *v = static_cast<const T *>(a.v) + h * D;
+    T *o = static_cast<T *>(a.o) + h * D;
+    for (long long t = t0; t < t1; ++t) {
+        head_step<T, D>(S, q + t * tok, k + t * tok, v + t * tok, a.g + t * gtok + goff,
+                        a.channel_gate != 0, a.beta[t * a.H + h], a.scale, o + t * tok,
+                        lane, w);
+    }
+    if (a.ht) {
+#pragma unroll
+        for (int m = 0; m < G::M; ++m)
+            *reinterpret_cast<f32x4 *>(const_cast<float *>(state_row<D>(a.ht + sslot, m, lane, w))) = S[m];
+    }
+}
+
+}  // namespace
+
+hipError_t launch_decode(bool bf16_io, int D, const DecodeArgs &a,
+                         const DecodeLayers &layers, hipStream_t s) {
+    const long long blocks = (long long)layers.n * a.B * a.H;
+    if (blocks <= 0) return hipSuccess;
+    dim3 grid((unsigned)blocks), block(256);
+    if (bf16_io) {
+        if (D == 128) hipLaunchKernelGGL((decode_kernel<bf16, 128>), grid, block, 0, s, a, layers);
+        else          hipLaunchKernelGGL((decode_kernel<bf16, 64>), grid, block, 0, s, a, layers);
+    } else {
+        if (D == 128) hipLaunchKernelGGL((decode_kernel<float, 128>), grid, block, 0, s, a, layers);
+        else          hipLaunchKernelGGL((decode_kernel<float, 64>), grid, block, 0, s, a, layers);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_prefill_recurrent(bool bf16_io, int D, const PrefillArgs &a,
+                                    hipStream_t s) {
+    const long long blocks = (long long)a.N * a.H;
+    if (blocks <= 0) return hipSuccess;
+    dim3 grid((unsigned)blocks), block(256);
+    if (bf16_io) {
+        if (D == 128) hipLaunchKernelGGL((prefill_recurrent_kernel<bf16, 128>), grid, block, 0, s, a);
+        else          hipLaunchKernelGGL((prefill_recurrent_kernel<bf16, 64>), grid, block, 0, s, a);
+    } else {
+        if (D == 128) hipLaunchKernelGGL((prefill_recurrent_kernel<float, 128>), grid, block, 0, s, a);
+        else          hipLaunchKernelGGL((prefill_recurrent_kernel<float, 64>), grid, block, 0, s, a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace gdr

@@ -1,0 +1,179 @@
+/*
+ * gdr.h -- C ABI of libgdr, the gated delta-rule hot path for MI355X (gfx950).
+ *
+ * The operation.  "Super Apriel: One Checkpoint, Many Speeds" (arXiv
+ * 2604.19877) builds every decoder layer with four mixer choices: full
+ * attention, sliding-window attention, Kimi Delta Attention (KDA) and Gated
+ * DeltaNet (GDN) (abstract; gist.science technical summary, section 2a).  The
+ * summary describes KDA as recurrent with a gate per key channel and GDN as
+ * recurrent with one scalar gate per head.  The pages print no formula; this
+ * library implements the standard gated delta rule, per sequence and head:
+ *
+ *     S_t = S_{t-1} Diag(a_t) (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+ *     o_t = scale * S_t q_t          (the state after the token's update)
+ *
+ * S is Dv x Dk, fp32, stored row-major with the key index contiguous
+ * (state[..., i, j], i < Dv, j < Dk).  The gate is passed as its logarithm
+ * g = ln a <= 0 (fp32): GDR_GATE_SCALAR takes one value per token and head,
+ * GDR_GATE_CHANNEL takes Dk values.  beta is one fp32 per token and head.
+ * A placement assigns one mixer per layer and can change between requests
+ * (abstract; summary section 2d); gdr_decode_placement steps only the layers
+ * it tags GDN or KDA.
+ *
+ * Conventions for every entry point.
+ *   - Pointers are DEVICE pointers unless marked "host".  Tensors are dense,
+ *     row-major, in the layouts given per function, and 16-byte aligned.
+ *   - The caller owns every buffer and the stream.  The library never
+ *     allocates, frees or synchronises; work is enqueued on `stream`
+ *     (a hipStream_t; NULL = the default stream) and the call returns.
+ *   - Every argument is checked on the host before any HIP call.  A bad
+ *     argument returns GDR_EINVAL or GDR_EUNSUPPORTED, launches nothing and
+ *     writes nothing.  A failed launch returns GDR_EHIP.  Faults during
+ *     execution surface at the caller's next synchronisation.
+ *   - gdr_last_error() returns a thread-local description of the last
+ *     non-OK status.  No C++ exception crosses this interface; all entry
+ *     points are reentrant.
+ *   - Supported shapes: Dk == Dv, Dk in {64, 128}; chunk == 64 (prefill).
+ *     q, k, v and o share one dtype (GDR_F32 or GDR_BF16); g, beta, states
+ *     are always fp32.  bf16 outputs are rounded to nearest-even.
+ *   - Setting the environment variable GDR_DEBUG=1 makes each call
+ *     synchronise its stream and check for errors (for tests only).
+ */
+#ifndef GDR_H
+#define GDR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int gdr_status;
+enum { GDR_OK = 0, GDR_EINVAL = 1, GDR_EUNSUPPORTED = 2, GDR_EHIP = 3 };
+
+/* dtype of q, k, v and o */
+enum gdr_dtype { GDR_F32 = 0, GDR_BF16 = 1 };
+
+/* GDN: g[..., H]   KDA: g[..., H, Dk] */
+enum gdr_gate { GDR_GATE_SCALAR = 0, GDR_GATE_CHANNEL = 1 };
+
+/* placement codes, one mixer per layer */
+enum gdr_mixer { GDR_FA = 0, GDR_SWA = 1, GDR_GDN = 2, GDR_KDA = 3 };
+
+/*
+ * Device workspace (bytes) that gdr_prefill_chunked_varlen needs for N
+ * packed sequences: a per-call schedule of N int32 entries, rounded up to
+ * 256 bytes.  The fixed-length prefill needs none (returns 0 for N <= 0).
+ */
+size_t gdr_prefill_workspace_bytes(int N);
+
+/*
+ * Chunked prefill over a fixed-length batch: the recurrence above for every
+ * (b, h), all T tokens, returning every output and (optionally) the final
+ * states.
+ *
+ *   dt, gk      dtype of q/k/v/o; gate kind
+ *   B, T, H     batch, tokens per sequence (T >= 0), heads
+ *   Dk, Dv      key and value widths (equal, 64 or 128)
+ *   chunk       64
+ *   scale       multiplies o only
+ *   q, k        [B, T, H, Dk]   dt
+ *   v           [B, T, H, Dv]   dt
+ *   g           [B, T, H] (scalar) or [B, T, H, Dk] (channel), fp32, <= 0
+ *   beta        [B, T, H] fp32
+ *   h0          [B, H, Dv, Dk] fp32 initial states, or NULL for zeros
+ *   o           [B, T, H, Dv]   dt (written)
+ *   ht          [B, H, Dv, Dk] fp32 final states (written), or NULL.
+ *               ht == h0 is allowed (in-place resume); no other aliasing.
+ *   stream      hipStream_t
+ *
+ * bf16 inputs run the chunked form on MFMA (chunk of 64 tokens, WY/UT
+ * transform inside the chunk, state carried between chunks in fp32).  fp32
+ * inputs run the recurrent form token by token in fp32 on the vector ALUs.
+ * With T == 0 nothing is written to o and ht = h0 (zeros if h0 is NULL).
+ * The chunked form forms exp(+-cumulative log-gate) inside a chunk; it is
+ * accurate while the per-channel sum of g over any 64 consecutive tokens of
+ * a chunk stays above -80.
+ */
+gdr_status gdr_prefill_chunked(enum gdr_dtype dt, enum gdr_gate gk, int B, int T,
+                               int H, int Dk, int Dv, int chunk, float scale,
+                               const void *q, const void *k, const void *v,
+                               const float *g, const float *beta, const float *h0,
+                               void *o, float *ht, void *stream);
+
+/*
+ * Chunked prefill over a packed variable-length batch.  Sequence n owns
+ * tokens [cu_seqlens[n], cu_seqlens[n+1]) of the packed axis; its state
+ * starts at h0[n] (zeros if h0 is NULL) and nothing crosses a boundary.
+ * Chunks start at each sequence's own first token.
+ *
+ *   N                 number of sequences (>= 0)
+ *   T_total           packed tokens (== cu_seqlens[N])
+ *   cu_seqlens        device int32 [N+1], non-decreasing, cu_seqlens[0] == 0
+ *   cu_seqlens_host   host copy of cu_seqlens, optional (NULL): when given
+ *                     it is validated on the host before launching
+ *   q, k              [T_total, H, Dk]   v, o [T_total, H, Dv]
+ *   g                 [T_total, H] or [T_total, H, Dk] fp32;  beta [T_total, H]
+ *   h0, ht            [N, H, Dv, Dk] fp32 (h0 may be NULL, ht may be NULL)
+ *   workspace         device buffer of gdr_prefill_workspace_bytes(N) bytes;
+ *                     the call writes its schedule there (longest sequence
+ *                     first) and it must not be shared with a concurrent call
+ * Other arguments as gdr_prefill_chunked.  Only bf16 runs chunked; fp32
+ * runs the recurrent form.  Without cu_seqlens_host, device offsets that
+ * violate the rules above give undefined results.
+ */
+gdr_status gdr_prefill_chunked_varlen(enum gdr_dtype dt, enum gdr_gate gk, int N,
+                                      int T_total, int H, int Dk, int Dv, int chunk,
+                                      float scale, const int32_t *cu_seqlens,
+                                      const int32_t *cu_seqlens_host,
+                                      const void *q, const void *k, const void *v,
+                                      const float *g, const float *beta,
+                                      const float *h0, void *o, float *ht,
+                                      void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * One decode token for B sequences and H heads: the fused state update.
+ * Each (b, h) state is read from HBM once and written once.
+ *
+ *   q, k   [B, H, Dk] dt;   v [B, H, Dv] dt
+ *   g      [B, H] (scalar) or [B, H, Dk] (channel) fp32;  beta [B, H] fp32
+ *   state  [B, H, Dv, Dk] fp32, updated in place
+ *   o      [B, H, Dv] dt (written)
+ */
+gdr_status gdr_decode_step(enum gdr_dtype dt, enum gdr_gate gk, int B, int H,
+                           int Dk, int Dv, float scale, const void *q,
+                           const void *k, const void *v, const float *g,
+                           const float *beta, float *state, void *o, void *stream);
+
+/*
+ * One decode token through a stack of L layers under a placement: every
+ * layer tagged GDR_GDN (scalar gate: reads g[l, b, h, 0]) or GDR_KDA
+ * (channel gate: reads g[l, b, h, :]) is stepped with gdr_decode_step's
+ * update, all in one launch.  Layers tagged GDR_FA or GDR_SWA are not
+ * touched: their slots of state_pool and o keep their bytes.
+ *
+ *   placement   host uint8 [L], codes gdr_mixer (0..3)
+ *   L           layers (1..1024)
+ *   q, k        [L, B, H, Dk] dt;  v [L, B, H, Dv] dt
+ *   g           [L, B, H, Dk] fp32;  beta [L, B, H] fp32
+ *   state_pool  [L, B, H, Dv, Dk] fp32, updated in place for GDN/KDA layers
+ *   o           [L, B, H, Dv] dt (written for GDN/KDA layers only)
+ */
+gdr_status gdr_decode_placement(const uint8_t *placement, int L, enum gdr_dtype dt,
+                                int B, int H, int Dk, int Dv, float scale,
+                                const void *q, const void *k, const void *v,
+                                const float *g, const float *beta,
+                                float *state_pool, void *o, void *stream);
+
+/* Thread-local text describing the last non-OK status of this thread. */
+const char *gdr_last_error(void);
+
+/* Library version string. */
+const char *gdr_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDR_H */

@@ -1,0 +1,143 @@
+"""CPU tests of the C ABI: the library loads without a GPU, exports every
+symbol include/gdr.h declares, and rejects bad arguments on the host before
+any HIP call (no compute is launched here)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import gated_delta_rule_44_amd as gdr
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdr.h")
+EINVAL, EUNSUPPORTED = 1, 2
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(gdr.lib_path()):
+        pytest.skip("libgdr.so not built")
+    return gdr._load()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdr_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    assert names == sorted(["gdr_prefill_workspace_bytes", "gdr_prefill_chunked",
+                            "gdr_prefill_chunked_varlen", "gdr_decode_step",
+                            "gdr_decode_placement", "gdr_last_error",
+                            "gdr_version"])
+
+
+def test_library_exports_every_declared_symbol(lib):
+    raw = ctypes.CDLL(gdr.lib_path())
+    for name in declared_functions():
+        assert hasattr(raw, name), name
+
+
+def test_version_and_workspace(lib):
+    assert gdr.version().startswith("gdr")
+    assert gdr.workspace_bytes(0) == 0
+    assert gdr.workspace_bytes(1) == 256
+    assert gdr.workspace_bytes(64) == 256
+    assert gdr.workspace_bytes(65) == 512
+
+
+F = ctypes.c_float
+FAKE = 1 << 20          # aligned, never dereferenced: validation fails first
+MIS = FAKE + 4          # misaligned
+
+
+def prefill(lib, dt=1, gk=0, B=1, T=64, H=1, Dk=128, Dv=128, chunk=64, q=FAKE,
+            k=FAKE, v=FAKE, g=FAKE, beta=FAKE, h0=None, o=FAKE, ht=FAKE):
+    return lib.gdr_prefill_chunked(dt, gk, B, T, H, Dk, Dv, chunk, F(1.0), q, k,
+                                   v, g, beta, h0, o, ht, None)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(dt=7), EINVAL, "dtype"),
+    (dict(gk=3), EINVAL, "gate kind"),
+    (dict(Dk=128, Dv=64), EUNSUPPORTED, "Dk"),
+    (dict(Dk=96, Dv=96), EUNSUPPORTED, "supported widths"),
+    (dict(chunk=32), EUNSUPPORTED, "chunk"),
+    (dict(B=-1), EINVAL, "bad sizes"),
+    (dict(T=-5), EINVAL, "bad sizes"),
+    (dict(H=0), EINVAL, "bad sizes"),
+    (dict(q=None), EINVAL, "q is NULL"),
+    (dict(k=MIS), EINVAL, "k is not 16-byte aligned"),
+    (dict(o=None), EINVAL, "o is NULL"),
+    (dict(h0=MIS), EINVAL, "h0 is not 16-byte aligned"),
+    (dict(h0=FAKE, ht=FAKE + 256), EINVAL, "overlap"),
+])
+def test_prefill_rejects(lib, kw, code, msg):
+    assert prefill(lib, **kw) == code
+    assert msg in lib.gdr_last_error().decode()
+
+
+def test_prefill_empty_batch_is_ok_without_gpu(lib):
+    assert prefill(lib, B=0) == 0
+
+
+def varlen(lib, N=2, Tt=10, cu=FAKE, host=None, ws=FAKE, ws_bytes=256, **kw):
+    a = dict(dt=1, gk=1, H=1, Dk=128, Dv=128, chunk=64, q=FAKE, k=FAKE, v=FAKE,
+             g=FAKE, beta=FAKE, h0=None, o=FAKE, ht=None)
+    a.update(kw)
+    hp = None if host is None else host.ctypes.data_as(ctypes.c_void_p)
+    return lib.gdr_prefill_chunked_varlen(
+        a["dt"], a["gk"], N, Tt, a["H"], a["Dk"], a["Dv"], a["chunk"], F(1.0),
+        cu, hp, a["q"], a["k"], a["v"], a["g"], a["beta"], a["h0"], a["o"],
+        a["ht"], ws, ws_bytes, None)
+
+
+def test_varlen_rejects(lib):
+    assert varlen(lib, cu=None) == EINVAL
+    bad = np.array([0, 5, 3], np.int32)
+    assert varlen(lib, Tt=3, host=bad) == EINVAL
+    assert "decreases" in lib.gdr_last_error().decode()
+    assert varlen(lib, Tt=9, host=np.array([0, 4, 10], np.int32)) == EINVAL
+    assert "T_total" in lib.gdr_last_error().decode()
+    assert varlen(lib, Tt=10, host=np.array([1, 4, 10], np.int32)) == EINVAL
+    assert varlen(lib, ws=None) == EINVAL
+    assert "workspace" in lib.gdr_last_error().decode()
+    assert varlen(lib, ws_bytes=8) == EINVAL
+    assert varlen(lib, N=0) == 0
+
+
+def test_decode_rejects(lib):
+    args = lambda **kw: [kw.get("dt", 1), kw.get("gk", 1), kw.get("B", 2), 4,  # noqa: E731
+                         kw.get("D", 128), kw.get("D", 128), F(1.0), FAKE, FAKE,
+                         FAKE, FAKE, FAKE, kw.get("state", FAKE), FAKE, None]
+    assert lib.gdr_decode_step(*args(D=32)) == EUNSUPPORTED
+    assert lib.gdr_decode_step(*args(state=None)) == EINVAL
+    assert lib.gdr_decode_step(*args(state=MIS)) == EINVAL
+    assert lib.gdr_decode_step(*args(B=0)) == 0
+
+
+def test_placement_rejects(lib):
+    def call(p, L=None, **kw):
+        p = np.asarray(p, np.uint8)
+        L = len(p) if L is None else L
+        return lib.gdr_decode_placement(
+            p.ctypes.data_as(ctypes.c_void_p), L, 1, kw.get("B", 2), 4, 128, 128,
+            F(1.0), FAKE, FAKE, FAKE, FAKE, FAKE, kw.get("pool", FAKE), FAKE, None)
+    assert call([0, 1, 4]) == EINVAL
+    assert "placement[2]" in lib.gdr_last_error().decode()
+    assert call([0, 2], L=0) == EINVAL
+    assert call([2, 3], pool=None) == EINVAL
+    assert call([0, 1, 0]) == 0            # nothing recurrent: nothing to do
+    assert lib.gdr_decode_placement(None, 3, 1, 2, 4, 128, 128, F(1.0), FAKE,
+                                    FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == EINVAL
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    monkeypatch.setattr(gdr, "_LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(gdr, "_lib", None)
+    with pytest.raises(gdr.GdrError, match="not built"):
+        gdr.version()

@@ -1,0 +1,237 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on
+seeded inputs, at sizes the oracle finishes in seconds that still span
+several chunks, Dv slices and a ragged tail, plus the edge cases."""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_44_amd as gdr
+import oracle
+from gated_delta_rule_44_amd import synthetic
+from tests.conftest import gpu_available
+from tests.gpu_util import announce, assert_close, to_np
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+DEV = torch.device("cuda:0")
+DTYPES = {"fp32": torch.float32, "bf16": torch.bfloat16}
+
+
+def sync():
+    torch.cuda.synchronize(DEV)
+
+
+# ----------------------------------------------------------------- decode
+@pytest.mark.parametrize("dt", ["fp32", "bf16"])
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_decode_step(dt, gate, D):
+    announce("decode_step %s %s D=%d" % (dt, gate, D))
+    x = synthetic.prefill_inputs(5, 1, 3, D, DTYPES[dt], gate, seed=11, device=DEV)
+    one = {n: x[n][:, 0].contiguous() for n in ("q", "k", "v", "g", "beta")}
+    st = x["h0"].clone()
+    o = gdr.decode_step(one["q"], one["k"], one["v"], one["g"], one["beta"], st,
+                        scale=0.8)
+    sync()
+    o_ref, st_ref = oracle.decode(one["q"], one["k"], one["v"], one["g"],
+                                  one["beta"], x["h0"], scale=0.8)
+    assert_close(o, o_ref, DTYPES[dt], "o")
+    assert_close(st, st_ref, DTYPES[dt], "state")
+    # the state update itself is fp32 either way
+    assert np.abs(to_np(st) - st_ref).max() < 1e-5
+
+
+@pytest.mark.parametrize("dt", ["fp32", "bf16"])
+def test_decode_placement_small(dt):
+    announce("decode_placement small %s" % dt)
+    place = np.array([0, 2, 1, 3, 3, 0, 2, 1], np.uint8)
+    x = synthetic.decode_inputs(8, 6, 3, 128, DTYPES[dt], place=place, seed=12,
+                                device=DEV)
+    pool0 = x["pool"].clone()
+    o = torch.full_like(x["v"], 7.0)
+    gdr.decode_placement(place, x["q"], x["k"], x["v"], x["g"], x["beta"],
+                         x["pool"], o=o)
+    sync()
+    for layer, code in enumerate(place):
+        if code in (synthetic.FA, synthetic.SWA):
+            assert torch.equal(x["pool"][layer], pool0[layer]), "state slot touched"
+            assert bool((o[layer] == 7.0).all()), "output slot touched"
+            continue
+        g = x["g"][layer] if code == synthetic.KDA else x["g"][layer][..., 0]
+        o_ref, st_ref = oracle.decode(x["q"][layer], x["k"][layer], x["v"][layer],
+                                      g, x["beta"][layer], pool0[layer])
+        assert_close(o[layer], o_ref, DTYPES[dt], "o layer %d" % layer)
+        assert_close(x["pool"][layer], st_ref, DTYPES[dt], "state layer %d" % layer)
+
+
+# ---------------------------------------------------------------- prefill
+def run_prefill(x, scale=1.0):
+    o, ht = gdr.prefill(x["q"], x["k"], x["v"], x["g"], x["beta"], h0=x["h0"],
+                        scale=scale)
+    sync()
+    return o, ht
+
+
+def check_prefill(x, o, ht, dtype, scale=1.0):
+    o_ref, ht_ref = oracle.forward(x["q"], x["k"], x["v"], x["g"], x["beta"],
+                                   h0=x["h0"], scale=scale)
+    eo = assert_close(o, o_ref, dtype, "o")
+    eh = assert_close(ht, ht_ref, dtype, "ht")
+    return eo, eh
+
+
+def test_prefill_recurrent_fp32_small_gdn_d64():
+    """The fp32 GDN workload: B=H=1, T=64, d=64, zero initial state."""
+    announce("prefill fp32 GDN T=64 d=64")
+    x = synthetic.prefill_inputs(1, 64, 1, 64, torch.float32, "scalar", seed=1000,
+                                 h0=False, device=DEV)
+    o, ht = run_prefill(x)
+    eo, eh = check_prefill(x, o, ht, torch.float32)
+    announce("  max-abs o=%.2e ht=%.2e" % (eo, eh))
+
+
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
+@pytest.mark.parametrize("D,T", [(64, 70), (128, 130)])
+def test_prefill_recurrent_fp32(gate, D, T):
+    announce("prefill fp32 %s D=%d T=%d" % (gate, D, T))
+    x = synthetic.prefill_inputs(2, T, 3, D, torch.float32, gate, seed=21, device=DEV)
+    o, ht = run_prefill(x, scale=0.5)
+    check_prefill(x, o, ht, torch.float32, scale=0.5)
+
+
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("T", [1, 17, 64, 65, 200, 320])
+def test_prefill_chunked_bf16(gate, D, T):
+    announce("prefill bf16 %s D=%d T=%d" % (gate, D, T))
+    x = synthetic.prefill_inputs(2, T, 3, D, torch.bfloat16, gate, seed=31 + T,
+                                 device=DEV)
+    o, ht = run_prefill(x, scale=0.9)
+    eo, eh = check_prefill(x, o, ht, torch.bfloat16, scale=0.9)
+    announce("  rel-fro o=%.2e ht=%.2e" % (eo, eh))
+
+
+def test_prefill_chunked_bf16_zero_h0_many_heads():
+    announce("prefill bf16 channel zero h0 B=1 T=256 H=9")
+    x = synthetic.prefill_inputs(1, 256, 9, 128, torch.bfloat16, "channel", seed=41,
+                                 h0=False, device=DEV)
+    o, ht = run_prefill(x)
+    check_prefill(x, o, ht, torch.bfloat16)
+
+
+@pytest.mark.parametrize("dt", ["fp32", "bf16"])
+def test_prefill_T0_returns_h0(dt):
+    x = synthetic.prefill_inputs(2, 0, 2, 128, DTYPES[dt], "channel", seed=5, device=DEV)
+    o, ht = run_prefill(x)
+    assert o.numel() == 0
+    assert torch.equal(ht, x["h0"])
+    x["h0"] = None
+    o, ht = run_prefill(x)
+    assert bool((ht == 0).all())
+
+
+@pytest.mark.parametrize("dt", ["fp32", "bf16"])
+def test_prefill_inplace_resume(dt):
+    """ht == h0 aliasing, and resume: 2 calls (split at 77) == 1 call."""
+    announce("prefill in-place resume %s" % dt)
+    x = synthetic.prefill_inputs(2, 160, 2, 128, DTYPES[dt], "scalar", seed=6, device=DEV)
+    o_full, ht_full = run_prefill(x)
+    st = x["h0"].clone()
+    parts = []
+    for lo, hi in ((0, 77), (77, 160)):
+        sl = {n: x[n][:, lo:hi].contiguous() for n in ("q", "k", "v", "g", "beta")}
+        o, _ = gdr.prefill(sl["q"], sl["k"], sl["v"], sl["g"], sl["beta"], h0=st, ht=st)
+        parts.append(o)
+    sync()
+    o_ref, ht_ref = oracle.forward(x["q"], x["k"], x["v"], x["g"], x["beta"], h0=x["h0"])
+    assert_close(torch.cat(parts, 1), o_ref, DTYPES[dt], "o split")
+    assert_close(st, ht_ref, DTYPES[dt], "ht split")
+
+
+def test_prefill_deterministic():
+    x = synthetic.prefill_inputs(2, 300, 4, 128, torch.bfloat16, "channel", seed=8, device=DEV)
+    o1, h1 = run_prefill(x)
+    o2, h2 = run_prefill(x)
+    assert torch.equal(o1, o2) and torch.equal(h1, h2)
+
+
+def test_prefill_equal_channel_gates_match_scalar_gate():
+    announce("KDA with equal channel gates vs GDN (bf16)")
+    x = synthetic.prefill_inputs(2, 200, 3, 128, torch.bfloat16, "scalar", seed=9, device=DEV)
+    oa, ha = run_prefill(x)
+    xc = dict(x)
+    xc["g"] = x["g"][..., None].expand(*x["g"].shape, 128).contiguous()
+    ob, hb = run_prefill(xc)
+    assert_close(ob, oa.float(), torch.bfloat16, "o")
+    assert_close(hb, ha, torch.bfloat16, "ht")
+
+
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
+def test_decode_steps_match_prefill(gate):
+    """T decode steps from h0 give the prefill's outputs and final state."""
+    announce("decode x T vs prefill %s" % gate)
+    T = 40
+    x = synthetic.prefill_inputs(2, T, 3, 128, torch.bfloat16, gate, seed=10, device=DEV)
+    o_p, ht_p = run_prefill(x)
+    st = x["h0"].clone()
+    outs = []
+    for t in range(T):
+        one = {n: x[n][:, t].contiguous() for n in ("q", "k", "v", "g", "beta")}
+        outs.append(gdr.decode_step(one["q"], one["k"], one["v"], one["g"], one["beta"], st))
+    sync()
+    assert_close(torch.stack(outs, 1), o_p.float(), torch.bfloat16, "o")
+    assert_close(st, ht_p, torch.bfloat16, "ht")
+
+
+def test_prefill_guard_bands():
+    """Writes stay inside o and ht: canaries around both are untouched."""
+    x = synthetic.prefill_inputs(1, 100, 2, 128, torch.bfloat16, "channel", seed=12, device=DEV)
+    pad = 4096
+    n_o = x["v"].numel()
+    n_h = x["h0"].numel()
+    o_buf = torch.full((n_o + 2 * pad,), 3.0, device=DEV, dtype=torch.bfloat16)
+    h_buf = torch.full((n_h + 2 * pad,), 5.0, device=DEV, dtype=torch.float32)
+    lib = gdr._load()
+    rc = lib.gdr_prefill_chunked(
+        1, 1, 1, 100, 2, 128, 128, 64, ctypes.c_float(1.0),
+        x["q"].data_ptr(), x["k"].data_ptr(), x["v"].data_ptr(), x["g"].data_ptr(),
+        x["beta"].data_ptr(), x["h0"].data_ptr(), o_buf.data_ptr() + 2 * pad,
+        h_buf.data_ptr() + 4 * pad, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert rc == 0, lib.gdr_last_error()
+    sync()
+    assert bool((o_buf[:pad] == 3.0).all()) and bool((o_buf[pad + n_o:] == 3.0).all())
+    assert bool((h_buf[:pad] == 5.0).all()) and bool((h_buf[pad + n_h:] == 5.0).all())
+    o_ref, ht_ref = oracle.forward(x["q"], x["k"], x["v"], x["g"], x["beta"], h0=x["h0"])
+    assert_close(o_buf[pad:pad + n_o].view(x["v"].shape), o_ref, torch.bfloat16, "o")
+
+
+# ----------------------------------------------------------------- varlen
+@pytest.mark.parametrize("dt", ["fp32", "bf16"])
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
+def test_prefill_varlen(dt, gate):
+    lens = [130, 0, 1, 64, 300, 17, 65]
+    announce("varlen %s %s lens=%s" % (dt, gate, lens))
+    x = synthetic.varlen_inputs(lens, 3, 128, DTYPES[dt], gate, seed=13, device=DEV)
+    o, ht = gdr.prefill_varlen(x["q"], x["k"], x["v"], x["g"], x["beta"],
+                               x["cu_seqlens"], h0=x["h0"],
+                               cu_seqlens_host=x["cu_seqlens_host"])
+    sync()
+    o_ref, ht_ref = oracle.forward(x["q"], x["k"], x["v"], x["g"], x["beta"],
+                                   h0=x["h0"], cu_seqlens=x["cu_seqlens_host"])
+    assert_close(o, o_ref, DTYPES[dt], "o")
+    assert_close(ht, ht_ref, DTYPES[dt], "ht")
+    # the empty sequence keeps its initial state exactly
+    assert torch.equal(ht[1], x["h0"][1])
+
+
+def test_prefill_varlen_equals_fixed_when_uniform():
+    x = synthetic.prefill_inputs(3, 150, 2, 128, torch.bfloat16, "channel", seed=14, device=DEV)
+    o1, h1 = run_prefill(x)
+    cu = torch.arange(4, device=DEV, dtype=torch.int32) * 150
+    flat = {n: x[n].reshape(450, *x[n].shape[2:]) for n in ("q", "k", "v", "g", "beta")}
+    o2, h2 = gdr.prefill_varlen(flat["q"], flat["k"], flat["v"], flat["g"], flat["beta"],
+                                cu, h0=x["h0"])
+    sync()
+    assert torch.equal(o1.reshape(450, 2, 128), o2) and torch.equal(h1, h2)
