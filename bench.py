@@ -1,0 +1,256 @@
+#!/usr/bin/env python3
+"""Throughput of the gated delta-rule hot path on one MI355X.
+
+Headline (the single JSON line's `value`): chunked prefill tokens/s on the
+Gated DeltaNet workload B=4, H=16, T=4096, d_k=d_v=128, bf16 q/k/v, fp32
+gates/beta/initial state, chunk 64 (one gdr_prefill_chunked launch per
+step, outputs plus final states).  Inputs are resident in HBM before timing
+and rotate over three input sets so that a step cannot be served from the
+256 MB last-level cache.
+
+The same line carries:
+  roofline      the prefill kernel's algorithmic HBM bytes per launch over
+                its average launch time (HIP events on the launch stream),
+                against 8 TB/s; `traffic` is the measured bytes per launch
+                from rocprofv3 FETCH_SIZE/WRITE_SIZE counters when given
+  cpu_baseline  the fp64 oracle on the host cores, on a bounded sample of
+                the same workload (the first tokens of every sequence/head)
+  secondary     the other hot-path entry points measured in the same run:
+                KDA prefill, the placement-driven decode step (state-update
+                GB/s and % of HBM peak) and the packed variable-length KDA
+                prefill.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+                       [--only-headline] [--no-cpu-baseline]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "GDN/KDA prefill tokens/s + decode state-update GB/s (% of HBM peak), 1 GPU"
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_TFLOPS = 2500.0
+D, C = 128, 64
+# counter summaries measured with rocprofv3 on this kernel build (see
+# profiles/); bytes per launch, or None when not measured for this build
+MEASURED_TRAFFIC = None
+
+
+def prefill_bytes(tokens_heads, units, gate):
+    """Algorithmic HBM bytes: q,k,v,o in bf16, beta and the gate in fp32 per
+    token-head; initial and final fp32 state per (sequence, head)."""
+    per_tok = 3 * D * 2 + D * 2 + 4 + (4 * D if gate == "channel" else 4)
+    return tokens_heads * per_tok + units * 2 * D * D * 4
+
+
+def prefill_flops(tokens_heads):
+    """Algorithmic flops of the chunked form per token-head (causal
+    triangles only): 5Cd + 6d^2 + C^2/3."""
+    return tokens_heads * (5 * C * D + 6 * D * D + C * C / 3.0)
+
+
+def decode_bytes(head_steps, gate_bytes):
+    """Per head-step: fp32 state read + write, q,k,v in bf16, o bf16, beta,
+    gate."""
+    return head_steps * (2 * D * D * 4 + 3 * D * 2 + D * 2 + 4) + gate_bytes
+
+
+def timed(fn, steps, warmup, stream):
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(steps):
+        fn(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps   # ms per step
+
+
+def bench_prefill(gdr, synthetic, torch, dev, B, T, H, gate, seed, steps, warmup,
+                  h0=True, sets=3):
+    xs = [synthetic.prefill_inputs(B, T, H, D, torch.bfloat16, gate, seed=seed + i,
+                                   h0=h0, device=dev) for i in range(sets)]
+    outs = [(torch.empty_like(x["v"]), torch.empty((B, H, D, D), device=dev,
+                                                     dtype=torch.float32)) for x in xs]
+    lib = gdr._load()
+    import ctypes
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    gk = 1 if gate == "channel" else 0
+    args = []
+    for x, (o, ht) in zip(xs, outs):
+        args.append([1, gk, B, T, H, D, D, C, ctypes.c_float(1.0)] +
+                    [ctypes.c_void_p(t.data_ptr()) if t is not None else None
+                     for t in (x["q"], x["k"], x["v"], x["g"], x["beta"], x["h0"], o, ht)]
+                    + [sp])
+
+    def step(i):
+        rc = lib.gdr_prefill_chunked(*args[i % sets])
+        if rc:
+            raise RuntimeError(lib.gdr_last_error().decode())
+    ms = timed(step, steps, warmup, stream)
+    del xs, outs
+    return ms
+
+
+def bench_varlen(gdr, synthetic, torch, dev, steps, warmup):
+    lens = synthetic.varlen_lengths(943)
+    x = synthetic.varlen_inputs(lens, 32, D, torch.bfloat16, "channel", seed=1004,
+                                device=dev)
+    o = torch.empty_like(x["v"])
+    ht = torch.empty_like(x["h0"])
+    ws = torch.empty(gdr.workspace_bytes(len(lens)), device=dev, dtype=torch.uint8)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        gdr.prefill_varlen(x["q"], x["k"], x["v"], x["g"], x["beta"], x["cu_seqlens"],
+                           h0=x["h0"], workspace=ws, ht=ht)
+    ms = timed(step, steps, warmup, stream)
+    tokens = sum(lens)
+    del x, o, ht
+    return ms, tokens, lens
+
+
+def bench_decode(gdr, synthetic, torch, dev, steps, warmup):
+    place = synthetic.placement(0, 48)
+    x = synthetic.decode_inputs(48, 256, 32, D, torch.bfloat16, place=place,
+                                seed=1003, device=dev)
+    o = torch.empty_like(x["v"])
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        gdr.decode_placement(place, x["q"], x["k"], x["v"], x["g"], x["beta"],
+                             x["pool"], o=o)
+    ms = timed(step, steps, warmup, stream)
+    n_gdn = int((place == synthetic.GDN).sum())
+    n_kda = int((place == synthetic.KDA).sum())
+    del x, o
+    return ms, n_gdn, n_kda, synthetic.placement_string(place)
+
+
+def cpu_baseline(synthetic, torch, target_s=12.0):
+    """fp64 oracle on the host: every (sequence, head) of the GDN prefill
+    workload, truncated to its first T_s tokens (T_s sized for ~target_s of
+    CPU time from a short calibration run)."""
+    import oracle
+    B, T, H = 4, 4096, 16
+    x = synthetic.prefill_inputs(B, T, H, D, torch.bfloat16, "scalar", seed=1001,
+                                 device="cpu")
+    threads = oracle.max_threads()
+
+    def run(ts):
+        sl = {n: x[n][:, :ts].contiguous() for n in ("q", "k", "v", "g", "beta")}
+        t0 = time.perf_counter()
+        oracle.forward(sl["q"], sl["k"], sl["v"], sl["g"], sl["beta"], h0=x["h0"])
+        return time.perf_counter() - t0
+
+    cal = 32
+    dt = run(cal)
+    ts = int(min(T, max(cal, cal * target_s / max(dt, 1e-6))))
+    dt = run(ts)
+    return {"value": B * ts / dt, "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "GDN prefill B=4 H=16 d=128, first %d of 4096 tokens of every "
+                      "sequence (all 64 sequence-heads), fp64 token-by-token, %.1f s"
+                      % (ts, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--only-headline", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(each GPU would run its own share of sequences/heads independently).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gated_delta_rule_44_amd as gdr
+    from gated_delta_rule_44_amd import synthetic
+    dev = torch.device("cuda:0")
+
+    B, T, H = 4, 4096, 16
+    ms = bench_prefill(gdr, synthetic, torch, dev, B, T, H, "scalar", 1001,
+                       args.steps, args.warmup)
+    tokens = B * T
+    th = tokens * H
+    nbytes = prefill_bytes(th, B * H, "scalar")
+    flops = prefill_flops(th)
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": tokens / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "gdn_prefill_B4_H16_T4096_d128_bf16", "B": B, "T": T,
+                   "H": H, "d_k": D, "d_v": D, "chunk": C, "gate": "scalar (GDN)",
+                   "state": "fp32, h0 and ht", "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": MEASURED_TRAFFIC,
+                     "kernel": "chunked_kernel<128, scalar gate>",
+                     "algorithmic_bytes_per_launch": nbytes,
+                     "mfma_tflops_alg": flops / (ms * 1e-3) / 1e12,
+                     "mfma_frac_alg": flops / (ms * 1e-3) / 1e12 / MFMA_BF16_TFLOPS},
+    }
+
+    if not args.only_headline:
+        sec = []
+        ms2 = bench_prefill(gdr, synthetic, torch, dev, 2, 8192, 32, "channel", 1002,
+                            args.steps, args.warmup, h0=False, sets=3)
+        th2 = 2 * 8192 * 32
+        b2 = prefill_bytes(th2, 64, "channel") - 64 * D * D * 4   # no h0 read
+        sec.append({"workload": "kda_prefill_B2_H32_T8192_d128_bf16",
+                    "ms_per_step": ms2, "tokens_per_s": 2 * 8192 / (ms2 * 1e-3),
+                    "GB_per_s": b2 / (ms2 * 1e-3) / 1e9,
+                    "frac_hbm": b2 / (ms2 * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                    "mfma_frac_alg": prefill_flops(th2) / (ms2 * 1e-3) / 1e12 / MFMA_BF16_TFLOPS})
+        ms3, n_gdn, n_kda, pstr = bench_decode(gdr, synthetic, torch, dev,
+                                               max(5, args.steps // 5), max(2, args.warmup // 5))
+        hs = (n_gdn + n_kda) * 256 * 32
+        b3 = decode_bytes(hs, (n_gdn * 4 + n_kda * 4 * D) * 256 * 32)
+        sec.append({"workload": "placement_decode_L48_B256_H32_d128_bf16",
+                    "placement": pstr, "recurrent_layers": n_gdn + n_kda,
+                    "ms_per_step": ms3, "tokens_per_s": 256 / (ms3 * 1e-3),
+                    "GB_per_s": b3 / (ms3 * 1e-3) / 1e9,
+                    "frac_hbm": b3 / (ms3 * 1e-3) / 1e9 / HBM_PEAK_GBS})
+        ms4, tok4, lens = bench_varlen(gdr, synthetic, torch, dev,
+                                       max(5, args.steps // 5), max(2, args.warmup // 5))
+        b4 = prefill_bytes(tok4 * 32, 16 * 32, "channel")
+        sec.append({"workload": "kda_varlen_N16_H32_d128_bf16", "tokens": tok4,
+                    "ms_per_step": ms4, "tokens_per_s": tok4 / (ms4 * 1e-3),
+                    "GB_per_s": b4 / (ms4 * 1e-3) / 1e9,
+                    "frac_hbm": b4 / (ms4 * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                    "mfma_frac_alg": prefill_flops(tok4 * 32) / (ms4 * 1e-3) / 1e12 / MFMA_BF16_TFLOPS})
+        line["secondary"] = sec
+
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(synthetic, torch)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
