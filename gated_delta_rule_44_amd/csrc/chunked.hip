@@ -38,6 +38,8 @@
 //   5  O = Qt S0^T + P U, and S^T <- e^{b_C} (.) S^T + Kh^T U
 // All contractions use bf16 operands with fp32 accumulation; the state is
 // carried in fp32 registers and rounded to bf16 only as an MFMA operand.
+#include <type_traits>
+
 #include "gdr_internal.h"
 
 namespace gdr {
@@ -96,12 +98,41 @@ __device__ inline bf16x8 frag_cols(const bf16 *base, int ld, int k0, int n0, int
     return __builtin_bit_cast(bf16x8, v);
 }
 
+// A copy of x the compiler cannot see through: lane-dependent addresses are
+// rebuilt from it each iteration instead of being hoisted out of the chunk
+// loop (where they would occupy registers for the whole loop).
+__device__ inline int opaque(int x) {
+    int y;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(y) : "v"(x));
+    return y;
+}
+
+// Per-thread indices used by every phase.
+template <int D> struct LaneIds {
+    int tid, lane, w, l15, l4;
+    int cg, rg;        // gate phase: 8-channel group, row group
+    int vr, vc;        // v tile: row, first column
+    __device__ explicit LaneIds(int t) {
+        constexpr int CG = D / 8;
+        constexpr int RPW = 64 / CG;
+        tid = t;
+        lane = t & 63;
+        w = __builtin_amdgcn_readfirstlane(t >> 6);
+        l15 = lane & 15;
+        l4 = lane >> 4;
+        cg = lane % CG;
+        rg = w * RPW + lane / CG;
+        vr = t >> 3;
+        vc = (t & 7) * 4;
+    }
+};
+
 template <int D, bool CH> struct Smem {
     static constexpr int PD = D + 8;   // padded row length for D-wide rows
     alignas(16) bf16 Q[C * PD];        // q (GDN) or q (.) e^b (KDA), [r][j]
     alignas(16) bf16 K[C * PD];        // k (GDN) or k (.) e^b (KDA), [r][j]
     alignas(16) bf16 Kb[CH ? C * PD : 8];   // k (.) e^-b (KDA), [r][j]
-    alignas(16) bf16 Kh[C * PD];       // k (.) e^{b_C - b}, [s][j]
+    alignas(16) bf16 Kh[2][C * PD];    // k (.) e^{b_C - b}, [s][j], by chunk parity
     alignas(16) bf16 S[BV * PD];       // bf16 copy of the state slice, [i][j]
     alignas(16) bf16 Tm[C * PC];       // T, [r][s]
     alignas(16) bf16 P[C * PC];        // P, [r][s]
@@ -110,30 +141,57 @@ template <int D, bool CH> struct Smem {
     alignas(16) bf16 V[C * PV];        // v tile, [r][i]
     alignas(16) float LT[C * PL];      // L^T = (diag(beta) A)^T, [s][r]
     alignas(16) float Y[4 * 16 * PY];  // inverted diagonal blocks, [b][r][c]
-    alignas(16) float gb[C];           // GDN: cumulative log gate per row
     alignas(16) float beta[C];
-    alignas(16) float gam[D];          // e^{b_C} per channel (GDN: gam[0])
-    alignas(16) float tot[NW * D];     // KDA: per-wave sums of g
+    alignas(16) float gb[2][C];        // GDN: cumulative log gate, by chunk parity
+    alignas(16) float gam[2][D];       // e^{b_C} per channel (GDN: [0]), by parity
+    alignas(16) float tot[CH ? NW * D : 4];   // KDA: per-wave sums of g
 };
 
+// A x B^T over a D-long contraction for one 16x16 output block: rows ra.. of
+// the row-major tile A and rows rb.. of the row-major tile B.
+template <int KS>
+__device__ inline f32x4 gemm_nt(const bf16 *A, int lda, int ra, const bf16 *B, int ldb, int rb,
+                                int lane, f32x4 acc) {
+    bf16x8 fa[KS], fb[KS];
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+        fa[kk] = frag_rows(A, lda, ra, 32 * kk, lane);
+        fb[kk] = frag_rows(B, ldb, rb, 32 * kk, lane);
+    }
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) acc = mfma32(fa[kk], fb[kk], acc);
+    return acc;
+}
+
+__device__ inline void tri_block(int tri, int &I, int &J) {
+    I = tri < 1 ? 0 : tri < 3 ? 1 : tri < 6 ? 2 : 3;
+    J = tri - I * (I + 1) / 2;
+}
+
+// Software pipeline.  Iteration j of the chunk loop works on three chunks at
+// once, with three workgroup barriers:
+//   chunk j-1 ("state"):  U = T X, then O = Qt S0^T + P U and the state update
+//   chunk j   ("prep"):   gated operands -> LDS, A -> L, T (diagonal blocks by
+//                         forward substitution, the rest by MFMA), P, X, Qt S0^T
+//   chunk j+1 ("gate"):   gate prefix sums and gated operands in registers
+//   chunk j+2:            global loads into registers
+//   phase A: U(j-1) || store gated operands of chunk j
+//   phase B: O(j-1), state update(j-1) || A(j), diagonal inverses || scan(j+1)
+//   phase C: T(j) off-diagonal (wave 0) || Qt S0^T(j), X(j) (waves 1-4)
+//            || P(j) (waves 5-7) || gated operands of chunk j+1 || loads j+2
 template <int D, bool CH>
 __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
     using Sm = Smem<D, CH>;
+    using LI = LaneIds<D>;
     constexpr int PD = Sm::PD;
     constexpr int NTILE = D / BV;
     constexpr int CG = D / 8;          // 8-channel groups per row
     constexpr int RPW = 64 / CG;       // row groups per wave
     constexpr int RPT = C / (NW * RPW);// rows per thread in the gate phase
     constexpr int KD = D / 32;         // x32 steps over a D-long contraction
-    constexpr int SB = D / 64;         // S^T blocks per wave (x2 value blocks / NW)
+    constexpr int SB = D / 64;         // S^T blocks per wave
     static_assert(RPT >= 1, "gate phase layout");
     __shared__ Sm sm;
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int w = tid >> 6;
-    const int l15 = lane & 15;
-    const int l4 = lane >> 4;
 
     // ---- work mapping: the Dv slices of one (sequence, head) share an XCD
     const int bid = blockIdx.x;
@@ -160,80 +218,95 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
     const bf16 *kg = static_cast<const bf16 *>(a.k) + (size_t)h * D;
     const bf16 *vg = static_cast<const bf16 *>(a.v) + (size_t)h * D + i0;
     bf16 *og = static_cast<bf16 *>(a.o) + (size_t)h * D + i0;
+    const long long nch = (t1 - t0 + C - 1) / C;
+    auto rows_of = [&](long long c) -> int {
+        const long long rem = t1 - (t0 + c * C);
+        return rem < C ? (int)rem : C;
+    };
+    const int tid0 = threadIdx.x;
 
     // T and P keep zero upper triangles: only lower blocks are ever written
-    for (int e = tid; e < C * PC; e += NT) {
+    for (int e = tid0; e < C * PC; e += NT) {
         sm.Tm[e] = (bf16)0.f;
         sm.P[e] = (bf16)0.f;
     }
 
     // ---- state S^T blocks in registers: wave w, block sb holds S^T[j][iv]
     //      for j = 16*Jk + 4*l4 + e, iv = 16*Jv + l15
-    auto jk_of = [&](int sb) { return SB == 2 ? w : (w >> 1); };
-    auto jv_of = [&](int sb) { return SB == 2 ? sb : (w & 1); };
+    auto jk_of = [](const LI &L, int sb) { return SB == 2 ? L.w : (L.w >> 1); };
+    auto jv_of = [](const LI &L, int sb) { return SB == 2 ? sb : (L.w & 1); };
     f32x4 St[SB];
+    {
+        const LI L(tid0);
 #pragma unroll
-    for (int sb = 0; sb < SB; ++sb) {
-        const int j = 16 * jk_of(sb) + 4 * l4;
-        const int iv = 16 * jv_of(sb) + l15;
-        f32x4 s = {0.f, 0.f, 0.f, 0.f};
-        if (a.h0) s = *reinterpret_cast<const f32x4 *>(a.h0 + sslot + (size_t)(i0 + iv) * D + j);
-        St[sb] = s;
-        *reinterpret_cast<bf16x4 *>(&sm.S[iv * PD + j]) = cvt4(s);
+        for (int sb = 0; sb < SB; ++sb) {
+            const int j = 16 * jk_of(L, sb) + 4 * L.l4;
+            const int iv = 16 * jv_of(L, sb) + L.l15;
+            f32x4 s = {0.f, 0.f, 0.f, 0.f};
+            if (a.h0) s = *reinterpret_cast<const f32x4 *>(a.h0 + sslot + (size_t)(i0 + iv) * D + j);
+            St[sb] = s;
+            *reinterpret_cast<bf16x4 *>(&sm.S[iv * PD + j]) = cvt4(s);
+        }
     }
 
-    // ---- gate-phase thread layout: 8 channels x RPT rows per thread
-    const int cg = lane % CG;
-    const int rg = w * RPW + lane / CG;
-    const int vr = tid >> 3;              // v tile: 8 threads per row, 4 values each
-    const int vc = (tid & 7) * 4;
-
-    // ---- prefetch registers for one chunk
-    bf16x8 q8[RPT], k8[RPT];
-    f32x4 g8[CH ? RPT : 1][2];
-    bf16x4 v4;
-    float gsc = 0.f, bet = 0.f;
-    auto prefetch = [&](long long tc, int Cc) {
+    // raw inputs held in registers ahead of use: the gate logs of the next
+    // chunk (reloaded right after its prefix sums are taken), q and k of the
+    // next chunk (reloaded right after they are gated), and v/beta of the
+    // next two chunks (by chunk parity)
+    bf16x8 rq[RPT], rk[RPT];
+    f32x4 rgc[CH ? RPT : 1][2];
+    float rgs = 0.f;
+    bf16x4 rv[2];
+    float rb[2];
+    rv[0] = rv[1] = bf16x4{};
+    rb[0] = rb[1] = 0.f;
+    auto load_g = [&](const LI &L, long long c) {
+        const long long tc = t0 + c * C;
+        const int Cc = rows_of(c);
+        if (CH) {
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) {
-            const int r = rg * RPT + i;
-            if (r < Cc) {
-                const size_t off = (size_t)(tc + r) * tokstride + 8 * cg;
-                q8[i] = ld8(qg + off);
-                k8[i] = ld8(kg + off);
-                if (CH) {
-                    const float *gp = a.g + ((size_t)(tc + r) * a.H + h) * D + 8 * cg;
-                    g8[i][0] = *reinterpret_cast<const f32x4 *>(gp);
-                    g8[i][1] = *reinterpret_cast<const f32x4 *>(gp + 4);
-                }
-            } else {
-                q8[i] = bf16x8{};
-                k8[i] = bf16x8{};
-                if (CH) {
-                    g8[i][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-                    g8[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int i = 0; i < RPT; ++i) {
+                const int r = L.rg * RPT + i;
+                if (r < Cc) {
+                    const float *gp = a.g + ((size_t)(tc + r) * a.H + h) * D + 8 * L.cg;
+                    rgc[i][0] = *reinterpret_cast<const f32x4 *>(gp);
+                    rgc[i][1] = *reinterpret_cast<const f32x4 *>(gp + 4);
+                } else {
+                    rgc[i][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    rgc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
                 }
             }
-        }
-        v4 = vr < Cc ? *reinterpret_cast<const bf16x4 *>(vg + (size_t)(tc + vr) * tokstride + vc)
-                     : bf16x4{};
-        if (tid < C) {
-            bet = tid < Cc ? a.beta[(size_t)(tc + tid) * a.H + h] : 0.f;
-            if (!CH) gsc = tid < Cc ? a.g[(size_t)(tc + tid) * a.H + h] : 0.f;
+        } else {
+            rgs = (L.tid < Cc) ? a.g[(size_t)(tc + L.tid) * a.H + h] : 0.f;
         }
     };
-
-    const long long nchunks = (t1 - t0 + C - 1) / C;
-    if (nchunks > 0) prefetch(t0, (int)((t1 - t0) < C ? (t1 - t0) : C));
-
-    for (long long c = 0; c < nchunks; ++c) {
+    auto load_qkvb = [&](const LI &L, long long c, int par) {
         const long long tc = t0 + c * C;
-        const int Cc = (int)((t1 - tc) < C ? (t1 - tc) : C);
+        const int Cc = rows_of(c);
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const int r = L.rg * RPT + i;
+            if (r < Cc) {
+                const size_t off = (size_t)(tc + r) * tokstride + 8 * L.cg;
+                rq[i] = ld8(qg + off);
+                rk[i] = ld8(kg + off);
+            } else {
+                rq[i] = bf16x8{};
+                rk[i] = bf16x8{};
+            }
+        }
+        rv[par] = L.vr < Cc ? *reinterpret_cast<const bf16x4 *>(vg + (size_t)(tc + L.vr) * tokstride + L.vc)
+                            : bf16x4{};
+        rb[par] = (L.tid < Cc) ? a.beta[(size_t)(tc + L.tid) * a.H + h] : 0.f;
+    };
 
-        // ================= 1a: stage v and beta; gate prefix sums ==========
-        *reinterpret_cast<bf16x4 *>(&sm.V[vr * PV + vc]) = v4;
-        if (tid < C) sm.beta[tid] = bet;
-        float cum[CH ? RPT : 1][8];
+    // gated operands Qt, Kt, Kb of the next chunk, held in registers from
+    // phase C to the next phase A
+    bf16x8 gq[RPT], gk[RPT], gkb[CH ? RPT : 1];
+    float cum[CH ? RPT : 1][8];
+
+    // prefix sums of the gate logs of one chunk (phase B)
+    auto scan = [&](const LI &L, int par) {
         if (CH) {
             float run[8];
 #pragma unroll
@@ -242,127 +315,189 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
             for (int i = 0; i < RPT; ++i) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    run[e] += g8[i][e >> 2][e & 3];
+                    run[e] += rgc[i][e >> 2][e & 3];
                     cum[i][e] = run[e];
                 }
             }
-            // inclusive scan of the row-group sums across the wave
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 float incl = run[e];
 #pragma unroll
                 for (int off = CG; off < 64; off *= 2) {
                     const float y = __shfl_up(incl, off);
-                    if (lane >= off) incl += y;
+                    if (L.lane >= off) incl += y;
                 }
 #pragma unroll
                 for (int i = 0; i < RPT; ++i) cum[i][e] += incl - run[e];
-                if (lane >= 64 - CG) sm.tot[w * D + 8 * cg + e] = incl;
+                if (L.lane >= 64 - CG) sm.tot[L.w * D + 8 * L.cg + e] = incl;
             }
-        } else if (w == 0) {
-            float gv = gsc;
+        } else if (L.w == 0) {
+            float gv = rgs;
 #pragma unroll
             for (int off = 1; off < 64; off *= 2) {
                 const float y = __shfl_up(gv, off);
-                if (lane >= off) gv += y;
+                if (L.lane >= off) gv += y;
             }
-            sm.gb[lane] = gv;
+            sm.gb[par][L.lane] = gv;
         }
-        __syncthreads();
+    };
 
-        // ================= 1b: gated operands in LDS ======================
+    // gated operands of one chunk (phase C): Qt, Kt, Kb into registers; Kh
+    // and e^{b_C} straight into their parity buffers
+    auto gate = [&](const LI &L, int par) {
         if (CH) {
             float bC[8], pre[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) { bC[e] = 0.f; pre[e] = 0.f; }
 #pragma unroll
             for (int ww = 0; ww < NW; ++ww) {
-                const f32x4 t0v = *reinterpret_cast<const f32x4 *>(&sm.tot[ww * D + 8 * cg]);
-                const f32x4 t1v = *reinterpret_cast<const f32x4 *>(&sm.tot[ww * D + 8 * cg + 4]);
-                const float tv[8] = {t0v.x, t0v.y, t0v.z, t0v.w, t1v.x, t1v.y, t1v.z, t1v.w};
+                const f32x4 ta = *reinterpret_cast<const f32x4 *>(&sm.tot[ww * D + 8 * L.cg]);
+                const f32x4 tb = *reinterpret_cast<const f32x4 *>(&sm.tot[ww * D + 8 * L.cg + 4]);
+                const float tv[8] = {ta.x, ta.y, ta.z, ta.w, tb.x, tb.y, tb.z, tb.w};
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     bC[e] += tv[e];
-                    pre[e] += ww < w ? tv[e] : 0.f;
+                    pre[e] += ww < L.w ? tv[e] : 0.f;
                 }
             }
             float gC[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) gC[e] = ex(bC[e]);
-            if (rg == 0) {
-                *reinterpret_cast<f32x4 *>(&sm.gam[8 * cg]) = f32x4{gC[0], gC[1], gC[2], gC[3]};
-                *reinterpret_cast<f32x4 *>(&sm.gam[8 * cg + 4]) = f32x4{gC[4], gC[5], gC[6], gC[7]};
+            if (L.rg == 0) {
+                *reinterpret_cast<f32x4 *>(&sm.gam[par][8 * L.cg]) = f32x4{gC[0], gC[1], gC[2], gC[3]};
+                *reinterpret_cast<f32x4 *>(&sm.gam[par][8 * L.cg + 4]) = f32x4{gC[4], gC[5], gC[6], gC[7]};
             }
 #pragma unroll
             for (int i = 0; i < RPT; ++i) {
-                const int r = rg * RPT + i;
+                const int r = L.rg * RPT + i;
                 float qt[8], kt[8], kb[8], kh[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const float eb = ex(cum[i][e] + pre[e]);
                     const float ebi = __builtin_amdgcn_rcpf(eb);
-                    const float kv = (float)k8[i][e];
-                    qt[e] = (float)q8[i][e] * eb;
+                    const float kv = (float)rk[i][e];
+                    qt[e] = (float)rq[i][e] * eb;
                     kt[e] = kv * eb;
                     kb[e] = kv * ebi;
                     kh[e] = kb[e] * gC[e];
                 }
-                *reinterpret_cast<bf16x8 *>(&sm.Q[r * PD + 8 * cg]) = cvt8(qt);
-                *reinterpret_cast<bf16x8 *>(&sm.K[r * PD + 8 * cg]) = cvt8(kt);
-                *reinterpret_cast<bf16x8 *>(&sm.Kb[r * PD + 8 * cg]) = cvt8(kb);
-                *reinterpret_cast<bf16x8 *>(&sm.Kh[r * PD + 8 * cg]) = cvt8(kh);
+                gq[i] = cvt8(qt);
+                gk[i] = cvt8(kt);
+                gkb[i] = cvt8(kb);
+                *reinterpret_cast<bf16x8 *>(&sm.Kh[par][r * PD + 8 * L.cg]) = cvt8(kh);
             }
         } else {
-            const float bC = sm.gb[C - 1];
-            if (tid == 0) sm.gam[0] = ex(bC);
+            const float bC = sm.gb[par][C - 1];
+            if (L.tid == 0) sm.gam[par][0] = ex(bC);
 #pragma unroll
             for (int i = 0; i < RPT; ++i) {
-                const int r = rg * RPT + i;
-                const float sc = ex(bC - sm.gb[r]);
+                const int r = L.rg * RPT + i;
+                const float sc = ex(bC - sm.gb[par][r]);
                 float kh[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) kh[e] = (float)k8[i][e] * sc;
-                *reinterpret_cast<bf16x8 *>(&sm.Q[r * PD + 8 * cg]) = q8[i];
-                *reinterpret_cast<bf16x8 *>(&sm.K[r * PD + 8 * cg]) = k8[i];
-                *reinterpret_cast<bf16x8 *>(&sm.Kh[r * PD + 8 * cg]) = cvt8(kh);
+                for (int e = 0; e < 8; ++e) kh[e] = (float)rk[i][e] * sc;
+                gq[i] = rq[i];
+                gk[i] = rk[i];
+                *reinterpret_cast<bf16x8 *>(&sm.Kh[par][r * PD + 8 * L.cg]) = cvt8(kh);
             }
         }
-        // the next chunk's global loads overlap with everything below
-        if (c + 1 < nchunks) {
-            const long long tn = tc + C;
-            prefetch(tn, (int)((t1 - tn) < C ? (t1 - tn) : C));
+    };
+
+    // gated operands, v tile and beta of one chunk into LDS (phase A)
+    auto store_gate = [&](const LI &L, int par) {
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const int r = L.rg * RPT + i;
+            *reinterpret_cast<bf16x8 *>(&sm.Q[r * PD + 8 * L.cg]) = gq[i];
+            *reinterpret_cast<bf16x8 *>(&sm.K[r * PD + 8 * L.cg]) = gk[i];
+            if (CH) *reinterpret_cast<bf16x8 *>(&sm.Kb[r * PD + 8 * L.cg]) = gkb[i];
         }
+        *reinterpret_cast<bf16x4 *>(&sm.V[L.vr * PV + L.vc]) = rv[par];
+        if (L.tid < C) sm.beta[L.tid] = rb[par];
+    };
+
+    f32x4 accQS[2];
+    accQS[0] = accQS[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const bf16 *Bop = CH ? sm.Kb : sm.K;
+
+    // ---- one pipeline iteration; PAR = parity of the prep chunk j
+    auto iteration = [&](auto par_tag, long long j) {
+        constexpr int PAR = decltype(par_tag)::value;
+        const LI L(opaque(tid0));
+        const int lane = L.lane, w = L.w, l15 = L.l15, l4 = L.l4;
+        const bool hasS = j >= 1;
+        const bool hasP = j < nch;
+        const bool hasG = j + 1 < nch;
+        const bool hasR = j + 2 < nch;
+        const float *gbP = sm.gb[PAR];
+
+        // ================= phase A ========================================
+        if (hasS) {   // U = T X of chunk j-1; wave w: row block w>>1, value block w&1
+            const int I = w >> 1, Jv = w & 1;
+            f32x4 u = {0.f, 0.f, 0.f, 0.f};
+            const bf16x8 t0f = frag_rows(sm.Tm, PC, 16 * I, 0, lane);
+            const bf16x8 x0f = frag_rows(sm.XT, PC, 16 * Jv, 0, lane);
+            if (I >= 2) {   // T is lower triangular: rows < 32 need s < 32 only
+                const bf16x8 t1f = frag_rows(sm.Tm, PC, 16 * I, 32, lane);
+                const bf16x8 x1f = frag_rows(sm.XT, PC, 16 * Jv, 32, lane);
+                u = mfma32(t1f, x1f, u);
+            }
+            u = mfma32(t0f, x0f, u);
+            *reinterpret_cast<bf16x4 *>(&sm.UT[(16 * Jv + l15) * PC + 16 * I + 4 * l4]) = cvt4(u);
+        }
+        if (hasP) store_gate(L, PAR);
         __syncthreads();
 
-        // ================= 2: A -> L^T, X, Qt S0^T ========================
-        const bf16 *Bop = CH ? sm.Kb : sm.K;
-        const int Iw = w >> 1;          // this wave's 16-row block of X, U, O
-        const int Jw = w & 1;           // and its 16-column value block
-        f32x4 accO;
-        {
-            // A jobs: lower blocks (I, J), J <= I, numbered 0..9; wave w takes
-            // job w and, for w < 2, job 8 + w
-            auto jobIJ = [](int tri, int &I, int &J) {
-                I = tri < 1 ? 0 : tri < 3 ? 1 : tri < 6 ? 2 : 3;
-                J = tri - I * (I + 1) / 2;
-            };
-            int I0, J0, I1, J1;
-            jobIJ(w, I0, J0);
-            jobIJ(8 + (w & 1), I1, J1);
-            const bool two = w < 2;
-            f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, x = a0, o = a0;
+        // ================= phase B ========================================
+        if (hasS) {
+            if (w >= 1 && w <= 4) {   // outputs of chunk j-1, row block w-1
+                const int I = w - 1;
+                const int Cc = rows_of(j - 1);
+                const long long tc = t0 + (j - 1) * C;
 #pragma unroll
-            for (int kk = 0; kk < KD; ++kk) {
-                const bf16x8 sop = frag_rows(sm.S, PD, 16 * Jw, 32 * kk, lane);
-                x = mfma32(frag_rows(sm.K, PD, 16 * Iw, 32 * kk, lane), sop, x);
-                o = mfma32(frag_rows(sm.Q, PD, 16 * Iw, 32 * kk, lane), sop, o);
-                a0 = mfma32(frag_rows(sm.K, PD, 16 * I0, 32 * kk, lane),
-                            frag_rows(Bop, PD, 16 * J0, 32 * kk, lane), a0);
-                if (two)
-                    a1 = mfma32(frag_rows(sm.K, PD, 16 * I1, 32 * kk, lane),
-                                frag_rows(Bop, PD, 16 * J1, 32 * kk, lane), a1);
+                for (int jv = 0; jv < 2; ++jv) {
+                    f32x4 o = accQS[jv];
+                    const bf16x8 p0 = frag_rows(sm.P, PC, 16 * I, 0, lane);
+                    const bf16x8 u0 = frag_rows(sm.UT, PC, 16 * jv, 0, lane);
+                    if (I >= 2) {
+                        const bf16x8 p1 = frag_rows(sm.P, PC, 16 * I, 32, lane);
+                        const bf16x8 u1 = frag_rows(sm.UT, PC, 16 * jv, 32, lane);
+                        o = mfma32(p1, u1, o);
+                    }
+                    o = mfma32(p0, u0, o);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = 16 * I + 4 * l4 + e;
+                        if (r < Cc)
+                            og[(size_t)(tc + r) * tokstride + 16 * jv + l15] = (bf16)(a.scale * o[e]);
+                    }
+                }
             }
-            // L^T[s][r] = beta_r * A[r][s] (s < r), zero elsewhere
+            // S^T <- e^{b_C} (.) S^T + Kh^T U  (chunk j-1: parity 1 - PAR)
+#pragma unroll
+            for (int sb = 0; sb < SB; ++sb) {
+                const int Jk = jk_of(L, sb);
+                const int Jv = jv_of(L, sb);
+                const int jc = 16 * Jk + 4 * l4;
+                f32x4 gm;
+                if (CH) gm = *reinterpret_cast<const f32x4 *>(&sm.gam[1 - PAR][jc]);
+                else    gm = f32x4{sm.gam[1 - PAR][0], sm.gam[1 - PAR][0], sm.gam[1 - PAR][0],
+                                   sm.gam[1 - PAR][0]};
+                const bf16x8 k0f = frag_cols(sm.Kh[1 - PAR], PD, 0, 16 * Jk, lane);
+                const bf16x8 k1f = frag_cols(sm.Kh[1 - PAR], PD, 32, 16 * Jk, lane);
+                const bf16x8 u0f = frag_rows(sm.UT, PC, 16 * Jv, 0, lane);
+                const bf16x8 u1f = frag_rows(sm.UT, PC, 16 * Jv, 32, lane);
+                f32x4 s = St[sb] * gm;
+                s = mfma32(k0f, u0f, s);
+                s = mfma32(k1f, u1f, s);
+                St[sb] = s;
+                *reinterpret_cast<bf16x4 *>(&sm.S[(16 * Jv + l15) * PD + jc]) = cvt4(s);
+            }
+        }
+        if (hasP) {
+            // A of chunk j -> L^T[s][r] = beta_r A[r][s] (s < r); GDN: times
+            // e^{b_r - b_s}.  Diagonal blocks go to waves 0, 5, 6, 7, which
+            // also invert them; off-diagonal blocks to waves 1-4.
             auto putL = [&](int I, int J, f32x4 acc) {
                 const int s = 16 * J + l15;
                 const int r0 = 16 * I + 4 * l4;
@@ -372,179 +507,187 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
                 for (int e = 0; e < 4; ++e) {
                     const int r = r0 + e;
                     float dv = 1.f;
-                    if (!CH) dv = ex(fminf(sm.gb[r] - sm.gb[s], 0.f));
+                    if (!CH) dv = ex(fminf(gbP[r] - gbP[s], 0.f));
                     val[e] = s < r ? acc[e] * dv * br[e] : 0.f;
                 }
                 *reinterpret_cast<f32x4 *>(&sm.LT[s * PL + r0]) = val;
             };
-            putL(I0, J0, a0);
-            if (two) putL(I1, J1, a1);
-            // X = V - Kt S0^T  (GDN: Kt S0^T = diag(e^b) k S0^T)
-            const int iv = 16 * Jw + l15;
-            const int r0 = 16 * Iw + 4 * l4;
-            f32x4 xv;
+            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            if (w >= 1 && w <= 4) {
+                // off-diagonal jobs: w1: (1,0),(2,0)  w2: (2,1),(3,0)  w3: (3,1)  w4: (3,2)
+                const int Ia = w == 1 ? 1 : w == 2 ? 2 : 3;
+                const int Ja = w == 1 ? 0 : w == 2 ? 1 : w == 3 ? 1 : 2;
+                const f32x4 aa = gemm_nt<KD>(sm.K, PD, 16 * Ia, Bop, PD, 16 * Ja, lane, z);
+                if (w <= 2) {
+                    const int Ib = w == 1 ? 2 : 3;
+                    const f32x4 ab = gemm_nt<KD>(sm.K, PD, 16 * Ib, Bop, PD, 0, lane, z);
+                    putL(Ib, 0, ab);
+                }
+                putL(Ia, Ja, aa);
+            } else {
+                const int b = w == 0 ? 0 : w - 4;
+                const f32x4 ad = gemm_nt<KD>(sm.K, PD, 16 * b, Bop, PD, 16 * b, lane, z);
+                putL(b, b, ad);
+                __threadfence_block();
+                // (I + L_bb) y = e_cc by right-looking forward substitution in
+                // fp32: lane column cc, all 16 rows in registers
+                const int cc = l15;
+                float y[16], acc[16];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float gr = CH ? 1.f : ex(sm.gb[r0 + e]);
-                xv[e] = (float)sm.V[(r0 + e) * PV + iv] - gr * x[e];
-                o[e] *= gr;
+                for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    y[r] = r == cc ? 1.f : (r > cc ? -acc[r] : 0.f);
+                    const float *lt = &sm.LT[(16 * b + r) * PL + 16 * b];   // column r of L_bb
+#pragma unroll
+                    for (int q4 = (r + 1) / 4; q4 < 4; ++q4) {
+                        const f32x4 col = *reinterpret_cast<const f32x4 *>(lt + 4 * q4);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (4 * q4 + e > r) acc[4 * q4 + e] += col[e] * y[r];
+                    }
+                }
+                if (lane < 16) {
+                    const float bcc = sm.beta[16 * b + cc];
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        sm.Y[(b * 16 + r) * PY + cc] = y[r];
+                        sm.Tm[(16 * b + r) * PC + 16 * b + cc] = (bf16)(y[r] * bcc);
+                    }
+                }
             }
-            *reinterpret_cast<bf16x4 *>(&sm.XT[iv * PC + r0]) = cvt4(xv);
-            accO = o;
         }
+        if (hasG) scan(L, 1 - PAR);
+        if (hasR) load_g(L, j + 2);
         __syncthreads();
 
-        // ================= 3: T (wave 0) || P (waves 1-7) =================
-        if (w == 0) {
-            // diagonal blocks: lane = (block b, column cc); right-looking
-            // forward substitution of (I + L_bb) y = e_cc in fp32
-            const int b = l4;
-            const int cc = l15;
-            float y[16], acc[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                y[r] = r == cc ? 1.f : (r > cc ? -acc[r] : 0.f);
-                // column r of L_bb = row r of L^T_bb
-                const float *lt = &sm.LT[(16 * b + r) * PL + 16 * b];
-#pragma unroll
-                for (int q4 = (r + 1) / 4; q4 < 4; ++q4) {
-                    const f32x4 col = *reinterpret_cast<const f32x4 *>(lt + 4 * q4);
+        // ================= phase C ========================================
+        if (hasP) {
+            if (w == 0) {
+                // off-diagonal blocks of T:  Y_ij = -Y_ii sum_{k=j}^{i-1} L_ik Y_kj
+                // on 16x16x16 MFMAs (A operand: row l15, cols 4*l4..+3;
+                // B operand: rows 4*l4..+3, col l15 == the accumulator layout)
+                auto opL = [&](int bi, int bk) -> bf16x4 {   // rows of L_ik
+                    const float *p = &sm.LT[(16 * bk + 4 * l4) * PL + 16 * bi + l15];
+                    return bf16x4{(bf16)p[0], (bf16)p[PL], (bf16)p[2 * PL], (bf16)p[3 * PL]};
+                };
+                auto opYA = [&](int bi) -> bf16x4 {
+                    return cvt4(*reinterpret_cast<const f32x4 *>(&sm.Y[(bi * 16 + l15) * PY + 4 * l4]));
+                };
+                auto opYB = [&](int bj) -> bf16x4 {
+                    const float *p = &sm.Y[(bj * 16 + 4 * l4) * PY + l15];
+                    return bf16x4{(bf16)p[0], (bf16)p[PY], (bf16)p[2 * PY], (bf16)p[3 * PY]};
+                };
+                const f32x4 z0 = {0.f, 0.f, 0.f, 0.f};
+                const bf16x4 B00 = opYB(0), B11 = opYB(1), B22 = opYB(2);
+                const bf16x4 A11 = opYA(1), A22 = opYA(2), A33 = opYA(3);
+                const bf16x4 L10 = opL(1, 0), L21 = opL(2, 1), L32 = opL(3, 2);
+                const bf16x4 L20 = opL(2, 0), L31 = opL(3, 1), L30 = opL(3, 0);
+                const f32x4 Y10 = -mfma16(A11, cvt4(mfma16(L10, B00, z0)), z0);
+                const f32x4 Y21 = -mfma16(A22, cvt4(mfma16(L21, B11, z0)), z0);
+                const f32x4 Y32 = -mfma16(A33, cvt4(mfma16(L32, B22, z0)), z0);
+                const f32x4 Y20 = -mfma16(A22, cvt4(mfma16(L21, cvt4(Y10), mfma16(L20, B00, z0))), z0);
+                const f32x4 Y31 = -mfma16(A33, cvt4(mfma16(L32, cvt4(Y21), mfma16(L31, B11, z0))), z0);
+                const f32x4 Y30 = -mfma16(
+                    A33, cvt4(mfma16(L32, cvt4(Y20), mfma16(L31, cvt4(Y10), mfma16(L30, B00, z0)))), z0);
+                auto put = [&](int bi, int bj, f32x4 yv) {
+                    const int s = 16 * bj + l15;
+                    const float bs = sm.beta[s];
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        if (4 * q4 + e > r) acc[4 * q4 + e] += col[e] * y[r];
+                        sm.Tm[(16 * bi + 4 * l4 + e) * PC + s] = (bf16)(yv[e] * bs);
+                };
+                put(1, 0, Y10);
+                put(2, 1, Y21);
+                put(3, 2, Y32);
+                put(2, 0, Y20);
+                put(3, 1, Y31);
+                put(3, 0, Y30);
+            } else if (w <= 4) {
+                // Qt S0^T (kept for the outputs) and X = V - Kt S0^T, row block w-1
+                const int I = w - 1;
+                const int r0 = 16 * I + 4 * l4;
+#pragma unroll
+                for (int jv = 0; jv < 2; ++jv) {
+                    bf16x8 sf[KD], kf[KD], qf[KD];
+#pragma unroll
+                    for (int kk = 0; kk < KD; ++kk) {
+                        sf[kk] = frag_rows(sm.S, PD, 16 * jv, 32 * kk, lane);
+                        kf[kk] = frag_rows(sm.K, PD, 16 * I, 32 * kk, lane);
+                        qf[kk] = frag_rows(sm.Q, PD, 16 * I, 32 * kk, lane);
+                    }
+                    f32x4 x = {0.f, 0.f, 0.f, 0.f}, o = x;
+#pragma unroll
+                    for (int kk = 0; kk < KD; ++kk) {
+                        x = mfma32(kf[kk], sf[kk], x);
+                        o = mfma32(qf[kk], sf[kk], o);
+                    }
+                    const int iv = 16 * jv + l15;
+                    f32x4 xv;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float gr = CH ? 1.f : ex(gbP[r0 + e]);
+                        xv[e] = (float)sm.V[(r0 + e) * PV + iv] - gr * x[e];
+                        o[e] *= gr;
+                    }
+                    *reinterpret_cast<bf16x4 *>(&sm.XT[iv * PC + r0]) = cvt4(xv);
+                    accQS[jv] = o;
+                }
+            } else {
+                // P = lower(Qt Kb^T) (GDN: (q k^T) (.) e^{b_r - b_s}); jobs
+                // 0-3 on wave 5, 4-6 on wave 6, 7-9 on wave 7
+                const int first = w == 5 ? 0 : w == 6 ? 4 : 7;
+                const int count = w == 5 ? 4 : 3;
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    if (t >= count) break;
+                    int I, J;
+                    tri_block(first + t, I, J);
+                    const f32x4 pj = gemm_nt<KD>(sm.Q, PD, 16 * I, Bop, PD, 16 * J, lane,
+                                                 f32x4{0.f, 0.f, 0.f, 0.f});
+                    const int s = 16 * J + l15;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = 16 * I + 4 * l4 + e;
+                        float dv = 1.f;
+                        if (!CH) dv = ex(fminf(gbP[r] - gbP[s], 0.f));
+                        sm.P[r * PC + s] = (bf16)(s <= r ? pj[e] * dv : 0.f);
+                    }
                 }
             }
-            const float bcc = sm.beta[16 * b + cc];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                sm.Y[(b * 16 + r) * PY + cc] = y[r];
-                sm.Tm[(16 * b + r) * PC + 16 * b + cc] = (bf16)(y[r] * bcc);
-            }
-            __threadfence_block();
-            // off-diagonal blocks, Y_ij = -Y_ii sum_{k=j}^{i-1} L_ik Y_kj, on
-            // 16x16x16 MFMAs.  A operand: row l15, cols 4*l4..+3; B operand:
-            // rows 4*l4..+3, col l15 (== the accumulator layout).
-            auto opL = [&](int bi, int bk) -> bf16x4 {   // L_ik rows: L^T columns
-                const float *p = &sm.LT[(16 * bk + 4 * l4) * PL + 16 * bi + l15];
-                return bf16x4{(bf16)p[0], (bf16)p[PL], (bf16)p[2 * PL], (bf16)p[3 * PL]};
-            };
-            auto opYA = [&](int bi) -> bf16x4 {
-                return cvt4(*reinterpret_cast<const f32x4 *>(&sm.Y[(bi * 16 + l15) * PY + 4 * l4]));
-            };
-            auto opYB = [&](int bj) -> bf16x4 {
-                const float *p = &sm.Y[(bj * 16 + 4 * l4) * PY + l15];
-                return bf16x4{(bf16)p[0], (bf16)p[PY], (bf16)p[2 * PY], (bf16)p[3 * PY]};
-            };
-            const f32x4 z0 = {0.f, 0.f, 0.f, 0.f};
-            const bf16x4 Y00 = opYB(0), Y11 = opYB(1), Y22 = opYB(2);
-            const bf16x4 A11 = opYA(1), A22 = opYA(2), A33 = opYA(3);
-            const bf16x4 L10 = opL(1, 0), L21 = opL(2, 1), L32 = opL(3, 2);
-            const bf16x4 L20 = opL(2, 0), L31 = opL(3, 1), L30 = opL(3, 0);
-            const f32x4 Y10 = -mfma16(A11, cvt4(mfma16(L10, Y00, z0)), z0);
-            const f32x4 Y21 = -mfma16(A22, cvt4(mfma16(L21, Y11, z0)), z0);
-            const f32x4 Y32 = -mfma16(A33, cvt4(mfma16(L32, Y22, z0)), z0);
-            const f32x4 Y20 = -mfma16(A22, cvt4(mfma16(L21, cvt4(Y10), mfma16(L20, Y00, z0))), z0);
-            const f32x4 Y31 = -mfma16(A33, cvt4(mfma16(L32, cvt4(Y21), mfma16(L31, Y11, z0))), z0);
-            const f32x4 Y30 = -mfma16(
-                A33, cvt4(mfma16(L32, cvt4(Y20), mfma16(L31, cvt4(Y10), mfma16(L30, Y00, z0)))), z0);
-            auto put = [&](int bi, int bj, f32x4 yv) {
-                const int s = 16 * bj + l15;
-                const float bs = sm.beta[s];
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    sm.Tm[(16 * bi + 4 * l4 + e) * PC + s] = (bf16)(yv[e] * bs);
-            };
-            put(1, 0, Y10);
-            put(2, 1, Y21);
-            put(3, 2, Y32);
-            put(2, 0, Y20);
-            put(3, 1, Y31);
-            put(3, 0, Y30);
-        } else {
-            // P jobs 0..9 over waves 1..7: job w-1, and job w+6 for w <= 3
-            auto jobIJ = [](int tri, int &I, int &J) {
-                I = tri < 1 ? 0 : tri < 3 ? 1 : tri < 6 ? 2 : 3;
-                J = tri - I * (I + 1) / 2;
-            };
-            int I0, J0, I1, J1;
-            jobIJ(w - 1, I0, J0);
-            jobIJ(w <= 3 ? w + 6 : 9, I1, J1);
-            const bool two = w <= 3;
-            f32x4 p0 = {0.f, 0.f, 0.f, 0.f}, p1 = p0;
-#pragma unroll
-            for (int kk = 0; kk < KD; ++kk) {
-                p0 = mfma32(frag_rows(sm.Q, PD, 16 * I0, 32 * kk, lane),
-                            frag_rows(Bop, PD, 16 * J0, 32 * kk, lane), p0);
-                if (two)
-                    p1 = mfma32(frag_rows(sm.Q, PD, 16 * I1, 32 * kk, lane),
-                                frag_rows(Bop, PD, 16 * J1, 32 * kk, lane), p1);
-            }
-            auto putP = [&](int I, int J, f32x4 acc) {
-                const int s = 16 * J + l15;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 16 * I + 4 * l4 + e;
-                    float dv = 1.f;
-                    if (!CH) dv = ex(fminf(sm.gb[r] - sm.gb[s], 0.f));
-                    sm.P[r * PC + s] = (bf16)(s <= r ? acc[e] * dv : 0.f);
-                }
-            };
-            putP(I0, J0, p0);
-            if (two) putP(I1, J1, p1);
+        }
+        if (hasG) gate(L, 1 - PAR);
+        if (hasR) load_qkvb(L, j + 2, PAR);
+        __syncthreads();
+    };
+
+    // ---- prologue: chunk 0 gated, chunk 1 loaded
+    {
+        const LI L(tid0);
+        if (nch > 0) {
+            load_g(L, 0);
+            load_qkvb(L, 0, 0);
+            scan(L, 0);
         }
         __syncthreads();
-
-        // ================= 4: U = T X =====================================
-        {
-            f32x4 u = {0.f, 0.f, 0.f, 0.f};
-            u = mfma32(frag_rows(sm.Tm, PC, 16 * Iw, 0, lane),
-                       frag_rows(sm.XT, PC, 16 * Jw, 0, lane), u);
-            if (Iw >= 2)   // T is lower triangular: rows < 32 need s < 32 only
-                u = mfma32(frag_rows(sm.Tm, PC, 16 * Iw, 32, lane),
-                           frag_rows(sm.XT, PC, 16 * Jw, 32, lane), u);
-            *reinterpret_cast<bf16x4 *>(&sm.UT[(16 * Jw + l15) * PC + 16 * Iw + 4 * l4]) = cvt4(u);
-        }
-        __syncthreads();
-
-        // ================= 5: outputs and the next state ==================
-        {
-            f32x4 o = accO;
-            o = mfma32(frag_rows(sm.P, PC, 16 * Iw, 0, lane),
-                       frag_rows(sm.UT, PC, 16 * Jw, 0, lane), o);
-            if (Iw >= 2)
-                o = mfma32(frag_rows(sm.P, PC, 16 * Iw, 32, lane),
-                           frag_rows(sm.UT, PC, 16 * Jw, 32, lane), o);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * Iw + 4 * l4 + e;
-                if (r < Cc) og[(size_t)(tc + r) * tokstride + 16 * Jw + l15] = (bf16)(a.scale * o[e]);
-            }
-        }
-#pragma unroll
-        for (int sb = 0; sb < SB; ++sb) {
-            const int Jk = jk_of(sb);
-            const int Jv = jv_of(sb);
-            const int j = 16 * Jk + 4 * l4;
-            f32x4 gm;
-            if (CH) gm = *reinterpret_cast<const f32x4 *>(&sm.gam[j]);
-            else    gm = f32x4{sm.gam[0], sm.gam[0], sm.gam[0], sm.gam[0]};
-            f32x4 s = St[sb] * gm;
-#pragma unroll
-            for (int kk = 0; kk < C / 32; ++kk)
-                s = mfma32(frag_cols(sm.Kh, PD, 32 * kk, 16 * Jk, lane),
-                           frag_rows(sm.UT, PC, 16 * Jv, 32 * kk, lane), s);
-            St[sb] = s;
-            *reinterpret_cast<bf16x4 *>(&sm.S[(16 * Jv + l15) * PD + j]) = cvt4(s);
+        if (nch > 0) gate(L, 0);
+        if (nch > 1) {
+            load_g(L, 1);
+            load_qkvb(L, 1, 1);
         }
     }
 
+    for (long long j = 0; j <= nch; j += 2) {
+        iteration(std::integral_constant<int, 0>{}, j);
+        if (j + 1 <= nch) iteration(std::integral_constant<int, 1>{}, j + 1);
+    }
+
     if (a.ht) {
+        const LI L(tid0);
 #pragma unroll
         for (int sb = 0; sb < SB; ++sb) {
-            const int j = 16 * jk_of(sb) + 4 * l4;
-            const int iv = 16 * jv_of(sb) + l15;
+            const int j = 16 * jk_of(L, sb) + 4 * L.l4;
+            const int iv = 16 * jv_of(L, sb) + L.l15;
             *reinterpret_cast<f32x4 *>(a.ht + sslot + (size_t)(i0 + iv) * D + j) = St[sb];
         }
     }

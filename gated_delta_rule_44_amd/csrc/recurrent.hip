@@ -9,16 +9,21 @@
 // key channel; Gated DeltaNet: one scalar a per head -- "Super Apriel: One
 // Checkpoint, Many Speeds", gist.science summary, section 2a).
 //
-// Layout.  A 256-thread workgroup (4 waves) owns one Dv x Dk fp32 state.  A
-// state row is D floats = D/4 lanes of float4, so each wave covers 64/(D/4)
-// rows per load and every load instruction of the workgroup reads one
-// contiguous block of rows: the state streams from HBM with dwordx4
-// accesses, once in and once out.  Thread (wave w, lane l) holds rows
+// Layout.  A state row is D floats = D/4 lanes of float4, so a 64-lane wave
+// covers 64/(D/4) rows per load and every load instruction of a 256-thread
+// workgroup reads one contiguous block of rows: the state streams from HBM
+// with dwordx4 accesses, once in and once out.  The decode spreads one state
+// over several workgroups (rows are independent); the recurrent prefill keeps
+// a whole state in one workgroup, thread (wave w, lane l) holding rows
 //     row(m) = m * RPI + w * RPW + l / LPR,   m < M
-// at columns 4 * (l % LPR) .. +3.  The two row dot products S'k and S'q are
-// reduced together by a recursive-halving exchange (reduce-scatter) across
-// the LPR lanes of a row, which leaves one finished dot product per lane.
+// at columns 4 * (l % LPR) .. +3, and reduces its 2M row dot products (S'k
+// and S'q) by a recursive-halving exchange across the LPR lanes of a row,
+// which leaves one finished dot product per lane.
 #include "gdr_internal.h"
+
+#ifndef GDR_DECODE_PASSES
+#define GDR_DECODE_PASSES 2   // 16 rows (8 KiB of state) per workgroup at D = 128
+#endif
 
 namespace gdr {
 namespace {
@@ -127,37 +132,83 @@ __device__ inline const float *state_row(const float *st, int m, int lane, int w
 }
 
 // ---------------------------------------------------------------------------
-// Decode: one workgroup per (recurrent layer, b, h).
-template <typename T, int D>
-__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a, DecodeLayers L) {
+// Decode, row-split: the rows of one state are independent (each row's dot
+// products need only that row and the head's shared q, k and gate), so a
+// head is spread over D / ROWS workgroups of ROWS rows each.  Small
+// per-workgroup footprints keep many independent read-then-write streams in
+// flight, which measures markedly faster than one 64 KiB state per
+// workgroup.  Thread (wave w, lane l) holds row
+//     rowblock * ROWS + p * RPP + w * RPW + l / LPR,  p < PASSES,
+// columns 4 * (l % LPR) .. +3.
+template <typename T, int D, int PASSES>
+__global__ __launch_bounds__(256) void decode_rows_kernel(DecodeArgs a, DecodeLayers L) {
     using G = Geom<D>;
+    constexpr int RPP = G::RPI;              // rows per pass of the workgroup
+    constexpr int ROWS = RPP * PASSES;
+    constexpr int NRB = D / ROWS;            // workgroups per head
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
     const int bh_count = a.B * a.H;
-    const int rec = blockIdx.x / bh_count;
-    const int bh = blockIdx.x - rec * bh_count;
+    const int rb = blockIdx.x % NRB;
+    const int slot_lin = blockIdx.x / NRB;
+    const int rec = slot_lin / bh_count;
+    const int bh = slot_lin - rec * bh_count;
     const int code = L.code[rec];
     const int layer = code >> 1;
     const bool channel = (code & 1) != 0;
     const size_t slot = (size_t)layer * bh_count + bh;
+    const int c0 = (lane % G::LPR) * 4;
+    const int sub = lane / G::LPR;
 
     float *st = a.state + slot * D * D;
-    f32x4 S[G::M];
+    f32x4 S[PASSES];
 #pragma unroll
-    for (int m = 0; m < G::M; ++m)
-        S[m] = __builtin_nontemporal_load(
-            reinterpret_cast<const f32x4 *>(state_row<D>(st, m, lane, w)));
-
-    head_step<T, D>(S, static_cast<const T *>(a.q) + slot * D,
-                    static_cast<const T *>(a.k) + slot * D,
-                    static_cast<const T *>(a.v) + slot * D,
-                    a.g + layer * a.g_layer + (long long)bh * a.g_bh, channel,
-                    a.beta[slot], a.scale, static_cast<T *>(a.o) + slot * D, lane, w);
-
+    for (int p = 0; p < PASSES; ++p) {
+        const int row = rb * ROWS + p * RPP + w * G::RPW + sub;
+        S[p] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(st + (size_t)row * D + c0));
+    }
+    const T *qp = static_cast<const T *>(a.q) + slot * D;
+    const T *kp = static_cast<const T *>(a.k) + slot * D;
+    const T *vp = static_cast<const T *>(a.v) + slot * D;
+    T *op = static_cast<T *>(a.o) + slot * D;
+    const float *gp = a.g + layer * a.g_layer + (long long)bh * a.g_bh;
+    const float beta = a.beta[slot];
+    const f32x4 kv = Elem<T>::load4(kp + c0);
+    const f32x4 qv = Elem<T>::load4(qp + c0);
+    f32x4 lg;
+    if (channel) {
+        lg = *reinterpret_cast<const f32x4 *>(gp + c0);
+    } else {
+        const float s = gp[0];
+        lg = f32x4{s, s, s, s};
+    }
+    constexpr float kLog2e = 1.4426950408889634f;
+    const f32x4 av = f32x4{__builtin_amdgcn_exp2f(lg.x * kLog2e), __builtin_amdgcn_exp2f(lg.y * kLog2e),
+                           __builtin_amdgcn_exp2f(lg.z * kLog2e), __builtin_amdgcn_exp2f(lg.w * kLog2e)};
+    const f32x4 ak = av * kv;
+    const f32x4 aq = av * qv;
+    float kq = dot4(kv, qv);
 #pragma unroll
-    for (int m = 0; m < G::M; ++m)
-        __builtin_nontemporal_store(
-            S[m], reinterpret_cast<f32x4 *>(const_cast<float *>(state_row<D>(st, m, lane, w))));
+    for (int mask = G::LPR / 2; mask >= 1; mask >>= 1) kq += __shfl_xor(kq, mask);
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+        const int row = rb * ROWS + p * RPP + w * G::RPW + sub;
+        // (S'k)_row and (S'q)_row: one halving step, then an all-reduce
+        const float yk = dot4(S[p], ak);
+        const float yq = dot4(S[p], aq);
+        const bool upper = (lane & (G::LPR / 2)) != 0;
+        float val = (upper ? yq : yk) + __shfl_xor(upper ? yk : yq, G::LPR / 2);
+#pragma unroll
+        for (int mask = G::LPR / 4; mask >= 1; mask >>= 1) val += __shfl_xor(val, mask);
+        // lanes in the lower half of the row now hold S'k, the upper half S'q
+        const float vrow = Elem<T>::load(vp + row);
+        const float u_lo = beta * (vrow - val);
+        const float u = __shfl_xor(u_lo, G::LPR / 2);
+        const float um = upper ? u : u_lo;       // every lane: u for its row
+        if (upper && (lane % (G::LPR / 2)) == 0) Elem<T>::store(op + row, a.scale * (val + um * kq));
+        S[p] = S[p] * av + um * kv;
+        __builtin_nontemporal_store(S[p], reinterpret_cast<f32x4 *>(st + (size_t)row * D + c0));
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -210,15 +261,20 @@ __global__ __launch_bounds__(256) void prefill_recurrent_kernel(PrefillArgs a) {
 
 hipError_t launch_decode(bool bf16_io, int D, const DecodeArgs &a,
                          const DecodeLayers &layers, hipStream_t s) {
-    const long long blocks = (long long)layers.n * a.B * a.H;
-    if (blocks <= 0) return hipSuccess;
+    const long long heads = (long long)layers.n * a.B * a.H;
+    if (heads <= 0) return hipSuccess;
+    // rows per workgroup: PASSES x (rows one workgroup-wide load covers)
+    constexpr int P128 = GDR_DECODE_PASSES, P64 = GDR_DECODE_PASSES;
+    const long long per_head = D == 128 ? 128 / (Geom<128>::RPI * P128) : 64 / (Geom<64>::RPI * P64);
+    const long long blocks = heads * per_head;
+    if (blocks >= (1LL << 31)) return hipErrorInvalidValue;
     dim3 grid((unsigned)blocks), block(256);
     if (bf16_io) {
-        if (D == 128) hipLaunchKernelGGL((decode_kernel<bf16, 128>), grid, block, 0, s, a, layers);
-        else          hipLaunchKernelGGL((decode_kernel<bf16, 64>), grid, block, 0, s, a, layers);
+        if (D == 128) hipLaunchKernelGGL((decode_rows_kernel<bf16, 128, P128>), grid, block, 0, s, a, layers);
+        else          hipLaunchKernelGGL((decode_rows_kernel<bf16, 64, P64>), grid, block, 0, s, a, layers);
     } else {
-        if (D == 128) hipLaunchKernelGGL((decode_kernel<float, 128>), grid, block, 0, s, a, layers);
-        else          hipLaunchKernelGGL((decode_kernel<float, 64>), grid, block, 0, s, a, layers);
+        if (D == 128) hipLaunchKernelGGL((decode_rows_kernel<float, 128, P128>), grid, block, 0, s, a, layers);
+        else          hipLaunchKernelGGL((decode_rows_kernel<float, 64, P64>), grid, block, 0, s, a, layers);
     }
     return hipGetLastError();
 }
