@@ -134,15 +134,17 @@ template <int D, bool CH> struct Smem {
     alignas(16) bf16 Kb[CH ? C * PD : 8];   // k (.) e^-b (KDA), [r][j]
     alignas(16) bf16 Kh[2][C * PD];    // k (.) e^{b_C - b}, [s][j], by chunk parity
     alignas(16) bf16 S[BV * PD];       // bf16 copy of the state slice, [i][j]
-    alignas(16) bf16 Tm[C * PC];       // T, [r][s]
-    alignas(16) bf16 P[C * PC];        // P, [r][s]
+    alignas(16) bf16 TT[C * PC];       // T^T, [s][r] (read back by transpose loads)
+    alignas(16) bf16 PT[C * PC];       // P^T, [s][r]
     alignas(16) bf16 XT[BV * PC];      // X^T, [i][s]
     alignas(16) bf16 UT[BV * PC];      // U^T, [i][s]
     alignas(16) bf16 V[C * PV];        // v tile, [r][i]
     alignas(16) float LT[C * PL];      // L^T = (diag(beta) A)^T, [s][r]
     alignas(16) float Y[4 * 16 * PY];  // inverted diagonal blocks, [b][r][c]
     alignas(16) float beta[C];
-    alignas(16) float gb[2][C];        // GDN: cumulative log gate, by chunk parity
+    alignas(16) float gb[2][C];        // GDN: cumulative log gate b_r, by chunk parity
+    alignas(16) float e1[2][C];        // GDN: e^{b_r}
+    alignas(16) float e2[2][C];        // GDN: e^{-b_r}
     alignas(16) float gam[2][D];       // e^{b_C} per channel (GDN: [0]), by parity
     alignas(16) float tot[CH ? NW * D : 4];   // KDA: per-wave sums of g
 };
@@ -189,7 +191,7 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
     constexpr int RPW = 64 / CG;       // row groups per wave
     constexpr int RPT = C / (NW * RPW);// rows per thread in the gate phase
     constexpr int KD = D / 32;         // x32 steps over a D-long contraction
-    constexpr int SB = D / 64;         // S^T blocks per wave
+    constexpr int SBK = D / 64;        // 16-row blocks of S^T per state wave
     static_assert(RPT >= 1, "gate phase layout");
     __shared__ Sm sm;
 
@@ -225,27 +227,33 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
     };
     const int tid0 = threadIdx.x;
 
-    // T and P keep zero upper triangles: only lower blocks are ever written
+    // T and P are lower triangular: the entries above the diagonal of T^T and
+    // P^T stay zero, only lower blocks are ever written
     for (int e = tid0; e < C * PC; e += NT) {
-        sm.Tm[e] = (bf16)0.f;
-        sm.P[e] = (bf16)0.f;
+        sm.TT[e] = (bf16)0.f;
+        sm.PT[e] = (bf16)0.f;
     }
 
-    // ---- state S^T blocks in registers: wave w, block sb holds S^T[j][iv]
-    //      for j = 16*Jk + 4*l4 + e, iv = 16*Jv + l15
-    auto jk_of = [](const LI &L, int sb) { return SB == 2 ? L.w : (L.w >> 1); };
-    auto jv_of = [](const LI &L, int sb) { return SB == 2 ? sb : (L.w & 1); };
-    f32x4 St[SB];
+    // ---- state S^T in registers of waves 4..7: wave w holds blocks
+    //      (Jk, Jv) for Jk = SBK*(w-4) + kb, Jv = 0, 1, i.e. S^T[j][iv] with
+    //      j = 16*Jk + 4*l4 + e, iv = 16*Jv + l15
+    f32x4 St[SBK][2];
     {
         const LI L(tid0);
 #pragma unroll
-        for (int sb = 0; sb < SB; ++sb) {
-            const int j = 16 * jk_of(L, sb) + 4 * L.l4;
-            const int iv = 16 * jv_of(L, sb) + L.l15;
-            f32x4 s = {0.f, 0.f, 0.f, 0.f};
-            if (a.h0) s = *reinterpret_cast<const f32x4 *>(a.h0 + sslot + (size_t)(i0 + iv) * D + j);
-            St[sb] = s;
-            *reinterpret_cast<bf16x4 *>(&sm.S[iv * PD + j]) = cvt4(s);
+        for (int kb = 0; kb < SBK; ++kb) {
+#pragma unroll
+            for (int jv = 0; jv < 2; ++jv) {
+                f32x4 sv = {0.f, 0.f, 0.f, 0.f};
+                if (L.w >= 4) {
+                    const int j = 16 * (SBK * (L.w - 4) + kb) + 4 * L.l4;
+                    const int iv = 16 * jv + L.l15;
+                    if (a.h0)
+                        sv = *reinterpret_cast<const f32x4 *>(a.h0 + sslot + (size_t)(i0 + iv) * D + j);
+                    *reinterpret_cast<bf16x4 *>(&sm.S[iv * PD + j]) = cvt4(sv);
+                }
+                St[kb][jv] = sv;
+            }
         }
     }
 
@@ -339,6 +347,8 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
                 if (L.lane >= off) gv += y;
             }
             sm.gb[par][L.lane] = gv;
+            sm.e1[par][L.lane] = ex(gv);
+            sm.e2[par][L.lane] = ex(-gv);
         }
     };
 
@@ -429,16 +439,15 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
         const bool hasP = j < nch;
         const bool hasG = j + 1 < nch;
         const bool hasR = j + 2 < nch;
-        const float *gbP = sm.gb[PAR];
 
         // ================= phase A ========================================
         if (hasS) {   // U = T X of chunk j-1; wave w: row block w>>1, value block w&1
             const int I = w >> 1, Jv = w & 1;
             f32x4 u = {0.f, 0.f, 0.f, 0.f};
-            const bf16x8 t0f = frag_rows(sm.Tm, PC, 16 * I, 0, lane);
+            const bf16x8 t0f = frag_cols(sm.TT, PC, 0, 16 * I, lane);
             const bf16x8 x0f = frag_rows(sm.XT, PC, 16 * Jv, 0, lane);
             if (I >= 2) {   // T is lower triangular: rows < 32 need s < 32 only
-                const bf16x8 t1f = frag_rows(sm.Tm, PC, 16 * I, 32, lane);
+                const bf16x8 t1f = frag_cols(sm.TT, PC, 32, 16 * I, lane);
                 const bf16x8 x1f = frag_rows(sm.XT, PC, 16 * Jv, 32, lane);
                 u = mfma32(t1f, x1f, u);
             }
@@ -449,88 +458,64 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
         __syncthreads();
 
         // ================= phase B ========================================
-        if (hasS) {
-            if (w >= 1 && w <= 4) {   // outputs of chunk j-1, row block w-1
-                const int I = w - 1;
-                const int Cc = rows_of(j - 1);
-                const long long tc = t0 + (j - 1) * C;
+        if (w < 4) {
+            if (hasP) {
+                // A and P of chunk j by 16-row blocks (I, J <= I); each wave
+                // loads its Kt/Qt rows once and shares each Kb load between A
+                // and P:  w0: (0,0),(3,0)  w1: (1,0),(1,1)  w2: (2,0..2)
+                // w3: (3,1..3).  Diagonal blocks are inverted by their wave.
+                const float *e1 = sm.e1[PAR];
+                const float *e2 = sm.e2[PAR];
+                auto frags = [&](const bf16 *M, int blk, bf16x8 (&f)[KD]) {
 #pragma unroll
-                for (int jv = 0; jv < 2; ++jv) {
-                    f32x4 o = accQS[jv];
-                    const bf16x8 p0 = frag_rows(sm.P, PC, 16 * I, 0, lane);
-                    const bf16x8 u0 = frag_rows(sm.UT, PC, 16 * jv, 0, lane);
-                    if (I >= 2) {
-                        const bf16x8 p1 = frag_rows(sm.P, PC, 16 * I, 32, lane);
-                        const bf16x8 u1 = frag_rows(sm.UT, PC, 16 * jv, 32, lane);
-                        o = mfma32(p1, u1, o);
-                    }
-                    o = mfma32(p0, u0, o);
+                    for (int kk = 0; kk < KD; ++kk) f[kk] = frag_rows(M, PD, 16 * blk, 32 * kk, lane);
+                };
+                // L^T[s][r] = beta_r A[r][s] (s < r) and P^T[s][r] = P[r][s]
+                // (s <= r); GDN scales both by e^{b_r} e^{-b_s}
+                auto put = [&](int I, int J, f32x4 av, f32x4 pv) {
+                    const int s = 16 * J + l15;
+                    const int r0 = 16 * I + 4 * l4;
+                    const f32x4 br = *reinterpret_cast<const f32x4 *>(&sm.beta[r0]);
+                    f32x4 dv = {1.f, 1.f, 1.f, 1.f};
+                    if (!CH) dv = *reinterpret_cast<const f32x4 *>(&e1[r0]) * e2[s];
+                    f32x4 lv, pm;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const int r = 16 * I + 4 * l4 + e;
-                        if (r < Cc)
-                            og[(size_t)(tc + r) * tokstride + 16 * jv + l15] = (bf16)(a.scale * o[e]);
+                        lv[e] = s < r0 + e ? av[e] * dv[e] * br[e] : 0.f;
+                        pm[e] = s <= r0 + e ? pv[e] * dv[e] : 0.f;
                     }
-                }
-            }
-            // S^T <- e^{b_C} (.) S^T + Kh^T U  (chunk j-1: parity 1 - PAR)
+                    *reinterpret_cast<f32x4 *>(&sm.LT[s * PL + r0]) = lv;
+                    *reinterpret_cast<bf16x4 *>(&sm.PT[s * PC + r0]) = cvt4(pm);
+                };
+                auto tile = [&](const bf16x8 (&kf)[KD], const bf16x8 (&qf)[KD], int I, int J) {
+                    bf16x8 bf[KD];
+                    frags(Bop, J, bf);
+                    f32x4 av = {0.f, 0.f, 0.f, 0.f}, pv = av;
 #pragma unroll
-            for (int sb = 0; sb < SB; ++sb) {
-                const int Jk = jk_of(L, sb);
-                const int Jv = jv_of(L, sb);
-                const int jc = 16 * Jk + 4 * l4;
-                f32x4 gm;
-                if (CH) gm = *reinterpret_cast<const f32x4 *>(&sm.gam[1 - PAR][jc]);
-                else    gm = f32x4{sm.gam[1 - PAR][0], sm.gam[1 - PAR][0], sm.gam[1 - PAR][0],
-                                   sm.gam[1 - PAR][0]};
-                const bf16x8 k0f = frag_cols(sm.Kh[1 - PAR], PD, 0, 16 * Jk, lane);
-                const bf16x8 k1f = frag_cols(sm.Kh[1 - PAR], PD, 32, 16 * Jk, lane);
-                const bf16x8 u0f = frag_rows(sm.UT, PC, 16 * Jv, 0, lane);
-                const bf16x8 u1f = frag_rows(sm.UT, PC, 16 * Jv, 32, lane);
-                f32x4 s = St[sb] * gm;
-                s = mfma32(k0f, u0f, s);
-                s = mfma32(k1f, u1f, s);
-                St[sb] = s;
-                *reinterpret_cast<bf16x4 *>(&sm.S[(16 * Jv + l15) * PD + jc]) = cvt4(s);
-            }
-        }
-        if (hasP) {
-            // A of chunk j -> L^T[s][r] = beta_r A[r][s] (s < r); GDN: times
-            // e^{b_r - b_s}.  Diagonal blocks go to waves 0, 5, 6, 7, which
-            // also invert them; off-diagonal blocks to waves 1-4.
-            auto putL = [&](int I, int J, f32x4 acc) {
-                const int s = 16 * J + l15;
-                const int r0 = 16 * I + 4 * l4;
-                const f32x4 br = *reinterpret_cast<const f32x4 *>(&sm.beta[r0]);
-                f32x4 val;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = r0 + e;
-                    float dv = 1.f;
-                    if (!CH) dv = ex(fminf(gbP[r] - gbP[s], 0.f));
-                    val[e] = s < r ? acc[e] * dv * br[e] : 0.f;
+                    for (int kk = 0; kk < KD; ++kk) {
+                        av = mfma32(kf[kk], bf[kk], av);
+                        pv = mfma32(qf[kk], bf[kk], pv);
+                    }
+                    put(I, J, av, pv);
+                };
+                const int Id = w;   // the diagonal block of this wave
+                {
+                    bf16x8 kf[KD], qf[KD];
+                    frags(sm.K, Id, kf);
+                    frags(sm.Q, Id, qf);
+                    const int J0 = w == 3 ? 1 : 0;
+                    for (int J = J0; J <= Id; ++J) tile(kf, qf, Id, J);
                 }
-                *reinterpret_cast<f32x4 *>(&sm.LT[s * PL + r0]) = val;
-            };
-            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-            if (w >= 1 && w <= 4) {
-                // off-diagonal jobs: w1: (1,0),(2,0)  w2: (2,1),(3,0)  w3: (3,1)  w4: (3,2)
-                const int Ia = w == 1 ? 1 : w == 2 ? 2 : 3;
-                const int Ja = w == 1 ? 0 : w == 2 ? 1 : w == 3 ? 1 : 2;
-                const f32x4 aa = gemm_nt<KD>(sm.K, PD, 16 * Ia, Bop, PD, 16 * Ja, lane, z);
-                if (w <= 2) {
-                    const int Ib = w == 1 ? 2 : 3;
-                    const f32x4 ab = gemm_nt<KD>(sm.K, PD, 16 * Ib, Bop, PD, 0, lane, z);
-                    putL(Ib, 0, ab);
+                if (w == 0) {
+                    bf16x8 kf[KD], qf[KD];
+                    frags(sm.K, 3, kf);
+                    frags(sm.Q, 3, qf);
+                    tile(kf, qf, 3, 0);
                 }
-                putL(Ia, Ja, aa);
-            } else {
-                const int b = w == 0 ? 0 : w - 4;
-                const f32x4 ad = gemm_nt<KD>(sm.K, PD, 16 * b, Bop, PD, 16 * b, lane, z);
-                putL(b, b, ad);
                 __threadfence_block();
                 // (I + L_bb) y = e_cc by right-looking forward substitution in
                 // fp32: lane column cc, all 16 rows in registers
+                const int b = Id;
                 const int cc = l15;
                 float y[16], acc[16];
 #pragma unroll
@@ -549,11 +534,60 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
                 }
                 if (lane < 16) {
                     const float bcc = sm.beta[16 * b + cc];
+                    float tv[16];
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         sm.Y[(b * 16 + r) * PY + cc] = y[r];
-                        sm.Tm[(16 * b + r) * PC + 16 * b + cc] = (bf16)(y[r] * bcc);
+                        tv[r] = y[r] * bcc;
                     }
+                    // T[16b + r][16b + cc] -> T^T row 16b + cc, columns 16b..16b+15
+                    *reinterpret_cast<bf16x8 *>(&sm.TT[(16 * b + cc) * PC + 16 * b]) = cvt8(tv);
+                    *reinterpret_cast<bf16x8 *>(&sm.TT[(16 * b + cc) * PC + 16 * b + 8]) = cvt8(tv + 8);
+                }
+            }
+        } else if (hasS) {
+            // outputs and state update of chunk j-1 (row block / key blocks of
+            // this wave)
+            const int I = w - 4;
+            const int Cc = rows_of(j - 1);
+            const long long tc = t0 + (j - 1) * C;
+            const bf16x8 p0 = frag_cols(sm.PT, PC, 0, 16 * I, lane);
+            const bf16x8 p1 = frag_cols(sm.PT, PC, 32, 16 * I, lane);
+            bf16x8 uf[2][2];
+#pragma unroll
+            for (int jv = 0; jv < 2; ++jv) {
+                uf[jv][0] = frag_rows(sm.UT, PC, 16 * jv, 0, lane);
+                uf[jv][1] = frag_rows(sm.UT, PC, 16 * jv, 32, lane);
+            }
+#pragma unroll
+            for (int jv = 0; jv < 2; ++jv) {
+                f32x4 o = mfma32(p0, uf[jv][0], accQS[jv]);
+                if (I >= 2) o = mfma32(p1, uf[jv][1], o);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 16 * I + 4 * l4 + e;
+                    if (r < Cc)
+                        og[(size_t)(tc + r) * tokstride + 16 * jv + l15] = (bf16)(a.scale * o[e]);
+                }
+            }
+            // S^T <- e^{b_C} (.) S^T + Kh^T U  (chunk j-1: parity 1 - PAR)
+#pragma unroll
+            for (int kb = 0; kb < SBK; ++kb) {
+                const int Jk = SBK * I + kb;
+                const int jc = 16 * Jk + 4 * l4;
+                f32x4 gm;
+                if (CH) gm = *reinterpret_cast<const f32x4 *>(&sm.gam[1 - PAR][jc]);
+                else    gm = f32x4{sm.gam[1 - PAR][0], sm.gam[1 - PAR][0], sm.gam[1 - PAR][0],
+                                   sm.gam[1 - PAR][0]};
+                const bf16x8 k0f = frag_cols(sm.Kh[1 - PAR], PD, 0, 16 * Jk, lane);
+                const bf16x8 k1f = frag_cols(sm.Kh[1 - PAR], PD, 32, 16 * Jk, lane);
+#pragma unroll
+                for (int jv = 0; jv < 2; ++jv) {
+                    f32x4 sv = St[kb][jv] * gm;
+                    sv = mfma32(k0f, uf[jv][0], sv);
+                    sv = mfma32(k1f, uf[jv][1], sv);
+                    St[kb][jv] = sv;
+                    *reinterpret_cast<bf16x4 *>(&sm.S[(16 * jv + l15) * PD + jc]) = cvt4(sv);
                 }
             }
         }
@@ -590,32 +624,34 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
                 const f32x4 Y31 = -mfma16(A33, cvt4(mfma16(L32, cvt4(Y21), mfma16(L31, B11, z0))), z0);
                 const f32x4 Y30 = -mfma16(
                     A33, cvt4(mfma16(L32, cvt4(Y20), mfma16(L31, cvt4(Y10), mfma16(L30, B00, z0)))), z0);
-                auto put = [&](int bi, int bj, f32x4 yv) {
+                // T_ij = Y_ij diag(beta_j) -> T^T[s][r..r+3]
+                auto putT = [&](int bi, int bj, f32x4 yv) {
                     const int s = 16 * bj + l15;
-                    const float bs = sm.beta[s];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        sm.Tm[(16 * bi + 4 * l4 + e) * PC + s] = (bf16)(yv[e] * bs);
+                    *reinterpret_cast<bf16x4 *>(&sm.TT[s * PC + 16 * bi + 4 * l4]) = cvt4(yv * sm.beta[s]);
                 };
-                put(1, 0, Y10);
-                put(2, 1, Y21);
-                put(3, 2, Y32);
-                put(2, 0, Y20);
-                put(3, 1, Y31);
-                put(3, 0, Y30);
-            } else if (w <= 4) {
-                // Qt S0^T (kept for the outputs) and X = V - Kt S0^T, row block w-1
-                const int I = w - 1;
+                putT(1, 0, Y10);
+                putT(2, 1, Y21);
+                putT(3, 2, Y32);
+                putT(2, 0, Y20);
+                putT(3, 1, Y31);
+                putT(3, 0, Y30);
+            } else if (w >= 4) {
+                // Qt S0^T (kept for the outputs) and X = V - Kt S0^T, row block w-4
+                const int I = w - 4;
                 const int r0 = 16 * I + 4 * l4;
+                bf16x8 kf[KD], qf[KD];
+#pragma unroll
+                for (int kk = 0; kk < KD; ++kk) {
+                    kf[kk] = frag_rows(sm.K, PD, 16 * I, 32 * kk, lane);
+                    qf[kk] = frag_rows(sm.Q, PD, 16 * I, 32 * kk, lane);
+                }
+                f32x4 gr = {1.f, 1.f, 1.f, 1.f};
+                if (!CH) gr = *reinterpret_cast<const f32x4 *>(&sm.e1[PAR][r0]);
 #pragma unroll
                 for (int jv = 0; jv < 2; ++jv) {
-                    bf16x8 sf[KD], kf[KD], qf[KD];
+                    bf16x8 sf[KD];
 #pragma unroll
-                    for (int kk = 0; kk < KD; ++kk) {
-                        sf[kk] = frag_rows(sm.S, PD, 16 * jv, 32 * kk, lane);
-                        kf[kk] = frag_rows(sm.K, PD, 16 * I, 32 * kk, lane);
-                        qf[kk] = frag_rows(sm.Q, PD, 16 * I, 32 * kk, lane);
-                    }
+                    for (int kk = 0; kk < KD; ++kk) sf[kk] = frag_rows(sm.S, PD, 16 * jv, 32 * kk, lane);
                     f32x4 x = {0.f, 0.f, 0.f, 0.f}, o = x;
 #pragma unroll
                     for (int kk = 0; kk < KD; ++kk) {
@@ -625,34 +661,10 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
                     const int iv = 16 * jv + l15;
                     f32x4 xv;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float gr = CH ? 1.f : ex(gbP[r0 + e]);
-                        xv[e] = (float)sm.V[(r0 + e) * PV + iv] - gr * x[e];
-                        o[e] *= gr;
-                    }
+                    for (int e = 0; e < 4; ++e)
+                        xv[e] = (float)sm.V[(r0 + e) * PV + iv] - gr[e] * x[e];
                     *reinterpret_cast<bf16x4 *>(&sm.XT[iv * PC + r0]) = cvt4(xv);
-                    accQS[jv] = o;
-                }
-            } else {
-                // P = lower(Qt Kb^T) (GDN: (q k^T) (.) e^{b_r - b_s}); jobs
-                // 0-3 on wave 5, 4-6 on wave 6, 7-9 on wave 7
-                const int first = w == 5 ? 0 : w == 6 ? 4 : 7;
-                const int count = w == 5 ? 4 : 3;
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    if (t >= count) break;
-                    int I, J;
-                    tri_block(first + t, I, J);
-                    const f32x4 pj = gemm_nt<KD>(sm.Q, PD, 16 * I, Bop, PD, 16 * J, lane,
-                                                 f32x4{0.f, 0.f, 0.f, 0.f});
-                    const int s = 16 * J + l15;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int r = 16 * I + 4 * l4 + e;
-                        float dv = 1.f;
-                        if (!CH) dv = ex(fminf(gbP[r] - gbP[s], 0.f));
-                        sm.P[r * PC + s] = (bf16)(s <= r ? pj[e] * dv : 0.f);
-                    }
+                    accQS[jv] = o * gr;
                 }
             }
         }
@@ -684,11 +696,16 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
 
     if (a.ht) {
         const LI L(tid0);
+        if (L.w >= 4) {
 #pragma unroll
-        for (int sb = 0; sb < SB; ++sb) {
-            const int j = 16 * jk_of(L, sb) + 4 * L.l4;
-            const int iv = 16 * jv_of(L, sb) + L.l15;
-            *reinterpret_cast<f32x4 *>(a.ht + sslot + (size_t)(i0 + iv) * D + j) = St[sb];
+            for (int kb = 0; kb < SBK; ++kb) {
+#pragma unroll
+                for (int jv = 0; jv < 2; ++jv) {
+                    const int j = 16 * (SBK * (L.w - 4) + kb) + 4 * L.l4;
+                    const int iv = 16 * jv + L.l15;
+                    *reinterpret_cast<f32x4 *>(a.ht + sslot + (size_t)(i0 + iv) * D + j) = St[kb][jv];
+                }
+            }
         }
     }
 }
