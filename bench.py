@@ -22,6 +22,7 @@ The same line carries:
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
                        [--only-headline] [--no-cpu-baseline]
+                       [--only {kda_prefill,decode,varlen}]   (one workload, for profiling)
 """
 import argparse
 import json
@@ -37,9 +38,24 @@ METRIC = "GDN/KDA prefill tokens/s + decode state-update GB/s (% of HBM peak), 1
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_TFLOPS = 2500.0
 D, C = 128, 64
-# counter summaries measured with rocprofv3 on this kernel build (see
-# profiles/); bytes per launch, or None when not measured for this build
-MEASURED_TRAFFIC = None
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "chunked_prefill_gdn_B4_H16_T4096_traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "gated_delta_rule_44_amd", "csrc", "chunked.hip")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the headline prefill kernel from rocprofv3
+    FETCH_SIZE / WRITE_SIZE counters (scaled by the factors a plain copy of
+    known size gives), or None when they were taken on another version of
+    the kernel source."""
+    import hashlib
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+        src = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != src:
+        return None
+    return rec["bytes_per_launch"]
 
 
 def prefill_bytes(tokens_heads, units, gate):
@@ -139,9 +155,10 @@ def bench_decode(gdr, synthetic, torch, dev, steps, warmup):
 
 
 def cpu_baseline(synthetic, torch, target_s=12.0):
-    """fp64 oracle on the host: every (sequence, head) of the GDN prefill
-    workload, truncated to its first T_s tokens (T_s sized for ~target_s of
-    CPU time from a short calibration run)."""
+    """fp64 oracle on the host cores over the GDN prefill workload (all 64
+    sequence-heads, 4096 tokens each), repeated until about target_s seconds
+    of wall time have accumulated (or truncated to fewer tokens per sequence
+    if one pass would take much longer)."""
     import oracle
     B, T, H = 4, 4096, 16
     x = synthetic.prefill_inputs(B, T, H, D, torch.bfloat16, "scalar", seed=1001,
@@ -154,15 +171,19 @@ def cpu_baseline(synthetic, torch, target_s=12.0):
         oracle.forward(sl["q"], sl["k"], sl["v"], sl["g"], sl["beta"], h0=x["h0"])
         return time.perf_counter() - t0
 
-    cal = 32
+    cal = 64
     dt = run(cal)
     ts = int(min(T, max(cal, cal * target_s / max(dt, 1e-6))))
-    dt = run(ts)
-    return {"value": B * ts / dt, "unit": "tokens/s", "cores": threads,
+    total_t, total_tok, reps = 0.0, 0, 0
+    while total_t < target_s * 0.8 or reps == 0:
+        total_t += run(ts)
+        total_tok += B * ts
+        reps += 1
+    return {"value": total_tok / total_t, "unit": "tokens/s", "cores": threads,
             "kind": "oracle",
             "sample": "GDN prefill B=4 H=16 d=128, first %d of 4096 tokens of every "
-                      "sequence (all 64 sequence-heads), fp64 token-by-token, %.1f s"
-                      % (ts, dt)}
+                      "sequence (all 64 sequence-heads), fp64 token-by-token, %d pass(es), "
+                      "%.1f s" % (ts, reps, total_t)}
 
 
 def main():
@@ -171,6 +192,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--only-headline", action="store_true")
+    ap.add_argument("--only", choices=["kda_prefill", "decode", "varlen"], default=None,
+                    help="time one secondary workload alone (for profiling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -183,6 +206,20 @@ def main():
     import gated_delta_rule_44_amd as gdr
     from gated_delta_rule_44_amd import synthetic
     dev = torch.device("cuda:0")
+
+    if args.only == "kda_prefill":
+        ms = bench_prefill(gdr, synthetic, torch, dev, 2, 8192, 32, "channel", 1002,
+                           args.steps, args.warmup, h0=False)
+        print(json.dumps({"workload": "kda_prefill_B2_H32_T8192_d128_bf16", "ms_per_step": ms}))
+        return
+    if args.only == "decode":
+        ms, _, _, _ = bench_decode(gdr, synthetic, torch, dev, args.steps, args.warmup)
+        print(json.dumps({"workload": "placement_decode_L48_B256_H32_d128_bf16", "ms_per_step": ms}))
+        return
+    if args.only == "varlen":
+        ms, _, _ = bench_varlen(gdr, synthetic, torch, dev, args.steps, args.warmup)
+        print(json.dumps({"workload": "kda_varlen_N16_H32_d128_bf16", "ms_per_step": ms}))
+        return
 
     B, T, H = 4, 4096, 16
     ms = bench_prefill(gdr, synthetic, torch, dev, B, T, H, "scalar", 1001,
@@ -210,7 +247,7 @@ def main():
                    "state": "fp32, h0 and ht", "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": MEASURED_TRAFFIC,
+                     "traffic": measured_traffic(),
                      "kernel": "chunked_kernel<128, scalar gate>",
                      "algorithmic_bytes_per_launch": nbytes,
                      "mfma_tflops_alg": flops / (ms * 1e-3) / 1e12,
