@@ -50,6 +50,9 @@ constexpr int NW = 8;       // waves per workgroup
 constexpr int NT = NW * 64; // threads per workgroup
 constexpr int BV = 32;      // value columns per workgroup
 constexpr int PC = C + 8;   // padded LDS row length for C-wide bf16 rows
+constexpr int PCT = C + 16; // C-wide bf16 rows read by transpose loads: a row
+                            // stride of 40 dwords puts 4 consecutive rows on
+                            // disjoint banks
 constexpr int PL = C + 4;   // padded LDS row length of the fp32 L^T
 constexpr int PY = 20;      // padded row length of the fp32 16x16 blocks
 constexpr int PV = BV + 8;  // padded LDS row length of the v tile
@@ -98,6 +101,52 @@ __device__ inline bf16x8 frag_cols(const bf16 *base, int ld, int k0, int n0, int
     return __builtin_bit_cast(bf16x8, v);
 }
 
+// x from lane q of each quad of lanes (DPP quad_perm broadcast).
+__device__ inline float quad_bcast(float x, int q) {
+    const int v = __builtin_bit_cast(int, x);
+    int r;
+    switch (q) {
+    case 0: r = __builtin_amdgcn_mov_dpp(v, 0x00, 0xF, 0xF, false); break;
+    case 1: r = __builtin_amdgcn_mov_dpp(v, 0x55, 0xF, 0xF, false); break;
+    case 2: r = __builtin_amdgcn_mov_dpp(v, 0xAA, 0xF, 0xF, false); break;
+    default: r = __builtin_amdgcn_mov_dpp(v, 0xFF, 0xF, 0xF, false); break;
+    }
+    return __builtin_bit_cast(float, r);
+}
+
+// Bounds-checked buffer accesses: a load past nbytes returns zeros and a
+// store past it is dropped, so ragged chunk tails and absent chunks need no
+// branches and every path issues the same memory operations (which keeps the
+// compiler's wait counts exact for loads issued a chunk ahead).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+// Every argument is wave-uniform at each call site; readfirstlane states it
+// so the descriptor lives in scalar registers (a descriptor in vector
+// registers would make the compiler loop over its distinct values).
+__device__ inline rsrc_t make_rsrc(const void *base, unsigned nbytes) {
+    const unsigned long long p = reinterpret_cast<unsigned long long>(base);
+    const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)p);
+    const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(p >> 32));
+    void *ub = reinterpret_cast<void *>(((unsigned long long)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0,
+                                             (int)__builtin_amdgcn_readfirstlane(nbytes),
+                                             0x00020000);
+}
+__device__ inline bf16x8 bload16(rsrc_t r, unsigned off) {
+    return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ inline f32x4 bload16f(rsrc_t r, unsigned off) {
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ inline bf16x4 bload8(rsrc_t r, unsigned off) {
+    return __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+__device__ inline float bload4(rsrc_t r, unsigned off) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+__device__ inline void bstore2(rsrc_t r, unsigned off, bf16 v) {
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, v), r, off, 0, 0);
+}
+
 // A copy of x the compiler cannot see through: lane-dependent addresses are
 // rebuilt from it each iteration instead of being hoisted out of the chunk
 // loop (where they would occupy registers for the whole loop).
@@ -132,15 +181,16 @@ template <int D, bool CH> struct Smem {
     alignas(16) bf16 Q[C * PD];        // q (GDN) or q (.) e^b (KDA), [r][j]
     alignas(16) bf16 K[C * PD];        // k (GDN) or k (.) e^b (KDA), [r][j]
     alignas(16) bf16 Kb[CH ? C * PD : 8];   // k (.) e^-b (KDA), [r][j]
-    alignas(16) bf16 Kh[2][C * PD];    // k (.) e^{b_C - b}, [s][j], by chunk parity
+    static constexpr int PDH = D + 16; // D-wide rows read by transpose loads
+    alignas(16) bf16 Kh[2][C * PDH];   // k (.) e^{b_C - b}, [s][j], by chunk parity
     alignas(16) bf16 S[BV * PD];       // bf16 copy of the state slice, [i][j]
-    alignas(16) bf16 TT[C * PC];       // T^T, [s][r] (read back by transpose loads)
-    alignas(16) bf16 PT[C * PC];       // P^T, [s][r]
+    alignas(16) bf16 TT[C * PCT];      // T^T, [s][r] (read back by transpose loads)
+    alignas(16) bf16 PT[C * PCT];      // P^T, [s][r]
     alignas(16) bf16 XT[BV * PC];      // X^T, [i][s]
     alignas(16) bf16 UT[BV * PC];      // U^T, [i][s]
     alignas(16) bf16 V[C * PV];        // v tile, [r][i]
     alignas(16) float LT[C * PL];      // L^T = (diag(beta) A)^T, [s][r]
-    alignas(16) float Y[4 * 16 * PY];  // inverted diagonal blocks, [b][r][c]
+    alignas(16) float YT[4 * 16 * PY]; // inverted diagonal blocks, transposed: [b][c][r]
     alignas(16) float beta[C];
     alignas(16) float gb[2][C];        // GDN: cumulative log gate b_r, by chunk parity
     alignas(16) float e1[2][C];        // GDN: e^{b_r}
@@ -186,6 +236,7 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
     using Sm = Smem<D, CH>;
     using LI = LaneIds<D>;
     constexpr int PD = Sm::PD;
+    constexpr int PDH = Sm::PDH;
     constexpr int NTILE = D / BV;
     constexpr int CG = D / 8;          // 8-channel groups per row
     constexpr int RPW = 64 / CG;       // row groups per wave
@@ -221,15 +272,11 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
     const bf16 *vg = static_cast<const bf16 *>(a.v) + (size_t)h * D + i0;
     bf16 *og = static_cast<bf16 *>(a.o) + (size_t)h * D + i0;
     const long long nch = (t1 - t0 + C - 1) / C;
-    auto rows_of = [&](long long c) -> int {
-        const long long rem = t1 - (t0 + c * C);
-        return rem < C ? (int)rem : C;
-    };
     const int tid0 = threadIdx.x;
 
     // T and P are lower triangular: the entries above the diagonal of T^T and
     // P^T stay zero, only lower blocks are ever written
-    for (int e = tid0; e < C * PC; e += NT) {
+    for (int e = tid0; e < C * PCT; e += NT) {
         sm.TT[e] = (bf16)0.f;
         sm.PT[e] = (bf16)0.f;
     }
@@ -268,44 +315,48 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
     float rb[2];
     rv[0] = rv[1] = bf16x4{};
     rb[0] = rb[1] = 0.f;
+    // rows of chunk c (0 past the end); the extents below cover exactly the
+    // valid rows, so loads of rows >= valid_rows(c) return zeros
+    auto valid_rows = [&](long long c) -> int {
+        const long long rem = t1 - (t0 + c * C);
+        return rem <= 0 ? 0 : (rem < C ? (int)rem : C);
+    };
     auto load_g = [&](const LI &L, long long c) {
         const long long tc = t0 + c * C;
-        const int Cc = rows_of(c);
+        const int Cc = valid_rows(c);
         if (CH) {
+            const unsigned rowb = (unsigned)(a.H * D * 4);
+            const rsrc_t rs = make_rsrc(a.g + ((size_t)tc * a.H + h) * D,
+                                        Cc ? (Cc - 1) * rowb + D * 4 : 0u);
 #pragma unroll
             for (int i = 0; i < RPT; ++i) {
-                const int r = L.rg * RPT + i;
-                if (r < Cc) {
-                    const float *gp = a.g + ((size_t)(tc + r) * a.H + h) * D + 8 * L.cg;
-                    rgc[i][0] = *reinterpret_cast<const f32x4 *>(gp);
-                    rgc[i][1] = *reinterpret_cast<const f32x4 *>(gp + 4);
-                } else {
-                    rgc[i][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-                    rgc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-                }
+                const unsigned off = (L.rg * RPT + i) * rowb + 32 * L.cg;
+                rgc[i][0] = bload16f(rs, off);
+                rgc[i][1] = bload16f(rs, off + 16);
             }
         } else {
-            rgs = (L.tid < Cc) ? a.g[(size_t)(tc + L.tid) * a.H + h] : 0.f;
+            const unsigned rowb = (unsigned)(a.H * 4);
+            const rsrc_t rs = make_rsrc(a.g + (size_t)tc * a.H + h, Cc ? (Cc - 1) * rowb + 4 : 0u);
+            rgs = bload4(rs, L.tid * rowb);
         }
     };
     auto load_qkvb = [&](const LI &L, long long c, int par) {
         const long long tc = t0 + c * C;
-        const int Cc = rows_of(c);
+        const int Cc = valid_rows(c);
+        const unsigned rowb = (unsigned)(tokstride * 2);
+        const rsrc_t rq_s = make_rsrc(qg + (size_t)tc * tokstride, Cc ? (Cc - 1) * rowb + D * 2 : 0u);
+        const rsrc_t rk_s = make_rsrc(kg + (size_t)tc * tokstride, Cc ? (Cc - 1) * rowb + D * 2 : 0u);
 #pragma unroll
         for (int i = 0; i < RPT; ++i) {
-            const int r = L.rg * RPT + i;
-            if (r < Cc) {
-                const size_t off = (size_t)(tc + r) * tokstride + 8 * L.cg;
-                rq[i] = ld8(qg + off);
-                rk[i] = ld8(kg + off);
-            } else {
-                rq[i] = bf16x8{};
-                rk[i] = bf16x8{};
-            }
+            const unsigned off = (L.rg * RPT + i) * rowb + 16 * L.cg;
+            rq[i] = bload16(rq_s, off);
+            rk[i] = bload16(rk_s, off);
         }
-        rv[par] = L.vr < Cc ? *reinterpret_cast<const bf16x4 *>(vg + (size_t)(tc + L.vr) * tokstride + L.vc)
-                            : bf16x4{};
-        rb[par] = (L.tid < Cc) ? a.beta[(size_t)(tc + L.tid) * a.H + h] : 0.f;
+        const rsrc_t rv_s = make_rsrc(vg + (size_t)tc * tokstride, Cc ? (Cc - 1) * rowb + BV * 2 : 0u);
+        rv[par] = bload8(rv_s, L.vr * rowb + 2 * L.vc);
+        const unsigned browb = (unsigned)(a.H * 4);
+        const rsrc_t rb_s = make_rsrc(a.beta + (size_t)tc * a.H + h, Cc ? (Cc - 1) * browb + 4 : 0u);
+        rb[par] = bload4(rb_s, L.tid * browb);
     };
 
     // gated operands Qt, Kt, Kb of the next chunk, held in registers from
@@ -394,7 +445,7 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
                 gq[i] = cvt8(qt);
                 gk[i] = cvt8(kt);
                 gkb[i] = cvt8(kb);
-                *reinterpret_cast<bf16x8 *>(&sm.Kh[par][r * PD + 8 * L.cg]) = cvt8(kh);
+                *reinterpret_cast<bf16x8 *>(&sm.Kh[par][r * PDH + 8 * L.cg]) = cvt8(kh);
             }
         } else {
             const float bC = sm.gb[par][C - 1];
@@ -408,7 +459,7 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
                 for (int e = 0; e < 8; ++e) kh[e] = (float)rk[i][e] * sc;
                 gq[i] = rq[i];
                 gk[i] = rk[i];
-                *reinterpret_cast<bf16x8 *>(&sm.Kh[par][r * PD + 8 * L.cg]) = cvt8(kh);
+                *reinterpret_cast<bf16x8 *>(&sm.Kh[par][r * PDH + 8 * L.cg]) = cvt8(kh);
             }
         }
     };
@@ -438,16 +489,15 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
         const bool hasS = j >= 1;
         const bool hasP = j < nch;
         const bool hasG = j + 1 < nch;
-        const bool hasR = j + 2 < nch;
 
         // ================= phase A ========================================
         if (hasS) {   // U = T X of chunk j-1; wave w: row block w>>1, value block w&1
             const int I = w >> 1, Jv = w & 1;
             f32x4 u = {0.f, 0.f, 0.f, 0.f};
-            const bf16x8 t0f = frag_cols(sm.TT, PC, 0, 16 * I, lane);
+            const bf16x8 t0f = frag_cols(sm.TT, PCT, 0, 16 * I, lane);
             const bf16x8 x0f = frag_rows(sm.XT, PC, 16 * Jv, 0, lane);
             if (I >= 2) {   // T is lower triangular: rows < 32 need s < 32 only
-                const bf16x8 t1f = frag_cols(sm.TT, PC, 32, 16 * I, lane);
+                const bf16x8 t1f = frag_cols(sm.TT, PCT, 32, 16 * I, lane);
                 const bf16x8 x1f = frag_rows(sm.XT, PC, 16 * Jv, 32, lane);
                 u = mfma32(t1f, x1f, u);
             }
@@ -458,6 +508,7 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
         __syncthreads();
 
         // ================= phase B ========================================
+        f32x4 ov[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
         if (w < 4) {
             if (hasP) {
                 // A and P of chunk j by 16-row blocks (I, J <= I); each wave
@@ -485,7 +536,7 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
                         pm[e] = s <= r0 + e ? pv[e] * dv[e] : 0.f;
                     }
                     *reinterpret_cast<f32x4 *>(&sm.LT[s * PL + r0]) = lv;
-                    *reinterpret_cast<bf16x4 *>(&sm.PT[s * PC + r0]) = cvt4(pm);
+                    *reinterpret_cast<bf16x4 *>(&sm.PT[s * PCT + r0]) = cvt4(pm);
                 };
                 auto tile = [&](const bf16x8 (&kf)[KD], const bf16x8 (&qf)[KD], int I, int J) {
                     bf16x8 bf[KD];
@@ -513,46 +564,40 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
                     tile(kf, qf, 3, 0);
                 }
                 __threadfence_block();
-                // (I + L_bb) y = e_cc by right-looking forward substitution in
-                // fp32: lane column cc, all 16 rows in registers
+                // (I + L_bb) Y = I by forward substitution in fp32.  Lane
+                // (column cq = lane >> 2, group gq = lane & 3) owns rows
+                // 4gq..4gq+3 of column cq; it preloads L[4gq+e][r] for all r
+                // (row r of L^T), and each y_r is broadcast from its owner
+                // lane to the quad by DPP, so no LDS access sits in the
+                // dependency chain.
                 const int b = Id;
-                const int cc = l15;
-                float y[16], acc[16];
+                const int cq = lane >> 2, gq = lane & 3;
+                f32x4 Lv[16];
 #pragma unroll
-                for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+                for (int r = 0; r < 16; ++r)
+                    Lv[r] = *reinterpret_cast<const f32x4 *>(&sm.LT[(16 * b + r) * PL + 16 * b + 4 * gq]);
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f}, y4 = acc;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    y[r] = r == cc ? 1.f : (r > cc ? -acc[r] : 0.f);
-                    const float *lt = &sm.LT[(16 * b + r) * PL + 16 * b];   // column r of L_bb
-#pragma unroll
-                    for (int q4 = (r + 1) / 4; q4 < 4; ++q4) {
-                        const f32x4 col = *reinterpret_cast<const f32x4 *>(lt + 4 * q4);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (4 * q4 + e > r) acc[4 * q4 + e] += col[e] * y[r];
-                    }
+                    const int e = r & 3, go = r >> 2;
+                    const float own = r == cq ? 1.f : (r > cq ? -acc[e] : 0.f);
+                    const float yr = quad_bcast(own, go);
+                    y4[e] = gq == go ? yr : y4[e];
+                    acc += Lv[r] * yr;   // L is strictly lower: rows <= r add zero
                 }
-                if (lane < 16) {
-                    const float bcc = sm.beta[16 * b + cc];
-                    float tv[16];
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        sm.Y[(b * 16 + r) * PY + cc] = y[r];
-                        tv[r] = y[r] * bcc;
-                    }
-                    // T[16b + r][16b + cc] -> T^T row 16b + cc, columns 16b..16b+15
-                    *reinterpret_cast<bf16x8 *>(&sm.TT[(16 * b + cc) * PC + 16 * b]) = cvt8(tv);
-                    *reinterpret_cast<bf16x8 *>(&sm.TT[(16 * b + cc) * PC + 16 * b + 8]) = cvt8(tv + 8);
+                {
+                    const float bc = sm.beta[16 * b + cq];
+                    // T[16b+4gq+e][16b+cq] -> T^T row 16b+cq;  Y^T[b][cq][4gq..]
+                    *reinterpret_cast<bf16x4 *>(&sm.TT[(16 * b + cq) * PCT + 16 * b + 4 * gq]) = cvt4(y4 * bc);
+                    *reinterpret_cast<f32x4 *>(&sm.YT[(b * 16 + cq) * PY + 4 * gq]) = y4;
                 }
             }
         } else if (hasS) {
             // outputs and state update of chunk j-1 (row block / key blocks of
             // this wave)
             const int I = w - 4;
-            const int Cc = rows_of(j - 1);
-            const long long tc = t0 + (j - 1) * C;
-            const bf16x8 p0 = frag_cols(sm.PT, PC, 0, 16 * I, lane);
-            const bf16x8 p1 = frag_cols(sm.PT, PC, 32, 16 * I, lane);
+            const bf16x8 p0 = frag_cols(sm.PT, PCT, 0, 16 * I, lane);
+            const bf16x8 p1 = frag_cols(sm.PT, PCT, 32, 16 * I, lane);
             bf16x8 uf[2][2];
 #pragma unroll
             for (int jv = 0; jv < 2; ++jv) {
@@ -563,12 +608,7 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
             for (int jv = 0; jv < 2; ++jv) {
                 f32x4 o = mfma32(p0, uf[jv][0], accQS[jv]);
                 if (I >= 2) o = mfma32(p1, uf[jv][1], o);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 16 * I + 4 * l4 + e;
-                    if (r < Cc)
-                        og[(size_t)(tc + r) * tokstride + 16 * jv + l15] = (bf16)(a.scale * o[e]);
-                }
+                ov[jv] = o * a.scale;
             }
             // S^T <- e^{b_C} (.) S^T + Kh^T U  (chunk j-1: parity 1 - PAR)
 #pragma unroll
@@ -579,8 +619,8 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
                 if (CH) gm = *reinterpret_cast<const f32x4 *>(&sm.gam[1 - PAR][jc]);
                 else    gm = f32x4{sm.gam[1 - PAR][0], sm.gam[1 - PAR][0], sm.gam[1 - PAR][0],
                                    sm.gam[1 - PAR][0]};
-                const bf16x8 k0f = frag_cols(sm.Kh[1 - PAR], PD, 0, 16 * Jk, lane);
-                const bf16x8 k1f = frag_cols(sm.Kh[1 - PAR], PD, 32, 16 * Jk, lane);
+                const bf16x8 k0f = frag_cols(sm.Kh[1 - PAR], PDH, 0, 16 * Jk, lane);
+                const bf16x8 k1f = frag_cols(sm.Kh[1 - PAR], PDH, 32, 16 * Jk, lane);
 #pragma unroll
                 for (int jv = 0; jv < 2; ++jv) {
                     f32x4 sv = St[kb][jv] * gm;
@@ -591,8 +631,21 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
                 }
             }
         }
+        {   // outputs of chunk j-1: every wave issues the stores, which land only
+            // for the state waves of a chunk that exists
+            const long long tc = t0 + (j - 1) * C;
+            const int Cc = (hasS && w >= 4) ? valid_rows(j - 1) : 0;
+            const unsigned rowb = (unsigned)(tokstride * 2);
+            const rsrc_t ro = make_rsrc(og + (size_t)tc * tokstride, Cc ? (Cc - 1) * rowb + BV * 2 : 0u);
+            const int I = w & 3;
+#pragma unroll
+            for (int jv = 0; jv < 2; ++jv)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    bstore2(ro, (16 * I + 4 * l4 + e) * rowb + 2 * (16 * jv + l15), (bf16)ov[jv][e]);
+        }
         if (hasG) scan(L, 1 - PAR);
-        if (hasR) load_g(L, j + 2);
+        load_g(L, j + 2);
         __syncthreads();
 
         // ================= phase C ========================================
@@ -605,12 +658,12 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
                     const float *p = &sm.LT[(16 * bk + 4 * l4) * PL + 16 * bi + l15];
                     return bf16x4{(bf16)p[0], (bf16)p[PL], (bf16)p[2 * PL], (bf16)p[3 * PL]};
                 };
-                auto opYA = [&](int bi) -> bf16x4 {
-                    return cvt4(*reinterpret_cast<const f32x4 *>(&sm.Y[(bi * 16 + l15) * PY + 4 * l4]));
-                };
-                auto opYB = [&](int bj) -> bf16x4 {
-                    const float *p = &sm.Y[(bj * 16 + 4 * l4) * PY + l15];
+                auto opYA = [&](int bi) -> bf16x4 {   // Y_ii[l15][4*l4..] = Y^T[4*l4..][l15]
+                    const float *p = &sm.YT[(bi * 16 + 4 * l4) * PY + l15];
                     return bf16x4{(bf16)p[0], (bf16)p[PY], (bf16)p[2 * PY], (bf16)p[3 * PY]};
+                };
+                auto opYB = [&](int bj) -> bf16x4 {   // Y_jj[4*l4..][l15] = Y^T[l15][4*l4..]
+                    return cvt4(*reinterpret_cast<const f32x4 *>(&sm.YT[(bj * 16 + l15) * PY + 4 * l4]));
                 };
                 const f32x4 z0 = {0.f, 0.f, 0.f, 0.f};
                 const bf16x4 B00 = opYB(0), B11 = opYB(1), B22 = opYB(2);
@@ -627,7 +680,7 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
                 // T_ij = Y_ij diag(beta_j) -> T^T[s][r..r+3]
                 auto putT = [&](int bi, int bj, f32x4 yv) {
                     const int s = 16 * bj + l15;
-                    *reinterpret_cast<bf16x4 *>(&sm.TT[s * PC + 16 * bi + 4 * l4]) = cvt4(yv * sm.beta[s]);
+                    *reinterpret_cast<bf16x4 *>(&sm.TT[s * PCT + 16 * bi + 4 * l4]) = cvt4(yv * sm.beta[s]);
                 };
                 putT(1, 0, Y10);
                 putT(2, 1, Y21);
@@ -669,30 +722,33 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
             }
         }
         if (hasG) gate(L, 1 - PAR);
-        if (hasR) load_qkvb(L, j + 2, PAR);
+        load_qkvb(L, j + 2, PAR);
         __syncthreads();
     };
 
     // ---- prologue: chunk 0 gated, chunk 1 loaded
     {
         const LI L(tid0);
-        if (nch > 0) {
-            load_g(L, 0);
-            load_qkvb(L, 0, 0);
-            scan(L, 0);
-        }
+        // unconditional even without a chunk (the loads then return zeros):
+        // every path waits on these registers before the loop
+        load_g(L, 0);
+        load_qkvb(L, 0, 0);
+        scan(L, 0);
         __syncthreads();
-        if (nch > 0) gate(L, 0);
-        if (nch > 1) {
-            load_g(L, 1);
-            load_qkvb(L, 1, 1);
-        }
+        gate(L, 0);
+        load_g(L, 1);
+        load_qkvb(L, 1, 1);
     }
 
-    for (long long j = 0; j <= nch; j += 2) {
+    // iterations j = 0..nch, in (even, odd) pairs with a trailing even one
+    // peeled off: the loop is entered only from the end of an odd iteration,
+    // so the loads in flight at its head are always the same
+    long long j = 0;
+    for (; j + 1 <= nch; j += 2) {
         iteration(std::integral_constant<int, 0>{}, j);
-        if (j + 1 <= nch) iteration(std::integral_constant<int, 1>{}, j + 1);
+        iteration(std::integral_constant<int, 1>{}, j + 1);
     }
+    if (j <= nch) iteration(std::integral_constant<int, 0>{}, j);
 
     if (a.ht) {
         const LI L(tid0);
