@@ -41,6 +41,7 @@
 #include <type_traits>
 
 #include "gdr_internal.h"
+#include "device_util.h"
 
 namespace gdr {
 namespace {
@@ -56,105 +57,6 @@ constexpr int PCT = C + 16; // C-wide bf16 rows read by transpose loads: a row
 constexpr int PL = C + 4;   // padded LDS row length of the fp32 L^T
 constexpr int PY = 20;      // padded row length of the fp32 16x16 blocks
 constexpr int PV = BV + 8;  // padded LDS row length of the v tile
-constexpr float kLog2e = 1.4426950408889634f;
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-
-__device__ inline float ex(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
-
-__device__ inline f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-__device__ inline f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
-}
-__device__ inline bf16x8 ld8(const bf16 *p) { return *reinterpret_cast<const bf16x8 *>(p); }
-__device__ inline bf16x4 cvt4(f32x4 x) {
-    return bf16x4{(bf16)x.x, (bf16)x.y, (bf16)x.z, (bf16)x.w};
-}
-__device__ inline bf16x8 cvt8(const float *x) {
-    return bf16x8{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3],
-                  (bf16)x[4], (bf16)x[5], (bf16)x[6], (bf16)x[7]};
-}
-
-// MFMA fragment of a row-major [rows][ld] bf16 tile: lane holds row
-// r0 + (lane & 15), columns k0 + 8 * (lane >> 4) .. +7.  This is the A operand
-// of A(rows) x B, and the B operand of X Y^T with Y row-major.
-__device__ inline bf16x8 frag_rows(const bf16 *base, int ld, int r0, int k0, int lane) {
-    return ld8(base + (r0 + (lane & 15)) * ld + k0 + 8 * (lane >> 4));
-}
-
-// MFMA fragment read across rows of a row-major [k][ld] bf16 tile: lane
-// holds column n0 + (lane & 15), rows k0 + 8 * (lane >> 4) .. +7.  Built from
-// two ds_read_b64_tr_b16: within each 16-lane group, output lane i, slot m
-// receives element (i & 3) of the 4-element segment addressed by lane
-// (i >> 2) + 4m; addressing row (j >> 2), columns 4 (j & 3) from lane j
-// therefore delivers rows 0..3 of column i to lane i.
-__device__ inline bf16x8 frag_cols(const bf16 *base, int ld, int k0, int n0, int lane) {
-    const int i = lane & 15;
-    const bf16 *p = base + (k0 + 8 * (lane >> 4) + (i >> 2)) * ld + n0 + 4 * (i & 3);
-    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p));
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p + 4 * ld));
-    typedef short s16x8 __attribute__((ext_vector_type(8)));
-    const s16x8 v = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-    return __builtin_bit_cast(bf16x8, v);
-}
-
-// x from lane q of each quad of lanes (DPP quad_perm broadcast).
-__device__ inline float quad_bcast(float x, int q) {
-    const int v = __builtin_bit_cast(int, x);
-    int r;
-    switch (q) {
-    case 0: r = __builtin_amdgcn_mov_dpp(v, 0x00, 0xF, 0xF, false); break;
-    case 1: r = __builtin_amdgcn_mov_dpp(v, 0x55, 0xF, 0xF, false); break;
-    case 2: r = __builtin_amdgcn_mov_dpp(v, 0xAA, 0xF, 0xF, false); break;
-    default: r = __builtin_amdgcn_mov_dpp(v, 0xFF, 0xF, 0xF, false); break;
-    }
-    return __builtin_bit_cast(float, r);
-}
-
-// Bounds-checked buffer accesses: a load past nbytes returns zeros and a
-// store past it is dropped, so ragged chunk tails and absent chunks need no
-// branches and every path issues the same memory operations (which keeps the
-// compiler's wait counts exact for loads issued a chunk ahead).
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-// Every argument is wave-uniform at each call site; readfirstlane states it
-// so the descriptor lives in scalar registers (a descriptor in vector
-// registers would make the compiler loop over its distinct values).
-__device__ inline rsrc_t make_rsrc(const void *base, unsigned nbytes) {
-    const unsigned long long p = reinterpret_cast<unsigned long long>(base);
-    const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)p);
-    const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(p >> 32));
-    void *ub = reinterpret_cast<void *>(((unsigned long long)hi << 32) | lo);
-    return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0,
-                                             (int)__builtin_amdgcn_readfirstlane(nbytes),
-                                             0x00020000);
-}
-__device__ inline bf16x8 bload16(rsrc_t r, unsigned off) {
-    return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
-__device__ inline f32x4 bload16f(rsrc_t r, unsigned off) {
-    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
-__device__ inline bf16x4 bload8(rsrc_t r, unsigned off) {
-    return __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
-}
-__device__ inline float bload4(rsrc_t r, unsigned off) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
-}
-__device__ inline void bstore2(rsrc_t r, unsigned off, bf16 v) {
-    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, v), r, off, 0, 0);
-}
-
-// A copy of x the compiler cannot see through: lane-dependent addresses are
-// rebuilt from it each iteration instead of being hoisted out of the chunk
-// loop (where they would occupy registers for the whole loop).
-__device__ inline int opaque(int x) {
-    int y;
-    asm volatile("v_mov_b32 %0, %1" : "=v"(y) : "v"(x));
-    return y;
-}
 
 // Per-thread indices used by every phase.
 template <int D> struct LaneIds {
@@ -783,6 +685,7 @@ __global__ __launch_bounds__(256) void schedule_kernel(const int32_t *cu, int N,
 }  // namespace
 
 hipError_t launch_prefill_chunked(int D, const PrefillArgs &a, hipStream_t s) {
+    if (!a.channel_gate) return launch_prefill_chain(D, a, s);
     const long long units = (long long)a.N * a.H;
     if (units <= 0) return hipSuccess;
     const int ntile = D / BV;

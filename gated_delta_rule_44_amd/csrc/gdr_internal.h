@@ -75,6 +75,8 @@ struct PrefillArgs {
 hipError_t launch_prefill_recurrent(bool bf16_io, int D, const PrefillArgs &a,
                                     hipStream_t s);
 hipError_t launch_prefill_chunked(int D, const PrefillArgs &a, hipStream_t s);
+// scalar gate: the state chain on dedicated waves (chunked_chain.hip)
+hipError_t launch_prefill_chain(int D, const PrefillArgs &a, hipStream_t s);
 hipError_t launch_varlen_schedule(const int32_t *cu_seqlens, int N,
                                   int32_t *order, hipStream_t s);
 
