@@ -178,8 +178,13 @@ __global__ __launch_bounds__(NT, 1) void chain_kernel(PrefillArgs a) {
         int c3 = 0, c2 = 0;   // c mod 3, c mod 2
         for (long long c = 0; c < nch; ++c, c3 = c3 == 2 ? 0 : c3 + 1, c2 ^= 1) {
             const bf16 *Kc = sm.K[c3];
-            // ---- alpha: X = V - diag(e^b) K S^T
+            // ---- alpha: X = V - diag(e^b) K S^T; then the operands of the
+            //      state update (k rows are final since their staging), so the
+            //      update need not wait on LDS
             f32x4 X[4];
+            bf16x8 KT[KS][2];
+            f32x4 hs[4];
+            float gC;
             {
                 const bf16 *Vc = sm.V[c2];
                 const float *feb = sm.feb[c3];
@@ -197,42 +202,53 @@ __global__ __launch_bounds__(NT, 1) void chain_kernel(PrefillArgs a) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) X[rb][e] = (float)vv[e] - eb[e] * xk[e];
                 }
-            }
-            __syncthreads();
-            // ---- beta: U = T X, S^T <- e^{b_C} S^T + K^T diag(e^{b_C - b}) U
-            {
-                const bf16 *TTc = sm.TT[c2];
-                const bf16x8 Bx[2] = {acc_pair(X[0], X[1]), acc_pair(X[2], X[3])};
-                f32x4 U[4];
-#pragma unroll
-                for (int sb = 0; sb < 4; ++sb) {
-                    U[sb] = mfma32z(tile_pair(TTc, sb, 0), Bx[0]);
-                    if (sb >= 2) U[sb] = mfma32(tile_pair(TTc, sb, 1), Bx[1], U[sb]);
-                }
-                sm.UB[ib][0][lane] = acc_pair(U[0], U[1]);
-                sm.UB[ib][1][lane] = acc_pair(U[2], U[3]);
-                const float *fhs = sm.fhs[c3];
-                f32x4 Uh[4];
-#pragma unroll
-                for (int sb = 0; sb < 4; ++sb)
-                    Uh[sb] = U[sb] * *reinterpret_cast<const f32x4 *>(&fhs[16 * sb + 4 * q4]);
-                const bf16x8 Bh[2] = {acc_pair(Uh[0], Uh[1]), acc_pair(Uh[2], Uh[3])};
-                const float gC = sm.fgc[c3][0];
                 // A operand K^T[16 Jk + l15][s] by transpose loads of the k
                 // rows: lane j of each 16-lane group addresses the four stored
                 // columns that hold k columns 16 Jk + 4 (j & 3) .. +3
 #pragma unroll
                 for (int jk = 0; jk < KS; ++jk) {
                     const int pc = 32 * (jk >> 1) + 8 * (l15 & 3) + 4 * (jk & 1);
-                    f32x4 sv = St[jk] * gC;
 #pragma unroll
                     for (int kk = 0; kk < 2; ++kk) {
                         const bf16 *p = Kc + (32 * kk + 4 * q4 + (l15 >> 2)) * PD + pc;
                         const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p));
                         const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p + 16 * PD));
-                        sv = mfma32(cat8(__builtin_bit_cast(bf16x4, lo), __builtin_bit_cast(bf16x4, hi)),
-                                    Bh[kk], sv);
+                        KT[jk][kk] = cat8(__builtin_bit_cast(bf16x4, lo), __builtin_bit_cast(bf16x4, hi));
                     }
+                }
+                const float *fhs = sm.fhs[c3];
+#pragma unroll
+                for (int sb = 0; sb < 4; ++sb) hs[sb] = *reinterpret_cast<const f32x4 *>(&fhs[16 * sb + 4 * q4]);
+                gC = sm.fgc[c3][0];
+            }
+            __syncthreads();
+            // ---- beta: U = T X, S^T <- e^{b_C} S^T + K^T diag(e^{b_C - b}) U
+            {
+                const bf16 *TTc = sm.TT[c2];
+                bf16x8 Ta[4][2];
+#pragma unroll
+                for (int sb = 0; sb < 4; ++sb) {
+                    Ta[sb][0] = tile_pair(TTc, sb, 0);
+                    Ta[sb][1] = sb >= 2 ? tile_pair(TTc, sb, 1) : bf16x8{};
+                }
+                const bf16x8 Bx[2] = {acc_pair(X[0], X[1]), acc_pair(X[2], X[3])};
+                f32x4 U[4];
+#pragma unroll
+                for (int sb = 0; sb < 4; ++sb) {
+                    U[sb] = mfma32z(Ta[sb][0], Bx[0]);
+                    if (sb >= 2) U[sb] = mfma32(Ta[sb][1], Bx[1], U[sb]);
+                }
+                sm.UB[ib][0][lane] = acc_pair(U[0], U[1]);
+                sm.UB[ib][1][lane] = acc_pair(U[2], U[3]);
+                f32x4 Uh[4];
+#pragma unroll
+                for (int sb = 0; sb < 4; ++sb) Uh[sb] = U[sb] * hs[sb];
+                const bf16x8 Bh[2] = {acc_pair(Uh[0], Uh[1]), acc_pair(Uh[2], Uh[3])};
+#pragma unroll
+                for (int jk = 0; jk < KS; ++jk) {
+                    f32x4 sv = St[jk] * gC;
+                    sv = mfma32(KT[jk][0], Bh[0], sv);
+                    sv = mfma32(KT[jk][1], Bh[1], sv);
                     St[jk] = sv;
                 }
                 publish_state();
@@ -323,45 +339,48 @@ __global__ __launch_bounds__(NT, 1) void chain_kernel(PrefillArgs a) {
             p = mfma32(kj[kk], qi[kk], p);
         }
     };
+    // gate and beta factors of block (I, J): b_r and beta_r of row r = 16I + l15,
+    // b_s and beta_s of rows s = 16J + 4 q4 .. +3 (read ahead of the MFMAs)
+    struct BlockF { float br, betar; f32x4 bs, betas; };
+    auto load_fac = [&](int I, int J, const float *fbv, const float *fbt) -> BlockF {
+        BlockF f;
+        f.br = fbv[16 * I + l15];
+        f.betar = fbt[16 * I + l15];
+        f.bs = *reinterpret_cast<const f32x4 *>(&fbv[16 * J + 4 * q4]);
+        f.betas = *reinterpret_cast<const f32x4 *>(&fbt[16 * J + 4 * q4]);
+        return f;
+    };
     // off-diagonal block (I > J): P_IJ^T and L_IJ^T into LDS
-    auto put_offdiag = [&](int I, int J, f32x4 g, f32x4 p, const float *fbv, const float *fbt,
-                           bf16 *PTn, bf16 *LTn) {
-        const int r = 16 * I + l15;
-        const float br = fbv[r], betar = fbt[r];
-        const f32x4 bs = *reinterpret_cast<const f32x4 *>(&fbv[16 * J + 4 * q4]);
+    auto put_offdiag = [&](int I, int J, f32x4 g, f32x4 p, const BlockF &F, bf16 *PTn, bf16 *LTn) {
         f32x4 pv, lv;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const float f = ex(br - bs[e]);
+            const float f = ex(F.br - F.bs[e]);
             pv[e] = f * p[e];
-            lv[e] = betar * f * g[e];
+            lv[e] = F.betar * f * g[e];
         }
         tile_st(PTn + tri(I, J) * 256, lane, pv);
         tile_st(LTn + ltri(I, J) * 256, lane, lv);
     };
     // diagonal block b: P_bb^T into LDS; M = L_bb as acc(M^T), acc(M) (the
     // Gram block is symmetric, so both come from the one product)
-    auto diag_prep = [&](int b, f32x4 g, f32x4 p, const float *fbv, const float *fbt, bf16 *PTn,
-                         f32x4 &MT, f32x4 &Mn) {
+    auto diag_prep = [&](int b, f32x4 g, f32x4 p, const BlockF &F, bf16 *PTn, f32x4 &MT, f32x4 &Mn) {
         const int rl = l15;
-        const float br = fbv[16 * b + rl], betar = fbt[16 * b + rl];
-        const f32x4 bs = *reinterpret_cast<const f32x4 *>(&fbv[16 * b + 4 * q4]);
-        const f32x4 betas = *reinterpret_cast<const f32x4 *>(&fbt[16 * b + 4 * q4]);
         f32x4 pv;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int sl = 4 * q4 + e;
-            const float d = br - bs[e];
+            const float d = F.br - F.bs[e];
             const float f = ex(sl <= rl ? d : -d);
             pv[e] = sl <= rl ? f * p[e] : 0.f;
-            MT[e] = sl < rl ? betar * f * g[e] : 0.f;
-            Mn[e] = sl > rl ? betas[e] * f * g[e] : 0.f;
+            MT[e] = sl < rl ? F.betar * f * g[e] : 0.f;
+            Mn[e] = sl > rl ? F.betas[e] * f * g[e] : 0.f;
         }
         tile_st(PTn + tri(b, b) * 256, lane, pv);
     };
     // Y_bb = (I + M)^{-1} = (I - M)(I + M^2)(I + M^4)(I + M^8) and Y_bb^T; an
     // MFMA with A operand acc(X^T) and B operand acc(Y) yields acc(X Y)
-    auto diag_invert = [&](int b, f32x4 MT, f32x4 Mn, const float *fbt, bf16 *TTn) {
+    auto diag_invert = [&](int b, f32x4 MT, f32x4 Mn, f32x4 betas, bf16 *TTn) {
         f32x4 I4;
 #pragma unroll
         for (int e = 0; e < 4; ++e) I4[e] = 4 * q4 + e == l15 ? 1.f : 0.f;
@@ -380,7 +399,6 @@ __global__ __launch_bounds__(NT, 1) void chain_kernel(PrefillArgs a) {
         const f32x4 YT = mfma16(cvt4(M8), cvt4(Z2T), Z2T);
         tile_st(sm.YD[b][0], lane, Y);
         tile_st(sm.YD[b][1], lane, YT);
-        const f32x4 betas = *reinterpret_cast<const f32x4 *>(&fbt[16 * b + 4 * q4]);
         tile_st(TTn + tri(b, b) * 256, lane, YT * betas);   // T_bb^T = diag(beta) Y_bb^T
     };
     // ---- outputs (waves 4, 5): O^T = scale (S Q^T diag(e^b) + U^T P^T), so
@@ -475,7 +493,8 @@ __global__ __launch_bounds__(NT, 1) void chain_kernel(PrefillArgs a) {
         bf16 *PTn = sm.PT[nm3];
         // ---------------- alpha: T off the diagonal of chunk c (its diagonal
         // blocks and L came from the previous iteration); diagonal block db of
-        // the A and P blocks of chunk c+1 ----------------
+        // the A and P blocks of chunk c+1.  Every LDS operand first. --------
+        BlockF Fd;
         {
             const bf16 *LTc = sm.LT[cpar];
             bf16x4 lt[6], yb[3], ya[3];
@@ -489,16 +508,18 @@ __global__ __launch_bounds__(NT, 1) void chain_kernel(PrefillArgs a) {
             bf16x8 kd[KD], qd[KD];
             frags(Kn, db, kd);
             frags(Qn, db, qd);
+            Fd = load_fac(db, db, fbv, fbt);
+            // beta_j of the off-diagonal blocks this wave forms: j = 0 (w2),
+            // 1 (w3), 2 (w6)
+            const float bj = sm.fbeta[cm3][16 * (w == 2 ? 0 : (w == 3 ? 1 : 2)) + l15];
             __builtin_amdgcn_sched_barrier(0);
             if (c >= 0 && w != 7) {
                 // Y_ij = -Y_ii sum_k L_ik Y_kj; T_ij = Y_ij diag(beta_j) stored as
                 // T_ij^T in accumulator order: element (4 q4 + e, l15) of Y_ij
                 // goes to lane 16 (l15 >> 2) + 4 q4 + e
-                const float *fbc = sm.fbeta[cm3];
                 bf16 *TTc = sm.TT[cpar];
                 auto fin = [&](int i, f32x4 v) -> f32x4 { return -mfma16z(ya[i - 1], cvt4(v)); };
                 auto putT = [&](int i, int j, f32x4 y) {
-                    const float bj = fbc[16 * j + l15];
                     bf16 *t = TTc + tri(i, j) * 256;
                     const int dl = 16 * (l15 >> 2) + 4 * q4;
 #pragma unroll
@@ -524,34 +545,40 @@ __global__ __launch_bounds__(NT, 1) void chain_kernel(PrefillArgs a) {
             }
             f32x4 g, p;
             products(kd, kd, qd, g, p);
-            diag_prep(db, g, p, fbv, fbt, PTn, dMT, dMn);
+            diag_prep(db, g, p, Fd, PTn, dMT, dMn);
         }
         __syncthreads();
-        // ---------------- beta: diagonal inverses of chunk c+1 and its
-        // off-diagonal A, P blocks:  w2: (1,0), (3,0)  w3: (2,1), (3,1)
-        // w6: (2,0)  w7: (3,2) ----------------
+        // ---------------- beta: staging (its loads are long done), then the
+        // diagonal inverses of chunk c+1 and its off-diagonal A, P blocks:
+        // w2: (1,0), (3,0)  w3: (2,1), (3,1)  w6: (2,0)  w7: (3,2) ----------
+        if (w >= 6) {
+            stage_store(c + 2, sm3);
+            stage_load(c + 3);
+        }
         {
             bf16 *LTn = sm.LT[npar];
             const int J = db < 2 ? db : (db == 2 ? 0 : 2);   // 0, 1, 0, 2
             const int I0 = db < 2 ? db + 1 : (db == 2 ? 2 : 3);
-            bf16x8 kj[KD], ki[KD], qi[KD];
+            bf16x8 kj[KD], ki[KD], qi[KD], k3[KD], q3[KD];
             frags(Kn, J, kj);
             frags(Kn, I0, ki);
             frags(Qn, I0, qi);
-            diag_invert(db, dMT, dMn, sm.fbeta[nm3], sm.TT[npar]);
+            const BlockF F0 = load_fac(I0, J, fbv, fbt);
+            BlockF F3 = F0;
+            if (db < 2) {
+                frags(Kn, 3, k3);
+                frags(Qn, 3, q3);
+                F3 = load_fac(3, J, fbv, fbt);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            diag_invert(db, dMT, dMn, Fd.betas, sm.TT[npar]);
             f32x4 g, p;
             products(kj, ki, qi, g, p);
-            put_offdiag(I0, J, g, p, fbv, fbt, PTn, LTn);
+            put_offdiag(I0, J, g, p, F0, PTn, LTn);
             if (db < 2) {
-                frags(Kn, 3, ki);
-                frags(Qn, 3, qi);
-                products(kj, ki, qi, g, p);
-                put_offdiag(3, J, g, p, fbv, fbt, PTn, LTn);
+                products(kj, k3, q3, g, p);
+                put_offdiag(3, J, g, p, F3, PTn, LTn);
             }
-        }
-        if (w >= 6) {
-            stage_store(c + 2, sm3);
-            stage_load(c + 3);
         }
         __syncthreads();
         advance();
