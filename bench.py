@@ -103,19 +103,21 @@ def bench_prefill(gdr, synthetic, torch, dev, B, T, H, gate, seed, steps, warmup
     stream = torch.cuda.current_stream(dev)
     sp = ctypes.c_void_p(stream.cuda_stream)
     gk = 1 if gate == "channel" else 0
+    nbytes = gdr.workspace_bytes(torch.bfloat16, gate == "channel", B, B * T, H)
+    ws = torch.empty(max(nbytes, 1), device=dev, dtype=torch.uint8)
     args = []
     for x, (o, ht) in zip(xs, outs):
         args.append([1, gk, B, T, H, D, D, C, ctypes.c_float(1.0)] +
                     [ctypes.c_void_p(t.data_ptr()) if t is not None else None
-                     for t in (x["q"], x["k"], x["v"], x["g"], x["beta"], x["h0"], o, ht)]
-                    + [sp])
+                     for t in (x["q"], x["k"], x["v"], x["g"], x["beta"], x["h0"], o, ht, ws)]
+                    + [ctypes.c_size_t(nbytes), sp])
 
     def step(i):
         rc = lib.gdr_prefill_chunked(*args[i % sets])
         if rc:
             raise RuntimeError(lib.gdr_last_error().decode())
     ms = timed(step, steps, warmup, stream)
-    del xs, outs
+    del xs, outs, ws
     return ms
 
 
@@ -125,7 +127,8 @@ def bench_varlen(gdr, synthetic, torch, dev, steps, warmup):
                                 device=dev)
     o = torch.empty_like(x["v"])
     ht = torch.empty_like(x["h0"])
-    ws = torch.empty(gdr.workspace_bytes(len(lens)), device=dev, dtype=torch.uint8)
+    ws = torch.empty(gdr.workspace_bytes(torch.bfloat16, True, len(lens), sum(lens), 32),
+                     device=dev, dtype=torch.uint8)
     stream = torch.cuda.current_stream(dev)
 
     def step(i):

@@ -51,10 +51,10 @@ def _load():
     lib.gdr_last_error.restype = ctypes.c_char_p
     lib.gdr_version.restype = ctypes.c_char_p
     lib.gdr_prefill_workspace_bytes.restype = Z
-    lib.gdr_prefill_workspace_bytes.argtypes = [I]
+    lib.gdr_prefill_workspace_bytes.argtypes = [I, I, I, ctypes.c_longlong, I]
     lib.gdr_prefill_chunked.restype = I
     lib.gdr_prefill_chunked.argtypes = [I, I, I, I, I, I, I, I, F,
-                                        P, P, P, P, P, P, P, P, P]
+                                        P, P, P, P, P, P, P, P, P, Z, P]
     lib.gdr_prefill_chunked_varlen.restype = I
     lib.gdr_prefill_chunked_varlen.argtypes = [I, I, I, I, I, I, I, I, F, P, P,
                                                P, P, P, P, P, P, P, P, P, Z, P]
@@ -71,8 +71,23 @@ def version() -> str:
     return _load().gdr_version().decode()
 
 
-def workspace_bytes(n_seqs: int) -> int:
-    return int(_load().gdr_prefill_workspace_bytes(int(n_seqs)))
+def workspace_bytes(dtype, gated_channels: bool, n_seqs: int, tokens: int,
+                    heads: int) -> int:
+    """Bytes of device workspace a prefill over n_seqs sequences of `tokens`
+    tokens in all needs (include/gdr.h, gdr_prefill_workspace_bytes)."""
+    dt = _BF16 if dtype == torch.bfloat16 else _F32
+    gk = _CHANNEL if gated_channels else _SCALAR
+    return int(_load().gdr_prefill_workspace_bytes(dt, gk, int(n_seqs), int(tokens),
+                                                   int(heads)))
+
+
+def _workspace(workspace, nbytes, dev):
+    if workspace is None:
+        return torch.empty(max(nbytes, 1), device=dev, dtype=torch.uint8)
+    _dense("workspace", workspace, device=dev)
+    _need(workspace.numel() * workspace.element_size() >= nbytes,
+          "workspace too small: %d bytes needed" % nbytes)
+    return workspace
 
 
 def _check(rc: int):
@@ -112,14 +127,15 @@ def _dense(name, t, dtype=None, device=None):
 
 
 def prefill(q, k, v, g, beta, h0=None, scale: float = 1.0,
-            output_final_state: bool = True, ht=None):
+            output_final_state: bool = True, ht=None, workspace=None):
     """Chunked prefill, fixed-length batch.
 
     q, k [B,T,H,D], v [B,T,H,D] (bf16: chunked MFMA path; fp32: recurrent
     path), g [B,T,H] (scalar gate) or [B,T,H,D] (channel gate) fp32 log
     gates, beta [B,T,H] fp32, h0 [B,H,D,D] fp32 or None.
     Returns (o [B,T,H,D], ht [B,H,D,D] fp32 or None).  ``ht`` may be passed
-    in (it may be h0 itself for an in-place resume).
+    in (it may be h0 itself for an in-place resume); ``workspace`` (a device
+    buffer of workspace_bytes(...) bytes) is allocated when not given.
     """
     B, T, H, D = q.shape
     dev = q.device
@@ -144,9 +160,12 @@ def prefill(q, k, v, g, beta, h0=None, scale: float = 1.0,
     if ht is not None:
         _dense("ht", ht, torch.float32, dev)
         _need(ht.shape == (B, H, D, D), "ht must be [B,H,D,D]")
+    nbytes = workspace_bytes(q.dtype, gk == _CHANNEL, B, B * T, H)
+    workspace = _workspace(workspace, nbytes, dev)
     _check(_load().gdr_prefill_chunked(
         _dt(q), gk, B, T, H, D, D, 64, float(scale), _ptr(q), _ptr(k), _ptr(v),
-        _ptr(g), _ptr(beta), _ptr(h0), _ptr(o), _ptr(ht), _stream(dev)))
+        _ptr(g), _ptr(beta), _ptr(h0), _ptr(o), _ptr(ht), _ptr(workspace), nbytes,
+        _stream(dev)))
     return o, ht
 
 
@@ -182,10 +201,8 @@ def prefill_varlen(q, k, v, g, beta, cu_seqlens, h0=None, scale: float = 1.0,
     o = torch.empty_like(v)
     if output_final_state and ht is None:
         ht = torch.empty((N, H, D, D), device=dev, dtype=torch.float32)
-    nbytes = workspace_bytes(N)
-    if workspace is None:
-        workspace = torch.empty(max(nbytes, 1), device=dev, dtype=torch.uint8)
-    _need(workspace.numel() * workspace.element_size() >= nbytes, "workspace too small")
+    nbytes = workspace_bytes(q.dtype, gk == _CHANNEL, N, Tt, H)
+    workspace = _workspace(workspace, nbytes, dev)
     hp = None if host is None else host.ctypes.data_as(ctypes.c_void_p)
     _check(_load().gdr_prefill_chunked_varlen(
         _dt(q), gk, N, Tt, H, D, D, 64, float(scale), _ptr(cu_seqlens), hp,

@@ -85,6 +85,35 @@ gdr_status check_prefill_ptrs(const char *what, const void *q, const void *k, co
     return GDR_OK;
 }
 
+gdr_status check_workspace(const char *what, const void *ws, size_t ws_bytes, size_t need) {
+    if (need == 0) return GDR_OK;
+    if (!ws || ws_bytes < need)
+        return fail(GDR_EINVAL, "%s: workspace of %zu bytes needed, %zu given", what, need,
+                    ws ? ws_bytes : (size_t)0);
+    if (!aligned16(ws)) return fail(GDR_EINVAL, "%s: workspace is not 16-byte aligned", what);
+    return GDR_OK;
+}
+
+// Workspace of one prefill call: the varlen schedule (N int32), the first
+// chunk of each packed sequence (N+1 int32) and, for the bf16 scalar-gate
+// chunked path, one kTileBytes record per (chunk, head).  Chunk records are
+// counted as tokens / 64 + N, which bounds sum_n ceil(len_n / 64).
+struct WsLayout {
+    size_t order, chunk_base, tiles, total;
+    long long max_chunks;
+};
+WsLayout ws_layout(bool tiles, int N, long long tokens, int H) {
+    WsLayout w{};
+    if (N <= 0 || tokens < 0 || H <= 0) return w;
+    auto r256 = [](size_t x) { return (x + 255) / 256 * 256; };
+    w.order = 0;
+    w.chunk_base = r256((size_t)N * sizeof(int32_t));
+    w.tiles = w.chunk_base + r256((size_t)(N + 1) * sizeof(int32_t));
+    w.max_chunks = tiles ? tokens / 64 + N : 0;
+    w.total = w.tiles + (size_t)w.max_chunks * H * gdr::kTileBytes;
+    return w;
+}
+
 }  // namespace
 
 extern "C" {
@@ -93,16 +122,16 @@ const char *gdr_last_error(void) { return g_err; }
 
 const char *gdr_version(void) { return "gdr 0.1.0 (gfx950)"; }
 
-size_t gdr_prefill_workspace_bytes(int N) {
-    if (N <= 0) return 0;
-    return (((size_t)N * sizeof(int32_t)) + 255) / 256 * 256;
+size_t gdr_prefill_workspace_bytes(enum gdr_dtype dt, enum gdr_gate gk, int N,
+                                   long long tokens, int H) {
+    return ws_layout(dt == GDR_BF16 && gk == GDR_GATE_SCALAR, N, tokens, H).total;
 }
 
 gdr_status gdr_prefill_chunked(enum gdr_dtype dt, enum gdr_gate gk, int B, int T, int H,
                                int Dk, int Dv, int chunk, float scale, const void *q,
                                const void *k, const void *v, const float *g,
                                const float *beta, const float *h0, void *o, float *ht,
-                               void *stream) {
+                               void *workspace, size_t ws_bytes, void *stream) {
     const char *what = "gdr_prefill_chunked";
     gdr_status st = check_common(dt, gk, Dk, Dv, what);
     if (st != GDR_OK) return st;
@@ -120,9 +149,15 @@ gdr_status gdr_prefill_chunked(enum gdr_dtype dt, enum gdr_gate gk, int B, int T
             return fail(GDR_EINVAL, "%s: h0 and ht overlap without being equal", what);
     }
     if (B == 0) return GDR_OK;
+    const bool tiles = dt == GDR_BF16 && gk == GDR_GATE_SCALAR;
+    const WsLayout L = ws_layout(tiles, B, (long long)B * T, H);
+    st = check_workspace(what, workspace, ws_bytes, tiles ? L.total : 0);
+    if (st != GDR_OK) return st;
     gdr::PrefillArgs a{};
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.h0 = h0; a.o = o; a.ht = ht;
-    a.cu_seqlens = nullptr; a.order = nullptr;
+    a.cu_seqlens = nullptr; a.order = nullptr; a.chunk_base = nullptr;
+    a.tiles = tiles ? static_cast<char *>(workspace) + L.tiles : nullptr;
+    a.max_chunks = tiles ? (long long)B * ((T + 63) / 64) : 0;
     a.N = B; a.T = T; a.H = H; a.scale = scale; a.channel_gate = gk == GDR_GATE_CHANNEL;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = dt == GDR_BF16 ? gdr::launch_prefill_chunked(Dk, a, s)
@@ -165,19 +200,22 @@ gdr_status gdr_prefill_chunked_varlen(enum gdr_dtype dt, enum gdr_gate gk, int N
         if (a0 < a1 + bytes && a1 < a0 + bytes)
             return fail(GDR_EINVAL, "%s: h0 and ht overlap without being equal", what);
     }
-    const size_t need = gdr_prefill_workspace_bytes(N);
-    if (!workspace || ws_bytes < need)
-        return fail(GDR_EINVAL, "%s: workspace of %zu bytes needed, %zu given", what, need,
-                    workspace ? ws_bytes : (size_t)0);
-    if (!aligned16(workspace)) return fail(GDR_EINVAL, "%s: workspace is not 16-byte aligned", what);
+    const bool tiles = dt == GDR_BF16 && gk == GDR_GATE_SCALAR;
+    const WsLayout L = ws_layout(tiles, N, T_total, H);
+    st = check_workspace(what, workspace, ws_bytes, L.total);
+    if (st != GDR_OK) return st;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
-    int32_t *order = static_cast<int32_t *>(workspace);
+    char *ws = static_cast<char *>(workspace);
+    int32_t *order = reinterpret_cast<int32_t *>(ws + L.order);
     hipError_t e = gdr::launch_varlen_schedule(cu_seqlens, N, order, s);
     if (e != hipSuccess) return finish(e, s, what);
     gdr::PrefillArgs a{};
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.h0 = h0; a.o = o; a.ht = ht;
     a.cu_seqlens = cu_seqlens; a.order = order;
+    a.chunk_base = reinterpret_cast<int32_t *>(ws + L.chunk_base);
+    a.tiles = tiles ? ws + L.tiles : nullptr;
+    a.max_chunks = L.max_chunks;
     a.N = N; a.T = 0; a.H = H; a.scale = scale; a.channel_gate = gk == GDR_GATE_CHANNEL;
     e = dt == GDR_BF16 ? gdr::launch_prefill_chunked(Dk, a, s)
                        : gdr::launch_prefill_recurrent(false, Dk, a, s);

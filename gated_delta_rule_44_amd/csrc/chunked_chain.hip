@@ -1,5 +1,7 @@
-// chunked_chain.hip -- chunked prefill of the gated delta rule with the
-// state recurrence on dedicated waves (scalar gate, Gated DeltaNet).
+// chunked_chain.hip -- chunked prefill of the gated delta rule for the scalar
+// gate (Gated DeltaNet) in two kernels: the chunk-local inverse of every
+// chunk in parallel, then the recurrence over chunks with the state on
+// dedicated waves.
 //
 // Chunked form ("Super Apriel: One Checkpoint, Many Speeds", gist.science
 // summary 2a, for the recurrence; the reorganisation into chunks is derived
@@ -11,39 +13,31 @@
 //     O = scale (diag(e^b) Q S^T + P U)
 //     S^T <- e^{b_C} S^T + K^T diag(e^{b_C - b}) U
 //
-// Work split.  The only dependency from chunk to chunk is the state, through
-// X, U and the update.  Two "chain" waves each own 16 of the workgroup's 32
-// value columns and keep their slice of S^T (Dk x 16, fp32) in accumulator
-// registers for the whole sequence; they do nothing but X, U and the update,
-// and publish S^T and U (as bf16 MFMA operands) for the output waves.  A
-// single wave streams LDS at only a fraction of the CU's bandwidth, so
-// everything else is spread over the other six waves, one or two chunks
-// behind or ahead: the A and P blocks and the inverse T (waves 2, 3, 6, 7),
-// the outputs O (waves 4, 5), staging of q, k, v into LDS and the gate
-// prefix sums (waves 4..7).
-//
-// Operands that come from accumulator registers (S^T, X, U) feed the next
-// MFMA directly in the paired k order of device_util.h.  q and k rows are
-// kept in LDS in that same order (within each 32-column block, columns
-// 4m..4m+3 and 16+4m..16+4m+3 are adjacent), so a paired A operand is one
-// 16-byte read; the A and P products take both operands from these rows, so
-// the order cancels there.  T and P live in LDS as 16x16 blocks in
-// accumulator order, transposed (block (i, j) holds T_ij^T), which is the A
-// operand of U = T X in the paired order.
-//
-// T by blocks.  Each diagonal block Y_bb = (I + L_bb)^{-1} is the finite
-// series (I - M)(I + M^2)(I + M^4)(I + M^8) of its strictly lower 16x16 block
-// M (M^16 = 0); the powers and products are 16x16x16 MFMAs, computed in
-// both orientations because an MFMA takes its A operand transposed relative
-// to the accumulator layout.  Off the diagonal, block forward substitution
+// prep_kernel (one workgroup per chunk and head) forms T, which does not
+// depend on the state, and writes it to the workspace as 16x16 blocks in
+// accumulator order, transposed (block (i, j) holds T_ij^T): the LDS image
+// the recurrence kernel reads it in, and the A operand of U = T X.  Each
+// diagonal block Y_bb = (I + L_bb)^{-1} is the finite series
+// (I - M)(I + M^2)(I + M^4)(I + M^8) of its strictly lower 16x16 block M
+// (M^16 = 0), on 16x16x16 MFMAs computed in both orientations because an
+// MFMA takes its A operand transposed relative to the accumulator layout.
+// Off the diagonal, block forward substitution
 // Y_ij = -Y_ii sum_{k=j}^{i-1} L_ik Y_kj; T = Y diag(beta).
 //
-// Two barriers per chunk; iteration c of the loop:
-//   alpha: chain: X (chunk c) | waves 2,3,6,7: T off the diagonal (c), A and
-//          P blocks (c+1) | waves 4,5: O (c-1), diag(e^b) Q S^T (c)
-//   beta:  chain: U, state update (c) | waves 2,3,6,7: diagonal blocks of T
-//          (c+1) | waves 4..7: q, k, v of chunk c+2 into LDS, gate prefix
-//          sums (c+2), global loads of chunk c+3
+// chain_kernel (one workgroup per sequence, head and 32-wide slice of Dv)
+// walks the chunks in order.  The only dependency from chunk to chunk is the
+// state, through X, U and the update.  Two "chain" waves (SIMDs 0 and 1)
+// each own 16 of the 32 value columns and keep their slice of S^T (Dk x 16,
+// fp32) in accumulator registers for the whole sequence; they do nothing but
+// X, U and the update, and publish S^T and U as bf16 MFMA operands.  Four
+// output waves (SIMDs 2 and 3) form P and O one chunk behind; two staging
+// waves (SIMDs 0 and 1, no MFMA work) and two of the output waves bring
+// q, k, v, T and the gate prefix sums of chunk c+2 into LDS while chunk c
+// runs, their global loads issued a whole iteration before the LDS stores.
+// Two barriers per chunk; iteration c:
+//   alpha: chain: X, U, state update (chunk c) | output waves: O (c-1),
+//          diag(e^b) Q S^T (c), P (c) | staging: global loads of c+3
+//   beta:  chain: publish U, S^T; k fragments of c+1 | staging: c+2 into LDS
 #include "gdr_internal.h"
 #include "device_util.h"
 
@@ -51,49 +45,265 @@ namespace gdr {
 namespace {
 
 constexpr int C = 64;        // chunk length
-constexpr int NW = 8;        // waves per workgroup
-constexpr int NT = NW * 64;  // threads per workgroup
-constexpr int BV = 32;       // value columns per workgroup
+constexpr int BV = 32;       // value columns per recurrence workgroup
 
 __device__ inline int tri(int i, int j) { return i * (i + 1) / 2 + j; }   // block (i >= j)
 __device__ inline int ltri(int i, int j) { return i * (i - 1) / 2 + j; }  // block (i > j)
 
+// ===========================================================================
+// prep_kernel: T of one (chunk, head)
+// ===========================================================================
+template <int D> struct PrepSmem {
+    static constexpr int PD = D + 16;   // conflict-free 16-byte row fragments
+    alignas(16) bf16 K[C * PD];
+    alignas(16) bf16 TT[10 * 256];      // T_ij^T, i >= j
+    alignas(16) bf16 LT[6 * 256];       // L_ij^T, i > j
+    alignas(16) bf16 YD[4][2][256];     // Y_bb, Y_bb^T
+    alignas(16) float fb[C];            // b_r
+    alignas(16) float fbeta[C];         // beta_r
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a) {
+    using Sm = PrepSmem<D>;
+    constexpr int PD = Sm::PD;
+    constexpr int KD = D / 32;
+    constexpr int CG = D / 8;           // 16-byte pieces per row
+    constexpr int NPC = C * CG / 256;
+    static_assert(NPC >= 1 && (C * CG) % 256 == 0, "staging layout");
+    static_assert(kTileBytes == 6 * 1024, "tile record: six operand pairs");
+    __shared__ Sm sm;
+
+    // ---- which chunk: ci counts chunks over all sequences
+    const int h = blockIdx.x % a.H;
+    const long long ci = blockIdx.x / a.H;
+    long long t0, t1, c;
+    if (a.cu_seqlens) {
+        if (ci >= a.chunk_base[a.N]) return;
+        int lo = 0, hi = a.N - 1;   // the last sequence whose first chunk is <= ci
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (a.chunk_base[mid] <= ci) lo = mid;
+            else hi = mid - 1;
+        }
+        t0 = a.cu_seqlens[lo];
+        t1 = a.cu_seqlens[lo + 1];
+        c = ci - a.chunk_base[lo];
+    } else {
+        const long long nch = (a.T + C - 1) / C;
+        const long long n = ci / nch;
+        c = ci - n * nch;
+        t0 = n * a.T;
+        t1 = t0 + a.T;
+    }
+    const long long tc = t0 + c * C;
+    const int Cc = (int)(t1 - tc < C ? t1 - tc : C);
+    const size_t tokstride = (size_t)a.H * D;
+    const unsigned rowb = (unsigned)(tokstride * 2);
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, l15 = lane & 15, q4 = lane >> 4;
+
+    // ---- k rows (rows past the sequence read as zeros), gate sums
+    {
+        const size_t base = (size_t)tc * tokstride + (size_t)h * D;
+        const rsrc_t rks = make_rsrc(static_cast<const bf16 *>(a.k) + base,
+                                     (unsigned)(Cc - 1) * rowb + D * 2);
+        bf16x8 vk[NPC];
+#pragma unroll
+        for (int i = 0; i < NPC; ++i) {
+            const int p = i * 256 + tid;
+            vk[i] = bload16(rks, (p / CG) * rowb + 16 * (p % CG));
+        }
+        float gv = 0.f, bv = 0.f;
+        if (w == 0) {
+            const unsigned hb = (unsigned)(a.H * 4);
+            const size_t gb = (size_t)tc * a.H + h;
+            const unsigned gext = (unsigned)(Cc - 1) * hb + 4;
+            gv = bload4(make_rsrc(a.g + gb, gext), lane * hb);
+            bv = bload4(make_rsrc(a.beta + gb, gext), lane * hb);
+        }
+#pragma unroll
+        for (int i = 0; i < NPC; ++i) {
+            const int p = i * 256 + tid;
+            *reinterpret_cast<bf16x8 *>(&sm.K[(p / CG) * PD + 8 * (p % CG)]) = vk[i];
+        }
+        if (w == 0) {
+            sm.fb[lane] = wave_prefix_sum(gv);
+            sm.fbeta[lane] = bv;
+        }
+    }
+    __syncthreads();
+
+    auto frags = [&](int blk, bf16x8 (&f)[KD]) {
+#pragma unroll
+        for (int kk = 0; kk < KD; ++kk) f[kk] = frag_rows(sm.K, PD, 16 * blk, 32 * kk, lane);
+    };
+    // G = K_J K_I^T: lane holds s = 16J + 4 q4 + e, r = 16I + l15
+    auto gram = [&](const bf16x8 (&kj)[KD], const bf16x8 (&ki)[KD]) -> f32x4 {
+        f32x4 g = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KD; ++kk) g = mfma32(kj[kk], ki[kk], g);
+        return g;
+    };
+    // off-diagonal block (I > J) of L, as L_IJ^T
+    auto put_L = [&](int I, int J, f32x4 g) {
+        const float br = sm.fb[16 * I + l15], betar = sm.fbeta[16 * I + l15];
+        const f32x4 bs = *reinterpret_cast<const f32x4 *>(&sm.fb[16 * J + 4 * q4]);
+        f32x4 lv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) lv[e] = betar * ex(br - bs[e]) * g[e];
+        tile_st(sm.LT + ltri(I, J) * 256, lane, lv);
+    };
+
+    // ---- wave w: diagonal block w of T by the series, and the
+    //      off-diagonal blocks of L  w0: (1,0), (3,0)  w1: (2,1), (3,1)
+    //      w2: (2,0)  w3: (3,2)
+    {
+        const int b = w;
+        bf16x8 kd[KD];
+        frags(b, kd);
+        const f32x4 g = gram(kd, kd);
+        // M = L_bb as acc(M^T) and acc(M): the Gram block is symmetric, so
+        // both come from the one product
+        const float br = sm.fb[16 * b + l15], betar = sm.fbeta[16 * b + l15];
+        const f32x4 bs = *reinterpret_cast<const f32x4 *>(&sm.fb[16 * b + 4 * q4]);
+        const f32x4 betas = *reinterpret_cast<const f32x4 *>(&sm.fbeta[16 * b + 4 * q4]);
+        f32x4 MT, Mn, I4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int sl = 4 * q4 + e;
+            const float d = br - bs[e];
+            const float f = ex(sl <= l15 ? d : -d);
+            MT[e] = sl < l15 ? betar * f * g[e] : 0.f;
+            Mn[e] = sl > l15 ? betas[e] * f * g[e] : 0.f;
+            I4[e] = sl == l15 ? 1.f : 0.f;
+        }
+        // Y = (I + M)^{-1} = (I - M)(I + M^2)(I + M^4)(I + M^8) and Y^T; an
+        // MFMA with A operand acc(X^T) and B operand acc(Y) yields acc(X Y)
+        const f32x4 IMn = I4 - Mn, IMT = I4 - MT;
+        const f32x4 M2 = mfma16z(cvt4(MT), cvt4(Mn));
+        const f32x4 M2T = mfma16z(cvt4(Mn), cvt4(MT));
+        const f32x4 Z1 = mfma16(cvt4(M2T), cvt4(IMn), IMn);
+        const f32x4 Z1T = mfma16(cvt4(M2), cvt4(IMT), IMT);
+        const f32x4 M4 = mfma16z(cvt4(M2T), cvt4(M2));
+        const f32x4 M4T = mfma16z(cvt4(M2), cvt4(M2T));
+        const f32x4 Z2 = mfma16(cvt4(M4T), cvt4(Z1), Z1);
+        const f32x4 Z2T = mfma16(cvt4(M4), cvt4(Z1T), Z1T);
+        const f32x4 M8 = mfma16z(cvt4(M4T), cvt4(M4));
+        const f32x4 M8T = mfma16z(cvt4(M4), cvt4(M4T));
+        const f32x4 Y = mfma16(cvt4(M8T), cvt4(Z2), Z2);
+        const f32x4 YT = mfma16(cvt4(M8), cvt4(Z2T), Z2T);
+        tile_st(sm.YD[b][0], lane, Y);
+        tile_st(sm.YD[b][1], lane, YT);
+        tile_st(sm.TT + tri(b, b) * 256, lane, YT * betas);   // T_bb^T = diag(beta) Y_bb^T
+
+        const int J = b < 2 ? b : (b == 2 ? 0 : 2);
+        const int I0 = b < 2 ? b + 1 : (b == 2 ? 2 : 3);
+        bf16x8 kj[KD], ki[KD];
+        frags(J, kj);
+        frags(I0, ki);
+        put_L(I0, J, gram(kj, ki));
+        if (b < 2) {
+            frags(3, ki);
+            put_L(3, J, gram(kj, ki));
+        }
+    }
+    __syncthreads();
+
+    // ---- T off the diagonal: waves 0, 1, 2 take block columns 0, 1, 2
+    if (w < 3) {
+        auto LTb = [&](int i, int j) { return tile_ld(sm.LT + ltri(i, j) * 256, lane); };
+        auto YB = [&](int j) { return tile_ld(sm.YD[j][0], lane); };   // B operand Y_jj
+        auto fin = [&](int i, f32x4 v) -> f32x4 {                      // -Y_ii v
+            return -mfma16z(tile_ld(sm.YD[i][1], lane), cvt4(v));
+        };
+        // T_ij = Y_ij diag(beta_j), stored as T_ij^T in accumulator order:
+        // element (4 q4 + e, l15) of Y_ij goes to lane 16 (l15 >> 2) + 4 q4 + e
+        const float bj = sm.fbeta[16 * w + l15];
+        auto putT = [&](int i, int j, f32x4 y) {
+            bf16 *t = sm.TT + tri(i, j) * 256;
+            const int dl = 16 * (l15 >> 2) + 4 * q4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) t[4 * (dl + e) + (l15 & 3)] = (bf16)(y[e] * bj);
+        };
+        if (w == 0) {
+            const f32x4 y10 = fin(1, mfma16z(LTb(1, 0), YB(0)));
+            const f32x4 y20 = fin(2, mfma16(LTb(2, 1), cvt4(y10), mfma16z(LTb(2, 0), YB(0))));
+            const f32x4 y30 = fin(3, mfma16(LTb(3, 2), cvt4(y20),
+                                            mfma16(LTb(3, 1), cvt4(y10), mfma16z(LTb(3, 0), YB(0)))));
+            putT(1, 0, y10);
+            putT(2, 0, y20);
+            putT(3, 0, y30);
+        } else if (w == 1) {
+            const f32x4 y21 = fin(2, mfma16z(LTb(2, 1), YB(1)));
+            const f32x4 y31 = fin(3, mfma16(LTb(3, 2), cvt4(y21), mfma16z(LTb(3, 1), YB(1))));
+            putT(2, 1, y21);
+            putT(3, 1, y31);
+        } else {
+            putT(3, 2, fin(3, mfma16z(LTb(3, 2), YB(2))));
+        }
+    }
+    __syncthreads();
+
+    // ---- T to the workspace as six 1 KB operand pairs: pair (sb, kk) holds,
+    //      for lane l, lane l's values of blocks (sb, 2kk) and (sb, 2kk+1)
+    //      (zero above the diagonal), so that one 16-byte read per lane gives
+    //      the A operand of U = T X for row block sb and token blocks 2kk, 2kk+1
+    {
+        const size_t rec = (size_t)(ci * a.H + h) * kTileBytes;
+        bf16x8 *dst = reinterpret_cast<bf16x8 *>(static_cast<char *>(a.tiles) + rec);
+        for (int i = tid; i < 6 * 64; i += 256) {
+            const int pr = i >> 6, l = i & 63;
+            const int sb = pr < 2 ? pr : (pr < 4 ? 2 : 3);
+            const int kk = pr < 2 ? 0 : ((pr - 2) & 1);
+            const bf16x4 lo = tile_ld(sm.TT + tri(sb, 2 * kk) * 256, l);
+            const bf16x4 hi = 2 * kk + 1 <= sb ? tile_ld(sm.TT + tri(sb, 2 * kk + 1) * 256, l) : bf16x4{};
+            dst[i] = cat8(lo, hi);
+        }
+    }
+}
+
+// ===========================================================================
+// chain_kernel: the recurrence over chunks
+// ===========================================================================
+// Operand pair (sb, kk) of the T record: index in the six 1 KB pairs.
+__device__ inline int tpair(int sb, int kk) { return sb < 2 ? sb : 2 * sb - 2 + kk; }
+
 template <int D> struct ChainSmem {
-    // q and k rows in paired column order; a row stride of 8 x odd dwords
-    // keeps the 16-byte row fragment reads free of bank conflicts (and halves
-    // those of the transpose reads of k, against 4 x odd)
+    // k rows; a row stride of 8 x odd dwords keeps the 16-byte row fragment
+    // reads free of bank conflicts (and halves those of the transpose reads,
+    // against 4 x odd)
     static constexpr int PD = D + 16;
     static constexpr int KD = D / 32;
     // v slice rows [r][i]; a stride of 24 dwords puts the 8 rows that one
     // transpose load touches per half-wave on disjoint banks
     static constexpr int PV = BV + 16;
-    alignas(16) bf16 Q[2][C * PD];      // by chunk parity
-    alignas(16) bf16 K[3][C * PD];      // by chunk mod 3
-    alignas(16) bf16 V[2][C * PV];      // by chunk parity
-    alignas(16) bf16 TT[2][10 * 256];   // T_ij^T, i >= j, by chunk parity
-    alignas(16) bf16 PT[3][10 * 256];   // P_ij^T, i >= j, by chunk mod 3
-    alignas(16) bf16 LT[2][6 * 256];    // L_ij^T, i > j, by chunk parity
-    alignas(16) bf16 YD[4][2][256];     // Y_bb and Y_bb^T of the next chunk
-    alignas(16) bf16x8 SB[2][KD][64];   // S^T as paired B operands, per chain wave
-    alignas(16) bf16x8 UB[2][2][64];    // U as paired B operands, per chain wave
-    alignas(16) float fb[3][C];         // b_r, by chunk mod 3
-    alignas(16) float feb[3][C];        // e^{b_r}
-    alignas(16) float fhs[3][C];        // e^{b_C - b_r}
-    alignas(16) float fbeta[3][C];      // beta_r
-    alignas(16) float fgc[3][4];        // e^{b_C}
+    alignas(16) bf16 K[2][C * PD];      // by chunk parity
+    alignas(16) bf16 V[2][C * PV];
+    alignas(16) bf16x8 TT[2][6][64];    // T as operand pairs
+    alignas(16) bf16x8 SB[2][KD][64];   // S^T as operands, per chain wave
+    alignas(16) bf16x8 UB[2][2][64];    // U as operands, per chain wave
+    alignas(16) float fb[2][C];         // b_r
+    alignas(16) float feb[2][C];        // e^{b_r}
+    alignas(16) float fgc[2][4];        // e^{b_C}
 };
 
 template <int D>
-__global__ __launch_bounds__(NT, 1) void chain_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
     using Sm = ChainSmem<D>;
     constexpr int PD = Sm::PD;
     constexpr int PV = Sm::PV;
     constexpr int NTILE = D / BV;
-    constexpr int KD = Sm::KD;          // paired k steps over Dk
+    constexpr int KD = Sm::KD;          // 32-wide k steps over Dk
     constexpr int KS = D / 16;          // 16-row blocks of S^T
-    constexpr int CG = D / 8;           // 16-byte pieces per q or k row
-    constexpr int NPC = C * CG / 256;   // pieces per staging thread and matrix
-    static_assert(NPC >= 1 && (C * CG) % 256 == 0, "staging layout");
+    constexpr int CG = D / 8;           // 16-byte pieces per k row
+    // staged pieces (16 bytes) per chunk: k rows, v slice rows, T record
+    constexpr int NKP = C * CG, NVP = C * BV / 8, NTP = (int)(kTileBytes / 16);
+    constexpr int NST = NKP + NVP + NTP;
+    constexpr int NI = NST / 128;       // per staging thread
+    static_assert(NI * 128 == NST && NKP % 64 == 0 && NVP % 64 == 0, "staging layout");
+    static_assert(NTP == 6 * 64, "tile record layout");
     __shared__ Sm sm;
 
     // ---- work mapping: the Dv slices of one (sequence, head) share an XCD
@@ -106,13 +316,15 @@ __global__ __launch_bounds__(NT, 1) void chain_kernel(PrefillArgs a) {
     const int rank = unit / a.H;
     const int h = unit - rank * a.H;
     const int n = a.order ? a.order[rank] : rank;
-    long long t0, t1;
+    long long t0, t1, cbase;
     if (a.cu_seqlens) {
         t0 = a.cu_seqlens[n];
         t1 = a.cu_seqlens[n + 1];
+        cbase = a.chunk_base[n];
     } else {
         t0 = (long long)n * a.T;
         t1 = t0 + a.T;
+        cbase = (long long)n * ((a.T + C - 1) / C);
     }
     const int i0 = tile * BV;
     const size_t sslot = ((size_t)n * a.H + h) * D * D;
@@ -129,65 +341,73 @@ __global__ __launch_bounds__(NT, 1) void chain_kernel(PrefillArgs a) {
     const int lane = tid & 63;
     const int l15 = lane & 15, q4 = lane >> 4;
 
-    // rows of chunk c that exist (0 past the end and for the placeholder
-    // chunks c < 0 of the pipeline start); buffer extents cover just these,
-    // so loads of other rows return zeros and stores to them are dropped
+    // rows of chunk c that exist (0 past the end and for c < 0); buffer
+    // extents cover just these, so loads of other rows return zeros and
+    // stores to them are dropped
     auto valid_rows = [&](long long c) -> int {
         const long long rem = t1 - (t0 + c * C);
         return (c < 0 || rem <= 0) ? 0 : (rem < C ? (int)rem : C);
     };
-    // first token of chunk c (the sequence start for the placeholder chunks,
-    // whose extent is zero)
+    // first token of chunk c (the sequence start for c < 0, whose extent is 0)
     auto chunk_tok = [&](long long c) -> long long { return c < 0 ? t0 : t0 + c * C; };
     auto extent = [&](long long c, unsigned row_bytes) -> unsigned {
         const int Cc = valid_rows(c);
         return Cc ? (unsigned)(Cc - 1) * rowb + row_bytes : 0u;
     };
-    // A operand of U = T X (or P U): blocks (i, 2kk) and (i, 2kk+1) of a
-    // transposed block store; blocks above the diagonal are zero
-    auto tile_pair = [&](const bf16 *base, int i, int kk) -> bf16x8 {
-        const bf16x4 lo = tile_ld(base + tri(i, 2 * kk) * 256, lane);
-        const bf16x4 hi = (2 * kk + 1 <= i) ? tile_ld(base + tri(i, 2 * kk + 1) * 256, lane)
-                                            : bf16x4{};
-        return cat8(lo, hi);
-    };
+    // The k index of the state.  A 16x16x32 MFMA sums over k; lane l of a
+    // row-fragment operand (16 bytes of one k row) supplies k = 32 kk + 8 (l >> 4)
+    // + u, u = 0..7.  The S^T accumulator blocks are numbered so that the pair
+    // (2 kk, 2 kk + 1) supplies exactly these k as the other operand: block jk
+    // holds rows 32 (jk >> 1) + 8 q4 + 4 (jk & 1) + e of S^T in lane (q4, e).
+    auto srow = [&](int jk, int e) -> int { return 32 * (jk >> 1) + 8 * q4 + 4 * (jk & 1) + e; };
+    const std::integral_constant<int, 0> R0;
+    const std::integral_constant<int, 1> R1;
 
     if (w < 2) {
         // =================================================================
         // chain waves: value columns 16 ib .. 16 ib + 15 of the slice
         // =================================================================
         const int ib = w;
-        f32x4 St[KS];   // S^T[16 Jk + 4 q4 + e][16 ib + l15] (fp32)
+        f32x4 St[KS];   // S^T[srow(jk, e)][16 ib + l15] (fp32)
 #pragma unroll
         for (int jk = 0; jk < KS; ++jk) {
             St[jk] = f32x4{0.f, 0.f, 0.f, 0.f};
             if (a.h0) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    St[jk][e] = a.h0[sslot + (size_t)(i0 + 16 * ib + l15) * D + 16 * jk + 4 * q4 + e];
+                    St[jk][e] = a.h0[sslot + (size_t)(i0 + 16 * ib + l15) * D + srow(jk, e)];
             }
         }
         auto publish_state = [&]() {
 #pragma unroll
             for (int kk = 0; kk < KD; ++kk) sm.SB[ib][kk][lane] = acc_pair(St[2 * kk], St[2 * kk + 1]);
         };
+        // k row fragments of a chunk, read a phase ahead of their use
+        bf16x8 Kf[4][KD];
+        auto read_kf = [&](long long c) {
+            const bf16 *Kc = sm.K[(int)(c & 1)];
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+                for (int kk = 0; kk < KD; ++kk) Kf[rb][kk] = frag_rows(Kc, PD, 16 * rb, 32 * kk, lane);
+        };
         publish_state();
-        __syncthreads();                      // chunk 0 staged
-        __syncthreads();                      // A, P of chunk 0
-        __syncthreads();                      // diagonal blocks of T of chunk 0
-        int c3 = 0, c2 = 0;   // c mod 3, c mod 2
-        for (long long c = 0; c < nch; ++c, c3 = c3 == 2 ? 0 : c3 + 1, c2 ^= 1) {
-            const bf16 *Kc = sm.K[c3];
-            // ---- alpha: X = V - diag(e^b) K S^T; then the operands of the
-            //      state update (k rows are final since their staging), so the
-            //      update need not wait on LDS
-            f32x4 X[4];
-            bf16x8 KT[KS][2];
-            f32x4 hs[4];
-            float gC;
+        __syncthreads();                      // chunks 0 and 1 staged
+        read_kf(0);
+        for (long long c = 0; c < nch; ++c) {
+            const int par = (int)(c & 1);
+            const bf16 *Kc = sm.K[par];
+            // ---- alpha: X = V - diag(e^b) K S^T, U = T X and the state
+            //      update, with every LDS operand read here
+            f32x4 X[4], eb[4];
             {
-                const bf16 *Vc = sm.V[c2];
-                const float *feb = sm.feb[c3];
+                const bf16 *Vc = sm.V[par];
+                bf16x4 vv[4];
+#pragma unroll
+                for (int rb = 0; rb < 4; ++rb) {
+                    vv[rb] = frag_col4(Vc, PV, 16 * rb, 16 * ib, lane);
+                    eb[rb] = *reinterpret_cast<const f32x4 *>(&sm.feb[par][16 * rb + 4 * q4]);
+                }
                 bf16x8 Bs[KD];
 #pragma unroll
                 for (int kk = 0; kk < KD; ++kk) Bs[kk] = acc_pair(St[2 * kk], St[2 * kk + 1]);
@@ -195,16 +415,18 @@ __global__ __launch_bounds__(NT, 1) void chain_kernel(PrefillArgs a) {
                 for (int rb = 0; rb < 4; ++rb) {
                     f32x4 xk = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int kk = 0; kk < KD; ++kk)
-                        xk = mfma32(frag_rows(Kc, PD, 16 * rb, 32 * kk, lane), Bs[kk], xk);
-                    const f32x4 eb = *reinterpret_cast<const f32x4 *>(&feb[16 * rb + 4 * q4]);
-                    const bf16x4 vv = frag_col4(Vc, PV, 16 * rb, 16 * ib, lane);
+                    for (int kk = 0; kk < KD; ++kk) xk = mfma32(Kf[rb][kk], Bs[kk], xk);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) X[rb][e] = (float)vv[e] - eb[e] * xk[e];
+                    for (int e = 0; e < 4; ++e) X[rb][e] = (float)vv[rb][e] - eb[rb][e] * xk[e];
                 }
-                // A operand K^T[16 Jk + l15][s] by transpose loads of the k
-                // rows: lane j of each 16-lane group addresses the four stored
-                // columns that hold k columns 16 Jk + 4 (j & 3) .. +3
+            }
+            // A operand K^T[k][s] of the update by transpose loads of the k
+            // rows: lane j of each 16-lane group addresses k columns
+            // 32 (jk >> 1) + 8 (j & 3) + 4 (jk & 1) .. +3, so output lane i
+            // receives k = srow(jk, .) for row i of the block
+            bf16x8 KT[KS][2], Ta[4][2];
+            float gC;
+            {
 #pragma unroll
                 for (int jk = 0; jk < KS; ++jk) {
                     const int pc = 32 * (jk >> 1) + 8 * (l15 & 3) + 4 * (jk & 1);
@@ -216,21 +438,16 @@ __global__ __launch_bounds__(NT, 1) void chain_kernel(PrefillArgs a) {
                         KT[jk][kk] = cat8(__builtin_bit_cast(bf16x4, lo), __builtin_bit_cast(bf16x4, hi));
                     }
                 }
-                const float *fhs = sm.fhs[c3];
-#pragma unroll
-                for (int sb = 0; sb < 4; ++sb) hs[sb] = *reinterpret_cast<const f32x4 *>(&fhs[16 * sb + 4 * q4]);
-                gC = sm.fgc[c3][0];
-            }
-            __syncthreads();
-            // ---- beta: U = T X, S^T <- e^{b_C} S^T + K^T diag(e^{b_C - b}) U
-            {
-                const bf16 *TTc = sm.TT[c2];
-                bf16x8 Ta[4][2];
 #pragma unroll
                 for (int sb = 0; sb < 4; ++sb) {
-                    Ta[sb][0] = tile_pair(TTc, sb, 0);
-                    Ta[sb][1] = sb >= 2 ? tile_pair(TTc, sb, 1) : bf16x8{};
+                    Ta[sb][0] = sm.TT[par][tpair(sb, 0)][lane];
+                    Ta[sb][1] = sb >= 2 ? sm.TT[par][tpair(sb, 1)][lane] : bf16x8{};
                 }
+                gC = sm.fgc[par][0];
+            }
+            // U = T X, S^T <- e^{b_C} S^T + K^T diag(e^{b_C - b}) U
+            bf16x8 Ub[2];
+            {
                 const bf16x8 Bx[2] = {acc_pair(X[0], X[1]), acc_pair(X[2], X[3])};
                 f32x4 U[4];
 #pragma unroll
@@ -238,11 +455,13 @@ __global__ __launch_bounds__(NT, 1) void chain_kernel(PrefillArgs a) {
                     U[sb] = mfma32z(Ta[sb][0], Bx[0]);
                     if (sb >= 2) U[sb] = mfma32(Ta[sb][1], Bx[1], U[sb]);
                 }
-                sm.UB[ib][0][lane] = acc_pair(U[0], U[1]);
-                sm.UB[ib][1][lane] = acc_pair(U[2], U[3]);
-                f32x4 Uh[4];
+                Ub[0] = acc_pair(U[0], U[1]);
+                Ub[1] = acc_pair(U[2], U[3]);
+                f32x4 Uh[4];   // e^{b_C - b_s} = e^{b_C} / e^{b_s}
 #pragma unroll
-                for (int sb = 0; sb < 4; ++sb) Uh[sb] = U[sb] * hs[sb];
+                for (int sb = 0; sb < 4; ++sb)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) Uh[sb][e] = U[sb][e] * (gC * __builtin_amdgcn_rcpf(eb[sb][e]));
                 const bf16x8 Bh[2] = {acc_pair(Uh[0], Uh[1]), acc_pair(Uh[2], Uh[3])};
 #pragma unroll
                 for (int jk = 0; jk < KS; ++jk) {
@@ -251,8 +470,13 @@ __global__ __launch_bounds__(NT, 1) void chain_kernel(PrefillArgs a) {
                     sv = mfma32(KT[jk][1], Bh[1], sv);
                     St[jk] = sv;
                 }
-                publish_state();
             }
+            __syncthreads();
+            // ---- beta: publish U and S^T; k fragments of the next chunk
+            sm.UB[ib][0][lane] = Ub[0];
+            sm.UB[ib][1][lane] = Ub[1];
+            publish_state();
+            read_kf(c + 1);
             __syncthreads();
         }
         __syncthreads();                      // outputs of the last chunk
@@ -262,327 +486,224 @@ __global__ __launch_bounds__(NT, 1) void chain_kernel(PrefillArgs a) {
             for (int jk = 0; jk < KS; ++jk)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    a.ht[sslot + (size_t)(i0 + 16 * ib + l15) * D + 16 * jk + 4 * q4 + e] = St[jk][e];
+                    a.ht[sslot + (size_t)(i0 + 16 * ib + l15) * D + srow(jk, e)] = St[jk][e];
         }
         return;
     }
 
-    // =====================================================================
-    // waves 2..7
-    // =====================================================================
-    // ---- staging (waves 4..7): q, k, v of one chunk, a chunk ahead
-    const int tl = tid - 256;
-    bf16x8 rq[NPC], rk[NPC], rv;
-    float rg = 0.f, rbt = 0.f;
+    if (w >= 4 && w < 6) {
+        // =================================================================
+        // staging waves: k rows, the v slice and the T record of chunk c+2
+        // into LDS during beta of iteration c, from registers loaded during
+        // alpha of iteration c-1 (two register sets); the gate prefix sums
+        // =================================================================
+        const int tl = tid - 256;
+        bf16x8 rs[2][NI];
+        float rg[2];
+        auto st_load = [&](long long c, auto S) {
+            constexpr int r = decltype(S)::value;
+            const size_t base = (size_t)chunk_tok(c) * tokstride;
+            const rsrc_t rks = make_rsrc(kg + base, extent(c, D * 2));
+            const rsrc_t rvs = make_rsrc(vg + base, extent(c, BV * 2));
+            const bool have = valid_rows(c) > 0 && cbase + c < a.max_chunks;
+            const size_t rec = (size_t)((have ? cbase + c : 0) * a.H + h) * kTileBytes;
+            const rsrc_t rts = make_rsrc(static_cast<const char *>(a.tiles) + rec,
+                                         have ? (unsigned)kTileBytes : 0u);
 #pragma unroll
-    for (int i = 0; i < NPC; ++i) rq[i] = rk[i] = bf16x8{};
-    rv = bf16x8{};
-    // stored chunk m of a row (8 values in paired order) holds columns
-    // 32(m>>2) + 4(m&3) .. +3 and the same 16 further on
-    auto chunk_col = [](int m) -> int { return 32 * (m >> 2) + 4 * (m & 3); };
-    auto stage_load = [&](long long c) {
-        const size_t base = (size_t)chunk_tok(c) * tokstride;
-        const rsrc_t rqs = make_rsrc(qg + base, extent(c, D * 2));
-        const rsrc_t rks = make_rsrc(kg + base, extent(c, D * 2));
-#pragma unroll
-        for (int i = 0; i < NPC; ++i) {
-            const int p = i * 256 + tl;
-            const unsigned off = (p / CG) * rowb + 2 * chunk_col(p % CG);
-            rq[i] = cat8(bload8(rqs, off), bload8(rqs, off + 32));
-            rk[i] = cat8(bload8(rks, off), bload8(rks, off + 32));
-        }
-        // v slice: 64 rows x 4 pieces of 8 values
-        rv = bload16(make_rsrc(vg + base, extent(c, BV * 2)), (tl >> 2) * rowb + 16 * (tl & 3));
-        if (w == 4) {   // gate log and beta of row `lane`
+            for (int i = 0; i < NI; ++i) {
+                const int p0 = i * 128 + 64 * (w - 4);   // this wave's first piece
+                const int p = i * 128 + tl;
+                if (p0 < NKP) {
+                    rs[r][i] = bload16(rks, (p / CG) * rowb + 16 * (p % CG));
+                } else if (p0 < NKP + NVP) {
+                    const int pv = p - NKP;
+                    rs[r][i] = bload16(rvs, (pv >> 2) * rowb + 16 * (pv & 3));
+                } else {
+                    rs[r][i] = bload16(rts, 16 * (p - NKP - NVP));
+                }
+            }
+            // gate log of row `lane` (both waves load it; wave 4 keeps it)
             const unsigned hb = (unsigned)(a.H * 4);
             const int Cc = valid_rows(c);
             const unsigned gext = Cc ? (unsigned)(Cc - 1) * hb + 4 : 0u;
-            const size_t gbase = (size_t)chunk_tok(c) * a.H + h;
-            rg = bload4(make_rsrc(a.g + gbase, gext), lane * hb);
-            rbt = bload4(make_rsrc(a.beta + gbase, gext), lane * hb);
-        }
-    };
-    auto stage_store = [&](long long c, int s3) {   // s3 = c mod 3
-        bf16 *Qd = sm.Q[c & 1];
-        bf16 *Kd = sm.K[s3];
+            rg[r] = bload4(make_rsrc(a.g + (size_t)chunk_tok(c) * a.H + h, gext), lane * hb);
+        };
+        auto st_store = [&](long long c, auto S) {
+            constexpr int r = decltype(S)::value;
+            const int par = (int)(c & 1);
 #pragma unroll
-        for (int i = 0; i < NPC; ++i) {
-            const int p = i * 256 + tl;
-            const int o = (p / CG) * PD + 8 * (p % CG);
-            *reinterpret_cast<bf16x8 *>(&Qd[o]) = rq[i];
-            *reinterpret_cast<bf16x8 *>(&Kd[o]) = rk[i];
-        }
-        *reinterpret_cast<bf16x8 *>(&sm.V[c & 1][(tl >> 2) * PV + 8 * (tl & 3)]) = rv;
-        if (w == 4) {   // inclusive prefix sum of the gate logs over the chunk
-            const float b = wave_prefix_sum(rg);
-            const float bC = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, b), 63));
-            sm.fb[s3][lane] = b;
-            sm.feb[s3][lane] = ex(b);
-            sm.fhs[s3][lane] = ex(bC - b);
-            sm.fbeta[s3][lane] = rbt;
-            if (lane == 0) sm.fgc[s3][0] = ex(bC);
-        }
-    };
-
-    // ---- A, P blocks (waves 2, 3, 6, 7)
-    auto frags = [&](const bf16 *M, int blk, bf16x8 (&f)[KD]) {
-#pragma unroll
-        for (int kk = 0; kk < KD; ++kk) f[kk] = frag_rows(M, PD, 16 * blk, 32 * kk, lane);
-    };
-    // G = K_J K_I^T and R = K_J Q_I^T: lane holds s = 16J + 4 q4 + e, r = 16I + l15
-    auto products = [&](const bf16x8 (&kj)[KD], const bf16x8 (&ki)[KD], const bf16x8 (&qi)[KD],
-                        f32x4 &g, f32x4 &p) {
-        g = p = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < KD; ++kk) {
-            g = mfma32(kj[kk], ki[kk], g);
-            p = mfma32(kj[kk], qi[kk], p);
-        }
-    };
-    // gate and beta factors of block (I, J): b_r and beta_r of row r = 16I + l15,
-    // b_s and beta_s of rows s = 16J + 4 q4 .. +3 (read ahead of the MFMAs)
-    struct BlockF { float br, betar; f32x4 bs, betas; };
-    auto load_fac = [&](int I, int J, const float *fbv, const float *fbt) -> BlockF {
-        BlockF f;
-        f.br = fbv[16 * I + l15];
-        f.betar = fbt[16 * I + l15];
-        f.bs = *reinterpret_cast<const f32x4 *>(&fbv[16 * J + 4 * q4]);
-        f.betas = *reinterpret_cast<const f32x4 *>(&fbt[16 * J + 4 * q4]);
-        return f;
-    };
-    // off-diagonal block (I > J): P_IJ^T and L_IJ^T into LDS
-    auto put_offdiag = [&](int I, int J, f32x4 g, f32x4 p, const BlockF &F, bf16 *PTn, bf16 *LTn) {
-        f32x4 pv, lv;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float f = ex(F.br - F.bs[e]);
-            pv[e] = f * p[e];
-            lv[e] = F.betar * f * g[e];
-        }
-        tile_st(PTn + tri(I, J) * 256, lane, pv);
-        tile_st(LTn + ltri(I, J) * 256, lane, lv);
-    };
-    // diagonal block b: P_bb^T into LDS; M = L_bb as acc(M^T), acc(M) (the
-    // Gram block is symmetric, so both come from the one product)
-    auto diag_prep = [&](int b, f32x4 g, f32x4 p, const BlockF &F, bf16 *PTn, f32x4 &MT, f32x4 &Mn) {
-        const int rl = l15;
-        f32x4 pv;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int sl = 4 * q4 + e;
-            const float d = F.br - F.bs[e];
-            const float f = ex(sl <= rl ? d : -d);
-            pv[e] = sl <= rl ? f * p[e] : 0.f;
-            MT[e] = sl < rl ? F.betar * f * g[e] : 0.f;
-            Mn[e] = sl > rl ? F.betas[e] * f * g[e] : 0.f;
-        }
-        tile_st(PTn + tri(b, b) * 256, lane, pv);
-    };
-    // Y_bb = (I + M)^{-1} = (I - M)(I + M^2)(I + M^4)(I + M^8) and Y_bb^T; an
-    // MFMA with A operand acc(X^T) and B operand acc(Y) yields acc(X Y)
-    auto diag_invert = [&](int b, f32x4 MT, f32x4 Mn, f32x4 betas, bf16 *TTn) {
-        f32x4 I4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) I4[e] = 4 * q4 + e == l15 ? 1.f : 0.f;
-        const f32x4 IMn = I4 - Mn, IMT = I4 - MT;
-        const f32x4 M2 = mfma16z(cvt4(MT), cvt4(Mn));
-        const f32x4 M2T = mfma16z(cvt4(Mn), cvt4(MT));
-        const f32x4 Z1 = mfma16(cvt4(M2T), cvt4(IMn), IMn);
-        const f32x4 Z1T = mfma16(cvt4(M2), cvt4(IMT), IMT);
-        const f32x4 M4 = mfma16z(cvt4(M2T), cvt4(M2));
-        const f32x4 M4T = mfma16z(cvt4(M2), cvt4(M2T));
-        const f32x4 Z2 = mfma16(cvt4(M4T), cvt4(Z1), Z1);
-        const f32x4 Z2T = mfma16(cvt4(M4), cvt4(Z1T), Z1T);
-        const f32x4 M8 = mfma16z(cvt4(M4T), cvt4(M4));
-        const f32x4 M8T = mfma16z(cvt4(M4), cvt4(M4T));
-        const f32x4 Y = mfma16(cvt4(M8T), cvt4(Z2), Z2);
-        const f32x4 YT = mfma16(cvt4(M8), cvt4(Z2T), Z2T);
-        tile_st(sm.YD[b][0], lane, Y);
-        tile_st(sm.YD[b][1], lane, YT);
-        tile_st(TTn + tri(b, b) * 256, lane, YT * betas);   // T_bb^T = diag(beta) Y_bb^T
-    };
-    // ---- outputs (waves 4, 5): O^T = scale (S Q^T diag(e^b) + U^T P^T), so
-    //      that a lane ends up with four adjacent columns of one output row;
-    //      the published S^T and U operands serve as A operands here and the
-    //      q rows and P blocks as B operands
-    const int ob = w & 1;          // value block of the output waves
-    f32x4 QS[4];                   // (Q S^T)^T[16 ob + 4 q4 + e][16 rb + l15]
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) QS[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // one alpha of the output waves: O of chunk c-1 (QS kept from the previous
-    // alpha, U and P published since) and QS of chunk c; every LDS operand is
-    // read before the first MFMA so the reads overlap
-    auto out_step = [&](long long c, int p3, int c3, int cpar) {
-        const bf16 *PTp = sm.PT[p3];
-        const bf16 *Qc = sm.Q[cpar];
-        const bf16x8 Au0 = sm.UB[ob][0][lane], Au1 = sm.UB[ob][1][lane];
-        bf16x8 Pb[4][2], As[KD], Qb[4][KD];
-        float ebr[4];
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-            Pb[rb][0] = tile_pair(PTp, rb, 0);
-            Pb[rb][1] = rb >= 2 ? tile_pair(PTp, rb, 1) : bf16x8{};
-            ebr[rb] = sm.feb[c3][16 * rb + l15];
-#pragma unroll
-            for (int kk = 0; kk < KD; ++kk) Qb[rb][kk] = frag_rows(Qc, PD, 16 * rb, 32 * kk, lane);
-        }
-#pragma unroll
-        for (int kk = 0; kk < KD; ++kk) As[kk] = sm.SB[ob][kk][lane];
-        __builtin_amdgcn_sched_barrier(0);
-        // O^T of chunk c-1 = QS + U^T P^T, stored as rows
-        const rsrc_t ro = make_rsrc(og + (size_t)chunk_tok(c - 1) * tokstride, extent(c - 1, BV * 2));
-        const unsigned voff = l15 * rowb + 2 * (16 * ob + 4 * q4);
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-            f32x4 o = mfma32(Au0, Pb[rb][0], QS[rb]);
-            if (rb >= 2) o = mfma32(Au1, Pb[rb][1], o);
-            bstore8s(ro, voff, 16 * rb * rowb, cvt4(o * a.scale));
-        }
-        // (diag(e^b) Q S^T)^T of chunk c, S entering chunk c
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-            f32x4 x = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < KD; ++kk) x = mfma32(As[kk], Qb[rb][kk], x);
-            QS[rb] = x * ebr[rb];
-        }
-    };
-
-    // diagonal block of this wave (waves 2, 3, 6, 7), carried from alpha to beta
-    const int db = (w & 1) + ((w >> 2) << 1);   // w2 -> 0, w3 -> 1, w6 -> 2, w7 -> 3
-    f32x4 dMT = {0.f, 0.f, 0.f, 0.f}, dMn = dMT;
-
-    if (w >= 4) {
-        stage_load(0);
-        stage_store(0, 0);
-        stage_load(1);
-        // let the loop be entered with nothing in flight, so the waits inside
-        // it follow only the loop's own loads
-        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-    }
-    __syncthreads();
-    // chunk indices mod 3 and parities of c-1, c, c+1, c+2 (c = -1 first);
-    // the output waves and the waves forming T run separate loops with the
-    // same barriers, like the chain waves, to keep their registers apart
-    int pm3 = 1, cm3 = 2, nm3 = 0, sm3 = 1;
-    int cpar = 1;
-    auto advance = [&]() {
-        pm3 = cm3;
-        cm3 = nm3;
-        nm3 = sm3;
-        sm3 = sm3 == 2 ? 0 : sm3 + 1;
-        cpar ^= 1;
-    };
-    if (w == 4 || w == 5) {
-        for (long long c = -1; c <= nch; ++c) {
-            out_step(c, pm3, cm3, cpar);
+            for (int i = 0; i < NI; ++i) {
+                const int p0 = i * 128 + 64 * (w - 4);
+                const int p = i * 128 + tl;
+                if (p0 < NKP) {
+                    *reinterpret_cast<bf16x8 *>(&sm.K[par][(p / CG) * PD + 8 * (p % CG)]) = rs[r][i];
+                } else if (p0 < NKP + NVP) {
+                    const int pv = p - NKP;
+                    *reinterpret_cast<bf16x8 *>(&sm.V[par][(pv >> 2) * PV + 8 * (pv & 3)]) = rs[r][i];
+                } else {
+                    (&sm.TT[par][0][0])[p - NKP - NVP] = rs[r][i];
+                }
+            }
+            if (w == 4) {   // inclusive prefix sum of the gate logs over the chunk
+                const float b = wave_prefix_sum(rg[r]);
+                const float bC = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, b), 63));
+                sm.fb[par][lane] = b;
+                sm.feb[par][lane] = ex(b);
+                if (lane == 0) sm.fgc[par][0] = ex(bC);
+            }
+        };
+        st_load(0, R0);
+        st_store(0, R0);
+        st_load(1, R0);
+        st_store(1, R0);
+        st_load(2, R0);
+        __syncthreads();
+        for (long long c = 0;; c += 2) {
+            st_load(c + 3, R1);
             __syncthreads();
-            stage_store(c + 2, sm3);
-            stage_load(c + 3);
+            st_store(c + 2, R0);
             __syncthreads();
-            advance();
+            if (c + 1 > nch) break;
+            st_load(c + 4, R0);
+            __syncthreads();
+            st_store(c + 3, R1);
+            __syncthreads();
+            if (c + 2 > nch) break;
         }
         return;
     }
-    for (long long c = -1; c <= nch; ++c) {
-        const int npar = cpar ^ 1;
-        const bf16 *Kn = sm.K[nm3];
-        const bf16 *Qn = sm.Q[npar];
-        const float *fbv = sm.fb[nm3];
-        const float *fbt = sm.fbeta[nm3];
-        bf16 *PTn = sm.PT[nm3];
-        // ---------------- alpha: T off the diagonal of chunk c (its diagonal
-        // blocks and L came from the previous iteration); diagonal block db of
-        // the A and P blocks of chunk c+1.  Every LDS operand first. --------
-        BlockF Fd;
-        {
-            const bf16 *LTc = sm.LT[cpar];
-            bf16x4 lt[6], yb[3], ya[3];
+
+    // =====================================================================
+    // output waves: row block RB of the chunk (waves 2, 3, 7, 6 take 0, 1, 2,
+    // 3, so each of SIMDs 2 and 3 carries 1 + 4 or 2 + 3 blocks of P), both
+    // value blocks.  O^T = scale (S Q^T diag(e^b) + U^T P^T) so that a lane
+    // ends up with four adjacent columns of one output row: the published
+    // S^T and U serve as A operands, the q rows and P^T as B operands.  P^T
+    // is formed in accumulator registers, so it feeds the MFMA directly.
+    // Iteration c, alpha: O of chunk c-1, QS and P of chunk c; beta: the q
+    // rows of chunk c+2, from global memory straight into registers.
+    // =====================================================================
+    auto out_loop = [&](auto RBc) {
+        constexpr int RB = decltype(RBc)::value;
+        constexpr int NP2 = (RB + 2) / 2;   // pairs of 16-token blocks J <= RB
+        bf16x8 Qr[2][KD];                   // q rows 16 RB + l15, two chunks
+        bf16x8 Pp[NP2];                     // P^T of the previous chunk, as B operand pairs
+        f32x4 QSp[2];                       // (Q S^T)^T[16 ob + 4 q4 + e][16 RB + l15], scaled by e^b
+        auto q_load = [&](long long c, auto S) {
+            constexpr int r = decltype(S)::value;
+            const rsrc_t rq = make_rsrc(qg + (size_t)chunk_tok(c) * tokstride, extent(c, D * 2));
+            const unsigned off = (16 * RB + l15) * rowb + 16 * q4;
 #pragma unroll
-            for (int t = 0; t < 6; ++t) lt[t] = tile_ld(LTc + t * 256, lane);
+            for (int kk = 0; kk < KD; ++kk) Qr[r][kk] = bload16(rq, off + 64 * kk);
+        };
+        auto iter = [&](long long c, auto S) {
+            constexpr int r = decltype(S)::value;
+            const int par = (int)(c & 1);
+            const bf16 *Kc = sm.K[par];
+            bf16x8 Au[2][NP2], As[2][KD], Kj[RB + 1][KD];
+            f32x4 bsJ[RB + 1];
 #pragma unroll
-            for (int t = 0; t < 3; ++t) {
-                yb[t] = tile_ld(sm.YD[t][0], lane);        // B operand Y_tt
-                ya[t] = tile_ld(sm.YD[t + 1][1], lane);    // acc(Y^T): A operand Y_{t+1,t+1}
+            for (int ob = 0; ob < 2; ++ob) {
+#pragma unroll
+                for (int k2 = 0; k2 < NP2; ++k2) Au[ob][k2] = sm.UB[ob][k2][lane];
+#pragma unroll
+                for (int kk = 0; kk < KD; ++kk) As[ob][kk] = sm.SB[ob][kk][lane];
             }
-            bf16x8 kd[KD], qd[KD];
-            frags(Kn, db, kd);
-            frags(Qn, db, qd);
-            Fd = load_fac(db, db, fbv, fbt);
-            // beta_j of the off-diagonal blocks this wave forms: j = 0 (w2),
-            // 1 (w3), 2 (w6)
-            const float bj = sm.fbeta[cm3][16 * (w == 2 ? 0 : (w == 3 ? 1 : 2)) + l15];
-            __builtin_amdgcn_sched_barrier(0);
-            if (c >= 0 && w != 7) {
-                // Y_ij = -Y_ii sum_k L_ik Y_kj; T_ij = Y_ij diag(beta_j) stored as
-                // T_ij^T in accumulator order: element (4 q4 + e, l15) of Y_ij
-                // goes to lane 16 (l15 >> 2) + 4 q4 + e
-                bf16 *TTc = sm.TT[cpar];
-                auto fin = [&](int i, f32x4 v) -> f32x4 { return -mfma16z(ya[i - 1], cvt4(v)); };
-                auto putT = [&](int i, int j, f32x4 y) {
-                    bf16 *t = TTc + tri(i, j) * 256;
-                    const int dl = 16 * (l15 >> 2) + 4 * q4;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) t[4 * (dl + e) + (l15 & 3)] = (bf16)(y[e] * bj);
-                };
-                // L_ij^T blocks: (1,0) 0, (2,0) 1, (2,1) 2, (3,0) 3, (3,1) 4, (3,2) 5
-                if (w == 2) {
-                    const f32x4 y10 = fin(1, mfma16z(lt[0], yb[0]));
-                    const f32x4 y20 = fin(2, mfma16(lt[2], cvt4(y10), mfma16z(lt[1], yb[0])));
-                    const f32x4 y30 = fin(3, mfma16(lt[5], cvt4(y20),
-                                                    mfma16(lt[4], cvt4(y10), mfma16z(lt[3], yb[0]))));
-                    putT(1, 0, y10);
-                    putT(2, 0, y20);
-                    putT(3, 0, y30);
-                } else if (w == 3) {
-                    const f32x4 y21 = fin(2, mfma16z(lt[2], yb[1]));
-                    const f32x4 y31 = fin(3, mfma16(lt[5], cvt4(y21), mfma16z(lt[4], yb[1])));
-                    putT(2, 1, y21);
-                    putT(3, 1, y31);
-                } else {
-                    putT(3, 2, fin(3, mfma16z(lt[5], yb[2])));
+            for (int J = 0; J <= RB; ++J) {
+#pragma unroll
+                for (int kk = 0; kk < KD; ++kk) Kj[J][kk] = frag_rows(Kc, PD, 16 * J, 32 * kk, lane);
+                bsJ[J] = *reinterpret_cast<const f32x4 *>(&sm.fb[par][16 * J + 4 * q4]);
+            }
+            const float ebr = sm.feb[par][16 * RB + l15];
+            const float br = sm.fb[par][16 * RB + l15];
+            __builtin_amdgcn_sched_barrier(0);
+            // O of chunk c-1
+            const rsrc_t ro = make_rsrc(og + (size_t)chunk_tok(c - 1) * tokstride, extent(c - 1, BV * 2));
+            const unsigned voff = l15 * rowb + 8 * q4;
+#pragma unroll
+            for (int ob = 0; ob < 2; ++ob) {
+                f32x4 o = QSp[ob];
+#pragma unroll
+                for (int k2 = 0; k2 < NP2; ++k2) o = mfma32(Au[ob][k2], Pp[k2], o);
+                bstore8s(ro, voff + 32 * ob, 16 * RB * rowb, cvt4(o * a.scale));
+            }
+            // diag(e^b) Q S^T of chunk c (S entering chunk c)
+#pragma unroll
+            for (int ob = 0; ob < 2; ++ob) {
+                f32x4 x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < KD; ++kk) x = mfma32(As[ob][kk], Qr[r][kk], x);
+                QSp[ob] = x * ebr;
+            }
+            // P of chunk c: K_J Q_RB^T gives lane s = 16 J + 4 q4 + e,
+            // r = 16 RB + l15, and P[r][s] = e^{b_r - b_s} q_r.k_s for s <= r
+            f32x4 pv[RB + 2];
+#pragma unroll
+            for (int J = 0; J <= RB; ++J) {
+                f32x4 p = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < KD; ++kk) p = mfma32(Kj[J][kk], Qr[r][kk], p);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float v = ex(br - bsJ[J][e]) * p[e];
+                    pv[J][e] = (J < RB || 4 * q4 + e <= l15) ? v : 0.f;
                 }
             }
-            f32x4 g, p;
-            products(kd, kd, qd, g, p);
-            diag_prep(db, g, p, Fd, PTn, dMT, dMn);
-        }
+            pv[RB + 1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int k2 = 0; k2 < NP2; ++k2) Pp[k2] = acc_pair(pv[2 * k2], pv[2 * k2 + 1]);
+        };
+        q_load(0, R0);
+        q_load(1, R1);
+        QSp[0] = QSp[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k2 = 0; k2 < NP2; ++k2) Pp[k2] = bf16x8{};
         __syncthreads();
-        // ---------------- beta: staging (its loads are long done), then the
-        // diagonal inverses of chunk c+1 and its off-diagonal A, P blocks:
-        // w2: (1,0), (3,0)  w3: (2,1), (3,1)  w6: (2,0)  w7: (3,2) ----------
-        if (w >= 6) {
-            stage_store(c + 2, sm3);
-            stage_load(c + 3);
+        for (long long c = 0;; c += 2) {
+            iter(c, R0);
+            __syncthreads();
+            q_load(c + 2, R0);
+            __syncthreads();
+            if (c + 1 > nch) break;
+            iter(c + 1, R1);
+            __syncthreads();
+            q_load(c + 3, R1);
+            __syncthreads();
+            if (c + 2 > nch) break;
         }
-        {
-            bf16 *LTn = sm.LT[npar];
-            const int J = db < 2 ? db : (db == 2 ? 0 : 2);   // 0, 1, 0, 2
-            const int I0 = db < 2 ? db + 1 : (db == 2 ? 2 : 3);
-            bf16x8 kj[KD], ki[KD], qi[KD], k3[KD], q3[KD];
-            frags(Kn, J, kj);
-            frags(Kn, I0, ki);
-            frags(Qn, I0, qi);
-            const BlockF F0 = load_fac(I0, J, fbv, fbt);
-            BlockF F3 = F0;
-            if (db < 2) {
-                frags(Kn, 3, k3);
-                frags(Qn, 3, q3);
-                F3 = load_fac(3, J, fbv, fbt);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            diag_invert(db, dMT, dMn, Fd.betas, sm.TT[npar]);
-            f32x4 g, p;
-            products(kj, ki, qi, g, p);
-            put_offdiag(I0, J, g, p, F0, PTn, LTn);
-            if (db < 2) {
-                products(kj, k3, q3, g, p);
-                put_offdiag(3, J, g, p, F3, PTn, LTn);
-            }
-        }
+    };
+    if (w == 2)      out_loop(std::integral_constant<int, 0>{});
+    else if (w == 3) out_loop(std::integral_constant<int, 1>{});
+    else if (w == 7) out_loop(std::integral_constant<int, 2>{});
+    else             out_loop(std::integral_constant<int, 3>{});
+}
+
+// First chunk of every packed sequence: base[n] = sum over m < n of
+// ceil(len_m / C), base[N] = the total.  One workgroup: each thread sums a
+// run of consecutive sequences, then an exclusive scan over the 256 runs.
+__global__ __launch_bounds__(256) void chunk_base_kernel(const int32_t *cu, int N, int32_t *base) {
+    __shared__ int part[256];
+    const int t = threadIdx.x;
+    const int per = (N + 255) / 256;
+    const int m0 = t * per < N ? t * per : N;
+    const int m1 = m0 + per < N ? m0 + per : N;
+    int s = 0;
+    for (int m = m0; m < m1; ++m) s += (cu[m + 1] - cu[m] + C - 1) / C;
+    part[t] = s;
+    __syncthreads();
+    for (int d = 1; d < 256; d <<= 1) {   // inclusive scan (Hillis-Steele)
+        const int x = t >= d ? part[t - d] : 0;
         __syncthreads();
-        advance();
+        part[t] += x;
+        __syncthreads();
     }
+    int acc = part[t] - s;                // exclusive
+    for (int m = m0; m < m1; ++m) {
+        base[m] = acc;
+        acc += (cu[m + 1] - cu[m] + C - 1) / C;
+    }
+    if (t == 255) base[N] = part[255];
 }
 
 }  // namespace
@@ -590,9 +711,23 @@ __global__ __launch_bounds__(NT, 1) void chain_kernel(PrefillArgs a) {
 hipError_t launch_prefill_chain(int D, const PrefillArgs &a, hipStream_t s) {
     const long long units = (long long)a.N * a.H;
     if (units <= 0) return hipSuccess;
+    if (a.cu_seqlens) {
+        hipLaunchKernelGGL(chunk_base_kernel, dim3(1), dim3(256), 0, s, a.cu_seqlens, a.N,
+                           a.chunk_base);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const long long prep_blocks = a.max_chunks * a.H;
+    if (prep_blocks > 0) {
+        dim3 grid((unsigned)prep_blocks), block(256);
+        if (D == 128) hipLaunchKernelGGL((prep_kernel<128>), grid, block, 0, s, a);
+        else          hipLaunchKernelGGL((prep_kernel<64>), grid, block, 0, s, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     const int ntile = D / BV;
     const long long blocks = ((units + 7) / 8) * 8 * ntile;
-    dim3 grid((unsigned)blocks), block(NT);
+    dim3 grid((unsigned)blocks), block(512);
     if (D == 128) hipLaunchKernelGGL((chain_kernel<128>), grid, block, 0, s, a);
     else          hipLaunchKernelGGL((chain_kernel<64>), grid, block, 0, s, a);
     return hipGetLastError();

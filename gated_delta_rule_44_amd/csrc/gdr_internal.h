@@ -67,10 +67,17 @@ struct PrefillArgs {
     float *ht;                    // [N, H, D, D] or nullptr
     const int32_t *cu_seqlens;    // [N+1] or nullptr (fixed length)
     const int32_t *order;         // schedule [N] or nullptr (identity)
+    int32_t *chunk_base;          // varlen: first chunk of each sequence [N+1] (written)
+    void *tiles;                  // scalar gate: one kTileBytes record per (chunk, head)
+    long long max_chunks;         // chunk records per head in tiles
     int N, T, H;                  // T used only when cu_seqlens == nullptr
     float scale;
     int channel_gate;
 };
+
+// Per (chunk, head) record of the scalar-gate chunked prefill's workspace:
+// T as six 1 KB MFMA operand pairs of its 16x16 blocks (bf16).
+constexpr size_t kTileBytes = 6 * 1024;
 
 hipError_t launch_prefill_recurrent(bool bf16_io, int D, const PrefillArgs &a,
                                     hipStream_t s);

@@ -62,11 +62,17 @@ enum gdr_gate { GDR_GATE_SCALAR = 0, GDR_GATE_CHANNEL = 1 };
 enum gdr_mixer { GDR_FA = 0, GDR_SWA = 1, GDR_GDN = 2, GDR_KDA = 3 };
 
 /*
- * Device workspace (bytes) that gdr_prefill_chunked_varlen needs for N
- * packed sequences: a per-call schedule of N int32 entries, rounded up to
- * 256 bytes.  The fixed-length prefill needs none (returns 0 for N <= 0).
+ * Device workspace (bytes) that a prefill call over N sequences of `tokens`
+ * tokens in all (B and B*T for gdr_prefill_chunked, N and T_total for
+ * gdr_prefill_chunked_varlen) and H heads needs with this dtype and gate
+ * kind: the varlen schedule and chunk offsets (N and N+1 int32, each rounded
+ * up to 256 bytes) and, for bf16 with the scalar gate, the chunk-local
+ * inverse T of every chunk and head (6 KiB per chunk and head, for
+ * tokens / 64 + N chunks, an upper bound).  Returns 0 for N <= 0, tokens < 0
+ * or H <= 0.  A buffer of this size serves either call with these sizes.
  */
-size_t gdr_prefill_workspace_bytes(int N);
+size_t gdr_prefill_workspace_bytes(enum gdr_dtype dt, enum gdr_gate gk, int N,
+                                   long long tokens, int H);
 
 /*
  * Chunked prefill over a fixed-length batch: the recurrence above for every
@@ -86,6 +92,12 @@ size_t gdr_prefill_workspace_bytes(int N);
  *   o           [B, T, H, Dv]   dt (written)
  *   ht          [B, H, Dv, Dk] fp32 final states (written), or NULL.
  *               ht == h0 is allowed (in-place resume); no other aliasing.
+ *   workspace   device buffer, 16-byte aligned, of at least
+ *               gdr_prefill_workspace_bytes(dt, gk, B, B*T, H) bytes, used
+ *               only for bf16 with the scalar gate (otherwise ignored and may
+ *               be NULL); scratch for the duration of the call, not to be
+ *               shared with a concurrent call
+ *   ws_bytes    its size
  *   stream      hipStream_t
  *
  * bf16 inputs run the chunked form on MFMA (chunk of 64 tokens, WY/UT
@@ -100,7 +112,8 @@ gdr_status gdr_prefill_chunked(enum gdr_dtype dt, enum gdr_gate gk, int B, int T
                                int H, int Dk, int Dv, int chunk, float scale,
                                const void *q, const void *k, const void *v,
                                const float *g, const float *beta, const float *h0,
-                               void *o, float *ht, void *stream);
+                               void *o, float *ht, void *workspace, size_t ws_bytes,
+                               void *stream);
 
 /*
  * Chunked prefill over a packed variable-length batch.  Sequence n owns
@@ -116,9 +129,12 @@ gdr_status gdr_prefill_chunked(enum gdr_dtype dt, enum gdr_gate gk, int B, int T
  *   q, k              [T_total, H, Dk]   v, o [T_total, H, Dv]
  *   g                 [T_total, H] or [T_total, H, Dk] fp32;  beta [T_total, H]
  *   h0, ht            [N, H, Dv, Dk] fp32 (h0 may be NULL, ht may be NULL)
- *   workspace         device buffer of gdr_prefill_workspace_bytes(N) bytes;
- *                     the call writes its schedule there (longest sequence
- *                     first) and it must not be shared with a concurrent call
+ *   workspace         device buffer, 16-byte aligned, of at least
+ *                     gdr_prefill_workspace_bytes(dt, gk, N, T_total, H)
+ *                     bytes; the call writes its schedule (longest sequence
+ *                     first), the chunk offsets and (bf16, scalar gate) the
+ *                     chunk-local matrices there; it must not be shared with
+ *                     a concurrent call
  * Other arguments as gdr_prefill_chunked.  Only bf16 runs chunked; fp32
  * runs the recurrent form.  Without cu_seqlens_host, device offsets that
  * violate the rules above give undefined results.

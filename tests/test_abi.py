@@ -7,6 +7,7 @@ import re
 
 import numpy as np
 import pytest
+import torch
 
 import gated_delta_rule_44_amd as gdr
 
@@ -44,10 +45,17 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_version_and_workspace(lib):
     assert gdr.version().startswith("gdr")
-    assert gdr.workspace_bytes(0) == 0
-    assert gdr.workspace_bytes(1) == 256
-    assert gdr.workspace_bytes(64) == 256
-    assert gdr.workspace_bytes(65) == 512
+    bf, f32 = torch.bfloat16, torch.float32
+    # schedule and chunk offsets: N and N+1 int32, each rounded up to 256 bytes
+    assert gdr.workspace_bytes(f32, False, 0, 0, 4) == 0
+    assert gdr.workspace_bytes(f32, False, 1, 100, 4) == 512
+    assert gdr.workspace_bytes(bf, True, 64, 100, 4) == 256 + 512
+    assert gdr.workspace_bytes(f32, True, 65, 100, 4) == 512 + 512
+    assert gdr.workspace_bytes(f32, False, 2, 100, 0) == 0
+    # bf16, scalar gate: + 6 KiB of T per (chunk, head), for
+    # tokens // 64 + N chunks
+    assert gdr.workspace_bytes(bf, False, 1, 64, 1) == 512 + 2 * 6144
+    assert gdr.workspace_bytes(bf, False, 4, 4 * 4096, 16) == 512 + (256 + 4) * 16 * 6144
 
 
 F = ctypes.c_float
@@ -56,9 +64,10 @@ MIS = FAKE + 4          # misaligned
 
 
 def prefill(lib, dt=1, gk=0, B=1, T=64, H=1, Dk=128, Dv=128, chunk=64, q=FAKE,
-            k=FAKE, v=FAKE, g=FAKE, beta=FAKE, h0=None, o=FAKE, ht=FAKE):
+            k=FAKE, v=FAKE, g=FAKE, beta=FAKE, h0=None, o=FAKE, ht=FAKE, ws=FAKE,
+            ws_bytes=1 << 30):
     return lib.gdr_prefill_chunked(dt, gk, B, T, H, Dk, Dv, chunk, F(1.0), q, k,
-                                   v, g, beta, h0, o, ht, None)
+                                   v, g, beta, h0, o, ht, ws, ws_bytes, None)
 
 
 @pytest.mark.parametrize("kw,code,msg", [
@@ -75,6 +84,9 @@ def prefill(lib, dt=1, gk=0, B=1, T=64, H=1, Dk=128, Dv=128, chunk=64, q=FAKE,
     (dict(o=None), EINVAL, "o is NULL"),
     (dict(h0=MIS), EINVAL, "h0 is not 16-byte aligned"),
     (dict(h0=FAKE, ht=FAKE + 256), EINVAL, "overlap"),
+    (dict(ws=None), EINVAL, "workspace of 12800 bytes needed, 0 given"),
+    (dict(ws_bytes=12799), EINVAL, "workspace of 12800 bytes needed"),
+    (dict(ws=MIS), EINVAL, "workspace is not 16-byte aligned"),
 ])
 def test_prefill_rejects(lib, kw, code, msg):
     assert prefill(lib, **kw) == code
@@ -85,7 +97,7 @@ def test_prefill_empty_batch_is_ok_without_gpu(lib):
     assert prefill(lib, B=0) == 0
 
 
-def varlen(lib, N=2, Tt=10, cu=FAKE, host=None, ws=FAKE, ws_bytes=256, **kw):
+def varlen(lib, N=2, Tt=10, cu=FAKE, host=None, ws=FAKE, ws_bytes=1 << 30, **kw):
     a = dict(dt=1, gk=1, H=1, Dk=128, Dv=128, chunk=64, q=FAKE, k=FAKE, v=FAKE,
              g=FAKE, beta=FAKE, h0=None, o=FAKE, ht=None)
     a.update(kw)

@@ -198,7 +198,8 @@ def test_prefill_guard_bands():
         1, 1, 1, 100, 2, 128, 128, 64, ctypes.c_float(1.0),
         x["q"].data_ptr(), x["k"].data_ptr(), x["v"].data_ptr(), x["g"].data_ptr(),
         x["beta"].data_ptr(), x["h0"].data_ptr(), o_buf.data_ptr() + 2 * pad,
-        h_buf.data_ptr() + 4 * pad, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        h_buf.data_ptr() + 4 * pad, None, 0,
+        ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
     assert rc == 0, lib.gdr_last_error()
     sync()
     assert bool((o_buf[:pad] == 3.0).all()) and bool((o_buf[pad + n_o:] == 3.0).all())
