@@ -30,14 +30,18 @@
 // each own 16 of the 32 value columns and keep their slice of S^T (Dk x 16,
 // fp32) in accumulator registers for the whole sequence; they do nothing but
 // X, U and the update, and publish S^T and U as bf16 MFMA operands.  Four
-// output waves (SIMDs 2 and 3) form P and O one chunk behind; two staging
-// waves (SIMDs 0 and 1, no MFMA work) and two of the output waves bring
-// q, k, v, T and the gate prefix sums of chunk c+2 into LDS while chunk c
-// runs, their global loads issued a whole iteration before the LDS stores.
+// output waves (SIMDs 2 and 3) each own a 16-row block: they load their q
+// rows from global memory straight into registers and form P and O one
+// chunk behind.  Two staging waves (SIMDs 0 and 1, no MFMA work) bring the
+// k rows, the v slice and the chunk's record (T and the decay factors)
+// of chunk c+2 into LDS while chunk c runs, their global loads issued a
+// whole iteration before the LDS stores.
 // Two barriers per chunk; iteration c:
-//   alpha: chain: X, U, state update (chunk c) | output waves: O (c-1),
-//          diag(e^b) Q S^T (c), P (c) | staging: global loads of c+3
-//   beta:  chain: publish U, S^T; k fragments of c+1 | staging: c+2 into LDS
+//   alpha: chain: X, U, state update (chunk c), from registers | output
+//          waves: O (c-1) | staging: chunk c+2 from registers into LDS
+//   beta:  chain: publish U, S^T; LDS operands of chunk c+1 into registers |
+//          output waves: diag(e^b) Q S^T and P (c), global loads of the q
+//          rows of c+2 | staging: global loads of chunk c+4
 #include "gdr_internal.h"
 #include "device_util.h"
 
@@ -71,7 +75,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a) {
     constexpr int CG = D / 8;           // 16-byte pieces per row
     constexpr int NPC = C * CG / 256;
     static_assert(NPC >= 1 && (C * CG) % 256 == 0, "staging layout");
-    static_assert(kTileBytes == 6 * 1024, "tile record: six operand pairs");
+    static_assert(kTileBytes == 6 * 1024 + 3 * C * 4, "tile record: six operand pairs, three factor rows");
     __shared__ Sm sm;
 
     // ---- which chunk: ci counts chunks over all sequences
@@ -246,10 +250,12 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a) {
     }
     __syncthreads();
 
-    // ---- T to the workspace as six 1 KB operand pairs: pair (sb, kk) holds,
-    //      for lane l, lane l's values of blocks (sb, 2kk) and (sb, 2kk+1)
-    //      (zero above the diagonal), so that one 16-byte read per lane gives
-    //      the A operand of U = T X for row block sb and token blocks 2kk, 2kk+1
+    // ---- the chunk's record in the workspace: T as six 1 KB operand pairs
+    //      (pair (sb, kk) holds,
+    //      for lane l, lane l's values of blocks (sb, 2kk) and (sb, 2kk+1),
+    //      zero above the diagonal, so that one 16-byte read per lane gives
+    //      the A operand of U = T X for row block sb and token blocks 2kk,
+    //      2kk+1), then three rows of 64 fp32 decay factors
     {
         const size_t rec = (size_t)(ci * a.H + h) * kTileBytes;
         bf16x8 *dst = reinterpret_cast<bf16x8 *>(static_cast<char *>(a.tiles) + rec);
@@ -260,6 +266,15 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a) {
             const bf16x4 lo = tile_ld(sm.TT + tri(sb, 2 * kk) * 256, l);
             const bf16x4 hi = 2 * kk + 1 <= sb ? tile_ld(sm.TT + tri(sb, 2 * kk + 1) * 256, l) : bf16x4{};
             dst[i] = cat8(lo, hi);
+        }
+        // then the decay factors of the chunk from b_r, the in-chunk inclusive
+        // prefix sums of the gate logs: e^{b_r}, e^{-b_r}, e^{b_C - b_r}
+        if (tid < C) {
+            float *f = reinterpret_cast<float *>(dst + 6 * 64);
+            const float b = sm.fb[tid];
+            f[tid] = ex(b);
+            f[C + tid] = ex(-b);
+            f[2 * C + tid] = ex(sm.fb[C - 1] - b);
         }
     }
 }
@@ -279,14 +294,17 @@ template <int D> struct ChainSmem {
     // v slice rows [r][i]; a stride of 24 dwords puts the 8 rows that one
     // transpose load touches per half-wave on disjoint banks
     static constexpr int PV = BV + 16;
-    alignas(16) bf16 K[2][C * PD];      // by chunk parity
-    alignas(16) bf16 V[2][C * PV];
-    alignas(16) bf16x8 TT[2][6][64];    // T as operand pairs
-    alignas(16) bf16x8 SB[2][KD][64];   // S^T as operands, per chain wave
+    struct TRec {                       // the chunk's workspace record
+        bf16x8 pairs[6][64];            // T as operand pairs
+        float eb[C];                    // e^{b_r}
+        float neb[C];                   // e^{-b_r}
+        float hs[C];                    // e^{b_C - b_r}
+    };
+    alignas(16) bf16 K[3][C * PD];      // by chunk mod 3
+    alignas(16) bf16 V[3][C * PV];      // by chunk mod 3
+    alignas(16) TRec TR[3];             // by chunk mod 3
+    alignas(16) bf16x8 SB[2][2][KD][64];// S^T entering a chunk (by parity), per chain wave
     alignas(16) bf16x8 UB[2][2][64];    // U as operands, per chain wave
-    alignas(16) float fb[2][C];         // b_r
-    alignas(16) float feb[2][C];        // e^{b_r}
-    alignas(16) float fgc[2][4];        // e^{b_C}
 };
 
 template <int D>
@@ -301,9 +319,9 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
     // staged pieces (16 bytes) per chunk: k rows, v slice rows, T record
     constexpr int NKP = C * CG, NVP = C * BV / 8, NTP = (int)(kTileBytes / 16);
     constexpr int NST = NKP + NVP + NTP;
-    constexpr int NI = NST / 128;       // per staging thread
-    static_assert(NI * 128 == NST && NKP % 64 == 0 && NVP % 64 == 0, "staging layout");
-    static_assert(NTP == 6 * 64, "tile record layout");
+    constexpr int NI = (NST + 127) / 128;   // per staging thread
+    static_assert(NKP % 64 == 0 && NVP % 64 == 0, "staging layout");
+    static_assert(sizeof(typename Sm::TRec) == kTileBytes, "tile record layout");
     __shared__ Sm sm;
 
     // ---- work mapping: the Dv slices of one (sequence, head) share an XCD
@@ -378,72 +396,71 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
                     St[jk][e] = a.h0[sslot + (size_t)(i0 + 16 * ib + l15) * D + srow(jk, e)];
             }
         }
-        auto publish_state = [&]() {
+        auto publish_state = [&](int spar) {   // S^T entering a chunk of parity spar
 #pragma unroll
-            for (int kk = 0; kk < KD; ++kk) sm.SB[ib][kk][lane] = acc_pair(St[2 * kk], St[2 * kk + 1]);
+            for (int kk = 0; kk < KD; ++kk) sm.SB[spar][ib][kk][lane] = acc_pair(St[2 * kk], St[2 * kk + 1]);
         };
-        // k row fragments of a chunk, read a phase ahead of their use
-        bf16x8 Kf[4][KD];
-        auto read_kf = [&](long long c) {
-            const bf16 *Kc = sm.K[(int)(c & 1)];
+        // operands of a chunk, read a phase ahead of their use: k row
+        // fragments, K^T, the v slice, T and the decay factors.  K^T comes
+        // from transpose loads of the k rows: lane j of each 16-lane group
+        // addresses k columns 32 (jk >> 1) + 8 (j & 3) + 4 (jk & 1) .. +3, so
+        // output lane i receives k = srow(jk, .) for row i of the block.
+        bf16x8 Kf[4][KD], KT[KS][2], Ta[4][2];
+        bf16x4 vv[4];
+        f32x4 eb[4], hs[4];
+        float gC = 0.f;
+        auto prefetch = [&](long long c, int m3) {
+            const bf16 *Kc = sm.K[m3];
+            const bf16 *Vc = sm.V[m3];
+            const typename Sm::TRec &R = sm.TR[m3];
 #pragma unroll
-            for (int rb = 0; rb < 4; ++rb)
+            for (int jk = 0; jk < KS; ++jk) {
+                const int pc = 32 * (jk >> 1) + 8 * (l15 & 3) + 4 * (jk & 1);
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    const bf16 *p = Kc + (32 * kk + 4 * q4 + (l15 >> 2)) * PD + pc;
+                    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p));
+                    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p + 16 * PD));
+                    KT[jk][kk] = cat8(__builtin_bit_cast(bf16x4, lo), __builtin_bit_cast(bf16x4, hi));
+                }
+            }
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) {
 #pragma unroll
                 for (int kk = 0; kk < KD; ++kk) Kf[rb][kk] = frag_rows(Kc, PD, 16 * rb, 32 * kk, lane);
+                vv[rb] = frag_col4(Vc, PV, 16 * rb, 16 * ib, lane);
+                eb[rb] = *reinterpret_cast<const f32x4 *>(&R.eb[16 * rb + 4 * q4]);
+                hs[rb] = *reinterpret_cast<const f32x4 *>(&R.hs[16 * rb + 4 * q4]);
+                Ta[rb][0] = R.pairs[tpair(rb, 0)][lane];
+                Ta[rb][1] = rb >= 2 ? R.pairs[tpair(rb, 1)][lane] : bf16x8{};
+            }
+            gC = R.eb[C - 1];
         };
-        publish_state();
+        publish_state(0);
         __syncthreads();                      // chunks 0 and 1 staged
-        read_kf(0);
+        prefetch(0, 0);
+        int m3 = 0;                           // c mod 3
         for (long long c = 0; c < nch; ++c) {
             const int par = (int)(c & 1);
-            const bf16 *Kc = sm.K[par];
+            const int n3 = m3 == 2 ? 0 : m3 + 1;
             // ---- alpha: X = V - diag(e^b) K S^T, U = T X and the state
-            //      update, with every LDS operand read here
-            f32x4 X[4], eb[4];
+            //      update, all from registers
+            f32x4 X[4];
             {
-                const bf16 *Vc = sm.V[par];
-                bf16x4 vv[4];
-#pragma unroll
-                for (int rb = 0; rb < 4; ++rb) {
-                    vv[rb] = frag_col4(Vc, PV, 16 * rb, 16 * ib, lane);
-                    eb[rb] = *reinterpret_cast<const f32x4 *>(&sm.feb[par][16 * rb + 4 * q4]);
-                }
                 bf16x8 Bs[KD];
 #pragma unroll
                 for (int kk = 0; kk < KD; ++kk) Bs[kk] = acc_pair(St[2 * kk], St[2 * kk + 1]);
+                f32x4 xk[4];
 #pragma unroll
                 for (int rb = 0; rb < 4; ++rb) {
-                    f32x4 xk = {0.f, 0.f, 0.f, 0.f};
+                    xk[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int kk = 0; kk < KD; ++kk) xk = mfma32(Kf[rb][kk], Bs[kk], xk);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) X[rb][e] = (float)vv[rb][e] - eb[rb][e] * xk[e];
-                }
-            }
-            // A operand K^T[k][s] of the update by transpose loads of the k
-            // rows: lane j of each 16-lane group addresses k columns
-            // 32 (jk >> 1) + 8 (j & 3) + 4 (jk & 1) .. +3, so output lane i
-            // receives k = srow(jk, .) for row i of the block
-            bf16x8 KT[KS][2], Ta[4][2];
-            float gC;
-            {
-#pragma unroll
-                for (int jk = 0; jk < KS; ++jk) {
-                    const int pc = 32 * (jk >> 1) + 8 * (l15 & 3) + 4 * (jk & 1);
-#pragma unroll
-                    for (int kk = 0; kk < 2; ++kk) {
-                        const bf16 *p = Kc + (32 * kk + 4 * q4 + (l15 >> 2)) * PD + pc;
-                        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p));
-                        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p + 16 * PD));
-                        KT[jk][kk] = cat8(__builtin_bit_cast(bf16x4, lo), __builtin_bit_cast(bf16x4, hi));
-                    }
+                    for (int kk = 0; kk < KD; ++kk) xk[rb] = mfma32(Kf[rb][kk], Bs[kk], xk[rb]);
                 }
 #pragma unroll
-                for (int sb = 0; sb < 4; ++sb) {
-                    Ta[sb][0] = sm.TT[par][tpair(sb, 0)][lane];
-                    Ta[sb][1] = sb >= 2 ? sm.TT[par][tpair(sb, 1)][lane] : bf16x8{};
-                }
-                gC = sm.fgc[par][0];
+                for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) X[rb][e] = (float)vv[rb][e] - eb[rb][e] * xk[rb][e];
             }
             // U = T X, S^T <- e^{b_C} S^T + K^T diag(e^{b_C - b}) U
             bf16x8 Ub[2];
@@ -457,11 +474,9 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
                 }
                 Ub[0] = acc_pair(U[0], U[1]);
                 Ub[1] = acc_pair(U[2], U[3]);
-                f32x4 Uh[4];   // e^{b_C - b_s} = e^{b_C} / e^{b_s}
+                f32x4 Uh[4];
 #pragma unroll
-                for (int sb = 0; sb < 4; ++sb)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) Uh[sb][e] = U[sb][e] * (gC * __builtin_amdgcn_rcpf(eb[sb][e]));
+                for (int sb = 0; sb < 4; ++sb) Uh[sb] = U[sb] * hs[sb];
                 const bf16x8 Bh[2] = {acc_pair(Uh[0], Uh[1]), acc_pair(Uh[2], Uh[3])};
 #pragma unroll
                 for (int jk = 0; jk < KS; ++jk) {
@@ -472,12 +487,13 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
                 }
             }
             __syncthreads();
-            // ---- beta: publish U and S^T; k fragments of the next chunk
+            // ---- beta: publish U and S^T; operands of the next chunk
             sm.UB[ib][0][lane] = Ub[0];
             sm.UB[ib][1][lane] = Ub[1];
-            publish_state();
-            read_kf(c + 1);
+            publish_state(par ^ 1);
+            prefetch(c + 1, n3);
             __syncthreads();
+            m3 = n3;
         }
         __syncthreads();                      // outputs of the last chunk
         __syncthreads();
@@ -493,13 +509,12 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
 
     if (w >= 4 && w < 6) {
         // =================================================================
-        // staging waves: k rows, the v slice and the T record of chunk c+2
-        // into LDS during beta of iteration c, from registers loaded during
-        // alpha of iteration c-1 (two register sets); the gate prefix sums
+        // staging waves: k rows, the v slice and the record (T, factors) of
+        // chunk c+2 into LDS during alpha of iteration c, from registers
+        // loaded during beta of iteration c-2 (two register sets)
         // =================================================================
         const int tl = tid - 256;
         bf16x8 rs[2][NI];
-        float rg[2];
         auto st_load = [&](long long c, auto S) {
             constexpr int r = decltype(S)::value;
             const size_t base = (size_t)chunk_tok(c) * tokstride;
@@ -522,34 +537,21 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
                     rs[r][i] = bload16(rts, 16 * (p - NKP - NVP));
                 }
             }
-            // gate log of row `lane` (both waves load it; wave 4 keeps it)
-            const unsigned hb = (unsigned)(a.H * 4);
-            const int Cc = valid_rows(c);
-            const unsigned gext = Cc ? (unsigned)(Cc - 1) * hb + 4 : 0u;
-            rg[r] = bload4(make_rsrc(a.g + (size_t)chunk_tok(c) * a.H + h, gext), lane * hb);
         };
-        auto st_store = [&](long long c, auto S) {
+        auto st_store = [&](int m3, auto S) {   // chunk c into slot m3 = c mod 3
             constexpr int r = decltype(S)::value;
-            const int par = (int)(c & 1);
 #pragma unroll
             for (int i = 0; i < NI; ++i) {
                 const int p0 = i * 128 + 64 * (w - 4);
                 const int p = i * 128 + tl;
                 if (p0 < NKP) {
-                    *reinterpret_cast<bf16x8 *>(&sm.K[par][(p / CG) * PD + 8 * (p % CG)]) = rs[r][i];
+                    *reinterpret_cast<bf16x8 *>(&sm.K[m3][(p / CG) * PD + 8 * (p % CG)]) = rs[r][i];
                 } else if (p0 < NKP + NVP) {
                     const int pv = p - NKP;
-                    *reinterpret_cast<bf16x8 *>(&sm.V[par][(pv >> 2) * PV + 8 * (pv & 3)]) = rs[r][i];
-                } else {
-                    (&sm.TT[par][0][0])[p - NKP - NVP] = rs[r][i];
+                    *reinterpret_cast<bf16x8 *>(&sm.V[m3][(pv >> 2) * PV + 8 * (pv & 3)]) = rs[r][i];
+                } else if (p < NST) {
+                    reinterpret_cast<bf16x8 *>(&sm.TR[m3])[p - NKP - NVP] = rs[r][i];
                 }
-            }
-            if (w == 4) {   // inclusive prefix sum of the gate logs over the chunk
-                const float b = wave_prefix_sum(rg[r]);
-                const float bC = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, b), 63));
-                sm.fb[par][lane] = b;
-                sm.feb[par][lane] = ex(b);
-                if (lane == 0) sm.fgc[par][0] = ex(bC);
             }
         };
         st_load(0, R0);
@@ -557,16 +559,20 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
         st_load(1, R0);
         st_store(1, R0);
         st_load(2, R0);
+        st_load(3, R1);
         __syncthreads();
+        int m3 = 2;                           // (c + 2) mod 3
         for (long long c = 0;; c += 2) {
-            st_load(c + 3, R1);
+            st_store(m3, R0);
+            m3 = m3 == 2 ? 0 : m3 + 1;
             __syncthreads();
-            st_store(c + 2, R0);
-            __syncthreads();
-            if (c + 1 > nch) break;
             st_load(c + 4, R0);
             __syncthreads();
-            st_store(c + 3, R1);
+            if (c + 1 > nch) break;
+            st_store(m3, R1);
+            m3 = m3 == 2 ? 0 : m3 + 1;
+            __syncthreads();
+            st_load(c + 5, R1);
             __syncthreads();
             if (c + 2 > nch) break;
         }
@@ -580,8 +586,11 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
     // ends up with four adjacent columns of one output row: the published
     // S^T and U serve as A operands, the q rows and P^T as B operands.  P^T
     // is formed in accumulator registers, so it feeds the MFMA directly.
-    // Iteration c, alpha: O of chunk c-1, QS and P of chunk c; beta: the q
-    // rows of chunk c+2, from global memory straight into registers.
+    // Iteration c, alpha: O of chunk c-1 (U of chunk c-1 was published during
+    // beta of c-1); beta: QS and P of chunk c (S^T entering chunk c was
+    // published during beta of c-1, and chunk c's k rows stay in LDS until
+    // alpha of c+1), then the q rows of chunk c+2, from global memory
+    // straight into registers.
     // =====================================================================
     auto out_loop = [&](auto RBc) {
         constexpr int RB = decltype(RBc)::value;
@@ -596,29 +605,13 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
 #pragma unroll
             for (int kk = 0; kk < KD; ++kk) Qr[r][kk] = bload16(rq, off + 64 * kk);
         };
-        auto iter = [&](long long c, auto S) {
-            constexpr int r = decltype(S)::value;
-            const int par = (int)(c & 1);
-            const bf16 *Kc = sm.K[par];
-            bf16x8 Au[2][NP2], As[2][KD], Kj[RB + 1][KD];
-            f32x4 bsJ[RB + 1];
+        // O of chunk c-1
+        auto o_step = [&](long long c) {
+            bf16x8 Au[2][NP2];
 #pragma unroll
-            for (int ob = 0; ob < 2; ++ob) {
+            for (int ob = 0; ob < 2; ++ob)
 #pragma unroll
                 for (int k2 = 0; k2 < NP2; ++k2) Au[ob][k2] = sm.UB[ob][k2][lane];
-#pragma unroll
-                for (int kk = 0; kk < KD; ++kk) As[ob][kk] = sm.SB[ob][kk][lane];
-            }
-#pragma unroll
-            for (int J = 0; J <= RB; ++J) {
-#pragma unroll
-                for (int kk = 0; kk < KD; ++kk) Kj[J][kk] = frag_rows(Kc, PD, 16 * J, 32 * kk, lane);
-                bsJ[J] = *reinterpret_cast<const f32x4 *>(&sm.fb[par][16 * J + 4 * q4]);
-            }
-            const float ebr = sm.feb[par][16 * RB + l15];
-            const float br = sm.fb[par][16 * RB + l15];
-            __builtin_amdgcn_sched_barrier(0);
-            // O of chunk c-1
             const rsrc_t ro = make_rsrc(og + (size_t)chunk_tok(c - 1) * tokstride, extent(c - 1, BV * 2));
             const unsigned voff = l15 * rowb + 8 * q4;
 #pragma unroll
@@ -628,7 +621,25 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
                 for (int k2 = 0; k2 < NP2; ++k2) o = mfma32(Au[ob][k2], Pp[k2], o);
                 bstore8s(ro, voff + 32 * ob, 16 * RB * rowb, cvt4(o * a.scale));
             }
-            // diag(e^b) Q S^T of chunk c (S entering chunk c)
+        };
+        // QS and P of chunk c (m3 = c mod 3)
+        auto qp_step = [&](long long c, int m3, auto S) {
+            constexpr int r = decltype(S)::value;
+            const bf16 *Kc = sm.K[m3];
+            bf16x8 As[2][KD], Kj[RB + 1][KD];
+            f32x4 nebJ[RB + 1];
+#pragma unroll
+            for (int ob = 0; ob < 2; ++ob)
+#pragma unroll
+                for (int kk = 0; kk < KD; ++kk) As[ob][kk] = sm.SB[(int)(c & 1)][ob][kk][lane];
+#pragma unroll
+            for (int J = 0; J <= RB; ++J) {
+#pragma unroll
+                for (int kk = 0; kk < KD; ++kk) Kj[J][kk] = frag_rows(Kc, PD, 16 * J, 32 * kk, lane);
+                nebJ[J] = *reinterpret_cast<const f32x4 *>(&sm.TR[m3].neb[16 * J + 4 * q4]);
+            }
+            const float ebr = sm.TR[m3].eb[16 * RB + l15];
+            // diag(e^b) Q S^T (S entering chunk c)
 #pragma unroll
             for (int ob = 0; ob < 2; ++ob) {
                 f32x4 x = {0.f, 0.f, 0.f, 0.f};
@@ -636,8 +647,8 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
                 for (int kk = 0; kk < KD; ++kk) x = mfma32(As[ob][kk], Qr[r][kk], x);
                 QSp[ob] = x * ebr;
             }
-            // P of chunk c: K_J Q_RB^T gives lane s = 16 J + 4 q4 + e,
-            // r = 16 RB + l15, and P[r][s] = e^{b_r - b_s} q_r.k_s for s <= r
+            // P: K_J Q_RB^T gives lane s = 16 J + 4 q4 + e, r = 16 RB + l15,
+            // and P[r][s] = e^{b_r} e^{-b_s} q_r.k_s for s <= r
             f32x4 pv[RB + 2];
 #pragma unroll
             for (int J = 0; J <= RB; ++J) {
@@ -646,7 +657,7 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
                 for (int kk = 0; kk < KD; ++kk) p = mfma32(Kj[J][kk], Qr[r][kk], p);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float v = ex(br - bsJ[J][e]) * p[e];
+                    const float v = ebr * nebJ[J][e] * p[e];
                     pv[J][e] = (J < RB || 4 * q4 + e <= l15) ? v : 0.f;
                 }
             }
@@ -660,15 +671,20 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
 #pragma unroll
         for (int k2 = 0; k2 < NP2; ++k2) Pp[k2] = bf16x8{};
         __syncthreads();
+        int m3 = 0;                           // c mod 3
         for (long long c = 0;; c += 2) {
-            iter(c, R0);
+            o_step(c);
             __syncthreads();
+            qp_step(c, m3, R0);
             q_load(c + 2, R0);
+            m3 = m3 == 2 ? 0 : m3 + 1;
             __syncthreads();
             if (c + 1 > nch) break;
-            iter(c + 1, R1);
+            o_step(c + 1);
             __syncthreads();
+            qp_step(c + 1, m3, R1);
             q_load(c + 3, R1);
+            m3 = m3 == 2 ? 0 : m3 + 1;
             __syncthreads();
             if (c + 2 > nch) break;
         }

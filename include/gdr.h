@@ -66,10 +66,11 @@ enum gdr_mixer { GDR_FA = 0, GDR_SWA = 1, GDR_GDN = 2, GDR_KDA = 3 };
  * tokens in all (B and B*T for gdr_prefill_chunked, N and T_total for
  * gdr_prefill_chunked_varlen) and H heads needs with this dtype and gate
  * kind: the varlen schedule and chunk offsets (N and N+1 int32, each rounded
- * up to 256 bytes) and, for bf16 with the scalar gate, the chunk-local
- * inverse T of every chunk and head (6 KiB per chunk and head, for
- * tokens / 64 + N chunks, an upper bound).  Returns 0 for N <= 0, tokens < 0
- * or H <= 0.  A buffer of this size serves either call with these sizes.
+ * up to 256 bytes) and, for bf16 with the scalar gate, a record of every
+ * chunk and head (the chunk-local inverse T and the chunk's decay
+ * factors, 6912 bytes) for tokens / 64 + N chunks, an upper bound.
+ * Returns 0 for N <= 0, tokens < 0 or H <= 0.  A buffer of this size
+ * serves either call with these sizes.
  */
 size_t gdr_prefill_workspace_bytes(enum gdr_dtype dt, enum gdr_gate gk, int N,
                                    long long tokens, int H);
