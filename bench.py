@@ -9,10 +9,13 @@ and rotate over three input sets so that a step cannot be served from the
 256 MB last-level cache.
 
 The same line carries:
-  roofline      the prefill kernel's algorithmic HBM bytes per launch over
-                its average launch time (HIP events on the launch stream),
-                against 8 TB/s; `traffic` is the measured bytes per launch
-                from rocprofv3 FETCH_SIZE/WRITE_SIZE counters when given
+  roofline      the prefill call's algorithmic HBM bytes over its average
+                time (HIP events on the launch stream), against 8 TB/s.  One
+                gdr_prefill_chunked call is two back-to-back kernels on that
+                stream: prep_kernel (the chunk-local inverses) and
+                chain_kernel (the recurrence, the dominant one); `traffic`
+                is the measured bytes per call from rocprofv3
+                FETCH_SIZE/WRITE_SIZE counters summed over both, when given
   cpu_baseline  the fp64 oracle on the host cores, on a bounded sample of
                 the same workload (the first tokens of every sequence/head)
   secondary     the other hot-path entry points measured in the same run:
@@ -39,11 +42,11 @@ HBM_PEAK_GBS = 8000.0
 MFMA_BF16_TFLOPS = 2500.0
 D, C = 128, 64
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "chunked_prefill_gdn_B4_H16_T4096_traffic.json")
-KERNEL_SRC = os.path.join(ROOT, "gated_delta_rule_44_amd", "csrc", "chunked.hip")
+KERNEL_SRC = os.path.join(ROOT, "gated_delta_rule_44_amd", "csrc", "chunked_chain.hip")
 
 
 def measured_traffic():
-    """HBM bytes per launch of the headline prefill kernel from rocprofv3
+    """HBM bytes per headline prefill call (its two kernels) from rocprofv3
     FETCH_SIZE / WRITE_SIZE counters (scaled by the factors a plain copy of
     known size gives), or None when they were taken on another version of
     the kernel source."""
@@ -251,7 +254,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": measured_traffic(),
-                     "kernel": "chunked_kernel<128, scalar gate>",
+                     "kernel": "prep_kernel<128> + chain_kernel<128> (one gdr_prefill_chunked call)",
                      "algorithmic_bytes_per_launch": nbytes,
                      "mfma_tflops_alg": flops / (ms * 1e-3) / 1e12,
                      "mfma_frac_alg": flops / (ms * 1e-3) / 1e12 / MFMA_BF16_TFLOPS},

@@ -386,16 +386,14 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
         // chain waves: value columns 16 ib .. 16 ib + 15 of the slice
         // =================================================================
         const int ib = w;
-        f32x4 St[KS];   // S^T[srow(jk, e)][16 ib + l15] (fp32)
+        // S^T[srow(jk, e)][16 ib + l15] (fp32); the four rows e of a block are
+        // adjacent columns of S, so they move as one 16-byte access
+        f32x4 St[KS];
+        const size_t srow0 = sslot + (size_t)(i0 + 16 * ib + l15) * D;
 #pragma unroll
-        for (int jk = 0; jk < KS; ++jk) {
-            St[jk] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (a.h0) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    St[jk][e] = a.h0[sslot + (size_t)(i0 + 16 * ib + l15) * D + srow(jk, e)];
-            }
-        }
+        for (int jk = 0; jk < KS; ++jk)
+            St[jk] = a.h0 ? *reinterpret_cast<const f32x4 *>(a.h0 + srow0 + srow(jk, 0))
+                          : f32x4{0.f, 0.f, 0.f, 0.f};
         auto publish_state = [&](int spar) {   // S^T entering a chunk of parity spar
 #pragma unroll
             for (int kk = 0; kk < KD; ++kk) sm.SB[spar][ib][kk][lane] = acc_pair(St[2 * kk], St[2 * kk + 1]);
@@ -499,10 +497,7 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
         __syncthreads();
         if (a.ht) {
 #pragma unroll
-            for (int jk = 0; jk < KS; ++jk)
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    a.ht[sslot + (size_t)(i0 + 16 * ib + l15) * D + srow(jk, e)] = St[jk][e];
+            for (int jk = 0; jk < KS; ++jk) *reinterpret_cast<f32x4 *>(a.ht + srow0 + srow(jk, 0)) = St[jk];
         }
         return;
     }
