@@ -208,6 +208,46 @@ def test_prefill_guard_bands():
     assert_close(o_buf[pad:pad + n_o].view(x["v"].shape), o_ref, torch.bfloat16, "o")
 
 
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
+def test_prefill_strong_decay(gate):
+    """Gates near the documented bound: about -50 per 64 tokens, so the
+    in-chunk decay factors span ~20 orders of magnitude."""
+    x = synthetic.prefill_inputs(1, 200, 2, 128, torch.bfloat16, gate, seed=21,
+                                 device=DEV, gate_scale=1.0)
+    announce("strong decay %s: min gate sum over the first chunk %.1f"
+             % (gate, float(x["g"][0, :64].sum(0).min())))
+    o, ht = run_prefill(x)
+    check_prefill(x, o, ht, torch.bfloat16)
+
+
+def test_prefill_guard_bands_scalar_gate_workspace():
+    """Scalar gate (prep and recurrence kernels): canaries around o, ht and
+    the exactly sized workspace stay untouched."""
+    B, T, H = 2, 150, 3
+    x = synthetic.prefill_inputs(B, T, H, 128, torch.bfloat16, "scalar", seed=22, device=DEV)
+    pad = 4096
+    n_o, n_h = x["v"].numel(), x["h0"].numel()
+    need = gdr.workspace_bytes(torch.bfloat16, False, B, B * T, H)
+    o_buf = torch.full((n_o + 2 * pad,), 3.0, device=DEV, dtype=torch.bfloat16)
+    h_buf = torch.full((n_h + 2 * pad,), 5.0, device=DEV, dtype=torch.float32)
+    w_buf = torch.full((need + 2 * pad,), 0xA5, device=DEV, dtype=torch.uint8)
+    lib = gdr._load()
+    rc = lib.gdr_prefill_chunked(
+        1, 0, B, T, H, 128, 128, 64, ctypes.c_float(1.0),
+        x["q"].data_ptr(), x["k"].data_ptr(), x["v"].data_ptr(), x["g"].data_ptr(),
+        x["beta"].data_ptr(), x["h0"].data_ptr(), o_buf.data_ptr() + 2 * pad,
+        h_buf.data_ptr() + 4 * pad, w_buf.data_ptr() + pad, need,
+        ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert rc == 0, lib.gdr_last_error()
+    sync()
+    assert bool((o_buf[:pad] == 3.0).all()) and bool((o_buf[pad + n_o:] == 3.0).all())
+    assert bool((h_buf[:pad] == 5.0).all()) and bool((h_buf[pad + n_h:] == 5.0).all())
+    assert bool((w_buf[:pad] == 0xA5).all()) and bool((w_buf[pad + need:] == 0xA5).all())
+    o_ref, ht_ref = oracle.forward(x["q"], x["k"], x["v"], x["g"], x["beta"], h0=x["h0"])
+    assert_close(o_buf[pad:pad + n_o].view(x["v"].shape), o_ref, torch.bfloat16, "o")
+    assert_close(h_buf[pad:pad + n_h].view(x["h0"].shape), ht_ref, torch.bfloat16, "ht")
+
+
 # ----------------------------------------------------------------- varlen
 @pytest.mark.parametrize("dt", ["fp32", "bf16"])
 @pytest.mark.parametrize("gate", ["scalar", "channel"])
@@ -227,8 +267,29 @@ def test_prefill_varlen(dt, gate):
     assert torch.equal(ht[1], x["h0"][1])
 
 
-def test_prefill_varlen_equals_fixed_when_uniform():
-    x = synthetic.prefill_inputs(3, 150, 2, 128, torch.bfloat16, "channel", seed=14, device=DEV)
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
+def test_prefill_varlen_many_short_sequences(gate):
+    """300 packed sequences (the chunk offsets take several sequences per
+    scan thread), lengths 0..130 including empty ones, no h0."""
+    rng = np.random.default_rng(23)
+    lens = [int(v) for v in rng.integers(0, 131, size=300)]
+    lens[5] = lens[77] = 0
+    announce("varlen %s: %d sequences, %d tokens" % (gate, len(lens), sum(lens)))
+    x = synthetic.varlen_inputs(lens, 2, 128, torch.bfloat16, gate, seed=23, h0=False,
+                                device=DEV)
+    o, ht = gdr.prefill_varlen(x["q"], x["k"], x["v"], x["g"], x["beta"],
+                               x["cu_seqlens"], cu_seqlens_host=x["cu_seqlens_host"])
+    sync()
+    o_ref, ht_ref = oracle.forward(x["q"], x["k"], x["v"], x["g"], x["beta"],
+                                   cu_seqlens=x["cu_seqlens_host"])
+    assert_close(o, o_ref, torch.bfloat16, "o")
+    assert_close(ht, ht_ref, torch.bfloat16, "ht")
+    assert not bool(ht[5].any()) and not bool(ht[77].any())
+
+
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
+def test_prefill_varlen_equals_fixed_when_uniform(gate):
+    x = synthetic.prefill_inputs(3, 150, 2, 128, torch.bfloat16, gate, seed=14, device=DEV)
     o1, h1 = run_prefill(x)
     cu = torch.arange(4, device=DEV, dtype=torch.int32) * 150
     flat = {n: x[n].reshape(450, *x[n].shape[2:]) for n in ("q", "k", "v", "g", "beta")}
