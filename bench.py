@@ -23,6 +23,10 @@ The same line carries:
                 GB/s and % of HBM peak) and the packed variable-length KDA
                 prefill.
 
+Defaults: 100 warmup steps and 200 timed steps (a fifth of each for the
+decode and varlen workloads): the GPU reaches its steady clock only after
+about a hundred prefill calls, so shorter warm-ups time part of the ramp.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
                        [--only-headline] [--no-cpu-baseline]
                        [--only {kda_prefill,decode,varlen}]   (one workload, for profiling)
@@ -195,8 +199,8 @@ def cpu_baseline(synthetic, torch, target_s=12.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--only-headline", action="store_true")
     ap.add_argument("--only", choices=["kda_prefill", "decode", "varlen"], default=None,
                     help="time one secondary workload alone (for profiling)")

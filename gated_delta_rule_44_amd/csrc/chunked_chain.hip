@@ -75,7 +75,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a) {
     constexpr int CG = D / 8;           // 16-byte pieces per row
     constexpr int NPC = C * CG / 256;
     static_assert(NPC >= 1 && (C * CG) % 256 == 0, "staging layout");
-    static_assert(kTileBytes == 6 * 1024 + 3 * C * 4, "tile record: six operand pairs, three factor rows");
+    static_assert(kTileBytes == 5 * 1024 + 2 * C * 4, "tile record: T operands, two factor rows");
     __shared__ Sm sm;
 
     // ---- which chunk: ci counts chunks over all sequences
@@ -250,31 +250,34 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a) {
     }
     __syncthreads();
 
-    // ---- the chunk's record in the workspace: T as six 1 KB operand pairs
-    //      (pair (sb, kk) holds,
-    //      for lane l, lane l's values of blocks (sb, 2kk) and (sb, 2kk+1),
-    //      zero above the diagonal, so that one 16-byte read per lane gives
-    //      the A operand of U = T X for row block sb and token blocks 2kk,
-    //      2kk+1), then three rows of 64 fp32 decay factors
+    // ---- the chunk's record in the workspace.  T as MFMA A operands of
+    //      U = T X: for row block sb and token blocks (2kk, 2kk+1), lane l
+    //      reads its values of the two 16x16 blocks (sb, 2kk), (sb, 2kk+1) as
+    //      one 16-byte piece.  The four pairs (1,0), (2,0), (3,0), (3,1) are
+    //      stored whole (1 KB each); the pairs (0,0) and (2,1), whose second
+    //      block lies above the diagonal, as their first block only (512
+    //      bytes).  Then two rows of 64 fp32 decay factors from b_r, the
+    //      in-chunk inclusive prefix sums of the gate logs: e^{b_r} and
+    //      e^{b_C - b_r}.
     {
         const size_t rec = (size_t)(ci * a.H + h) * kTileBytes;
-        bf16x8 *dst = reinterpret_cast<bf16x8 *>(static_cast<char *>(a.tiles) + rec);
-        for (int i = tid; i < 6 * 64; i += 256) {
-            const int pr = i >> 6, l = i & 63;
-            const int sb = pr < 2 ? pr : (pr < 4 ? 2 : 3);
-            const int kk = pr < 2 ? 0 : ((pr - 2) & 1);
-            const bf16x4 lo = tile_ld(sm.TT + tri(sb, 2 * kk) * 256, l);
-            const bf16x4 hi = 2 * kk + 1 <= sb ? tile_ld(sm.TT + tri(sb, 2 * kk + 1) * 256, l) : bf16x4{};
-            dst[i] = cat8(lo, hi);
+        char *dst = static_cast<char *>(a.tiles) + rec;
+        for (int i = tid; i < 4 * 64; i += 256) {
+            const int pr = i >> 6, l = i & 63;          // pairs (1,0) (2,0) (3,0) (3,1)
+            const int sb = pr == 0 ? 1 : (pr == 1 ? 2 : 3);
+            const int kk = pr == 3 ? 1 : 0;
+            reinterpret_cast<bf16x8 *>(dst)[i] = cat8(tile_ld(sm.TT + tri(sb, 2 * kk) * 256, l),
+                                                      tile_ld(sm.TT + tri(sb, 2 * kk + 1) * 256, l));
         }
-        // then the decay factors of the chunk from b_r, the in-chunk inclusive
-        // prefix sums of the gate logs: e^{b_r}, e^{-b_r}, e^{b_C - b_r}
-        if (tid < C) {
-            float *f = reinterpret_cast<float *>(dst + 6 * 64);
-            const float b = sm.fb[tid];
-            f[tid] = ex(b);
-            f[C + tid] = ex(-b);
-            f[2 * C + tid] = ex(sm.fb[C - 1] - b);
+        if (tid < 2 * 64) {                             // first blocks of (0,0), (2,1)
+            const int l = tid & 63;
+            reinterpret_cast<bf16x4 *>(dst + 4096)[tid] = tile_ld(sm.TT + (tid < 64 ? tri(0, 0) : tri(2, 2)) * 256, l);
+        } else if (tid < 2 * 64 + C) {
+            const int r = tid - 2 * 64;
+            float *f = reinterpret_cast<float *>(dst + 5120);
+            const float b = sm.fb[r];
+            f[r] = ex(b);
+            f[C + r] = ex(sm.fb[C - 1] - b);
         }
     }
 }
@@ -282,9 +285,6 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a) {
 // ===========================================================================
 // chain_kernel: the recurrence over chunks
 // ===========================================================================
-// Operand pair (sb, kk) of the T record: index in the six 1 KB pairs.
-__device__ inline int tpair(int sb, int kk) { return sb < 2 ? sb : 2 * sb - 2 + kk; }
-
 template <int D> struct ChainSmem {
     // k rows; a row stride of 8 x odd dwords keeps the 16-byte row fragment
     // reads free of bank conflicts (and halves those of the transpose reads,
@@ -295,9 +295,9 @@ template <int D> struct ChainSmem {
     // transpose load touches per half-wave on disjoint banks
     static constexpr int PV = BV + 16;
     struct TRec {                       // the chunk's workspace record
-        bf16x8 pairs[6][64];            // T as operand pairs
+        bf16x8 pairs[4][64];            // T operand pairs (1,0), (2,0), (3,0), (3,1)
+        bf16x4 halves[2][64];           // first blocks of the pairs (0,0), (2,1)
         float eb[C];                    // e^{b_r}
-        float neb[C];                   // e^{-b_r}
         float hs[C];                    // e^{b_C - b_r}
     };
     alignas(16) bf16 K[3][C * PD];      // by chunk mod 3
@@ -429,8 +429,9 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
                 vv[rb] = frag_col4(Vc, PV, 16 * rb, 16 * ib, lane);
                 eb[rb] = *reinterpret_cast<const f32x4 *>(&R.eb[16 * rb + 4 * q4]);
                 hs[rb] = *reinterpret_cast<const f32x4 *>(&R.hs[16 * rb + 4 * q4]);
-                Ta[rb][0] = R.pairs[tpair(rb, 0)][lane];
-                Ta[rb][1] = rb >= 2 ? R.pairs[tpair(rb, 1)][lane] : bf16x8{};
+                Ta[rb][0] = rb == 0 ? cat8(R.halves[0][lane], bf16x4{}) : R.pairs[rb - 1][lane];
+                Ta[rb][1] = rb == 2 ? cat8(R.halves[1][lane], bf16x4{})
+                          : (rb == 3 ? R.pairs[3][lane] : bf16x8{});
             }
             gC = R.eb[C - 1];
         };
@@ -631,7 +632,9 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
             for (int J = 0; J <= RB; ++J) {
 #pragma unroll
                 for (int kk = 0; kk < KD; ++kk) Kj[J][kk] = frag_rows(Kc, PD, 16 * J, 32 * kk, lane);
-                nebJ[J] = *reinterpret_cast<const f32x4 *>(&sm.TR[m3].neb[16 * J + 4 * q4]);
+                const f32x4 ebJ = *reinterpret_cast<const f32x4 *>(&sm.TR[m3].eb[16 * J + 4 * q4]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) nebJ[J][e] = __builtin_amdgcn_rcpf(ebJ[e]);   // e^{-b_s}
             }
             const float ebr = sm.TR[m3].eb[16 * RB + l15];
             // diag(e^b) Q S^T (S entering chunk c)

@@ -76,9 +76,9 @@ struct PrefillArgs {
 };
 
 // Per (chunk, head) record of the scalar-gate chunked prefill's workspace:
-// T as six 1 KB MFMA operand pairs of its 16x16 blocks (bf16), then three
+// T as MFMA operands of its 16x16 blocks (bf16, 5 KiB), then two
 // rows of the chunk's 64 decay factors (fp32).
-constexpr size_t kTileBytes = 6 * 1024 + 3 * 64 * 4;
+constexpr size_t kTileBytes = 5 * 1024 + 2 * 64 * 4;
 
 hipError_t launch_prefill_recurrent(bool bf16_io, int D, const PrefillArgs &a,
                                     hipStream_t s);

@@ -68,7 +68,7 @@ enum gdr_mixer { GDR_FA = 0, GDR_SWA = 1, GDR_GDN = 2, GDR_KDA = 3 };
  * kind: the varlen schedule and chunk offsets (N and N+1 int32, each rounded
  * up to 256 bytes) and, for bf16 with the scalar gate, a record of every
  * chunk and head (the chunk-local inverse T and the chunk's decay
- * factors, 6912 bytes) for tokens / 64 + N chunks, an upper bound.
+ * factors, 5632 bytes) for tokens / 64 + N chunks, an upper bound.
  * Returns 0 for N <= 0, tokens < 0 or H <= 0.  A buffer of this size
  * serves either call with these sizes.
  */

@@ -52,10 +52,10 @@ def test_version_and_workspace(lib):
     assert gdr.workspace_bytes(bf, True, 64, 100, 4) == 256 + 512
     assert gdr.workspace_bytes(f32, True, 65, 100, 4) == 512 + 512
     assert gdr.workspace_bytes(f32, False, 2, 100, 0) == 0
-    # bf16, scalar gate: + 6912 bytes (T and decay factors) per (chunk, head), for
+    # bf16, scalar gate: + 5632 bytes (T and decay factors) per (chunk, head), for
     # tokens // 64 + N chunks
-    assert gdr.workspace_bytes(bf, False, 1, 64, 1) == 512 + 2 * 6912
-    assert gdr.workspace_bytes(bf, False, 4, 4 * 4096, 16) == 512 + (256 + 4) * 16 * 6912
+    assert gdr.workspace_bytes(bf, False, 1, 64, 1) == 512 + 2 * 5632
+    assert gdr.workspace_bytes(bf, False, 4, 4 * 4096, 16) == 512 + (256 + 4) * 16 * 5632
 
 
 F = ctypes.c_float
@@ -84,8 +84,8 @@ def prefill(lib, dt=1, gk=0, B=1, T=64, H=1, Dk=128, Dv=128, chunk=64, q=FAKE,
     (dict(o=None), EINVAL, "o is NULL"),
     (dict(h0=MIS), EINVAL, "h0 is not 16-byte aligned"),
     (dict(h0=FAKE, ht=FAKE + 256), EINVAL, "overlap"),
-    (dict(ws=None), EINVAL, "workspace of 14336 bytes needed, 0 given"),
-    (dict(ws_bytes=14335), EINVAL, "workspace of 14336 bytes needed"),
+    (dict(ws=None), EINVAL, "workspace of 11776 bytes needed, 0 given"),
+    (dict(ws_bytes=11775), EINVAL, "workspace of 11776 bytes needed"),
     (dict(ws=MIS), EINVAL, "workspace is not 16-byte aligned"),
 ])
 def test_prefill_rejects(lib, kw, code, msg):
