@@ -14,15 +14,14 @@
 //     S^T <- e^{b_C} S^T + K^T diag(e^{b_C - b}) U
 //
 // prep_kernel (one workgroup per chunk and head) forms T, which does not
-// depend on the state, and writes it to the workspace as 16x16 blocks in
-// accumulator order, transposed (block (i, j) holds T_ij^T): the LDS image
-// the recurrence kernel reads it in, and the A operand of U = T X.  Each
-// diagonal block Y_bb = (I + L_bb)^{-1} is the finite series
-// (I - M)(I + M^2)(I + M^4)(I + M^8) of its strictly lower 16x16 block M
-// (M^16 = 0), on 16x16x16 MFMAs computed in both orientations because an
-// MFMA takes its A operand transposed relative to the accumulator layout.
-// Off the diagonal, block forward substitution
-// Y_ij = -Y_ii sum_{k=j}^{i-1} L_ik Y_kj; T = Y diag(beta).
+// depend on the state, and writes it with the chunk's decay factors to a
+// record in the workspace, laid out as the MFMA A operands of U = T X (one
+// 16-byte piece per lane and operand).  Each diagonal block
+// Y_bb = (I + L_bb)^{-1} is the finite series (I - M)(I + M^2)(I + M^4)(I + M^8)
+// of its strictly lower 16x16 block M (M^16 = 0), on 16x16x16 MFMAs computed
+// in both orientations because an MFMA takes its A operand transposed
+// relative to the accumulator layout.  Off the diagonal, block forward
+// substitution Y_ij = -Y_ii sum_{k=j}^{i-1} L_ik Y_kj; T = Y diag(beta).
 //
 // chain_kernel (one workgroup per sequence, head and 32-wide slice of Dv)
 // walks the chunks in order.  The only dependency from chunk to chunk is the
@@ -34,8 +33,8 @@
 // rows from global memory straight into registers and form P and O one
 // chunk behind.  Two staging waves (SIMDs 0 and 1, no MFMA work) bring the
 // k rows, the v slice and the chunk's record (T and the decay factors)
-// of chunk c+2 into LDS while chunk c runs, their global loads issued a
-// whole iteration before the LDS stores.
+// of chunk c+2 into LDS while chunk c runs, their global loads issued one
+// and a half iterations before the LDS stores.
 // Two barriers per chunk; iteration c:
 //   alpha: chain: X, U, state update (chunk c), from registers | output
 //          waves: O (c-1) | staging: chunk c+2 from registers into LDS
