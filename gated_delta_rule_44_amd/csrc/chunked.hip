@@ -1,14 +1,14 @@
-// chunked.hip -- chunked prefill of the gated delta rule on gfx950 MFMA.
+// chunked.hip -- chunked prefill of the gated delta rule with a per-channel
+// gate (Kimi Delta Attention) on gfx950 MFMA.
 //
-// Recurrence (per sequence and head; KDA: per-channel gate, GDN: scalar gate,
-// "Super Apriel: One Checkpoint, Many Speeds", gist.science summary 2a):
+// Recurrence (per sequence and head, "Super Apriel: One Checkpoint, Many
+// Speeds", gist.science summary 2a):
 //     S_t = S_{t-1} Diag(a_t)(I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
 //     o_t = scale * S_t q_t.
 //
 // Chunked form used here (an exact reorganisation; derivation below).  For a
 // chunk of C = 64 tokens starting from state S0 (Dv x Dk), with the
-// in-chunk cumulative log gate b_r = sum_{s<=r} g_s (per channel for KDA,
-// one scalar for GDN):
+// in-chunk cumulative log gate b_r = sum_{s<=r} g_s (per key channel):
 //     Qt = q (.) e^{b},  Kt = k (.) e^{b},  Kb = k (.) e^{-b},
 //     Kh = k (.) e^{b_C - b}                            (rows are tokens)
 //     A  = strict_lower(Kt Kb^T),  P = lower(Qt Kb^T)     (C x C)
@@ -20,24 +20,31 @@
 // is S_r = S_{r-1} Diag(a_r) + u_r k_r^T, so S_r = S0 Gamma_r
 // + sum_{s<=r} u_s (k_s (.) e^{b_r - b_s})^T with Gamma_r = Diag(e^{b_r}).
 // Substituting into u_r gives (I + diag(beta) A) U = diag(beta)(V - Kt S0^T);
-// o_r = S_r q_r gives O; S_C is the r = C case.  For GDN every exponential is
-// one scalar per token, so A and P are scaled by e^{b_r - b_s} after the
-// product and Kt, Qt are row scalings applied to the products.
+// o_r = S_r q_r gives O; S_C is the r = C case.  (The scalar gate takes the
+// two-kernel path of chunked_chain.hip.)
 //
 // Work split.  One workgroup (8 waves) owns one (sequence, head, 32-wide
 // slice of Dv) and walks its chunks in order; rows of S never mix, so the
 // Dv slices of a head are independent.  The slices of one head run on one
 // XCD so their shared reads of q, k and g hit the same L2.  Each chunk:
-//   1  gate prefix sums and gated operands -> LDS (next chunk's global
-//      loads are issued right after, into registers)
-//   2  A (for L = diag(beta) A), X = V - Kt S0^T and Qt S0^T on MFMA
-//   3  wave 0: T = (I + L)^{-1} diag(beta): the four 16x16 diagonal blocks by
-//      forward substitution in fp32, the others by 16x16x16 MFMA block
-//      substitution; waves 1-7 meanwhile form P on MFMA
+//   1  prefix sums of the gate logs (two chunks ahead) and the gated
+//      operands (one chunk ahead, in registers)
+//   2  A (for L = diag(beta) A) and P by 16x16 blocks on MFMA; the four
+//      diagonal blocks of (I + L)^{-1} by forward substitution in fp32
+//   3  wave 0: the off-diagonal blocks of T = (I + L)^{-1} diag(beta) by
+//      16x16x16 MFMA block substitution; waves 4-7: X = V - Kt S0^T and
+//      Qt S0^T on MFMA
 //   4  U = T X
-//   5  O = Qt S0^T + P U, and S^T <- e^{b_C} (.) S^T + Kh^T U
+//   5  O = Qt S0^T + P U, and S^T <- e^{b_C} (.) (S^T + Kb^T U), which is
+//      e^{b_C} (.) S^T + Kh^T U without forming Kh
 // All contractions use bf16 operands with fp32 accumulation; the state is
 // carried in fp32 registers and rounded to bf16 only as an MFMA operand.
+//
+// Gate layout.  Lane l of wave w holds rows RPT (w RPW + l / CG) .. +RPT-1
+// of key channels 8 (l % CG) .. +7 (CG = D/8 channel groups, RPW = 64/CG row
+// groups per wave), so each load instruction reads whole rows; the prefix
+// sums over rows run inside the wave by shuffles, then across the waves
+// through per-wave totals in LDS that two waves turn into prefixes.
 #include <type_traits>
 
 #include "gdr_internal.h"
@@ -60,31 +67,31 @@ constexpr int PV = BV + 8;  // padded LDS row length of the v tile
 
 // Per-thread indices used by every phase.
 template <int D> struct LaneIds {
+    static constexpr int CG = D / 8;           // 8-channel groups per row
+    static constexpr int RPW = 64 / CG;        // row groups per wave
+    static constexpr int RPT = C / (NW * RPW); // rows per thread in the gate phase
     int tid, lane, w, l15, l4;
-    int cg, rg;        // gate phase: 8-channel group, row group
+    int cg, rgl, rg;   // gate phase: channel group, row group in the wave / block
     int vr, vc;        // v tile: row, first column
     __device__ explicit LaneIds(int t) {
-        constexpr int CG = D / 8;
-        constexpr int RPW = 64 / CG;
         tid = t;
         lane = t & 63;
         w = __builtin_amdgcn_readfirstlane(t >> 6);
         l15 = lane & 15;
         l4 = lane >> 4;
         cg = lane % CG;
-        rg = w * RPW + lane / CG;
+        rgl = lane / CG;
+        rg = w * RPW + rgl;
         vr = t >> 3;
         vc = (t & 7) * 4;
     }
 };
 
-template <int D, bool CH> struct Smem {
+template <int D> struct Smem {
     static constexpr int PD = D + 8;   // padded row length for D-wide rows
-    alignas(16) bf16 Q[C * PD];        // q (GDN) or q (.) e^b (KDA), [r][j]
-    alignas(16) bf16 K[C * PD];        // k (GDN) or k (.) e^b (KDA), [r][j]
-    alignas(16) bf16 Kb[CH ? C * PD : 8];   // k (.) e^-b (KDA), [r][j]
-    static constexpr int PDH = D + 16; // D-wide rows read by transpose loads
-    alignas(16) bf16 Kh[2][C * PDH];   // k (.) e^{b_C - b}, [s][j], by chunk parity
+    alignas(16) bf16 Q[C * PD];        // q (.) e^b, [r][j]
+    alignas(16) bf16 K[C * PD];        // k (.) e^b, [r][j]
+    alignas(16) bf16 Kb[2][C * PD];    // k (.) e^-b, [r][j], by chunk parity
     alignas(16) bf16 S[BV * PD];       // bf16 copy of the state slice, [i][j]
     alignas(16) bf16 TT[C * PCT];      // T^T, [s][r] (read back by transpose loads)
     alignas(16) bf16 PT[C * PCT];      // P^T, [s][r]
@@ -94,55 +101,40 @@ template <int D, bool CH> struct Smem {
     alignas(16) float LT[C * PL];      // L^T = (diag(beta) A)^T, [s][r]
     alignas(16) float YT[4 * 16 * PY]; // inverted diagonal blocks, transposed: [b][c][r]
     alignas(16) float beta[C];
-    alignas(16) float gb[2][C];        // GDN: cumulative log gate b_r, by chunk parity
-    alignas(16) float e1[2][C];        // GDN: e^{b_r}
-    alignas(16) float e2[2][C];        // GDN: e^{-b_r}
-    alignas(16) float gam[2][D];       // e^{b_C} per channel (GDN: [0]), by parity
-    alignas(16) float tot[CH ? NW * D : 4];   // KDA: per-wave sums of g
+    alignas(16) float gam[2][D];       // e^{b_C} per channel, by chunk parity
+    // per chunk parity: the per-wave sums of the gate logs [w][j], turned in
+    // place into their exclusive prefix over the waves, and the chunk total
+    // b_C in row NW, all times log2(e)
+    alignas(16) float pfx[2][(NW + 1) * D];
 };
 
-// A x B^T over a D-long contraction for one 16x16 output block: rows ra.. of
-// the row-major tile A and rows rb.. of the row-major tile B.
-template <int KS>
-__device__ inline f32x4 gemm_nt(const bf16 *A, int lda, int ra, const bf16 *B, int ldb, int rb,
-                                int lane, f32x4 acc) {
-    bf16x8 fa[KS], fb[KS];
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-        fa[kk] = frag_rows(A, lda, ra, 32 * kk, lane);
-        fb[kk] = frag_rows(B, ldb, rb, 32 * kk, lane);
-    }
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) acc = mfma32(fa[kk], fb[kk], acc);
-    return acc;
-}
 
-__device__ inline void tri_block(int tri, int &I, int &J) {
-    I = tri < 1 ? 0 : tri < 3 ? 1 : tri < 6 ? 2 : 3;
-    J = tri - I * (I + 1) / 2;
-}
-
-// Software pipeline.  Iteration j of the chunk loop works on three chunks at
+// Software pipeline.  Iteration j of the chunk loop works on four chunks at
 // once, with three workgroup barriers:
 //   chunk j-1 ("state"):  U = T X, then O = Qt S0^T + P U and the state update
 //   chunk j   ("prep"):   gated operands -> LDS, A -> L, T (diagonal blocks by
 //                         forward substitution, the rest by MFMA), P, X, Qt S0^T
-//   chunk j+1 ("gate"):   gate prefix sums and gated operands in registers
-//   chunk j+2:            global loads into registers
+//   chunk j+1 ("gate"):   gated operands in registers
+//   chunk j+2 ("scan"):   prefix sums of the gate logs
 //   phase A: U(j-1) || store gated operands of chunk j
-//   phase B: O(j-1), state update(j-1) || A(j), diagonal inverses || scan(j+1)
-//   phase C: T(j) off-diagonal (wave 0) || Qt S0^T(j), X(j) (waves 1-4)
-//            || P(j) (waves 5-7) || gated operands of chunk j+1 || loads j+2
-template <int D, bool CH>
+//   phase B: waves 0-3: the diagonal block (b, b) of A and P, its inverse,
+//            and block (b, b-1);  waves 4-7: O(j-1) and the state update
+//            (j-1), then blocks (2,0), (3,0), (3,1);  all: prefix sums of
+//            the gate logs of chunk j+2 within each wave, loads of g(j+3)
+//   phase C: T(j) off-diagonal (wave 0) || Qt S0^T(j), X(j) (waves 4-7);
+//            all: P(j) -> LDS; waves 1-2: prefixes over the waves for chunk
+//            j+2; all: gated operands of chunk j+1, loads of q, k, v(j+2)
+// P(j) is held in registers from phase B to phase C because the O of chunk
+// j-1 reads the previous P during phase B.
+template <int D>
 __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
-    using Sm = Smem<D, CH>;
+    using Sm = Smem<D>;
     using LI = LaneIds<D>;
     constexpr int PD = Sm::PD;
-    constexpr int PDH = Sm::PDH;
     constexpr int NTILE = D / BV;
-    constexpr int CG = D / 8;          // 8-channel groups per row
-    constexpr int RPW = 64 / CG;       // row groups per wave
-    constexpr int RPT = C / (NW * RPW);// rows per thread in the gate phase
+    constexpr int CG = LI::CG;
+    constexpr int RPW = LI::RPW;
+    constexpr int RPT = LI::RPT;
     constexpr int KD = D / 32;         // x32 steps over a D-long contraction
     constexpr int SBK = D / 64;        // 16-row blocks of S^T per state wave
     static_assert(RPT >= 1, "gate phase layout");
@@ -211,8 +203,7 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
     // next chunk (reloaded right after they are gated), and v/beta of the
     // next two chunks (by chunk parity)
     bf16x8 rq[RPT], rk[RPT];
-    f32x4 rgc[CH ? RPT : 1][2];
-    float rgs = 0.f;
+    f32x4 rgc[RPT][2];
     bf16x4 rv[2];
     float rb[2];
     rv[0] = rv[1] = bf16x4{};
@@ -226,20 +217,14 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
     auto load_g = [&](const LI &L, long long c) {
         const long long tc = t0 + c * C;
         const int Cc = valid_rows(c);
-        if (CH) {
-            const unsigned rowb = (unsigned)(a.H * D * 4);
-            const rsrc_t rs = make_rsrc(a.g + ((size_t)tc * a.H + h) * D,
-                                        Cc ? (Cc - 1) * rowb + D * 4 : 0u);
+        const unsigned rowb = (unsigned)(a.H * D * 4);
+        const rsrc_t rs = make_rsrc(a.g + ((size_t)tc * a.H + h) * D,
+                                    Cc ? (Cc - 1) * rowb + D * 4 : 0u);
 #pragma unroll
-            for (int i = 0; i < RPT; ++i) {
-                const unsigned off = (L.rg * RPT + i) * rowb + 32 * L.cg;
-                rgc[i][0] = bload16f(rs, off);
-                rgc[i][1] = bload16f(rs, off + 16);
-            }
-        } else {
-            const unsigned rowb = (unsigned)(a.H * 4);
-            const rsrc_t rs = make_rsrc(a.g + (size_t)tc * a.H + h, Cc ? (Cc - 1) * rowb + 4 : 0u);
-            rgs = bload4(rs, L.tid * rowb);
+        for (int i = 0; i < RPT; ++i) {
+            const unsigned off = (L.rg * RPT + i) * rowb + 32 * L.cg;
+            rgc[i][0] = bload16f(rs, off);
+            rgc[i][1] = bload16f(rs, off + 16);
         }
     };
     auto load_qkvb = [&](const LI &L, long long c, int par) {
@@ -262,107 +247,106 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
     };
 
     // gated operands Qt, Kt, Kb of the next chunk, held in registers from
-    // phase C to the next phase A
-    bf16x8 gq[RPT], gk[RPT], gkb[CH ? RPT : 1];
-    float cum[CH ? RPT : 1][8];
+    // phase C to the next phase A; prefix sums of the gate logs within the
+    // wave for the next two chunks (by chunk parity), held from their scan
+    // (phase B, two chunks ahead) to their gating
+    bf16x8 gq[RPT], gk[RPT], gkb[RPT];
+    float cum[2][RPT][8];
+    constexpr float kL2e = 1.4426950408889634f;
 
-    // prefix sums of the gate logs of one chunk (phase B)
-    auto scan = [&](const LI &L, int par) {
-        if (CH) {
-            float run[8];
+    // prefix sums of the gate logs of one chunk over this wave's rows
+    // (phase B); the wave's per-channel totals go to pfx[par]
+    auto scan = [&](const LI &L, auto par_tag) {
+        constexpr int par = decltype(par_tag)::value;
+        float run[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) run[e] = 0.f;
+        for (int e = 0; e < 8; ++e) run[e] = 0.f;
 #pragma unroll
-            for (int i = 0; i < RPT; ++i) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    run[e] += rgc[i][e >> 2][e & 3];
-                    cum[i][e] = run[e];
-                }
-            }
+        for (int i = 0; i < RPT; ++i) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                float incl = run[e];
-#pragma unroll
-                for (int off = CG; off < 64; off *= 2) {
-                    const float y = __shfl_up(incl, off);
-                    if (L.lane >= off) incl += y;
-                }
-#pragma unroll
-                for (int i = 0; i < RPT; ++i) cum[i][e] += incl - run[e];
-                if (L.lane >= 64 - CG) sm.tot[L.w * D + 8 * L.cg + e] = incl;
+                run[e] += rgc[i][e >> 2][e & 3];
+                cum[par][i][e] = run[e];
             }
-        } else if (L.w == 0) {
-            float gv = rgs;
+        }
+        // scan of the row-group totals across the wave: the eight channels'
+        // shuffles of one step are issued together so their LDS round trips
+        // overlap
+        float incl[8];
 #pragma unroll
-            for (int off = 1; off < 64; off *= 2) {
-                const float y = __shfl_up(gv, off);
-                if (L.lane >= off) gv += y;
-            }
-            sm.gb[par][L.lane] = gv;
-            sm.e1[par][L.lane] = ex(gv);
-            sm.e2[par][L.lane] = ex(-gv);
+        for (int e = 0; e < 8; ++e) incl[e] = run[e];
+#pragma unroll
+        for (int off = CG; off < 64; off *= 2) {
+            float y[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[e] = __shfl_up(incl[e], off);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) incl[e] += L.lane >= off ? y[e] : 0.f;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+#pragma unroll
+            for (int i = 0; i < RPT; ++i) cum[par][i][e] += incl[e] - run[e];
+        }
+        if (L.lane >= 64 - CG) {
+            float *t = &sm.pfx[par][L.w * D + 8 * L.cg];
+            *reinterpret_cast<f32x4 *>(t) = f32x4{incl[0], incl[1], incl[2], incl[3]};
+            *reinterpret_cast<f32x4 *>(t + 4) = f32x4{incl[4], incl[5], incl[6], incl[7]};
         }
     };
 
-    // gated operands of one chunk (phase C): Qt, Kt, Kb into registers; Kh
-    // and e^{b_C} straight into their parity buffers
-    auto gate = [&](const LI &L, int par) {
-        if (CH) {
-            float bC[8], pre[8];
+    // per-wave totals -> exclusive prefix over the waves and chunk total, one
+    // thread per key channel (threads 64 .. 64+D-1, phase C)
+    auto prefix = [&](int par) {
+        const int ch = tid0 - 64;
+        if (ch >= 0 && ch < D) {
+            float t[NW];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) { bC[e] = 0.f; pre[e] = 0.f; }
+            for (int ww = 0; ww < NW; ++ww) t[ww] = sm.pfx[par][ww * D + ch];
+            float acc = 0.f;
 #pragma unroll
             for (int ww = 0; ww < NW; ++ww) {
-                const f32x4 ta = *reinterpret_cast<const f32x4 *>(&sm.tot[ww * D + 8 * L.cg]);
-                const f32x4 tb = *reinterpret_cast<const f32x4 *>(&sm.tot[ww * D + 8 * L.cg + 4]);
-                const float tv[8] = {ta.x, ta.y, ta.z, ta.w, tb.x, tb.y, tb.z, tb.w};
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    bC[e] += tv[e];
-                    pre[e] += ww < L.w ? tv[e] : 0.f;
-                }
+                sm.pfx[par][ww * D + ch] = acc * kL2e;
+                acc += t[ww];
             }
+            sm.pfx[par][NW * D + ch] = acc * kL2e;
+        }
+    };
+
+    // gated operands of one chunk (phase C): Qt, Kt, Kb into registers and
+    // e^{b_C} into its parity buffer
+    auto gate = [&](const LI &L, auto par_tag) {
+        constexpr int par = decltype(par_tag)::value;
+        const float *pw = &sm.pfx[par][L.w * D + 8 * L.cg];
+        const float *pc = &sm.pfx[par][NW * D + 8 * L.cg];
+        const f32x4 p0 = *reinterpret_cast<const f32x4 *>(pw);
+        const f32x4 p1 = *reinterpret_cast<const f32x4 *>(pw + 4);
+        const f32x4 c0 = *reinterpret_cast<const f32x4 *>(pc);
+        const f32x4 c1 = *reinterpret_cast<const f32x4 *>(pc + 4);
+        const float pre[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+        const float bC[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+        if (L.rg == 0) {
             float gC[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) gC[e] = ex(bC[e]);
-            if (L.rg == 0) {
-                *reinterpret_cast<f32x4 *>(&sm.gam[par][8 * L.cg]) = f32x4{gC[0], gC[1], gC[2], gC[3]};
-                *reinterpret_cast<f32x4 *>(&sm.gam[par][8 * L.cg + 4]) = f32x4{gC[4], gC[5], gC[6], gC[7]};
+            for (int e = 0; e < 8; ++e) gC[e] = __builtin_amdgcn_exp2f(bC[e]);
+            *reinterpret_cast<f32x4 *>(&sm.gam[par][8 * L.cg]) = f32x4{gC[0], gC[1], gC[2], gC[3]};
+            *reinterpret_cast<f32x4 *>(&sm.gam[par][8 * L.cg + 4]) = f32x4{gC[4], gC[5], gC[6], gC[7]};
+        }
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            float qt[8], kt[8], kb[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float eb = __builtin_amdgcn_exp2f(__builtin_fmaf(cum[par][i][e], kL2e, pre[e]));
+                const float ebi = __builtin_amdgcn_rcpf(eb);
+                const float kv = (float)rk[i][e];
+                qt[e] = (float)rq[i][e] * eb;
+                kt[e] = kv * eb;
+                kb[e] = kv * ebi;
             }
-#pragma unroll
-            for (int i = 0; i < RPT; ++i) {
-                const int r = L.rg * RPT + i;
-                float qt[8], kt[8], kb[8], kh[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float eb = ex(cum[i][e] + pre[e]);
-                    const float ebi = __builtin_amdgcn_rcpf(eb);
-                    const float kv = (float)rk[i][e];
-                    qt[e] = (float)rq[i][e] * eb;
-                    kt[e] = kv * eb;
-                    kb[e] = kv * ebi;
-                    kh[e] = kb[e] * gC[e];
-                }
-                gq[i] = cvt8(qt);
-                gk[i] = cvt8(kt);
-                gkb[i] = cvt8(kb);
-                *reinterpret_cast<bf16x8 *>(&sm.Kh[par][r * PDH + 8 * L.cg]) = cvt8(kh);
-            }
-        } else {
-            const float bC = sm.gb[par][C - 1];
-            if (L.tid == 0) sm.gam[par][0] = ex(bC);
-#pragma unroll
-            for (int i = 0; i < RPT; ++i) {
-                const int r = L.rg * RPT + i;
-                const float sc = ex(bC - sm.gb[par][r]);
-                float kh[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) kh[e] = (float)rk[i][e] * sc;
-                gq[i] = rq[i];
-                gk[i] = rk[i];
-                *reinterpret_cast<bf16x8 *>(&sm.Kh[par][r * PDH + 8 * L.cg]) = cvt8(kh);
-            }
+            gq[i] = cvt8(qt);
+            gk[i] = cvt8(kt);
+            gkb[i] = cvt8(kb);
         }
     };
 
@@ -373,15 +357,16 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
             const int r = L.rg * RPT + i;
             *reinterpret_cast<bf16x8 *>(&sm.Q[r * PD + 8 * L.cg]) = gq[i];
             *reinterpret_cast<bf16x8 *>(&sm.K[r * PD + 8 * L.cg]) = gk[i];
-            if (CH) *reinterpret_cast<bf16x8 *>(&sm.Kb[r * PD + 8 * L.cg]) = gkb[i];
+            *reinterpret_cast<bf16x8 *>(&sm.Kb[par][r * PD + 8 * L.cg]) = gkb[i];
         }
         *reinterpret_cast<bf16x4 *>(&sm.V[L.vr * PV + L.vc]) = rv[par];
         if (L.tid < C) sm.beta[L.tid] = rb[par];
     };
 
+    // Qt S0^T of the prep chunk, transposed ([i][r]: lane holds columns
+    // 16 jv + 4 l4 .. +3 of row 16 I + l15), kept for its outputs
     f32x4 accQS[2];
     accQS[0] = accQS[1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const bf16 *Bop = CH ? sm.Kb : sm.K;
 
     // ---- one pipeline iteration; PAR = parity of the prep chunk j
     auto iteration = [&](auto par_tag, long long j) {
@@ -391,6 +376,43 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
         const bool hasS = j >= 1;
         const bool hasP = j < nch;
         const bool hasG = j + 1 < nch;
+
+        auto frags = [&](const bf16 *M, int blk, bf16x8 (&f)[KD]) {
+#pragma unroll
+            for (int kk = 0; kk < KD; ++kk) f[kk] = frag_rows(M, PD, 16 * blk, 32 * kk, lane);
+        };
+        // A and P block (I, J): Kt and Qt rows of block I against Kb rows of J
+        auto gram = [&](const bf16x8 (&kf)[KD], const bf16x8 (&qf)[KD], const bf16x8 (&bf)[KD],
+                        f32x4 &av, f32x4 &pv) {
+            av = f32x4{0.f, 0.f, 0.f, 0.f};
+            pv = av;
+#pragma unroll
+            for (int kk = 0; kk < KD; ++kk) {
+                av = mfma32(kf[kk], bf[kk], av);
+                pv = mfma32(qf[kk], bf[kk], pv);
+            }
+        };
+        // L^T[s][r] = beta_r A[r][s] for s < r
+        auto putL = [&](int I, int J, f32x4 av) {
+            const int s = 16 * J + l15;
+            const int r0 = 16 * I + 4 * l4;
+            const f32x4 br = *reinterpret_cast<const f32x4 *>(&sm.beta[r0]);
+            f32x4 lv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) lv[e] = s < r0 + e ? av[e] * br[e] : 0.f;
+            *reinterpret_cast<f32x4 *>(&sm.LT[s * PL + r0]) = lv;
+        };
+        // P^T[s][r] = P[r][s] for s <= r
+        auto putP = [&](int I, int J, f32x4 pv) {
+            const int s = 16 * J + l15;
+            const int r0 = 16 * I + 4 * l4;
+            f32x4 pm;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) pm[e] = s <= r0 + e ? pv[e] : 0.f;
+            *reinterpret_cast<bf16x4 *>(&sm.PT[s * PCT + r0]) = cvt4(pm);
+        };
+        // P blocks of chunk j computed in phase B, written in phase C
+        f32x4 pdiag = {0.f, 0.f, 0.f, 0.f}, poff = pdiag;
 
         // ================= phase A ========================================
         if (hasS) {   // U = T X of chunk j-1; wave w: row block w>>1, value block w&1
@@ -410,60 +432,22 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
         __syncthreads();
 
         // ================= phase B ========================================
-        f32x4 ov[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
         if (w < 4) {
             if (hasP) {
-                // A and P of chunk j by 16-row blocks (I, J <= I); each wave
-                // loads its Kt/Qt rows once and shares each Kb load between A
-                // and P:  w0: (0,0),(3,0)  w1: (1,0),(1,1)  w2: (2,0..2)
-                // w3: (3,1..3).  Diagonal blocks are inverted by their wave.
-                const float *e1 = sm.e1[PAR];
-                const float *e2 = sm.e2[PAR];
-                auto frags = [&](const bf16 *M, int blk, bf16x8 (&f)[KD]) {
-#pragma unroll
-                    for (int kk = 0; kk < KD; ++kk) f[kk] = frag_rows(M, PD, 16 * blk, 32 * kk, lane);
-                };
-                // L^T[s][r] = beta_r A[r][s] (s < r) and P^T[s][r] = P[r][s]
-                // (s <= r); GDN scales both by e^{b_r} e^{-b_s}
-                auto put = [&](int I, int J, f32x4 av, f32x4 pv) {
-                    const int s = 16 * J + l15;
-                    const int r0 = 16 * I + 4 * l4;
-                    const f32x4 br = *reinterpret_cast<const f32x4 *>(&sm.beta[r0]);
-                    f32x4 dv = {1.f, 1.f, 1.f, 1.f};
-                    if (!CH) dv = *reinterpret_cast<const f32x4 *>(&e1[r0]) * e2[s];
-                    f32x4 lv, pm;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        lv[e] = s < r0 + e ? av[e] * dv[e] * br[e] : 0.f;
-                        pm[e] = s <= r0 + e ? pv[e] * dv[e] : 0.f;
-                    }
-                    *reinterpret_cast<f32x4 *>(&sm.LT[s * PL + r0]) = lv;
-                    *reinterpret_cast<bf16x4 *>(&sm.PT[s * PCT + r0]) = cvt4(pm);
-                };
-                auto tile = [&](const bf16x8 (&kf)[KD], const bf16x8 (&qf)[KD], int I, int J) {
-                    bf16x8 bf[KD];
-                    frags(Bop, J, bf);
-                    f32x4 av = {0.f, 0.f, 0.f, 0.f}, pv = av;
-#pragma unroll
-                    for (int kk = 0; kk < KD; ++kk) {
-                        av = mfma32(kf[kk], bf[kk], av);
-                        pv = mfma32(qf[kk], bf[kk], pv);
-                    }
-                    put(I, J, av, pv);
-                };
-                const int Id = w;   // the diagonal block of this wave
-                {
-                    bf16x8 kf[KD], qf[KD];
-                    frags(sm.K, Id, kf);
-                    frags(sm.Q, Id, qf);
-                    const int J0 = w == 3 ? 1 : 0;
-                    for (int J = J0; J <= Id; ++J) tile(kf, qf, Id, J);
-                }
-                if (w == 0) {
-                    bf16x8 kf[KD], qf[KD];
-                    frags(sm.K, 3, kf);
-                    frags(sm.Q, 3, qf);
-                    tile(kf, qf, 3, 0);
+                // diagonal block (b, b) and, for b >= 1, block (b, b-1): the
+                // latter's products run while the diagonal block is inverted
+                const int b = w;
+                bf16x8 kf[KD], qf[KD], bf[KD];
+                frags(sm.K, b, kf);
+                frags(sm.Q, b, qf);
+                frags(sm.Kb[PAR], b, bf);
+                f32x4 ad;
+                gram(kf, qf, bf, ad, pdiag);
+                putL(b, b, ad);
+                f32x4 aoff = {0.f, 0.f, 0.f, 0.f};
+                if (b >= 1) {
+                    frags(sm.Kb[PAR], b - 1, bf);
+                    gram(kf, qf, bf, aoff, poff);
                 }
                 __threadfence_block();
                 // (I + L_bb) Y = I by forward substitution in fp32.  Lane
@@ -472,82 +456,90 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
                 // (row r of L^T), and each y_r is broadcast from its owner
                 // lane to the quad by DPP, so no LDS access sits in the
                 // dependency chain.
-                const int b = Id;
-                const int cq = lane >> 2, gq = lane & 3;
+                const int cq = lane >> 2, gq4 = lane & 3;
                 f32x4 Lv[16];
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
-                    Lv[r] = *reinterpret_cast<const f32x4 *>(&sm.LT[(16 * b + r) * PL + 16 * b + 4 * gq]);
+                    Lv[r] = *reinterpret_cast<const f32x4 *>(&sm.LT[(16 * b + r) * PL + 16 * b + 4 * gq4]);
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f}, y4 = acc;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int e = r & 3, go = r >> 2;
                     const float own = r == cq ? 1.f : (r > cq ? -acc[e] : 0.f);
                     const float yr = quad_bcast(own, go);
-                    y4[e] = gq == go ? yr : y4[e];
+                    y4[e] = gq4 == go ? yr : y4[e];
                     acc += Lv[r] * yr;   // L is strictly lower: rows <= r add zero
                 }
                 {
                     const float bc = sm.beta[16 * b + cq];
                     // T[16b+4gq+e][16b+cq] -> T^T row 16b+cq;  Y^T[b][cq][4gq..]
-                    *reinterpret_cast<bf16x4 *>(&sm.TT[(16 * b + cq) * PCT + 16 * b + 4 * gq]) = cvt4(y4 * bc);
-                    *reinterpret_cast<f32x4 *>(&sm.YT[(b * 16 + cq) * PY + 4 * gq]) = y4;
+                    *reinterpret_cast<bf16x4 *>(&sm.TT[(16 * b + cq) * PCT + 16 * b + 4 * gq4]) = cvt4(y4 * bc);
+                    *reinterpret_cast<f32x4 *>(&sm.YT[(b * 16 + cq) * PY + 4 * gq4]) = y4;
                 }
+                if (b >= 1) putL(b, b - 1, aoff);
             }
-        } else if (hasS) {
-            // outputs and state update of chunk j-1 (row block / key blocks of
-            // this wave)
-            const int I = w - 4;
-            const bf16x8 p0 = frag_cols(sm.PT, PCT, 0, 16 * I, lane);
-            const bf16x8 p1 = frag_cols(sm.PT, PCT, 32, 16 * I, lane);
-            bf16x8 uf[2][2];
-#pragma unroll
-            for (int jv = 0; jv < 2; ++jv) {
-                uf[jv][0] = frag_rows(sm.UT, PC, 16 * jv, 0, lane);
-                uf[jv][1] = frag_rows(sm.UT, PC, 16 * jv, 32, lane);
-            }
-#pragma unroll
-            for (int jv = 0; jv < 2; ++jv) {
-                f32x4 o = mfma32(p0, uf[jv][0], accQS[jv]);
-                if (I >= 2) o = mfma32(p1, uf[jv][1], o);
-                ov[jv] = o * a.scale;
-            }
-            // S^T <- e^{b_C} (.) S^T + Kh^T U  (chunk j-1: parity 1 - PAR)
-#pragma unroll
-            for (int kb = 0; kb < SBK; ++kb) {
-                const int Jk = SBK * I + kb;
-                const int jc = 16 * Jk + 4 * l4;
-                f32x4 gm;
-                if (CH) gm = *reinterpret_cast<const f32x4 *>(&sm.gam[1 - PAR][jc]);
-                else    gm = f32x4{sm.gam[1 - PAR][0], sm.gam[1 - PAR][0], sm.gam[1 - PAR][0],
-                                   sm.gam[1 - PAR][0]};
-                const bf16x8 k0f = frag_cols(sm.Kh[1 - PAR], PDH, 0, 16 * Jk, lane);
-                const bf16x8 k1f = frag_cols(sm.Kh[1 - PAR], PDH, 32, 16 * Jk, lane);
+        } else {
+            if (hasS) {
+                // outputs and state update of chunk j-1 (row block / key
+                // blocks of this wave).  O^T = U^T P^T + (Qt S0^T)^T: lane
+                // holds columns 16 jv + 4 l4 .. +3 of output row 16 I + l15.
+                const int I = w - 4;
+                const bf16x8 p0 = frag_cols(sm.PT, PCT, 0, 16 * I, lane);
+                const bf16x8 p1 = frag_cols(sm.PT, PCT, 32, 16 * I, lane);
+                bf16x8 uf[2][2];
 #pragma unroll
                 for (int jv = 0; jv < 2; ++jv) {
-                    f32x4 sv = St[kb][jv] * gm;
-                    sv = mfma32(k0f, uf[jv][0], sv);
-                    sv = mfma32(k1f, uf[jv][1], sv);
-                    St[kb][jv] = sv;
-                    *reinterpret_cast<bf16x4 *>(&sm.S[(16 * jv + l15) * PD + jc]) = cvt4(sv);
+                    uf[jv][0] = frag_rows(sm.UT, PC, 16 * jv, 0, lane);
+                    uf[jv][1] = frag_rows(sm.UT, PC, 16 * jv, 32, lane);
+                }
+                f32x4 ov[2];
+#pragma unroll
+                for (int jv = 0; jv < 2; ++jv) {
+                    f32x4 o = mfma32(uf[jv][0], p0, accQS[jv]);
+                    if (I >= 2) o = mfma32(uf[jv][1], p1, o);
+                    ov[jv] = o * a.scale;
+                }
+                {
+                    const long long tc = t0 + (j - 1) * C;
+                    const int Cc = valid_rows(j - 1);
+                    const unsigned rowb = (unsigned)(tokstride * 2);
+                    const rsrc_t ro = make_rsrc(og + (size_t)tc * tokstride, (Cc - 1) * rowb + BV * 2);
+#pragma unroll
+                    for (int jv = 0; jv < 2; ++jv)
+                        bstore8s(ro, (16 * I + l15) * rowb + 2 * (16 * jv + 4 * l4), 0u, cvt4(ov[jv]));
+                }
+                // S^T <- e^{b_C} (.) (S^T + Kb^T U)  (chunk j-1: parity 1 - PAR),
+                // which equals e^{b_C} (.) S^T + Kh^T U
+#pragma unroll
+                for (int kb = 0; kb < SBK; ++kb) {
+                    const int Jk = SBK * I + kb;
+                    const int jc = 16 * Jk + 4 * l4;
+                    const f32x4 gm = *reinterpret_cast<const f32x4 *>(&sm.gam[1 - PAR][jc]);
+                    const bf16x8 k0f = frag_cols(sm.Kb[1 - PAR], PD, 0, 16 * Jk, lane);
+                    const bf16x8 k1f = frag_cols(sm.Kb[1 - PAR], PD, 32, 16 * Jk, lane);
+#pragma unroll
+                    for (int jv = 0; jv < 2; ++jv) {
+                        f32x4 sv = mfma32(k0f, uf[jv][0], St[kb][jv]);
+                        sv = mfma32(k1f, uf[jv][1], sv) * gm;
+                        St[kb][jv] = sv;
+                        *reinterpret_cast<bf16x4 *>(&sm.S[(16 * jv + l15) * PD + jc]) = cvt4(sv);
+                    }
                 }
             }
+            if (hasP && w < 7) {
+                // blocks (2,0), (3,0), (3,1) of A and P
+                const int I = w == 4 ? 2 : 3, J = w == 6 ? 1 : 0;
+                bf16x8 kf[KD], qf[KD], bf[KD];
+                frags(sm.K, I, kf);
+                frags(sm.Q, I, qf);
+                frags(sm.Kb[PAR], J, bf);
+                f32x4 aoff;
+                gram(kf, qf, bf, aoff, poff);
+                putL(I, J, aoff);
+            }
         }
-        {   // outputs of chunk j-1: every wave issues the stores, which land only
-            // for the state waves of a chunk that exists
-            const long long tc = t0 + (j - 1) * C;
-            const int Cc = (hasS && w >= 4) ? valid_rows(j - 1) : 0;
-            const unsigned rowb = (unsigned)(tokstride * 2);
-            const rsrc_t ro = make_rsrc(og + (size_t)tc * tokstride, Cc ? (Cc - 1) * rowb + BV * 2 : 0u);
-            const int I = w & 3;
-#pragma unroll
-            for (int jv = 0; jv < 2; ++jv)
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    bstore2(ro, (16 * I + 4 * l4 + e) * rowb + 2 * (16 * jv + l15), (bf16)ov[jv][e]);
-        }
-        if (hasG) scan(L, 1 - PAR);
-        load_g(L, j + 2);
+        if (j + 2 < nch) scan(L, par_tag);
+        load_g(L, j + 3);
         __syncthreads();
 
         // ================= phase C ========================================
@@ -567,6 +559,7 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
                 auto opYB = [&](int bj) -> bf16x4 {   // Y_jj[4*l4..][l15] = Y^T[l15][4*l4..]
                     return cvt4(*reinterpret_cast<const f32x4 *>(&sm.YT[(bj * 16 + l15) * PY + 4 * l4]));
                 };
+                const float bt0 = sm.beta[l15], bt1 = sm.beta[16 + l15], bt2 = sm.beta[32 + l15];
                 const f32x4 z0 = {0.f, 0.f, 0.f, 0.f};
                 const bf16x4 B00 = opYB(0), B11 = opYB(1), B22 = opYB(2);
                 const bf16x4 A11 = opYA(1), A22 = opYA(2), A33 = opYA(3);
@@ -580,18 +573,19 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
                 const f32x4 Y30 = -mfma16(
                     A33, cvt4(mfma16(L32, cvt4(Y20), mfma16(L31, cvt4(Y10), mfma16(L30, B00, z0)))), z0);
                 // T_ij = Y_ij diag(beta_j) -> T^T[s][r..r+3]
-                auto putT = [&](int bi, int bj, f32x4 yv) {
+                auto putT = [&](int bi, int bj, f32x4 yv, float bt) {
                     const int s = 16 * bj + l15;
-                    *reinterpret_cast<bf16x4 *>(&sm.TT[s * PCT + 16 * bi + 4 * l4]) = cvt4(yv * sm.beta[s]);
+                    *reinterpret_cast<bf16x4 *>(&sm.TT[s * PCT + 16 * bi + 4 * l4]) = cvt4(yv * bt);
                 };
-                putT(1, 0, Y10);
-                putT(2, 1, Y21);
-                putT(3, 2, Y32);
-                putT(2, 0, Y20);
-                putT(3, 1, Y31);
-                putT(3, 0, Y30);
+                putT(1, 0, Y10, bt0);
+                putT(2, 1, Y21, bt1);
+                putT(3, 2, Y32, bt2);
+                putT(2, 0, Y20, bt0);
+                putT(3, 1, Y31, bt1);
+                putT(3, 0, Y30, bt0);
             } else if (w >= 4) {
-                // Qt S0^T (kept for the outputs) and X = V - Kt S0^T, row block w-4
+                // Qt S0^T (kept for the outputs, transposed) and X = V - Kt S0^T,
+                // row block w-4
                 const int I = w - 4;
                 const int r0 = 16 * I + 4 * l4;
                 bf16x8 kf[KD], qf[KD];
@@ -600,8 +594,6 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
                     kf[kk] = frag_rows(sm.K, PD, 16 * I, 32 * kk, lane);
                     qf[kk] = frag_rows(sm.Q, PD, 16 * I, 32 * kk, lane);
                 }
-                f32x4 gr = {1.f, 1.f, 1.f, 1.f};
-                if (!CH) gr = *reinterpret_cast<const f32x4 *>(&sm.e1[PAR][r0]);
 #pragma unroll
                 for (int jv = 0; jv < 2; ++jv) {
                     bf16x8 sf[KD];
@@ -611,34 +603,46 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
 #pragma unroll
                     for (int kk = 0; kk < KD; ++kk) {
                         x = mfma32(kf[kk], sf[kk], x);
-                        o = mfma32(qf[kk], sf[kk], o);
+                        o = mfma32(sf[kk], qf[kk], o);
                     }
                     const int iv = 16 * jv + l15;
                     f32x4 xv;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        xv[e] = (float)sm.V[(r0 + e) * PV + iv] - gr[e] * x[e];
+                    for (int e = 0; e < 4; ++e) xv[e] = (float)sm.V[(r0 + e) * PV + iv] - x[e];
                     *reinterpret_cast<bf16x4 *>(&sm.XT[iv * PC + r0]) = cvt4(xv);
-                    accQS[jv] = o * gr;
+                    accQS[jv] = o;
                 }
             }
+            // P(j) blocks computed in phase B
+            if (w < 4) {
+                putP(w, w, pdiag);
+                if (w >= 1) putP(w, w - 1, poff);
+            } else if (w < 7) {
+                putP(w == 4 ? 2 : 3, w == 6 ? 1 : 0, poff);
+            }
         }
-        if (hasG) gate(L, 1 - PAR);
+        if (j + 2 < nch) prefix(PAR);
+        if (hasG) gate(L, std::integral_constant<int, 1 - PAR>{});
         load_qkvb(L, j + 2, PAR);
         __syncthreads();
     };
 
-    // ---- prologue: chunk 0 gated, chunk 1 loaded
+    // ---- prologue: chunks 0 and 1 scanned, chunk 0 gated, chunk 1 loaded
     {
         const LI L(tid0);
         // unconditional even without a chunk (the loads then return zeros):
         // every path waits on these registers before the loop
         load_g(L, 0);
         load_qkvb(L, 0, 0);
-        scan(L, 0);
-        __syncthreads();
-        gate(L, 0);
+        scan(L, std::integral_constant<int, 0>{});
         load_g(L, 1);
+        __syncthreads();
+        prefix(0);
+        scan(L, std::integral_constant<int, 1>{});
+        load_g(L, 2);
+        __syncthreads();
+        prefix(1);
+        gate(L, std::integral_constant<int, 0>{});
         load_qkvb(L, 1, 1);
     }
 
@@ -691,13 +695,8 @@ hipError_t launch_prefill_chunked(int D, const PrefillArgs &a, hipStream_t s) {
     const int ntile = D / BV;
     const long long blocks = ((units + 7) / 8) * 8 * ntile;
     dim3 grid((unsigned)blocks), block(NT);
-    if (D == 128) {
-        if (a.channel_gate) hipLaunchKernelGGL((chunked_kernel<128, true>), grid, block, 0, s, a);
-        else                hipLaunchKernelGGL((chunked_kernel<128, false>), grid, block, 0, s, a);
-    } else {
-        if (a.channel_gate) hipLaunchKernelGGL((chunked_kernel<64, true>), grid, block, 0, s, a);
-        else                hipLaunchKernelGGL((chunked_kernel<64, false>), grid, block, 0, s, a);
-    }
+    if (D == 128) hipLaunchKernelGGL((chunked_kernel<128>), grid, block, 0, s, a);
+    else          hipLaunchKernelGGL((chunked_kernel<64>), grid, block, 0, s, a);
     return hipGetLastError();
 }
 
