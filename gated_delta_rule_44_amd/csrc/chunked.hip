@@ -40,11 +40,12 @@
 // All contractions use bf16 operands with fp32 accumulation; the state is
 // carried in fp32 registers and rounded to bf16 only as an MFMA operand.
 //
-// Gate layout.  Lane l of wave w holds rows RPT (w RPW + l / CG) .. +RPT-1
-// of key channels 8 (l % CG) .. +7 (CG = D/8 channel groups, RPW = 64/CG row
+// Gate layout.  Lane l of wave w holds rows RPT (w RPW + l % RPW) .. +RPT-1
+// of key channels 8 (l / RPW) .. +7 (CG = D/8 channel groups, RPW = 64/CG row
 // groups per wave), so each load instruction reads whole rows; the prefix
-// sums over rows run inside the wave by shuffles, then across the waves
-// through per-wave totals in LDS that two waves turn into prefixes.
+// sums over rows run inside the wave across the RPW adjacent lanes of a
+// channel group (DPP), then across the waves through per-wave totals in LDS
+// that two waves turn into prefixes.
 #include <type_traits>
 
 #include "gdr_internal.h"
@@ -61,8 +62,8 @@ constexpr int PC = C + 8;   // padded LDS row length for C-wide bf16 rows
 constexpr int PCT = C + 16; // C-wide bf16 rows read by transpose loads: a row
                             // stride of 40 dwords puts 4 consecutive rows on
                             // disjoint banks
-constexpr int PL = C + 4;   // padded LDS row length of the fp32 L^T
-constexpr int PY = 20;      // padded row length of the fp32 16x16 blocks
+constexpr int PY = 24;      // padded row length of the bf16 Y^T blocks (read by
+                            // transpose loads: 4 consecutive rows on disjoint banks)
 constexpr int PV = BV + 8;  // padded LDS row length of the v tile
 
 // Per-thread indices used by every phase.
@@ -79,13 +80,35 @@ template <int D> struct LaneIds {
         w = __builtin_amdgcn_readfirstlane(t >> 6);
         l15 = lane & 15;
         l4 = lane >> 4;
-        cg = lane % CG;
-        rgl = lane / CG;
+        cg = lane / RPW;
+        rgl = lane % RPW;
         rg = w * RPW + rgl;
         vr = t >> 3;
         vc = (t & 7) * 4;
     }
 };
+
+// Inclusive prefix sum over the RPW (4 or 8) adjacent lanes of each group:
+// two quad permutes within the quad, then for RPW = 8 the last lane of the
+// lower quad added to the upper quad (quad broadcast, row_shr:4).
+template <int RPW>
+__device__ inline float group_scan(float x, int lane) {
+    auto dpp = [](float v, auto ctrl) -> float {
+        return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                     decltype(ctrl)::value, 0xF, 0xF, true));
+    };
+    const int q = lane & 3;
+    float y = dpp(x, std::integral_constant<int, 0x90>{});   // quad_perm [0,0,1,2]
+    x += q >= 1 ? y : 0.f;
+    y = dpp(x, std::integral_constant<int, 0x40>{});         // quad_perm [0,0,0,1]
+    x += q >= 2 ? y : 0.f;
+    if (RPW == 8) {
+        y = dpp(dpp(x, std::integral_constant<int, 0xFF>{}),  // quad_perm [3,3,3,3]
+                std::integral_constant<int, 0x114>{});        // row_shr:4
+        x += (lane & 4) ? y : 0.f;
+    }
+    return x;
+}
 
 template <int D> struct Smem {
     static constexpr int PD = D + 8;   // padded row length for D-wide rows
@@ -98,8 +121,10 @@ template <int D> struct Smem {
     alignas(16) bf16 XT[BV * PC];      // X^T, [i][s]
     alignas(16) bf16 UT[BV * PC];      // U^T, [i][s]
     alignas(16) bf16 V[C * PV];        // v tile, [r][i]
-    alignas(16) float LT[C * PL];      // L^T = (diag(beta) A)^T, [s][r]
-    alignas(16) float YT[4 * 16 * PY]; // inverted diagonal blocks, transposed: [b][c][r]
+    alignas(16) bf16 LTo[C * PCT];     // L^T = (diag(beta) A)^T below the diagonal blocks, [s][r]
+    alignas(16) bf16 YT[4 * 16 * PY];  // inverted diagonal blocks, transposed: [b][c][r]
+    alignas(16) float QS[8 * 64 * 4];  // Qt S0^T of the prep chunk, transposed, in
+                                       // accumulator order: [4 jv + I][lane][e]
     alignas(16) float beta[C];
     alignas(16) float gam[2][D];       // e^{b_C} per channel, by chunk parity
     // per chunk parity: the per-wave sums of the gate logs [w][j], turned in
@@ -116,9 +141,9 @@ template <int D> struct Smem {
 //                         forward substitution, the rest by MFMA), P, X, Qt S0^T
 //   chunk j+1 ("gate"):   gated operands in registers
 //   chunk j+2 ("scan"):   prefix sums of the gate logs
-//   phase A: U(j-1) || store gated operands of chunk j
+//   phase A: U(j-1) (waves 0-3) || store gated operands of chunk j
 //   phase B: waves 0-3: the diagonal block (b, b) of A and P, its inverse,
-//            and block (b, b-1);  waves 4-7: O(j-1) and the state update
+//            block (b, b-1), then O(j-1);  waves 4-7: the state update
 //            (j-1), then blocks (2,0), (3,0), (3,1);  all: prefix sums of
 //            the gate logs of chunk j+2 within each wave, loads of g(j+3)
 //   phase C: T(j) off-diagonal (wave 0) || Qt S0^T(j), X(j) (waves 4-7);
@@ -269,26 +294,16 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
                 cum[par][i][e] = run[e];
             }
         }
-        // scan of the row-group totals across the wave: the eight channels'
-        // shuffles of one step are issued together so their LDS round trips
-        // overlap
+        // scan of the row-group totals across the lanes of the channel group
         float incl[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) incl[e] = run[e];
-#pragma unroll
-        for (int off = CG; off < 64; off *= 2) {
-            float y[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) y[e] = __shfl_up(incl[e], off);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) incl[e] += L.lane >= off ? y[e] : 0.f;
-        }
+        for (int e = 0; e < 8; ++e) incl[e] = group_scan<RPW>(run[e], L.lane);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
 #pragma unroll
             for (int i = 0; i < RPT; ++i) cum[par][i][e] += incl[e] - run[e];
         }
-        if (L.lane >= 64 - CG) {
+        if (L.rgl == RPW - 1) {
             float *t = &sm.pfx[par][L.w * D + 8 * L.cg];
             *reinterpret_cast<f32x4 *>(t) = f32x4{incl[0], incl[1], incl[2], incl[3]};
             *reinterpret_cast<f32x4 *>(t + 4) = f32x4{incl[4], incl[5], incl[6], incl[7]};
@@ -363,11 +378,6 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
         if (L.tid < C) sm.beta[L.tid] = rb[par];
     };
 
-    // Qt S0^T of the prep chunk, transposed ([i][r]: lane holds columns
-    // 16 jv + 4 l4 .. +3 of row 16 I + l15), kept for its outputs
-    f32x4 accQS[2];
-    accQS[0] = accQS[1] = f32x4{0.f, 0.f, 0.f, 0.f};
-
     // ---- one pipeline iteration; PAR = parity of the prep chunk j
     auto iteration = [&](auto par_tag, long long j) {
         constexpr int PAR = decltype(par_tag)::value;
@@ -392,15 +402,12 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
                 pv = mfma32(qf[kk], bf[kk], pv);
             }
         };
-        // L^T[s][r] = beta_r A[r][s] for s < r
+        // L^T[s][r] = beta_r A[r][s] of a block below the diagonal (I > J)
         auto putL = [&](int I, int J, f32x4 av) {
             const int s = 16 * J + l15;
             const int r0 = 16 * I + 4 * l4;
             const f32x4 br = *reinterpret_cast<const f32x4 *>(&sm.beta[r0]);
-            f32x4 lv;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) lv[e] = s < r0 + e ? av[e] * br[e] : 0.f;
-            *reinterpret_cast<f32x4 *>(&sm.LT[s * PL + r0]) = lv;
+            *reinterpret_cast<bf16x4 *>(&sm.LTo[s * PCT + r0]) = cvt4(av * br);
         };
         // P^T[s][r] = P[r][s] for s <= r
         auto putP = [&](int I, int J, f32x4 pv) {
@@ -415,18 +422,18 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
         f32x4 pdiag = {0.f, 0.f, 0.f, 0.f}, poff = pdiag;
 
         // ================= phase A ========================================
-        if (hasS) {   // U = T X of chunk j-1; wave w: row block w>>1, value block w&1
-            const int I = w >> 1, Jv = w & 1;
-            f32x4 u = {0.f, 0.f, 0.f, 0.f};
+        if (hasS && w < 4) {   // U = T X of chunk j-1; wave w: row block w
+            const int I = w;
             const bf16x8 t0f = frag_cols(sm.TT, PCT, 0, 16 * I, lane);
-            const bf16x8 x0f = frag_rows(sm.XT, PC, 16 * Jv, 0, lane);
-            if (I >= 2) {   // T is lower triangular: rows < 32 need s < 32 only
-                const bf16x8 t1f = frag_cols(sm.TT, PCT, 32, 16 * I, lane);
-                const bf16x8 x1f = frag_rows(sm.XT, PC, 16 * Jv, 32, lane);
-                u = mfma32(t1f, x1f, u);
+            bf16x8 t1f = {};
+            if (I >= 2) t1f = frag_cols(sm.TT, PCT, 32, 16 * I, lane);
+#pragma unroll
+            for (int jv = 0; jv < 2; ++jv) {
+                f32x4 u = mfma32(t0f, frag_rows(sm.XT, PC, 16 * jv, 0, lane), f32x4{0.f, 0.f, 0.f, 0.f});
+                if (I >= 2)   // T is lower triangular: rows < 32 need s < 32 only
+                    u = mfma32(t1f, frag_rows(sm.XT, PC, 16 * jv, 32, lane), u);
+                *reinterpret_cast<bf16x4 *>(&sm.UT[(16 * jv + l15) * PC + 16 * I + 4 * l4]) = cvt4(u);
             }
-            u = mfma32(t0f, x0f, u);
-            *reinterpret_cast<bf16x4 *>(&sm.UT[(16 * Jv + l15) * PC + 16 * I + 4 * l4]) = cvt4(u);
         }
         if (hasP) store_gate(L, PAR);
         __syncthreads();
@@ -441,72 +448,75 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
                 frags(sm.K, b, kf);
                 frags(sm.Q, b, qf);
                 frags(sm.Kb[PAR], b, bf);
-                f32x4 ad;
+                f32x4 ad, adT = {0.f, 0.f, 0.f, 0.f};
                 gram(kf, qf, bf, ad, pdiag);
-                putL(b, b, ad);
+#pragma unroll
+                for (int kk = 0; kk < KD; ++kk) adT = mfma32(bf[kk], kf[kk], adT);   // A_bb^T
                 f32x4 aoff = {0.f, 0.f, 0.f, 0.f};
                 if (b >= 1) {
                     frags(sm.Kb[PAR], b - 1, bf);
                     gram(kf, qf, bf, aoff, poff);
                 }
-                __threadfence_block();
-                // (I + L_bb) Y = I by forward substitution in fp32.  Lane
-                // (column cq = lane >> 2, group gq = lane & 3) owns rows
-                // 4gq..4gq+3 of column cq; it preloads L[4gq+e][r] for all r
-                // (row r of L^T), and each y_r is broadcast from its owner
-                // lane to the quad by DPP, so no LDS access sits in the
-                // dependency chain.
-                const int cq = lane >> 2, gq4 = lane & 3;
-                f32x4 Lv[16];
+                // M = L_bb = strict_lower(diag(beta) A_bb) as acc(M) and
+                // acc(M^T); Y = (I + M)^{-1} = (I - M)(I + M^2)(I + M^4)(I + M^8)
+                // (M^16 = 0).  An MFMA with A operand acc(X^T) and B operand
+                // acc(Z) yields acc(X Z).
+                const float bl = sm.beta[16 * b + l15];
+                const f32x4 br4 = *reinterpret_cast<const f32x4 *>(&sm.beta[16 * b + 4 * l4]);
+                f32x4 MT, Mn, I4;
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    Lv[r] = *reinterpret_cast<const f32x4 *>(&sm.LT[(16 * b + r) * PL + 16 * b + 4 * gq4]);
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f}, y4 = acc;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int e = r & 3, go = r >> 2;
-                    const float own = r == cq ? 1.f : (r > cq ? -acc[e] : 0.f);
-                    const float yr = quad_bcast(own, go);
-                    y4[e] = gq4 == go ? yr : y4[e];
-                    acc += Lv[r] * yr;   // L is strictly lower: rows <= r add zero
+                for (int e = 0; e < 4; ++e) {
+                    const int sl = 4 * l4 + e;
+                    MT[e] = sl < l15 ? bl * adT[e] : 0.f;
+                    Mn[e] = sl > l15 ? br4[e] * ad[e] : 0.f;
+                    I4[e] = sl == l15 ? 1.f : 0.f;
                 }
-                {
-                    const float bc = sm.beta[16 * b + cq];
-                    // T[16b+4gq+e][16b+cq] -> T^T row 16b+cq;  Y^T[b][cq][4gq..]
-                    *reinterpret_cast<bf16x4 *>(&sm.TT[(16 * b + cq) * PCT + 16 * b + 4 * gq4]) = cvt4(y4 * bc);
-                    *reinterpret_cast<f32x4 *>(&sm.YT[(b * 16 + cq) * PY + 4 * gq4]) = y4;
-                }
+                const f32x4 M2 = mfma16z(cvt4(MT), cvt4(Mn));
+                const f32x4 M2T = mfma16z(cvt4(Mn), cvt4(MT));
+                const f32x4 Z1 = mfma16(cvt4(M2T), cvt4(I4 - Mn), I4 - Mn);
+                const f32x4 M4 = mfma16z(cvt4(M2T), cvt4(M2));
+                const f32x4 M4T = mfma16z(cvt4(M2), cvt4(M2T));
+                const f32x4 Z2 = mfma16(cvt4(M4T), cvt4(Z1), Z1);
+                const f32x4 M8T = mfma16z(cvt4(M4), cvt4(M4T));
+                const f32x4 Y = mfma16(cvt4(M8T), cvt4(Z2), Z2);
+                // acc(Y): Y[4 l4 + e][l15] -> T^T[s = l15][r] = Y[r][s] beta_s and
+                // Y^T[b][c = l15][r]
+                *reinterpret_cast<bf16x4 *>(&sm.TT[(16 * b + l15) * PCT + 16 * b + 4 * l4]) = cvt4(Y * bl);
+                *reinterpret_cast<bf16x4 *>(&sm.YT[(16 * b + l15) * PY + 4 * l4]) = cvt4(Y);
                 if (b >= 1) putL(b, b - 1, aoff);
+            }
+            if (hasS) {
+                // outputs of chunk j-1, row block w.  O^T = U^T P^T + (Qt S0^T)^T:
+                // lane holds columns 16 jv + 4 l4 .. +3 of output row 16 I + l15.
+                const int I = w;
+                const bf16x8 p0 = frag_cols(sm.PT, PCT, 0, 16 * I, lane);
+                bf16x8 p1 = {};
+                if (I >= 2) p1 = frag_cols(sm.PT, PCT, 32, 16 * I, lane);
+                f32x4 ov[2];
+#pragma unroll
+                for (int jv = 0; jv < 2; ++jv) {
+                    const f32x4 qs = *reinterpret_cast<const f32x4 *>(&sm.QS[((4 * jv + I) * 64 + lane) * 4]);
+                    f32x4 o = mfma32(frag_rows(sm.UT, PC, 16 * jv, 0, lane), p0, qs);
+                    if (I >= 2) o = mfma32(frag_rows(sm.UT, PC, 16 * jv, 32, lane), p1, o);
+                    ov[jv] = o * a.scale;
+                }
+                const long long tc = t0 + (j - 1) * C;
+                const int Cc = valid_rows(j - 1);
+                const unsigned rowb = (unsigned)(tokstride * 2);
+                const rsrc_t ro = make_rsrc(og + (size_t)tc * tokstride, (Cc - 1) * rowb + BV * 2);
+#pragma unroll
+                for (int jv = 0; jv < 2; ++jv)
+                    bstore8s(ro, (16 * I + l15) * rowb + 2 * (16 * jv + 4 * l4), 0u, cvt4(ov[jv]));
             }
         } else {
             if (hasS) {
-                // outputs and state update of chunk j-1 (row block / key
-                // blocks of this wave).  O^T = U^T P^T + (Qt S0^T)^T: lane
-                // holds columns 16 jv + 4 l4 .. +3 of output row 16 I + l15.
+                // state update of chunk j-1 (key blocks of this wave)
                 const int I = w - 4;
-                const bf16x8 p0 = frag_cols(sm.PT, PCT, 0, 16 * I, lane);
-                const bf16x8 p1 = frag_cols(sm.PT, PCT, 32, 16 * I, lane);
                 bf16x8 uf[2][2];
 #pragma unroll
                 for (int jv = 0; jv < 2; ++jv) {
                     uf[jv][0] = frag_rows(sm.UT, PC, 16 * jv, 0, lane);
                     uf[jv][1] = frag_rows(sm.UT, PC, 16 * jv, 32, lane);
-                }
-                f32x4 ov[2];
-#pragma unroll
-                for (int jv = 0; jv < 2; ++jv) {
-                    f32x4 o = mfma32(uf[jv][0], p0, accQS[jv]);
-                    if (I >= 2) o = mfma32(uf[jv][1], p1, o);
-                    ov[jv] = o * a.scale;
-                }
-                {
-                    const long long tc = t0 + (j - 1) * C;
-                    const int Cc = valid_rows(j - 1);
-                    const unsigned rowb = (unsigned)(tokstride * 2);
-                    const rsrc_t ro = make_rsrc(og + (size_t)tc * tokstride, (Cc - 1) * rowb + BV * 2);
-#pragma unroll
-                    for (int jv = 0; jv < 2; ++jv)
-                        bstore8s(ro, (16 * I + l15) * rowb + 2 * (16 * jv + 4 * l4), 0u, cvt4(ov[jv]));
                 }
                 // S^T <- e^{b_C} (.) (S^T + Kb^T U)  (chunk j-1: parity 1 - PAR),
                 // which equals e^{b_C} (.) S^T + Kh^T U
@@ -548,16 +558,14 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
                 // off-diagonal blocks of T:  Y_ij = -Y_ii sum_{k=j}^{i-1} L_ik Y_kj
                 // on 16x16x16 MFMAs (A operand: row l15, cols 4*l4..+3;
                 // B operand: rows 4*l4..+3, col l15 == the accumulator layout)
-                auto opL = [&](int bi, int bk) -> bf16x4 {   // rows of L_ik
-                    const float *p = &sm.LT[(16 * bk + 4 * l4) * PL + 16 * bi + l15];
-                    return bf16x4{(bf16)p[0], (bf16)p[PL], (bf16)p[2 * PL], (bf16)p[3 * PL]};
+                auto opL = [&](int bi, int bk) -> bf16x4 {   // L_ik[l15][4*l4..] = L^T[16bk+4*l4..][16bi+l15]
+                    return frag_col4(sm.LTo, PCT, 16 * bk, 16 * bi, lane);
                 };
                 auto opYA = [&](int bi) -> bf16x4 {   // Y_ii[l15][4*l4..] = Y^T[4*l4..][l15]
-                    const float *p = &sm.YT[(bi * 16 + 4 * l4) * PY + l15];
-                    return bf16x4{(bf16)p[0], (bf16)p[PY], (bf16)p[2 * PY], (bf16)p[3 * PY]};
+                    return frag_col4(sm.YT, PY, 16 * bi, 0, lane);
                 };
                 auto opYB = [&](int bj) -> bf16x4 {   // Y_jj[4*l4..][l15] = Y^T[l15][4*l4..]
-                    return cvt4(*reinterpret_cast<const f32x4 *>(&sm.YT[(bj * 16 + l15) * PY + 4 * l4]));
+                    return *reinterpret_cast<const bf16x4 *>(&sm.YT[(bj * 16 + l15) * PY + 4 * l4]);
                 };
                 const float bt0 = sm.beta[l15], bt1 = sm.beta[16 + l15], bt2 = sm.beta[32 + l15];
                 const f32x4 z0 = {0.f, 0.f, 0.f, 0.f};
@@ -584,8 +592,8 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
                 putT(3, 1, Y31, bt1);
                 putT(3, 0, Y30, bt0);
             } else if (w >= 4) {
-                // Qt S0^T (kept for the outputs, transposed) and X = V - Kt S0^T,
-                // row block w-4
+                // Qt S0^T (for the outputs, transposed, to LDS) and
+                // X = V - Kt S0^T, row block w-4
                 const int I = w - 4;
                 const int r0 = 16 * I + 4 * l4;
                 bf16x8 kf[KD], qf[KD];
@@ -606,11 +614,12 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
                         o = mfma32(sf[kk], qf[kk], o);
                     }
                     const int iv = 16 * jv + l15;
+                    const bf16x4 vr4 = frag_col4(sm.V, PV, 16 * I, 16 * jv, lane);   // V[r0 + e][iv]
                     f32x4 xv;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) xv[e] = (float)sm.V[(r0 + e) * PV + iv] - x[e];
+                    for (int e = 0; e < 4; ++e) xv[e] = (float)vr4[e] - x[e];
                     *reinterpret_cast<bf16x4 *>(&sm.XT[iv * PC + r0]) = cvt4(xv);
-                    accQS[jv] = o;
+                    *reinterpret_cast<f32x4 *>(&sm.QS[((4 * jv + I) * 64 + lane) * 4]) = o;
                 }
             }
             // P(j) blocks computed in phase B
