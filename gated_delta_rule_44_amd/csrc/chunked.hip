@@ -379,12 +379,12 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
     };
 
     // ---- one pipeline iteration; PAR = parity of the prep chunk j
-    auto iteration = [&](auto par_tag, long long j) {
+    auto iteration = [&](auto par_tag, auto s_tag, auto p_tag, long long j) {
         constexpr int PAR = decltype(par_tag)::value;
         const LI L(opaque(tid0));
         const int lane = L.lane, w = L.w, l15 = L.l15, l4 = L.l4;
-        const bool hasS = j >= 1;
-        const bool hasP = j < nch;
+        constexpr bool hasS = decltype(s_tag)::value;   // j >= 1
+        constexpr bool hasP = decltype(p_tag)::value;   // j < nch
         const bool hasG = j + 1 < nch;
 
         auto frags = [&](const bf16 *M, int blk, bf16x8 (&f)[KD]) {
@@ -655,15 +655,27 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
         load_qkvb(L, 1, 1);
     }
 
-    // iterations j = 0..nch, in (even, odd) pairs with a trailing even one
-    // peeled off: the loop is entered only from the end of an odd iteration,
-    // so the loads in flight at its head are always the same
-    long long j = 0;
-    for (; j + 1 <= nch; j += 2) {
-        iteration(std::integral_constant<int, 0>{}, j);
-        iteration(std::integral_constant<int, 1>{}, j + 1);
+    // iterations j = 0..nch: iteration 0 has no state chunk and iteration nch
+    // no prep chunk; the ones between have both and are specialised for it,
+    // so each wave's work in a phase is straight-line code.  They run in
+    // (odd, even) pairs, so the loop is always entered from the end of an even
+    // iteration and the loads in flight at its head are always the same.
+    if (nch > 0) {
+        using E = std::integral_constant<int, 0>;
+        using O = std::integral_constant<int, 1>;
+        iteration(E{}, std::false_type{}, std::true_type{}, 0);
+        long long j = 1;
+        for (; j + 1 < nch; j += 2) {
+            iteration(O{}, std::true_type{}, std::true_type{}, j);
+            iteration(E{}, std::true_type{}, std::true_type{}, j + 1);
+        }
+        if (j < nch) {
+            iteration(O{}, std::true_type{}, std::true_type{}, j);
+            ++j;
+        }
+        if (j & 1) iteration(O{}, std::true_type{}, std::false_type{}, j);
+        else       iteration(E{}, std::true_type{}, std::false_type{}, j);
     }
-    if (j <= nch) iteration(std::integral_constant<int, 0>{}, j);
 
     if (a.ht) {
         const LI L(tid0);
