@@ -220,6 +220,22 @@ def test_prefill_strong_decay(gate):
     check_prefill(x, o, ht, torch.bfloat16)
 
 
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
+def test_prefill_decay_at_the_documented_limit(gate):
+    """A constant gate of -75/64 per token puts the cumulative log decay of
+    every full chunk at -75, inside the bound the header states (-80): the
+    chunk's e^{+-b} factors span 65 orders of magnitude and the outputs must
+    still meet the bf16 bar."""
+    x = synthetic.prefill_inputs(1, 200, 2, 128, torch.bfloat16, gate, seed=23, device=DEV)
+    x["g"] = torch.full_like(x["g"], -75.0 / 64.0)
+    announce("decay at the limit %s: gate sum per chunk %.1f"
+             % (gate, float(x["g"][0, :64].sum(0).min())))
+    o, ht = run_prefill(x)
+    assert bool(torch.isfinite(o.float()).all()) and bool(torch.isfinite(ht).all())
+    eo, eh = check_prefill(x, o, ht, torch.bfloat16)
+    announce("  rel-fro o=%.2e ht=%.2e" % (eo, eh))
+
+
 def test_prefill_guard_bands_scalar_gate_workspace():
     """Scalar gate (prep and recurrence kernels): canaries around o, ht and
     the exactly sized workspace stay untouched."""
