@@ -138,7 +138,8 @@ template <int D> struct Smem {
 // once, with three workgroup barriers:
 //   chunk j-1 ("state"):  U = T X, then O = Qt S0^T + P U and the state update
 //   chunk j   ("prep"):   gated operands -> LDS, A -> L, T (diagonal blocks by
-//                         forward substitution, the rest by MFMA), P, X, Qt S0^T
+//                         the MFMA series, the rest by block substitution), P,
+//                         X, Qt S0^T
 //   chunk j+1 ("gate"):   gated operands in registers
 //   chunk j+2 ("scan"):   prefix sums of the gate logs
 //   phase A: U(j-1) (waves 0-3) || store gated operands of chunk j
@@ -157,7 +158,6 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
     using LI = LaneIds<D>;
     constexpr int PD = Sm::PD;
     constexpr int NTILE = D / BV;
-    constexpr int CG = LI::CG;
     constexpr int RPW = LI::RPW;
     constexpr int RPT = LI::RPT;
     constexpr int KD = D / 32;         // x32 steps over a D-long contraction
@@ -223,10 +223,10 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
         }
     }
 
-    // raw inputs held in registers ahead of use: the gate logs of the next
-    // chunk (reloaded right after its prefix sums are taken), q and k of the
-    // next chunk (reloaded right after they are gated), and v/beta of the
-    // next two chunks (by chunk parity)
+    // raw inputs held in registers ahead of use: the gate logs of the chunk
+    // to be scanned next (reloaded right after its prefix sums are taken), q
+    // and k of the chunk to be gated next (reloaded right after they are
+    // gated), and v/beta of the next two chunks (by chunk parity)
     bf16x8 rq[RPT], rk[RPT];
     f32x4 rgc[RPT][2];
     bf16x4 rv[2];
