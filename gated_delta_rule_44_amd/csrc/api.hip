@@ -44,6 +44,10 @@ gdr_status finish(hipError_t launch, hipStream_t s, const char *what) {
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
+// (sequence, head) pairs of one prefill call: the prefill kernels launch up
+// to four workgroups per pair, rounded up to eight pairs, in a 31-bit grid
+constexpr long long kMaxPairs = 1LL << 28;
+
 gdr_status check_common(int dt, int gk, int Dk, int Dv, const char *what) {
     if (dt != GDR_F32 && dt != GDR_BF16)
         return fail(GDR_EINVAL, "%s: dtype %d is not GDR_F32 or GDR_BF16", what, dt);
@@ -140,6 +144,11 @@ gdr_status gdr_prefill_chunked(enum gdr_dtype dt, enum gdr_gate gk, int B, int T
         return fail(GDR_EINVAL, "%s: bad sizes B=%d T=%d H=%d", what, B, T, H);
     if ((long long)B * T * H * Dk >= (1LL << 40))
         return fail(GDR_EUNSUPPORTED, "%s: problem too large", what);
+    // one workgroup per (sequence, head, value slice): the grid must stay a
+    // 31-bit count (with the bound above, so does the number of chunk records)
+    if ((long long)B * H > kMaxPairs)
+        return fail(GDR_EUNSUPPORTED, "%s: %lld (sequence, head) pairs exceed %lld", what,
+                    (long long)B * H, kMaxPairs);
     st = check_prefill_ptrs(what, q, k, v, g, beta, h0, o, ht, (long long)B * T);
     if (st != GDR_OK) return st;
     if (h0 && ht && h0 != ht) {
@@ -180,6 +189,9 @@ gdr_status gdr_prefill_chunked_varlen(enum gdr_dtype dt, enum gdr_gate gk, int N
         return fail(GDR_EINVAL, "%s: bad sizes N=%d T_total=%d H=%d", what, N, T_total, H);
     if ((long long)T_total * H * Dk >= (1LL << 40))
         return fail(GDR_EUNSUPPORTED, "%s: problem too large", what);
+    if ((long long)N * H > kMaxPairs)
+        return fail(GDR_EUNSUPPORTED, "%s: %lld (sequence, head) pairs exceed %lld", what,
+                    (long long)N * H, kMaxPairs);
     if (N == 0) return GDR_OK;
     if (!cu_seqlens) return fail(GDR_EINVAL, "%s: cu_seqlens is NULL", what);
     if (cu_seqlens_host) {

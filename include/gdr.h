@@ -33,7 +33,10 @@
  *   - gdr_last_error() returns a thread-local description of the last
  *     non-OK status.  No C++ exception crosses this interface; all entry
  *     points are reentrant.
- *   - Supported shapes: Dk == Dv, Dk in {64, 128}; chunk == 64 (prefill).
+ *   - Supported shapes: Dk == Dv, Dk in {64, 128}; chunk == 64 (prefill);
+ *     per prefill call fewer than 2^40 elements in q and at most 2^28
+ *     (sequence, head) pairs, per decode call fewer than 2^31 stepped
+ *     (layer, b, h) slots (GDR_EUNSUPPORTED otherwise).
  *     q, k, v and o share one dtype (GDR_F32 or GDR_BF16); g, beta, states
  *     are always fp32.  bf16 outputs are rounded to nearest-even.
  *   - Setting the environment variable GDR_DEBUG=1 makes each call

@@ -79,6 +79,7 @@ def prefill(lib, dt=1, gk=0, B=1, T=64, H=1, Dk=128, Dv=128, chunk=64, q=FAKE,
     (dict(B=-1), EINVAL, "bad sizes"),
     (dict(T=-5), EINVAL, "bad sizes"),
     (dict(H=0), EINVAL, "bad sizes"),
+    (dict(B=1 << 20, T=1, H=1 << 9), EUNSUPPORTED, "(sequence, head) pairs exceed"),
     (dict(q=None), EINVAL, "q is NULL"),
     (dict(k=MIS), EINVAL, "k is not 16-byte aligned"),
     (dict(o=None), EINVAL, "o is NULL"),
@@ -120,6 +121,8 @@ def test_varlen_rejects(lib):
     assert "workspace" in lib.gdr_last_error().decode()
     assert varlen(lib, ws_bytes=8) == EINVAL
     assert varlen(lib, N=0) == 0
+    assert varlen(lib, N=1 << 20, H=1 << 9) == EUNSUPPORTED
+    assert "pairs exceed" in lib.gdr_last_error().decode()
 
 
 def test_decode_rejects(lib):
