@@ -143,6 +143,32 @@ def decode_inputs(L, B, H, D, dtype=torch.bfloat16, place=None, seed=0,
     return dict(q=q, k=k, v=v, g=g, beta=beta, pool=st, placement=place)
 
 
+def pool_states(P, H, D, seed=0, device="cpu"):
+    """A state pool [P,H,D,D] fp32 with 0.02*N(0,1) entries (the law of the
+    initial states), drawn slot by slot."""
+    gen = _gen(seed, device)
+    st = torch.empty((P, H, D, D), device=device, dtype=torch.float32)
+    for p in range(P):
+        st[p].normal_(0.0, 0.02, generator=gen)
+    return st
+
+
+def serving_slots(B, P, idle=0, seed=0):
+    """Distinct pool slots for B sequences (a seeded draw from 0..P-1 with
+    numpy's PCG64), `idle` of them replaced by -1.  int32 numpy array."""
+    rng = np.random.default_rng(seed)
+    s = rng.permutation(P)[:B].astype(np.int32)
+    if idle:
+        s[rng.choice(B, idle, replace=False)] = -1
+    return s
+
+
+def accepted_counts(B, n, seed=0):
+    """Accepted prefix length of each sequence's n drafted tokens, uniform
+    on 0..n (numpy's PCG64).  int32 numpy array."""
+    return np.random.default_rng(seed).integers(0, n + 1, B).astype(np.int32)
+
+
 @dataclass(frozen=True)
 class Workload:
     name: str

@@ -133,3 +133,78 @@ def decode(q, k, v, g, beta, state, scale: float = 1.0, threads=None, lib=None):
 
 def max_threads(lib=None) -> int:
     return (lib or load()).gdr_oracle_max_threads()
+
+
+def _slot_ok(s, pool):
+    return 0 <= int(s) < pool
+
+
+def decode_tokens(q, k, v, g, beta, state_pool, slot=None, checkpoints=False,
+                  scale: float = 1.0, threads=None, lib=None):
+    """n decode tokens for each of B sequences whose states live in a pool.
+
+    q,k [B,n,H,Dk], v [B,n,H,Dv], g [B,n,H] or [B,n,H,Dk], beta [B,n,H],
+    state_pool [P,H,Dv,Dk], slot [B] (None: slot b; a value outside 0..P-1
+    marks an idle sequence).  Written out from the definition: the state of
+    each active sequence is gathered from its slot, the recurrence runs over
+    its n tokens (``forward``), and the final state is scattered back -- or,
+    with checkpoints, the state after token t is the final state of the
+    recurrence over tokens 0..t (one ``forward`` per prefix) and the pool is
+    left as it was.  Returns (o [B,n,H,Dv] with NaN rows for idle sequences,
+    new pool [P,H,Dv,Dk], checkpoints [B,n,H,Dv,Dk] or None), all float64.
+    """
+    qf, kf, vf, gf, bf = (_f32(x) for x in (q, k, v, g, beta))
+    pool = _f32(state_pool)
+    B, n = qf.shape[:2]
+    P = pool.shape[0]
+    slots = np.arange(B) if slot is None else np.asarray(
+        slot.cpu() if hasattr(slot, "cpu") else slot, dtype=np.int64)
+    act = np.array([b for b in range(B) if _slot_ok(slots[b], P)], dtype=np.int64)
+    o = np.full(vf.shape, np.nan)
+    new_pool = pool.astype(np.float64)
+    ck = None
+    if checkpoints:
+        ck = np.full((B, n) + pool.shape[1:], np.nan)
+    if len(act) == 0 or n == 0:
+        return o, new_pool, ck
+    h0 = pool[slots[act]]
+    sel = lambda x: x[act]  # noqa: E731
+    o_a, ht = forward(sel(qf), sel(kf), sel(vf), sel(gf), sel(bf), h0=h0,
+                      scale=scale, threads=threads, lib=lib)
+    o[act] = o_a
+    if checkpoints:
+        for t in range(n):
+            pre = lambda x: np.ascontiguousarray(x[act, :t + 1])  # noqa: E731
+            _, st = forward(pre(qf), pre(kf), pre(vf), pre(gf), pre(bf), h0=h0,
+                            scale=scale, threads=threads, lib=lib)
+            ck[act, t] = st
+    else:
+        new_pool[slots[act]] = ht
+    return o, new_pool, ck
+
+
+def forward_pool(q, k, v, g, beta, cu_seqlens, state_pool, h0_slot, ht_slot,
+                 scale: float = 1.0, threads=None, lib=None):
+    """Packed-batch recurrence with initial and final states in a pool.
+
+    Sequence n starts from state_pool[h0_slot[n]] (zeros when the slot is
+    outside 0..P-1) and its final state is written to state_pool[ht_slot[n]]
+    (nothing when outside).  Gather, ``forward``, scatter.  Returns
+    (o [T_tot,H,Dv], new pool [P,H,Dv,Dk]) as float64.
+    """
+    pool = _f32(state_pool)
+    P = pool.shape[0]
+    to_np = lambda x: np.asarray(x.cpu() if hasattr(x, "cpu") else x, dtype=np.int64)  # noqa: E731
+    s0, s1 = to_np(h0_slot), to_np(ht_slot)
+    N = len(s0)
+    h0 = np.zeros((N,) + pool.shape[1:], dtype=np.float32)
+    for i in range(N):
+        if _slot_ok(s0[i], P):
+            h0[i] = pool[s0[i]]
+    o, ht = forward(q, k, v, g, beta, h0=h0, cu_seqlens=cu_seqlens, scale=scale,
+                    threads=threads, lib=lib)
+    new_pool = pool.astype(np.float64)
+    for i in range(N):
+        if _slot_ok(s1[i], P):
+            new_pool[s1[i]] = ht[i]
+    return o, new_pool
