@@ -20,8 +20,10 @@ The same line carries:
                 the same workload (the first tokens of every sequence/head)
   secondary     the other hot-path entry points measured in the same run:
                 KDA prefill, the placement-driven decode step (state-update
-                GB/s and % of HBM peak) and the packed variable-length KDA
-                prefill.
+                GB/s and % of HBM peak), the packed variable-length KDA
+                prefill, the drafted decode (4 tokens with per-token
+                checkpoints, then the commit of the accepted prefixes) on a
+                slot-indexed pool, and the packed KDA prefill through a pool.
 
 Defaults: 100 warmup steps and 200 timed steps (a fifth of each for the
 decode and varlen workloads): the GPU reaches its steady clock only after
@@ -29,7 +31,8 @@ about a hundred prefill calls, so shorter warm-ups time part of the ramp.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
                        [--only-headline] [--no-cpu-baseline]
-                       [--only {kda_prefill,decode,varlen}]   (one workload, for profiling)
+                       [--only {kda_prefill,decode,varlen,draft,varlen_pool}]
+                       (one workload, for profiling)
 """
 import argparse
 import json
@@ -164,6 +167,58 @@ def bench_decode(gdr, synthetic, torch, dev, steps, warmup):
     return ms, n_gdn, n_kda, synthetic.placement_string(place)
 
 
+def bench_draft(gdr, synthetic, torch, dev, steps, warmup):
+    """Drafted decode: 4 tokens for 256 sequences x 32 heads (GDN, bf16) whose
+    states sit in a 512-slot pool, with a checkpoint after every token, then
+    the commit of the accepted prefixes.  The two calls are timed apart."""
+    B, n, H, P = 256, 4, 32, 512
+    x = synthetic.prefill_inputs(B, n, H, D, torch.bfloat16, "scalar", seed=1005,
+                                 h0=False, device=dev)
+    pool = synthetic.pool_states(P, H, D, seed=1006, device=dev)
+    slot = torch.from_numpy(synthetic.serving_slots(B, P, seed=1007)).to(dev)
+    acc_np = synthetic.accepted_counts(B, n, seed=1008)
+    acc = torch.from_numpy(acc_np).to(dev)
+    ck = torch.empty((B, n, H, D, D), device=dev, dtype=torch.float32)
+    o = torch.empty_like(x["v"])
+    stream = torch.cuda.current_stream(dev)
+    args = [x[k] for k in ("q", "k", "v", "g", "beta")]
+
+    def draft(i):
+        gdr.decode_tokens(*args, pool, slot=slot, checkpoints=ck, o=o)
+
+    def commit(i):
+        gdr.decode_commit(ck, acc, pool, slot=slot)
+    ms_d = timed(draft, steps, warmup, stream)
+    ms_c = timed(commit, steps, warmup, stream)
+    kept = int((acc_np >= 1).sum())
+    del x, pool, ck, o
+    return ms_d, ms_c, B, n, H, kept
+
+
+def bench_varlen_pool(gdr, synthetic, torch, dev, steps, warmup):
+    """The KDA packed workload with its states in a 40-slot pool (each
+    sequence starts from one slot and ends in another)."""
+    lens = synthetic.varlen_lengths(943)
+    N, H, P = len(lens), 32, 40
+    x = synthetic.varlen_inputs(lens, H, D, torch.bfloat16, "channel", seed=1004,
+                                h0=False, device=dev)
+    pool = synthetic.pool_states(P, H, D, seed=1009, device=dev)
+    import numpy as np
+    h0s = np.arange(N, dtype=np.int32)
+    hts = np.arange(N, 2 * N, dtype=np.int32)
+    h0t, htt = torch.from_numpy(h0s).to(dev), torch.from_numpy(hts).to(dev)
+    ws = torch.empty(gdr.workspace_bytes(torch.bfloat16, True, N, sum(lens), H),
+                     device=dev, dtype=torch.uint8)
+    stream = torch.cuda.current_stream(dev)
+    args = [x[k] for k in ("q", "k", "v", "g", "beta")]
+
+    def step(i):
+        gdr.prefill_varlen_pool(*args, x["cu_seqlens"], pool, h0t, htt, workspace=ws)
+    ms = timed(step, steps, warmup, stream)
+    del x, pool, ws
+    return ms, sum(lens)
+
+
 def cpu_baseline(synthetic, torch, target_s=12.0):
     """fp64 oracle on the host cores over the GDN prefill workload (all 64
     sequence-heads, 4096 tokens each), repeated until about target_s seconds
@@ -202,7 +257,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--only-headline", action="store_true")
-    ap.add_argument("--only", choices=["kda_prefill", "decode", "varlen"], default=None,
+    ap.add_argument("--only", choices=["kda_prefill", "decode", "varlen", "draft", "varlen_pool"],
+                    default=None,
                     help="time one secondary workload alone (for profiling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -229,6 +285,15 @@ def main():
     if args.only == "varlen":
         ms, _, _ = bench_varlen(gdr, synthetic, torch, dev, args.steps, args.warmup)
         print(json.dumps({"workload": "kda_varlen_N16_H32_d128_bf16", "ms_per_step": ms}))
+        return
+    if args.only == "draft":
+        md, mc, _, _, _, _ = bench_draft(gdr, synthetic, torch, dev, args.steps, args.warmup)
+        print(json.dumps({"workload": "gdn_draft_decode_B256_n4_H32_d128_bf16",
+                          "ms_draft": md, "ms_commit": mc}))
+        return
+    if args.only == "varlen_pool":
+        ms, _ = bench_varlen_pool(gdr, synthetic, torch, dev, args.steps, args.warmup)
+        print(json.dumps({"workload": "kda_varlen_pool_N16_H32_d128_bf16", "ms_per_step": ms}))
         return
 
     B, T, H = 4, 4096, 16
@@ -292,6 +357,25 @@ def main():
                     "GB_per_s": b4 / (ms4 * 1e-3) / 1e9,
                     "frac_hbm": b4 / (ms4 * 1e-3) / 1e9 / HBM_PEAK_GBS,
                     "mfma_frac_alg": prefill_flops(tok4 * 32) / (ms4 * 1e-3) / 1e12 / MFMA_BF16_TFLOPS})
+        md, mc, Bd, nd, Hd, kept = bench_draft(gdr, synthetic, torch, dev,
+                                               max(5, args.steps // 5), max(2, args.warmup // 5))
+        state = D * D * 4
+        bd = Bd * Hd * ((1 + nd) * state + nd * (3 * D * 2 + D * 2 + 4 + 4))
+        bc = kept * Hd * 2 * state
+        sec.append({"workload": "gdn_draft_decode_B256_n4_H32_d128_bf16",
+                    "pool_slots": 512, "draft_tokens": nd,
+                    "ms_draft": md, "draft_GB_per_s": bd / (md * 1e-3) / 1e9,
+                    "draft_frac_hbm": bd / (md * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                    "draft_tokens_per_s": Bd * nd / (md * 1e-3),
+                    "ms_commit": mc, "commit_GB_per_s": bc / (mc * 1e-3) / 1e9,
+                    "commit_frac_hbm": bc / (mc * 1e-3) / 1e9 / HBM_PEAK_GBS})
+        ms6, tok6 = bench_varlen_pool(gdr, synthetic, torch, dev,
+                                      max(5, args.steps // 5), max(2, args.warmup // 5))
+        b6 = prefill_bytes(tok6 * 32, 16 * 32, "channel")
+        sec.append({"workload": "kda_varlen_pool_N16_H32_d128_bf16", "pool_slots": 40,
+                    "ms_per_step": ms6, "tokens_per_s": tok6 / (ms6 * 1e-3),
+                    "GB_per_s": b6 / (ms6 * 1e-3) / 1e9,
+                    "frac_hbm": b6 / (ms6 * 1e-3) / 1e9 / HBM_PEAK_GBS})
         line["secondary"] = sec
 
     if not args.no_cpu_baseline:

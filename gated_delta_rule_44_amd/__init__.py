@@ -19,8 +19,8 @@ import os
 
 import torch
 
-__all__ = ["prefill", "prefill_varlen", "decode_step", "decode_placement",
-           "workspace_bytes", "version", "GdrError", "lib_path",
+__all__ = ["prefill", "prefill_varlen", "prefill_varlen_pool", "decode_step",
+           "decode_placement", "decode_tokens", "decode_commit", "workspace_bytes", "version", "GdrError", "lib_path",
            "FA", "SWA", "GDN", "KDA"]
 
 FA, SWA, GDN, KDA = 0, 1, 2, 3
@@ -63,6 +63,15 @@ def _load():
     lib.gdr_decode_placement.restype = I
     lib.gdr_decode_placement.argtypes = [P, I, I, I, I, I, I, F,
                                          P, P, P, P, P, P, P, P]
+    lib.gdr_prefill_varlen_pool.restype = I
+    lib.gdr_prefill_varlen_pool.argtypes = [I, I, I, I, I, I, I, I, F, P, P,
+                                            P, P, P, P, P, I, P, P, P, P, P, P,
+                                            P, Z, P]
+    lib.gdr_decode_tokens.restype = I
+    lib.gdr_decode_tokens.argtypes = [I, I, I, I, I, I, I, F, P, P, P, P, P,
+                                      P, P, I, P, P, P, P]
+    lib.gdr_decode_commit.restype = I
+    lib.gdr_decode_commit.argtypes = [I, I, I, I, I, P, I, P, P, P, P]
     _lib = lib
     return lib
 
@@ -256,3 +265,120 @@ def decode_placement(placement, q, k, v, g, beta, state_pool, scale: float = 1.0
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_pool),
         _ptr(o), _stream(dev)))
     return o
+
+
+def _host_i32(x, n, name):
+    import numpy as np
+    a = np.ascontiguousarray(np.asarray(x, dtype=np.int32))
+    _need(a.shape == (n,), "%s must have %d entries" % (name, n))
+    return a
+
+
+def prefill_varlen_pool(q, k, v, g, beta, cu_seqlens, state_pool, h0_slot, ht_slot,
+                        scale: float = 1.0, cu_seqlens_host=None, slots_host=None,
+                        workspace=None):
+    """Packed-batch prefill with states in a slot-indexed pool.
+
+    As prefill_varlen, but sequence n starts from state_pool[h0_slot[n]]
+    (zeros for slot -1) and its final state is written to
+    state_pool[ht_slot[n]] (not stored for -1).  state_pool [P,H,D,D] fp32;
+    h0_slot, ht_slot int32 [N] on the GPU.  slots_host = (h0 slots, ht slots)
+    as host sequences makes the library validate them.  Returns o.
+    """
+    Tt, H, D = q.shape
+    dev = q.device
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _dense(n, t, q.dtype, dev)
+    _dense("g", g, torch.float32, dev)
+    _dense("beta", beta, torch.float32, dev)
+    _dense("cu_seqlens", cu_seqlens, torch.int32, dev)
+    _dense("state_pool", state_pool, torch.float32, dev)
+    N = cu_seqlens.numel() - 1
+    _dense("h0_slot", h0_slot, torch.int32, dev)
+    _dense("ht_slot", ht_slot, torch.int32, dev)
+    _need(h0_slot.shape == (N,) and ht_slot.shape == (N,), "slot maps must be [N]")
+    gk = _CHANNEL if g.dim() == 3 else _SCALAR
+    _need(g.shape == ((Tt, H, D) if gk == _CHANNEL else (Tt, H)), "bad gate shape")
+    _need(beta.shape == (Tt, H), "beta must be [T_tot,H]")
+    _need(state_pool.dim() == 4 and state_pool.shape[1:] == (H, D, D),
+          "state_pool must be [P,H,D,D]")
+    host = None if cu_seqlens_host is None else _host_i32(cu_seqlens_host, N + 1,
+                                                           "cu_seqlens_host")
+    h0h = hth = None
+    if slots_host is not None:
+        h0h = _host_i32(slots_host[0], N, "h0 slots")
+        hth = _host_i32(slots_host[1], N, "ht slots")
+    o = torch.empty_like(v)
+    nbytes = workspace_bytes(q.dtype, gk == _CHANNEL, N, Tt, H)
+    workspace = _workspace(workspace, nbytes, dev)
+    hp = lambda a: None if a is None else a.ctypes.data_as(ctypes.c_void_p)  # noqa: E731
+    _check(_load().gdr_prefill_varlen_pool(
+        _dt(q), gk, N, Tt, H, D, D, 64, float(scale), _ptr(cu_seqlens), hp(host),
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), state_pool.shape[0],
+        _ptr(state_pool), _ptr(h0_slot), _ptr(ht_slot), hp(h0h), hp(hth), _ptr(o),
+        _ptr(workspace), nbytes, _stream(dev)))
+    return o
+
+
+def decode_tokens(q, k, v, g, beta, state_pool, slot=None, checkpoints=None,
+                  scale: float = 1.0, slot_host=None, o=None):
+    """n tokens per sequence in one launch.
+
+    q, k, v [B,n,H,D]; g [B,n,H] or [B,n,H,D]; beta [B,n,H]; state_pool
+    [P,H,D,D] fp32; slot int32 [B] on the GPU (None: slot b; -1: idle).
+    checkpoints: None (the pool is advanced in place), True (allocate) or a
+    [B,n,H,D,D] fp32 tensor that receives the state after every token while
+    the pool keeps its bytes.  Returns o, or (o, checkpoints) when
+    checkpoints is given.
+    """
+    B, n, H, D = q.shape
+    dev = q.device
+    for nm, t in (("q", q), ("k", k), ("v", v)):
+        _dense(nm, t, q.dtype, dev)
+    _dense("g", g, torch.float32, dev)
+    _dense("beta", beta, torch.float32, dev)
+    _dense("state_pool", state_pool, torch.float32, dev)
+    _need(k.shape == q.shape and v.shape == q.shape, "q, k, v shapes differ")
+    _need(beta.shape == (B, n, H), "beta must be [B,n,H]")
+    gk = _CHANNEL if g.dim() == 4 else _SCALAR
+    _need(g.shape == ((B, n, H, D) if gk == _CHANNEL else (B, n, H)), "bad gate shape")
+    _need(state_pool.dim() == 4 and state_pool.shape[1:] == (H, D, D),
+          "state_pool must be [P,H,D,D]")
+    if slot is not None:
+        _dense("slot", slot, torch.int32, dev)
+        _need(slot.shape == (B,), "slot must be [B]")
+    sh = None if slot_host is None else _host_i32(slot_host, B, "slot_host")
+    ret_ckpt = checkpoints is not None
+    if checkpoints is True:
+        checkpoints = torch.empty((B, n, H, D, D), device=dev, dtype=torch.float32)
+    if ret_ckpt:
+        _dense("checkpoints", checkpoints, torch.float32, dev)
+        _need(checkpoints.shape == (B, n, H, D, D), "checkpoints must be [B,n,H,D,D]")
+    if o is None:
+        o = torch.empty_like(v)
+    _check(_load().gdr_decode_tokens(
+        _dt(q), gk, B, n, H, D, D, float(scale), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+        _ptr(beta), _ptr(slot), None if sh is None else sh.ctypes.data_as(ctypes.c_void_p),
+        state_pool.shape[0], _ptr(state_pool), _ptr(checkpoints if ret_ckpt else None),
+        _ptr(o), _stream(dev)))
+    return (o, checkpoints) if ret_ckpt else o
+
+
+def decode_commit(checkpoints, accepted, state_pool, slot=None):
+    """Keep the state after the accepted prefix: for 1 <= accepted[b] <= n the
+    pool slot of sequence b receives checkpoints[b, accepted[b]-1]; other
+    counts leave it.  checkpoints [B,n,H,D,D], accepted int32 [B] on the GPU."""
+    B, n, H, D, _ = checkpoints.shape
+    dev = checkpoints.device
+    _dense("checkpoints", checkpoints, torch.float32, dev)
+    _dense("accepted", accepted, torch.int32, dev)
+    _dense("state_pool", state_pool, torch.float32, dev)
+    _need(accepted.shape == (B,), "accepted must be [B]")
+    _need(state_pool.dim() == 4 and state_pool.shape[1:] == (H, D, D),
+          "state_pool must be [P,H,D,D]")
+    if slot is not None:
+        _dense("slot", slot, torch.int32, dev)
+        _need(slot.shape == (B,), "slot must be [B]")
+    _check(_load().gdr_decode_commit(
+        B, n, H, D, D, _ptr(slot), state_pool.shape[0], _ptr(accepted),
+        _ptr(checkpoints), _ptr(state_pool), _stream(dev)))

@@ -118,6 +118,15 @@ WsLayout ws_layout(bool tiles, int N, long long tokens, int H) {
     return w;
 }
 
+// packed-batch prefill shared by the plain and the pool entry points
+gdr_status prefill_varlen_impl(const char *what, int dt, int gk, int N, int T_total, int H,
+                               int Dk, int Dv, int chunk, float scale,
+                               const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
+                               const void *q, const void *k, const void *v, const float *g,
+                               const float *beta, const float *h0, void *o, float *ht,
+                               const int32_t *h0_slot, const int32_t *ht_slot, long long pool,
+                               void *workspace, size_t ws_bytes, void *stream);
+
 }  // namespace
 
 extern "C" {
@@ -182,6 +191,28 @@ gdr_status gdr_prefill_chunked_varlen(enum gdr_dtype dt, enum gdr_gate gk, int N
                                       void *o, float *ht, void *workspace, size_t ws_bytes,
                                       void *stream) {
     const char *what = "gdr_prefill_chunked_varlen";
+    if (h0 && ht && h0 != ht && N > 0 && H > 0 && Dk > 0 && Dv > 0) {
+        const size_t bytes = (size_t)N * H * Dv * Dk * sizeof(float);
+        const char *a0 = (const char *)h0, *a1 = (const char *)ht;
+        if (a0 < a1 + bytes && a1 < a0 + bytes)
+            return fail(GDR_EINVAL, "%s: h0 and ht overlap without being equal", what);
+    }
+    return prefill_varlen_impl(what, dt, gk, N, T_total, H, Dk, Dv, chunk, scale, cu_seqlens,
+                               cu_seqlens_host, q, k, v, g, beta, h0, o, ht, nullptr, nullptr,
+                               0, workspace, ws_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+gdr_status prefill_varlen_impl(const char *what, int dt, int gk, int N, int T_total, int H,
+                               int Dk, int Dv, int chunk, float scale,
+                               const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
+                               const void *q, const void *k, const void *v, const float *g,
+                               const float *beta, const float *h0, void *o, float *ht,
+                               const int32_t *h0_slot, const int32_t *ht_slot, long long pool,
+                               void *workspace, size_t ws_bytes, void *stream) {
     gdr_status st = check_common(dt, gk, Dk, Dv, what);
     if (st != GDR_OK) return st;
     if (chunk != 64) return fail(GDR_EUNSUPPORTED, "%s: chunk = %d; only 64 is supported", what, chunk);
@@ -206,12 +237,6 @@ gdr_status gdr_prefill_chunked_varlen(enum gdr_dtype dt, enum gdr_gate gk, int N
     }
     st = check_prefill_ptrs(what, q, k, v, g, beta, h0, o, ht, T_total);
     if (st != GDR_OK) return st;
-    if (h0 && ht && h0 != ht) {
-        const size_t bytes = (size_t)N * H * Dv * Dk * sizeof(float);
-        const char *a0 = (const char *)h0, *a1 = (const char *)ht;
-        if (a0 < a1 + bytes && a1 < a0 + bytes)
-            return fail(GDR_EINVAL, "%s: h0 and ht overlap without being equal", what);
-    }
     const bool tiles = dt == GDR_BF16 && gk == GDR_GATE_SCALAR;
     const WsLayout L = ws_layout(tiles, N, T_total, H);
     st = check_workspace(what, workspace, ws_bytes, L.total);
@@ -229,9 +254,62 @@ gdr_status gdr_prefill_chunked_varlen(enum gdr_dtype dt, enum gdr_gate gk, int N
     a.tiles = tiles ? ws + L.tiles : nullptr;
     a.max_chunks = L.max_chunks;
     a.N = N; a.T = 0; a.H = H; a.scale = scale; a.channel_gate = gk == GDR_GATE_CHANNEL;
+    a.h0_slot = h0_slot; a.ht_slot = ht_slot; a.pool = pool;
     e = dt == GDR_BF16 ? gdr::launch_prefill_chunked(Dk, a, s)
                        : gdr::launch_prefill_recurrent(false, Dk, a, s);
     return finish(e, s, what);
+}
+
+}  // namespace
+
+extern "C" {
+
+
+gdr_status gdr_prefill_varlen_pool(enum gdr_dtype dt, enum gdr_gate gk, int N, int T_total,
+                                   int H, int Dk, int Dv, int chunk, float scale,
+                                   const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
+                                   const void *q, const void *k, const void *v,
+                                   const float *g, const float *beta, int pool_slots,
+                                   float *state_pool, const int32_t *h0_slot,
+                                   const int32_t *ht_slot, const int32_t *h0_slot_host,
+                                   const int32_t *ht_slot_host, void *o, void *workspace,
+                                   size_t ws_bytes, void *stream) {
+    const char *what = "gdr_prefill_varlen_pool";
+    if (pool_slots < 0) return fail(GDR_EINVAL, "%s: pool_slots = %d", what, pool_slots);
+    if (N > 0) {
+        if (!h0_slot || !ht_slot) return fail(GDR_EINVAL, "%s: h0_slot and ht_slot are required", what);
+        REQUIRE_PTR(state_pool, "state_pool");
+        if ((long long)pool_slots * H >= (1LL << 31))
+            return fail(GDR_EUNSUPPORTED, "%s: pool of %d slots x %d heads too large", what,
+                        pool_slots, H);
+    }
+    if (h0_slot_host && ht_slot_host && N > 0) {
+        for (int n = 0; n < N; ++n) {
+            if (h0_slot_host[n] < -1 || h0_slot_host[n] >= pool_slots)
+                return fail(GDR_EINVAL, "%s: h0_slot[%d] = %d outside -1..%d", what, n,
+                            h0_slot_host[n], pool_slots - 1);
+            if (ht_slot_host[n] < -1 || ht_slot_host[n] >= pool_slots)
+                return fail(GDR_EINVAL, "%s: ht_slot[%d] = %d outside -1..%d", what, n,
+                            ht_slot_host[n], pool_slots - 1);
+        }
+        // a slot written by one sequence is neither written nor read by another
+        for (int n = 0; n < N; ++n) {
+            const int s = ht_slot_host[n];
+            if (s < 0) continue;
+            for (int m = 0; m < N; ++m) {
+                if (m == n) continue;
+                if (ht_slot_host[m] == s)
+                    return fail(GDR_EINVAL, "%s: sequences %d and %d both write slot %d", what,
+                                n, m, s);
+                if (h0_slot_host[m] == s)
+                    return fail(GDR_EINVAL, "%s: sequence %d reads slot %d that sequence %d writes",
+                                what, m, s, n);
+            }
+        }
+    }
+    return prefill_varlen_impl(what, dt, gk, N, T_total, H, Dk, Dv, chunk, scale, cu_seqlens,
+                               cu_seqlens_host, q, k, v, g, beta, state_pool, o, state_pool,
+                               h0_slot, ht_slot, pool_slots, workspace, ws_bytes, stream);
 }
 
 gdr_status gdr_decode_step(enum gdr_dtype dt, enum gdr_gate gk, int B, int H, int Dk, int Dv,
@@ -301,6 +379,93 @@ gdr_status gdr_decode_placement(const uint8_t *placement, int L, enum gdr_dtype 
     a.g_layer = (long long)B * H * Dk;
     hipStream_t s = static_cast<hipStream_t>(stream);
     return finish(gdr::launch_decode(dt == GDR_BF16, Dk, a, layers, s), s, what);
+}
+
+gdr_status gdr_decode_tokens(enum gdr_dtype dt, enum gdr_gate gk, int B, int n_tok, int H,
+                             int Dk, int Dv, float scale, const void *q, const void *k,
+                             const void *v, const float *g, const float *beta,
+                             const int32_t *slot, const int32_t *slot_host, int pool_slots,
+                             float *state_pool, float *checkpoints, void *o, void *stream) {
+    const char *what = "gdr_decode_tokens";
+    gdr_status st = check_common(dt, gk, Dk, Dv, what);
+    if (st != GDR_OK) return st;
+    if (B < 0 || n_tok < 0 || H <= 0 || pool_slots < 0)
+        return fail(GDR_EINVAL, "%s: bad sizes B=%d n_tok=%d H=%d pool_slots=%d", what, B,
+                    n_tok, H, pool_slots);
+    if ((long long)B * H >= (1LL << 27) || (long long)pool_slots * H >= (1LL << 31) ||
+        (long long)B * n_tok * H * Dk >= (1LL << 40))
+        return fail(GDR_EUNSUPPORTED, "%s: problem too large", what);
+    if (!slot && pool_slots < B)
+        return fail(GDR_EINVAL, "%s: without a slot map the pool needs B = %d slots, has %d",
+                    what, B, pool_slots);
+    if (slot_host) {
+        if (!slot) return fail(GDR_EINVAL, "%s: slot_host given without slot", what);
+        for (int b = 0; b < B; ++b)
+            if (slot_host[b] < -1 || slot_host[b] >= pool_slots)
+                return fail(GDR_EINVAL, "%s: slot[%d] = %d outside -1..%d", what, b,
+                            slot_host[b], pool_slots - 1);
+        // two sequences on one slot would race; sort a copy to find repeats
+        int32_t *tmp = static_cast<int32_t *>(malloc(sizeof(int32_t) * (B > 0 ? B : 1)));
+        if (!tmp) return fail(GDR_EINVAL, "%s: host memory for the slot check", what);
+        memcpy(tmp, slot_host, sizeof(int32_t) * B);
+        qsort(tmp, B, sizeof(int32_t), [](const void *x, const void *y) {
+            const int32_t a = *static_cast<const int32_t *>(x), b = *static_cast<const int32_t *>(y);
+            return (a > b) - (a < b);
+        });
+        int dup = -1;
+        for (int b = 1; b < B && dup < 0; ++b)
+            if (tmp[b] >= 0 && tmp[b] == tmp[b - 1]) dup = tmp[b];
+        free(tmp);
+        if (dup >= 0) return fail(GDR_EINVAL, "%s: slot %d is used by two sequences", what, dup);
+    }
+    if (B == 0 || n_tok == 0) return GDR_OK;
+    REQUIRE_PTR(q, "q");
+    REQUIRE_PTR(k, "k");
+    REQUIRE_PTR(v, "v");
+    REQUIRE_PTR(g, "g");
+    if (!beta) return fail(GDR_EINVAL, "%s: beta is NULL", what);
+    REQUIRE_PTR(state_pool, "state_pool");
+    REQUIRE_ALIGNED_OR_NULL(checkpoints, "checkpoints");
+    if (!o) return fail(GDR_EINVAL, "%s: o is NULL", what);
+    if (checkpoints) {
+        const size_t pb = (size_t)pool_slots * H * Dv * Dk * sizeof(float);
+        const size_t cb = (size_t)B * n_tok * H * Dv * Dk * sizeof(float);
+        const char *p0 = (const char *)state_pool, *c0 = (const char *)checkpoints;
+        if (p0 < c0 + cb && c0 < p0 + pb)
+            return fail(GDR_EINVAL, "%s: checkpoints overlap state_pool", what);
+    }
+    gdr::TokensArgs a{};
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+    a.slot = slot; a.pool = pool_slots; a.state = state_pool; a.ckpt = checkpoints; a.o = o;
+    a.B = B; a.n = n_tok; a.H = H; a.scale = scale; a.channel_gate = gk == GDR_GATE_CHANNEL;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return finish(gdr::launch_decode_tokens(dt == GDR_BF16, Dk, a, s), s, what);
+}
+
+gdr_status gdr_decode_commit(int B, int n_tok, int H, int Dk, int Dv, const int32_t *slot,
+                             int pool_slots, const int32_t *accepted, const float *checkpoints,
+                             float *state_pool, void *stream) {
+    const char *what = "gdr_decode_commit";
+    gdr_status st = check_common(GDR_F32, GDR_GATE_SCALAR, Dk, Dv, what);
+    if (st != GDR_OK) return st;
+    if (B < 0 || n_tok < 0 || H <= 0 || pool_slots < 0)
+        return fail(GDR_EINVAL, "%s: bad sizes B=%d n_tok=%d H=%d pool_slots=%d", what, B,
+                    n_tok, H, pool_slots);
+    if ((long long)B * H >= (1LL << 27) || (long long)pool_slots * H >= (1LL << 31))
+        return fail(GDR_EUNSUPPORTED, "%s: problem too large", what);
+    if (!slot && pool_slots < B)
+        return fail(GDR_EINVAL, "%s: without a slot map the pool needs B = %d slots, has %d",
+                    what, B, pool_slots);
+    if (B == 0 || n_tok == 0) return GDR_OK;
+    if (!accepted) return fail(GDR_EINVAL, "%s: accepted is NULL", what);
+    REQUIRE_PTR(checkpoints, "checkpoints");
+    REQUIRE_PTR(state_pool, "state_pool");
+    gdr::TokensArgs a{};
+    a.slot = slot; a.pool = pool_slots; a.state = state_pool;
+    a.ckpt = const_cast<float *>(checkpoints);
+    a.B = B; a.n = n_tok; a.H = H;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return finish(gdr::launch_decode_commit(Dk, a, accepted, s), s, what);
 }
 
 }  // extern "C"

@@ -184,7 +184,6 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
         t1 = t0 + a.T;
     }
     const int i0 = tile * BV;
-    const size_t sslot = ((size_t)n * a.H + h) * D * D;
     const size_t tokstride = (size_t)a.H * D;
     const bf16 *qg = static_cast<const bf16 *>(a.q) + (size_t)h * D;
     const bf16 *kg = static_cast<const bf16 *>(a.k) + (size_t)h * D;
@@ -206,6 +205,7 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
     f32x4 St[SBK][2];
     {
         const LI L(tid0);
+        const float *h0p = seq_h0<D>(a, n, h);
 #pragma unroll
         for (int kb = 0; kb < SBK; ++kb) {
 #pragma unroll
@@ -214,8 +214,8 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
                 if (L.w >= 4) {
                     const int j = 16 * (SBK * (L.w - 4) + kb) + 4 * L.l4;
                     const int iv = 16 * jv + L.l15;
-                    if (a.h0)
-                        sv = *reinterpret_cast<const f32x4 *>(a.h0 + sslot + (size_t)(i0 + iv) * D + j);
+                    if (h0p)
+                        sv = *reinterpret_cast<const f32x4 *>(h0p + (size_t)(i0 + iv) * D + j);
                     *reinterpret_cast<bf16x4 *>(&sm.S[iv * PD + j]) = cvt4(sv);
                 }
                 St[kb][jv] = sv;
@@ -677,7 +677,7 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
         else       iteration(E{}, std::true_type{}, std::false_type{}, j);
     }
 
-    if (a.ht) {
+    if (float *htp = seq_ht<D>(a, n, h)) {
         const LI L(tid0);
         if (L.w >= 4) {
 #pragma unroll
@@ -686,7 +686,7 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
                 for (int jv = 0; jv < 2; ++jv) {
                     const int j = 16 * (SBK * (L.w - 4) + kb) + 4 * L.l4;
                     const int iv = 16 * jv + L.l15;
-                    *reinterpret_cast<f32x4 *>(a.ht + sslot + (size_t)(i0 + iv) * D + j) = St[kb][jv];
+                    *reinterpret_cast<f32x4 *>(htp + (size_t)(i0 + iv) * D + j) = St[kb][jv];
                 }
             }
         }

@@ -344,7 +344,6 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
         cbase = (long long)n * ((a.T + C - 1) / C);
     }
     const int i0 = tile * BV;
-    const size_t sslot = ((size_t)n * a.H + h) * D * D;
     const size_t tokstride = (size_t)a.H * D;
     const unsigned rowb = (unsigned)(tokstride * 2);   // bytes between tokens
     const bf16 *qg = static_cast<const bf16 *>(a.q) + (size_t)h * D;
@@ -388,11 +387,12 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
         // S^T[srow(jk, e)][16 ib + l15] (fp32); the four rows e of a block are
         // adjacent columns of S, so they move as one 16-byte access
         f32x4 St[KS];
-        const size_t srow0 = sslot + (size_t)(i0 + 16 * ib + l15) * D;
+        const size_t srow0 = (size_t)(i0 + 16 * ib + l15) * D;
+        const float *h0p = seq_h0<D>(a, n, h);
 #pragma unroll
         for (int jk = 0; jk < KS; ++jk)
-            St[jk] = a.h0 ? *reinterpret_cast<const f32x4 *>(a.h0 + srow0 + srow(jk, 0))
-                          : f32x4{0.f, 0.f, 0.f, 0.f};
+            St[jk] = h0p ? *reinterpret_cast<const f32x4 *>(h0p + srow0 + srow(jk, 0))
+                         : f32x4{0.f, 0.f, 0.f, 0.f};
         auto publish_state = [&](int spar) {   // S^T entering a chunk of parity spar
 #pragma unroll
             for (int kk = 0; kk < KD; ++kk) sm.SB[spar][ib][kk][lane] = acc_pair(St[2 * kk], St[2 * kk + 1]);
@@ -495,9 +495,9 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
         }
         __syncthreads();                      // outputs of the last chunk
         __syncthreads();
-        if (a.ht) {
+        if (float *htp = seq_ht<D>(a, n, h)) {
 #pragma unroll
-            for (int jk = 0; jk < KS; ++jk) *reinterpret_cast<f32x4 *>(a.ht + srow0 + srow(jk, 0)) = St[jk];
+            for (int jk = 0; jk < KS; ++jk) *reinterpret_cast<f32x4 *>(htp + srow0 + srow(jk, 0)) = St[jk];
         }
         return;
     }

@@ -57,6 +57,26 @@ struct DecodeArgs {
 hipError_t launch_decode(bool bf16_io, int D, const DecodeArgs &a,
                          const DecodeLayers &layers, hipStream_t s);
 
+// Several tokens per sequence in one launch, state in a slot-indexed pool.
+struct TokensArgs {
+    const void *q, *k, *v;        // [B, n, H, D] dt
+    const float *g;               // [B, n, H] or [B, n, H, D]
+    const float *beta;            // [B, n, H]
+    const int32_t *slot;          // [B] pool slot of each sequence, or nullptr (slot b)
+    long long pool;               // slots in state
+    float *state;                 // [pool, H, D, D]
+    float *ckpt;                  // [B, n, H, D, D] state after each token, or nullptr
+    void *o;                      // [B, n, H, D] dt
+    int B, n, H;
+    float scale;
+    int channel_gate;
+};
+
+hipError_t launch_decode_tokens(bool bf16_io, int D, const TokensArgs &a, hipStream_t s);
+// state[slot[b], h] <- ckpt[b, accepted[b] - 1, h] where 1 <= accepted[b] <= n
+hipError_t launch_decode_commit(int D, const TokensArgs &a, const int32_t *accepted,
+                                hipStream_t s);
+
 // Fixed-length (cu_seqlens == nullptr, T = seq_len) or packed batches.
 struct PrefillArgs {
     const void *q, *k, *v;        // [tokens, H, D] dt
@@ -73,7 +93,33 @@ struct PrefillArgs {
     int N, T, H;                  // T used only when cu_seqlens == nullptr
     float scale;
     int channel_gate;
+    // pool form: h0 == ht == a [pool, H, D, D] state pool, sequence n starts
+    // from slot h0_slot[n] and ends in slot ht_slot[n]; nullptr = slot n
+    const int32_t *h0_slot, *ht_slot;
+    long long pool;
 };
+
+// Initial state of sequence n, head h (nullptr: start from zeros) and where
+// its final state goes (nullptr: not stored).  A pool slot outside
+// [0, pool) selects zeros / no store.
+template <int D>
+__device__ inline const float *seq_h0(const PrefillArgs &a, int n, int h) {
+    long long s = n;
+    if (a.h0_slot) {
+        s = a.h0_slot[n];
+        if (s < 0 || s >= a.pool) return nullptr;
+    }
+    return a.h0 ? a.h0 + ((size_t)s * a.H + h) * D * D : nullptr;
+}
+template <int D>
+__device__ inline float *seq_ht(const PrefillArgs &a, int n, int h) {
+    long long s = n;
+    if (a.ht_slot) {
+        s = a.ht_slot[n];
+        if (s < 0 || s >= a.pool) return nullptr;
+    }
+    return a.ht ? a.ht + ((size_t)s * a.H + h) * D * D : nullptr;
+}
 
 // Per (chunk, head) record of the scalar-gate chunked prefill's workspace:
 // T as MFMA operands of its 16x16 blocks (bf16, 5 KiB), then two

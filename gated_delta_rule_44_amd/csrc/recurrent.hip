@@ -212,6 +212,147 @@ __global__ __launch_bounds__(256) void decode_rows_kernel(DecodeArgs a, DecodeLa
 }
 
 // ---------------------------------------------------------------------------
+// Several tokens per sequence in one launch (drafted tokens of speculative
+// decoding, or a short continuation): the decode update above applied to
+// tokens 0 .. n-1 in order with the state slice resident in registers, so
+// the state is read from HBM once.  With a checkpoint buffer the state after
+// every token is written there and the pool keeps its bytes (the caller
+// installs the state after the accepted prefix with the commit kernel);
+// without one the state after the last token replaces the pool's.  The
+// state lives in a slot-indexed pool: sequence b uses slot slot[b], and a
+// slot outside [0, pool) marks an idle sequence that is skipped.
+template <int PASSES>
+struct TokIn {
+    f32x4 k, q, lg;
+    float beta;
+    float v[PASSES];
+};
+
+template <typename T, int D, int PASSES>
+__device__ __forceinline__ TokIn<PASSES> load_token(const TokensArgs &a, size_t bth, int c0,
+                                                    const int (&row)[PASSES]) {
+    TokIn<PASSES> x;
+    const T *kp = static_cast<const T *>(a.k) + bth * D;
+    const T *qp = static_cast<const T *>(a.q) + bth * D;
+    const T *vp = static_cast<const T *>(a.v) + bth * D;
+    x.k = Elem<T>::load4(kp + c0);
+    x.q = Elem<T>::load4(qp + c0);
+    if (a.channel_gate) {
+        x.lg = *reinterpret_cast<const f32x4 *>(a.g + bth * D + c0);
+    } else {
+        const float s = a.g[bth];
+        x.lg = f32x4{s, s, s, s};
+    }
+    x.beta = a.beta[bth];
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) x.v[p] = Elem<T>::load(vp + row[p]);
+    return x;
+}
+
+template <typename T, int D, int PASSES>
+__global__ __launch_bounds__(256) void decode_tokens_kernel(TokensArgs a) {
+    using G = Geom<D>;
+    constexpr int RPP = G::RPI;
+    constexpr int ROWS = RPP * PASSES;
+    constexpr int NRB = D / ROWS;
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    const int rb = blockIdx.x % NRB;
+    const int bh = blockIdx.x / NRB;
+    const int b = bh / a.H;
+    const int h = bh - b * a.H;
+    long long slot = b;
+    if (a.slot) {
+        slot = a.slot[b];
+        if (slot < 0 || slot >= a.pool) return;
+    }
+    const int c0 = (lane % G::LPR) * 4;
+    const int sub = lane / G::LPR;
+    int row[PASSES];
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) row[p] = rb * ROWS + p * RPP + w * G::RPW + sub;
+
+    float *st = a.state + ((size_t)slot * a.H + h) * D * D;
+    f32x4 S[PASSES];
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p)
+        S[p] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(st + (size_t)row[p] * D + c0));
+
+    const size_t bh0 = (size_t)b * a.n * a.H + h;        // (b, token 0, h)
+    TokIn<PASSES> cur = load_token<T, D, PASSES>(a, bh0, c0, row);
+    constexpr float kLog2e = 1.4426950408889634f;
+    for (int t = 0; t < a.n; ++t) {
+        const size_t bth = bh0 + (size_t)t * a.H;
+        const TokIn<PASSES> nxt = t + 1 < a.n ? load_token<T, D, PASSES>(a, bth + a.H, c0, row) : cur;
+        const f32x4 av = f32x4{__builtin_amdgcn_exp2f(cur.lg.x * kLog2e), __builtin_amdgcn_exp2f(cur.lg.y * kLog2e),
+                               __builtin_amdgcn_exp2f(cur.lg.z * kLog2e), __builtin_amdgcn_exp2f(cur.lg.w * kLog2e)};
+        const f32x4 ak = av * cur.k;
+        const f32x4 aq = av * cur.q;
+        float kq = dot4(cur.k, cur.q);
+#pragma unroll
+        for (int mask = G::LPR / 2; mask >= 1; mask >>= 1) kq += __shfl_xor(kq, mask);
+        T *op = static_cast<T *>(a.o) + bth * D;
+#pragma unroll
+        for (int p = 0; p < PASSES; ++p) {
+            const float yk = dot4(S[p], ak);
+            const float yq = dot4(S[p], aq);
+            const bool upper = (lane & (G::LPR / 2)) != 0;
+            float val = (upper ? yq : yk) + __shfl_xor(upper ? yk : yq, G::LPR / 2);
+#pragma unroll
+            for (int mask = G::LPR / 4; mask >= 1; mask >>= 1) val += __shfl_xor(val, mask);
+            const float u_lo = cur.beta * (cur.v[p] - val);
+            const float u = __shfl_xor(u_lo, G::LPR / 2);
+            const float um = upper ? u : u_lo;
+            if (upper && (lane % (G::LPR / 2)) == 0) Elem<T>::store(op + row[p], a.scale * (val + um * kq));
+            S[p] = S[p] * av + um * cur.k;
+        }
+        if (a.ckpt) {
+            float *cp = a.ckpt + bth * D * D;
+#pragma unroll
+            for (int p = 0; p < PASSES; ++p)
+                __builtin_nontemporal_store(S[p], reinterpret_cast<f32x4 *>(cp + (size_t)row[p] * D + c0));
+        }
+        cur = nxt;
+    }
+    if (!a.ckpt) {
+#pragma unroll
+        for (int p = 0; p < PASSES; ++p)
+            __builtin_nontemporal_store(S[p], reinterpret_cast<f32x4 *>(st + (size_t)row[p] * D + c0));
+    }
+}
+
+// Install the state after the accepted prefix: for 1 <= accepted[b] <= n the
+// checkpoint of token accepted[b] - 1 replaces the pool slot's state; other
+// counts (0: every drafted token rejected) leave the slot as it is.  One
+// workgroup copies 16 KiB of one state.
+template <int D>
+__global__ __launch_bounds__(256) void commit_kernel(TokensArgs a, const int32_t *accepted) {
+    constexpr int PIECE = 4096;                 // floats per workgroup
+    constexpr int NP = D * D / PIECE;
+    constexpr int V = PIECE / 4 / 256;          // float4 per thread
+    const int piece = blockIdx.x % NP;
+    const int bh = blockIdx.x / NP;
+    const int b = bh / a.H;
+    const int h = bh - b * a.H;
+    const int m = accepted[b];
+    if (m < 1 || m > a.n) return;
+    long long slot = b;
+    if (a.slot) {
+        slot = a.slot[b];
+        if (slot < 0 || slot >= a.pool) return;
+    }
+    const f32x4 *src = reinterpret_cast<const f32x4 *>(
+        a.ckpt + (((size_t)b * a.n + (m - 1)) * a.H + h) * D * D + (size_t)piece * PIECE);
+    f32x4 *dst = reinterpret_cast<f32x4 *>(a.state + ((size_t)slot * a.H + h) * D * D +
+                                           (size_t)piece * PIECE);
+    f32x4 x[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) x[i] = __builtin_nontemporal_load(src + i * 256 + threadIdx.x);
+#pragma unroll
+    for (int i = 0; i < V; ++i) __builtin_nontemporal_store(x[i], dst + i * 256 + threadIdx.x);
+}
+
+// ---------------------------------------------------------------------------
 // Prefill in the recurrent form: one workgroup per (sequence, head) walks
 // its tokens in order with the state resident in registers.
 template <typename T, int D>
@@ -230,13 +371,13 @@ __global__ __launch_bounds__(256) void prefill_recurrent_kernel(PrefillArgs a) {
         t0 = (long long)n * a.T;
         t1 = t0 + a.T;
     }
-    const size_t sslot = ((size_t)n * a.H + h) * D * D;
+    const float *h0p = seq_h0<D>(a, n, h);
 
     f32x4 S[G::M];
 #pragma unroll
     for (int m = 0; m < G::M; ++m)
-        S[m] = a.h0 ? *reinterpret_cast<const f32x4 *>(state_row<D>(a.h0 + sslot, m, lane, w))
-                    : f32x4{0.f, 0.f, 0.f, 0.f};
+        S[m] = h0p ? *reinterpret_cast<const f32x4 *>(state_row<D>(h0p, m, lane, w))
+                   : f32x4{0.f, 0.f, 0.f, 0.f};
 
     const size_t tok = (size_t)a.H * D;                 // q/k/v/o token stride
     const size_t gtok = a.channel_gate ? tok : (size_t)a.H;
@@ -250,10 +391,10 @@ __global__ __launch_bounds__(256) void prefill_recurrent_kernel(PrefillArgs a) {
                         a.channel_gate != 0, a.beta[t * a.H + h], a.scale, o + t * tok,
                         lane, w);
     }
-    if (a.ht) {
+    if (float *htp = seq_ht<D>(a, n, h)) {
 #pragma unroll
         for (int m = 0; m < G::M; ++m)
-            *reinterpret_cast<f32x4 *>(const_cast<float *>(state_row<D>(a.ht + sslot, m, lane, w))) = S[m];
+            *reinterpret_cast<f32x4 *>(const_cast<float *>(state_row<D>(htp, m, lane, w))) = S[m];
     }
 }
 
@@ -276,6 +417,34 @@ hipError_t launch_decode(bool bf16_io, int D, const DecodeArgs &a,
         if (D == 128) hipLaunchKernelGGL((decode_rows_kernel<float, 128, P128>), grid, block, 0, s, a, layers);
         else          hipLaunchKernelGGL((decode_rows_kernel<float, 64, P64>), grid, block, 0, s, a, layers);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_tokens(bool bf16_io, int D, const TokensArgs &a, hipStream_t s) {
+    if ((long long)a.B * a.H <= 0 || a.n <= 0) return hipSuccess;
+    constexpr int P = GDR_DECODE_PASSES;
+    const long long per_head = D == 128 ? 128 / (Geom<128>::RPI * P) : 64 / (Geom<64>::RPI * P);
+    const long long blocks = (long long)a.B * a.H * per_head;
+    if (blocks >= (1LL << 31)) return hipErrorInvalidValue;
+    dim3 grid((unsigned)blocks), block(256);
+    if (bf16_io) {
+        if (D == 128) hipLaunchKernelGGL((decode_tokens_kernel<bf16, 128, P>), grid, block, 0, s, a);
+        else          hipLaunchKernelGGL((decode_tokens_kernel<bf16, 64, P>), grid, block, 0, s, a);
+    } else {
+        if (D == 128) hipLaunchKernelGGL((decode_tokens_kernel<float, 128, P>), grid, block, 0, s, a);
+        else          hipLaunchKernelGGL((decode_tokens_kernel<float, 64, P>), grid, block, 0, s, a);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_commit(int D, const TokensArgs &a, const int32_t *accepted,
+                                hipStream_t s) {
+    if ((long long)a.B * a.H <= 0 || a.n <= 0) return hipSuccess;
+    const long long blocks = (long long)a.B * a.H * (D * D / 4096);
+    if (blocks >= (1LL << 31)) return hipErrorInvalidValue;
+    dim3 grid((unsigned)blocks), block(256);
+    if (D == 128) hipLaunchKernelGGL((commit_kernel<128>), grid, block, 0, s, a, accepted);
+    else          hipLaunchKernelGGL((commit_kernel<64>), grid, block, 0, s, a, accepted);
     return hipGetLastError();
 }
 

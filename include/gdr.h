@@ -186,6 +186,88 @@ gdr_status gdr_decode_placement(const uint8_t *placement, int L, enum gdr_dtype 
                                 const float *g, const float *beta,
                                 float *state_pool, void *o, void *stream);
 
+/*
+ * Serving forms.  A serving loop keeps every live request's states in one
+ * pool and refers to them by slot; a placement can change from one request
+ * to the next (abstract; summary section 2d), so a request's layers are
+ * addressed per call.  The shared checkpoint also drafts tokens for
+ * speculative decoding with a cheaper placement (abstract; summary section
+ * 2d; "Component-Aware Self-Speculative Decoding in Hybrid Language Models",
+ * abstract, on linear-attention layers as the draft): the verifier needs
+ * the state after each drafted token so that the state after the accepted
+ * prefix can be kept.
+ */
+
+/*
+ * Packed-batch prefill whose initial and final states live in a
+ * slot-indexed pool: sequence n starts from state_pool[h0_slot[n]] and its
+ * final state is written to state_pool[ht_slot[n]].  Slot -1 (any value
+ * outside 0..pool_slots-1) means: start from zeros / do not store.
+ * h0_slot[n] == ht_slot[n] continues a request in place.
+ *
+ *   pool_slots        slots in the pool (>= 0)
+ *   state_pool        [pool_slots, H, Dv, Dk] fp32
+ *   h0_slot, ht_slot  device int32 [N], both required
+ *   h0_slot_host, ht_slot_host
+ *                     host copies, optional (NULL): when both are given
+ *                     they are validated first -- values in -1..pool_slots-1,
+ *                     no slot written by two sequences, no slot read by one
+ *                     sequence and written by another (such calls race;
+ *                     without the host copies their result is undefined)
+ * Other arguments, the workspace and the numerics as
+ * gdr_prefill_chunked_varlen.
+ */
+gdr_status gdr_prefill_varlen_pool(enum gdr_dtype dt, enum gdr_gate gk, int N,
+                                   int T_total, int H, int Dk, int Dv, int chunk,
+                                   float scale, const int32_t *cu_seqlens,
+                                   const int32_t *cu_seqlens_host,
+                                   const void *q, const void *k, const void *v,
+                                   const float *g, const float *beta, int pool_slots,
+                                   float *state_pool, const int32_t *h0_slot,
+                                   const int32_t *ht_slot, const int32_t *h0_slot_host,
+                                   const int32_t *ht_slot_host, void *o,
+                                   void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * n_tok decode tokens for each of B sequences in one launch: gdr_decode_step's
+ * update applied to tokens 0 .. n_tok-1 in order, with each state read from
+ * HBM once.  Sequence b's state is state_pool[slot[b]] (slot[b] = b when
+ * slot is NULL); a slot outside 0..pool_slots-1 marks an idle sequence:
+ * nothing of it is read or written.
+ *
+ *   q, k          [B, n_tok, H, Dk] dt;  v, o [B, n_tok, H, Dv] dt
+ *   g             [B, n_tok, H] (scalar) or [B, n_tok, H, Dk] (channel) fp32
+ *   beta          [B, n_tok, H] fp32
+ *   slot          device int32 [B] or NULL (then pool_slots >= B)
+ *   slot_host     host copy of slot, optional: validated first (values in
+ *                 -1..pool_slots-1, no slot used twice; two sequences on one
+ *                 slot race, and without the host copy the result is
+ *                 undefined)
+ *   state_pool    [pool_slots, H, Dv, Dk] fp32
+ *   checkpoints   [B, n_tok, H, Dv, Dk] fp32 or NULL.  NULL: the state after
+ *                 the last token replaces the pool's.  Given: the state after
+ *                 token t is written to checkpoints[b, t] and the pool keeps
+ *                 its bytes (see gdr_decode_commit).  Must not overlap the
+ *                 pool.
+ */
+gdr_status gdr_decode_tokens(enum gdr_dtype dt, enum gdr_gate gk, int B, int n_tok, int H,
+                             int Dk, int Dv, float scale, const void *q, const void *k,
+                             const void *v, const float *g, const float *beta,
+                             const int32_t *slot, const int32_t *slot_host,
+                             int pool_slots, float *state_pool, float *checkpoints,
+                             void *o, void *stream);
+
+/*
+ * Keep the state after the accepted prefix of a checkpointed
+ * gdr_decode_tokens call: for 1 <= accepted[b] <= n_tok the pool slot of
+ * sequence b receives checkpoints[b, accepted[b] - 1]; any other count (0:
+ * every drafted token rejected) leaves it unchanged.  slot, pool_slots,
+ * B, n_tok, H, Dk, Dv as in that call; accepted is device int32 [B].
+ */
+gdr_status gdr_decode_commit(int B, int n_tok, int H, int Dk, int Dv, const int32_t *slot,
+                             int pool_slots, const int32_t *accepted,
+                             const float *checkpoints, float *state_pool, void *stream);
+
 /* Thread-local text describing the last non-OK status of this thread. */
 const char *gdr_last_error(void);
 

@@ -33,8 +33,9 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == sorted(["gdr_prefill_workspace_bytes", "gdr_prefill_chunked",
                             "gdr_prefill_chunked_varlen", "gdr_decode_step",
-                            "gdr_decode_placement", "gdr_last_error",
-                            "gdr_version"])
+                            "gdr_decode_placement", "gdr_prefill_varlen_pool",
+                            "gdr_decode_tokens", "gdr_decode_commit",
+                            "gdr_last_error", "gdr_version"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -149,6 +150,68 @@ def test_placement_rejects(lib):
     assert call([0, 1, 0]) == 0            # nothing recurrent: nothing to do
     assert lib.gdr_decode_placement(None, 3, 1, 2, 4, 128, 128, F(1.0), FAKE,
                                     FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == EINVAL
+
+
+def _hp(a):
+    return None if a is None else np.asarray(a, np.int32).ctypes.data_as(ctypes.c_void_p)
+
+
+def tokens(lib, B=3, n=4, H=2, D=128, slot=FAKE, slot_host=None, pool=8, state=FAKE,
+           ckpt=None, o=FAKE, q=FAKE):
+    hs = None if slot_host is None else np.asarray(slot_host, np.int32)
+    return lib.gdr_decode_tokens(1, 0, B, n, H, D, D, F(1.0), q, FAKE, FAKE, FAKE,
+                                 FAKE, slot, None if hs is None else
+                                 hs.ctypes.data_as(ctypes.c_void_p), pool, state,
+                                 ckpt, o, None)
+
+
+def test_decode_tokens_rejects(lib):
+    err = lambda: lib.gdr_last_error().decode()  # noqa: E731
+    assert tokens(lib, slot=None, pool=2) == EINVAL and "pool needs B = 3" in err()
+    assert tokens(lib, slot_host=[0, 8, 1]) == EINVAL and "slot[1] = 8" in err()
+    assert tokens(lib, slot_host=[0, -2, 1]) == EINVAL and "slot[1] = -2" in err()
+    assert tokens(lib, slot_host=[5, 2, 5]) == EINVAL and "slot 5 is used by two" in err()
+    assert tokens(lib, slot=None, slot_host=[0, 1, 2]) == EINVAL
+    assert tokens(lib, state=None) == EINVAL and "state_pool is NULL" in err()
+    assert tokens(lib, ckpt=MIS) == EINVAL
+    assert tokens(lib, ckpt=FAKE + 4096) == EINVAL and "overlap" in err()
+    assert tokens(lib, q=None) == EINVAL
+    assert tokens(lib, D=96) == EUNSUPPORTED
+    assert tokens(lib, B=-1) == EINVAL
+    # nothing to do: no launch, no GPU needed
+    assert tokens(lib, n=0) == 0
+    assert tokens(lib, B=0, slot_host=[]) == 0
+
+
+def test_decode_commit_rejects(lib):
+    call = lambda **kw: lib.gdr_decode_commit(  # noqa: E731
+        kw.get("B", 2), 3, 2, kw.get("D", 128), kw.get("D", 128), kw.get("slot", FAKE),
+        kw.get("pool", 4), kw.get("acc", FAKE), kw.get("ckpt", FAKE),
+        kw.get("state", FAKE), None)
+    assert call(acc=None) == EINVAL and "accepted" in lib.gdr_last_error().decode()
+    assert call(ckpt=None) == EINVAL
+    assert call(state=MIS) == EINVAL
+    assert call(slot=None, pool=1) == EINVAL
+    assert call(D=32) == EUNSUPPORTED
+    assert call(B=0) == 0
+
+
+def pool_prefill(lib, N=2, h0s=FAKE, hts=FAKE, h0h=None, hth=None, pool=4, state=FAKE):
+    return lib.gdr_prefill_varlen_pool(
+        1, 1, N, 10, 1, 128, 128, 64, F(1.0), FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE,
+        pool, state, h0s, hts, _hp(h0h), _hp(hth), FAKE, FAKE, 1 << 30, None)
+
+
+def test_prefill_pool_rejects(lib):
+    err = lambda: lib.gdr_last_error().decode()  # noqa: E731
+    assert pool_prefill(lib, h0s=None) == EINVAL and "required" in err()
+    assert pool_prefill(lib, state=None) == EINVAL
+    assert pool_prefill(lib, h0h=[0, 4], hth=[1, 2]) == EINVAL and "h0_slot[1] = 4" in err()
+    assert pool_prefill(lib, h0h=[0, 1], hth=[-3, 2]) == EINVAL and "ht_slot[0]" in err()
+    assert pool_prefill(lib, h0h=[0, 1], hth=[3, 3]) == EINVAL and "both write slot 3" in err()
+    assert pool_prefill(lib, h0h=[0, 1], hth=[1, 2]) == EINVAL and "reads slot 1" in err()
+    assert pool_prefill(lib, pool=-1) == EINVAL
+    assert pool_prefill(lib, N=0) == 0
 
 
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
