@@ -124,6 +124,29 @@ __device__ inline void head_step(f32x4 (&S)[Geom<D>::M], const T *qp, const T *k
     }
 }
 
+// Consecutive workgroups go to the eight XCDs in turn, each with its own L2.
+// The NRB workgroups of one head share its q, k and gate vectors, so they
+// are numbered to run on one XCD, two heads after another: each XCD then
+// streams 2 * D * D * 4 contiguous bytes of state per run, and all but the
+// first workgroup of a head find its vectors in L2 (measured on the
+// 48-layer decode: 4.45 ms with heads spread over XCDs, 4.18 ms with one
+// head per run, 4.01 ms with two, 4.11 ms with four).  Heads beyond the
+// last multiple of 16 keep the plain order.
+template <int NRB>
+__device__ inline void xcd_head_block(int i, long long heads, int &head, int &rb) {
+    constexpr int G = 2;                       // heads per run on one XCD
+    const long long full = (heads / (8 * G)) * 8 * G * NRB;
+    if (i < full) {
+        const int x = i & 7, j = i >> 3;
+        const int run = j / (NRB * G), r = j % (NRB * G);
+        head = (run * 8 + x) * G + r / NRB;
+        rb = r % NRB;
+    } else {
+        head = i / NRB;
+        rb = i % NRB;
+    }
+}
+
 template <int D>
 __device__ inline const float *state_row(const float *st, int m, int lane, int w) {
     using G = Geom<D>;
@@ -149,8 +172,8 @@ __global__ __launch_bounds__(256) void decode_rows_kernel(DecodeArgs a, DecodeLa
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
     const int bh_count = a.B * a.H;
-    const int rb = blockIdx.x % NRB;
-    const int slot_lin = blockIdx.x / NRB;
+    int rb, slot_lin;
+    xcd_head_block<NRB>(blockIdx.x, (long long)L.n * bh_count, slot_lin, rb);
     const int rec = slot_lin / bh_count;
     const int bh = slot_lin - rec * bh_count;
     const int code = L.code[rec];
@@ -257,8 +280,8 @@ __global__ __launch_bounds__(256) void decode_tokens_kernel(TokensArgs a) {
     constexpr int NRB = D / ROWS;
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
-    const int rb = blockIdx.x % NRB;
-    const int bh = blockIdx.x / NRB;
+    int rb, bh;
+    xcd_head_block<NRB>(blockIdx.x, (long long)a.B * a.H, bh, rb);
     const int b = bh / a.H;
     const int h = bh - b * a.H;
     long long slot = b;
@@ -330,8 +353,8 @@ __global__ __launch_bounds__(256) void commit_kernel(TokensArgs a, const int32_t
     constexpr int PIECE = 4096;                 // floats per workgroup
     constexpr int NP = D * D / PIECE;
     constexpr int V = PIECE / 4 / 256;          // float4 per thread
-    const int piece = blockIdx.x % NP;
-    const int bh = blockIdx.x / NP;
+    int piece, bh;
+    xcd_head_block<NP>(blockIdx.x, (long long)a.B * a.H, bh, piece);
     const int b = bh / a.H;
     const int h = bh - b * a.H;
     const int m = accepted[b];
