@@ -143,6 +143,44 @@ def decode_inputs(L, B, H, D, dtype=torch.bfloat16, place=None, seed=0,
     return dict(q=q, k=k, v=v, g=g, beta=beta, pool=st, placement=place)
 
 
+def _draw_raw(shape_tok, H, D, dtype, gate, gen, device, h0_shape=None):
+    """Raw projections: q, k, v ~ N(0,1) (q and k not normalised), beta and
+    gate logits ~ N(0,1), all stored in dtype; h0 0.02 N(0,1) fp32."""
+    q = torch.randn((*shape_tok, H, D), generator=gen, device=device).to(dtype)
+    k = torch.randn((*shape_tok, H, D), generator=gen, device=device).to(dtype)
+    v = torch.randn((*shape_tok, H, D), generator=gen, device=device).to(dtype)
+    xb = torch.randn((*shape_tok, H), generator=gen, device=device).to(dtype)
+    gshape = (*shape_tok, H, D) if gate == "channel" else (*shape_tok, H)
+    xg = torch.randn(gshape, generator=gen, device=device).to(dtype)
+    h0 = None
+    if h0_shape is not None:
+        h0 = torch.randn(h0_shape, generator=gen, device=device, dtype=torch.float32) * 0.02
+    return dict(q=q.contiguous(), k=k.contiguous(), v=v.contiguous(),
+                gate_logit=xg.contiguous(), beta_logit=xb.contiguous(), h0=h0,
+                gate_scale=GATE_SCALE[gate])
+
+
+def raw_prefill_inputs(B, T, H, D, dtype=torch.bfloat16, gate="scalar", seed=0,
+                       h0=True, device="cpu"):
+    """Fixed-length batch of raw projections for the fused-preprocessing
+    calls: q, k, v [B,T,H,D], gate_logit [B,T,H](,D), beta_logit [B,T,H],
+    all in dtype, h0 [B,H,D,D] fp32 or None, and the gate scale c."""
+    return _draw_raw((B, T), H, D, dtype, gate, _gen(seed, device), device,
+                     h0_shape=(B, H, D, D) if h0 else None)
+
+
+def raw_varlen_inputs(lengths, H, D, dtype=torch.bfloat16, gate="channel", seed=0,
+                      h0=True, device="cpu"):
+    """Packed batch of raw projections (as raw_prefill_inputs) with
+    cu_seqlens on the device and as a host numpy copy."""
+    cu = cu_from_lengths(lengths)
+    d = _draw_raw((int(cu[-1]),), H, D, dtype, gate, _gen(seed, device), device,
+                  h0_shape=(len(lengths), H, D, D) if h0 else None)
+    d["cu_seqlens"] = torch.from_numpy(cu).to(device)
+    d["cu_seqlens_host"] = cu
+    return d
+
+
 def pool_states(P, H, D, seed=0, device="cpu"):
     """A state pool [P,H,D,D] fp32 with 0.02*N(0,1) entries (the law of the
     initial states), drawn slot by slot."""

@@ -208,3 +208,31 @@ def forward_pool(q, k, v, g, beta, cu_seqlens, state_pool, h0_slot, ht_slot,
         if _slot_ok(s1[i], P):
             new_pool[s1[i]] = ht[i]
     return o, new_pool
+
+
+# Fused input preprocessing.  The kernels can take the projections as they
+# come out of a layer: q and k un-normalised, and logits for beta and the
+# gate.  The definitions, in fp64:
+#     q_hat = q / sqrt(|q|^2 + NORM_EPS)        (per token and head)
+#     beta  = 1 / (1 + e^{-x_beta})
+#     g     = -c * softplus(x_g) = -c * ln(1 + e^{x_g})
+NORM_EPS = 1e-6
+
+
+def _f64(x):
+    return _f32(x).astype(np.float64)
+
+
+def preprocess(q, k, gate_logit, beta_logit, gate_scale: float):
+    """Raw projections -> (q_hat, k_hat, g, beta) as float32 arrays.
+
+    The fp64 results are rounded once to float32, the width the recurrence
+    oracle reads (a relative change below 2^-24)."""
+    qf, kf, xg, xb = (_f64(x) for x in (q, k, gate_logit, beta_logit))
+    qh = qf / np.sqrt((qf * qf).sum(-1, keepdims=True) + NORM_EPS)
+    kh = kf / np.sqrt((kf * kf).sum(-1, keepdims=True) + NORM_EPS)
+    beta = 1.0 / (1.0 + np.exp(-xb))
+    # ln(1 + e^x) without overflow: max(x, 0) + ln(1 + e^{-|x|})
+    softplus = np.maximum(xg, 0.0) + np.log1p(np.exp(-np.abs(xg)))
+    g = -float(gate_scale) * softplus
+    return tuple(np.ascontiguousarray(a.astype(np.float32)) for a in (qh, kh, g, beta))

@@ -149,3 +149,128 @@ def test_serving_pins_catch_slot_mistakes(oracle_lib):
                                    lib=oracle_lib, **kw)
     with pytest.raises(AssertionError):
         pin_pool_prefill_pure_decay(swapped)
+
+
+# --------------------------------------------------------------------------
+# Fused input preprocessing: q and k normalised per token, beta from its
+# logit by the logistic function, g = -c softplus(logit).
+
+def _fused(q, k, v, xg, xb, c, **kw):
+    qh, kh, g, beta = oracle.preprocess(q, k, xg, xb, c)
+    return oracle.forward(qh, kh, v, g, beta, **kw)
+
+
+# One token worked by hand (Dk = Dv = 2): q = (3, 4) -> (0.6, 0.8);
+# k = (0, 2) -> (0, 1); beta logit 0 -> 1/2; gate logit 0 with c = 1 ->
+# g = -ln 2, a = 1/2.  From S0 = [[1, 2], [3, 4]]: S' = S0 / 2,
+# S'k = (1, 2), u = (5 - 1, 6 - 2) / 2 = (2, 2), S1 = [[0.5, 3], [1.5, 4]],
+# o = S1 q = (2.7, 4.1).
+def pin_fused_worked_example(fused):
+    q = np.array([[[[3.0, 4.0]]]], np.float32)
+    k = np.array([[[[0.0, 2.0]]]], np.float32)
+    v = np.array([[[[5.0, 6.0]]]], np.float32)
+    S0 = np.array([[[[1.0, 2.0], [3.0, 4.0]]]], np.float32)
+    for channel in (False, True):
+        xg = np.zeros((1, 1, 1, 2) if channel else (1, 1, 1), np.float32)
+        xb = np.zeros((1, 1, 1), np.float32)
+        o, ht = fused(q, k, v, xg, xb, 1.0, h0=S0)
+        # the 1e-6 inside the norms moves the result by about 1e-7
+        np.testing.assert_allclose(o[0, 0, 0], [2.7, 4.1], atol=1e-6)
+        np.testing.assert_allclose(ht[0, 0], [[0.5, 3.0], [1.5, 4.0]], atol=1e-6)
+
+
+# Scale invariance: multiplying q_t or k_t by any positive number changes
+# nothing once they are normalised.
+def pin_fused_scale_invariance(fused):
+    rng = np.random.default_rng(24)
+    B, T, H, D = 2, 7, 2, 8
+    q = rng.standard_normal((B, T, H, D)).astype(np.float32)
+    k = rng.standard_normal((B, T, H, D)).astype(np.float32)
+    v = rng.standard_normal((B, T, H, D)).astype(np.float32)
+    xb = rng.standard_normal((B, T, H)).astype(np.float32)
+    S0 = (0.1 * rng.standard_normal((B, H, D, D))).astype(np.float32)
+    sq = rng.uniform(0.5, 4.0, (B, T, H, 1)).astype(np.float32)
+    sk = rng.uniform(0.5, 4.0, (B, T, H, 1)).astype(np.float32)
+    for channel in (False, True):
+        xg = rng.standard_normal((B, T, H, D) if channel else (B, T, H)).astype(np.float32)
+        o1, h1 = fused(q, k, v, xg, xb, 0.3, h0=S0)
+        o2, h2 = fused(q * sq, k * sk, v, xg, xb, 0.3, h0=S0)
+        np.testing.assert_allclose(o2, o1, rtol=1e-5, atol=1e-6)
+        np.testing.assert_allclose(h2, h1, rtol=1e-5, atol=1e-6)
+
+
+# Saturated logits reduce the fused form to the retrieval closed form:
+# beta logit 40 -> beta = 1 (to 4e-18), gate logit -40 -> a = 1 (to 4e-18),
+# keys that are orthonormal rows times 3, q_t = k_t / 2: o_t = v_t.
+def pin_fused_saturated_retrieval(fused):
+    rng = np.random.default_rng(25)
+    D, T = 16, 10
+    Qm, _ = np.linalg.qr(rng.standard_normal((D, D)))
+    keys = (3.0 * Qm[:T]).astype(np.float32)[None, :, None, :]
+    v = rng.standard_normal((1, T, 1, D)).astype(np.float32)
+    xb = np.full((1, T, 1), 40.0, np.float32)
+    for channel in (False, True):
+        xg = np.full((1, T, 1, D) if channel else (1, T, 1), -40.0, np.float32)
+        o, ht = fused(keys * 0.5, keys, v, xg, xb, 1.0)
+        np.testing.assert_allclose(o, v.astype(np.float64), atol=2e-6)
+
+
+# Gate alone: beta logit -40 (beta = 4e-18), gate logit 0 with c = 0.5 gives
+# a = 2^-0.5 per token, so S_t = 2^{-t/2} S0 and o_t = S_t q_hat_t.
+def pin_fused_pure_decay(fused):
+    rng = np.random.default_rng(26)
+    B, T, H, D = 2, 6, 3, 8
+    q = rng.standard_normal((B, T, H, D)).astype(np.float32)
+    k = rng.standard_normal((B, T, H, D)).astype(np.float32)
+    v = rng.standard_normal((B, T, H, D)).astype(np.float32)
+    xb = np.full((B, T, H), -40.0, np.float32)
+    S0 = rng.standard_normal((B, H, D, D)).astype(np.float32)
+    qh = q.astype(np.float64) / np.linalg.norm(q.astype(np.float64), axis=-1, keepdims=True)
+    for channel in (False, True):
+        xg = np.zeros((B, T, H, D) if channel else (B, T, H), np.float32)
+        o, ht = fused(q, k, v, xg, xb, 0.5, h0=S0)
+        # g is rounded to float32 once per token: a relative 1e-8 over six tokens
+        np.testing.assert_allclose(ht, S0 * 2.0 ** (-T / 2), rtol=1e-7, atol=1e-12)
+        for t in range(T):
+            St = S0.astype(np.float64) * 2.0 ** (-(t + 1) / 2)
+            np.testing.assert_allclose(o[:, t], np.einsum("bhij,bhj->bhi", St, qh[:, t]),
+                                       rtol=1e-6, atol=1e-6)
+
+
+FUSED_PINS = [pin_fused_worked_example, pin_fused_scale_invariance,
+              pin_fused_saturated_retrieval, pin_fused_pure_decay]
+
+
+@pytest.mark.parametrize("pin", FUSED_PINS, ids=lambda f: f.__name__)
+def test_oracle_fused_pin(pin, oracle_lib):
+    pin(functools.partial(_fused, lib=oracle_lib))
+
+
+# Plausible mistakes in the preprocessing fail a pin: no normalisation,
+# the logistic function of the wrong sign, softplus without its minus sign,
+# a gate scale that is dropped, and the norm taken over the wrong axis.
+@pytest.mark.parametrize("mistake", ["no_norm", "sigmoid_sign", "softplus_sign",
+                                     "drop_scale", "norm_axis"])
+def test_fused_pins_catch_mistakes(mistake, oracle_lib):
+    def bad(q, k, v, xg, xb, c, **kw):
+        qh, kh, g, beta = oracle.preprocess(q, k, xg, xb, c)
+        if mistake == "no_norm":
+            qh, kh = np.asarray(q, np.float32), np.asarray(k, np.float32)
+        elif mistake == "sigmoid_sign":
+            beta = (1 - beta).astype(np.float32)
+        elif mistake == "softplus_sign":
+            g = (-g).astype(np.float32)
+        elif mistake == "drop_scale":
+            g = (g / c).astype(np.float32)
+        elif mistake == "norm_axis":
+            kf = np.asarray(k, np.float64)
+            kh = (kf / np.sqrt((kf * kf).sum(-2, keepdims=True) + 1e-6)).astype(np.float32)
+        return oracle.forward(qh, kh, v, g, beta, lib=oracle_lib, **kw)
+    failed = 0
+    for pin in FUSED_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(bad)
+        except AssertionError:
+            failed += 1
+    assert failed >= 1, "no pin caught %s" % mistake
