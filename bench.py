@@ -23,7 +23,9 @@ The same line carries:
                 GB/s and % of HBM peak), the packed variable-length KDA
                 prefill, the drafted decode (4 tokens with per-token
                 checkpoints, then the commit of the accepted prefixes) on a
-                slot-indexed pool, and the packed KDA prefill through a pool.
+                slot-indexed pool, the packed KDA prefill through a pool, and
+                the GDN and KDA prefill on raw projections (fused q/k
+                normalisation, beta and gate from bf16 logits).
 
 Defaults: 100 warmup steps and 200 timed steps (a fifth of each for the
 decode and varlen workloads): the GPU reaches its steady clock only after
@@ -31,7 +33,7 @@ about a hundred prefill calls, so shorter warm-ups time part of the ramp.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
                        [--only-headline] [--no-cpu-baseline]
-                       [--only {kda_prefill,decode,varlen,draft,varlen_pool}]
+                       [--only {kda_prefill,decode,varlen,draft,varlen_pool,fused_gdn,fused_kda}]
                        (one workload, for profiling)
 """
 import argparse
@@ -128,6 +130,26 @@ def bench_prefill(gdr, synthetic, torch, dev, B, T, H, gate, seed, steps, warmup
             raise RuntimeError(lib.gdr_last_error().decode())
     ms = timed(step, steps, warmup, stream)
     del xs, outs, ws
+    return ms
+
+
+def bench_fused(gdr, synthetic, torch, dev, B, T, H, gate, seed, steps, warmup, h0=True,
+                sets=3):
+    """Chunked prefill on raw projections (fused preprocessing): q, k, v and
+    the logits in bf16, rotating over `sets` input sets."""
+    xs = [synthetic.raw_prefill_inputs(B, T, H, D, torch.bfloat16, gate, seed=seed + i,
+                                       h0=h0, device=dev) for i in range(sets)]
+    ht = torch.empty((B, H, D, D), device=dev, dtype=torch.float32)
+    ws = torch.empty(max(gdr.fused_workspace_bytes(torch.bfloat16, gate == "channel", B, B * T, H), 1),
+                     device=dev, dtype=torch.uint8)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        x = xs[i % sets]
+        gdr.prefill_fused(x["q"], x["k"], x["v"], x["gate_logit"], x["beta_logit"],
+                          x["gate_scale"], h0=x["h0"], ht=ht, workspace=ws)
+    ms = timed(step, steps, warmup, stream)
+    del xs, ht, ws
     return ms
 
 
@@ -257,7 +279,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--only-headline", action="store_true")
-    ap.add_argument("--only", choices=["kda_prefill", "decode", "varlen", "draft", "varlen_pool"],
+    ap.add_argument("--only", choices=["kda_prefill", "decode", "varlen", "draft", "varlen_pool",
+                                       "fused_gdn", "fused_kda"],
                     default=None,
                     help="time one secondary workload alone (for profiling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -285,6 +308,17 @@ def main():
     if args.only == "varlen":
         ms, _, _ = bench_varlen(gdr, synthetic, torch, dev, args.steps, args.warmup)
         print(json.dumps({"workload": "kda_varlen_N16_H32_d128_bf16", "ms_per_step": ms}))
+        return
+    if args.only in ("fused_gdn", "fused_kda"):
+        if args.only == "fused_gdn":
+            ms = bench_fused(gdr, synthetic, torch, dev, 4, 4096, 16, "scalar", 1011,
+                             args.steps, args.warmup)
+            name = "fused_gdn_prefill_B4_H16_T4096_d128_bf16"
+        else:
+            ms = bench_fused(gdr, synthetic, torch, dev, 2, 8192, 32, "channel", 1012,
+                             args.steps, args.warmup, h0=False)
+            name = "fused_kda_prefill_B2_H32_T8192_d128_bf16"
+        print(json.dumps({"workload": name, "ms_per_step": ms}))
         return
     if args.only == "draft":
         md, mc, _, _, _, _ = bench_draft(gdr, synthetic, torch, dev, args.steps, args.warmup)
@@ -376,6 +410,21 @@ def main():
                     "ms_per_step": ms6, "tokens_per_s": tok6 / (ms6 * 1e-3),
                     "GB_per_s": b6 / (ms6 * 1e-3) / 1e9,
                     "frac_hbm": b6 / (ms6 * 1e-3) / 1e9 / HBM_PEAK_GBS})
+        # fused preprocessing: raw bf16 projections and logits (gate 2 B per
+        # value instead of 4), q/k normalised in the kernels
+        for gate, B_, T_, H_, seed, h0_, name in (
+                ("scalar", 4, 4096, 16, 1011, True, "fused_gdn_prefill_B4_H16_T4096_d128_bf16"),
+                ("channel", 2, 8192, 32, 1012, False, "fused_kda_prefill_B2_H32_T8192_d128_bf16")):
+            msf = bench_fused(gdr, synthetic, torch, dev, B_, T_, H_, gate, seed,
+                              args.steps, args.warmup, h0=h0_)
+            thf = B_ * T_ * H_
+            per_tok = 3 * D * 2 + D * 2 + 2 + (2 * D if gate == "channel" else 2)
+            bf = thf * per_tok + B_ * H_ * (2 if h0_ else 1) * D * D * 4
+            sec.append({"workload": name, "ms_per_step": msf,
+                        "tokens_per_s": B_ * T_ / (msf * 1e-3),
+                        "GB_per_s": bf / (msf * 1e-3) / 1e9,
+                        "frac_hbm": bf / (msf * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                        "mfma_frac_alg": prefill_flops(thf) / (msf * 1e-3) / 1e12 / MFMA_BF16_TFLOPS})
         line["secondary"] = sec
 
     if not args.no_cpu_baseline:

@@ -20,7 +20,9 @@ import os
 import torch
 
 __all__ = ["prefill", "prefill_varlen", "prefill_varlen_pool", "decode_step",
-           "decode_placement", "decode_tokens", "decode_commit", "workspace_bytes", "version", "GdrError", "lib_path",
+           "decode_placement", "decode_tokens", "decode_commit", "workspace_bytes",
+           "prefill_fused", "prefill_varlen_fused", "decode_tokens_fused",
+           "fused_workspace_bytes", "version", "GdrError", "lib_path",
            "FA", "SWA", "GDN", "KDA"]
 
 FA, SWA, GDN, KDA = 0, 1, 2, 3
@@ -72,6 +74,17 @@ def _load():
                                       P, P, I, P, P, P, P]
     lib.gdr_decode_commit.restype = I
     lib.gdr_decode_commit.argtypes = [I, I, I, I, I, P, I, P, P, P, P]
+    lib.gdr_prefill_fused_workspace_bytes.restype = Z
+    lib.gdr_prefill_fused_workspace_bytes.argtypes = [I, I, I, ctypes.c_longlong, I]
+    lib.gdr_prefill_chunked_fused.restype = I
+    lib.gdr_prefill_chunked_fused.argtypes = [I, I, I, I, I, I, I, I, F,
+                                              P, P, P, P, P, F, P, P, P, P, Z, P]
+    lib.gdr_prefill_varlen_fused.restype = I
+    lib.gdr_prefill_varlen_fused.argtypes = [I, I, I, I, I, I, I, I, F, P, P,
+                                             P, P, P, P, P, F, P, P, P, P, Z, P]
+    lib.gdr_decode_tokens_fused.restype = I
+    lib.gdr_decode_tokens_fused.argtypes = [I, I, I, I, I, I, I, F, P, P, P, P, P, F,
+                                            P, P, I, P, P, P, P]
     _lib = lib
     return lib
 
@@ -382,3 +395,114 @@ def decode_commit(checkpoints, accepted, state_pool, slot=None):
     _check(_load().gdr_decode_commit(
         B, n, H, D, D, _ptr(slot), state_pool.shape[0], _ptr(accepted),
         _ptr(checkpoints), _ptr(state_pool), _stream(dev)))
+
+
+# --------------------------------------------------------------------------
+# Fused input preprocessing: raw projections in, the kernels normalise q and
+# k per token and form beta = sigmoid(beta_logit) and
+# g = -gate_scale * softplus(gate_logit).  Logits share the dtype of q.
+
+def fused_workspace_bytes(dtype, gated_channels: bool, n_seqs: int, tokens: int,
+                          heads: int) -> int:
+    return int(_load().gdr_prefill_fused_workspace_bytes(
+        _BF16 if dtype == torch.bfloat16 else _F32, _CHANNEL if gated_channels else _SCALAR,
+        n_seqs, tokens, heads))
+
+
+def _raw_checks(q, k, v, gate_logit, beta_logit, lead):
+    dev = q.device
+    for n, t in (("q", q), ("k", k), ("v", v), ("gate_logit", gate_logit),
+                 ("beta_logit", beta_logit)):
+        _dense(n, t, q.dtype, dev)
+    D = q.shape[-1]
+    _need(k.shape == q.shape and v.shape == q.shape, "q, k, v shapes differ")
+    _need(tuple(beta_logit.shape) == lead, "beta_logit must be %s" % (lead,))
+    if tuple(gate_logit.shape) == lead + (D,):
+        return _CHANNEL
+    _need(tuple(gate_logit.shape) == lead, "gate_logit must be %s or %s" % (lead, lead + (D,)))
+    return _SCALAR
+
+
+def prefill_fused(q, k, v, gate_logit, beta_logit, gate_scale: float, h0=None,
+                  scale: float = 1.0, output_final_state: bool = True, ht=None,
+                  workspace=None):
+    """prefill() on raw projections: q, k, v [B,T,H,D]; gate_logit [B,T,H] or
+    [B,T,H,D] and beta_logit [B,T,H] in the dtype of q.  Returns (o, ht)."""
+    B, T, H, D = q.shape
+    dev = q.device
+    gk = _raw_checks(q, k, v, gate_logit, beta_logit, (B, T, H))
+    if h0 is not None:
+        _dense("h0", h0, torch.float32, dev)
+        _need(h0.shape == (B, H, D, D), "h0 must be [B,H,D,D]")
+    o = torch.empty_like(v)
+    if output_final_state and ht is None:
+        ht = torch.empty((B, H, D, D), device=dev, dtype=torch.float32)
+    if ht is not None:
+        _dense("ht", ht, torch.float32, dev)
+        _need(ht.shape == (B, H, D, D), "ht must be [B,H,D,D]")
+    nbytes = fused_workspace_bytes(q.dtype, gk == _CHANNEL, B, B * T, H)
+    workspace = _workspace(workspace, nbytes, dev)
+    _check(_load().gdr_prefill_chunked_fused(
+        _dt(q), gk, B, T, H, D, D, 64, float(scale), _ptr(q), _ptr(k), _ptr(v),
+        _ptr(gate_logit), _ptr(beta_logit), float(gate_scale), _ptr(h0), _ptr(o), _ptr(ht),
+        _ptr(workspace), nbytes, _stream(dev)))
+    return o, ht
+
+
+def prefill_varlen_fused(q, k, v, gate_logit, beta_logit, gate_scale: float, cu_seqlens,
+                         h0=None, scale: float = 1.0, cu_seqlens_host=None,
+                         output_final_state: bool = True, workspace=None, ht=None):
+    """prefill_varlen() on raw projections: q, k, v [T_tot,H,D]; gate_logit
+    [T_tot,H] or [T_tot,H,D] and beta_logit [T_tot,H] in the dtype of q."""
+    Tt, H, D = q.shape
+    dev = q.device
+    gk = _raw_checks(q, k, v, gate_logit, beta_logit, (Tt, H))
+    _dense("cu_seqlens", cu_seqlens, torch.int32, dev)
+    N = cu_seqlens.numel() - 1
+    if h0 is not None:
+        _dense("h0", h0, torch.float32, dev)
+        _need(h0.shape == (N, H, D, D), "h0 must be [N,H,D,D]")
+    host = None if cu_seqlens_host is None else _host_i32(cu_seqlens_host, N + 1,
+                                                           "cu_seqlens_host")
+    o = torch.empty_like(v)
+    if output_final_state and ht is None:
+        ht = torch.empty((N, H, D, D), device=dev, dtype=torch.float32)
+    nbytes = fused_workspace_bytes(q.dtype, gk == _CHANNEL, N, Tt, H)
+    workspace = _workspace(workspace, nbytes, dev)
+    _check(_load().gdr_prefill_varlen_fused(
+        _dt(q), gk, N, Tt, H, D, D, 64, float(scale), _ptr(cu_seqlens),
+        None if host is None else host.ctypes.data_as(ctypes.c_void_p),
+        _ptr(q), _ptr(k), _ptr(v), _ptr(gate_logit), _ptr(beta_logit), float(gate_scale),
+        _ptr(h0), _ptr(o), _ptr(ht), _ptr(workspace), nbytes, _stream(dev)))
+    return o, ht
+
+
+def decode_tokens_fused(q, k, v, gate_logit, beta_logit, gate_scale: float, state_pool,
+                        slot=None, checkpoints=None, scale: float = 1.0, slot_host=None,
+                        o=None):
+    """decode_tokens() on raw projections: q, k, v [B,n,H,D]; gate_logit
+    [B,n,H] or [B,n,H,D] and beta_logit [B,n,H] in the dtype of q."""
+    B, n, H, D = q.shape
+    dev = q.device
+    gk = _raw_checks(q, k, v, gate_logit, beta_logit, (B, n, H))
+    _dense("state_pool", state_pool, torch.float32, dev)
+    _need(state_pool.dim() == 4 and state_pool.shape[1:] == (H, D, D),
+          "state_pool must be [P,H,D,D]")
+    if slot is not None:
+        _dense("slot", slot, torch.int32, dev)
+        _need(slot.shape == (B,), "slot must be [B]")
+    sh = None if slot_host is None else _host_i32(slot_host, B, "slot_host")
+    ret_ckpt = checkpoints is not None
+    if checkpoints is True:
+        checkpoints = torch.empty((B, n, H, D, D), device=dev, dtype=torch.float32)
+    if ret_ckpt:
+        _dense("checkpoints", checkpoints, torch.float32, dev)
+        _need(checkpoints.shape == (B, n, H, D, D), "checkpoints must be [B,n,H,D,D]")
+    if o is None:
+        o = torch.empty_like(v)
+    _check(_load().gdr_decode_tokens_fused(
+        _dt(q), gk, B, n, H, D, D, float(scale), _ptr(q), _ptr(k), _ptr(v),
+        _ptr(gate_logit), _ptr(beta_logit), float(gate_scale), _ptr(slot),
+        None if sh is None else sh.ctypes.data_as(ctypes.c_void_p), state_pool.shape[0],
+        _ptr(state_pool), _ptr(checkpoints if ret_ckpt else None), _ptr(o), _stream(dev)))
+    return (o, checkpoints) if ret_ckpt else o

@@ -74,7 +74,7 @@ gdr_status check_common(int dt, int gk, int Dk, int Dv, const char *what) {
     } while (0)
 
 gdr_status check_prefill_ptrs(const char *what, const void *q, const void *k, const void *v,
-                              const float *g, const float *beta, const float *h0,
+                              const void *g, const void *beta, const float *h0,
                               const void *o, const float *ht, long long tokens) {
     if (tokens > 0) {
         REQUIRE_PTR(q, "q");
@@ -106,7 +106,7 @@ struct WsLayout {
     size_t order, chunk_base, tiles, total;
     long long max_chunks;
 };
-WsLayout ws_layout(bool tiles, int N, long long tokens, int H) {
+WsLayout ws_layout(bool tiles, int N, long long tokens, int H, size_t rec = gdr::kTileBytes) {
     WsLayout w{};
     if (N <= 0 || tokens < 0 || H <= 0) return w;
     auto r256 = [](size_t x) { return (x + 255) / 256 * 256; };
@@ -114,18 +114,33 @@ WsLayout ws_layout(bool tiles, int N, long long tokens, int H) {
     w.chunk_base = r256((size_t)N * sizeof(int32_t));
     w.tiles = w.chunk_base + r256((size_t)(N + 1) * sizeof(int32_t));
     w.max_chunks = tiles ? tokens / 64 + N : 0;
-    w.total = w.tiles + (size_t)w.max_chunks * H * gdr::kTileBytes;
+    w.total = w.tiles + (size_t)w.max_chunks * H * rec;
     return w;
 }
 
 // packed-batch prefill shared by the plain and the pool entry points
+// g and beta: fp32 gate logs and write strengths, or (raw) logits in dt
 gdr_status prefill_varlen_impl(const char *what, int dt, int gk, int N, int T_total, int H,
                                int Dk, int Dv, int chunk, float scale,
                                const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
-                               const void *q, const void *k, const void *v, const float *g,
-                               const float *beta, const float *h0, void *o, float *ht,
-                               const int32_t *h0_slot, const int32_t *ht_slot, long long pool,
-                               void *workspace, size_t ws_bytes, void *stream);
+                               const void *q, const void *k, const void *v, const void *g,
+                               const void *beta, bool raw, float gate_scale, const float *h0,
+                               void *o, float *ht, const int32_t *h0_slot,
+                               const int32_t *ht_slot, long long pool, void *workspace,
+                               size_t ws_bytes, void *stream);
+gdr_status prefill_fixed_impl(const char *what, int dt, int gk, int B, int T, int H, int Dk,
+                              int Dv, int chunk, float scale, const void *q, const void *k,
+                              const void *v, const void *g, const void *beta, bool raw,
+                              float gate_scale, const float *h0, void *o, float *ht,
+                              void *workspace, size_t ws_bytes, void *stream);
+
+size_t record_bytes(bool raw) { return raw ? gdr::kTileBytesRaw : gdr::kTileBytes; }
+
+gdr_status check_gate_scale(const char *what, float c) {
+    if (!(c >= 0.f))   // also rejects NaN
+        return fail(GDR_EINVAL, "%s: gate_scale = %g; it must be >= 0", what, (double)c);
+    return GDR_OK;
+}
 
 }  // namespace
 
@@ -140,12 +155,44 @@ size_t gdr_prefill_workspace_bytes(enum gdr_dtype dt, enum gdr_gate gk, int N,
     return ws_layout(dt == GDR_BF16 && gk == GDR_GATE_SCALAR, N, tokens, H).total;
 }
 
+size_t gdr_prefill_fused_workspace_bytes(enum gdr_dtype dt, enum gdr_gate gk, int N,
+                                         long long tokens, int H) {
+    return ws_layout(dt == GDR_BF16 && gk == GDR_GATE_SCALAR, N, tokens, H,
+                     gdr::kTileBytesRaw).total;
+}
+
 gdr_status gdr_prefill_chunked(enum gdr_dtype dt, enum gdr_gate gk, int B, int T, int H,
                                int Dk, int Dv, int chunk, float scale, const void *q,
                                const void *k, const void *v, const float *g,
                                const float *beta, const float *h0, void *o, float *ht,
                                void *workspace, size_t ws_bytes, void *stream) {
-    const char *what = "gdr_prefill_chunked";
+    return prefill_fixed_impl("gdr_prefill_chunked", dt, gk, B, T, H, Dk, Dv, chunk, scale, q, k,
+                              v, g, beta, false, 0.f, h0, o, ht, workspace, ws_bytes, stream);
+}
+
+gdr_status gdr_prefill_chunked_fused(enum gdr_dtype dt, enum gdr_gate gk, int B, int T, int H,
+                                     int Dk, int Dv, int chunk, float scale, const void *q,
+                                     const void *k, const void *v, const void *gate_logit,
+                                     const void *beta_logit, float gate_scale, const float *h0,
+                                     void *o, float *ht, void *workspace, size_t ws_bytes,
+                                     void *stream) {
+    const char *what = "gdr_prefill_chunked_fused";
+    gdr_status st = check_gate_scale(what, gate_scale);
+    if (st != GDR_OK) return st;
+    return prefill_fixed_impl(what, dt, gk, B, T, H, Dk, Dv, chunk, scale, q, k, v, gate_logit,
+                              beta_logit, true, gate_scale, h0, o, ht, workspace, ws_bytes,
+                              stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+gdr_status prefill_fixed_impl(const char *what, int dt, int gk, int B, int T, int H, int Dk,
+                              int Dv, int chunk, float scale, const void *q, const void *k,
+                              const void *v, const void *g, const void *beta, bool raw,
+                              float gate_scale, const float *h0, void *o, float *ht,
+                              void *workspace, size_t ws_bytes, void *stream) {
     gdr_status st = check_common(dt, gk, Dk, Dv, what);
     if (st != GDR_OK) return st;
     if (chunk != 64) return fail(GDR_EUNSUPPORTED, "%s: chunk = %d; only 64 is supported", what, chunk);
@@ -168,11 +215,16 @@ gdr_status gdr_prefill_chunked(enum gdr_dtype dt, enum gdr_gate gk, int B, int T
     }
     if (B == 0) return GDR_OK;
     const bool tiles = dt == GDR_BF16 && gk == GDR_GATE_SCALAR;
-    const WsLayout L = ws_layout(tiles, B, (long long)B * T, H);
+    const WsLayout L = ws_layout(tiles, B, (long long)B * T, H, record_bytes(raw));
     st = check_workspace(what, workspace, ws_bytes, tiles ? L.total : 0);
     if (st != GDR_OK) return st;
     gdr::PrefillArgs a{};
-    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.h0 = h0; a.o = o; a.ht = ht;
+    a.q = q; a.k = k; a.v = v; a.h0 = h0; a.o = o; a.ht = ht;
+    if (raw) {
+        a.xg = g; a.xb = beta; a.gate_scale = gate_scale;
+    } else {
+        a.g = static_cast<const float *>(g); a.beta = static_cast<const float *>(beta);
+    }
     a.cu_seqlens = nullptr; a.order = nullptr; a.chunk_base = nullptr;
     a.tiles = tiles ? static_cast<char *>(workspace) + L.tiles : nullptr;
     a.max_chunks = tiles ? (long long)B * ((T + 63) / 64) : 0;
@@ -182,6 +234,10 @@ gdr_status gdr_prefill_chunked(enum gdr_dtype dt, enum gdr_gate gk, int B, int T
                                   : gdr::launch_prefill_recurrent(false, Dk, a, s);
     return finish(e, s, what);
 }
+
+}  // namespace
+
+extern "C" {
 
 gdr_status gdr_prefill_chunked_varlen(enum gdr_dtype dt, enum gdr_gate gk, int N, int T_total,
                                       int H, int Dk, int Dv, int chunk, float scale,
@@ -198,8 +254,30 @@ gdr_status gdr_prefill_chunked_varlen(enum gdr_dtype dt, enum gdr_gate gk, int N
             return fail(GDR_EINVAL, "%s: h0 and ht overlap without being equal", what);
     }
     return prefill_varlen_impl(what, dt, gk, N, T_total, H, Dk, Dv, chunk, scale, cu_seqlens,
-                               cu_seqlens_host, q, k, v, g, beta, h0, o, ht, nullptr, nullptr,
-                               0, workspace, ws_bytes, stream);
+                               cu_seqlens_host, q, k, v, g, beta, false, 0.f, h0, o, ht,
+                               nullptr, nullptr, 0, workspace, ws_bytes, stream);
+}
+
+gdr_status gdr_prefill_varlen_fused(enum gdr_dtype dt, enum gdr_gate gk, int N, int T_total,
+                                    int H, int Dk, int Dv, int chunk, float scale,
+                                    const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
+                                    const void *q, const void *k, const void *v,
+                                    const void *gate_logit, const void *beta_logit,
+                                    float gate_scale, const float *h0, void *o, float *ht,
+                                    void *workspace, size_t ws_bytes, void *stream) {
+    const char *what = "gdr_prefill_varlen_fused";
+    gdr_status st = check_gate_scale(what, gate_scale);
+    if (st != GDR_OK) return st;
+    if (h0 && ht && h0 != ht && N > 0 && H > 0 && Dk > 0 && Dv > 0) {
+        const size_t bytes = (size_t)N * H * Dv * Dk * sizeof(float);
+        const char *a0 = (const char *)h0, *a1 = (const char *)ht;
+        if (a0 < a1 + bytes && a1 < a0 + bytes)
+            return fail(GDR_EINVAL, "%s: h0 and ht overlap without being equal", what);
+    }
+    return prefill_varlen_impl(what, dt, gk, N, T_total, H, Dk, Dv, chunk, scale, cu_seqlens,
+                               cu_seqlens_host, q, k, v, gate_logit, beta_logit, true,
+                               gate_scale, h0, o, ht, nullptr, nullptr, 0, workspace, ws_bytes,
+                               stream);
 }
 
 }  // extern "C"
@@ -209,10 +287,11 @@ namespace {
 gdr_status prefill_varlen_impl(const char *what, int dt, int gk, int N, int T_total, int H,
                                int Dk, int Dv, int chunk, float scale,
                                const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
-                               const void *q, const void *k, const void *v, const float *g,
-                               const float *beta, const float *h0, void *o, float *ht,
-                               const int32_t *h0_slot, const int32_t *ht_slot, long long pool,
-                               void *workspace, size_t ws_bytes, void *stream) {
+                               const void *q, const void *k, const void *v, const void *g,
+                               const void *beta, bool raw, float gate_scale, const float *h0,
+                               void *o, float *ht, const int32_t *h0_slot,
+                               const int32_t *ht_slot, long long pool, void *workspace,
+                               size_t ws_bytes, void *stream) {
     gdr_status st = check_common(dt, gk, Dk, Dv, what);
     if (st != GDR_OK) return st;
     if (chunk != 64) return fail(GDR_EUNSUPPORTED, "%s: chunk = %d; only 64 is supported", what, chunk);
@@ -238,7 +317,7 @@ gdr_status prefill_varlen_impl(const char *what, int dt, int gk, int N, int T_to
     st = check_prefill_ptrs(what, q, k, v, g, beta, h0, o, ht, T_total);
     if (st != GDR_OK) return st;
     const bool tiles = dt == GDR_BF16 && gk == GDR_GATE_SCALAR;
-    const WsLayout L = ws_layout(tiles, N, T_total, H);
+    const WsLayout L = ws_layout(tiles, N, T_total, H, record_bytes(raw));
     st = check_workspace(what, workspace, ws_bytes, L.total);
     if (st != GDR_OK) return st;
 
@@ -248,7 +327,12 @@ gdr_status prefill_varlen_impl(const char *what, int dt, int gk, int N, int T_to
     hipError_t e = gdr::launch_varlen_schedule(cu_seqlens, N, order, s);
     if (e != hipSuccess) return finish(e, s, what);
     gdr::PrefillArgs a{};
-    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.h0 = h0; a.o = o; a.ht = ht;
+    a.q = q; a.k = k; a.v = v; a.h0 = h0; a.o = o; a.ht = ht;
+    if (raw) {
+        a.xg = g; a.xb = beta; a.gate_scale = gate_scale;
+    } else {
+        a.g = static_cast<const float *>(g); a.beta = static_cast<const float *>(beta);
+    }
     a.cu_seqlens = cu_seqlens; a.order = order;
     a.chunk_base = reinterpret_cast<int32_t *>(ws + L.chunk_base);
     a.tiles = tiles ? ws + L.tiles : nullptr;
@@ -308,8 +392,9 @@ gdr_status gdr_prefill_varlen_pool(enum gdr_dtype dt, enum gdr_gate gk, int N, i
         }
     }
     return prefill_varlen_impl(what, dt, gk, N, T_total, H, Dk, Dv, chunk, scale, cu_seqlens,
-                               cu_seqlens_host, q, k, v, g, beta, state_pool, o, state_pool,
-                               h0_slot, ht_slot, pool_slots, workspace, ws_bytes, stream);
+                               cu_seqlens_host, q, k, v, g, beta, false, 0.f, state_pool, o,
+                               state_pool, h0_slot, ht_slot, pool_slots, workspace, ws_bytes,
+                               stream);
 }
 
 gdr_status gdr_decode_step(enum gdr_dtype dt, enum gdr_gate gk, int B, int H, int Dk, int Dv,
@@ -381,12 +466,17 @@ gdr_status gdr_decode_placement(const uint8_t *placement, int L, enum gdr_dtype 
     return finish(gdr::launch_decode(dt == GDR_BF16, Dk, a, layers, s), s, what);
 }
 
-gdr_status gdr_decode_tokens(enum gdr_dtype dt, enum gdr_gate gk, int B, int n_tok, int H,
-                             int Dk, int Dv, float scale, const void *q, const void *k,
-                             const void *v, const float *g, const float *beta,
-                             const int32_t *slot, const int32_t *slot_host, int pool_slots,
-                             float *state_pool, float *checkpoints, void *o, void *stream) {
-    const char *what = "gdr_decode_tokens";
+}  // extern "C"
+
+namespace {
+
+// g and beta are fp32 gate logs and write strengths, or (raw) logits in dt
+gdr_status decode_tokens_impl(const char *what, int dt, int gk, int B, int n_tok, int H,
+                              int Dk, int Dv, float scale, const void *q, const void *k,
+                              const void *v, const void *g, const void *beta, bool raw,
+                              float gate_scale, const int32_t *slot, const int32_t *slot_host,
+                              int pool_slots, float *state_pool, float *checkpoints, void *o,
+                              void *stream) {
     gdr_status st = check_common(dt, gk, Dk, Dv, what);
     if (st != GDR_OK) return st;
     if (B < 0 || n_tok < 0 || H <= 0 || pool_slots < 0)
@@ -435,12 +525,47 @@ gdr_status gdr_decode_tokens(enum gdr_dtype dt, enum gdr_gate gk, int B, int n_t
             return fail(GDR_EINVAL, "%s: checkpoints overlap state_pool", what);
     }
     gdr::TokensArgs a{};
-    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+    a.q = q; a.k = k; a.v = v;
+    if (raw) {
+        a.xg = g; a.xb = beta; a.gate_scale = gate_scale;
+    } else {
+        a.g = static_cast<const float *>(g); a.beta = static_cast<const float *>(beta);
+    }
     a.slot = slot; a.pool = pool_slots; a.state = state_pool; a.ckpt = checkpoints; a.o = o;
     a.B = B; a.n = n_tok; a.H = H; a.scale = scale; a.channel_gate = gk == GDR_GATE_CHANNEL;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    return finish(gdr::launch_decode_tokens(dt == GDR_BF16, Dk, a, s), s, what);
+    return finish(gdr::launch_decode_tokens(dt == GDR_BF16, Dk, a, s, raw), s, what);
 }
+
+}  // namespace
+
+extern "C" {
+
+gdr_status gdr_decode_tokens(enum gdr_dtype dt, enum gdr_gate gk, int B, int n_tok, int H,
+                             int Dk, int Dv, float scale, const void *q, const void *k,
+                             const void *v, const float *g, const float *beta,
+                             const int32_t *slot, const int32_t *slot_host, int pool_slots,
+                             float *state_pool, float *checkpoints, void *o, void *stream) {
+    return decode_tokens_impl("gdr_decode_tokens", dt, gk, B, n_tok, H, Dk, Dv, scale, q, k, v,
+                              g, beta, false, 0.f, slot, slot_host, pool_slots, state_pool,
+                              checkpoints, o, stream);
+}
+
+gdr_status gdr_decode_tokens_fused(enum gdr_dtype dt, enum gdr_gate gk, int B, int n_tok,
+                                   int H, int Dk, int Dv, float scale, const void *q,
+                                   const void *k, const void *v, const void *gate_logit,
+                                   const void *beta_logit, float gate_scale,
+                                   const int32_t *slot, const int32_t *slot_host,
+                                   int pool_slots, float *state_pool, float *checkpoints,
+                                   void *o, void *stream) {
+    const char *what = "gdr_decode_tokens_fused";
+    if (!(gate_scale >= 0.f))   // also rejects NaN
+        return fail(GDR_EINVAL, "%s: gate_scale = %g; it must be >= 0", what, (double)gate_scale);
+    return decode_tokens_impl(what, dt, gk, B, n_tok, H, Dk, Dv, scale, q, k, v, gate_logit,
+                              beta_logit, true, gate_scale, slot, slot_host, pool_slots,
+                              state_pool, checkpoints, o, stream);
+}
+
 
 gdr_status gdr_decode_commit(int B, int n_tok, int H, int Dk, int Dv, const int32_t *slot,
                              int pool_slots, const int32_t *accepted, const float *checkpoints,

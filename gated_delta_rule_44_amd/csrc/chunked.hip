@@ -152,7 +152,12 @@ template <int D> struct Smem {
 //            j+2; all: gated operands of chunk j+1, loads of q, k, v(j+2)
 // P(j) is held in registers from phase B to phase C because the O of chunk
 // j-1 reads the previous P during phase B.
-template <int D>
+// RAW: raw projections (fused preprocessing).  q and k are normalised at
+// gating time (the row norms come from the 16 lanes that hold a row), the
+// gate logits are turned into -c softplus at the scan (zero for rows past the
+// sequence end, which must not decay the state), beta from its logit when
+// staged.
+template <int D, bool RAW>
 __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
     using Sm = Smem<D>;
     using LI = LaneIds<D>;
@@ -229,6 +234,8 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
     // gated), and v/beta of the next two chunks (by chunk parity)
     bf16x8 rq[RPT], rk[RPT];
     f32x4 rgc[RPT][2];
+    bf16x8 rgx[RPT];                 // RAW: gate logits
+    float rgf[RPT][8];               // RAW: their gate logs, -c softplus
     bf16x4 rv[2];
     float rb[2];
     rv[0] = rv[1] = bf16x4{};
@@ -242,6 +249,14 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
     auto load_g = [&](const LI &L, long long c) {
         const long long tc = t0 + c * C;
         const int Cc = valid_rows(c);
+        if (RAW) {
+            const unsigned rowx = (unsigned)(a.H * D * 2);
+            const rsrc_t rs = make_rsrc(static_cast<const bf16 *>(a.xg) + ((size_t)tc * a.H + h) * D,
+                                        Cc ? (Cc - 1) * rowx + D * 2 : 0u);
+#pragma unroll
+            for (int i = 0; i < RPT; ++i) rgx[i] = bload16(rs, (L.rg * RPT + i) * rowx + 16 * L.cg);
+            return;
+        }
         const unsigned rowb = (unsigned)(a.H * D * 4);
         const rsrc_t rs = make_rsrc(a.g + ((size_t)tc * a.H + h) * D,
                                     Cc ? (Cc - 1) * rowb + D * 4 : 0u);
@@ -266,9 +281,16 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
         }
         const rsrc_t rv_s = make_rsrc(vg + (size_t)tc * tokstride, Cc ? (Cc - 1) * rowb + BV * 2 : 0u);
         rv[par] = bload8(rv_s, L.vr * rowb + 2 * L.vc);
-        const unsigned browb = (unsigned)(a.H * 4);
-        const rsrc_t rb_s = make_rsrc(a.beta + (size_t)tc * a.H + h, Cc ? (Cc - 1) * browb + 4 : 0u);
-        rb[par] = bload4(rb_s, L.tid * browb);
+        if (RAW) {
+            const unsigned browx = (unsigned)(a.H * 2);
+            const rsrc_t rb_s = make_rsrc(static_cast<const bf16 *>(a.xb) + (size_t)tc * a.H + h,
+                                          Cc ? (Cc - 1) * browx + 2 : 0u);
+            rb[par] = bf16_bits_to_float(bload2(rb_s, L.tid * browx));
+        } else {
+            const unsigned browb = (unsigned)(a.H * 4);
+            const rsrc_t rb_s = make_rsrc(a.beta + (size_t)tc * a.H + h, Cc ? (Cc - 1) * browb + 4 : 0u);
+            rb[par] = bload4(rb_s, L.tid * browb);
+        }
     };
 
     // gated operands Qt, Kt, Kb of the next chunk, held in registers from
@@ -281,6 +303,18 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
 
     // prefix sums of the gate logs of one chunk over this wave's rows
     // (phase B); the wave's per-channel totals go to pfx[par]
+    // RAW: gate logs of chunk c from its logits (zero past the sequence end),
+    // a phase ahead of the scan that reads them
+    auto softplus_g = [&](const LI &L, long long c) {
+        const int Cc = valid_rows(c);
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const bool live = L.rg * RPT + i < Cc;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                rgf[i][e] = live ? neg_softplus((float)rgx[i][e], a.gate_scale) : 0.f;
+        }
+    };
     auto scan = [&](const LI &L, auto par_tag) {
         constexpr int par = decltype(par_tag)::value;
         float run[8];
@@ -290,7 +324,7 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
         for (int i = 0; i < RPT; ++i) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                run[e] += rgc[i][e >> 2][e & 3];
+                run[e] += RAW ? rgf[i][e] : rgc[i][e >> 2][e & 3];
                 cum[par][i][e] = run[e];
             }
         }
@@ -350,12 +384,27 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
 #pragma unroll
         for (int i = 0; i < RPT; ++i) {
             float qt[8], kt[8], kb[8];
+            float nq = 1.f, nk = 1.f;
+            if (RAW) {
+                // |q_r|^2, |k_r|^2 over the CG lanes holding row r (lanes
+                // rgl + RPW m)
+                float sq = 0.f, sk = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    sq = __builtin_fmaf((float)rq[i][e], (float)rq[i][e], sq);
+                    sk = __builtin_fmaf((float)rk[i][e], (float)rk[i][e], sk);
+                }
+                sq = sum_stride<RPW>(sq);
+                sk = sum_stride<RPW>(sk);
+                nq = inv_norm(sq);
+                nk = inv_norm(sk);
+            }
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float eb = __builtin_amdgcn_exp2f(__builtin_fmaf(cum[par][i][e], kL2e, pre[e]));
                 const float ebi = __builtin_amdgcn_rcpf(eb);
-                const float kv = (float)rk[i][e];
-                qt[e] = (float)rq[i][e] * eb;
+                const float kv = RAW ? (float)rk[i][e] * nk : (float)rk[i][e];
+                qt[e] = (RAW ? (float)rq[i][e] * nq : (float)rq[i][e]) * eb;
                 kt[e] = kv * eb;
                 kb[e] = kv * ebi;
             }
@@ -375,7 +424,7 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
             *reinterpret_cast<bf16x8 *>(&sm.Kb[par][r * PD + 8 * L.cg]) = gkb[i];
         }
         *reinterpret_cast<bf16x4 *>(&sm.V[L.vr * PV + L.vc]) = rv[par];
-        if (L.tid < C) sm.beta[L.tid] = rb[par];
+        if (L.tid < C) sm.beta[L.tid] = RAW ? logistic(rb[par]) : rb[par];
     };
 
     // ---- one pipeline iteration; PAR = parity of the prep chunk j
@@ -436,6 +485,7 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
             }
         }
         if (hasP) store_gate(L, PAR);
+        if (RAW && j + 2 < nch) softplus_g(L, j + 2);
         __syncthreads();
 
         // ================= phase B ========================================
@@ -643,10 +693,12 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
         // every path waits on these registers before the loop
         load_g(L, 0);
         load_qkvb(L, 0, 0);
+        if (RAW) softplus_g(L, 0);
         scan(L, std::integral_constant<int, 0>{});
         load_g(L, 1);
         __syncthreads();
         prefix(0);
+        if (RAW) softplus_g(L, 1);
         scan(L, std::integral_constant<int, 1>{});
         load_g(L, 2);
         __syncthreads();
@@ -716,8 +768,13 @@ hipError_t launch_prefill_chunked(int D, const PrefillArgs &a, hipStream_t s) {
     const int ntile = D / BV;
     const long long blocks = ((units + 7) / 8) * 8 * ntile;
     dim3 grid((unsigned)blocks), block(NT);
-    if (D == 128) hipLaunchKernelGGL((chunked_kernel<128>), grid, block, 0, s, a);
-    else          hipLaunchKernelGGL((chunked_kernel<64>), grid, block, 0, s, a);
+    if (a.xg) {
+        if (D == 128) hipLaunchKernelGGL((chunked_kernel<128, true>), grid, block, 0, s, a);
+        else          hipLaunchKernelGGL((chunked_kernel<64, true>), grid, block, 0, s, a);
+    } else {
+        if (D == 128) hipLaunchKernelGGL((chunked_kernel<128, false>), grid, block, 0, s, a);
+        else          hipLaunchKernelGGL((chunked_kernel<64, false>), grid, block, 0, s, a);
+    }
     return hipGetLastError();
 }
 

@@ -64,9 +64,14 @@ template <int D> struct PrepSmem {
     alignas(16) bf16 YD[4][2][256];     // Y_bb, Y_bb^T
     alignas(16) float fb[C];            // b_r
     alignas(16) float fbeta[C];         // beta_r
+    alignas(16) float frk[C];           // 1 / |k_r| (fused preprocessing)
 };
 
-template <int D>
+// RAW (fused preprocessing): gate and beta from their logits, the Gram
+// blocks scaled by the inverse key norms 1/|k_r| 1/|k_s|, and a 6 KiB
+// record whose factor rows are e^{b_r}, e^{b_C - b_r}/|k_r|, e^{b_r}/|k_r|
+// and e^{-b_r}/|k_r| (the chain kernel applies 1/|q_r| itself).
+template <int D, bool RAW>
 __global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a) {
     using Sm = PrepSmem<D>;
     constexpr int PD = Sm::PD;
@@ -75,6 +80,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a) {
     constexpr int NPC = C * CG / 256;
     static_assert(NPC >= 1 && (C * CG) % 256 == 0, "staging layout");
     static_assert(kTileBytes == 5 * 1024 + 2 * C * 4, "tile record: T operands, two factor rows");
+    constexpr size_t REC = RAW ? kTileBytesRaw : kTileBytes;
     __shared__ Sm sm;
 
     // ---- which chunk: ci counts chunks over all sequences
@@ -120,11 +126,35 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a) {
         }
         float gv = 0.f, bv = 0.f;
         if (w == 0) {
-            const unsigned hb = (unsigned)(a.H * 4);
             const size_t gb = (size_t)tc * a.H + h;
-            const unsigned gext = (unsigned)(Cc - 1) * hb + 4;
-            gv = bload4(make_rsrc(a.g + gb, gext), lane * hb);
-            bv = bload4(make_rsrc(a.beta + gb, gext), lane * hb);
+            if (RAW) {
+                // rows past the sequence end keep g = 0 and beta = 0
+                const unsigned hx = (unsigned)(a.H * 2);
+                const unsigned xext = (unsigned)(Cc - 1) * hx + 2;
+                const float xg = bf16_bits_to_float(
+                    bload2(make_rsrc(static_cast<const bf16 *>(a.xg) + gb, xext), lane * hx));
+                const float xb = bf16_bits_to_float(
+                    bload2(make_rsrc(static_cast<const bf16 *>(a.xb) + gb, xext), lane * hx));
+                gv = lane < Cc ? neg_softplus(xg, a.gate_scale) : 0.f;
+                bv = lane < Cc ? logistic(xb) : 0.f;
+            } else {
+                const unsigned hb = (unsigned)(a.H * 4);
+                const unsigned gext = (unsigned)(Cc - 1) * hb + 4;
+                gv = bload4(make_rsrc(a.g + gb, gext), lane * hb);
+                bv = bload4(make_rsrc(a.beta + gb, gext), lane * hb);
+            }
+        }
+        if (RAW) {
+            // |k_r|^2 over the CG consecutive lanes that hold row r
+#pragma unroll
+            for (int i = 0; i < NPC; ++i) {
+                float ss = 0.f;
+#pragma unroll
+                for (int u = 0; u < 8; ++u) ss = __builtin_fmaf((float)vk[i][u], (float)vk[i][u], ss);
+                ss = sum_group<CG>(ss);
+                const int p = i * 256 + tid;
+                if (p % CG == 0) sm.frk[p / CG] = inv_norm(ss);
+            }
         }
 #pragma unroll
         for (int i = 0; i < NPC; ++i) {
@@ -149,10 +179,18 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a) {
         for (int kk = 0; kk < KD; ++kk) g = mfma32(kj[kk], ki[kk], g);
         return g;
     };
+    // Gram block (I, J) of the normalised keys: times 1/|k_r| 1/|k_s|
+    auto knorm = [&](int I, int J, f32x4 g) -> f32x4 {
+        if (!RAW) return g;
+        const float nr = sm.frk[16 * I + l15];
+        const f32x4 ns = *reinterpret_cast<const f32x4 *>(&sm.frk[16 * J + 4 * q4]);
+        return g * ns * nr;
+    };
     // off-diagonal block (I > J) of L, as L_IJ^T
     auto put_L = [&](int I, int J, f32x4 g) {
         const float br = sm.fb[16 * I + l15], betar = sm.fbeta[16 * I + l15];
         const f32x4 bs = *reinterpret_cast<const f32x4 *>(&sm.fb[16 * J + 4 * q4]);
+        g = knorm(I, J, g);
         f32x4 lv;
 #pragma unroll
         for (int e = 0; e < 4; ++e) lv[e] = betar * ex(br - bs[e]) * g[e];
@@ -166,7 +204,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a) {
         const int b = w;
         bf16x8 kd[KD];
         frags(b, kd);
-        const f32x4 g = gram(kd, kd);
+        const f32x4 g = knorm(b, b, gram(kd, kd));
         // M = L_bb as acc(M^T) and acc(M): the Gram block is symmetric, so
         // both come from the one product
         const float br = sm.fb[16 * b + l15], betar = sm.fbeta[16 * b + l15];
@@ -259,7 +297,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a) {
     //      in-chunk inclusive prefix sums of the gate logs: e^{b_r} and
     //      e^{b_C - b_r}.
     {
-        const size_t rec = (size_t)(ci * a.H + h) * kTileBytes;
+        const size_t rec = (size_t)(ci * a.H + h) * REC;
         char *dst = static_cast<char *>(a.tiles) + rec;
         for (int i = tid; i < 4 * 64; i += 256) {
             const int pr = i >> 6, l = i & 63;          // pairs (1,0) (2,0) (3,0) (3,1)
@@ -276,7 +314,14 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a) {
             float *f = reinterpret_cast<float *>(dst + 5120);
             const float b = sm.fb[r];
             f[r] = ex(b);
-            f[C + r] = ex(sm.fb[C - 1] - b);
+            if (RAW) {
+                const float nk = sm.frk[r];
+                f[C + r] = ex(sm.fb[C - 1] - b) * nk;
+                f[2 * C + r] = ex(b) * nk;
+                f[3 * C + r] = ex(-b) * nk;
+            } else {
+                f[C + r] = ex(sm.fb[C - 1] - b);
+            }
         }
     }
 }
@@ -284,7 +329,23 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a) {
 // ===========================================================================
 // chain_kernel: the recurrence over chunks
 // ===========================================================================
-template <int D> struct ChainSmem {
+// the chunk's workspace record as the prep kernel writes it
+template <bool RAW> struct TRecT {
+    bf16x8 pairs[4][64];            // T operand pairs (1,0), (2,0), (3,0), (3,1)
+    bf16x4 halves[2][64];           // first blocks of the pairs (0,0), (2,1)
+    float eb[C];                    // e^{b_r}
+    float hs[C];                    // e^{b_C - b_r}
+};
+template <> struct TRecT<true> {
+    bf16x8 pairs[4][64];
+    bf16x4 halves[2][64];
+    float eb[C];                    // e^{b_r}
+    float hs[C];                    // e^{b_C - b_r} / |k_r|
+    float ek[C];                    // e^{b_r} / |k_r|
+    float nk[C];                    // e^{-b_r} / |k_r|
+};
+
+template <int D, bool RAW> struct ChainSmem {
     // k rows; a row stride of 8 x odd dwords keeps the 16-byte row fragment
     // reads free of bank conflicts (and halves those of the transpose reads,
     // against 4 x odd)
@@ -293,12 +354,7 @@ template <int D> struct ChainSmem {
     // v slice rows [r][i]; a stride of 24 dwords puts the 8 rows that one
     // transpose load touches per half-wave on disjoint banks
     static constexpr int PV = BV + 16;
-    struct TRec {                       // the chunk's workspace record
-        bf16x8 pairs[4][64];            // T operand pairs (1,0), (2,0), (3,0), (3,1)
-        bf16x4 halves[2][64];           // first blocks of the pairs (0,0), (2,1)
-        float eb[C];                    // e^{b_r}
-        float hs[C];                    // e^{b_C - b_r}
-    };
+    using TRec = TRecT<RAW>;
     alignas(16) bf16 K[3][C * PD];      // by chunk mod 3
     alignas(16) bf16 V[3][C * PV];      // by chunk mod 3
     alignas(16) TRec TR[3];             // by chunk mod 3
@@ -306,9 +362,10 @@ template <int D> struct ChainSmem {
     alignas(16) bf16x8 UB[2][2][64];    // U as operands, per chain wave
 };
 
-template <int D>
+template <int D, bool RAW>
 __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
-    using Sm = ChainSmem<D>;
+    using Sm = ChainSmem<D, RAW>;
+    constexpr size_t REC = RAW ? kTileBytesRaw : kTileBytes;
     constexpr int PD = Sm::PD;
     constexpr int PV = Sm::PV;
     constexpr int NTILE = D / BV;
@@ -316,11 +373,11 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
     constexpr int KS = D / 16;          // 16-row blocks of S^T
     constexpr int CG = D / 8;           // 16-byte pieces per k row
     // staged pieces (16 bytes) per chunk: k rows, v slice rows, T record
-    constexpr int NKP = C * CG, NVP = C * BV / 8, NTP = (int)(kTileBytes / 16);
+    constexpr int NKP = C * CG, NVP = C * BV / 8, NTP = (int)(REC / 16);
     constexpr int NST = NKP + NVP + NTP;
     constexpr int NI = (NST + 127) / 128;   // per staging thread
     static_assert(NKP % 64 == 0 && NVP % 64 == 0, "staging layout");
-    static_assert(sizeof(typename Sm::TRec) == kTileBytes, "tile record layout");
+    static_assert(sizeof(typename Sm::TRec) == REC, "tile record layout");
     __shared__ Sm sm;
 
     // ---- work mapping: the Dv slices of one (sequence, head) share an XCD
@@ -426,7 +483,8 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
 #pragma unroll
                 for (int kk = 0; kk < KD; ++kk) Kf[rb][kk] = frag_rows(Kc, PD, 16 * rb, 32 * kk, lane);
                 vv[rb] = frag_col4(Vc, PV, 16 * rb, 16 * ib, lane);
-                eb[rb] = *reinterpret_cast<const f32x4 *>(&R.eb[16 * rb + 4 * q4]);
+                if constexpr (RAW) eb[rb] = *reinterpret_cast<const f32x4 *>(&R.ek[16 * rb + 4 * q4]);
+                else               eb[rb] = *reinterpret_cast<const f32x4 *>(&R.eb[16 * rb + 4 * q4]);
                 hs[rb] = *reinterpret_cast<const f32x4 *>(&R.hs[16 * rb + 4 * q4]);
                 Ta[rb][0] = rb == 0 ? cat8(R.halves[0][lane], bf16x4{}) : R.pairs[rb - 1][lane];
                 Ta[rb][1] = rb == 2 ? cat8(R.halves[1][lane], bf16x4{})
@@ -516,9 +574,9 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
             const rsrc_t rks = make_rsrc(kg + base, extent(c, D * 2));
             const rsrc_t rvs = make_rsrc(vg + base, extent(c, BV * 2));
             const bool have = valid_rows(c) > 0 && cbase + c < a.max_chunks;
-            const size_t rec = (size_t)((have ? cbase + c : 0) * a.H + h) * kTileBytes;
+            const size_t rec = (size_t)((have ? cbase + c : 0) * a.H + h) * REC;
             const rsrc_t rts = make_rsrc(static_cast<const char *>(a.tiles) + rec,
-                                         have ? (unsigned)kTileBytes : 0u);
+                                         have ? (unsigned)REC : 0u);
 #pragma unroll
             for (int i = 0; i < NI; ++i) {
                 const int p0 = i * 128 + 64 * (w - 4);   // this wave's first piece
@@ -631,11 +689,26 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
             for (int J = 0; J <= RB; ++J) {
 #pragma unroll
                 for (int kk = 0; kk < KD; ++kk) Kj[J][kk] = frag_rows(Kc, PD, 16 * J, 32 * kk, lane);
-                const f32x4 ebJ = *reinterpret_cast<const f32x4 *>(&sm.TR[m3].eb[16 * J + 4 * q4]);
+                if constexpr (RAW) {
+                    nebJ[J] = *reinterpret_cast<const f32x4 *>(&sm.TR[m3].nk[16 * J + 4 * q4]);
+                } else {
+                    const f32x4 ebJ = *reinterpret_cast<const f32x4 *>(&sm.TR[m3].eb[16 * J + 4 * q4]);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) nebJ[J][e] = __builtin_amdgcn_rcpf(ebJ[e]);   // e^{-b_s}
+                    for (int e = 0; e < 4; ++e) nebJ[J][e] = __builtin_amdgcn_rcpf(ebJ[e]);   // e^{-b_s}
+                }
             }
-            const float ebr = sm.TR[m3].eb[16 * RB + l15];
+            float ebr = sm.TR[m3].eb[16 * RB + l15];
+            if constexpr (RAW) {
+                // 1/|q_r| for the lane's row: its 8 KD values, then the four
+                // lanes (q4) that share the row
+                float ss = 0.f;
+#pragma unroll
+                for (int kk = 0; kk < KD; ++kk)
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) ss = __builtin_fmaf((float)Qr[r][kk][u], (float)Qr[r][kk][u], ss);
+                ss = swap_sum32(swap_sum16(ss));
+                ebr *= inv_norm(ss);
+            }
             // diag(e^b) Q S^T (S entering chunk c)
 #pragma unroll
             for (int ob = 0; ob < 2; ++ob) {
@@ -733,16 +806,26 @@ hipError_t launch_prefill_chain(int D, const PrefillArgs &a, hipStream_t s) {
     const long long prep_blocks = a.max_chunks * a.H;
     if (prep_blocks > 0) {
         dim3 grid((unsigned)prep_blocks), block(256);
-        if (D == 128) hipLaunchKernelGGL((prep_kernel<128>), grid, block, 0, s, a);
-        else          hipLaunchKernelGGL((prep_kernel<64>), grid, block, 0, s, a);
+        if (a.xg) {
+            if (D == 128) hipLaunchKernelGGL((prep_kernel<128, true>), grid, block, 0, s, a);
+            else          hipLaunchKernelGGL((prep_kernel<64, true>), grid, block, 0, s, a);
+        } else {
+            if (D == 128) hipLaunchKernelGGL((prep_kernel<128, false>), grid, block, 0, s, a);
+            else          hipLaunchKernelGGL((prep_kernel<64, false>), grid, block, 0, s, a);
+        }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     const int ntile = D / BV;
     const long long blocks = ((units + 7) / 8) * 8 * ntile;
     dim3 grid((unsigned)blocks), block(512);
-    if (D == 128) hipLaunchKernelGGL((chain_kernel<128>), grid, block, 0, s, a);
-    else          hipLaunchKernelGGL((chain_kernel<64>), grid, block, 0, s, a);
+    if (a.xg) {
+        if (D == 128) hipLaunchKernelGGL((chain_kernel<128, true>), grid, block, 0, s, a);
+        else          hipLaunchKernelGGL((chain_kernel<64, true>), grid, block, 0, s, a);
+    } else {
+        if (D == 128) hipLaunchKernelGGL((chain_kernel<128, false>), grid, block, 0, s, a);
+        else          hipLaunchKernelGGL((chain_kernel<64, false>), grid, block, 0, s, a);
+    }
     return hipGetLastError();
 }
 

@@ -187,6 +187,48 @@ __device__ inline f32x4 mfma32z(bf16x8 a, bf16x8 b) {
 __device__ inline f32x4 mfma16z(bf16x4 a, bf16x4 b) {
     return mfma16(a, b, f32x4{0.f, 0.f, 0.f, 0.f});
 }
+// Cross-lane sums on the VALU (no LDS round trip, so no wait on other LDS
+// traffic in flight).  DPP within a 16-lane row; the gfx950 swaps across
+// rows: v_permlane16_swap exchanges odd rows of one register with even rows
+// of the other, v_permlane32_swap the upper half of one with the lower half
+// of the other, so with both registers holding x, their sum is
+// x[l] + x[l ^ 16] (resp. x[l ^ 32]) in every lane.  (Written out in asm:
+// both registers of a swap carry a result; s_nop 1 covers the VALU write ->
+// permlane read hazard.)
+template <int CTRL>
+__device__ inline float dpp_f(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                 CTRL, 0xF, 0xF, true));
+}
+__device__ inline float swap_sum16(float x) {
+    float a = x, b = x;
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+    return a + b;
+}
+__device__ inline float swap_sum32(float x) {
+    float a = x, b = x;
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+    return a + b;
+}
+// sum over the lanes of the wave congruent to this one modulo S (S = 4 or 8)
+template <int S>
+__device__ inline float sum_stride(float x) {
+    static_assert(S == 4 || S == 8, "stride");
+    x += dpp_f<0x128>(x);                   // row_ror:8
+    if (S == 4) x += dpp_f<0x124>(x);       // row_ror:4
+    return swap_sum32(swap_sum16(x));
+}
+// sum over each aligned group of G consecutive lanes (G = 8 or 16)
+template <int G>
+__device__ inline float sum_group(float x) {
+    static_assert(G == 8 || G == 16, "group");
+    x += dpp_f<0xB1>(x);                    // quad_perm [1,0,3,2]
+    x += dpp_f<0x4E>(x);                    // quad_perm [2,3,0,1]
+    x += dpp_f<0x141>(x);                   // row_half_mirror
+    if (G == 16) x += dpp_f<0x140>(x);      // row_mirror
+    return x;
+}
+
 __device__ inline float bf16_bits_to_float(unsigned short h) {
     return __builtin_bit_cast(float, (unsigned)h << 16);
 }

@@ -36,6 +36,27 @@ template <> struct Elem<bf16> {
     }
 };
 
+// Fused input preprocessing: the kernels can take raw projections and form
+// the recurrence inputs themselves, per token and head,
+//     q <- q / sqrt(|q|^2 + kNormEps),  k likewise,
+//     beta = 1 / (1 + e^{-x_beta}),     g = -c ln(1 + e^{x_g}),
+// with the logits stored in the dtype of q.
+constexpr float kNormEps = 1e-6f;
+constexpr float kLog2eF = 1.4426950408889634f;
+constexpr float kLn2F = 0.6931471805599453f;
+
+__device__ inline float logistic(float x) {
+    return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-x * kLog2eF));
+}
+// -c softplus(x) = -c (max(x, 0) + ln(1 + e^{-|x|})); v_log_f32 is log2
+__device__ inline float neg_softplus(float x, float c) {
+    const float e = __builtin_amdgcn_exp2f(-__builtin_fabsf(x) * kLog2eF);
+    return -c * (__builtin_fmaxf(x, 0.f) + __builtin_amdgcn_logf(1.f + e) * kLn2F);
+}
+__device__ inline float inv_norm(float sum_sq) {
+    return __builtin_amdgcn_rsqf(sum_sq + kNormEps);
+}
+
 // One recurrent layer slot for the decode kernel: layer index and gate kind.
 struct DecodeLayers {
     int n;                        // number of layers to step
@@ -70,9 +91,14 @@ struct TokensArgs {
     int B, n, H;
     float scale;
     int channel_gate;
+    // raw projections (fused preprocessing): logits in dt, laid out as g
+    // and beta; q and k are normalised in the kernel
+    const void *xg, *xb;
+    float gate_scale;
 };
 
-hipError_t launch_decode_tokens(bool bf16_io, int D, const TokensArgs &a, hipStream_t s);
+hipError_t launch_decode_tokens(bool bf16_io, int D, const TokensArgs &a, hipStream_t s,
+                                bool raw = false);
 // state[slot[b], h] <- ckpt[b, accepted[b] - 1, h] where 1 <= accepted[b] <= n
 hipError_t launch_decode_commit(int D, const TokensArgs &a, const int32_t *accepted,
                                 hipStream_t s);
@@ -97,6 +123,11 @@ struct PrefillArgs {
     // from slot h0_slot[n] and ends in slot ht_slot[n]; nullptr = slot n
     const int32_t *h0_slot, *ht_slot;
     long long pool;
+    // raw projections (fused preprocessing) when xg != nullptr: gate and
+    // beta logits in the dtype of q, laid out as g and beta; q and k are
+    // normalised in the kernels
+    const void *xg, *xb;
+    float gate_scale;
 };
 
 // Initial state of sequence n, head h (nullptr: start from zeros) and where
@@ -125,6 +156,9 @@ __device__ inline float *seq_ht(const PrefillArgs &a, int n, int h) {
 // T as MFMA operands of its 16x16 blocks (bf16, 5 KiB), then two
 // rows of the chunk's 64 decay factors (fp32).
 constexpr size_t kTileBytes = 5 * 1024 + 2 * 64 * 4;
+// With fused preprocessing the record carries the key norms folded into
+// two more factor rows (6 KiB).
+constexpr size_t kTileBytesRaw = kTileBytes + 2 * 64 * 4;
 
 hipError_t launch_prefill_recurrent(bool bf16_io, int D, const PrefillArgs &a,
                                     hipStream_t s);

@@ -47,22 +47,47 @@ __device__ inline float dot4(f32x4 a, f32x4 b) {
 
 // One token's update of the state slice S held by this thread.  qp, kp, vp
 // point at the head's D-vector for this token, gp at its gate logs (D values
-// for a channel gate, one for a scalar gate).  The output is written to op.
-template <typename T, int D>
+// for a channel gate, one for a scalar gate; fp32).  The output is written
+// to op.  RAW (fused preprocessing): gp points at gate logits of type T and
+// beta is a logit; q and k are normalised over the LPR lanes of the row.
+template <typename T, int D, bool RAW>
 __device__ inline void head_step(f32x4 (&S)[Geom<D>::M], const T *qp, const T *kp,
-                                 const T *vp, const float *gp, bool channel,
-                                 float beta, float scale, T *op, int lane, int w) {
+                                 const T *vp, const void *gp, bool channel,
+                                 float beta, float scale, float gate_scale, T *op, int lane,
+                                 int w) {
     using G = Geom<D>;
     const int c0 = (lane % G::LPR) * 4;
     const int sub = lane / G::LPR;
-    const f32x4 kv = Elem<T>::load4(kp + c0);
-    const f32x4 qv = Elem<T>::load4(qp + c0);
+    f32x4 kv = Elem<T>::load4(kp + c0);
+    f32x4 qv = Elem<T>::load4(qp + c0);
     f32x4 lg;
-    if (channel) {
-        lg = *reinterpret_cast<const f32x4 *>(gp + c0);
+    if (RAW) {
+        const T *xg = static_cast<const T *>(gp);
+        if (channel) {
+            lg = Elem<T>::load4(xg + c0);
+        } else {
+            const float s = Elem<T>::load(xg);
+            lg = f32x4{s, s, s, s};
+        }
+        lg = f32x4{neg_softplus(lg.x, gate_scale), neg_softplus(lg.y, gate_scale),
+                   neg_softplus(lg.z, gate_scale), neg_softplus(lg.w, gate_scale)};
+        beta = logistic(beta);
+        float sk = dot4(kv, kv), sq = dot4(qv, qv);
+#pragma unroll
+        for (int mask = G::LPR / 2; mask >= 1; mask >>= 1) {
+            sk += __shfl_xor(sk, mask);
+            sq += __shfl_xor(sq, mask);
+        }
+        kv = kv * inv_norm(sk);
+        qv = qv * inv_norm(sq);
     } else {
-        const float s = gp[0];
-        lg = f32x4{s, s, s, s};
+        const float *g = static_cast<const float *>(gp);
+        if (channel) {
+            lg = *reinterpret_cast<const f32x4 *>(g + c0);
+        } else {
+            const float s = g[0];
+            lg = f32x4{s, s, s, s};
+        }
     }
     constexpr float kLog2e = 1.4426950408889634f;
     const f32x4 a = f32x4{__builtin_amdgcn_exp2f(lg.x * kLog2e),
@@ -251,7 +276,8 @@ struct TokIn {
     float v[PASSES];
 };
 
-template <typename T, int D, int PASSES>
+// RAW: the gate and beta slots hold the logits, still to be transformed
+template <typename T, int D, int PASSES, bool RAW>
 __device__ __forceinline__ TokIn<PASSES> load_token(const TokensArgs &a, size_t bth, int c0,
                                                     const int (&row)[PASSES]) {
     TokIn<PASSES> x;
@@ -260,19 +286,30 @@ __device__ __forceinline__ TokIn<PASSES> load_token(const TokensArgs &a, size_t 
     const T *vp = static_cast<const T *>(a.v) + bth * D;
     x.k = Elem<T>::load4(kp + c0);
     x.q = Elem<T>::load4(qp + c0);
-    if (a.channel_gate) {
-        x.lg = *reinterpret_cast<const f32x4 *>(a.g + bth * D + c0);
+    if (RAW) {
+        const T *xg = static_cast<const T *>(a.xg);
+        if (a.channel_gate) {
+            x.lg = Elem<T>::load4(xg + bth * D + c0);
+        } else {
+            const float s = Elem<T>::load(xg + bth);
+            x.lg = f32x4{s, s, s, s};
+        }
+        x.beta = Elem<T>::load(static_cast<const T *>(a.xb) + bth);
     } else {
-        const float s = a.g[bth];
-        x.lg = f32x4{s, s, s, s};
+        if (a.channel_gate) {
+            x.lg = *reinterpret_cast<const f32x4 *>(a.g + bth * D + c0);
+        } else {
+            const float s = a.g[bth];
+            x.lg = f32x4{s, s, s, s};
+        }
+        x.beta = a.beta[bth];
     }
-    x.beta = a.beta[bth];
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) x.v[p] = Elem<T>::load(vp + row[p]);
     return x;
 }
 
-template <typename T, int D, int PASSES>
+template <typename T, int D, int PASSES, bool RAW>
 __global__ __launch_bounds__(256) void decode_tokens_kernel(TokensArgs a) {
     using G = Geom<D>;
     constexpr int RPP = G::RPI;
@@ -302,11 +339,26 @@ __global__ __launch_bounds__(256) void decode_tokens_kernel(TokensArgs a) {
         S[p] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(st + (size_t)row[p] * D + c0));
 
     const size_t bh0 = (size_t)b * a.n * a.H + h;        // (b, token 0, h)
-    TokIn<PASSES> cur = load_token<T, D, PASSES>(a, bh0, c0, row);
+    TokIn<PASSES> cur = load_token<T, D, PASSES, RAW>(a, bh0, c0, row);
     constexpr float kLog2e = 1.4426950408889634f;
     for (int t = 0; t < a.n; ++t) {
         const size_t bth = bh0 + (size_t)t * a.H;
-        const TokIn<PASSES> nxt = t + 1 < a.n ? load_token<T, D, PASSES>(a, bth + a.H, c0, row) : cur;
+        const TokIn<PASSES> nxt = t + 1 < a.n ? load_token<T, D, PASSES, RAW>(a, bth + a.H, c0, row) : cur;
+        if (RAW) {
+            // |k|^2 and |q|^2 over the LPR lanes of the row, then the
+            // normalised vectors, beta and the gate logs from their logits
+            float sk = dot4(cur.k, cur.k), sq = dot4(cur.q, cur.q);
+#pragma unroll
+            for (int mask = G::LPR / 2; mask >= 1; mask >>= 1) {
+                sk += __shfl_xor(sk, mask);
+                sq += __shfl_xor(sq, mask);
+            }
+            cur.k = cur.k * inv_norm(sk);
+            cur.q = cur.q * inv_norm(sq);
+            cur.beta = logistic(cur.beta);
+            cur.lg = f32x4{neg_softplus(cur.lg.x, a.gate_scale), neg_softplus(cur.lg.y, a.gate_scale),
+                           neg_softplus(cur.lg.z, a.gate_scale), neg_softplus(cur.lg.w, a.gate_scale)};
+        }
         const f32x4 av = f32x4{__builtin_amdgcn_exp2f(cur.lg.x * kLog2e), __builtin_amdgcn_exp2f(cur.lg.y * kLog2e),
                                __builtin_amdgcn_exp2f(cur.lg.z * kLog2e), __builtin_amdgcn_exp2f(cur.lg.w * kLog2e)};
         const f32x4 ak = av * cur.k;
@@ -378,7 +430,7 @@ __global__ __launch_bounds__(256) void commit_kernel(TokensArgs a, const int32_t
 // ---------------------------------------------------------------------------
 // Prefill in the recurrent form: one workgroup per (sequence, head) walks
 // its tokens in order with the state resident in registers.
-template <typename T, int D>
+template <typename T, int D, bool RAW>
 __global__ __launch_bounds__(256) void prefill_recurrent_kernel(PrefillArgs a) {
     using G = Geom<D>;
     const int lane = threadIdx.x & 63;
@@ -410,9 +462,17 @@ __global__ __launch_bounds__(256) void prefill_recurrent_kernel(PrefillArgs a) {
     const T *v = static_cast<const T *>(a.v) + h * D;
     T *o = static_cast<T *>(a.o) + h * D;
     for (long long t = t0; t < t1; ++t) {
-        head_step<T, D>(S, q + t * tok, k + t * tok, v + t * tok, a.g + t * gtok + goff,
-                        a.channel_gate != 0, a.beta[t * a.H + h], a.scale, o + t * tok,
-                        lane, w);
+        if (RAW) {
+            const T *xg = static_cast<const T *>(a.xg) + t * gtok + goff;
+            const float xb = Elem<T>::load(static_cast<const T *>(a.xb) + t * a.H + h);
+            head_step<T, D, true>(S, q + t * tok, k + t * tok, v + t * tok, xg,
+                                  a.channel_gate != 0, xb, a.scale, a.gate_scale, o + t * tok,
+                                  lane, w);
+        } else {
+            head_step<T, D, false>(S, q + t * tok, k + t * tok, v + t * tok,
+                                   a.g + t * gtok + goff, a.channel_gate != 0,
+                                   a.beta[t * a.H + h], a.scale, 0.f, o + t * tok, lane, w);
+        }
     }
     if (float *htp = seq_ht<D>(a, n, h)) {
 #pragma unroll
@@ -443,20 +503,29 @@ hipError_t launch_decode(bool bf16_io, int D, const DecodeArgs &a,
     return hipGetLastError();
 }
 
-hipError_t launch_decode_tokens(bool bf16_io, int D, const TokensArgs &a, hipStream_t s) {
+template <bool RAW>
+void launch_tokens(bool bf16_io, int D, const TokensArgs &a, dim3 grid, hipStream_t s) {
+    constexpr int P = GDR_DECODE_PASSES;
+    dim3 block(256);
+    if (bf16_io) {
+        if (D == 128) hipLaunchKernelGGL((decode_tokens_kernel<bf16, 128, P, RAW>), grid, block, 0, s, a);
+        else          hipLaunchKernelGGL((decode_tokens_kernel<bf16, 64, P, RAW>), grid, block, 0, s, a);
+    } else {
+        if (D == 128) hipLaunchKernelGGL((decode_tokens_kernel<float, 128, P, RAW>), grid, block, 0, s, a);
+        else          hipLaunchKernelGGL((decode_tokens_kernel<float, 64, P, RAW>), grid, block, 0, s, a);
+    }
+}
+
+hipError_t launch_decode_tokens(bool bf16_io, int D, const TokensArgs &a, hipStream_t s,
+                                bool raw) {
     if ((long long)a.B * a.H <= 0 || a.n <= 0) return hipSuccess;
     constexpr int P = GDR_DECODE_PASSES;
     const long long per_head = D == 128 ? 128 / (Geom<128>::RPI * P) : 64 / (Geom<64>::RPI * P);
     const long long blocks = (long long)a.B * a.H * per_head;
     if (blocks >= (1LL << 31)) return hipErrorInvalidValue;
-    dim3 grid((unsigned)blocks), block(256);
-    if (bf16_io) {
-        if (D == 128) hipLaunchKernelGGL((decode_tokens_kernel<bf16, 128, P>), grid, block, 0, s, a);
-        else          hipLaunchKernelGGL((decode_tokens_kernel<bf16, 64, P>), grid, block, 0, s, a);
-    } else {
-        if (D == 128) hipLaunchKernelGGL((decode_tokens_kernel<float, 128, P>), grid, block, 0, s, a);
-        else          hipLaunchKernelGGL((decode_tokens_kernel<float, 64, P>), grid, block, 0, s, a);
-    }
+    dim3 grid((unsigned)blocks);
+    if (raw) launch_tokens<true>(bf16_io, D, a, grid, s);
+    else     launch_tokens<false>(bf16_io, D, a, grid, s);
     return hipGetLastError();
 }
 
@@ -476,12 +545,22 @@ hipError_t launch_prefill_recurrent(bool bf16_io, int D, const PrefillArgs &a,
     const long long blocks = (long long)a.N * a.H;
     if (blocks <= 0) return hipSuccess;
     dim3 grid((unsigned)blocks), block(256);
-    if (bf16_io) {
-        if (D == 128) hipLaunchKernelGGL((prefill_recurrent_kernel<bf16, 128>), grid, block, 0, s, a);
-        else          hipLaunchKernelGGL((prefill_recurrent_kernel<bf16, 64>), grid, block, 0, s, a);
+    if (a.xg) {
+        if (bf16_io) {
+            if (D == 128) hipLaunchKernelGGL((prefill_recurrent_kernel<bf16, 128, true>), grid, block, 0, s, a);
+            else          hipLaunchKernelGGL((prefill_recurrent_kernel<bf16, 64, true>), grid, block, 0, s, a);
+        } else {
+            if (D == 128) hipLaunchKernelGGL((prefill_recurrent_kernel<float, 128, true>), grid, block, 0, s, a);
+            else          hipLaunchKernelGGL((prefill_recurrent_kernel<float, 64, true>), grid, block, 0, s, a);
+        }
     } else {
-        if (D == 128) hipLaunchKernelGGL((prefill_recurrent_kernel<float, 128>), grid, block, 0, s, a);
-        else          hipLaunchKernelGGL((prefill_recurrent_kernel<float, 64>), grid, block, 0, s, a);
+        if (bf16_io) {
+            if (D == 128) hipLaunchKernelGGL((prefill_recurrent_kernel<bf16, 128, false>), grid, block, 0, s, a);
+            else          hipLaunchKernelGGL((prefill_recurrent_kernel<bf16, 64, false>), grid, block, 0, s, a);
+        } else {
+            if (D == 128) hipLaunchKernelGGL((prefill_recurrent_kernel<float, 128, false>), grid, block, 0, s, a);
+            else          hipLaunchKernelGGL((prefill_recurrent_kernel<float, 64, false>), grid, block, 0, s, a);
+        }
     }
     return hipGetLastError();
 }

@@ -268,6 +268,58 @@ gdr_status gdr_decode_commit(int B, int n_tok, int H, int Dk, int Dv, const int3
                              int pool_slots, const int32_t *accepted,
                              const float *checkpoints, float *state_pool, void *stream);
 
+/*
+ * Fused input preprocessing.  A layer's projections reach the mixer raw: q
+ * and k before their L2 normalisation, and logits for beta and the gate.
+ * These calls take them as they are and form the recurrence inputs inside
+ * the kernels, per token and head, in fp32:
+ *
+ *     q <- q / sqrt(|q|^2 + 1e-6),   k likewise,
+ *     beta = 1 / (1 + exp(-beta_logit)),
+ *     g = ln a = -gate_scale * ln(1 + exp(gate_logit)).
+ *
+ * gate_logit and beta_logit are in the dtype of q (bf16 or fp32), laid out as
+ * g and beta of the plain calls (gate_logit [.., H] for GDR_GATE_SCALAR,
+ * [.., H, Dk] for GDR_GATE_CHANNEL).  gate_scale >= 0 (GDR_EINVAL
+ * otherwise).  The pages give no preprocessing; these three are the usual
+ * forms of the operations, and taking them inside the kernels saves the
+ * separate passes over q, k and the gate, and halves the gate bytes of a
+ * bf16 caller.  Everything else -- layouts, h0/ht, aliasing, numerics of the
+ * recurrence, errors -- is as in the plain call named.
+ */
+
+/* Workspace of the fused prefill calls: as gdr_prefill_workspace_bytes, with
+ * 6144-byte chunk records (the key norms folded into two more factor rows). */
+size_t gdr_prefill_fused_workspace_bytes(enum gdr_dtype dt, enum gdr_gate gk, int N,
+                                         long long tokens, int H);
+
+/* gdr_prefill_chunked on raw projections (workspace: the size above). */
+gdr_status gdr_prefill_chunked_fused(enum gdr_dtype dt, enum gdr_gate gk, int B, int T,
+                                     int H, int Dk, int Dv, int chunk, float scale,
+                                     const void *q, const void *k, const void *v,
+                                     const void *gate_logit, const void *beta_logit,
+                                     float gate_scale, const float *h0, void *o, float *ht,
+                                     void *workspace, size_t ws_bytes, void *stream);
+
+/* gdr_prefill_chunked_varlen on raw projections (workspace: the size above). */
+gdr_status gdr_prefill_varlen_fused(enum gdr_dtype dt, enum gdr_gate gk, int N,
+                                    int T_total, int H, int Dk, int Dv, int chunk,
+                                    float scale, const int32_t *cu_seqlens,
+                                    const int32_t *cu_seqlens_host, const void *q,
+                                    const void *k, const void *v, const void *gate_logit,
+                                    const void *beta_logit, float gate_scale,
+                                    const float *h0, void *o, float *ht, void *workspace,
+                                    size_t ws_bytes, void *stream);
+
+/* gdr_decode_tokens on raw projections. */
+gdr_status gdr_decode_tokens_fused(enum gdr_dtype dt, enum gdr_gate gk, int B, int n_tok,
+                                   int H, int Dk, int Dv, float scale, const void *q,
+                                   const void *k, const void *v, const void *gate_logit,
+                                   const void *beta_logit, float gate_scale,
+                                   const int32_t *slot, const int32_t *slot_host,
+                                   int pool_slots, float *state_pool, float *checkpoints,
+                                   void *o, void *stream);
+
 /* Thread-local text describing the last non-OK status of this thread. */
 const char *gdr_last_error(void);
 

@@ -35,6 +35,8 @@ def test_header_declares_the_boundary():
                             "gdr_prefill_chunked_varlen", "gdr_decode_step",
                             "gdr_decode_placement", "gdr_prefill_varlen_pool",
                             "gdr_decode_tokens", "gdr_decode_commit",
+                            "gdr_prefill_fused_workspace_bytes", "gdr_prefill_chunked_fused",
+                            "gdr_prefill_varlen_fused", "gdr_decode_tokens_fused",
                             "gdr_last_error", "gdr_version"])
 
 
@@ -212,6 +214,39 @@ def test_prefill_pool_rejects(lib):
     assert pool_prefill(lib, h0h=[0, 1], hth=[1, 2]) == EINVAL and "reads slot 1" in err()
     assert pool_prefill(lib, pool=-1) == EINVAL
     assert pool_prefill(lib, N=0) == 0
+
+
+def test_fused_rejects(lib):
+    err = lambda: lib.gdr_last_error().decode()  # noqa: E731
+    bf, f32 = torch.bfloat16, torch.float32
+    # the fused records are 6144 bytes (two more factor rows)
+    assert gdr.fused_workspace_bytes(bf, False, 1, 64, 1) == 512 + 2 * 6144
+    assert gdr.fused_workspace_bytes(bf, True, 1, 64, 1) == gdr.workspace_bytes(bf, True, 1, 64, 1)
+    assert gdr.fused_workspace_bytes(f32, False, 1, 64, 1) == 512
+
+    def fixed(c=1.0, ws_bytes=1 << 30, **kw):
+        return lib.gdr_prefill_chunked_fused(
+            1, kw.get("gk", 0), 1, 64, 1, 128, 128, 64, F(1.0), FAKE, FAKE, FAKE,
+            kw.get("xg", FAKE), kw.get("xb", FAKE), F(c), None, FAKE, FAKE, FAKE, ws_bytes, None)
+    assert fixed(c=-0.5) == EINVAL and "gate_scale" in err()
+    assert fixed(c=float("nan")) == EINVAL
+    assert fixed(xg=None) == EINVAL and "g is NULL" in err()
+    assert fixed(ws_bytes=512 + 2 * 6144 - 1) == EINVAL and "workspace of 12800" in err()
+
+    def varlen_f(c=1.0, N=2, **kw):
+        return lib.gdr_prefill_varlen_fused(
+            1, 1, N, 10, 1, 128, 128, 64, F(1.0), FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE,
+            F(c), None, FAKE, None, FAKE, 1 << 30, None)
+    assert varlen_f(c=-1.0) == EINVAL
+    assert varlen_f(N=0) == 0
+
+    def tok(c=1.0, **kw):
+        return lib.gdr_decode_tokens_fused(1, 1, 2, 3, 2, 128, 128, F(1.0), FAKE, FAKE, FAKE,
+                                           FAKE, FAKE, F(c), None, None, kw.get("pool", 2),
+                                           kw.get("state", FAKE), None, FAKE, None)
+    assert tok(c=-2.0) == EINVAL
+    assert tok(pool=1) == EINVAL and "pool needs" in err()
+    assert tok(state=None) == EINVAL
 
 
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):

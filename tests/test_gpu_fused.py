@@ -1,0 +1,129 @@
+"""GPU parity of the fused-preprocessing calls (raw q and k, beta and gate
+logits) through the C ABI against the fp64 oracle: oracle.preprocess turns
+the stored raw values into the recurrence inputs, then the same fp64
+recurrence as for the plain calls.  Ragged chunk tails matter here: rows
+past a sequence's end must not add a gate to the chunk's total decay."""
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_44_amd as gdr
+import oracle
+from gated_delta_rule_44_amd import synthetic
+from tests.conftest import gpu_available
+from tests.gpu_util import announce, assert_close
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+DEV = torch.device("cuda:0")
+DTYPES = {"fp32": torch.float32, "bf16": torch.bfloat16}
+RAW = ("q", "k", "v", "gate_logit", "beta_logit")
+
+
+def sync():
+    torch.cuda.synchronize(DEV)
+
+
+def _ref_inputs(x):
+    qh, kh, g, beta = oracle.preprocess(x["q"], x["k"], x["gate_logit"], x["beta_logit"],
+                                        x["gate_scale"])
+    return qh, kh, x["v"], g, beta
+
+
+@pytest.mark.parametrize("dt", ["fp32", "bf16"])
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("T", [1, 65, 200])
+def test_prefill_fused(dt, gate, D, T):
+    announce("prefill_fused %s %s D=%d T=%d" % (dt, gate, D, T))
+    x = synthetic.raw_prefill_inputs(2, T, 3, D, DTYPES[dt], gate, seed=50 + T, device=DEV)
+    o, ht = gdr.prefill_fused(*[x[n] for n in RAW], x["gate_scale"], h0=x["h0"], scale=0.7)
+    sync()
+    o_ref, ht_ref = oracle.forward(*_ref_inputs(x), h0=x["h0"], scale=0.7)
+    eo = assert_close(o, o_ref, DTYPES[dt], "o")
+    eh = assert_close(ht, ht_ref, DTYPES[dt], "ht")
+    announce("  err o=%.2e ht=%.2e" % (eo, eh))
+
+
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
+def test_prefill_fused_zero_h0_and_empty(gate):
+    announce("prefill_fused no h0, T=0 %s" % gate)
+    x = synthetic.raw_prefill_inputs(2, 130, 2, 128, torch.bfloat16, gate, seed=60,
+                                     h0=False, device=DEV)
+    o, ht = gdr.prefill_fused(*[x[n] for n in RAW], x["gate_scale"])
+    sync()
+    o_ref, ht_ref = oracle.forward(*_ref_inputs(x))
+    assert_close(o, o_ref, torch.bfloat16, "o")
+    assert_close(ht, ht_ref, torch.bfloat16, "ht")
+    e = synthetic.raw_prefill_inputs(2, 0, 2, 128, torch.bfloat16, gate, seed=61, device=DEV)
+    _, ht0 = gdr.prefill_fused(*[e[n] for n in RAW], e["gate_scale"], h0=e["h0"])
+    sync()
+    assert torch.equal(ht0, e["h0"])
+
+
+@pytest.mark.parametrize("dt", ["fp32", "bf16"])
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
+def test_prefill_varlen_fused(dt, gate):
+    announce("prefill_varlen_fused %s %s" % (dt, gate))
+    lens = [70, 0, 130, 33, 64, 1]
+    x = synthetic.raw_varlen_inputs(lens, 3, 128, DTYPES[dt], gate, seed=62, device=DEV)
+    o, ht = gdr.prefill_varlen_fused(*[x[n] for n in RAW], x["gate_scale"], x["cu_seqlens"],
+                                     h0=x["h0"], cu_seqlens_host=x["cu_seqlens_host"])
+    sync()
+    o_ref, ht_ref = oracle.forward(*_ref_inputs(x), h0=x["h0"],
+                                   cu_seqlens=x["cu_seqlens_host"])
+    eo = assert_close(o, o_ref, DTYPES[dt], "o")
+    eh = assert_close(ht, ht_ref, DTYPES[dt], "ht")
+    assert torch.equal(ht[1], x["h0"][1]), "empty sequence"
+    announce("  err o=%.2e ht=%.2e" % (eo, eh))
+
+
+@pytest.mark.parametrize("dt", ["fp32", "bf16"])
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_decode_tokens_fused(dt, gate, D):
+    announce("decode_tokens_fused %s %s D=%d" % (dt, gate, D))
+    B, n, H, P = 5, 4, 3, 8
+    x = synthetic.raw_prefill_inputs(B, n, H, D, DTYPES[dt], gate, seed=63, h0=False,
+                                     device=DEV)
+    pool0 = synthetic.pool_states(P, H, D, seed=64, device=DEV)
+    slot_np = synthetic.serving_slots(B, P, idle=1, seed=65)
+    act = np.flatnonzero(slot_np >= 0)
+    pool = pool0.clone()
+    o, ck = gdr.decode_tokens_fused(*[x[nm] for nm in RAW], x["gate_scale"], pool,
+                                    slot=torch.from_numpy(slot_np).to(DEV), checkpoints=True,
+                                    scale=0.9)
+    sync()
+    qh, kh, v, g, beta = _ref_inputs(x)
+    o_ref, _, ck_ref = oracle.decode_tokens(qh, kh, v, g, beta, pool0, slot=slot_np,
+                                            checkpoints=True, scale=0.9)
+    assert torch.equal(pool, pool0)
+    eo = assert_close(o[act], o_ref[act], DTYPES[dt], "o")
+    ec = assert_close(ck[act], ck_ref[act], DTYPES[dt], "checkpoints")
+    announce("  err o=%.2e ckpt=%.2e" % (eo, ec))
+
+
+def _sampled_fused(B, T, H, gate, seed, pairs):
+    x = synthetic.raw_prefill_inputs(B, T, H, 128, torch.bfloat16, gate, seed=seed,
+                                     h0=gate == "scalar", device=DEV)
+    o, ht = gdr.prefill_fused(*[x[n] for n in RAW], x["gate_scale"], h0=x["h0"])
+    sync()
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(ht).all())
+    for b, h in pairs:
+        sl = {n: x[n][b:b + 1, :, h:h + 1].contiguous() for n in RAW}
+        sl["gate_scale"] = x["gate_scale"]
+        h0 = None if x["h0"] is None else x["h0"][b:b + 1, h:h + 1].contiguous()
+        o_ref, ht_ref = oracle.forward(*_ref_inputs(sl), h0=h0)
+        eo = assert_close(o[b:b + 1, :, h:h + 1], o_ref, torch.bfloat16, "o[%d,:,%d]" % (b, h))
+        eh = assert_close(ht[b:b + 1, h:h + 1], ht_ref, torch.bfloat16, "ht[%d,%d]" % (b, h))
+        announce("  (b=%d,h=%d) rel-fro o=%.2e ht=%.2e" % (b, h, eo, eh))
+
+
+def test_fused_gdn_prefill_B4_H16_T4096():
+    announce("fused GDN prefill B=4 H=16 T=4096 (raw projections)")
+    _sampled_fused(4, 4096, 16, "scalar", 1011, [(0, 0), (2, 9), (3, 15)])
+
+
+def test_fused_kda_prefill_B2_H32_T8192():
+    announce("fused KDA prefill B=2 H=32 T=8192 (raw projections)")
+    _sampled_fused(2, 8192, 32, "channel", 1012, [(0, 3), (1, 30)])
