@@ -236,3 +236,49 @@ def preprocess(q, k, gate_logit, beta_logit, gate_scale: float):
     softplus = np.maximum(xg, 0.0) + np.log1p(np.exp(-np.abs(xg)))
     g = -float(gate_scale) * softplus
     return tuple(np.ascontiguousarray(a.astype(np.float32)) for a in (qh, kh, g, beta))
+
+
+# --------------------------------------------------------------------------
+# Backward: the vector-Jacobian product of the recurrence.  Written out as
+# the forward recurrence in plain PyTorch CPU ops in fp64 (token by token,
+# the same steps as gdr_oracle.c) and differentiated by autograd: for
+# upstream gradients dO (of o) and dht (of the final state), it returns the
+# gradients of L = sum(o * dO) + sum(S_T * dht).
+
+def forward_torch(q, k, v, g, beta, h0=None, scale: float = 1.0):
+    """The recurrence on float64 torch tensors (fixed-length batch layouts
+    as ``forward``), differentiable.  Returns (o, S_T)."""
+    import torch
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    channel = g.dim() == q.dim()
+    S = (torch.zeros((B, H, Dv, Dk), dtype=torch.float64) if h0 is None else h0)
+    outs = []
+    for t in range(T):
+        a = torch.exp(g[:, t])                                   # [B,H,Dk] or [B,H]
+        S = S * (a[:, :, None, :] if channel else a[:, :, None, None])
+        kt, qt, vt = k[:, t], q[:, t], v[:, t]
+        y = torch.einsum("bhij,bhj->bhi", S, kt)
+        u = beta[:, t][..., None] * (vt - y)
+        S = S + u[..., :, None] * kt[..., None, :]
+        outs.append(scale * torch.einsum("bhij,bhj->bhi", S, qt))
+    return torch.stack(outs, 1), S
+
+
+def backward(q, k, v, g, beta, do, h0=None, dht=None, scale: float = 1.0):
+    """Gradients (dq, dk, dv, dg, dbeta, dh0) as float64 numpy arrays for a
+    fixed-length batch (layouts as ``forward``; do like v, dht like h0)."""
+    import torch
+    to = lambda x: torch.tensor(_f64(x), dtype=torch.float64, requires_grad=True)  # noqa: E731
+    qt, kt, vt, gt, bt = (to(x) for x in (q, k, v, g, beta))
+    B, T, H, Dk = qt.shape
+    Dv = vt.shape[-1]
+    h0t = to(h0) if h0 is not None else torch.zeros((B, H, Dv, Dk), dtype=torch.float64,
+                                                     requires_grad=True)
+    o, ST = forward_torch(qt, kt, vt, gt, bt, h0t, scale)
+    loss = (o * torch.tensor(_f64(do))).sum()
+    if dht is not None:
+        loss = loss + (ST * torch.tensor(_f64(dht))).sum()
+    grads = torch.autograd.grad(loss, [qt, kt, vt, gt, bt, h0t], allow_unused=True)
+    return tuple(np.zeros(x.shape) if gr is None else gr.detach().numpy()
+                 for gr, x in zip(grads, (qt, kt, vt, gt, bt, h0t)))
