@@ -25,7 +25,8 @@ The same line carries:
                 checkpoints, then the commit of the accepted prefixes) on a
                 slot-indexed pool, the packed KDA prefill through a pool, and
                 the GDN and KDA prefill on raw projections (fused q/k
-                normalisation, beta and gate from bf16 logits).
+                normalisation, beta and gate from bf16 logits), and the
+                backward of the GDN and KDA prefill workloads.
 
 Defaults: 100 warmup steps and 200 timed steps (a fifth of each for the
 decode and varlen workloads): the GPU reaches its steady clock only after
@@ -33,7 +34,8 @@ about a hundred prefill calls, so shorter warm-ups time part of the ramp.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
                        [--only-headline] [--no-cpu-baseline]
-                       [--only {kda_prefill,decode,varlen,draft,varlen_pool,fused_gdn,fused_kda}]
+                       [--only {kda_prefill,decode,varlen,draft,varlen_pool,fused_gdn,fused_kda,
+                                backward_gdn,backward_kda}]
                        (one workload, for profiling)
 """
 import argparse
@@ -151,6 +153,46 @@ def bench_fused(gdr, synthetic, torch, dev, B, T, H, gate, seed, steps, warmup, 
     ms = timed(step, steps, warmup, stream)
     del xs, ht, ws
     return ms
+
+
+def bench_backward(gdr, synthetic, torch, dev, B, T, H, gate, seed, steps, warmup, h0=True):
+    """Gradients of the chunked prefill (gdr_backward_chunked): all inputs and
+    the upstream gradients resident, outputs and workspace preallocated."""
+    x = synthetic.prefill_inputs(B, T, H, D, torch.bfloat16, gate, seed=seed, h0=h0, device=dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed + 50)
+    do = torch.randn((B, T, H, D), generator=gen, device=dev).to(torch.bfloat16)
+    dht = torch.randn((B, H, D, D), generator=gen, device=dev) * 0.1
+    lib = gdr._load()
+    import ctypes
+    f32 = dict(device=dev, dtype=torch.float32)
+    outs = [torch.empty((B, T, H, D), **f32) for _ in range(3)] + \
+        [torch.empty(x["g"].shape, **f32), torch.empty((B, T, H), **f32),
+         torch.empty((B, H, D, D), **f32)]
+    nbytes = int(lib.gdr_backward_workspace_bytes(1 if gate == "channel" else 0, B, T, H, D, D))
+    ws = torch.empty(nbytes, device=dev, dtype=torch.uint8)
+    stream = torch.cuda.current_stream(dev)
+    P = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    args = [1, 1 if gate == "channel" else 0, B, T, H, D, D, C, ctypes.c_float(1.0),
+            P(x["q"]), P(x["k"]), P(x["v"]), P(x["g"]), P(x["beta"]), P(x["h0"]), P(do), P(dht)] + \
+        [P(t) for t in outs] + [P(ws), ctypes.c_size_t(nbytes), ctypes.c_void_p(stream.cuda_stream)]
+
+    def step(i):
+        rc = lib.gdr_backward_chunked(*args)
+        if rc:
+            raise RuntimeError(lib.gdr_last_error().decode())
+    ms = timed(step, steps, warmup, stream)
+    del x, outs, ws
+    return ms
+
+
+def backward_bytes(tokens_heads, units, gate, h0=True):
+    """Algorithmic HBM bytes of one backward call: q, k, v, do in bf16, g and
+    beta read; dq, dk, dv in fp32, dg and dbeta written, per token-head;
+    h0, dht read and dh0 written per (sequence, head)."""
+    gb = 4 * D if gate == "channel" else 4
+    per_tok = 4 * D * 2 + gb + 4 + 3 * D * 4 + gb + 4
+    return tokens_heads * per_tok + units * (3 if h0 else 2) * D * D * 4
 
 
 def bench_varlen(gdr, synthetic, torch, dev, steps, warmup):
@@ -280,7 +322,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--only-headline", action="store_true")
     ap.add_argument("--only", choices=["kda_prefill", "decode", "varlen", "draft", "varlen_pool",
-                                       "fused_gdn", "fused_kda"],
+                                       "fused_gdn", "fused_kda", "backward_gdn", "backward_kda"],
                     default=None,
                     help="time one secondary workload alone (for profiling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -318,6 +360,17 @@ def main():
             ms = bench_fused(gdr, synthetic, torch, dev, 2, 8192, 32, "channel", 1012,
                              args.steps, args.warmup, h0=False)
             name = "fused_kda_prefill_B2_H32_T8192_d128_bf16"
+        print(json.dumps({"workload": name, "ms_per_step": ms}))
+        return
+    if args.only in ("backward_gdn", "backward_kda"):
+        if args.only == "backward_gdn":
+            ms = bench_backward(gdr, synthetic, torch, dev, 4, 4096, 16, "scalar", 1001,
+                                args.steps, args.warmup)
+            name = "backward_gdn_B4_H16_T4096_d128_bf16"
+        else:
+            ms = bench_backward(gdr, synthetic, torch, dev, 2, 8192, 32, "channel", 1002,
+                                args.steps, args.warmup, h0=False)
+            name = "backward_kda_B2_H32_T8192_d128_bf16"
         print(json.dumps({"workload": name, "ms_per_step": ms}))
         return
     if args.only == "draft":
@@ -425,6 +478,17 @@ def main():
                         "GB_per_s": bf / (msf * 1e-3) / 1e9,
                         "frac_hbm": bf / (msf * 1e-3) / 1e9 / HBM_PEAK_GBS,
                         "mfma_frac_alg": prefill_flops(thf) / (msf * 1e-3) / 1e12 / MFMA_BF16_TFLOPS})
+        # backward of the two prefill workloads
+        for gate, B_, T_, H_, seed, h0_, name in (
+                ("scalar", 4, 4096, 16, 1001, True, "backward_gdn_B4_H16_T4096_d128_bf16"),
+                ("channel", 2, 8192, 32, 1002, False, "backward_kda_B2_H32_T8192_d128_bf16")):
+            msb = bench_backward(gdr, synthetic, torch, dev, B_, T_, H_, gate, seed,
+                                 max(5, args.steps // 5), max(2, args.warmup // 5), h0=h0_)
+            bb = backward_bytes(B_ * T_ * H_, B_ * H_, gate, h0_)
+            sec.append({"workload": name, "ms_per_step": msb,
+                        "tokens_per_s": B_ * T_ / (msb * 1e-3),
+                        "GB_per_s": bb / (msb * 1e-3) / 1e9,
+                        "frac_hbm": bb / (msb * 1e-3) / 1e9 / HBM_PEAK_GBS})
         line["secondary"] = sec
 
     if not args.no_cpu_baseline:

@@ -22,7 +22,7 @@ import torch
 __all__ = ["prefill", "prefill_varlen", "prefill_varlen_pool", "decode_step",
            "decode_placement", "decode_tokens", "decode_commit", "workspace_bytes",
            "prefill_fused", "prefill_varlen_fused", "decode_tokens_fused",
-           "fused_workspace_bytes", "version", "GdrError", "lib_path",
+           "fused_workspace_bytes", "backward", "version", "GdrError", "lib_path",
            "FA", "SWA", "GDN", "KDA"]
 
 FA, SWA, GDN, KDA = 0, 1, 2, 3
@@ -82,6 +82,11 @@ def _load():
     lib.gdr_prefill_varlen_fused.restype = I
     lib.gdr_prefill_varlen_fused.argtypes = [I, I, I, I, I, I, I, I, F, P, P,
                                              P, P, P, P, P, F, P, P, P, P, Z, P]
+    lib.gdr_backward_workspace_bytes.restype = Z
+    lib.gdr_backward_workspace_bytes.argtypes = [I, I, I, I, I, I]
+    lib.gdr_backward_chunked.restype = I
+    lib.gdr_backward_chunked.argtypes = [I, I, I, I, I, I, I, I, F, P, P, P, P, P, P, P, P,
+                                         P, P, P, P, P, P, P, Z, P]
     lib.gdr_decode_tokens_fused.restype = I
     lib.gdr_decode_tokens_fused.argtypes = [I, I, I, I, I, I, I, F, P, P, P, P, P, F,
                                             P, P, I, P, P, P, P]
@@ -506,3 +511,38 @@ def decode_tokens_fused(q, k, v, gate_logit, beta_logit, gate_scale: float, stat
         None if sh is None else sh.ctypes.data_as(ctypes.c_void_p), state_pool.shape[0],
         _ptr(state_pool), _ptr(checkpoints if ret_ckpt else None), _ptr(o), _stream(dev)))
     return (o, checkpoints) if ret_ckpt else o
+
+
+def backward(q, k, v, g, beta, do, h0=None, dht=None, scale: float = 1.0,
+             workspace=None):
+    """Gradients of prefill() for a fixed-length bf16 batch.
+
+    q, k, v, do [B,T,H,D] bf16; g [B,T,H] or [B,T,H,D] and beta [B,T,H]
+    fp32; h0 and dht [B,H,D,D] fp32 or None.  Returns fp32
+    (dq, dk, dv, dg, dbeta, dh0)."""
+    B, T, H, D = q.shape
+    dev = q.device
+    for n, t in (("q", q), ("k", k), ("v", v), ("do", do)):
+        _dense(n, t, torch.bfloat16, dev)
+    _dense("g", g, torch.float32, dev)
+    _dense("beta", beta, torch.float32, dev)
+    _need(k.shape == q.shape and v.shape == q.shape and do.shape == q.shape, "shapes differ")
+    _need(beta.shape == (B, T, H), "beta must be [B,T,H]")
+    gk = _CHANNEL if g.dim() == 4 else _SCALAR
+    _need(g.shape == ((B, T, H, D) if gk == _CHANNEL else (B, T, H)), "bad gate shape")
+    for n, t in (("h0", h0), ("dht", dht)):
+        if t is not None:
+            _dense(n, t, torch.float32, dev)
+            _need(t.shape == (B, H, D, D), "%s must be [B,H,D,D]" % n)
+    f32 = dict(device=dev, dtype=torch.float32)
+    dq, dk, dv = (torch.empty((B, T, H, D), **f32) for _ in range(3))
+    dg = torch.empty(g.shape, **f32)
+    dbeta = torch.empty((B, T, H), **f32)
+    dh0 = torch.empty((B, H, D, D), **f32)
+    nbytes = int(_load().gdr_backward_workspace_bytes(gk, B, T, H, D, D))
+    workspace = _workspace(workspace, nbytes, dev)
+    _check(_load().gdr_backward_chunked(
+        _BF16, gk, B, T, H, D, D, 64, float(scale), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+        _ptr(beta), _ptr(h0), _ptr(do), _ptr(dht), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg),
+        _ptr(dbeta), _ptr(dh0), _ptr(workspace), nbytes, _stream(dev)))
+    return dq, dk, dv, dg, dbeta, dh0

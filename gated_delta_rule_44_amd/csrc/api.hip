@@ -567,6 +567,109 @@ gdr_status gdr_decode_tokens_fused(enum gdr_dtype dt, enum gdr_gate gk, int B, i
 }
 
 
+}  // extern "C"
+
+namespace {
+
+// Backward workspace: the chunk-entering states and the chunk state
+// gradients ([B, H, nc, Dv, Dk] fp32 each), the forward's outputs (bf16,
+// unused) and the forward's own workspace.
+struct BwdWs {
+    size_t states, dstates, o, fwd, total;
+};
+BwdWs bwd_layout(int gk, int B, int T, int H, int Dk, int Dv) {
+    BwdWs w{};
+    if (B <= 0 || T <= 0 || H <= 0 || Dk <= 0 || Dv <= 0) return w;
+    auto r256 = [](size_t x) { return (x + 255) / 256 * 256; };
+    const size_t nc = ((size_t)T + 63) / 64;
+    const size_t st = (size_t)B * H * nc * Dv * Dk * sizeof(float);
+    w.states = 0;
+    w.dstates = st;
+    w.o = 2 * st;
+    w.fwd = w.o + r256((size_t)B * T * H * Dv * 2);
+    w.total = w.fwd + ws_layout(gk == GDR_GATE_SCALAR, B, (long long)B * T, H).total;
+    return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t gdr_backward_workspace_bytes(enum gdr_gate gk, int B, int T, int H, int Dk, int Dv) {
+    return bwd_layout(gk, B, T, H, Dk, Dv).total;
+}
+
+gdr_status gdr_backward_chunked(enum gdr_dtype dt, enum gdr_gate gk, int B, int T, int H,
+                                int Dk, int Dv, int chunk, float scale, const void *q,
+                                const void *k, const void *v, const float *g,
+                                const float *beta, const float *h0, const void *d_o,
+                                const float *dht, float *dq, float *dk, float *dv, float *dg,
+                                float *dbeta, float *dh0, void *workspace, size_t ws_bytes,
+                                void *stream) {
+    const char *what = "gdr_backward_chunked";
+    gdr_status st = check_common(dt, gk, Dk, Dv, what);
+    if (st != GDR_OK) return st;
+    if (dt != GDR_BF16)
+        return fail(GDR_EUNSUPPORTED, "%s: only bf16 inputs have a backward", what);
+    if (chunk != 64) return fail(GDR_EUNSUPPORTED, "%s: chunk = %d; only 64 is supported", what, chunk);
+    if (B < 0 || T < 0 || H <= 0)
+        return fail(GDR_EINVAL, "%s: bad sizes B=%d T=%d H=%d", what, B, T, H);
+    if ((long long)B * T * H * Dk >= (1LL << 40))
+        return fail(GDR_EUNSUPPORTED, "%s: problem too large", what);
+    if ((long long)B * H * 8 >= (1LL << 31) || (long long)B * ((T + 63) / 64) * H >= (1LL << 31))
+        return fail(GDR_EUNSUPPORTED, "%s: grid too large", what);
+    if ((long long)B * T > 0) {
+        REQUIRE_PTR(q, "q");
+        REQUIRE_PTR(k, "k");
+        REQUIRE_PTR(v, "v");
+        REQUIRE_PTR(g, "g");
+        if (!beta) return fail(GDR_EINVAL, "%s: beta is NULL", what);
+        REQUIRE_PTR(d_o, "do");
+        REQUIRE_PTR(dq, "dq");
+        REQUIRE_PTR(dk, "dk");
+        REQUIRE_PTR(dv, "dv");
+        if (!dg) return fail(GDR_EINVAL, "%s: dg is NULL", what);
+        if (!dbeta) return fail(GDR_EINVAL, "%s: dbeta is NULL", what);
+    }
+    REQUIRE_ALIGNED_OR_NULL(h0, "h0");
+    REQUIRE_ALIGNED_OR_NULL(dht, "dht");
+    REQUIRE_ALIGNED_OR_NULL(dh0, "dh0");
+    const BwdWs W = bwd_layout(gk, B, T, H, Dk, Dv);
+    const size_t need = W.total;
+    st = check_workspace(what, workspace, ws_bytes, need);
+    if (st != GDR_OK) return st;
+    if (B == 0) return GDR_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (T == 0) {
+        // no tokens: dS_0 = dS_T
+        if (!dh0) return GDR_OK;
+        return finish(gdr::launch_copy_or_zero(dh0, dht, (size_t)B * H * Dv * Dk, s), s, what);
+    }
+    char *ws = static_cast<char *>(workspace);
+    // 1. the forward, keeping the state that enters every chunk
+    const bool tiles = gk == GDR_GATE_SCALAR;
+    const WsLayout FL = ws_layout(tiles, B, (long long)B * T, H);
+    gdr::PrefillArgs f{};
+    f.q = q; f.k = k; f.v = v; f.g = g; f.beta = beta; f.h0 = h0;
+    f.o = ws + W.o; f.ht = nullptr;
+    f.cu_seqlens = nullptr; f.order = nullptr; f.chunk_base = nullptr;
+    f.tiles = tiles ? ws + W.fwd + FL.tiles : nullptr;
+    f.max_chunks = tiles ? (long long)B * ((T + 63) / 64) : 0;
+    f.N = B; f.T = T; f.H = H; f.scale = scale; f.channel_gate = gk == GDR_GATE_CHANNEL;
+    f.states = reinterpret_cast<float *>(ws + W.states);
+    hipError_t e = gdr::launch_prefill_chunked(Dk, f, s);
+    if (e != hipSuccess) return finish(e, s, what);
+    // 2, 3. the adjoint pass and the chunk gradients
+    gdr::BwdArgs a{};
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.h0 = h0; a.dout = d_o; a.dht = dht;
+    a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbeta = dbeta; a.dh0 = dh0;
+    a.states = reinterpret_cast<float *>(ws + W.states);
+    a.dstates = reinterpret_cast<float *>(ws + W.dstates);
+    a.B = B; a.T = T; a.H = H; a.nc = (T + 63) / 64; a.scale = scale;
+    a.channel_gate = gk == GDR_GATE_CHANNEL;
+    return finish(gdr::launch_backward(Dk, a, s), s, what);
+}
+
 gdr_status gdr_decode_commit(int B, int n_tok, int H, int Dk, int Dv, const int32_t *slot,
                              int pool_slots, const int32_t *accepted, const float *checkpoints,
                              float *state_pool, void *stream) {

@@ -1,0 +1,809 @@
+// backward.hip -- gradients of the chunked gated delta rule on gfx950.
+//
+// Forward, per sequence and head ("Super Apriel: One Checkpoint, Many
+// Speeds", gist.science summary 2a, for the two gate kinds):
+//     S_t = S_{t-1} Diag(a_t)(I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+//     o_t = scale * S_t q_t,   a_t = e^{g_t}.
+// For upstream gradients dO (of o) and dS_T (of the final state) the
+// backward returns dq, dk, dv, dg, dbeta and dS_0 in three launches:
+//
+// 1. the chunked forward (chunked.hip / chunked_chain.hip) with its
+//    optional output of the state entering every chunk of 64 tokens.
+// 2. dstate_pass_kernel: the adjoint recurrence in reverse,
+//        G_{t-1} = (G_t + scale do_t q_t^T)(I - beta_t k_t k_t^T) Diag(a_t),
+//    G_{T-1} = dS_T, where G_t is the gradient of the state after token t
+//    through everything but o_t.  Row-local like the forward.  It stores
+//    G at the last token of every chunk (the chunk's dS_C) and writes
+//    dS_0 = G_{-1}.
+// 3. chunk_grad_kernel: per (chunk, head), from the entering state S0 and
+//    dS_C, every input gradient of the chunk by differentiating the chunked
+//    form (see chunked.hip) -- with b the in-chunk cumulative log gate,
+//    E = e^b, Qt = q.E, Kt = k.E, Kb = k/E, Kh = Kb e^{b_C}:
+//        A = strict_lower(Kt Kb^T), P = lower(Qt Kb^T),
+//        N = (I + diag(beta) A)^{-1}, T = N diag(beta),
+//        X = V - Kt S0^T, U = T X,
+//        O = scale (Qt S0^T + P U),  S_C = S0 Diag(e^{b_C}) + U^T Kh.
+//    With dSg = dS_C Diag(e^{b_C}):
+//        dU  = Kb dSg^T + scale P^T dO          dKh.Kh / Kb = U dSg
+//        dP  = scale lower(dO U^T)              dQt = scale dO S0 + dP Kb
+//        dT  = lower(dU X^T)                    dX  = T^T dU = dV
+//        dN  = dT diag(beta)                    dbeta_s += sum_r dT_rs N_rs
+//        dM  = -N^T dN N^T                      dA  = strict_lower(diag(beta) dM)
+//        dbeta_r += sum_s dM_rs A_rs
+//        dKt = -dX S0 + dA Kb                   dKb = dP^T Qt + dA^T Kt + U dSg
+//        dq = dQt.E,  dk = dKt.E + dKb/E,  db_r = dQt.Qt + dKt.Kt - dKb.Kb
+//        db_C = sum_r (U dSg).Kb + sum_i dSg_i.S0_i
+//        dg_s = sum_{r >= s} db_r + db_C     (summed over channels for GDN)
+//    The Kh part h_r = (U dSg).Kb enters db_r with a minus sign and db_C
+//    with a plus sign; summed, it adds sum_{r < s} h_r to dg_s, which is how
+//    it is computed (the two large terms would otherwise cancel in bf16).
+//    The products run on 16x16x32 bf16 MFMAs with fp32 accumulation (the
+//    fp32 states S0 and dS_C as hi + lo bf16 pairs); the triangular inverse
+//    by substitution in fp32.  The diagonals of T and dP, rounded once to
+//    bf16 as operands, get their rounding error added back in fp32 (in a
+//    short chunk they carry most of the weight, and one rounding of them is
+//    a correlated error in everything downstream).
+#include "gdr_internal.h"
+#include "device_util.h"
+
+namespace gdr {
+namespace {
+
+constexpr int C = 64;
+
+// ===========================================================================
+// The adjoint pass: 256 threads hold 16 (D = 128) or 32 (D = 64) rows of one
+// head's state gradient; lane group of LPR lanes per row, float4 per lane.
+// ===========================================================================
+template <int D> struct RowG {
+    static constexpr int LPR = D / 4;          // lanes per row
+    static constexpr int RPW = 64 / LPR;       // rows per wave per pass
+    static constexpr int RPP = 4 * RPW;        // rows per pass
+    static constexpr int ROWS = 2 * RPP;       // rows per workgroup (two passes)
+    static constexpr int NRB = D / ROWS;       // workgroups per head
+};
+
+__device__ inline float dot4b(f32x4 a, f32x4 b) {
+    return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
+}
+
+// x of lane l ^ (LPR / 2): the other half of a row of LPR lanes.  LPR = 32:
+// the neighbouring 16-lane row, from the gfx950 v_permlane16_swap (odd rows
+// of one register swapped with even rows of the other, so with both holding
+// x, the first holds the even row's values and the second the odd row's);
+// LPR = 16: DPP row_ror:8.
+template <int LPR>
+__device__ inline float half_partner(float x, int lane) {
+    if (LPR == 16) return dpp_f<0x128>(x);
+    float a = x, b = x;
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+    return (lane & 16) ? a : b;
+}
+// The two row dot products (pass 0 and 1) of this lane's rows, summed over
+// the LPR lanes of each row: one halving exchange, then a sum over the half
+// (DPP), then the halves swapped back; returns (d0, d1) in every lane.  All
+// on the VALU: the chain of LDS round trips of __shfl_xor set the time of
+// every step of the pass.
+template <int LPR>
+__device__ inline void row_dots(float y0, float y1, int lane, float &d0, float &d1) {
+    const bool upper = (lane & (LPR / 2)) != 0;
+    float val = (upper ? y1 : y0) + half_partner<LPR>(upper ? y0 : y1, lane);
+    val = sum_group<LPR / 2>(val);
+    const float other = half_partner<LPR>(val, lane);
+    d0 = upper ? other : val;
+    d1 = upper ? val : other;
+}
+
+// Inputs of one token for the rows of this lane, loaded PF tokens ahead of
+// their use: the passes are chains of dependent steps, so a load issued for
+// the current token would put its latency on every step.
+constexpr int PF = 8;
+template <int D>
+struct TokRow {
+    f32x4 k, q, lg;
+    float beta, x0, x1;     // x: v (forward) or do (adjoint) at the two rows
+};
+
+template <typename T, int D, bool ADJ>
+__device__ __forceinline__ void load_row_tok(const BwdArgs &a, size_t r, int c0, const int (&row)[2],
+                                             TokRow<D> &x) {
+    x.k = Elem<T>::load4(static_cast<const T *>(a.k) + r * D + c0);
+    if (ADJ) x.q = Elem<T>::load4(static_cast<const T *>(a.q) + r * D + c0);
+    if (a.channel_gate) {
+        x.lg = *reinterpret_cast<const f32x4 *>(a.g + r * D + c0);
+    } else {
+        const float s = a.g[r];
+        x.lg = f32x4{s, s, s, s};
+    }
+    x.beta = a.beta[r];
+    const T *xp = static_cast<const T *>(ADJ ? a.dout : a.v) + r * D;
+    x.x0 = Elem<T>::load(xp + row[0]);
+    x.x1 = Elem<T>::load(xp + row[1]);
+}
+
+__device__ inline f32x4 gate_factors(f32x4 lg) {
+    return f32x4{__builtin_amdgcn_exp2f(lg.x * kLog2e), __builtin_amdgcn_exp2f(lg.y * kLog2e),
+                 __builtin_amdgcn_exp2f(lg.z * kLog2e), __builtin_amdgcn_exp2f(lg.w * kLog2e)};
+}
+
+// The adjoint recurrence in reverse, storing each chunk's dS_C, then dS_0.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void dstate_pass_kernel(BwdArgs a) {
+    using G = RowG<D>;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int rb = blockIdx.x % G::NRB;
+    const int bh = blockIdx.x / G::NRB;
+    const int b = bh / a.H, h = bh - b * a.H;
+    const int c0 = (lane % G::LPR) * 4, sub = lane / G::LPR;
+    int row[2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) row[p] = rb * G::ROWS + p * G::RPP + w * G::RPW + sub;
+    f32x4 Z[2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+        Z[p] = a.dht ? *reinterpret_cast<const f32x4 *>(a.dht + (size_t)bh * D * D + (size_t)row[p] * D + c0)
+                     : f32x4{0.f, 0.f, 0.f, 0.f};
+    float *dst = a.dstates + (size_t)bh * a.nc * D * D;
+    const size_t r0 = (size_t)b * a.T * a.H + h;
+    TokRow<D> buf[PF];
+#pragma unroll
+    for (int i = 0; i < PF; ++i)
+        if (a.T - 1 - i >= 0) load_row_tok<T, D, true>(a, r0 + (size_t)(a.T - 1 - i) * a.H, c0, row, buf[i]);
+    for (int tb = 0; tb < a.T; tb += PF) {
+#pragma unroll
+        for (int i = 0; i < PF; ++i) {
+            const int t = a.T - 1 - (tb + i);
+            if (t < 0) break;
+            if (t == a.T - 1 || t % C == C - 1) {
+#pragma unroll
+                for (int p = 0; p < 2; ++p)
+                    *reinterpret_cast<f32x4 *>(dst + (size_t)(t / C) * D * D + (size_t)row[p] * D + c0) = Z[p];
+            }
+            const TokRow<D> x = buf[i];
+            if (t - PF >= 0) load_row_tok<T, D, true>(a, r0 + (size_t)(t - PF) * a.H, c0, row, buf[i]);
+            const f32x4 av = gate_factors(x.lg);
+            const f32x4 z0 = Z[0] + (a.scale * x.x0) * x.q;
+            const f32x4 z1 = Z[1] + (a.scale * x.x1) * x.q;
+            float y0, y1;
+            row_dots<G::LPR>(dot4b(z0, x.k), dot4b(z1, x.k), lane, y0, y1);
+            Z[0] = (z0 - (x.beta * y0) * x.k) * av;
+            Z[1] = (z1 - (x.beta * y1) * x.k) * av;
+        }
+    }
+    if (a.dh0) {
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+            *reinterpret_cast<f32x4 *>(a.dh0 + (size_t)bh * D * D + (size_t)row[p] * D + c0) = Z[p];
+    }
+}
+
+// ===========================================================================
+// chunk_grad_kernel
+// ===========================================================================
+constexpr int PC = C + 8;     // row length of the C x C bf16 matrices in LDS
+
+template <int D> struct GradSmem {
+    static constexpr int PD = D + 8;
+    alignas(16) bf16 Qt[C * PD];      // q e^b            [r][j]
+    alignas(16) bf16 Kt[C * PD];      // k e^b
+    alignas(16) bf16 Kb[C * PD];      // k e^-b
+    alignas(16) bf16 X[C * PD];       // X, later dX      [r][i]
+    alignas(16) bf16 U[C * PD];
+    alignas(16) bf16 dU[C * PD];
+    alignas(16) float Nf[C * C];      // L, then N = (I + L)^{-1}  [r][s]
+    alignas(16) bf16 Tb[C * PC];      // T, later Y = dN N^T
+    alignas(16) bf16 Pb[C * PC];      // P, later dN
+    alignas(16) bf16 dPb[C * PC];     // dP, later dA
+    alignas(16) bf16 Nb[C * PC];      // N
+    alignas(16) float beta[C];
+    alignas(16) float eC[D];          // e^{b_C} per channel (scalar gate: all equal)
+    alignas(16) float dbC[D];         // gradient of b_C per channel
+    alignas(16) float dbeta[C];
+    alignas(16) float dbrow[C];       // scalar gate: db per row
+    alignas(16) float hrow[C];        // scalar gate: Kh part of db per row
+    alignas(16) float tcor[C];        // T_rr - bf16(T_rr): the diagonal of T is beta
+    alignas(16) float pcor[C];        // dP_rr - bf16(dP_rr)
+    alignas(16) float bs[C];          // scalar gate: b per row
+};
+
+// MFMA fragments from global memory: fp32 row-major [rows][ld] (rows of the
+// fragment along the matrix rows) and its column form, bf16 likewise; rows
+// at or past `valid` read as zeros.  The fp32 ones (the states and their
+// gradients) come as a pair hi + lo of bf16 values, hi = bf16(x) and
+// lo = bf16(x - hi), so that two MFMAs carry about 16 bits of x: the
+// gate gradient sums terms that cancel to a fraction of their size.
+struct Frag2 {
+    bf16x8 hi, lo;
+};
+__device__ inline Frag2 split8(const float (&v)[8]) {
+    Frag2 f;
+    f.hi = cvt8(v);
+    float r[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) r[u] = v[u] - (float)f.hi[u];
+    f.lo = cvt8(r);
+    return f;
+}
+__device__ inline Frag2 g_rows_f32(const float *base, size_t ld, int r0, int k0, int lane,
+                                   const float *cs) {
+    const float *p = base + (size_t)(r0 + (lane & 15)) * ld + k0 + 8 * (lane >> 4);
+    const f32x4 x0 = *reinterpret_cast<const f32x4 *>(p);
+    const f32x4 x1 = *reinterpret_cast<const f32x4 *>(p + 4);
+    float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    if (cs) {
+        const float *c = cs + k0 + 8 * (lane >> 4);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] *= c[u];
+    }
+    return split8(v);
+}
+__device__ inline Frag2 g_cols_f32(const float *base, size_t ld, int k0, int n0, int lane,
+                                   float cscale) {
+    const float *p = base + (size_t)(k0 + 8 * (lane >> 4)) * ld + n0 + (lane & 15);
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = p[(size_t)u * ld] * cscale;
+    return split8(v);
+}
+// A x (hi + lo), A as the first operand; (hi + lo) x B
+__device__ inline f32x4 mfma_ab2(bf16x8 a, const Frag2 &b, f32x4 c) {
+    return mfma32(a, b.lo, mfma32(a, b.hi, c));
+}
+__device__ inline bf16x8 g_rows_bf(const bf16 *base, size_t ld, int r0, int k0, int lane, int valid) {
+    const int r = r0 + (lane & 15);
+    if (r >= valid) return bf16x8{};
+    return *reinterpret_cast<const bf16x8 *>(base + (size_t)r * ld + k0 + 8 * (lane >> 4));
+}
+__device__ inline bf16x8 g_cols_bf(const bf16 *base, size_t ld, int k0, int n0, int lane, int valid) {
+    const int kb = k0 + 8 * (lane >> 4);
+    const bf16 *p = base + n0 + (lane & 15);
+    bf16x8 v;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = kb + u < valid ? p[(size_t)(kb + u) * ld] : (bf16)0.f;
+    return v;
+}
+
+// sum of x over the four lanes (l & 15) + 16 m, m = 0..3
+__device__ inline float sum_quads(float x) { return swap_sum32(swap_sum16(x)); }
+
+template <int D, bool CH>
+__global__ __launch_bounds__(256) void chunk_grad_kernel(BwdArgs a) {
+    using Sm = GradSmem<D>;
+    constexpr int PD = Sm::PD;
+    constexpr int KD = D / 32;         // 32-wide k steps over D
+    constexpr int NB = D / 16;         // 16-wide column blocks of a C x D matrix
+    __shared__ Sm sm;
+
+    const int h = blockIdx.x % a.H;
+    const int ci = blockIdx.x / a.H;          // chunk over the batch: b nc + c
+    const int b = ci / a.nc, c = ci - b * a.nc;
+    const int t0 = c * C;
+    const int Cc = a.T - t0 < C ? a.T - t0 : C;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l15 = lane & 15, q4 = lane >> 4;
+    const size_t rowD = (size_t)a.H * D;                      // token stride of q, k, v, o
+    const size_t tok0 = (size_t)b * a.T + t0;                 // first token row (b T + t0)
+    const bf16 *qg = static_cast<const bf16 *>(a.q) + (tok0 * a.H + h) * D;
+    const bf16 *kg = static_cast<const bf16 *>(a.k) + (tok0 * a.H + h) * D;
+    const bf16 *vg = static_cast<const bf16 *>(a.v) + (tok0 * a.H + h) * D;
+    const bf16 *dog = static_cast<const bf16 *>(a.dout) + (tok0 * a.H + h) * D;
+    const size_t gstr = CH ? rowD : (size_t)a.H;              // token stride of g
+    const float *gg = a.g + (CH ? (tok0 * a.H + h) * D : tok0 * a.H + h);
+    const float *bg = a.beta + tok0 * a.H + h;
+    const size_t sbh = ((size_t)b * a.H + h) * a.nc + c;
+    const float *S0 = a.states + sbh * D * D;                  // [i][j]
+    const float *dSC = a.dstates + sbh * D * D;                // [i][j]
+
+    // ---- 1. gate sums, gated operands, beta; zero the accumulators
+    if (tid < C) {
+        sm.beta[tid] = tid < Cc ? bg[(size_t)tid * a.H] : 0.f;
+        sm.dbeta[tid] = 0.f;
+        sm.dbrow[tid] = 0.f;
+        sm.hrow[tid] = 0.f;
+    }
+    if (!CH && w == 0) {
+        const float gv = lane < Cc ? gg[(size_t)lane * gstr] : 0.f;
+        sm.bs[lane] = wave_prefix_sum(gv);
+    }
+    if (tid < D) sm.dbC[tid] = 0.f;
+    __syncthreads();
+    if (tid < D) {
+        // one channel per thread, 16 rows of loads in flight at a time
+        const int j = tid;
+        float run = 0.f;
+        for (int r0 = 0; r0 < C; r0 += 16) {
+            float gv[16], qv[16], kv[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const int r = r0 + u;
+                gv[u] = CH && r < Cc ? gg[(size_t)r * gstr + j] : 0.f;
+                qv[u] = r < Cc ? (float)qg[(size_t)r * rowD + j] : 0.f;
+                kv[u] = r < Cc ? (float)kg[(size_t)r * rowD + j] : 0.f;
+            }
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const int r = r0 + u;
+                run += gv[u];
+                const float e = ex(CH ? run : sm.bs[r]);
+                const float ei = __builtin_amdgcn_rcpf(e);
+                sm.Qt[r * PD + j] = (bf16)(qv[u] * e);
+                sm.Kt[r * PD + j] = (bf16)(kv[u] * e);
+                sm.Kb[r * PD + j] = (bf16)(kv[u] * ei);
+                if (r == C - 1) sm.eC[j] = e;
+            }
+        }
+    }
+    __syncthreads();
+
+    const int I = w;                           // this wave's 16-row block
+    auto zero4 = []() { return f32x4{0.f, 0.f, 0.f, 0.f}; };
+    // r, s of accumulator element e of block (I, J)
+    auto rowof = [&](int e) { return 16 * I + 4 * q4 + e; };
+
+    // ---- 2. A = strict_lower(Kt Kb^T), P = lower(Qt Kb^T); L = diag(beta) A
+    f32x4 Areg[4];
+#pragma unroll
+    for (int J = 0; J < 4; ++J) {
+        f32x4 av = zero4(), pv = zero4();
+        if (J <= I) {
+#pragma unroll
+            for (int kk = 0; kk < KD; ++kk) {
+                const bf16x8 kb = frag_rows(sm.Kb, PD, 16 * J, 32 * kk, lane);
+                av = mfma32(frag_rows(sm.Kt, PD, 16 * I, 32 * kk, lane), kb, av);
+                pv = mfma32(frag_rows(sm.Qt, PD, 16 * I, 32 * kk, lane), kb, pv);
+            }
+        }
+        const int s = 16 * J + l15;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = rowof(e);
+            if (!(s < r)) av[e] = 0.f;
+            if (!(s <= r)) pv[e] = 0.f;
+            sm.Nf[r * C + s] = sm.beta[r] * av[e];
+            sm.Pb[r * PC + s] = (bf16)pv[e];
+        }
+        Areg[J] = av;
+    }
+    __syncthreads();
+
+    // ---- 3. N = (I + L)^{-1}, in fp32.  The 16x16 blocks of L below the
+    //         diagonal are saved (over U, free until step 5); the four
+    //         diagonal blocks are inverted by substitution, lane 16 b + c of
+    //         wave 0 taking column c of block b; then the blocks below the
+    //         diagonal, N_ij = -N_ii sum_{k=j}^{i-1} L_ik N_kj, one block
+    //         diagonal i - j = d at a time, by 16x16 products on all threads
+    {
+        float *Ls = reinterpret_cast<float *>(sm.U);   // [ltri(i, k)][16][16]
+        float *Tm = Ls + 6 * 256;                      // [3][16][16]
+        static_assert(sizeof(sm.U) >= sizeof(float) * 9 * 256, "inverse scratch");
+        const int tr = tid >> 4, tc = tid & 15;
+#pragma unroll
+        for (int i = 1; i < 4; ++i)
+#pragma unroll
+            for (int k = 0; k < i; ++k)
+                Ls[(i * (i - 1) / 2 + k) * 256 + tid] = sm.Nf[(16 * i + tr) * C + 16 * k + tc];
+        if (w == 0) {
+            const int base = 16 * (lane >> 4), c = lane & 15;
+            float n[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float acc = r == c ? 1.f : 0.f;
+#pragma unroll
+                for (int m = 0; m < r; ++m) acc -= sm.Nf[(base + r) * C + base + m] * n[m];
+                n[r] = acc;
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sm.Nf[(base + r) * C + base + c] = n[r];
+        }
+        __syncthreads();
+        for (int d = 1; d < 4; ++d) {
+            for (int jb = 0; jb + d < 4; ++jb) {
+                const int ib = jb + d;
+                float acc = 0.f;
+                for (int kb = jb; kb < ib; ++kb) {
+                    const float *L = Ls + (ib * (ib - 1) / 2 + kb) * 256;
+#pragma unroll
+                    for (int m = 0; m < 16; ++m)
+                        acc += L[tr * 16 + m] * sm.Nf[(16 * kb + m) * C + 16 * jb + tc];
+                }
+                Tm[jb * 256 + tid] = acc;
+            }
+            __syncthreads();
+            for (int jb = 0; jb + d < 4; ++jb) {
+                const int ib = jb + d;
+                float acc = 0.f;
+#pragma unroll
+                for (int m = 0; m < 16; ++m)
+                    acc += sm.Nf[(16 * ib + tr) * C + 16 * ib + m] * Tm[jb * 256 + m * 16 + tc];
+                sm.Nf[(16 * ib + tr) * C + 16 * jb + tc] = -acc;
+            }
+            __syncthreads();
+        }
+    }
+    for (int e = tid; e < C * C; e += 256) {
+        const int r = e / C, s = e % C;
+        const float nv = sm.Nf[e];
+        const float tv = nv * sm.beta[s];
+        const bf16 tb = (bf16)tv;
+        sm.Nb[r * PC + s] = (bf16)nv;
+        sm.Tb[r * PC + s] = tb;
+        if (r == s) sm.tcor[r] = tv - (float)tb;
+    }
+    __syncthreads();
+
+    // ---- 4. X = V - Kt S0^T  (S0 [i][j] as the B operand of X Y^T)
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb) {
+        f32x4 x = zero4();
+#pragma unroll
+        for (int kk = 0; kk < KD; ++kk)
+            x = mfma_ab2(frag_rows(sm.Kt, PD, 16 * I, 32 * kk, lane),
+                         g_rows_f32(S0, D, 16 * cb, 32 * kk, lane, nullptr), x);
+        const int i = 16 * cb + l15;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = rowof(e);
+            const float vv = r < Cc ? (float)vg[(size_t)r * rowD + i] : 0.f;
+            sm.X[r * PD + i] = (bf16)(vv - x[e]);
+        }
+    }
+    __syncthreads();
+
+    // ---- 5. U = T X
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb) {
+        f32x4 u = zero4();
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+            u = mfma32(frag_rows(sm.Tb, PC, 16 * I, 32 * kk, lane), frag_cols(sm.X, PD, 32 * kk, 16 * cb, lane), u);
+        const int i = 16 * cb + l15;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = rowof(e);
+            sm.U[r * PD + i] = (bf16)(u[e] + sm.tcor[r] * (float)sm.X[r * PD + i]);
+        }
+    }
+    __syncthreads();
+
+    // ---- 6. dU = Kb dSg^T + scale P^T dO
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb) {
+        f32x4 d1 = zero4(), d2 = zero4();
+#pragma unroll
+        for (int kk = 0; kk < KD; ++kk)
+            d1 = mfma_ab2(frag_rows(sm.Kb, PD, 16 * I, 32 * kk, lane),
+                          g_rows_f32(dSC, D, 16 * cb, 32 * kk, lane, sm.eC), d1);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+            d2 = mfma32(frag_cols(sm.Pb, PC, 32 * kk, 16 * I, lane),
+                        g_cols_bf(dog, rowD, 32 * kk, 16 * cb, lane, Cc), d2);
+        const int i = 16 * cb + l15;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sm.dU[rowof(e) * PD + i] = (bf16)(d1[e] + a.scale * d2[e]);
+    }
+
+    // ---- 7. dKbh = U dSg (the Kh part of dKb, kept apart for dg)
+    f32x4 dQt[NB], dKt[NB], dKb[NB], dKbh[NB];
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb) {
+        f32x4 x = zero4();
+#pragma unroll
+        for (int kk = 0; kk < KD; ++kk)
+            x = mfma_ab2(frag_rows(sm.U, PD, 16 * I, 32 * kk, lane),
+                         g_cols_f32(dSC, D, 32 * kk, 16 * cb, lane, sm.eC[16 * cb + l15]), x);
+        dKbh[cb] = x;
+        dKb[cb] = zero4();
+    }
+    __syncthreads();
+
+    // ---- 8. dP = scale lower(dO U^T)
+#pragma unroll
+    for (int J = 0; J < 4; ++J) {
+        f32x4 p = zero4();
+        if (J <= I) {
+#pragma unroll
+            for (int kk = 0; kk < KD; ++kk)
+                p = mfma32(g_rows_bf(dog, rowD, 16 * I, 32 * kk, lane, Cc),
+                           frag_rows(sm.U, PD, 16 * J, 32 * kk, lane), p);
+        }
+        const int s = 16 * J + l15;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = rowof(e);
+            const float pv = s <= r ? a.scale * p[e] : 0.f;
+            const bf16 pb = (bf16)pv;
+            sm.dPb[r * PC + s] = pb;
+            if (s == r) sm.pcor[r] = pv - (float)pb;
+        }
+    }
+    __syncthreads();
+
+    // ---- 9, 10. dQt = scale dO S0 + dP Kb;  dKb += dP^T Qt
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb) {
+        f32x4 x = zero4(), y = zero4();
+#pragma unroll
+        for (int kk = 0; kk < KD; ++kk)
+            x = mfma_ab2(g_rows_bf(dog, rowD, 16 * I, 32 * kk, lane, Cc),
+                         g_cols_f32(S0, D, 32 * kk, 16 * cb, lane, 1.f), x);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            y = mfma32(frag_rows(sm.dPb, PC, 16 * I, 32 * kk, lane), frag_cols(sm.Kb, PD, 32 * kk, 16 * cb, lane), y);
+            dKb[cb] = mfma32(frag_cols(sm.dPb, PC, 32 * kk, 16 * I, lane),
+                             frag_cols(sm.Qt, PD, 32 * kk, 16 * cb, lane), dKb[cb]);
+        }
+        dQt[cb] = a.scale * x + y;
+        const int j = 16 * cb + l15;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = rowof(e);
+            dQt[cb][e] += sm.pcor[r] * (float)sm.Kb[r * PD + j];
+            dKb[cb][e] += sm.pcor[r] * (float)sm.Qt[r * PD + j];
+        }
+    }
+
+    // ---- 11. dT = lower(dU X^T); dbeta_s += sum_r dT_rs N_rs; dN = dT diag(beta)
+#pragma unroll
+    for (int J = 0; J < 4; ++J) {
+        f32x4 t = zero4();
+        if (J <= I) {
+#pragma unroll
+            for (int kk = 0; kk < KD; ++kk)
+                t = mfma32(frag_rows(sm.dU, PD, 16 * I, 32 * kk, lane), frag_rows(sm.X, PD, 16 * J, 32 * kk, lane), t);
+        }
+        const int s = 16 * J + l15;
+        const float bs_ = sm.beta[s];
+        float part = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = rowof(e);
+            const float tv = s <= r ? t[e] : 0.f;
+            part += tv * sm.Nf[r * C + s];
+            sm.Pb[r * PC + s] = (bf16)(tv * bs_);
+        }
+        part = sum_quads(part);
+        if (q4 == 0 && J <= I) atomicAdd(&sm.dbeta[s], part);
+    }
+    __syncthreads();
+
+    // ---- 12. dX = T^T dU (= dV), kept in X;  13. dKt = -dX S0
+    f32x4 dX[NB];
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb) {
+        f32x4 x = zero4();
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+            x = mfma32(frag_cols(sm.Tb, PC, 32 * kk, 16 * I, lane), frag_cols(sm.dU, PD, 32 * kk, 16 * cb, lane), x);
+        const int i = 16 * cb + l15;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] += sm.tcor[rowof(e)] * (float)sm.dU[rowof(e) * PD + i];
+        dX[cb] = x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = rowof(e);
+            if (r < Cc) a.dv[((tok0 + r) * a.H + h) * D + i] = x[e];
+        }
+    }
+    __syncthreads();                           // X and T no longer read
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb) {
+        const int i = 16 * cb + l15;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sm.X[rowof(e) * PD + i] = (bf16)dX[cb][e];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb) {
+        f32x4 x = zero4();
+#pragma unroll
+        for (int kk = 0; kk < KD; ++kk)
+            x = mfma_ab2(frag_rows(sm.X, PD, 16 * I, 32 * kk, lane),
+                         g_cols_f32(S0, D, 32 * kk, 16 * cb, lane, 1.f), x);
+        dKt[cb] = -x;
+    }
+
+    // ---- 14. Y = dN N^T (into Tb), dM = -N^T Y;  dbeta_r += sum_s dM_rs A_rs;
+    //          dA = strict_lower(diag(beta) dM) (into dPb)
+#pragma unroll
+    for (int J = 0; J < 4; ++J) {
+        f32x4 y = zero4();
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+            y = mfma32(frag_rows(sm.Pb, PC, 16 * I, 32 * kk, lane), frag_rows(sm.Nb, PC, 16 * J, 32 * kk, lane), y);
+        const int s = 16 * J + l15;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sm.Tb[rowof(e) * PC + s] = (bf16)y[e];
+    }
+    __syncthreads();
+    float dbr[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int J = 0; J < 4; ++J) {
+        f32x4 m = zero4();
+        if (J <= I) {
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+                m = mfma32(frag_cols(sm.Nb, PC, 32 * kk, 16 * I, lane), frag_cols(sm.Tb, PC, 32 * kk, 16 * J, lane), m);
+        }
+        const int s = 16 * J + l15;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = rowof(e);
+            const float dm = s < r ? -m[e] : 0.f;
+            dbr[e] += dm * Areg[J][e];
+            sm.dPb[r * PC + s] = (bf16)(sm.beta[r] * dm);
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const float v = sum_group<16>(dbr[e]);
+        if (l15 == 0) atomicAdd(&sm.dbeta[rowof(e)], v);
+    }
+    __syncthreads();
+
+    // ---- 15. dKt += dA Kb;  dKb += dA^T Kt
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb) {
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            dKt[cb] = mfma32(frag_rows(sm.dPb, PC, 16 * I, 32 * kk, lane), frag_cols(sm.Kb, PD, 32 * kk, 16 * cb, lane), dKt[cb]);
+            dKb[cb] = mfma32(frag_cols(sm.dPb, PC, 32 * kk, 16 * I, lane), frag_cols(sm.Kt, PD, 32 * kk, 16 * cb, lane), dKb[cb]);
+        }
+    }
+    __syncthreads();                           // gated operands no longer read
+
+    // ---- 16. db and h from the bf16 gated operands the products used (so
+    //          that the pairs of terms that cancel exactly in dg -- a P or A
+    //          entry seen from its row and from its column -- cancel to fp32
+    //          accuracy); then E; dq, dk; dg by reverse sums; dbeta
+    float *dbf = reinterpret_cast<float *>(sm.U);    // db [r][j] (channel gate), over U, dU
+    float *hf = reinterpret_cast<float *>(sm.Tb);    // h [r][j] (channel gate), over Tb..Nb
+    float *Ef = reinterpret_cast<float *>(sm.Qt);    // e^b [r][j] (channel gate), over Qt, Kt
+    static_assert(sizeof(sm.U) + sizeof(sm.dU) >= sizeof(float) * C * D, "db overlay");
+    static_assert(sizeof(sm.Tb) + sizeof(sm.Pb) + sizeof(sm.dPb) + sizeof(sm.Nb) >= sizeof(float) * C * D,
+                  "h overlay");
+    static_assert(sizeof(sm.Qt) + sizeof(sm.Kt) >= sizeof(float) * C * D, "E overlay");
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb) {
+        const int j = 16 * cb + l15;
+        float rowsum[4], hsum[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = rowof(e);
+            const float qt = (float)sm.Qt[r * PD + j];
+            const float kt = (float)sm.Kt[r * PD + j];
+            const float kb = (float)sm.Kb[r * PD + j];
+            rowsum[e] = dQt[cb][e] * qt + dKt[cb][e] * kt - dKb[cb][e] * kb;
+            hsum[e] = dKbh[cb][e] * kb;
+        }
+        if (CH) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                dbf[rowof(e) * D + j] = rowsum[e];
+                hf[rowof(e) * D + j] = hsum[e];
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float v = sum_group<16>(rowsum[e]);
+                const float hv = sum_group<16>(hsum[e]);
+                if (l15 == 0) {
+                    atomicAdd(&sm.dbrow[rowof(e)], v);
+                    atomicAdd(&sm.hrow[rowof(e)], hv);
+                }
+            }
+        }
+    }
+    __syncthreads();                           // Qt, Kt no longer read
+    if (CH) {
+        if (tid < D) {
+            float run = 0.f;
+            for (int r0 = 0; r0 < C; r0 += 16) {
+                float gv[16];
+#pragma unroll
+                for (int u = 0; u < 16; ++u)
+                    gv[u] = r0 + u < Cc ? gg[(size_t)(r0 + u) * gstr + tid] : 0.f;
+#pragma unroll
+                for (int u = 0; u < 16; ++u) {
+                    run += gv[u];
+                    Ef[(r0 + u) * D + tid] = ex(run);
+                }
+            }
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb) {
+        const int j = 16 * cb + l15;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = rowof(e);
+            const float E = CH ? Ef[r * D + j] : ex(sm.bs[r]);
+            const float Ei = __builtin_amdgcn_rcpf(E);
+            if (r < Cc) {
+                const size_t o = ((tok0 + r) * a.H + h) * D + j;
+                a.dq[o] = dQt[cb][e] * E;
+                a.dk[o] = dKt[cb][e] * E + (dKb[cb][e] + dKbh[cb][e]) * Ei;
+            }
+        }
+    }
+    // db_C (the Kh part is in h): sum_i dSg_i (.) S0_i
+    if (tid < D) {
+        float acc = 0.f;
+#pragma unroll 16
+        for (int i = 0; i < D; ++i) acc += dSC[(size_t)i * D + tid] * S0[(size_t)i * D + tid];
+        atomicAdd(&sm.dbC[tid], acc * sm.eC[tid]);
+    }
+    __syncthreads();
+    if (CH) {
+        if (tid < D) {
+            // h enters dg_s as its sum over r < s (an exclusive prefix)
+            float pre = 0.f;
+            for (int r = 0; r < C; ++r) {
+                const float hv = hf[r * D + tid];
+                hf[r * D + tid] = pre;
+                pre += hv;
+            }
+            float run = sm.dbC[tid];
+            for (int r = C - 1; r >= 0; --r) {
+                run += dbf[r * D + tid];
+                if (r < Cc) a.dg[(tok0 + r) * a.H * D + (size_t)h * D + tid] = run + hf[r * D + tid];
+            }
+        }
+    } else if (w == 0) {
+        // scalar gate: db_C summed over channels, then reverse sums over rows
+        float tot = 0.f;
+        for (int j = lane; j < D; j += 64) tot += sm.dbC[j];
+        tot = sum_quads(sum_group<16>(tot));
+        float pre = 0.f, mine = 0.f;
+        for (int r = 0; r < C; ++r) {
+            if (r == lane) mine = pre;
+            pre += sm.hrow[r];
+        }
+        float run = tot;
+        for (int r = C - 1; r >= 0; --r) {
+            run += sm.dbrow[r];
+            if (r == lane && r < Cc) a.dg[(tok0 + r) * a.H + h] = run + mine;
+        }
+    }
+    if (tid < Cc) a.dbeta[(tok0 + tid) * a.H + h] = sm.dbeta[tid];
+}
+
+// dst = src, or zeros without src (a kernel, so that the call can be
+// captured in a graph)
+__global__ __launch_bounds__(256) void copy_or_zero_kernel(float *dst, const float *src, size_t n) {
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) dst[i] = src ? src[i] : 0.f;
+}
+
+}  // namespace
+
+hipError_t launch_copy_or_zero(float *dst, const float *src, size_t n, hipStream_t s) {
+    if (n == 0) return hipSuccess;
+    const size_t blocks = (n + 255) / 256;
+    if (blocks >= (1ULL << 31)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(copy_or_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s, dst, src, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_backward(int D, const BwdArgs &a, hipStream_t s) {
+    const long long heads = (long long)a.B * a.H;
+    if (heads <= 0) return hipSuccess;
+    if (a.T == 0) return hipSuccess;
+    const long long rows_blocks = heads * (D == 128 ? RowG<128>::NRB : RowG<64>::NRB);
+    const long long chunk_blocks = (long long)a.B * a.nc * a.H;
+    if (rows_blocks >= (1LL << 31) || chunk_blocks >= (1LL << 31)) return hipErrorInvalidValue;
+    dim3 gr((unsigned)rows_blocks), gc((unsigned)chunk_blocks), blk(256);
+    if (D == 128) {
+        hipLaunchKernelGGL((dstate_pass_kernel<bf16, 128>), gr, blk, 0, s, a);
+        if (a.channel_gate) hipLaunchKernelGGL((chunk_grad_kernel<128, true>), gc, blk, 0, s, a);
+        else                hipLaunchKernelGGL((chunk_grad_kernel<128, false>), gc, blk, 0, s, a);
+    } else {
+        hipLaunchKernelGGL((dstate_pass_kernel<bf16, 64>), gr, blk, 0, s, a);
+        if (a.channel_gate) hipLaunchKernelGGL((chunk_grad_kernel<64, true>), gc, blk, 0, s, a);
+        else                hipLaunchKernelGGL((chunk_grad_kernel<64, false>), gc, blk, 0, s, a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace gdr

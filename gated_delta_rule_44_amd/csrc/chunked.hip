@@ -222,6 +222,9 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
                     if (h0p)
                         sv = *reinterpret_cast<const f32x4 *>(h0p + (size_t)(i0 + iv) * D + j);
                     *reinterpret_cast<bf16x4 *>(&sm.S[iv * PD + j]) = cvt4(sv);
+                    if (a.states && nch > 0)        // the state entering chunk 0
+                        *reinterpret_cast<f32x4 *>(a.states + ((size_t)n * a.H + h) * nch * D * D +
+                                                   (size_t)(i0 + iv) * D + j) = sv;
                 }
                 St[kb][jv] = sv;
             }
@@ -583,6 +586,9 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
                         sv = mfma32(k1f, uf[jv][1], sv) * gm;
                         St[kb][jv] = sv;
                         *reinterpret_cast<bf16x4 *>(&sm.S[(16 * jv + l15) * PD + jc]) = cvt4(sv);
+                        if (a.states && j < nch)   // the state entering chunk j
+                            *reinterpret_cast<f32x4 *>(a.states + (((size_t)n * a.H + h) * nch + j) * D * D +
+                                                       (size_t)(i0 + 16 * jv + l15) * D + jc) = sv;
                     }
                 }
             }

@@ -499,6 +499,11 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
         for (long long c = 0; c < nch; ++c) {
             const int par = (int)(c & 1);
             const int n3 = m3 == 2 ? 0 : m3 + 1;
+            if (a.states) {                   // the state entering chunk c
+                float *sp = a.states + (((size_t)n * a.H + h) * nch + c) * D * D + srow0;
+#pragma unroll
+                for (int jk = 0; jk < KS; ++jk) *reinterpret_cast<f32x4 *>(sp + srow(jk, 0)) = St[jk];
+            }
             // ---- alpha: X = V - diag(e^b) K S^T, U = T X and the state
             //      update, all from registers
             f32x4 X[4];

@@ -128,6 +128,10 @@ struct PrefillArgs {
     // normalised in the kernels
     const void *xg, *xb;
     float gate_scale;
+    // fixed-length bf16 path only: when set, the state entering every chunk
+    // of every (sequence, head), [N, H, ceil(T / 64), D, D] fp32 (for the
+    // backward)
+    float *states;
 };
 
 // Initial state of sequence n, head h (nullptr: start from zeros) and where
@@ -159,6 +163,24 @@ constexpr size_t kTileBytes = 5 * 1024 + 2 * 64 * 4;
 // With fused preprocessing the record carries the key norms folded into
 // two more factor rows (6 KiB).
 constexpr size_t kTileBytesRaw = kTileBytes + 2 * 64 * 4;
+
+// Backward of the chunked prefill (fixed-length batch, bf16 q/k/v/do).
+struct BwdArgs {
+    const void *q, *k, *v;        // [B, T, H, D] bf16
+    const float *g, *beta;        // [B, T, H(, D)], [B, T, H]
+    const float *h0;              // [B, H, D, D] or nullptr
+    const void *dout;             // [B, T, H, D] bf16: gradient of o
+    const float *dht;             // [B, H, D, D] or nullptr: gradient of the final state
+    float *dq, *dk, *dv;          // [B, T, H, D]
+    float *dg, *dbeta;            // like g, beta
+    float *dh0;                   // [B, H, D, D] or nullptr
+    float *states, *dstates;      // workspace: [B, H, nc, D, D] each
+    int B, T, H, nc;
+    float scale;
+    int channel_gate;
+};
+hipError_t launch_backward(int D, const BwdArgs &a, hipStream_t s);
+hipError_t launch_copy_or_zero(float *dst, const float *src, size_t n, hipStream_t s);
 
 hipError_t launch_prefill_recurrent(bool bf16_io, int D, const PrefillArgs &a,
                                     hipStream_t s);

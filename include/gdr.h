@@ -320,6 +320,43 @@ gdr_status gdr_decode_tokens_fused(enum gdr_dtype dt, enum gdr_gate gk, int B, i
                                    int pool_slots, float *state_pool, float *checkpoints,
                                    void *o, void *stream);
 
+/*
+ * Backward of the chunked prefill, for training (the pages train the
+ * supernet by distillation and then fine-tuning, summary section 2b).  For a
+ * fixed-length batch and the upstream gradients d_o (of o) and dht (of the
+ * final states), returns the gradients of every input of gdr_prefill_chunked:
+ * the vector-Jacobian product of the recurrence stated at the top of this
+ * header.
+ *
+ *   dt, gk, B, T, H, Dk, Dv, chunk, scale, q, k, v, g, beta, h0
+ *                as gdr_prefill_chunked (dt must be GDR_BF16)
+ *   d_o          [B, T, H, Dv] bf16: gradient of o
+ *   dht          [B, H, Dv, Dk] fp32 or NULL (zero)
+ *   dq, dk       [B, T, H, Dk] fp32 (written)
+ *   dv           [B, T, H, Dv] fp32 (written)
+ *   dg           like g, fp32 (written);  dbeta [B, T, H] fp32 (written)
+ *   dh0          [B, H, Dv, Dk] fp32 (written) or NULL
+ *   workspace    device buffer of gdr_backward_workspace_bytes(gk, B, T, H,
+ *                Dk, Dv) bytes (the state entering and the state gradient
+ *                leaving every chunk of 64 tokens in fp32, the forward's own
+ *                outputs and workspace), 16-byte aligned
+ *
+ * Three stages: the chunked forward storing the state that enters every
+ * chunk, the adjoint recurrence in reverse storing each chunk's state
+ * gradient (and dh0), and one MFMA workgroup per (chunk, head) for the
+ * chunk-local gradients.  fp32 inputs are GDR_EUNSUPPORTED.
+ * Numerics: bf16 operands with fp32 accumulation, as the forward.
+ */
+size_t gdr_backward_workspace_bytes(enum gdr_gate gk, int B, int T, int H, int Dk, int Dv);
+
+gdr_status gdr_backward_chunked(enum gdr_dtype dt, enum gdr_gate gk, int B, int T, int H,
+                                int Dk, int Dv, int chunk, float scale, const void *q,
+                                const void *k, const void *v, const float *g,
+                                const float *beta, const float *h0, const void *d_o,
+                                const float *dht, float *dq, float *dk, float *dv, float *dg,
+                                float *dbeta, float *dh0, void *workspace, size_t ws_bytes,
+                                void *stream);
+
 /* Thread-local text describing the last non-OK status of this thread. */
 const char *gdr_last_error(void);
 

@@ -37,6 +37,7 @@ def test_header_declares_the_boundary():
                             "gdr_decode_tokens", "gdr_decode_commit",
                             "gdr_prefill_fused_workspace_bytes", "gdr_prefill_chunked_fused",
                             "gdr_prefill_varlen_fused", "gdr_decode_tokens_fused",
+                            "gdr_backward_workspace_bytes", "gdr_backward_chunked",
                             "gdr_last_error", "gdr_version"])
 
 
@@ -247,6 +248,29 @@ def test_fused_rejects(lib):
     assert tok(c=-2.0) == EINVAL
     assert tok(pool=1) == EINVAL and "pool needs" in err()
     assert tok(state=None) == EINVAL
+
+
+def test_backward_rejects(lib):
+    err = lambda: lib.gdr_last_error().decode()  # noqa: E731
+    # chunk states and state gradients, the forward's outputs (bf16, rounded
+    # to 256 bytes) and its workspace (for the scalar gate: 5632-byte records)
+    st = 2 * 3 * 2 * 128 * 128 * 4
+    o = (2 * 100 * 3 * 128 * 2 + 255) // 256 * 256
+    assert lib.gdr_backward_workspace_bytes(1, 2, 100, 3, 128, 128) == 2 * st + o + 512
+    assert lib.gdr_backward_workspace_bytes(0, 2, 100, 3, 128, 128) == \
+        2 * st + o + 512 + (200 // 64 + 2) * 3 * 5632
+    assert lib.gdr_backward_workspace_bytes(1, 2, 0, 3, 128, 128) == 0
+
+    def call(dt=1, ws_bytes=1 << 30, T=100, **kw):
+        return lib.gdr_backward_chunked(
+            dt, 1, 2, T, 3, 128, 128, 64, F(1.0), FAKE, FAKE, FAKE, FAKE, FAKE, None,
+            kw.get("do", FAKE), None, FAKE, FAKE, FAKE, kw.get("dg", FAKE), FAKE, None,
+            kw.get("ws", FAKE), ws_bytes, None)
+    assert call(dt=0) == EUNSUPPORTED and "bf16" in err()
+    assert call(do=None) == EINVAL and "do is NULL" in err()
+    assert call(dg=None) == EINVAL
+    assert call(ws_bytes=100) == EINVAL and "workspace" in err()
+    assert call(ws=MIS) == EINVAL
 
 
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
