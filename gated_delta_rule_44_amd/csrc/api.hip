@@ -573,9 +573,10 @@ namespace {
 
 // Backward workspace: the chunk-entering states and the chunk state
 // gradients ([B, H, nc, Dv, Dk] fp32 each), the forward's outputs (bf16,
-// unused) and the forward's own workspace.
+// unused), the forward's own workspace and the adjoint chain's per-chunk
+// records.
 struct BwdWs {
-    size_t states, dstates, o, fwd, total;
+    size_t states, dstates, o, fwd, recs, total;
 };
 BwdWs bwd_layout(int gk, int B, int T, int H, int Dk, int Dv) {
     BwdWs w{};
@@ -587,7 +588,8 @@ BwdWs bwd_layout(int gk, int B, int T, int H, int Dk, int Dv) {
     w.dstates = st;
     w.o = 2 * st;
     w.fwd = w.o + r256((size_t)B * T * H * Dv * 2);
-    w.total = w.fwd + ws_layout(gk == GDR_GATE_SCALAR, B, (long long)B * T, H).total;
+    w.recs = w.fwd + r256(ws_layout(gk == GDR_GATE_SCALAR, B, (long long)B * T, H).total);
+    w.total = w.recs + (size_t)B * H * nc * gdr::backward_record_bytes(Dk);
     return w;
 }
 
@@ -665,6 +667,7 @@ gdr_status gdr_backward_chunked(enum gdr_dtype dt, enum gdr_gate gk, int B, int 
     a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbeta = dbeta; a.dh0 = dh0;
     a.states = reinterpret_cast<float *>(ws + W.states);
     a.dstates = reinterpret_cast<float *>(ws + W.dstates);
+    a.recs = ws + W.recs;
     a.B = B; a.T = T; a.H = H; a.nc = (T + 63) / 64; a.scale = scale;
     a.channel_gate = gk == GDR_GATE_CHANNEL;
     return finish(gdr::launch_backward(Dk, a, s), s, what);

@@ -5,16 +5,16 @@
 //     S_t = S_{t-1} Diag(a_t)(I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
 //     o_t = scale * S_t q_t,   a_t = e^{g_t}.
 // For upstream gradients dO (of o) and dS_T (of the final state) the
-// backward returns dq, dk, dv, dg, dbeta and dS_0 in three launches:
+// backward returns dq, dk, dv, dg, dbeta and dS_0 in three stages:
 //
 // 1. the chunked forward (chunked.hip / chunked_chain.hip) with its
 //    optional output of the state entering every chunk of 64 tokens.
-// 2. dstate_pass_kernel: the adjoint recurrence in reverse,
-//        G_{t-1} = (G_t + scale do_t q_t^T)(I - beta_t k_t k_t^T) Diag(a_t),
-//    G_{T-1} = dS_T, where G_t is the gradient of the state after token t
-//    through everything but o_t.  Row-local like the forward.  It stores
-//    G at the last token of every chunk (the chunk's dS_C) and writes
-//    dS_0 = G_{-1}.
+// 2. chunk_grad_kernel<.., PREP>: per (chunk, head), the chunk-local
+//    matrices of the state gradient's recurrence (below) into a record;
+//    adjoint_chain_kernel: that recurrence chunk by chunk in reverse,
+//        dS_{c-1} = dS_c Diag(e^{b_C}) + scale dO^T Qt - dU^T W,
+//        dU = Kb (dS_c Diag(e^{b_C}))^T + scale P^T dO,  W = T Kt,
+//    from dS_{last} = dS_T; it stores every chunk's dS_C and dS_0.
 // 3. chunk_grad_kernel: per (chunk, head), from the entering state S0 and
 //    dS_C, every input gradient of the chunk by differentiating the chunked
 //    form (see chunked.hip) -- with b the in-chunk cumulative log gate,
@@ -50,132 +50,6 @@ namespace gdr {
 namespace {
 
 constexpr int C = 64;
-
-// ===========================================================================
-// The adjoint pass: 256 threads hold 16 (D = 128) or 32 (D = 64) rows of one
-// head's state gradient; lane group of LPR lanes per row, float4 per lane.
-// ===========================================================================
-template <int D> struct RowG {
-    static constexpr int LPR = D / 4;          // lanes per row
-    static constexpr int RPW = 64 / LPR;       // rows per wave per pass
-    static constexpr int RPP = 4 * RPW;        // rows per pass
-    static constexpr int ROWS = 2 * RPP;       // rows per workgroup (two passes)
-    static constexpr int NRB = D / ROWS;       // workgroups per head
-};
-
-__device__ inline float dot4b(f32x4 a, f32x4 b) {
-    return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
-}
-
-// x of lane l ^ (LPR / 2): the other half of a row of LPR lanes.  LPR = 32:
-// the neighbouring 16-lane row, from the gfx950 v_permlane16_swap (odd rows
-// of one register swapped with even rows of the other, so with both holding
-// x, the first holds the even row's values and the second the odd row's);
-// LPR = 16: DPP row_ror:8.
-template <int LPR>
-__device__ inline float half_partner(float x, int lane) {
-    if (LPR == 16) return dpp_f<0x128>(x);
-    float a = x, b = x;
-    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
-    return (lane & 16) ? a : b;
-}
-// The two row dot products (pass 0 and 1) of this lane's rows, summed over
-// the LPR lanes of each row: one halving exchange, then a sum over the half
-// (DPP), then the halves swapped back; returns (d0, d1) in every lane.  All
-// on the VALU: the chain of LDS round trips of __shfl_xor set the time of
-// every step of the pass.
-template <int LPR>
-__device__ inline void row_dots(float y0, float y1, int lane, float &d0, float &d1) {
-    const bool upper = (lane & (LPR / 2)) != 0;
-    float val = (upper ? y1 : y0) + half_partner<LPR>(upper ? y0 : y1, lane);
-    val = sum_group<LPR / 2>(val);
-    const float other = half_partner<LPR>(val, lane);
-    d0 = upper ? other : val;
-    d1 = upper ? val : other;
-}
-
-// Inputs of one token for the rows of this lane, loaded PF tokens ahead of
-// their use: the passes are chains of dependent steps, so a load issued for
-// the current token would put its latency on every step.
-constexpr int PF = 8;
-template <int D>
-struct TokRow {
-    f32x4 k, q, lg;
-    float beta, x0, x1;     // x: v (forward) or do (adjoint) at the two rows
-};
-
-template <typename T, int D, bool ADJ>
-__device__ __forceinline__ void load_row_tok(const BwdArgs &a, size_t r, int c0, const int (&row)[2],
-                                             TokRow<D> &x) {
-    x.k = Elem<T>::load4(static_cast<const T *>(a.k) + r * D + c0);
-    if (ADJ) x.q = Elem<T>::load4(static_cast<const T *>(a.q) + r * D + c0);
-    if (a.channel_gate) {
-        x.lg = *reinterpret_cast<const f32x4 *>(a.g + r * D + c0);
-    } else {
-        const float s = a.g[r];
-        x.lg = f32x4{s, s, s, s};
-    }
-    x.beta = a.beta[r];
-    const T *xp = static_cast<const T *>(ADJ ? a.dout : a.v) + r * D;
-    x.x0 = Elem<T>::load(xp + row[0]);
-    x.x1 = Elem<T>::load(xp + row[1]);
-}
-
-__device__ inline f32x4 gate_factors(f32x4 lg) {
-    return f32x4{__builtin_amdgcn_exp2f(lg.x * kLog2e), __builtin_amdgcn_exp2f(lg.y * kLog2e),
-                 __builtin_amdgcn_exp2f(lg.z * kLog2e), __builtin_amdgcn_exp2f(lg.w * kLog2e)};
-}
-
-// The adjoint recurrence in reverse, storing each chunk's dS_C, then dS_0.
-template <typename T, int D>
-__global__ __launch_bounds__(256) void dstate_pass_kernel(BwdArgs a) {
-    using G = RowG<D>;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int rb = blockIdx.x % G::NRB;
-    const int bh = blockIdx.x / G::NRB;
-    const int b = bh / a.H, h = bh - b * a.H;
-    const int c0 = (lane % G::LPR) * 4, sub = lane / G::LPR;
-    int row[2];
-#pragma unroll
-    for (int p = 0; p < 2; ++p) row[p] = rb * G::ROWS + p * G::RPP + w * G::RPW + sub;
-    f32x4 Z[2];
-#pragma unroll
-    for (int p = 0; p < 2; ++p)
-        Z[p] = a.dht ? *reinterpret_cast<const f32x4 *>(a.dht + (size_t)bh * D * D + (size_t)row[p] * D + c0)
-                     : f32x4{0.f, 0.f, 0.f, 0.f};
-    float *dst = a.dstates + (size_t)bh * a.nc * D * D;
-    const size_t r0 = (size_t)b * a.T * a.H + h;
-    TokRow<D> buf[PF];
-#pragma unroll
-    for (int i = 0; i < PF; ++i)
-        if (a.T - 1 - i >= 0) load_row_tok<T, D, true>(a, r0 + (size_t)(a.T - 1 - i) * a.H, c0, row, buf[i]);
-    for (int tb = 0; tb < a.T; tb += PF) {
-#pragma unroll
-        for (int i = 0; i < PF; ++i) {
-            const int t = a.T - 1 - (tb + i);
-            if (t < 0) break;
-            if (t == a.T - 1 || t % C == C - 1) {
-#pragma unroll
-                for (int p = 0; p < 2; ++p)
-                    *reinterpret_cast<f32x4 *>(dst + (size_t)(t / C) * D * D + (size_t)row[p] * D + c0) = Z[p];
-            }
-            const TokRow<D> x = buf[i];
-            if (t - PF >= 0) load_row_tok<T, D, true>(a, r0 + (size_t)(t - PF) * a.H, c0, row, buf[i]);
-            const f32x4 av = gate_factors(x.lg);
-            const f32x4 z0 = Z[0] + (a.scale * x.x0) * x.q;
-            const f32x4 z1 = Z[1] + (a.scale * x.x1) * x.q;
-            float y0, y1;
-            row_dots<G::LPR>(dot4b(z0, x.k), dot4b(z1, x.k), lane, y0, y1);
-            Z[0] = (z0 - (x.beta * y0) * x.k) * av;
-            Z[1] = (z1 - (x.beta * y1) * x.k) * av;
-        }
-    }
-    if (a.dh0) {
-#pragma unroll
-        for (int p = 0; p < 2; ++p)
-            *reinterpret_cast<f32x4 *>(a.dh0 + (size_t)bh * D * D + (size_t)row[p] * D + c0) = Z[p];
-    }
-}
 
 // ===========================================================================
 // chunk_grad_kernel
@@ -266,7 +140,19 @@ __device__ inline bf16x8 g_cols_bf(const bf16 *base, size_t ld, int k0, int n0, 
 // sum of x over the four lanes (l & 15) + 16 m, m = 0..3
 __device__ inline float sum_quads(float x) { return swap_sum32(swap_sum16(x)); }
 
-template <int D, bool CH>
+// Per-chunk record of the adjoint chain: the chunk-local matrices that the
+// state gradient's recurrence needs, in bf16, and e^{b_C} in fp32.
+template <int D> struct ChainRec {
+    static constexpr size_t QT = 0;                          // Qt [C][D]
+    static constexpr size_t KB = QT + (size_t)C * D * 2;     // Kb [C][D]
+    static constexpr size_t W = KB + (size_t)C * D * 2;      // W = T Kt [C][D]
+    static constexpr size_t P = W + (size_t)C * D * 2;       // P [C][C]
+    static constexpr size_t EC = P + (size_t)C * C * 2;      // e^{b_C} [D] fp32
+    static constexpr size_t BYTES = EC + (size_t)D * 4;
+};
+
+// PREP: stop after T and write the chunk's ChainRec (no S0 or dS_C needed).
+template <int D, bool CH, bool PREP>
 __global__ __launch_bounds__(256) void chunk_grad_kernel(BwdArgs a) {
     using Sm = GradSmem<D>;
     constexpr int PD = Sm::PD;
@@ -431,6 +317,40 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(BwdArgs a) {
         if (r == s) sm.tcor[r] = tv - (float)tb;
     }
     __syncthreads();
+
+    if constexpr (PREP) {
+        // W = T Kt (the diagonal of T compensated), then the record
+        using R = ChainRec<D>;
+        char *rec = static_cast<char *>(a.recs) + (((size_t)b * a.H + h) * a.nc + c) * R::BYTES;
+        bf16 *Wg = reinterpret_cast<bf16 *>(rec + R::W);
+#pragma unroll
+        for (int cb = 0; cb < NB; ++cb) {
+            f32x4 x = zero4();
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+                x = mfma32(frag_rows(sm.Tb, PC, 16 * I, 32 * kk, lane), frag_cols(sm.Kt, PD, 32 * kk, 16 * cb, lane), x);
+            const int j = 16 * cb + l15;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = rowof(e);
+                Wg[r * D + j] = (bf16)(x[e] + sm.tcor[r] * (float)sm.Kt[r * PD + j]);
+            }
+        }
+        bf16 *Qg = reinterpret_cast<bf16 *>(rec + R::QT);
+        bf16 *Kg = reinterpret_cast<bf16 *>(rec + R::KB);
+        for (int p = tid; p < C * D / 8; p += 256) {
+            const int r = p / (D / 8), j = 8 * (p % (D / 8));
+            *reinterpret_cast<bf16x8 *>(Qg + r * D + j) = *reinterpret_cast<const bf16x8 *>(&sm.Qt[r * PD + j]);
+            *reinterpret_cast<bf16x8 *>(Kg + r * D + j) = *reinterpret_cast<const bf16x8 *>(&sm.Kb[r * PD + j]);
+        }
+        bf16 *Pg = reinterpret_cast<bf16 *>(rec + R::P);
+        for (int p = tid; p < C * C / 8; p += 256) {
+            const int r = p / (C / 8), sc = 8 * (p % (C / 8));
+            *reinterpret_cast<bf16x8 *>(Pg + r * C + sc) = *reinterpret_cast<const bf16x8 *>(&sm.Pb[r * PC + sc]);
+        }
+        if (tid < D) reinterpret_cast<float *>(rec + R::EC)[tid] = sm.eC[tid];
+        return;
+    }
 
     // ---- 4. X = V - Kt S0^T  (S0 [i][j] as the B operand of X Y^T)
 #pragma unroll
@@ -769,6 +689,153 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(BwdArgs a) {
     if (tid < Cc) a.dbeta[(tok0 + tid) * a.H + h] = sm.dbeta[tid];
 }
 
+// ===========================================================================
+// adjoint_chain_kernel: the state gradient chunk by chunk, in reverse.  From
+// the chunked form, with dSg = dS_C Diag(e^{b_C}),
+//     dU = Kb dSg^T + scale P^T dO,    dS_0 = dSg + scale dO^T Qt - dU^T W,
+// W = T Kt; the rows of dS (value index) never mix, so one workgroup owns a
+// 32-row slice of one (sequence, head) and walks its chunks from the last,
+// dS in fp32 accumulators (wave w: rows 16 (w & 1) .., key blocks
+// 4 (w >> 1) .. +3), staging each chunk's ChainRec and dO slice in LDS.  It
+// stores every chunk's dS_C and finally dS_0 (dh0).
+// ===========================================================================
+constexpr int BVA = 32;     // value rows per chain workgroup
+
+template <int D> struct ChainSmem {
+    static constexpr int PD = D + 8, PV = BVA + 8;
+    alignas(16) bf16 Qt[C * PD];
+    alignas(16) bf16 Kb[C * PD];
+    alignas(16) bf16 W[C * PD];
+    alignas(16) bf16 P[C * PC];
+    alignas(16) float eC[D];
+    alignas(16) bf16 dO[C * PV];      // [r][i]
+    alignas(16) bf16 dSh[BVA * PD];   // dSg as hi + lo bf16, [i][j]
+    alignas(16) bf16 dSl[BVA * PD];
+    alignas(16) bf16 dU[C * PV];      // [r][i]
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void adjoint_chain_kernel(BwdArgs a) {
+    using Sm = ChainSmem<D>;
+    using R = ChainRec<D>;
+    constexpr int PD = Sm::PD, PV = Sm::PV;
+    constexpr int NTL = D / BVA;
+    constexpr int CB = D / 32;        // key blocks per wave: 32 x D of dS over 4 waves
+    __shared__ Sm sm;
+    // the value slices of one (sequence, head) on one XCD
+    const int bid = blockIdx.x;
+    const int xcd = bid & 7, jj = bid >> 3;
+    const int tile = jj % NTL;
+    const int unit = (jj / NTL) * 8 + xcd;
+    if (unit >= a.B * a.H) return;
+    const int b = unit / a.H, h = unit - b * a.H;
+    const int i0 = tile * BVA;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l15 = lane & 15, q4 = lane >> 4;
+    const int ib = w & 1, jb0 = CB * (w >> 1);
+    const size_t rowD = (size_t)a.H * D;
+    const size_t bh = (size_t)b * a.H + h;
+
+    // dS tiles: element e of tile t = row i0 + 16 ib + 4 q4 + e, column 16 (jb0 + t) + l15
+    f32x4 dS[CB];
+#pragma unroll
+    for (int t = 0; t < CB; ++t) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const size_t o = bh * D * D + (size_t)(i0 + 16 * ib + 4 * q4 + e) * D + 16 * (jb0 + t) + l15;
+            dS[t][e] = a.dht ? a.dht[o] : 0.f;
+        }
+    }
+    for (int c = a.nc - 1; c >= 0; --c) {
+        const int t0 = c * C;
+        const int Cc = a.T - t0 < C ? a.T - t0 : C;
+        // dS_C of chunk c
+        float *dsc = a.dstates + (bh * a.nc + c) * D * D;
+#pragma unroll
+        for (int t = 0; t < CB; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                dsc[(size_t)(i0 + 16 * ib + 4 * q4 + e) * D + 16 * (jb0 + t) + l15] = dS[t][e];
+        // stage the record and the dO slice
+        const char *rec = static_cast<const char *>(a.recs) + (bh * a.nc + c) * R::BYTES;
+        for (int p = tid; p < C * D / 8; p += 256) {
+            const int r = p / (D / 8), j = 8 * (p % (D / 8));
+            *reinterpret_cast<bf16x8 *>(&sm.Qt[r * PD + j]) = *reinterpret_cast<const bf16x8 *>(rec + R::QT + 2 * (r * D + j));
+            *reinterpret_cast<bf16x8 *>(&sm.Kb[r * PD + j]) = *reinterpret_cast<const bf16x8 *>(rec + R::KB + 2 * (r * D + j));
+            *reinterpret_cast<bf16x8 *>(&sm.W[r * PD + j]) = *reinterpret_cast<const bf16x8 *>(rec + R::W + 2 * (r * D + j));
+        }
+        for (int p = tid; p < C * C / 8; p += 256) {
+            const int r = p / (C / 8), sc = 8 * (p % (C / 8));
+            *reinterpret_cast<bf16x8 *>(&sm.P[r * PC + sc]) = *reinterpret_cast<const bf16x8 *>(rec + R::P + 2 * (r * C + sc));
+        }
+        if (tid < D) sm.eC[tid] = reinterpret_cast<const float *>(rec + R::EC)[tid];
+        {
+            const int r = tid >> 2, seg = 8 * (tid & 3);      // 64 rows x 4 pieces of 8
+            bf16x8 v = {};
+            if (r < Cc)
+                v = *reinterpret_cast<const bf16x8 *>(static_cast<const bf16 *>(a.dout) +
+                                                      (((size_t)b * a.T + t0 + r) * a.H + h) * D + i0 + seg);
+            *reinterpret_cast<bf16x8 *>(&sm.dO[r * PV + seg]) = v;
+        }
+        __syncthreads();
+        // dSg = dS e^{b_C} as hi + lo bf16
+#pragma unroll
+        for (int t = 0; t < CB; ++t) {
+            const int j = 16 * (jb0 + t) + l15;
+            const float ec = sm.eC[j];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float v = dS[t][e] * ec;
+                const bf16 hi = (bf16)v;
+                const int ii = 16 * ib + 4 * q4 + e;
+                sm.dSh[ii * PD + j] = hi;
+                sm.dSl[ii * PD + j] = (bf16)(v - (float)hi);
+            }
+        }
+        __syncthreads();
+        // dU = Kb dSg^T + scale P^T dO: wave w takes row block w, both value blocks
+#pragma unroll
+        for (int vb = 0; vb < 2; ++vb) {
+            f32x4 x = {0.f, 0.f, 0.f, 0.f}, y = x;
+#pragma unroll
+            for (int kk = 0; kk < D / 32; ++kk) {
+                const bf16x8 kf = frag_rows(sm.Kb, PD, 16 * w, 32 * kk, lane);
+                x = mfma32(kf, frag_rows(sm.dSh, PD, 16 * vb, 32 * kk, lane), x);
+                x = mfma32(kf, frag_rows(sm.dSl, PD, 16 * vb, 32 * kk, lane), x);
+            }
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+                y = mfma32(frag_cols(sm.P, PC, 32 * kk, 16 * w, lane), frag_cols(sm.dO, PV, 32 * kk, 16 * vb, lane), y);
+            const int i = 16 * vb + l15;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sm.dU[(16 * w + 4 * q4 + e) * PV + i] = (bf16)(x[e] + a.scale * y[e]);
+        }
+        __syncthreads();
+        // dS_0 = dSg + scale dO^T Qt - dU^T W
+#pragma unroll
+        for (int t = 0; t < CB; ++t) {
+            const int jb = jb0 + t;
+            f32x4 x = {0.f, 0.f, 0.f, 0.f}, y = x;
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                x = mfma32(frag_cols(sm.dO, PV, 32 * kk, 16 * ib, lane), frag_cols(sm.Qt, PD, 32 * kk, 16 * jb, lane), x);
+                y = mfma32(frag_cols(sm.dU, PV, 32 * kk, 16 * ib, lane), frag_cols(sm.W, PD, 32 * kk, 16 * jb, lane), y);
+            }
+            const float ec = sm.eC[16 * jb + l15];
+            dS[t] = dS[t] * ec + a.scale * x - y;
+        }
+        __syncthreads();                       // before the next chunk's staging
+    }
+    if (a.dh0) {
+#pragma unroll
+        for (int t = 0; t < CB; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                a.dh0[bh * D * D + (size_t)(i0 + 16 * ib + 4 * q4 + e) * D + 16 * (jb0 + t) + l15] = dS[t][e];
+    }
+}
+
 // dst = src, or zeros without src (a kernel, so that the call can be
 // captured in a graph)
 __global__ __launch_bounds__(256) void copy_or_zero_kernel(float *dst, const float *src, size_t n) {
@@ -786,22 +853,30 @@ hipError_t launch_copy_or_zero(float *dst, const float *src, size_t n, hipStream
     return hipGetLastError();
 }
 
+size_t backward_record_bytes(int D) {
+    return D == 128 ? ChainRec<128>::BYTES : ChainRec<64>::BYTES;
+}
+
 hipError_t launch_backward(int D, const BwdArgs &a, hipStream_t s) {
     const long long heads = (long long)a.B * a.H;
     if (heads <= 0) return hipSuccess;
     if (a.T == 0) return hipSuccess;
-    const long long rows_blocks = heads * (D == 128 ? RowG<128>::NRB : RowG<64>::NRB);
+    const long long chain_blocks = ((heads + 7) / 8) * 8 * (D / BVA);
     const long long chunk_blocks = (long long)a.B * a.nc * a.H;
-    if (rows_blocks >= (1LL << 31) || chunk_blocks >= (1LL << 31)) return hipErrorInvalidValue;
-    dim3 gr((unsigned)rows_blocks), gc((unsigned)chunk_blocks), blk(256);
+    if (chain_blocks >= (1LL << 31) || chunk_blocks >= (1LL << 31)) return hipErrorInvalidValue;
+    dim3 gr((unsigned)chain_blocks), gc((unsigned)chunk_blocks), blk(256);
     if (D == 128) {
-        hipLaunchKernelGGL((dstate_pass_kernel<bf16, 128>), gr, blk, 0, s, a);
-        if (a.channel_gate) hipLaunchKernelGGL((chunk_grad_kernel<128, true>), gc, blk, 0, s, a);
-        else                hipLaunchKernelGGL((chunk_grad_kernel<128, false>), gc, blk, 0, s, a);
+        if (a.channel_gate) hipLaunchKernelGGL((chunk_grad_kernel<128, true, true>), gc, blk, 0, s, a);
+        else                hipLaunchKernelGGL((chunk_grad_kernel<128, false, true>), gc, blk, 0, s, a);
+        hipLaunchKernelGGL(adjoint_chain_kernel<128>, gr, blk, 0, s, a);
+        if (a.channel_gate) hipLaunchKernelGGL((chunk_grad_kernel<128, true, false>), gc, blk, 0, s, a);
+        else                hipLaunchKernelGGL((chunk_grad_kernel<128, false, false>), gc, blk, 0, s, a);
     } else {
-        hipLaunchKernelGGL((dstate_pass_kernel<bf16, 64>), gr, blk, 0, s, a);
-        if (a.channel_gate) hipLaunchKernelGGL((chunk_grad_kernel<64, true>), gc, blk, 0, s, a);
-        else                hipLaunchKernelGGL((chunk_grad_kernel<64, false>), gc, blk, 0, s, a);
+        if (a.channel_gate) hipLaunchKernelGGL((chunk_grad_kernel<64, true, true>), gc, blk, 0, s, a);
+        else                hipLaunchKernelGGL((chunk_grad_kernel<64, false, true>), gc, blk, 0, s, a);
+        hipLaunchKernelGGL(adjoint_chain_kernel<64>, gr, blk, 0, s, a);
+        if (a.channel_gate) hipLaunchKernelGGL((chunk_grad_kernel<64, true, false>), gc, blk, 0, s, a);
+        else                hipLaunchKernelGGL((chunk_grad_kernel<64, false, false>), gc, blk, 0, s, a);
     }
     return hipGetLastError();
 }

@@ -175,12 +175,14 @@ struct BwdArgs {
     float *dg, *dbeta;            // like g, beta
     float *dh0;                   // [B, H, D, D] or nullptr
     float *states, *dstates;      // workspace: [B, H, nc, D, D] each
+    void *recs;                   // workspace: one record per (b, h, chunk)
     int B, T, H, nc;
     float scale;
     int channel_gate;
 };
 hipError_t launch_backward(int D, const BwdArgs &a, hipStream_t s);
 hipError_t launch_copy_or_zero(float *dst, const float *src, size_t n, hipStream_t s);
+size_t backward_record_bytes(int D);
 
 hipError_t launch_prefill_recurrent(bool bf16_io, int D, const PrefillArgs &a,
                                     hipStream_t s);

@@ -339,11 +339,13 @@ gdr_status gdr_decode_tokens_fused(enum gdr_dtype dt, enum gdr_gate gk, int B, i
  *   workspace    device buffer of gdr_backward_workspace_bytes(gk, B, T, H,
  *                Dk, Dv) bytes (the state entering and the state gradient
  *                leaving every chunk of 64 tokens in fp32, the forward's own
- *                outputs and workspace), 16-byte aligned
+ *                outputs and workspace, and per chunk the bf16 matrices of
+ *                the state gradient's recurrence), 16-byte aligned
  *
  * Three stages: the chunked forward storing the state that enters every
- * chunk, the adjoint recurrence in reverse storing each chunk's state
- * gradient (and dh0), and one MFMA workgroup per (chunk, head) for the
+ * chunk; the state gradient's recurrence over chunks in reverse (its
+ * chunk-local matrices first, all chunks in parallel), storing each chunk's
+ * state gradient and dh0; and one MFMA workgroup per (chunk, head) for the
  * chunk-local gradients.  fp32 inputs are GDR_EUNSUPPORTED.
  * Numerics: bf16 operands with fp32 accumulation, as the forward.
  */
