@@ -193,31 +193,62 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(BwdArgs a) {
         sm.bs[lane] = wave_prefix_sum(gv);
     }
     if (tid < D) sm.dbC[tid] = 0.f;
+    // q, k and (channel gate) g of the chunk into LDS that steps 1-3 do not
+    // otherwise use (X, U, dU and Nf are contiguous), with 16-byte loads
+    // from all threads, all in flight together; rows past the end as zeros
+    char *stage = reinterpret_cast<char *>(sm.X);
+    bf16 *qst = reinterpret_cast<bf16 *>(stage);
+    bf16 *kst = reinterpret_cast<bf16 *>(stage + C * D * 2);
+    float *gst = reinterpret_cast<float *>(stage + 2 * C * D * 2);
+    static_assert(sizeof(sm.X) + sizeof(sm.U) + sizeof(sm.dU) + sizeof(sm.Nf) >= (size_t)C * D * 8,
+                  "staging of q, k, g");
+    {
+        constexpr int NQ = C * D / 8 / 256;          // 16-byte pieces of q per thread
+        constexpr int NG = CH ? C * D / 4 / 256 : 0;  // of g
+        bf16x8 qv[NQ], kv[NQ];
+        f32x4 gv[NG > 0 ? NG : 1];
+#pragma unroll
+        for (int it = 0; it < NQ; ++it) {
+            const int p = it * 256 + tid, r = p / (D / 8), j = 8 * (p % (D / 8));
+            qv[it] = kv[it] = bf16x8{};
+            if (r < Cc) {
+                qv[it] = *reinterpret_cast<const bf16x8 *>(qg + (size_t)r * rowD + j);
+                kv[it] = *reinterpret_cast<const bf16x8 *>(kg + (size_t)r * rowD + j);
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < NG; ++it) {
+            const int p = it * 256 + tid, r = p / (D / 4), j = 4 * (p % (D / 4));
+            gv[it] = r < Cc ? *reinterpret_cast<const f32x4 *>(gg + (size_t)r * gstr + j)
+                            : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int it = 0; it < NQ; ++it) {
+            const int p = it * 256 + tid, r = p / (D / 8), j = 8 * (p % (D / 8));
+            *reinterpret_cast<bf16x8 *>(qst + r * D + j) = qv[it];
+            *reinterpret_cast<bf16x8 *>(kst + r * D + j) = kv[it];
+        }
+#pragma unroll
+        for (int it = 0; it < NG; ++it) {
+            const int p = it * 256 + tid, r = p / (D / 4), j = 4 * (p % (D / 4));
+            *reinterpret_cast<f32x4 *>(gst + r * D + j) = gv[it];
+        }
+    }
     __syncthreads();
     if (tid < D) {
-        // one channel per thread, 16 rows of loads in flight at a time
+        // one channel per thread: the gate sums down the rows, the gated operands
         const int j = tid;
         float run = 0.f;
-        for (int r0 = 0; r0 < C; r0 += 16) {
-            float gv[16], qv[16], kv[16];
-#pragma unroll
-            for (int u = 0; u < 16; ++u) {
-                const int r = r0 + u;
-                gv[u] = CH && r < Cc ? gg[(size_t)r * gstr + j] : 0.f;
-                qv[u] = r < Cc ? (float)qg[(size_t)r * rowD + j] : 0.f;
-                kv[u] = r < Cc ? (float)kg[(size_t)r * rowD + j] : 0.f;
-            }
-#pragma unroll
-            for (int u = 0; u < 16; ++u) {
-                const int r = r0 + u;
-                run += gv[u];
-                const float e = ex(CH ? run : sm.bs[r]);
-                const float ei = __builtin_amdgcn_rcpf(e);
-                sm.Qt[r * PD + j] = (bf16)(qv[u] * e);
-                sm.Kt[r * PD + j] = (bf16)(kv[u] * e);
-                sm.Kb[r * PD + j] = (bf16)(kv[u] * ei);
-                if (r == C - 1) sm.eC[j] = e;
-            }
+#pragma unroll 8
+        for (int r = 0; r < C; ++r) {
+            if (CH) run += gst[r * D + j];
+            const float e = ex(CH ? run : sm.bs[r]);
+            const float ei = __builtin_amdgcn_rcpf(e);
+            const float qv = (float)qst[r * D + j], kv = (float)kst[r * D + j];
+            sm.Qt[r * PD + j] = (bf16)(qv * e);
+            sm.Kt[r * PD + j] = (bf16)(kv * e);
+            sm.Kb[r * PD + j] = (bf16)(kv * ei);
+            if (r == C - 1) sm.eC[j] = e;
         }
     }
     __syncthreads();
@@ -352,7 +383,16 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(BwdArgs a) {
         return;
     }
 
-    // ---- 4. X = V - Kt S0^T  (S0 [i][j] as the B operand of X Y^T)
+    // ---- 4. X = V - Kt S0^T  (S0 [i][j] as the B operand of X Y^T); V
+    //         first staged in X with 16-byte loads
+#pragma unroll
+    for (int it = 0; it < C * D / 8 / 256; ++it) {
+        const int p = it * 256 + tid, r = p / (D / 8), j = 8 * (p % (D / 8));
+        bf16x8 vv = {};
+        if (r < Cc) vv = *reinterpret_cast<const bf16x8 *>(vg + (size_t)r * rowD + j);
+        *reinterpret_cast<bf16x8 *>(&sm.X[r * PD + j]) = vv;
+    }
+    __syncthreads();
 #pragma unroll
     for (int cb = 0; cb < NB; ++cb) {
         f32x4 x = zero4();
@@ -364,8 +404,7 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(BwdArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int r = rowof(e);
-            const float vv = r < Cc ? (float)vg[(size_t)r * rowD + i] : 0.f;
-            sm.X[r * PD + i] = (bf16)(vv - x[e]);
+            sm.X[r * PD + i] = (bf16)((float)sm.X[r * PD + i] - x[e]);
         }
     }
     __syncthreads();
