@@ -61,10 +61,21 @@ template <int D> struct GradSmem {
     alignas(16) bf16 Qt[C * PD];      // q e^b            [r][j]
     alignas(16) bf16 Kt[C * PD];      // k e^b
     alignas(16) bf16 Kb[C * PD];      // k e^-b
-    alignas(16) bf16 X[C * PD];       // X, later dX      [r][i]
-    alignas(16) bf16 U[C * PD];
-    alignas(16) bf16 dU[C * PD];
-    alignas(16) float Nf[C * C];      // L, then N = (I + L)^{-1}  [r][s]
+    static constexpr int PQ = 32 + 8;  // row length of a C x 32 slice
+    // one region, used in turn by the steps
+    union alignas(16) {
+        char stage[C * D * 8];        // step 1: q, k (bf16) and g (fp32) of the chunk
+        struct {
+            float Nf[C * C];          // L, then N = (I + L)^{-1}  [r][s]
+            float L[9 * 256];         // blocks of L below the diagonal, products
+        } inv;                        // steps 2, 3
+        struct {                      // steps 4-13, 32 value columns i at a time
+            bf16 S0h[32 * PD], S0l[32 * PD];   // S0 rows i of the slice, hi + lo
+            bf16 dSh[32 * PD], dSl[32 * PD];   // dSg likewise
+            bf16 X[C * PQ], U[C * PQ], dU[C * PQ], dO[C * PQ], dX[C * PQ];   // [r][i]
+        } sl;
+        float db[C * D];              // step 16
+    } R;
     alignas(16) bf16 Tb[C * PC];      // T, later Y = dN N^T
     alignas(16) bf16 Pb[C * PC];      // P, later dN
     alignas(16) bf16 dPb[C * PC];     // dP, later dA
@@ -180,6 +191,7 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(BwdArgs a) {
     const size_t sbh = ((size_t)b * a.H + h) * a.nc + c;
     const float *S0 = a.states + sbh * D * D;                  // [i][j]
     const float *dSC = a.dstates + sbh * D * D;                // [i][j]
+    float *const Nf = sm.R.inv.Nf;
 
     // ---- 1. gate sums, gated operands, beta; zero the accumulators
     if (tid < C) {
@@ -194,14 +206,12 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(BwdArgs a) {
     }
     if (tid < D) sm.dbC[tid] = 0.f;
     // q, k and (channel gate) g of the chunk into LDS that steps 1-3 do not
-    // otherwise use (X, U, dU and Nf are contiguous), with 16-byte loads
+    // otherwise use, with 16-byte loads
     // from all threads, all in flight together; rows past the end as zeros
-    char *stage = reinterpret_cast<char *>(sm.X);
+    char *stage = sm.R.stage;
     bf16 *qst = reinterpret_cast<bf16 *>(stage);
     bf16 *kst = reinterpret_cast<bf16 *>(stage + C * D * 2);
     float *gst = reinterpret_cast<float *>(stage + 2 * C * D * 2);
-    static_assert(sizeof(sm.X) + sizeof(sm.U) + sizeof(sm.dU) + sizeof(sm.Nf) >= (size_t)C * D * 8,
-                  "staging of q, k, g");
     {
         constexpr int NQ = C * D / 8 / 256;          // 16-byte pieces of q per thread
         constexpr int NG = CH ? C * D / 4 / 256 : 0;  // of g
@@ -277,7 +287,7 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(BwdArgs a) {
             const int r = rowof(e);
             if (!(s < r)) av[e] = 0.f;
             if (!(s <= r)) pv[e] = 0.f;
-            sm.Nf[r * C + s] = sm.beta[r] * av[e];
+            Nf[r * C + s] = sm.beta[r] * av[e];
             sm.Pb[r * PC + s] = (bf16)pv[e];
         }
         Areg[J] = av;
@@ -285,21 +295,20 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(BwdArgs a) {
     __syncthreads();
 
     // ---- 3. N = (I + L)^{-1}, in fp32.  The 16x16 blocks of L below the
-    //         diagonal are saved (over U, free until step 5); the four
+    //         diagonal are saved; the four
     //         diagonal blocks are inverted by substitution, lane 16 b + c of
     //         wave 0 taking column c of block b; then the blocks below the
     //         diagonal, N_ij = -N_ii sum_{k=j}^{i-1} L_ik N_kj, one block
     //         diagonal i - j = d at a time, by 16x16 products on all threads
     {
-        float *Ls = reinterpret_cast<float *>(sm.U);   // [ltri(i, k)][16][16]
+        float *Ls = sm.R.inv.L;                        // [ltri(i, k)][16][16]
         float *Tm = Ls + 6 * 256;                      // [3][16][16]
-        static_assert(sizeof(sm.U) >= sizeof(float) * 9 * 256, "inverse scratch");
         const int tr = tid >> 4, tc = tid & 15;
 #pragma unroll
         for (int i = 1; i < 4; ++i)
 #pragma unroll
             for (int k = 0; k < i; ++k)
-                Ls[(i * (i - 1) / 2 + k) * 256 + tid] = sm.Nf[(16 * i + tr) * C + 16 * k + tc];
+                Ls[(i * (i - 1) / 2 + k) * 256 + tid] = Nf[(16 * i + tr) * C + 16 * k + tc];
         if (w == 0) {
             const int base = 16 * (lane >> 4), c = lane & 15;
             float n[16];
@@ -307,11 +316,11 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(BwdArgs a) {
             for (int r = 0; r < 16; ++r) {
                 float acc = r == c ? 1.f : 0.f;
 #pragma unroll
-                for (int m = 0; m < r; ++m) acc -= sm.Nf[(base + r) * C + base + m] * n[m];
+                for (int m = 0; m < r; ++m) acc -= Nf[(base + r) * C + base + m] * n[m];
                 n[r] = acc;
             }
 #pragma unroll
-            for (int r = 0; r < 16; ++r) sm.Nf[(base + r) * C + base + c] = n[r];
+            for (int r = 0; r < 16; ++r) Nf[(base + r) * C + base + c] = n[r];
         }
         __syncthreads();
         for (int d = 1; d < 4; ++d) {
@@ -322,7 +331,7 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(BwdArgs a) {
                     const float *L = Ls + (ib * (ib - 1) / 2 + kb) * 256;
 #pragma unroll
                     for (int m = 0; m < 16; ++m)
-                        acc += L[tr * 16 + m] * sm.Nf[(16 * kb + m) * C + 16 * jb + tc];
+                        acc += L[tr * 16 + m] * Nf[(16 * kb + m) * C + 16 * jb + tc];
                 }
                 Tm[jb * 256 + tid] = acc;
             }
@@ -332,15 +341,15 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(BwdArgs a) {
                 float acc = 0.f;
 #pragma unroll
                 for (int m = 0; m < 16; ++m)
-                    acc += sm.Nf[(16 * ib + tr) * C + 16 * ib + m] * Tm[jb * 256 + m * 16 + tc];
-                sm.Nf[(16 * ib + tr) * C + 16 * jb + tc] = -acc;
+                    acc += Nf[(16 * ib + tr) * C + 16 * ib + m] * Tm[jb * 256 + m * 16 + tc];
+                Nf[(16 * ib + tr) * C + 16 * jb + tc] = -acc;
             }
             __syncthreads();
         }
     }
     for (int e = tid; e < C * C; e += 256) {
         const int r = e / C, s = e % C;
-        const float nv = sm.Nf[e];
+        const float nv = Nf[e];
         const float tv = nv * sm.beta[s];
         const bf16 tb = (bf16)tv;
         sm.Nb[r * PC + s] = (bf16)nv;
@@ -383,142 +392,168 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(BwdArgs a) {
         return;
     }
 
-    // ---- 4. X = V - Kt S0^T  (S0 [i][j] as the B operand of X Y^T); V
-    //         first staged in X with 16-byte loads
+    // ---- 4-13. The products with S0 and dSg, 32 value columns i at a
+    //         time.  Each slice -- rows i of S0 and dSg (as hi + lo bf16,
+    //         dSg = dS_C with the column scale e^{b_C}) and columns i of V
+    //         and dO -- is staged in LDS once, the next slice's loads in
+    //         flight meanwhile.  X, U, dU and dX = dV are column-local
+    //         (U = T X, dX = T^T dU), so only their slice is kept; the
+    //         products over i (dT, dP, dQt, dKt, dKbh) accumulate in
+    //         registers.  db_C's S0 part, sum_i dSg_i.S0_i, is summed from
+    //         the fp32 loads.
+    float Nreg[4][4];                          // N of this wave's blocks, in fp32
 #pragma unroll
-    for (int it = 0; it < C * D / 8 / 256; ++it) {
-        const int p = it * 256 + tid, r = p / (D / 8), j = 8 * (p % (D / 8));
-        bf16x8 vv = {};
-        if (r < Cc) vv = *reinterpret_cast<const bf16x8 *>(vg + (size_t)r * rowD + j);
-        *reinterpret_cast<bf16x8 *>(&sm.X[r * PD + j]) = vv;
-    }
-    __syncthreads();
+    for (int J = 0; J < 4; ++J)
 #pragma unroll
-    for (int cb = 0; cb < NB; ++cb) {
-        f32x4 x = zero4();
+        for (int e = 0; e < 4; ++e) Nreg[J][e] = Nf[rowof(e) * C + 16 * J + l15];
+    __syncthreads();                           // Nf no longer read
+
+    auto &sl = sm.R.sl;
+    constexpr int PQ = Sm::PQ;
+    constexpr int NS4 = 32 * D / 4 / 256;      // 16-byte pieces of a state slice per thread
+    f32x4 ps[NS4], pd[NS4];
+    bf16x8 pv, po;
+    float dbc[4] = {0.f, 0.f, 0.f, 0.f};       // columns jc .. jc + 3 of db_C
+    const int jc = 4 * (tid % (D / 4));
+    const int vr = tid >> 2, vc = 8 * (tid & 3);   // V, dO slice: row, column in the slice
+    auto fetch = [&](int sc) {
 #pragma unroll
-        for (int kk = 0; kk < KD; ++kk)
-            x = mfma_ab2(frag_rows(sm.Kt, PD, 16 * I, 32 * kk, lane),
-                         g_rows_f32(S0, D, 16 * cb, 32 * kk, lane, nullptr), x);
-        const int i = 16 * cb + l15;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int r = rowof(e);
-            sm.X[r * PD + i] = (bf16)((float)sm.X[r * PD + i] - x[e]);
+        for (int it = 0; it < NS4; ++it) {
+            const int ii = (it * 256 + tid) / (D / 4);
+            const size_t o = (size_t)(32 * sc + ii) * D + jc;
+            ps[it] = *reinterpret_cast<const f32x4 *>(S0 + o);
+            pd[it] = *reinterpret_cast<const f32x4 *>(dSC + o);
         }
-    }
-    __syncthreads();
-
-    // ---- 5. U = T X
-#pragma unroll
-    for (int cb = 0; cb < NB; ++cb) {
-        f32x4 u = zero4();
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-            u = mfma32(frag_rows(sm.Tb, PC, 16 * I, 32 * kk, lane), frag_cols(sm.X, PD, 32 * kk, 16 * cb, lane), u);
-        const int i = 16 * cb + l15;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int r = rowof(e);
-            sm.U[r * PD + i] = (bf16)(u[e] + sm.tcor[r] * (float)sm.X[r * PD + i]);
+        pv = po = bf16x8{};
+        if (vr < Cc) {
+            pv = *reinterpret_cast<const bf16x8 *>(vg + (size_t)vr * rowD + 32 * sc + vc);
+            po = *reinterpret_cast<const bf16x8 *>(dog + (size_t)vr * rowD + 32 * sc + vc);
         }
-    }
-    __syncthreads();
+    };
+    auto put = [&]() {
+        const f32x4 ec = *reinterpret_cast<const f32x4 *>(&sm.eC[jc]);
+#pragma unroll
+        for (int it = 0; it < NS4; ++it) {
+            const int ii = (it * 256 + tid) / (D / 4);
+            bf16x4 sh, sl4, dh, dl;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float sv = ps[it][u], dv = pd[it][u] * ec[u];
+                dbc[u] += sv * dv;
+                sh[u] = (bf16)sv;
+                sl4[u] = (bf16)(sv - (float)sh[u]);
+                dh[u] = (bf16)dv;
+                dl[u] = (bf16)(dv - (float)dh[u]);
+            }
+            *reinterpret_cast<bf16x4 *>(&sl.S0h[ii * PD + jc]) = sh;
+            *reinterpret_cast<bf16x4 *>(&sl.S0l[ii * PD + jc]) = sl4;
+            *reinterpret_cast<bf16x4 *>(&sl.dSh[ii * PD + jc]) = dh;
+            *reinterpret_cast<bf16x4 *>(&sl.dSl[ii * PD + jc]) = dl;
+        }
+        *reinterpret_cast<bf16x8 *>(&sl.X[vr * PQ + vc]) = pv;
+        *reinterpret_cast<bf16x8 *>(&sl.dO[vr * PQ + vc]) = po;
+    };
 
-    // ---- 6. dU = Kb dSg^T + scale P^T dO
+    f32x4 dQt[NB], dKt[NB], dKb[NB], dKbh[NB], dPa[4], dTa[4];
 #pragma unroll
-    for (int cb = 0; cb < NB; ++cb) {
-        f32x4 d1 = zero4(), d2 = zero4();
+    for (int cb = 0; cb < NB; ++cb) dQt[cb] = dKt[cb] = dKbh[cb] = zero4();
 #pragma unroll
-        for (int kk = 0; kk < KD; ++kk)
-            d1 = mfma_ab2(frag_rows(sm.Kb, PD, 16 * I, 32 * kk, lane),
-                          g_rows_f32(dSC, D, 16 * cb, 32 * kk, lane, sm.eC), d1);
+    for (int J = 0; J < 4; ++J) dPa[J] = dTa[J] = zero4();
+    fetch(0);
+    for (int sc = 0; sc < D / 32; ++sc) {
+        put();
+        if (sc + 1 < D / 32) fetch(sc + 1);
+        __syncthreads();
+        // X = V - Kt S0^T and dU = Kb dSg^T + scale P^T dO on the slice
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-            d2 = mfma32(frag_cols(sm.Pb, PC, 32 * kk, 16 * I, lane),
-                        g_cols_bf(dog, rowD, 32 * kk, 16 * cb, lane, Cc), d2);
-        const int i = 16 * cb + l15;
+        for (int cl = 0; cl < 2; ++cl) {
+            f32x4 x = zero4(), du = zero4(), dp = zero4();
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sm.dU[rowof(e) * PD + i] = (bf16)(d1[e] + a.scale * d2[e]);
+            for (int kk = 0; kk < KD; ++kk) {
+                x = mfma_ab2(frag_rows(sm.Kt, PD, 16 * I, 32 * kk, lane),
+                             Frag2{frag_rows(sl.S0h, PD, 16 * cl, 32 * kk, lane),
+                                   frag_rows(sl.S0l, PD, 16 * cl, 32 * kk, lane)}, x);
+                du = mfma_ab2(frag_rows(sm.Kb, PD, 16 * I, 32 * kk, lane),
+                              Frag2{frag_rows(sl.dSh, PD, 16 * cl, 32 * kk, lane),
+                                    frag_rows(sl.dSl, PD, 16 * cl, 32 * kk, lane)}, du);
+            }
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+                dp = mfma32(frag_cols(sm.Pb, PC, 32 * kk, 16 * I, lane), frag_cols(sl.dO, PQ, 32 * kk, 16 * cl, lane), dp);
+            const int il = 16 * cl + l15;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = rowof(e);
+                sl.X[r * PQ + il] = (bf16)((float)sl.X[r * PQ + il] - x[e]);
+                sl.dU[r * PQ + il] = (bf16)(du[e] + a.scale * dp[e]);
+            }
+        }
+        __syncthreads();
+        // U = T X, dX = T^T dU (= dV; the diagonal of T compensated), dT += dU X^T
+#pragma unroll
+        for (int cl = 0; cl < 2; ++cl) {
+            f32x4 u = zero4(), dx = zero4();
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                u = mfma32(frag_rows(sm.Tb, PC, 16 * I, 32 * kk, lane), frag_cols(sl.X, PQ, 32 * kk, 16 * cl, lane), u);
+                dx = mfma32(frag_cols(sm.Tb, PC, 32 * kk, 16 * I, lane), frag_cols(sl.dU, PQ, 32 * kk, 16 * cl, lane), dx);
+            }
+            const int il = 16 * cl + l15, i = 32 * sc + il;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = rowof(e);
+                sl.U[r * PQ + il] = (bf16)(u[e] + sm.tcor[r] * (float)sl.X[r * PQ + il]);
+                const float dxv = dx[e] + sm.tcor[r] * (float)sl.dU[r * PQ + il];
+                sl.dX[r * PQ + il] = (bf16)dxv;
+                if (r < Cc) a.dv[((tok0 + r) * a.H + h) * D + i] = dxv;
+            }
+        }
+        {
+            const bf16x8 du = frag_rows(sl.dU, PQ, 16 * I, 0, lane);
+#pragma unroll
+            for (int J = 0; J < 4; ++J)
+                if (J <= I) dTa[J] = mfma32(du, frag_rows(sl.X, PQ, 16 * J, 0, lane), dTa[J]);
+        }
+        __syncthreads();
+        // dP += dO U^T;  over the slice's rows of S0 and dSg: dQt += dO S0,
+        // dKt += dX S0 (negated below), dKbh += U dSg
+        {
+            const bf16x8 ao = frag_rows(sl.dO, PQ, 16 * I, 0, lane);
+            const bf16x8 ax = frag_rows(sl.dX, PQ, 16 * I, 0, lane);
+            const bf16x8 au = frag_rows(sl.U, PQ, 16 * I, 0, lane);
+#pragma unroll
+            for (int J = 0; J < 4; ++J)
+                if (J <= I) dPa[J] = mfma32(ao, frag_rows(sl.U, PQ, 16 * J, 0, lane), dPa[J]);
+#pragma unroll
+            for (int cb = 0; cb < NB; ++cb) {
+                const Frag2 s0{frag_cols(sl.S0h, PD, 0, 16 * cb, lane), frag_cols(sl.S0l, PD, 0, 16 * cb, lane)};
+                dQt[cb] = mfma_ab2(ao, s0, dQt[cb]);
+                dKt[cb] = mfma_ab2(ax, s0, dKt[cb]);
+                dKbh[cb] = mfma_ab2(au, Frag2{frag_cols(sl.dSh, PD, 0, 16 * cb, lane),
+                                              frag_cols(sl.dSl, PD, 0, 16 * cb, lane)}, dKbh[cb]);
+            }
+        }
+        __syncthreads();
     }
-
-    // ---- 7. dKbh = U dSg (the Kh part of dKb, kept apart for dg)
-    f32x4 dQt[NB], dKt[NB], dKb[NB], dKbh[NB];
 #pragma unroll
-    for (int cb = 0; cb < NB; ++cb) {
-        f32x4 x = zero4();
-#pragma unroll
-        for (int kk = 0; kk < KD; ++kk)
-            x = mfma_ab2(frag_rows(sm.U, PD, 16 * I, 32 * kk, lane),
-                         g_cols_f32(dSC, D, 32 * kk, 16 * cb, lane, sm.eC[16 * cb + l15]), x);
-        dKbh[cb] = x;
-        dKb[cb] = zero4();
-    }
-    __syncthreads();
+    for (int u = 0; u < 4; ++u) atomicAdd(&sm.dbC[jc + u], dbc[u]);
 
-    // ---- 8. dP = scale lower(dO U^T)
+    // ---- 8, 11. dP = scale lower(dO U^T) (its diagonal's rounding kept);
+    //         dT = lower(dU X^T): dbeta_s += sum_r dT_rs N_rs, dN = dT diag(beta)
 #pragma unroll
     for (int J = 0; J < 4; ++J) {
-        f32x4 p = zero4();
-        if (J <= I) {
-#pragma unroll
-            for (int kk = 0; kk < KD; ++kk)
-                p = mfma32(g_rows_bf(dog, rowD, 16 * I, 32 * kk, lane, Cc),
-                           frag_rows(sm.U, PD, 16 * J, 32 * kk, lane), p);
-        }
-        const int s = 16 * J + l15;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int r = rowof(e);
-            const float pv = s <= r ? a.scale * p[e] : 0.f;
-            const bf16 pb = (bf16)pv;
-            sm.dPb[r * PC + s] = pb;
-            if (s == r) sm.pcor[r] = pv - (float)pb;
-        }
-    }
-    __syncthreads();
-
-    // ---- 9, 10. dQt = scale dO S0 + dP Kb;  dKb += dP^T Qt
-#pragma unroll
-    for (int cb = 0; cb < NB; ++cb) {
-        f32x4 x = zero4(), y = zero4();
-#pragma unroll
-        for (int kk = 0; kk < KD; ++kk)
-            x = mfma_ab2(g_rows_bf(dog, rowD, 16 * I, 32 * kk, lane, Cc),
-                         g_cols_f32(S0, D, 32 * kk, 16 * cb, lane, 1.f), x);
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            y = mfma32(frag_rows(sm.dPb, PC, 16 * I, 32 * kk, lane), frag_cols(sm.Kb, PD, 32 * kk, 16 * cb, lane), y);
-            dKb[cb] = mfma32(frag_cols(sm.dPb, PC, 32 * kk, 16 * I, lane),
-                             frag_cols(sm.Qt, PD, 32 * kk, 16 * cb, lane), dKb[cb]);
-        }
-        dQt[cb] = a.scale * x + y;
-        const int j = 16 * cb + l15;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int r = rowof(e);
-            dQt[cb][e] += sm.pcor[r] * (float)sm.Kb[r * PD + j];
-            dKb[cb][e] += sm.pcor[r] * (float)sm.Qt[r * PD + j];
-        }
-    }
-
-    // ---- 11. dT = lower(dU X^T); dbeta_s += sum_r dT_rs N_rs; dN = dT diag(beta)
-#pragma unroll
-    for (int J = 0; J < 4; ++J) {
-        f32x4 t = zero4();
-        if (J <= I) {
-#pragma unroll
-            for (int kk = 0; kk < KD; ++kk)
-                t = mfma32(frag_rows(sm.dU, PD, 16 * I, 32 * kk, lane), frag_rows(sm.X, PD, 16 * J, 32 * kk, lane), t);
-        }
         const int s = 16 * J + l15;
         const float bs_ = sm.beta[s];
         float part = 0.f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int r = rowof(e);
-            const float tv = s <= r ? t[e] : 0.f;
-            part += tv * sm.Nf[r * C + s];
+            const float pv = s <= r ? a.scale * dPa[J][e] : 0.f;
+            const bf16 pb = (bf16)pv;
+            sm.dPb[r * PC + s] = pb;
+            if (s == r) sm.pcor[r] = pv - (float)pb;
+            const float tv = s <= r ? dTa[J][e] : 0.f;
+            part += tv * Nreg[J][e];
             sm.Pb[r * PC + s] = (bf16)(tv * bs_);
         }
         part = sum_quads(part);
@@ -526,40 +561,26 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(BwdArgs a) {
     }
     __syncthreads();
 
-    // ---- 12. dX = T^T dU (= dV), kept in X;  13. dKt = -dX S0
-    f32x4 dX[NB];
+    // ---- 9, 10. dQt = scale dO S0 + dP Kb;  dKb = dP^T Qt;  dKt = -dX S0
 #pragma unroll
     for (int cb = 0; cb < NB; ++cb) {
-        f32x4 x = zero4();
+        f32x4 y = zero4();
+        dKb[cb] = zero4();
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-            x = mfma32(frag_cols(sm.Tb, PC, 32 * kk, 16 * I, lane), frag_cols(sm.dU, PD, 32 * kk, 16 * cb, lane), x);
-        const int i = 16 * cb + l15;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] += sm.tcor[rowof(e)] * (float)sm.dU[rowof(e) * PD + i];
-        dX[cb] = x;
+        for (int kk = 0; kk < 2; ++kk) {
+            y = mfma32(frag_rows(sm.dPb, PC, 16 * I, 32 * kk, lane), frag_cols(sm.Kb, PD, 32 * kk, 16 * cb, lane), y);
+            dKb[cb] = mfma32(frag_cols(sm.dPb, PC, 32 * kk, 16 * I, lane),
+                             frag_cols(sm.Qt, PD, 32 * kk, 16 * cb, lane), dKb[cb]);
+        }
+        dQt[cb] = a.scale * dQt[cb] + y;
+        dKt[cb] = -dKt[cb];
+        const int j = 16 * cb + l15;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int r = rowof(e);
-            if (r < Cc) a.dv[((tok0 + r) * a.H + h) * D + i] = x[e];
+            dQt[cb][e] += sm.pcor[r] * (float)sm.Kb[r * PD + j];
+            dKb[cb][e] += sm.pcor[r] * (float)sm.Qt[r * PD + j];
         }
-    }
-    __syncthreads();                           // X and T no longer read
-#pragma unroll
-    for (int cb = 0; cb < NB; ++cb) {
-        const int i = 16 * cb + l15;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sm.X[rowof(e) * PD + i] = (bf16)dX[cb][e];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int cb = 0; cb < NB; ++cb) {
-        f32x4 x = zero4();
-#pragma unroll
-        for (int kk = 0; kk < KD; ++kk)
-            x = mfma_ab2(frag_rows(sm.X, PD, 16 * I, 32 * kk, lane),
-                         g_cols_f32(S0, D, 32 * kk, 16 * cb, lane, 1.f), x);
-        dKt[cb] = -x;
     }
 
     // ---- 14. Y = dN N^T (into Tb), dM = -N^T Y;  dbeta_r += sum_s dM_rs A_rs;
@@ -615,10 +636,9 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(BwdArgs a) {
     //          that the pairs of terms that cancel exactly in dg -- a P or A
     //          entry seen from its row and from its column -- cancel to fp32
     //          accuracy); then E; dq, dk; dg by reverse sums; dbeta
-    float *dbf = reinterpret_cast<float *>(sm.U);    // db [r][j] (channel gate), over U, dU
+    float *dbf = sm.R.db;                            // db [r][j] (channel gate)
     float *hf = reinterpret_cast<float *>(sm.Tb);    // h [r][j] (channel gate), over Tb..Nb
     float *Ef = reinterpret_cast<float *>(sm.Qt);    // e^b [r][j] (channel gate), over Qt, Kt
-    static_assert(sizeof(sm.U) + sizeof(sm.dU) >= sizeof(float) * C * D, "db overlay");
     static_assert(sizeof(sm.Tb) + sizeof(sm.Pb) + sizeof(sm.dPb) + sizeof(sm.Nb) >= sizeof(float) * C * D,
                   "h overlay");
     static_assert(sizeof(sm.Qt) + sizeof(sm.Kt) >= sizeof(float) * C * D, "E overlay");
@@ -685,13 +705,6 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(BwdArgs a) {
                 a.dk[o] = dKt[cb][e] * E + (dKb[cb][e] + dKbh[cb][e]) * Ei;
             }
         }
-    }
-    // db_C (the Kh part is in h): sum_i dSg_i (.) S0_i
-    if (tid < D) {
-        float acc = 0.f;
-#pragma unroll 16
-        for (int i = 0; i < D; ++i) acc += dSC[(size_t)i * D + tid] * S0[(size_t)i * D + tid];
-        atomicAdd(&sm.dbC[tid], acc * sm.eC[tid]);
     }
     __syncthreads();
     if (CH) {
