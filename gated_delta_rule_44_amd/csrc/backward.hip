@@ -799,9 +799,35 @@ __global__ __launch_bounds__(256) void adjoint_chain_kernel(BwdArgs a) {
             dS[t][e] = a.dht ? a.dht[o] : 0.f;
         }
     }
+    // the next chunk's record and dO slice, in registers while this one is
+    // worked on
+    constexpr int NR = C * D / 8 / 256, NP = C * C / 8 / 256;
+    bf16x8 rq[NR], rk[NR], rw[NR], rp[NP], rdo;
+    float rec_ = 0.f;
+    auto fetch = [&](int c) {
+        const char *rec = static_cast<const char *>(a.recs) + (bh * a.nc + c) * R::BYTES;
+#pragma unroll
+        for (int it = 0; it < NR; ++it) {
+            const int p = it * 256 + tid, r = p / (D / 8), j = 8 * (p % (D / 8));
+            rq[it] = *reinterpret_cast<const bf16x8 *>(rec + R::QT + 2 * (r * D + j));
+            rk[it] = *reinterpret_cast<const bf16x8 *>(rec + R::KB + 2 * (r * D + j));
+            rw[it] = *reinterpret_cast<const bf16x8 *>(rec + R::W + 2 * (r * D + j));
+        }
+#pragma unroll
+        for (int it = 0; it < NP; ++it) {
+            const int p = it * 256 + tid, r = p / (C / 8), sc = 8 * (p % (C / 8));
+            rp[it] = *reinterpret_cast<const bf16x8 *>(rec + R::P + 2 * (r * C + sc));
+        }
+        if (tid < D) rec_ = reinterpret_cast<const float *>(rec + R::EC)[tid];
+        const int t0 = c * C, r = tid >> 2;                 // 64 rows x 4 pieces of 8
+        rdo = bf16x8{};
+        if (r < a.T - t0)
+            rdo = *reinterpret_cast<const bf16x8 *>(static_cast<const bf16 *>(a.dout) +
+                                                    (((size_t)b * a.T + t0 + r) * a.H + h) * D + i0 + 8 * (tid & 3));
+    };
+    static_assert(C * D / 8 % 256 == 0 && C * C / 8 % 256 == 0, "record pieces per thread");
+    if (a.nc > 0) fetch(a.nc - 1);
     for (int c = a.nc - 1; c >= 0; --c) {
-        const int t0 = c * C;
-        const int Cc = a.T - t0 < C ? a.T - t0 : C;
         // dS_C of chunk c
         float *dsc = a.dstates + (bh * a.nc + c) * D * D;
 #pragma unroll
@@ -809,27 +835,22 @@ __global__ __launch_bounds__(256) void adjoint_chain_kernel(BwdArgs a) {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 dsc[(size_t)(i0 + 16 * ib + 4 * q4 + e) * D + 16 * (jb0 + t) + l15] = dS[t][e];
-        // stage the record and the dO slice
-        const char *rec = static_cast<const char *>(a.recs) + (bh * a.nc + c) * R::BYTES;
-        for (int p = tid; p < C * D / 8; p += 256) {
-            const int r = p / (D / 8), j = 8 * (p % (D / 8));
-            *reinterpret_cast<bf16x8 *>(&sm.Qt[r * PD + j]) = *reinterpret_cast<const bf16x8 *>(rec + R::QT + 2 * (r * D + j));
-            *reinterpret_cast<bf16x8 *>(&sm.Kb[r * PD + j]) = *reinterpret_cast<const bf16x8 *>(rec + R::KB + 2 * (r * D + j));
-            *reinterpret_cast<bf16x8 *>(&sm.W[r * PD + j]) = *reinterpret_cast<const bf16x8 *>(rec + R::W + 2 * (r * D + j));
+        // stage the record and the dO slice (loaded during the previous chunk)
+#pragma unroll
+        for (int it = 0; it < NR; ++it) {
+            const int p = it * 256 + tid, r = p / (D / 8), j = 8 * (p % (D / 8));
+            *reinterpret_cast<bf16x8 *>(&sm.Qt[r * PD + j]) = rq[it];
+            *reinterpret_cast<bf16x8 *>(&sm.Kb[r * PD + j]) = rk[it];
+            *reinterpret_cast<bf16x8 *>(&sm.W[r * PD + j]) = rw[it];
         }
-        for (int p = tid; p < C * C / 8; p += 256) {
-            const int r = p / (C / 8), sc = 8 * (p % (C / 8));
-            *reinterpret_cast<bf16x8 *>(&sm.P[r * PC + sc]) = *reinterpret_cast<const bf16x8 *>(rec + R::P + 2 * (r * C + sc));
+#pragma unroll
+        for (int it = 0; it < NP; ++it) {
+            const int p = it * 256 + tid, r = p / (C / 8), sc = 8 * (p % (C / 8));
+            *reinterpret_cast<bf16x8 *>(&sm.P[r * PC + sc]) = rp[it];
         }
-        if (tid < D) sm.eC[tid] = reinterpret_cast<const float *>(rec + R::EC)[tid];
-        {
-            const int r = tid >> 2, seg = 8 * (tid & 3);      // 64 rows x 4 pieces of 8
-            bf16x8 v = {};
-            if (r < Cc)
-                v = *reinterpret_cast<const bf16x8 *>(static_cast<const bf16 *>(a.dout) +
-                                                      (((size_t)b * a.T + t0 + r) * a.H + h) * D + i0 + seg);
-            *reinterpret_cast<bf16x8 *>(&sm.dO[r * PV + seg]) = v;
-        }
+        if (tid < D) sm.eC[tid] = rec_;
+        *reinterpret_cast<bf16x8 *>(&sm.dO[(tid >> 2) * PV + 8 * (tid & 3)]) = rdo;
+        if (c > 0) fetch(c - 1);
         __syncthreads();
         // dSg = dS e^{b_C} as hi + lo bf16
 #pragma unroll
