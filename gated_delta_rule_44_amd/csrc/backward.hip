@@ -205,27 +205,26 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(BwdArgs a) {
         sm.bs[lane] = wave_prefix_sum(gv);
     }
     if (tid < D) sm.dbC[tid] = 0.f;
-    // q, k and (channel gate) g of the chunk into LDS that steps 1-3 do not
-    // otherwise use, with 16-byte loads
-    // from all threads, all in flight together; rows past the end as zeros
-    char *stage = sm.R.stage;
-    bf16 *qst = reinterpret_cast<bf16 *>(stage);
-    bf16 *kst = reinterpret_cast<bf16 *>(stage + C * D * 2);
-    float *gst = reinterpret_cast<float *>(stage + 2 * C * D * 2);
-    {
-        constexpr int NQ = C * D / 8 / 256;          // 16-byte pieces of q per thread
-        constexpr int NG = CH ? C * D / 4 / 256 : 0;  // of g
-        bf16x8 qv[NQ], kv[NQ];
-        f32x4 gv[NG > 0 ? NG : 1];
+    // q and k of the chunk in registers (16-byte loads from all threads, all
+    // in flight together), the channel gate g in LDS, rows past the end as
+    // zeros
+    constexpr int NQ = C * D / 8 / 256;        // 16-byte pieces of q per thread
+    float *gst = reinterpret_cast<float *>(sm.R.stage);        // g, then b  [r][j]
+    float *gtot = gst + C * D;                                 // part sums of g
+    static_assert(sizeof(sm.R) >= sizeof(float) * (C * D + 256), "gate staging");
+    bf16x8 qv[NQ], kv[NQ];
 #pragma unroll
-        for (int it = 0; it < NQ; ++it) {
-            const int p = it * 256 + tid, r = p / (D / 8), j = 8 * (p % (D / 8));
-            qv[it] = kv[it] = bf16x8{};
-            if (r < Cc) {
-                qv[it] = *reinterpret_cast<const bf16x8 *>(qg + (size_t)r * rowD + j);
-                kv[it] = *reinterpret_cast<const bf16x8 *>(kg + (size_t)r * rowD + j);
-            }
+    for (int it = 0; it < NQ; ++it) {
+        const int p = it * 256 + tid, r = p / (D / 8), j = 8 * (p % (D / 8));
+        qv[it] = kv[it] = bf16x8{};
+        if (r < Cc) {
+            qv[it] = *reinterpret_cast<const bf16x8 *>(qg + (size_t)r * rowD + j);
+            kv[it] = *reinterpret_cast<const bf16x8 *>(kg + (size_t)r * rowD + j);
         }
+    }
+    if constexpr (CH) {
+        constexpr int NG = C * D / 4 / 256;
+        f32x4 gv[NG];
 #pragma unroll
         for (int it = 0; it < NG; ++it) {
             const int p = it * 256 + tid, r = p / (D / 4), j = 4 * (p % (D / 4));
@@ -233,32 +232,61 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(BwdArgs a) {
                             : f32x4{0.f, 0.f, 0.f, 0.f};
         }
 #pragma unroll
-        for (int it = 0; it < NQ; ++it) {
-            const int p = it * 256 + tid, r = p / (D / 8), j = 8 * (p % (D / 8));
-            *reinterpret_cast<bf16x8 *>(qst + r * D + j) = qv[it];
-            *reinterpret_cast<bf16x8 *>(kst + r * D + j) = kv[it];
-        }
-#pragma unroll
         for (int it = 0; it < NG; ++it) {
             const int p = it * 256 + tid, r = p / (D / 4), j = 4 * (p % (D / 4));
             *reinterpret_cast<f32x4 *>(gst + r * D + j) = gv[it];
         }
+        __syncthreads();
+        // b = running sums of g down the rows: 256 / D parts of the rows per
+        // channel, each summed by one thread, then offset by the parts above
+        constexpr int NH = 256 / D, RH = C / NH;
+        const int j = tid % D, part = tid / D;
+        float rs[RH], run = 0.f;
+#pragma unroll
+        for (int u = 0; u < RH; ++u) {
+            run += gst[(part * RH + u) * D + j];
+            rs[u] = run;
+        }
+        gtot[part * D + j] = run;
+        __syncthreads();
+        float off = 0.f;
+        for (int q = 0; q < part; ++q) off += gtot[q * D + j];
+#pragma unroll
+        for (int u = 0; u < RH; ++u) gst[(part * RH + u) * D + j] = rs[u] + off;
     }
     __syncthreads();
-    if (tid < D) {
-        // one channel per thread: the gate sums down the rows, the gated operands
-        const int j = tid;
-        float run = 0.f;
-#pragma unroll 8
-        for (int r = 0; r < C; ++r) {
-            if (CH) run += gst[r * D + j];
-            const float e = ex(CH ? run : sm.bs[r]);
-            const float ei = __builtin_amdgcn_rcpf(e);
-            const float qv = (float)qst[r * D + j], kv = (float)kst[r * D + j];
-            sm.Qt[r * PD + j] = (bf16)(qv * e);
-            sm.Kt[r * PD + j] = (bf16)(kv * e);
-            sm.Kb[r * PD + j] = (bf16)(kv * ei);
-            if (r == C - 1) sm.eC[j] = e;
+    // gated operands Qt = q e^b, Kt = k e^b, Kb = k e^-b
+#pragma unroll
+    for (int it = 0; it < NQ; ++it) {
+        const int p = it * 256 + tid, r = p / (D / 8), j = 8 * (p % (D / 8));
+        float e[8];
+        if constexpr (CH) {
+            const f32x4 b0 = *reinterpret_cast<const f32x4 *>(gst + r * D + j);
+            const f32x4 b1 = *reinterpret_cast<const f32x4 *>(gst + r * D + j + 4);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                e[u] = ex(b0[u]);
+                e[u + 4] = ex(b1[u]);
+            }
+        } else {
+            const float er = ex(sm.bs[r]);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) e[u] = er;
+        }
+        bf16x8 qt, kt, kb;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const float qf = (float)qv[it][u], kf = (float)kv[it][u];
+            qt[u] = (bf16)(qf * e[u]);
+            kt[u] = (bf16)(kf * e[u]);
+            kb[u] = (bf16)(kf * __builtin_amdgcn_rcpf(e[u]));
+        }
+        *reinterpret_cast<bf16x8 *>(&sm.Qt[r * PD + j]) = qt;
+        *reinterpret_cast<bf16x8 *>(&sm.Kt[r * PD + j]) = kt;
+        *reinterpret_cast<bf16x8 *>(&sm.Kb[r * PD + j]) = kb;
+        if (r == C - 1) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) sm.eC[j + u] = e[u];
         }
     }
     __syncthreads();
@@ -299,7 +327,7 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(BwdArgs a) {
     //         diagonal blocks are inverted by substitution, lane 16 b + c of
     //         wave 0 taking column c of block b; then the blocks below the
     //         diagonal, N_ij = -N_ii sum_{k=j}^{i-1} L_ik N_kj, one block
-    //         diagonal i - j = d at a time, by 16x16 products on all threads
+    //         diagonal i - j = d at a time
     {
         float *Ls = sm.R.inv.L;                        // [ltri(i, k)][16][16]
         float *Tm = Ls + 6 * 256;                      // [3][16][16]
@@ -323,26 +351,33 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(BwdArgs a) {
             for (int r = 0; r < 16; ++r) Nf[(base + r) * C + base + c] = n[r];
         }
         __syncthreads();
+        // wave w takes block (w + d, w), on fp32 MFMAs (16x16x4: lane l holds
+        // A[l & 15][l >> 4], B[l >> 4][l & 15]); the product L N through a
+        // wave-private block of LDS into the layout of an operand
         for (int d = 1; d < 4; ++d) {
-            for (int jb = 0; jb + d < 4; ++jb) {
-                const int ib = jb + d;
-                float acc = 0.f;
+            const int jb = w, ib = w + d;
+            if (ib < 4) {
+                float *Tw = Tm + w * 256;
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
                 for (int kb = jb; kb < ib; ++kb) {
                     const float *L = Ls + (ib * (ib - 1) / 2 + kb) * 256;
 #pragma unroll
-                    for (int m = 0; m < 16; ++m)
-                        acc += L[tr * 16 + m] * Nf[(16 * kb + m) * C + 16 * jb + tc];
+                    for (int kk = 0; kk < 4; ++kk)
+                        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(L[l15 * 16 + 4 * kk + q4],
+                                                                   Nf[(16 * kb + 4 * kk + q4) * C + 16 * jb + l15], acc, 0, 0, 0);
                 }
-                Tm[jb * 256 + tid] = acc;
-            }
-            __syncthreads();
-            for (int jb = 0; jb + d < 4; ++jb) {
-                const int ib = jb + d;
-                float acc = 0.f;
 #pragma unroll
-                for (int m = 0; m < 16; ++m)
-                    acc += Nf[(16 * ib + tr) * C + 16 * ib + m] * Tm[jb * 256 + m * 16 + tc];
-                Nf[(16 * ib + tr) * C + 16 * jb + tc] = -acc;
+                for (int e = 0; e < 4; ++e) Tw[(4 * q4 + e) * 16 + l15] = acc[e];
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                f32x4 n = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk)
+                    n = __builtin_amdgcn_mfma_f32_16x16x4f32(Nf[(16 * ib + l15) * C + 16 * ib + 4 * kk + q4],
+                                                             Tw[(4 * kk + q4) * 16 + l15], n, 0, 0, 0);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) Nf[(16 * ib + 4 * q4 + e) * C + 16 * jb + l15] = -n[e];
             }
             __syncthreads();
         }
