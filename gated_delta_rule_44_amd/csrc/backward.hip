@@ -162,6 +162,43 @@ template <int D> struct ChainRec {
     static constexpr size_t BYTES = EC + (size_t)D * 4;
 };
 
+// Channel gate: b = running sums down the rows of the chunk's g [C][D]
+// (global, token stride gstr, rows at or past Cc as zeros), into gs [C][D]
+// in LDS.  All threads load with 16-byte loads; then 256 / D parts of the
+// rows per channel are summed by one thread each and offset by the parts
+// above (tot: 256 floats of LDS).  Ends with a barrier.
+template <int D>
+__device__ inline void gate_running_sums(float *gs, float *tot, const float *gg, size_t gstr, int Cc, int tid) {
+    constexpr int NG = C * D / 4 / 256;
+    f32x4 gv[NG];
+#pragma unroll
+    for (int it = 0; it < NG; ++it) {
+        const int p = it * 256 + tid, r = p / (D / 4), j = 4 * (p % (D / 4));
+        gv[it] = r < Cc ? *reinterpret_cast<const f32x4 *>(gg + (size_t)r * gstr + j) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int it = 0; it < NG; ++it) {
+        const int p = it * 256 + tid, r = p / (D / 4), j = 4 * (p % (D / 4));
+        *reinterpret_cast<f32x4 *>(gs + r * D + j) = gv[it];
+    }
+    __syncthreads();
+    constexpr int NH = 256 / D, RH = C / NH;
+    const int j = tid % D, part = tid / D;
+    float rs[RH], run = 0.f;
+#pragma unroll
+    for (int u = 0; u < RH; ++u) {
+        run += gs[(part * RH + u) * D + j];
+        rs[u] = run;
+    }
+    tot[part * D + j] = run;
+    __syncthreads();
+    float off = 0.f;
+    for (int q = 0; q < part; ++q) off += tot[q * D + j];
+#pragma unroll
+    for (int u = 0; u < RH; ++u) gs[(part * RH + u) * D + j] = rs[u] + off;
+    __syncthreads();
+}
+
 // PREP: stop after T and write the chunk's ChainRec (no S0 or dS_C needed).
 template <int D, bool CH, bool PREP>
 __global__ __launch_bounds__(256) void chunk_grad_kernel(BwdArgs a) {
@@ -222,39 +259,8 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(BwdArgs a) {
             kv[it] = *reinterpret_cast<const bf16x8 *>(kg + (size_t)r * rowD + j);
         }
     }
-    if constexpr (CH) {
-        constexpr int NG = C * D / 4 / 256;
-        f32x4 gv[NG];
-#pragma unroll
-        for (int it = 0; it < NG; ++it) {
-            const int p = it * 256 + tid, r = p / (D / 4), j = 4 * (p % (D / 4));
-            gv[it] = r < Cc ? *reinterpret_cast<const f32x4 *>(gg + (size_t)r * gstr + j)
-                            : f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-#pragma unroll
-        for (int it = 0; it < NG; ++it) {
-            const int p = it * 256 + tid, r = p / (D / 4), j = 4 * (p % (D / 4));
-            *reinterpret_cast<f32x4 *>(gst + r * D + j) = gv[it];
-        }
-        __syncthreads();
-        // b = running sums of g down the rows: 256 / D parts of the rows per
-        // channel, each summed by one thread, then offset by the parts above
-        constexpr int NH = 256 / D, RH = C / NH;
-        const int j = tid % D, part = tid / D;
-        float rs[RH], run = 0.f;
-#pragma unroll
-        for (int u = 0; u < RH; ++u) {
-            run += gst[(part * RH + u) * D + j];
-            rs[u] = run;
-        }
-        gtot[part * D + j] = run;
-        __syncthreads();
-        float off = 0.f;
-        for (int q = 0; q < part; ++q) off += gtot[q * D + j];
-#pragma unroll
-        for (int u = 0; u < RH; ++u) gst[(part * RH + u) * D + j] = rs[u] + off;
-    }
-    __syncthreads();
+    if constexpr (CH) gate_running_sums<D>(gst, gtot, gg, gstr, Cc, tid);
+    else __syncthreads();
     // gated operands Qt = q e^b, Kt = k e^b, Kb = k e^-b
 #pragma unroll
     for (int it = 0; it < NQ; ++it) {
@@ -677,62 +683,49 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(BwdArgs a) {
     static_assert(sizeof(sm.Tb) + sizeof(sm.Pb) + sizeof(sm.dPb) + sizeof(sm.Nb) >= sizeof(float) * C * D,
                   "h overlay");
     static_assert(sizeof(sm.Qt) + sizeof(sm.Kt) >= sizeof(float) * C * D, "E overlay");
+    float rowacc[4] = {0.f, 0.f, 0.f, 0.f}, hacc[4] = {0.f, 0.f, 0.f, 0.f};   // scalar gate
 #pragma unroll
     for (int cb = 0; cb < NB; ++cb) {
         const int j = 16 * cb + l15;
-        float rowsum[4], hsum[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int r = rowof(e);
             const float qt = (float)sm.Qt[r * PD + j];
             const float kt = (float)sm.Kt[r * PD + j];
             const float kb = (float)sm.Kb[r * PD + j];
-            rowsum[e] = dQt[cb][e] * qt + dKt[cb][e] * kt - dKb[cb][e] * kb;
-            hsum[e] = dKbh[cb][e] * kb;
-        }
-        if (CH) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                dbf[rowof(e) * D + j] = rowsum[e];
-                hf[rowof(e) * D + j] = hsum[e];
+            const float rowsum = dQt[cb][e] * qt + dKt[cb][e] * kt - dKb[cb][e] * kb;
+            const float hsum = dKbh[cb][e] * kb;
+            if (CH) {
+                dbf[r * D + j] = rowsum;
+                hf[r * D + j] = hsum;
+            } else {
+                rowacc[e] += rowsum;
+                hacc[e] += hsum;
             }
-        } else {
+        }
+    }
+    if (!CH) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float v = sum_group<16>(rowsum[e]);
-                const float hv = sum_group<16>(hsum[e]);
-                if (l15 == 0) {
-                    atomicAdd(&sm.dbrow[rowof(e)], v);
-                    atomicAdd(&sm.hrow[rowof(e)], hv);
-                }
+        for (int e = 0; e < 4; ++e) {
+            const float v = sum_group<16>(rowacc[e]);
+            const float hv = sum_group<16>(hacc[e]);
+            if (l15 == 0) {
+                atomicAdd(&sm.dbrow[rowof(e)], v);
+                atomicAdd(&sm.hrow[rowof(e)], hv);
             }
         }
     }
     __syncthreads();                           // Qt, Kt no longer read
-    if (CH) {
-        if (tid < D) {
-            float run = 0.f;
-            for (int r0 = 0; r0 < C; r0 += 16) {
-                float gv[16];
-#pragma unroll
-                for (int u = 0; u < 16; ++u)
-                    gv[u] = r0 + u < Cc ? gg[(size_t)(r0 + u) * gstr + tid] : 0.f;
-#pragma unroll
-                for (int u = 0; u < 16; ++u) {
-                    run += gv[u];
-                    Ef[(r0 + u) * D + tid] = ex(run);
-                }
-            }
-        }
-        __syncthreads();
-    }
+    float *ptot = reinterpret_cast<float *>(sm.R.stage) + C * D;   // 512 floats past db
+    static_assert(sizeof(sm.R) >= sizeof(float) * (C * D + 512), "part sums");
+    if constexpr (CH) gate_running_sums<D>(Ef, ptot, gg, gstr, Cc, tid);   // b, over Qt and Kt
 #pragma unroll
     for (int cb = 0; cb < NB; ++cb) {
         const int j = 16 * cb + l15;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int r = rowof(e);
-            const float E = CH ? Ef[r * D + j] : ex(sm.bs[r]);
+            const float E = ex(CH ? Ef[r * D + j] : sm.bs[r]);
             const float Ei = __builtin_amdgcn_rcpf(E);
             if (r < Cc) {
                 const size_t o = ((tok0 + r) * a.H + h) * D + j;
@@ -743,35 +736,46 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(BwdArgs a) {
     }
     __syncthreads();
     if (CH) {
-        if (tid < D) {
-            // h enters dg_s as its sum over r < s (an exclusive prefix)
-            float pre = 0.f;
-            for (int r = 0; r < C; ++r) {
-                const float hv = hf[r * D + tid];
-                hf[r * D + tid] = pre;
-                pre += hv;
-            }
-            float run = sm.dbC[tid];
-            for (int r = C - 1; r >= 0; --r) {
-                run += dbf[r * D + tid];
-                if (r < Cc) a.dg[(tok0 + r) * a.H * D + (size_t)h * D + tid] = run + hf[r * D + tid];
-            }
+        // dg_s = sum_{r >= s} db_r + db_C + sum_{r < s} h_r per channel: 256 / D
+        // parts of the rows per channel, each taken by one thread, with the
+        // sums of the other parts as offsets
+        constexpr int NH = 256 / D, RH = C / NH;
+        const int j = tid % D, part = tid / D;
+        float hs = 0.f, ds = 0.f;
+#pragma unroll
+        for (int u = 0; u < RH; ++u) {
+            hs += hf[(part * RH + u) * D + j];
+            ds += dbf[(part * RH + u) * D + j];
+        }
+        ptot[part * D + j] = hs;
+        ptot[(NH + part) * D + j] = ds;
+        __syncthreads();
+        float pre = 0.f, run = sm.dbC[j];
+        for (int q = 0; q < part; ++q) pre += ptot[q * D + j];
+        for (int q = NH - 1; q > part; --q) run += ptot[(NH + q) * D + j];
+        float hx[RH];
+#pragma unroll
+        for (int u = 0; u < RH; ++u) {
+            hx[u] = pre;
+            pre += hf[(part * RH + u) * D + j];
+        }
+#pragma unroll
+        for (int u = RH - 1; u >= 0; --u) {
+            const int r = part * RH + u;
+            run += dbf[r * D + j];
+            if (r < Cc) a.dg[(tok0 + r) * a.H * D + (size_t)h * D + j] = run + hx[u];
         }
     } else if (w == 0) {
-        // scalar gate: db_C summed over channels, then reverse sums over rows
+        // scalar gate: db_C summed over channels; lane 63 - s takes row s:
+        // the suffix sum of db over rows >= s, the prefix of h over rows < s
         float tot = 0.f;
         for (int j = lane; j < D; j += 64) tot += sm.dbC[j];
         tot = sum_quads(sum_group<16>(tot));
-        float pre = 0.f, mine = 0.f;
-        for (int r = 0; r < C; ++r) {
-            if (r == lane) mine = pre;
-            pre += sm.hrow[r];
-        }
-        float run = tot;
-        for (int r = C - 1; r >= 0; --r) {
-            run += sm.dbrow[r];
-            if (r == lane && r < Cc) a.dg[(tok0 + r) * a.H + h] = run + mine;
-        }
+        const float hx = wave_prefix_sum(lane > 0 ? sm.hrow[lane - 1] : 0.f);   // row lane
+        const int s = C - 1 - lane;
+        const float suf = wave_prefix_sum(sm.dbrow[s]);
+        const float hs = __shfl(hx, s);
+        if (s < Cc) a.dg[(tok0 + s) * a.H + h] = tot + suf + hs;
     }
     if (tid < Cc) a.dbeta[(tok0 + tid) * a.H + h] = sm.dbeta[tid];
 }
