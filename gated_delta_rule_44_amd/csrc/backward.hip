@@ -321,7 +321,9 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(BwdArgs a) {
             const int r = rowof(e);
             if (!(s < r)) av[e] = 0.f;
             if (!(s <= r)) pv[e] = 0.f;
-            Nf[r * C + s] = sm.beta[r] * av[e];
+            const float lv = sm.beta[r] * av[e];
+            Nf[r * C + s] = lv;
+            if (J < I) sm.R.inv.L[(I * (I - 1) / 2 + J) * 256 + (4 * q4 + e) * 16 + l15] = lv;
             sm.Pb[r * PC + s] = (bf16)pv[e];
         }
         Areg[J] = av;
@@ -335,14 +337,8 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(BwdArgs a) {
     //         diagonal, N_ij = -N_ii sum_{k=j}^{i-1} L_ik N_kj, one block
     //         diagonal i - j = d at a time
     {
-        float *Ls = sm.R.inv.L;                        // [ltri(i, k)][16][16]
-        float *Tm = Ls + 6 * 256;                      // [3][16][16]
-        const int tr = tid >> 4, tc = tid & 15;
-#pragma unroll
-        for (int i = 1; i < 4; ++i)
-#pragma unroll
-            for (int k = 0; k < i; ++k)
-                Ls[(i * (i - 1) / 2 + k) * 256 + tid] = Nf[(16 * i + tr) * C + 16 * k + tc];
+        const float *Ls = sm.R.inv.L;                  // [ltri(i, k)][16][16], from step 2
+        float *Tm = sm.R.inv.L + 6 * 256;              // [3][16][16]
         if (w == 0) {
             const int base = 16 * (lane >> 4), c = lane & 15;
             float n[16];
@@ -388,14 +384,24 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(BwdArgs a) {
             __syncthreads();
         }
     }
-    for (int e = tid; e < C * C; e += 256) {
-        const int r = e / C, s = e % C;
-        const float nv = Nf[e];
-        const float tv = nv * sm.beta[s];
-        const bf16 tb = (bf16)tv;
-        sm.Nb[r * PC + s] = (bf16)nv;
-        sm.Tb[r * PC + s] = tb;
-        if (r == s) sm.tcor[r] = tv - (float)tb;
+    {
+        // N and T = N diag(beta) to bf16, 16 entries of a row per thread
+        const int r = tid >> 2, s0 = 16 * (tid & 3);
+        bf16x8 nb[2], tb[2];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const float nv = Nf[r * C + s0 + u];
+            const float tv = nv * sm.beta[s0 + u];
+            const bf16 t16 = (bf16)tv;
+            nb[u >> 3][u & 7] = (bf16)nv;
+            tb[u >> 3][u & 7] = t16;
+            if (s0 + u == r) sm.tcor[r] = tv - (float)t16;
+        }
+#pragma unroll
+        for (int hlf = 0; hlf < 2; ++hlf) {
+            *reinterpret_cast<bf16x8 *>(&sm.Nb[r * PC + s0 + 8 * hlf]) = nb[hlf];
+            *reinterpret_cast<bf16x8 *>(&sm.Tb[r * PC + s0 + 8 * hlf]) = tb[hlf];
+        }
     }
     __syncthreads();
 
