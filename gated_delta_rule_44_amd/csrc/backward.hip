@@ -342,12 +342,23 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(BwdArgs a) {
         if (w == 0) {
             const int base = 16 * (lane >> 4), c = lane & 15;
             float n[16];
+            // row r of the block as four 16-byte reads (the same address
+            // across the block's lanes), the next row's in flight
+            auto lrow = [&](int r, f32x4 (&L)[4]) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v) L[v] = *reinterpret_cast<const f32x4 *>(&Nf[(base + r) * C + base + 4 * v]);
+            };
+            f32x4 Lc[4], Ln[4];
+            lrow(0, Lc);
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
+                if (r + 1 < 16) lrow(r + 1, Ln);
                 float acc = r == c ? 1.f : 0.f;
 #pragma unroll
-                for (int m = 0; m < r; ++m) acc -= Nf[(base + r) * C + base + m] * n[m];
+                for (int m = 0; m < r; ++m) acc -= Lc[m >> 2][m & 3] * n[m];
                 n[r] = acc;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) Lc[v] = Ln[v];
             }
 #pragma unroll
             for (int r = 0; r < 16; ++r) Nf[(base + r) * C + base + c] = n[r];
@@ -384,24 +395,23 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(BwdArgs a) {
             __syncthreads();
         }
     }
-    {
-        // N and T = N diag(beta) to bf16, 16 entries of a row per thread
-        const int r = tid >> 2, s0 = 16 * (tid & 3);
-        bf16x8 nb[2], tb[2];
+    // N and T = N diag(beta) to bf16, four consecutive entries per thread
+    // and read (a wave reads 1 KiB of consecutive LDS per instruction)
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
-            const float nv = Nf[r * C + s0 + u];
-            const float tv = nv * sm.beta[s0 + u];
-            const bf16 t16 = (bf16)tv;
-            nb[u >> 3][u & 7] = (bf16)nv;
-            tb[u >> 3][u & 7] = t16;
-            if (s0 + u == r) sm.tcor[r] = tv - (float)t16;
-        }
+    for (int it = 0; it < C * C / 4 / 256; ++it) {
+        const int p = it * 256 + tid, r = p / (C / 4), s0 = 4 * (p % (C / 4));
+        const f32x4 nv = *reinterpret_cast<const f32x4 *>(&Nf[r * C + s0]);
+        const f32x4 bv = *reinterpret_cast<const f32x4 *>(&sm.beta[s0]);
+        bf16x4 nb, tb;
 #pragma unroll
-        for (int hlf = 0; hlf < 2; ++hlf) {
-            *reinterpret_cast<bf16x8 *>(&sm.Nb[r * PC + s0 + 8 * hlf]) = nb[hlf];
-            *reinterpret_cast<bf16x8 *>(&sm.Tb[r * PC + s0 + 8 * hlf]) = tb[hlf];
+        for (int u = 0; u < 4; ++u) {
+            const float tv = nv[u] * bv[u];
+            nb[u] = (bf16)nv[u];
+            tb[u] = (bf16)tv;
+            if (s0 + u == r) sm.tcor[r] = tv - (float)tb[u];
         }
+        *reinterpret_cast<bf16x4 *>(&sm.Nb[r * PC + s0]) = nb;
+        *reinterpret_cast<bf16x4 *>(&sm.Tb[r * PC + s0]) = tb;
     }
     __syncthreads();
 
