@@ -56,6 +56,23 @@ def test_backward(gate, D, T):
 
 
 @pytest.mark.parametrize("gate", ["scalar", "channel"])
+def test_backward_strong_decay(gate):
+    """Gates of about -50 per 64 tokens (the forward's strong-decay case):
+    the chunk's e^{+-b} factors span ~20 orders of magnitude, in the gated
+    operands and in dq = dQt e^b, dk = dKt e^b + dKb e^-b."""
+    B, T, H, D = 1, 150, 2, 128
+    x = synthetic.prefill_inputs(B, T, H, D, torch.bfloat16, gate, seed=21, device=DEV,
+                                 gate_scale=1.0)
+    announce("backward strong decay %s: min gate sum over the first chunk %.1f"
+             % (gate, float(x["g"][0, :64].sum(0).min())))
+    do, dht = _upstream(B, T, H, D, 90)
+    got = gdr.backward(x["q"], x["k"], x["v"], x["g"], x["beta"], do, h0=x["h0"], dht=dht)
+    sync()
+    ref = oracle.backward(x["q"], x["k"], x["v"], x["g"], x["beta"], do, h0=x["h0"], dht=dht)
+    _check(got, ref, "strong decay %s" % gate)
+
+
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
 def test_backward_without_h0_and_dht(gate):
     announce("backward no h0/dht %s" % gate)
     B, T, H, D = 1, 100, 3, 128
