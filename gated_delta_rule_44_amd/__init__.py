@@ -22,7 +22,8 @@ import torch
 __all__ = ["prefill", "prefill_varlen", "prefill_varlen_pool", "decode_step",
            "decode_placement", "decode_tokens", "decode_commit", "workspace_bytes",
            "prefill_fused", "prefill_varlen_fused", "decode_tokens_fused",
-           "fused_workspace_bytes", "backward", "version", "GdrError", "lib_path",
+           "fused_workspace_bytes", "backward", "backward_varlen", "version", "GdrError",
+           "lib_path",
            "FA", "SWA", "GDN", "KDA"]
 
 FA, SWA, GDN, KDA = 0, 1, 2, 3
@@ -90,6 +91,11 @@ def _load():
     lib.gdr_decode_tokens_fused.restype = I
     lib.gdr_decode_tokens_fused.argtypes = [I, I, I, I, I, I, I, F, P, P, P, P, P, F,
                                             P, P, I, P, P, P, P]
+    lib.gdr_backward_varlen_workspace_bytes.restype = Z
+    lib.gdr_backward_varlen_workspace_bytes.argtypes = [I, I, ctypes.c_longlong, I, I, I]
+    lib.gdr_backward_chunked_varlen.restype = I
+    lib.gdr_backward_chunked_varlen.argtypes = [I, I, I, I, I, I, I, I, F, P, P, P, P, P, P,
+                                                P, P, P, P, P, P, P, P, P, P, P, Z, P]
     _lib = lib
     return lib
 
@@ -545,4 +551,47 @@ def backward(q, k, v, g, beta, do, h0=None, dht=None, scale: float = 1.0,
         _BF16, gk, B, T, H, D, D, 64, float(scale), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
         _ptr(beta), _ptr(h0), _ptr(do), _ptr(dht), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg),
         _ptr(dbeta), _ptr(dh0), _ptr(workspace), nbytes, _stream(dev)))
+    return dq, dk, dv, dg, dbeta, dh0
+
+
+def backward_varlen(q, k, v, g, beta, do, cu_seqlens, h0=None, dht=None, scale: float = 1.0,
+                    cu_seqlens_host=None, workspace=None):
+    """Gradients of prefill_varlen() for a packed bf16 batch.
+
+    q, k, v, do [T_tot,H,D] bf16; g [T_tot,H] or [T_tot,H,D] and beta
+    [T_tot,H] fp32; cu_seqlens int32 [N+1] on the GPU; h0 and dht [N,H,D,D]
+    fp32 or None.  Returns fp32 (dq, dk, dv, dg, dbeta, dh0)."""
+    Tt, H, D = q.shape
+    dev = q.device
+    for n, t in (("q", q), ("k", k), ("v", v), ("do", do)):
+        _dense(n, t, torch.bfloat16, dev)
+    _dense("g", g, torch.float32, dev)
+    _dense("beta", beta, torch.float32, dev)
+    _dense("cu_seqlens", cu_seqlens, torch.int32, dev)
+    N = cu_seqlens.numel() - 1
+    _need(k.shape == q.shape and v.shape == q.shape and do.shape == q.shape, "shapes differ")
+    _need(beta.shape == (Tt, H), "beta must be [T_tot,H]")
+    gk = _CHANNEL if g.dim() == 3 else _SCALAR
+    _need(g.shape == ((Tt, H, D) if gk == _CHANNEL else (Tt, H)), "bad gate shape")
+    for n, t in (("h0", h0), ("dht", dht)):
+        if t is not None:
+            _dense(n, t, torch.float32, dev)
+            _need(t.shape == (N, H, D, D), "%s must be [N,H,D,D]" % n)
+    host = None
+    if cu_seqlens_host is not None:
+        import numpy as np
+        host = np.ascontiguousarray(np.asarray(cu_seqlens_host, dtype=np.int32))
+        _need(host.shape == (N + 1,), "cu_seqlens_host must have N+1 entries")
+    f32 = dict(device=dev, dtype=torch.float32)
+    dq, dk, dv = (torch.empty((Tt, H, D), **f32) for _ in range(3))
+    dg = torch.empty(g.shape, **f32)
+    dbeta = torch.empty((Tt, H), **f32)
+    dh0 = torch.empty((N, H, D, D), **f32)
+    nbytes = int(_load().gdr_backward_varlen_workspace_bytes(gk, N, Tt, H, D, D))
+    workspace = _workspace(workspace, nbytes, dev)
+    hp = None if host is None else host.ctypes.data_as(ctypes.c_void_p)
+    _check(_load().gdr_backward_chunked_varlen(
+        _BF16, gk, N, Tt, H, D, D, 64, float(scale), _ptr(cu_seqlens), hp, _ptr(q), _ptr(k),
+        _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(do), _ptr(dht), _ptr(dq), _ptr(dk),
+        _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(dh0), _ptr(workspace), nbytes, _stream(dev)))
     return dq, dk, dv, dg, dbeta, dh0

@@ -571,34 +571,42 @@ gdr_status gdr_decode_tokens_fused(enum gdr_dtype dt, enum gdr_gate gk, int B, i
 
 namespace {
 
-// Backward workspace: the chunk-entering states and the chunk state
-// gradients ([B, H, nc, Dv, Dk] fp32 each), the forward's outputs (bf16,
-// unused), the forward's own workspace and the adjoint chain's per-chunk
-// records.
+// Backward workspace for N sequences, `tokens` tokens and `chunks` chunk
+// slots (fixed length: N ceil(T / 64); packed: the bound tokens / 64 + N):
+// the chunk-entering states and the chunk state gradients ([chunks, H, Dv,
+// Dk] fp32 each), the forward's outputs (bf16, unused), the forward's own
+// workspace (its schedule and chunk_base are reused) and the adjoint
+// chain's per-chunk records.
 struct BwdWs {
     size_t states, dstates, o, fwd, recs, total;
 };
-BwdWs bwd_layout(int gk, int B, int T, int H, int Dk, int Dv) {
+BwdWs bwd_layout(int gk, int N, long long tokens, long long chunks, int H, int Dk, int Dv) {
     BwdWs w{};
-    if (B <= 0 || T <= 0 || H <= 0 || Dk <= 0 || Dv <= 0) return w;
+    if (N <= 0 || tokens <= 0 || chunks <= 0 || H <= 0 || Dk <= 0 || Dv <= 0) return w;
     auto r256 = [](size_t x) { return (x + 255) / 256 * 256; };
-    const size_t nc = ((size_t)T + 63) / 64;
-    const size_t st = (size_t)B * H * nc * Dv * Dk * sizeof(float);
+    const size_t st = (size_t)chunks * H * Dv * Dk * sizeof(float);
     w.states = 0;
     w.dstates = st;
     w.o = 2 * st;
-    w.fwd = w.o + r256((size_t)B * T * H * Dv * 2);
-    w.recs = w.fwd + r256(ws_layout(gk == GDR_GATE_SCALAR, B, (long long)B * T, H).total);
-    w.total = w.recs + (size_t)B * H * nc * gdr::backward_record_bytes(Dk);
+    w.fwd = w.o + r256((size_t)tokens * H * Dv * 2);
+    w.recs = w.fwd + r256(ws_layout(gk == GDR_GATE_SCALAR, N, tokens, H).total);
+    w.total = w.recs + (size_t)chunks * H * gdr::backward_record_bytes(Dk);
     return w;
 }
+long long fixed_chunks(int B, int T) { return (long long)B * ((T + 63) / 64); }
+long long packed_chunks(int N, long long tokens) { return tokens / 64 + N; }
 
 }  // namespace
 
 extern "C" {
 
 size_t gdr_backward_workspace_bytes(enum gdr_gate gk, int B, int T, int H, int Dk, int Dv) {
-    return bwd_layout(gk, B, T, H, Dk, Dv).total;
+    return bwd_layout(gk, B, (long long)B * T, fixed_chunks(B, T), H, Dk, Dv).total;
+}
+
+size_t gdr_backward_varlen_workspace_bytes(enum gdr_gate gk, int N, long long tokens, int H,
+                                           int Dk, int Dv) {
+    return bwd_layout(gk, N, tokens, packed_chunks(N, tokens), H, Dk, Dv).total;
 }
 
 gdr_status gdr_backward_chunked(enum gdr_dtype dt, enum gdr_gate gk, int B, int T, int H,
@@ -636,7 +644,7 @@ gdr_status gdr_backward_chunked(enum gdr_dtype dt, enum gdr_gate gk, int B, int 
     REQUIRE_ALIGNED_OR_NULL(h0, "h0");
     REQUIRE_ALIGNED_OR_NULL(dht, "dht");
     REQUIRE_ALIGNED_OR_NULL(dh0, "dh0");
-    const BwdWs W = bwd_layout(gk, B, T, H, Dk, Dv);
+    const BwdWs W = bwd_layout(gk, B, (long long)B * T, fixed_chunks(B, T), H, Dk, Dv);
     const size_t need = W.total;
     st = check_workspace(what, workspace, ws_bytes, need);
     if (st != GDR_OK) return st;
@@ -668,7 +676,99 @@ gdr_status gdr_backward_chunked(enum gdr_dtype dt, enum gdr_gate gk, int B, int 
     a.states = reinterpret_cast<float *>(ws + W.states);
     a.dstates = reinterpret_cast<float *>(ws + W.dstates);
     a.recs = ws + W.recs;
+    a.cu_seqlens = nullptr; a.chunk_base = nullptr; a.chunks = fixed_chunks(B, T);
     a.B = B; a.T = T; a.H = H; a.nc = (T + 63) / 64; a.scale = scale;
+    a.channel_gate = gk == GDR_GATE_CHANNEL;
+    return finish(gdr::launch_backward(Dk, a, s), s, what);
+}
+
+gdr_status gdr_backward_chunked_varlen(enum gdr_dtype dt, enum gdr_gate gk, int N, int T_total,
+                                       int H, int Dk, int Dv, int chunk, float scale,
+                                       const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
+                                       const void *q, const void *k, const void *v,
+                                       const float *g, const float *beta, const float *h0,
+                                       const void *d_o, const float *dht, float *dq, float *dk,
+                                       float *dv, float *dg, float *dbeta, float *dh0,
+                                       void *workspace, size_t ws_bytes, void *stream) {
+    const char *what = "gdr_backward_chunked_varlen";
+    gdr_status st = check_common(dt, gk, Dk, Dv, what);
+    if (st != GDR_OK) return st;
+    if (dt != GDR_BF16)
+        return fail(GDR_EUNSUPPORTED, "%s: only bf16 inputs have a backward", what);
+    if (chunk != 64) return fail(GDR_EUNSUPPORTED, "%s: chunk = %d; only 64 is supported", what, chunk);
+    if (N < 0 || T_total < 0 || H <= 0)
+        return fail(GDR_EINVAL, "%s: bad sizes N=%d T_total=%d H=%d", what, N, T_total, H);
+    if ((long long)T_total * H * Dk >= (1LL << 40))
+        return fail(GDR_EUNSUPPORTED, "%s: problem too large", what);
+    const long long chunks = packed_chunks(N, T_total);
+    if ((long long)N * H * 8 >= (1LL << 31) || chunks * H >= (1LL << 31))
+        return fail(GDR_EUNSUPPORTED, "%s: grid too large", what);
+    if (N == 0) return GDR_OK;
+    if (!cu_seqlens) return fail(GDR_EINVAL, "%s: cu_seqlens is NULL", what);
+    if (cu_seqlens_host) {
+        if (cu_seqlens_host[0] != 0)
+            return fail(GDR_EINVAL, "%s: cu_seqlens[0] = %d, expected 0", what, cu_seqlens_host[0]);
+        for (int i = 0; i < N; ++i)
+            if (cu_seqlens_host[i + 1] < cu_seqlens_host[i])
+                return fail(GDR_EINVAL, "%s: cu_seqlens decreases at %d", what, i);
+        if (cu_seqlens_host[N] != T_total)
+            return fail(GDR_EINVAL, "%s: cu_seqlens[N] = %d but T_total = %d", what,
+                        cu_seqlens_host[N], T_total);
+    }
+    if (T_total > 0) {
+        REQUIRE_PTR(q, "q");
+        REQUIRE_PTR(k, "k");
+        REQUIRE_PTR(v, "v");
+        REQUIRE_PTR(g, "g");
+        if (!beta) return fail(GDR_EINVAL, "%s: beta is NULL", what);
+        REQUIRE_PTR(d_o, "do");
+        REQUIRE_PTR(dq, "dq");
+        REQUIRE_PTR(dk, "dk");
+        REQUIRE_PTR(dv, "dv");
+        if (!dg) return fail(GDR_EINVAL, "%s: dg is NULL", what);
+        if (!dbeta) return fail(GDR_EINVAL, "%s: dbeta is NULL", what);
+    }
+    REQUIRE_ALIGNED_OR_NULL(h0, "h0");
+    REQUIRE_ALIGNED_OR_NULL(dht, "dht");
+    REQUIRE_ALIGNED_OR_NULL(dh0, "dh0");
+    const BwdWs W = bwd_layout(gk, N, T_total, chunks, H, Dk, Dv);
+    st = check_workspace(what, workspace, ws_bytes, W.total);
+    if (st != GDR_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (T_total == 0) {
+        // no tokens in any sequence: dS_0 = dS_T
+        if (!dh0) return GDR_OK;
+        return finish(gdr::launch_copy_or_zero(dh0, dht, (size_t)N * H * Dv * Dk, s), s, what);
+    }
+    char *ws = static_cast<char *>(workspace);
+    const bool tiles = gk == GDR_GATE_SCALAR;
+    const WsLayout FL = ws_layout(tiles, N, T_total, H);
+    int32_t *order = reinterpret_cast<int32_t *>(ws + W.fwd + FL.order);
+    int32_t *cbase = reinterpret_cast<int32_t *>(ws + W.fwd + FL.chunk_base);
+    // 1. the forward (longest sequences first), keeping the state that
+    //    enters every chunk at its global chunk index
+    hipError_t e = gdr::launch_varlen_schedule(cu_seqlens, N, order, s);
+    if (e == hipSuccess) e = gdr::launch_chunk_base(cu_seqlens, N, cbase, s);
+    if (e != hipSuccess) return finish(e, s, what);
+    gdr::PrefillArgs f{};
+    f.q = q; f.k = k; f.v = v; f.g = g; f.beta = beta; f.h0 = h0;
+    f.o = ws + W.o; f.ht = nullptr;
+    f.cu_seqlens = cu_seqlens; f.order = order; f.chunk_base = cbase;
+    f.tiles = tiles ? ws + W.fwd + FL.tiles : nullptr;
+    f.max_chunks = FL.max_chunks;
+    f.N = N; f.T = 0; f.H = H; f.scale = scale; f.channel_gate = gk == GDR_GATE_CHANNEL;
+    f.states = reinterpret_cast<float *>(ws + W.states);
+    e = gdr::launch_prefill_chunked(Dk, f, s);
+    if (e != hipSuccess) return finish(e, s, what);
+    // 2, 3. the adjoint pass and the chunk gradients
+    gdr::BwdArgs a{};
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.h0 = h0; a.dout = d_o; a.dht = dht;
+    a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbeta = dbeta; a.dh0 = dh0;
+    a.states = reinterpret_cast<float *>(ws + W.states);
+    a.dstates = reinterpret_cast<float *>(ws + W.dstates);
+    a.recs = ws + W.recs;
+    a.cu_seqlens = cu_seqlens; a.chunk_base = cbase; a.chunks = chunks;
+    a.B = N; a.T = 0; a.H = H; a.nc = 0; a.scale = scale;
     a.channel_gate = gk == GDR_GATE_CHANNEL;
     return finish(gdr::launch_backward(Dk, a, s), s, what);
 }

@@ -199,6 +199,37 @@ __device__ inline void gate_running_sums(float *gs, float *tot, const float *gg,
     __syncthreads();
 }
 
+// The chunks of all sequences are numbered one after the other: sequence n's
+// chunk c is global chunk base_n + c (fixed length: n nc + c).  Per global
+// chunk: its sequence, its index in the sequence, the sequence's first token
+// and length; false past the last chunk (packed batches: the grid is sized
+// for an upper bound).
+struct ChunkLoc {
+    int n, c;
+    long long seq0, len;
+};
+__device__ inline bool locate_chunk(const BwdArgs &a, long long gc, ChunkLoc &L) {
+    if (a.cu_seqlens) {
+        if (gc >= a.chunk_base[a.B]) return false;
+        int lo = 0, hi = a.B;                  // chunk_base[lo] <= gc < chunk_base[hi]
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (a.chunk_base[mid] <= gc) lo = mid;
+            else hi = mid;
+        }
+        L.n = lo;
+        L.c = (int)(gc - a.chunk_base[lo]);
+        L.seq0 = a.cu_seqlens[lo];
+        L.len = a.cu_seqlens[lo + 1] - L.seq0;
+    } else {
+        L.n = (int)(gc / a.nc);
+        L.c = (int)(gc - (long long)L.n * a.nc);
+        L.seq0 = (long long)L.n * a.T;
+        L.len = a.T;
+    }
+    return true;
+}
+
 // PREP: stop after T and write the chunk's ChainRec (no S0 or dS_C needed).
 template <int D, bool CH, bool PREP>
 __global__ __launch_bounds__(256) void chunk_grad_kernel(BwdArgs a) {
@@ -209,15 +240,16 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(BwdArgs a) {
     __shared__ Sm sm;
 
     const int h = blockIdx.x % a.H;
-    const int ci = blockIdx.x / a.H;          // chunk over the batch: b nc + c
-    const int b = ci / a.nc, c = ci - b * a.nc;
-    const int t0 = c * C;
-    const int Cc = a.T - t0 < C ? a.T - t0 : C;
+    const long long gc = blockIdx.x / a.H;    // global chunk
+    ChunkLoc loc;
+    if (!locate_chunk(a, gc, loc)) return;
+    const int t0 = loc.c * C;
+    const int Cc = loc.len - t0 < C ? (int)(loc.len - t0) : C;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l15 = lane & 15, q4 = lane >> 4;
     const size_t rowD = (size_t)a.H * D;                      // token stride of q, k, v, o
-    const size_t tok0 = (size_t)b * a.T + t0;                 // first token row (b T + t0)
+    const size_t tok0 = (size_t)(loc.seq0 + t0);              // first token row
     const bf16 *qg = static_cast<const bf16 *>(a.q) + (tok0 * a.H + h) * D;
     const bf16 *kg = static_cast<const bf16 *>(a.k) + (tok0 * a.H + h) * D;
     const bf16 *vg = static_cast<const bf16 *>(a.v) + (tok0 * a.H + h) * D;
@@ -225,7 +257,7 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(BwdArgs a) {
     const size_t gstr = CH ? rowD : (size_t)a.H;              // token stride of g
     const float *gg = a.g + (CH ? (tok0 * a.H + h) * D : tok0 * a.H + h);
     const float *bg = a.beta + tok0 * a.H + h;
-    const size_t sbh = ((size_t)b * a.H + h) * a.nc + c;
+    const size_t sbh = (size_t)gc * a.H + h;                  // [chunk][head] records
     const float *S0 = a.states + sbh * D * D;                  // [i][j]
     const float *dSC = a.dstates + sbh * D * D;                // [i][j]
     float *const Nf = sm.R.inv.Nf;
@@ -418,7 +450,7 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(BwdArgs a) {
     if constexpr (PREP) {
         // W = T Kt (the diagonal of T compensated), then the record
         using R = ChainRec<D>;
-        char *rec = static_cast<char *>(a.recs) + (((size_t)b * a.H + h) * a.nc + c) * R::BYTES;
+        char *rec = static_cast<char *>(a.recs) + sbh * R::BYTES;
         bf16 *Wg = reinterpret_cast<bf16 *>(rec + R::W);
 #pragma unroll
         for (int cb = 0; cb < NB; ++cb) {
@@ -835,7 +867,18 @@ __global__ __launch_bounds__(256) void adjoint_chain_kernel(BwdArgs a) {
     const int tile = jj % NTL;
     const int unit = (jj / NTL) * 8 + xcd;
     if (unit >= a.B * a.H) return;
-    const int b = unit / a.H, h = unit - b * a.H;
+    const int b = unit / a.H, h = unit - b * a.H;     // sequence b
+    long long seq0, len, cb;                          // first token, length, first global chunk
+    if (a.cu_seqlens) {
+        seq0 = a.cu_seqlens[b];
+        len = a.cu_seqlens[b + 1] - seq0;
+        cb = a.chunk_base[b];
+    } else {
+        seq0 = (long long)b * a.T;
+        len = a.T;
+        cb = (long long)b * a.nc;
+    }
+    const int nch = (int)((len + C - 1) / C);
     const int i0 = tile * BVA;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -860,7 +903,7 @@ __global__ __launch_bounds__(256) void adjoint_chain_kernel(BwdArgs a) {
     bf16x8 rq[NR], rk[NR], rw[NR], rp[NP], rdo;
     float rec_ = 0.f;
     auto fetch = [&](int c) {
-        const char *rec = static_cast<const char *>(a.recs) + (bh * a.nc + c) * R::BYTES;
+        const char *rec = static_cast<const char *>(a.recs) + ((size_t)(cb + c) * a.H + h) * R::BYTES;
 #pragma unroll
         for (int it = 0; it < NR; ++it) {
             const int p = it * 256 + tid, r = p / (D / 8), j = 8 * (p % (D / 8));
@@ -876,15 +919,15 @@ __global__ __launch_bounds__(256) void adjoint_chain_kernel(BwdArgs a) {
         if (tid < D) rec_ = reinterpret_cast<const float *>(rec + R::EC)[tid];
         const int t0 = c * C, r = tid >> 2;                 // 64 rows x 4 pieces of 8
         rdo = bf16x8{};
-        if (r < a.T - t0)
+        if (r < len - t0)
             rdo = *reinterpret_cast<const bf16x8 *>(static_cast<const bf16 *>(a.dout) +
-                                                    (((size_t)b * a.T + t0 + r) * a.H + h) * D + i0 + 8 * (tid & 3));
+                                                    ((size_t)(seq0 + t0 + r) * a.H + h) * D + i0 + 8 * (tid & 3));
     };
     static_assert(C * D / 8 % 256 == 0 && C * C / 8 % 256 == 0, "record pieces per thread");
-    if (a.nc > 0) fetch(a.nc - 1);
-    for (int c = a.nc - 1; c >= 0; --c) {
+    if (nch > 0) fetch(nch - 1);
+    for (int c = nch - 1; c >= 0; --c) {
         // dS_C of chunk c
-        float *dsc = a.dstates + (bh * a.nc + c) * D * D;
+        float *dsc = a.dstates + ((size_t)(cb + c) * a.H + h) * D * D;
 #pragma unroll
         for (int t = 0; t < CB; ++t)
 #pragma unroll
@@ -987,10 +1030,9 @@ size_t backward_record_bytes(int D) {
 
 hipError_t launch_backward(int D, const BwdArgs &a, hipStream_t s) {
     const long long heads = (long long)a.B * a.H;
-    if (heads <= 0) return hipSuccess;
-    if (a.T == 0) return hipSuccess;
+    if (heads <= 0 || a.chunks <= 0) return hipSuccess;
     const long long chain_blocks = ((heads + 7) / 8) * 8 * (D / BVA);
-    const long long chunk_blocks = (long long)a.B * a.nc * a.H;
+    const long long chunk_blocks = a.chunks * a.H;
     if (chain_blocks >= (1LL << 31) || chunk_blocks >= (1LL << 31)) return hipErrorInvalidValue;
     dim3 gr((unsigned)chain_blocks), gc((unsigned)chunk_blocks), blk(256);
     if (D == 128) {

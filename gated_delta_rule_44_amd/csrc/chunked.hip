@@ -195,6 +195,8 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
     const bf16 *vg = static_cast<const bf16 *>(a.v) + (size_t)h * D + i0;
     bf16 *og = static_cast<bf16 *>(a.o) + (size_t)h * D + i0;
     const long long nch = (t1 - t0 + C - 1) / C;
+    // first global chunk of the sequence (the index of its states)
+    const long long cbase = !a.states ? 0 : a.cu_seqlens ? a.chunk_base[n] : (long long)n * nch;
     const int tid0 = threadIdx.x;
 
     // T and P are lower triangular: the entries above the diagonal of T^T and
@@ -223,7 +225,7 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
                         sv = *reinterpret_cast<const f32x4 *>(h0p + (size_t)(i0 + iv) * D + j);
                     *reinterpret_cast<bf16x4 *>(&sm.S[iv * PD + j]) = cvt4(sv);
                     if (a.states && nch > 0)        // the state entering chunk 0
-                        *reinterpret_cast<f32x4 *>(a.states + ((size_t)n * a.H + h) * nch * D * D +
+                        *reinterpret_cast<f32x4 *>(a.states + ((size_t)cbase * a.H + h) * D * D +
                                                    (size_t)(i0 + iv) * D + j) = sv;
                 }
                 St[kb][jv] = sv;
@@ -587,7 +589,7 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
                         St[kb][jv] = sv;
                         *reinterpret_cast<bf16x4 *>(&sm.S[(16 * jv + l15) * PD + jc]) = cvt4(sv);
                         if (a.states && j < nch)   // the state entering chunk j
-                            *reinterpret_cast<f32x4 *>(a.states + (((size_t)n * a.H + h) * nch + j) * D * D +
+                            *reinterpret_cast<f32x4 *>(a.states + ((size_t)(cbase + j) * a.H + h) * D * D +
                                                        (size_t)(i0 + 16 * jv + l15) * D + jc) = sv;
                     }
                 }

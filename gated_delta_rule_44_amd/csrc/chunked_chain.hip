@@ -500,7 +500,7 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
             const int par = (int)(c & 1);
             const int n3 = m3 == 2 ? 0 : m3 + 1;
             if (a.states) {                   // the state entering chunk c
-                float *sp = a.states + (((size_t)n * a.H + h) * nch + c) * D * D + srow0;
+                float *sp = a.states + ((size_t)(cbase + c) * a.H + h) * D * D + srow0;
 #pragma unroll
                 for (int jk = 0; jk < KS; ++jk) *reinterpret_cast<f32x4 *>(sp + srow(jk, 0)) = St[jk];
             }
@@ -798,6 +798,13 @@ __global__ __launch_bounds__(256) void chunk_base_kernel(const int32_t *cu, int 
 }
 
 }  // namespace
+
+hipError_t launch_chunk_base(const int32_t *cu_seqlens, int N, int32_t *chunk_base,
+                             hipStream_t s) {
+    if (N < 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(chunk_base_kernel, dim3(1), dim3(256), 0, s, cu_seqlens, N, chunk_base);
+    return hipGetLastError();
+}
 
 hipError_t launch_prefill_chain(int D, const PrefillArgs &a, hipStream_t s) {
     const long long units = (long long)a.N * a.H;

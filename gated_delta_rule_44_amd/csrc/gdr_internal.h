@@ -128,9 +128,10 @@ struct PrefillArgs {
     // normalised in the kernels
     const void *xg, *xb;
     float gate_scale;
-    // fixed-length bf16 path only: when set, the state entering every chunk
-    // of every (sequence, head), [N, H, ceil(T / 64), D, D] fp32 (for the
-    // backward)
+    // bf16 path only: when set, the state entering every chunk of every
+    // (sequence, head), [chunks, H, D, D] fp32 at global chunk
+    // chunk_base[n] + c (fixed length: n ceil(T / 64) + c; packed batches
+    // need chunk_base filled) -- for the backward
     float *states;
 };
 
@@ -164,22 +165,33 @@ constexpr size_t kTileBytes = 5 * 1024 + 2 * 64 * 4;
 // two more factor rows (6 KiB).
 constexpr size_t kTileBytesRaw = kTileBytes + 2 * 64 * 4;
 
-// Backward of the chunked prefill (fixed-length batch, bf16 q/k/v/do).
+// Backward of the chunked prefill (bf16 q/k/v/do), a fixed-length batch
+// (cu_seqlens == nullptr: B sequences of T tokens, nc = ceil(T / 64) chunks
+// each) or a packed one (B sequences, cu_seqlens [B+1], chunk_base [B+1]
+// their first global chunks).  Per-chunk workspace is indexed
+// [global chunk][head]: sequence n's chunk c is global chunk
+// chunk_base[n] + c (fixed length: n nc + c).
 struct BwdArgs {
-    const void *q, *k, *v;        // [B, T, H, D] bf16
-    const float *g, *beta;        // [B, T, H(, D)], [B, T, H]
+    const void *q, *k, *v;        // [tokens, H, D] bf16
+    const float *g, *beta;        // [tokens, H(, D)], [tokens, H]
     const float *h0;              // [B, H, D, D] or nullptr
-    const void *dout;             // [B, T, H, D] bf16: gradient of o
+    const void *dout;             // [tokens, H, D] bf16: gradient of o
     const float *dht;             // [B, H, D, D] or nullptr: gradient of the final state
-    float *dq, *dk, *dv;          // [B, T, H, D]
+    float *dq, *dk, *dv;          // [tokens, H, D]
     float *dg, *dbeta;            // like g, beta
     float *dh0;                   // [B, H, D, D] or nullptr
-    float *states, *dstates;      // workspace: [B, H, nc, D, D] each
-    void *recs;                   // workspace: one record per (b, h, chunk)
-    int B, T, H, nc;
+    float *states, *dstates;      // workspace: [chunks, H, D, D] each
+    void *recs;                   // workspace: one record per (global chunk, head)
+    const int32_t *cu_seqlens;    // [B+1] or nullptr (fixed length)
+    const int32_t *chunk_base;    // [B+1] (packed batches)
+    long long chunks;             // global chunks the grid covers (an upper bound when packed)
+    int B, T, H, nc;              // T, nc: fixed length only
     float scale;
     int channel_gate;
 };
+// chunk_base[n] = sum over m < n of ceil(len_m / 64), n = 0..N
+hipError_t launch_chunk_base(const int32_t *cu_seqlens, int N, int32_t *chunk_base,
+                             hipStream_t s);
 hipError_t launch_backward(int D, const BwdArgs &a, hipStream_t s);
 hipError_t launch_copy_or_zero(float *dst, const float *src, size_t n, hipStream_t s);
 size_t backward_record_bytes(int D);

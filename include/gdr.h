@@ -359,6 +359,42 @@ gdr_status gdr_backward_chunked(enum gdr_dtype dt, enum gdr_gate gk, int B, int 
                                 float *dbeta, float *dh0, void *workspace, size_t ws_bytes,
                                 void *stream);
 
+/*
+ * The same backward for a packed batch of N variable-length sequences (the
+ * layout of gdr_prefill_chunked_varlen): the gradients of every input of
+ * that call.
+ *
+ *   dt, gk, N, T_total, H, Dk, Dv, chunk, scale, cu_seqlens,
+ *   cu_seqlens_host, q, k, v, g, beta, h0
+ *                as gdr_prefill_chunked_varlen (dt must be GDR_BF16)
+ *   d_o          [T_total, H, Dv] bf16: gradient of o
+ *   dht          [N, H, Dv, Dk] fp32 or NULL (zero)
+ *   dq, dk, dv   [T_total, H, D] fp32 (written)
+ *   dg, dbeta    like g and beta, fp32 (written)
+ *   dh0          [N, H, Dv, Dk] fp32 (written) or NULL; an empty sequence's
+ *                dh0 is its dht
+ *   workspace    device buffer of gdr_backward_varlen_workspace_bytes(gk, N,
+ *                T_total, H, Dk, Dv) bytes (as the fixed-length form's, sized
+ *                for T_total / 64 + N chunks), 16-byte aligned
+ *
+ * The sequences' chunks are numbered one after the other on the device
+ * (from cu_seqlens); the forward runs longest sequence first, the state
+ * gradient's recurrence walks each (sequence, head) in reverse, and the
+ * chunk-local gradients take one workgroup per (chunk, head) as in the
+ * fixed-length form.
+ */
+size_t gdr_backward_varlen_workspace_bytes(enum gdr_gate gk, int N, long long tokens, int H,
+                                           int Dk, int Dv);
+
+gdr_status gdr_backward_chunked_varlen(enum gdr_dtype dt, enum gdr_gate gk, int N, int T_total,
+                                       int H, int Dk, int Dv, int chunk, float scale,
+                                       const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
+                                       const void *q, const void *k, const void *v,
+                                       const float *g, const float *beta, const float *h0,
+                                       const void *d_o, const float *dht, float *dq, float *dk,
+                                       float *dv, float *dg, float *dbeta, float *dh0,
+                                       void *workspace, size_t ws_bytes, void *stream);
+
 /* Thread-local text describing the last non-OK status of this thread. */
 const char *gdr_last_error(void);
 

@@ -38,6 +38,8 @@ def test_header_declares_the_boundary():
                             "gdr_prefill_fused_workspace_bytes", "gdr_prefill_chunked_fused",
                             "gdr_prefill_varlen_fused", "gdr_decode_tokens_fused",
                             "gdr_backward_workspace_bytes", "gdr_backward_chunked",
+                            "gdr_backward_varlen_workspace_bytes",
+                            "gdr_backward_chunked_varlen",
                             "gdr_last_error", "gdr_version"])
 
 
@@ -274,6 +276,40 @@ def test_backward_rejects(lib):
     assert call(dg=None) == EINVAL
     assert call(ws_bytes=100) == EINVAL and "workspace" in err()
     assert call(ws=MIS) == EINVAL
+
+
+def test_backward_varlen_rejects(lib):
+    err = lambda: lib.gdr_last_error().decode()  # noqa: E731
+    # as the fixed-length form, for tokens / 64 + N = 3 chunk slots (N = 2
+    # sequences, 100 tokens, H = 3)
+    chunks = 100 // 64 + 2
+    st = chunks * 3 * 128 * 128 * 4
+    o = (100 * 3 * 128 * 2 + 255) // 256 * 256
+    rec = chunks * 3 * (3 * 64 * 128 * 2 + 64 * 64 * 2 + 128 * 4)
+    fwd_gdn = (512 + chunks * 3 * 5632 + 255) // 256 * 256
+    assert lib.gdr_backward_varlen_workspace_bytes(1, 2, 100, 3, 128, 128) == 2 * st + o + 512 + rec
+    assert lib.gdr_backward_varlen_workspace_bytes(0, 2, 100, 3, 128, 128) == \
+        2 * st + o + fwd_gdn + rec
+    assert lib.gdr_backward_varlen_workspace_bytes(1, 2, 0, 3, 128, 128) == 0
+
+    def call(dt=1, N=2, T_total=100, ws_bytes=1 << 30, cu=FAKE, host=None, **kw):
+        hp = None
+        if host is not None:
+            arr = (ctypes.c_int32 * len(host))(*host)
+            hp = ctypes.cast(arr, ctypes.c_void_p)
+            call.keep = arr
+        return lib.gdr_backward_chunked_varlen(
+            dt, 1, N, T_total, 3, 128, 128, 64, F(1.0), cu, hp, FAKE, FAKE, FAKE, FAKE, FAKE,
+            None, kw.get("do", FAKE), None, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+            kw.get("ws", FAKE), ws_bytes, None)
+    assert call(dt=0) == EUNSUPPORTED and "bf16" in err()
+    assert call(cu=None) == EINVAL and "cu_seqlens" in err()
+    assert call(host=[0, 60, 40]) == EINVAL and "decreases" in err()
+    assert call(host=[0, 40, 90]) == EINVAL and "T_total" in err()
+    assert call(host=[1, 40, 100]) == EINVAL
+    assert call(do=None) == EINVAL and "do is NULL" in err()
+    assert call(ws_bytes=100) == EINVAL and "workspace" in err()
+    assert call(N=0) == 0
 
 
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):

@@ -72,6 +72,86 @@ def test_backward_strong_decay(gate):
     _check(got, ref, "strong decay %s" % gate)
 
 
+def _varlen_case(lens, H, D, gate, seed, scale=0.8):
+    x = synthetic.varlen_inputs(lens, H, D, torch.bfloat16, gate, seed=seed, device=DEV)
+    cu = x["cu_seqlens_host"]
+    Tt, N = int(cu[-1]), len(lens)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(seed + 1)
+    do = torch.randn((Tt, H, D), generator=gen, device=DEV).to(torch.bfloat16)
+    dht = torch.randn((N, H, D, D), generator=gen, device=DEV) * 0.1
+    return x, do, dht
+
+
+def _varlen_oracle(x, do, dht, scale):
+    """oracle.backward sequence by sequence (an empty sequence: dh0 = dht)."""
+    cu = x["cu_seqlens_host"]
+    N = len(cu) - 1
+    Tt, H, D = x["q"].shape
+    ref = [np.zeros((Tt, H, D)), np.zeros((Tt, H, D)), np.zeros((Tt, H, D)),
+           np.zeros(tuple(x["g"].shape)), np.zeros((Tt, H)), np.zeros((N, H, D, D))]
+    for n in range(N):
+        a, b = int(cu[n]), int(cu[n + 1])
+        if b == a:
+            ref[5][n] = dht[n].double().cpu().numpy()
+            continue
+        r = oracle.backward(*(t[a:b][None] for t in (x["q"], x["k"], x["v"], x["g"],
+                                                      x["beta"], do)),
+                            h0=x["h0"][n:n + 1], dht=dht[n:n + 1], scale=scale)
+        for i in range(5):
+            ref[i][a:b] = r[i][0]
+        ref[5][n] = r[5][0]
+    return ref
+
+
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_backward_varlen(gate, D):
+    """A packed batch with ragged tails, a one-token and an empty sequence."""
+    lens = [150, 1, 0, 64, 65, 200]
+    announce("backward varlen %s D=%d lengths %s" % (gate, D, lens))
+    x, do, dht = _varlen_case(lens, 2, D, gate, 60 + D)
+    got = gdr.backward_varlen(x["q"], x["k"], x["v"], x["g"], x["beta"], do, x["cu_seqlens"],
+                              h0=x["h0"], dht=dht, scale=0.8,
+                              cu_seqlens_host=x["cu_seqlens_host"])
+    sync()
+    _check(got, _varlen_oracle(x, do, dht, 0.8), "varlen %s D=%d" % (gate, D))
+
+
+def test_backward_varlen_long_sequences():
+    """Sequences of 700 to 3000 tokens, channel gate, d = 128."""
+    lens = [700, 3000, 17, 640]
+    announce("backward varlen channel D=128 lengths %s" % lens)
+    x, do, dht = _varlen_case(lens, 2, 128, "channel", 77)
+    got = gdr.backward_varlen(x["q"], x["k"], x["v"], x["g"], x["beta"], do, x["cu_seqlens"],
+                              h0=x["h0"], dht=dht, scale=0.8)
+    sync()
+    _check(got, _varlen_oracle(x, do, dht, 0.8), "varlen long")
+
+
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
+def test_backward_varlen_equal_lengths_match_fixed(gate):
+    """A packed batch of equal lengths is the fixed-length batch: the same
+    kernels on the same chunks give the same bits -- except where LDS float
+    atomics sum a chunk's rows in whatever order they arrive (dg, dbeta),
+    which agree to fp32 rounding."""
+    B, T, H, D = 3, 150, 2, 128
+    x = synthetic.prefill_inputs(B, T, H, D, torch.bfloat16, gate, seed=88, device=DEV)
+    do, dht = _upstream(B, T, H, D, 89)
+    fixed = gdr.backward(x["q"], x["k"], x["v"], x["g"], x["beta"], do, h0=x["h0"], dht=dht)
+    cu = torch.arange(0, (B + 1) * T, T, dtype=torch.int32, device=DEV)
+    flat = lambda t: t.reshape((B * T,) + tuple(t.shape[2:]))  # noqa: E731
+    packed = gdr.backward_varlen(*(flat(x[n]) for n in ("q", "k", "v", "g", "beta")), flat(do),
+                                 cu, h0=x["h0"], dht=dht)
+    sync()
+    for n, a, b in zip(NAMES, fixed, packed):
+        a = a if n == "dh0" else flat(a)
+        if n in ("dg", "dbeta"):
+            assert float((a - b).abs().max()) <= 1e-5 * float(a.abs().max()), n
+        else:
+            assert torch.equal(a, b), n
+
+
 @pytest.mark.parametrize("gate", ["scalar", "channel"])
 def test_backward_without_h0_and_dht(gate):
     announce("backward no h0/dht %s" % gate)
