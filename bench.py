@@ -26,7 +26,8 @@ The same line carries:
                 slot-indexed pool, the packed KDA prefill through a pool, and
                 the GDN and KDA prefill on raw projections (fused q/k
                 normalisation, beta and gate from bf16 logits), and the
-                backward of the GDN and KDA prefill workloads.
+                backward of the GDN and KDA prefill workloads and of the
+                packed KDA workload.
 
 Defaults: 100 warmup steps and 200 timed steps (a fifth of each for the
 decode and varlen workloads): the GPU reaches its steady clock only after
@@ -35,7 +36,7 @@ about a hundred prefill calls, so shorter warm-ups time part of the ramp.
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
                        [--only-headline] [--no-cpu-baseline]
                        [--only {kda_prefill,decode,varlen,draft,varlen_pool,fused_gdn,fused_kda,
-                                backward_gdn,backward_kda}]
+                                backward_gdn,backward_kda,backward_kda_varlen}]
                        (one workload, for profiling)
 """
 import argparse
@@ -186,6 +187,40 @@ def bench_backward(gdr, synthetic, torch, dev, B, T, H, gate, seed, steps, warmu
     return ms
 
 
+def bench_backward_varlen(gdr, synthetic, torch, dev, steps, warmup):
+    """Gradients of the packed KDA prefill (gdr_backward_chunked_varlen) on the
+    varlen workload: 16 sequences of 512..65536 tokens, H = 32."""
+    lens = synthetic.varlen_lengths(943)
+    H = 32
+    x = synthetic.varlen_inputs(lens, H, D, torch.bfloat16, "channel", seed=1004, device=dev)
+    Tt, N = sum(lens), len(lens)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1054)
+    do = torch.randn((Tt, H, D), generator=gen, device=dev).to(torch.bfloat16)
+    dht = torch.randn((N, H, D, D), generator=gen, device=dev) * 0.1
+    lib = gdr._load()
+    import ctypes
+    f32 = dict(device=dev, dtype=torch.float32)
+    outs = [torch.empty((Tt, H, D), **f32) for _ in range(3)] + \
+        [torch.empty(x["g"].shape, **f32), torch.empty((Tt, H), **f32),
+         torch.empty((N, H, D, D), **f32)]
+    nbytes = int(lib.gdr_backward_varlen_workspace_bytes(1, N, Tt, H, D, D))
+    ws = torch.empty(nbytes, device=dev, dtype=torch.uint8)
+    stream = torch.cuda.current_stream(dev)
+    P = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    args = [1, 1, N, Tt, H, D, D, C, ctypes.c_float(1.0), P(x["cu_seqlens"]), None,
+            P(x["q"]), P(x["k"]), P(x["v"]), P(x["g"]), P(x["beta"]), P(x["h0"]), P(do), P(dht)] + \
+        [P(t) for t in outs] + [P(ws), ctypes.c_size_t(nbytes), ctypes.c_void_p(stream.cuda_stream)]
+
+    def step(i):
+        rc = lib.gdr_backward_chunked_varlen(*args)
+        if rc:
+            raise RuntimeError(lib.gdr_last_error().decode())
+    ms = timed(step, steps, warmup, stream)
+    del x, outs, ws
+    return ms, Tt, N
+
+
 def backward_bytes(tokens_heads, units, gate, h0=True):
     """Algorithmic HBM bytes of one backward call: q, k, v, do in bf16, g and
     beta read; dq, dk, dv in fp32, dg and dbeta written, per token-head;
@@ -322,7 +357,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--only-headline", action="store_true")
     ap.add_argument("--only", choices=["kda_prefill", "decode", "varlen", "draft", "varlen_pool",
-                                       "fused_gdn", "fused_kda", "backward_gdn", "backward_kda"],
+                                       "fused_gdn", "fused_kda", "backward_gdn", "backward_kda",
+                                       "backward_kda_varlen"],
                     default=None,
                     help="time one secondary workload alone (for profiling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -372,6 +408,10 @@ def main():
                                 args.steps, args.warmup, h0=False)
             name = "backward_kda_B2_H32_T8192_d128_bf16"
         print(json.dumps({"workload": name, "ms_per_step": ms}))
+        return
+    if args.only == "backward_kda_varlen":
+        ms, _, _ = bench_backward_varlen(gdr, synthetic, torch, dev, args.steps, args.warmup)
+        print(json.dumps({"workload": "backward_kda_varlen_N16_H32_d128_bf16", "ms_per_step": ms}))
         return
     if args.only == "draft":
         md, mc, _, _, _, _ = bench_draft(gdr, synthetic, torch, dev, args.steps, args.warmup)
@@ -489,6 +529,13 @@ def main():
                         "tokens_per_s": B_ * T_ / (msb * 1e-3),
                         "GB_per_s": bb / (msb * 1e-3) / 1e9,
                         "frac_hbm": bb / (msb * 1e-3) / 1e9 / HBM_PEAK_GBS})
+        msv, tokv, nv = bench_backward_varlen(gdr, synthetic, torch, dev,
+                                              max(3, args.steps // 40), max(1, args.warmup // 50))
+        bb = backward_bytes(tokv * 32, nv * 32, "channel", True)
+        sec.append({"workload": "backward_kda_varlen_N16_H32_d128_bf16", "tokens": tokv,
+                    "ms_per_step": msv, "tokens_per_s": tokv / (msv * 1e-3),
+                    "GB_per_s": bb / (msv * 1e-3) / 1e9,
+                    "frac_hbm": bb / (msv * 1e-3) / 1e9 / HBM_PEAK_GBS})
         line["secondary"] = sec
 
     if not args.no_cpu_baseline:

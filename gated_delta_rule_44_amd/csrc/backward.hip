@@ -833,12 +833,15 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(BwdArgs a) {
 // the chunked form, with dSg = dS_C Diag(e^{b_C}),
 //     dU = Kb dSg^T + scale P^T dO,    dS_0 = dSg + scale dO^T Qt - dU^T W,
 // W = T Kt; the rows of dS (value index) never mix, so one workgroup owns a
-// 32-row slice of one (sequence, head) and walks its chunks from the last,
-// dS in fp32 accumulators (wave w: rows 16 (w & 1) .., key blocks
-// 4 (w >> 1) .. +3), staging each chunk's ChainRec and dO slice in LDS.  It
-// stores every chunk's dS_C and finally dS_0 (dh0).
+// BVA-row slice of one (sequence, head) and walks its chunks from the last,
+// dS in fp32 accumulators (each wave a quarter of the key columns), staging
+// each chunk's ChainRec and dO slice in LDS (the next chunk's loaded into
+// registers meanwhile).  It stores every chunk's dS_C and finally dS_0
+// (dh0).  Two workgroups fit on a CU: when there are more (sequence, head,
+// slice) units than CUs, that doubles the chunks in flight.
 // ===========================================================================
-constexpr int BVA = 32;     // value rows per chain workgroup
+constexpr int BVA = 16;     // value rows per chain workgroup (76.8 KB of LDS at D = 128: two per CU)
+constexpr int NVB = BVA / 16, NDP = BVA / 8;   // 16-row value blocks; 8-wide dO pieces per row
 
 template <int D> struct ChainSmem {
     static constexpr int PD = D + 8, PV = BVA + 8;
@@ -859,7 +862,7 @@ __global__ __launch_bounds__(256) void adjoint_chain_kernel(BwdArgs a) {
     using R = ChainRec<D>;
     constexpr int PD = Sm::PD, PV = Sm::PV;
     constexpr int NTL = D / BVA;
-    constexpr int CB = D / 32;        // key blocks per wave: 32 x D of dS over 4 waves
+    constexpr int CB = D * NVB / 64;  // key blocks per wave: BVA x D of dS over 4 waves
     __shared__ Sm sm;
     // the value slices of one (sequence, head) on one XCD
     const int bid = blockIdx.x;
@@ -883,7 +886,7 @@ __global__ __launch_bounds__(256) void adjoint_chain_kernel(BwdArgs a) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l15 = lane & 15, q4 = lane >> 4;
-    const int ib = w & 1, jb0 = CB * (w >> 1);
+    const int ib = w % NVB, jb0 = CB * (w / NVB);
     const size_t rowD = (size_t)a.H * D;
     const size_t bh = (size_t)b * a.H + h;
 
@@ -917,11 +920,11 @@ __global__ __launch_bounds__(256) void adjoint_chain_kernel(BwdArgs a) {
             rp[it] = *reinterpret_cast<const bf16x8 *>(rec + R::P + 2 * (r * C + sc));
         }
         if (tid < D) rec_ = reinterpret_cast<const float *>(rec + R::EC)[tid];
-        const int t0 = c * C, r = tid >> 2;                 // 64 rows x 4 pieces of 8
+        const int t0 = c * C, r = tid / NDP;                // 64 rows x NDP pieces of 8
         rdo = bf16x8{};
-        if (r < len - t0)
+        if (tid < C * NDP && r < len - t0)
             rdo = *reinterpret_cast<const bf16x8 *>(static_cast<const bf16 *>(a.dout) +
-                                                    ((size_t)(seq0 + t0 + r) * a.H + h) * D + i0 + 8 * (tid & 3));
+                                                    ((size_t)(seq0 + t0 + r) * a.H + h) * D + i0 + 8 * (tid % NDP));
     };
     static_assert(C * D / 8 % 256 == 0 && C * C / 8 % 256 == 0, "record pieces per thread");
     if (nch > 0) fetch(nch - 1);
@@ -947,7 +950,7 @@ __global__ __launch_bounds__(256) void adjoint_chain_kernel(BwdArgs a) {
             *reinterpret_cast<bf16x8 *>(&sm.P[r * PC + sc]) = rp[it];
         }
         if (tid < D) sm.eC[tid] = rec_;
-        *reinterpret_cast<bf16x8 *>(&sm.dO[(tid >> 2) * PV + 8 * (tid & 3)]) = rdo;
+        if (tid < C * NDP) *reinterpret_cast<bf16x8 *>(&sm.dO[(tid / NDP) * PV + 8 * (tid % NDP)]) = rdo;
         if (c > 0) fetch(c - 1);
         __syncthreads();
         // dSg = dS e^{b_C} as hi + lo bf16
@@ -967,7 +970,7 @@ __global__ __launch_bounds__(256) void adjoint_chain_kernel(BwdArgs a) {
         __syncthreads();
         // dU = Kb dSg^T + scale P^T dO: wave w takes row block w, both value blocks
 #pragma unroll
-        for (int vb = 0; vb < 2; ++vb) {
+        for (int vb = 0; vb < NVB; ++vb) {
             f32x4 x = {0.f, 0.f, 0.f, 0.f}, y = x;
 #pragma unroll
             for (int kk = 0; kk < D / 32; ++kk) {
