@@ -5,7 +5,9 @@
 //     S_t = S_{t-1} Diag(a_t)(I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
 //     o_t = scale * S_t q_t,   a_t = e^{g_t}.
 // For upstream gradients dO (of o) and dS_T (of the final state) the
-// backward returns dq, dk, dv, dg, dbeta and dS_0 in three stages:
+// backward returns dq, dk, dv, dg, dbeta and dS_0 in three stages, for a
+// fixed-length or a packed batch alike (per-chunk data is indexed by global
+// chunk, the chunks of all sequences numbered one after the other):
 //
 // 1. the chunked forward (chunked.hip / chunked_chain.hip) with its
 //    optional output of the state entering every chunk of 64 tokens.
