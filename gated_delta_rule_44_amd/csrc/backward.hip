@@ -166,25 +166,25 @@ template <int D> struct ChainRec {
 
 // Channel gate: b = running sums down the rows of the chunk's g [C][D]
 // (global, token stride gstr, rows at or past Cc as zeros), into gs [C][D]
-// in LDS.  All threads load with 16-byte loads; then 256 / D parts of the
-// rows per channel are summed by one thread each and offset by the parts
-// above (tot: 256 floats of LDS).  Ends with a barrier.
-template <int D>
+// in LDS.  All NT threads load with 16-byte loads; then NT / D parts of
+// the rows per channel are summed by one thread each and offset by the
+// parts above (tot: NT floats of LDS).  Ends with a barrier.
+template <int D, int NT>
 __device__ inline void gate_running_sums(float *gs, float *tot, const float *gg, size_t gstr, int Cc, int tid) {
-    constexpr int NG = C * D / 4 / 256;
+    constexpr int NG = C * D / 4 / NT;
     f32x4 gv[NG];
 #pragma unroll
     for (int it = 0; it < NG; ++it) {
-        const int p = it * 256 + tid, r = p / (D / 4), j = 4 * (p % (D / 4));
+        const int p = it * NT + tid, r = p / (D / 4), j = 4 * (p % (D / 4));
         gv[it] = r < Cc ? *reinterpret_cast<const f32x4 *>(gg + (size_t)r * gstr + j) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
     for (int it = 0; it < NG; ++it) {
-        const int p = it * 256 + tid, r = p / (D / 4), j = 4 * (p % (D / 4));
+        const int p = it * NT + tid, r = p / (D / 4), j = 4 * (p % (D / 4));
         *reinterpret_cast<f32x4 *>(gs + r * D + j) = gv[it];
     }
     __syncthreads();
-    constexpr int NH = 256 / D, RH = C / NH;
+    constexpr int NH = NT / D, RH = C / NH;
     const int j = tid % D, part = tid / D;
     float rs[RH], run = 0.f;
 #pragma unroll
@@ -234,11 +234,13 @@ __device__ inline bool locate_chunk(const BwdArgs &a, long long gc, ChunkLoc &L)
 
 // PREP: stop after T and write the chunk's ChainRec (no S0 or dS_C needed).
 template <int D, bool CH, bool PREP>
-__global__ __launch_bounds__(256) void chunk_grad_kernel(BwdArgs a) {
+__global__ __launch_bounds__(512) void chunk_grad_kernel(BwdArgs a) {
     using Sm = GradSmem<D>;
     constexpr int PD = Sm::PD;
     constexpr int KD = D / 32;         // 32-wide k steps over D
     constexpr int NB = D / 16;         // 16-wide column blocks of a C x D matrix
+    constexpr int NT = 512;            // eight waves: two per row block I, each
+    constexpr int NBH = NB / 2;        // with half of the column blocks (or of J)
     __shared__ Sm sm;
 
     const int h = blockIdx.x % a.H;
@@ -249,6 +251,7 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(BwdArgs a) {
     const int Cc = loc.len - t0 < C ? (int)(loc.len - t0) : C;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int half = w >> 2, cb0 = half * NBH;
     const int l15 = lane & 15, q4 = lane >> 4;
     const size_t rowD = (size_t)a.H * D;                      // token stride of q, k, v, o
     const size_t tok0 = (size_t)(loc.seq0 + t0);              // first token row
@@ -279,26 +282,26 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(BwdArgs a) {
     // q and k of the chunk in registers (16-byte loads from all threads, all
     // in flight together), the channel gate g in LDS, rows past the end as
     // zeros
-    constexpr int NQ = C * D / 8 / 256;        // 16-byte pieces of q per thread
+    constexpr int NQ = C * D / 8 / NT;         // 16-byte pieces of q per thread
     float *gst = reinterpret_cast<float *>(sm.R.stage);        // g, then b  [r][j]
     float *gtot = gst + C * D;                                 // part sums of g
-    static_assert(sizeof(sm.R) >= sizeof(float) * (C * D + 256), "gate staging");
+    static_assert(sizeof(sm.R) >= sizeof(float) * (C * D + NT), "gate staging");
     bf16x8 qv[NQ], kv[NQ];
 #pragma unroll
     for (int it = 0; it < NQ; ++it) {
-        const int p = it * 256 + tid, r = p / (D / 8), j = 8 * (p % (D / 8));
+        const int p = it * NT + tid, r = p / (D / 8), j = 8 * (p % (D / 8));
         qv[it] = kv[it] = bf16x8{};
         if (r < Cc) {
             qv[it] = *reinterpret_cast<const bf16x8 *>(qg + (size_t)r * rowD + j);
             kv[it] = *reinterpret_cast<const bf16x8 *>(kg + (size_t)r * rowD + j);
         }
     }
-    if constexpr (CH) gate_running_sums<D>(gst, gtot, gg, gstr, Cc, tid);
+    if constexpr (CH) gate_running_sums<D, NT>(gst, gtot, gg, gstr, Cc, tid);
     else __syncthreads();
     // gated operands Qt = q e^b, Kt = k e^b, Kb = k e^-b
 #pragma unroll
     for (int it = 0; it < NQ; ++it) {
-        const int p = it * 256 + tid, r = p / (D / 8), j = 8 * (p % (D / 8));
+        const int p = it * NT + tid, r = p / (D / 8), j = 8 * (p % (D / 8));
         float e[8];
         if constexpr (CH) {
             const f32x4 b0 = *reinterpret_cast<const f32x4 *>(gst + r * D + j);
@@ -331,15 +334,16 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(BwdArgs a) {
     }
     __syncthreads();
 
-    const int I = w;                           // this wave's 16-row block
+    const int I = w & 3;                       // this wave's 16-row block
     auto zero4 = []() { return f32x4{0.f, 0.f, 0.f, 0.f}; };
     // r, s of accumulator element e of block (I, J)
     auto rowof = [&](int e) { return 16 * I + 4 * q4 + e; };
 
     // ---- 2. A = strict_lower(Kt Kb^T), P = lower(Qt Kb^T); L = diag(beta) A
-    f32x4 Areg[4];
+    f32x4 Areg[2];                             // blocks J = 2 half + Ji
 #pragma unroll
-    for (int J = 0; J < 4; ++J) {
+    for (int Ji = 0; Ji < 2; ++Ji) {
+        const int J = 2 * half + Ji;
         f32x4 av = zero4(), pv = zero4();
         if (J <= I) {
 #pragma unroll
@@ -360,7 +364,7 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(BwdArgs a) {
             if (J < I) sm.R.inv.L[(I * (I - 1) / 2 + J) * 256 + (4 * q4 + e) * 16 + l15] = lv;
             sm.Pb[r * PC + s] = (bf16)pv[e];
         }
-        Areg[J] = av;
+        Areg[Ji] = av;
     }
     __syncthreads();
 
@@ -432,8 +436,8 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(BwdArgs a) {
     // N and T = N diag(beta) to bf16, four consecutive entries per thread
     // and read (a wave reads 1 KiB of consecutive LDS per instruction)
 #pragma unroll
-    for (int it = 0; it < C * C / 4 / 256; ++it) {
-        const int p = it * 256 + tid, r = p / (C / 4), s0 = 4 * (p % (C / 4));
+    for (int it = 0; it < C * C / 4 / NT; ++it) {
+        const int p = it * NT + tid, r = p / (C / 4), s0 = 4 * (p % (C / 4));
         const f32x4 nv = *reinterpret_cast<const f32x4 *>(&Nf[r * C + s0]);
         const f32x4 bv = *reinterpret_cast<const f32x4 *>(&sm.beta[s0]);
         bf16x4 nb, tb;
@@ -455,7 +459,8 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(BwdArgs a) {
         char *rec = static_cast<char *>(a.recs) + sbh * R::BYTES;
         bf16 *Wg = reinterpret_cast<bf16 *>(rec + R::W);
 #pragma unroll
-        for (int cb = 0; cb < NB; ++cb) {
+        for (int cbi = 0; cbi < NBH; ++cbi) {
+            const int cb = cb0 + cbi;
             f32x4 x = zero4();
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
@@ -469,13 +474,13 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(BwdArgs a) {
         }
         bf16 *Qg = reinterpret_cast<bf16 *>(rec + R::QT);
         bf16 *Kg = reinterpret_cast<bf16 *>(rec + R::KB);
-        for (int p = tid; p < C * D / 8; p += 256) {
+        for (int p = tid; p < C * D / 8; p += NT) {
             const int r = p / (D / 8), j = 8 * (p % (D / 8));
             *reinterpret_cast<bf16x8 *>(Qg + r * D + j) = *reinterpret_cast<const bf16x8 *>(&sm.Qt[r * PD + j]);
             *reinterpret_cast<bf16x8 *>(Kg + r * D + j) = *reinterpret_cast<const bf16x8 *>(&sm.Kb[r * PD + j]);
         }
         bf16 *Pg = reinterpret_cast<bf16 *>(rec + R::P);
-        for (int p = tid; p < C * C / 8; p += 256) {
+        for (int p = tid; p < C * C / 8; p += NT) {
             const int r = p / (C / 8), sc = 8 * (p % (C / 8));
             *reinterpret_cast<bf16x8 *>(Pg + r * C + sc) = *reinterpret_cast<const bf16x8 *>(&sm.Pb[r * PC + sc]);
         }
@@ -492,31 +497,32 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(BwdArgs a) {
     //         products over i (dT, dP, dQt, dKt, dKbh) accumulate in
     //         registers.  db_C's S0 part, sum_i dSg_i.S0_i, is summed from
     //         the fp32 loads.
-    float Nreg[4][4];                          // N of this wave's blocks, in fp32
+    float Nreg[2][4];                          // N of this wave's blocks, in fp32
 #pragma unroll
-    for (int J = 0; J < 4; ++J)
+    for (int Ji = 0; Ji < 2; ++Ji)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) Nreg[J][e] = Nf[rowof(e) * C + 16 * J + l15];
+        for (int e = 0; e < 4; ++e) Nreg[Ji][e] = Nf[rowof(e) * C + 16 * (2 * half + Ji) + l15];
     __syncthreads();                           // Nf no longer read
 
     auto &sl = sm.R.sl;
     constexpr int PQ = Sm::PQ;
-    constexpr int NS4 = 32 * D / 4 / 256;      // 16-byte pieces of a state slice per thread
+    constexpr int NS4 = 32 * D / 4 / NT;       // 16-byte pieces of a state slice per thread
     f32x4 ps[NS4], pd[NS4];
     bf16x8 pv, po;
     float dbc[4] = {0.f, 0.f, 0.f, 0.f};       // columns jc .. jc + 3 of db_C
     const int jc = 4 * (tid % (D / 4));
-    const int vr = tid >> 2, vc = 8 * (tid & 3);   // V, dO slice: row, column in the slice
+    const bool vown = tid < 256;               // threads staging the V and dO slices
+    const int vr = (tid & 255) >> 2, vc = 8 * (tid & 3);   // their row, column in the slice
     auto fetch = [&](int sc) {
 #pragma unroll
         for (int it = 0; it < NS4; ++it) {
-            const int ii = (it * 256 + tid) / (D / 4);
+            const int ii = (it * NT + tid) / (D / 4);
             const size_t o = (size_t)(32 * sc + ii) * D + jc;
             ps[it] = *reinterpret_cast<const f32x4 *>(S0 + o);
             pd[it] = *reinterpret_cast<const f32x4 *>(dSC + o);
         }
         pv = po = bf16x8{};
-        if (vr < Cc) {
+        if (vown && vr < Cc) {
             pv = *reinterpret_cast<const bf16x8 *>(vg + (size_t)vr * rowD + 32 * sc + vc);
             po = *reinterpret_cast<const bf16x8 *>(dog + (size_t)vr * rowD + 32 * sc + vc);
         }
@@ -525,7 +531,7 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(BwdArgs a) {
         const f32x4 ec = *reinterpret_cast<const f32x4 *>(&sm.eC[jc]);
 #pragma unroll
         for (int it = 0; it < NS4; ++it) {
-            const int ii = (it * 256 + tid) / (D / 4);
+            const int ii = (it * NT + tid) / (D / 4);
             bf16x4 sh, sl4, dh, dl;
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
@@ -541,23 +547,26 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(BwdArgs a) {
             *reinterpret_cast<bf16x4 *>(&sl.dSh[ii * PD + jc]) = dh;
             *reinterpret_cast<bf16x4 *>(&sl.dSl[ii * PD + jc]) = dl;
         }
-        *reinterpret_cast<bf16x8 *>(&sl.X[vr * PQ + vc]) = pv;
-        *reinterpret_cast<bf16x8 *>(&sl.dO[vr * PQ + vc]) = po;
+        if (vown) {
+            *reinterpret_cast<bf16x8 *>(&sl.X[vr * PQ + vc]) = pv;
+            *reinterpret_cast<bf16x8 *>(&sl.dO[vr * PQ + vc]) = po;
+        }
     };
 
-    f32x4 dQt[NB], dKt[NB], dKb[NB], dKbh[NB], dPa[4], dTa[4];
+    // column blocks cb0 + cbi and row blocks J = 2 half + Ji of this wave
+    f32x4 dQt[NBH], dKt[NBH], dKb[NBH], dKbh[NBH], dPa[2], dTa[2];
 #pragma unroll
-    for (int cb = 0; cb < NB; ++cb) dQt[cb] = dKt[cb] = dKbh[cb] = zero4();
+    for (int cbi = 0; cbi < NBH; ++cbi) dQt[cbi] = dKt[cbi] = dKbh[cbi] = zero4();
 #pragma unroll
-    for (int J = 0; J < 4; ++J) dPa[J] = dTa[J] = zero4();
+    for (int Ji = 0; Ji < 2; ++Ji) dPa[Ji] = dTa[Ji] = zero4();
     fetch(0);
     for (int sc = 0; sc < D / 32; ++sc) {
         put();
         if (sc + 1 < D / 32) fetch(sc + 1);
         __syncthreads();
         // X = V - Kt S0^T and dU = Kb dSg^T + scale P^T dO on the slice
-#pragma unroll
-        for (int cl = 0; cl < 2; ++cl) {
+        {
+            const int cl = half;
             f32x4 x = zero4(), du = zero4(), dp = zero4();
 #pragma unroll
             for (int kk = 0; kk < KD; ++kk) {
@@ -581,8 +590,8 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(BwdArgs a) {
         }
         __syncthreads();
         // U = T X, dX = T^T dU (= dV; the diagonal of T compensated), dT += dU X^T
-#pragma unroll
-        for (int cl = 0; cl < 2; ++cl) {
+        {
+            const int cl = half;
             f32x4 u = zero4(), dx = zero4();
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
@@ -602,8 +611,10 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(BwdArgs a) {
         {
             const bf16x8 du = frag_rows(sl.dU, PQ, 16 * I, 0, lane);
 #pragma unroll
-            for (int J = 0; J < 4; ++J)
-                if (J <= I) dTa[J] = mfma32(du, frag_rows(sl.X, PQ, 16 * J, 0, lane), dTa[J]);
+            for (int Ji = 0; Ji < 2; ++Ji) {
+                const int J = 2 * half + Ji;
+                if (J <= I) dTa[Ji] = mfma32(du, frag_rows(sl.X, PQ, 16 * J, 0, lane), dTa[Ji]);
+            }
         }
         __syncthreads();
         // dP += dO U^T;  over the slice's rows of S0 and dSg: dQt += dO S0,
@@ -613,15 +624,18 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(BwdArgs a) {
             const bf16x8 ax = frag_rows(sl.dX, PQ, 16 * I, 0, lane);
             const bf16x8 au = frag_rows(sl.U, PQ, 16 * I, 0, lane);
 #pragma unroll
-            for (int J = 0; J < 4; ++J)
-                if (J <= I) dPa[J] = mfma32(ao, frag_rows(sl.U, PQ, 16 * J, 0, lane), dPa[J]);
+            for (int Ji = 0; Ji < 2; ++Ji) {
+                const int J = 2 * half + Ji;
+                if (J <= I) dPa[Ji] = mfma32(ao, frag_rows(sl.U, PQ, 16 * J, 0, lane), dPa[Ji]);
+            }
 #pragma unroll
-            for (int cb = 0; cb < NB; ++cb) {
+            for (int cbi = 0; cbi < NBH; ++cbi) {
+                const int cb = cb0 + cbi;
                 const Frag2 s0{frag_cols(sl.S0h, PD, 0, 16 * cb, lane), frag_cols(sl.S0l, PD, 0, 16 * cb, lane)};
-                dQt[cb] = mfma_ab2(ao, s0, dQt[cb]);
-                dKt[cb] = mfma_ab2(ax, s0, dKt[cb]);
-                dKbh[cb] = mfma_ab2(au, Frag2{frag_cols(sl.dSh, PD, 0, 16 * cb, lane),
-                                              frag_cols(sl.dSl, PD, 0, 16 * cb, lane)}, dKbh[cb]);
+                dQt[cbi] = mfma_ab2(ao, s0, dQt[cbi]);
+                dKt[cbi] = mfma_ab2(ax, s0, dKt[cbi]);
+                dKbh[cbi] = mfma_ab2(au, Frag2{frag_cols(sl.dSh, PD, 0, 16 * cb, lane),
+                                                frag_cols(sl.dSl, PD, 0, 16 * cb, lane)}, dKbh[cbi]);
             }
         }
         __syncthreads();
@@ -632,19 +646,20 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(BwdArgs a) {
     // ---- 8, 11. dP = scale lower(dO U^T) (its diagonal's rounding kept);
     //         dT = lower(dU X^T): dbeta_s += sum_r dT_rs N_rs, dN = dT diag(beta)
 #pragma unroll
-    for (int J = 0; J < 4; ++J) {
+    for (int Ji = 0; Ji < 2; ++Ji) {
+        const int J = 2 * half + Ji;
         const int s = 16 * J + l15;
         const float bs_ = sm.beta[s];
         float part = 0.f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int r = rowof(e);
-            const float pv = s <= r ? a.scale * dPa[J][e] : 0.f;
+            const float pv = s <= r ? a.scale * dPa[Ji][e] : 0.f;
             const bf16 pb = (bf16)pv;
             sm.dPb[r * PC + s] = pb;
             if (s == r) sm.pcor[r] = pv - (float)pb;
-            const float tv = s <= r ? dTa[J][e] : 0.f;
-            part += tv * Nreg[J][e];
+            const float tv = s <= r ? dTa[Ji][e] : 0.f;
+            part += tv * Nreg[Ji][e];
             sm.Pb[r * PC + s] = (bf16)(tv * bs_);
         }
         part = sum_quads(part);
@@ -654,30 +669,32 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(BwdArgs a) {
 
     // ---- 9, 10. dQt = scale dO S0 + dP Kb;  dKb = dP^T Qt;  dKt = -dX S0
 #pragma unroll
-    for (int cb = 0; cb < NB; ++cb) {
+    for (int cbi = 0; cbi < NBH; ++cbi) {
+        const int cb = cb0 + cbi;
         f32x4 y = zero4();
-        dKb[cb] = zero4();
+        dKb[cbi] = zero4();
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             y = mfma32(frag_rows(sm.dPb, PC, 16 * I, 32 * kk, lane), frag_cols(sm.Kb, PD, 32 * kk, 16 * cb, lane), y);
-            dKb[cb] = mfma32(frag_cols(sm.dPb, PC, 32 * kk, 16 * I, lane),
-                             frag_cols(sm.Qt, PD, 32 * kk, 16 * cb, lane), dKb[cb]);
+            dKb[cbi] = mfma32(frag_cols(sm.dPb, PC, 32 * kk, 16 * I, lane),
+                              frag_cols(sm.Qt, PD, 32 * kk, 16 * cb, lane), dKb[cbi]);
         }
-        dQt[cb] = a.scale * dQt[cb] + y;
-        dKt[cb] = -dKt[cb];
+        dQt[cbi] = a.scale * dQt[cbi] + y;
+        dKt[cbi] = -dKt[cbi];
         const int j = 16 * cb + l15;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int r = rowof(e);
-            dQt[cb][e] += sm.pcor[r] * (float)sm.Kb[r * PD + j];
-            dKb[cb][e] += sm.pcor[r] * (float)sm.Qt[r * PD + j];
+            dQt[cbi][e] += sm.pcor[r] * (float)sm.Kb[r * PD + j];
+            dKb[cbi][e] += sm.pcor[r] * (float)sm.Qt[r * PD + j];
         }
     }
 
     // ---- 14. Y = dN N^T (into Tb), dM = -N^T Y;  dbeta_r += sum_s dM_rs A_rs;
     //          dA = strict_lower(diag(beta) dM) (into dPb)
 #pragma unroll
-    for (int J = 0; J < 4; ++J) {
+    for (int Ji = 0; Ji < 2; ++Ji) {
+        const int J = 2 * half + Ji;
         f32x4 y = zero4();
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
@@ -689,7 +706,8 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(BwdArgs a) {
     __syncthreads();
     float dbr[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int J = 0; J < 4; ++J) {
+    for (int Ji = 0; Ji < 2; ++Ji) {
+        const int J = 2 * half + Ji;
         f32x4 m = zero4();
         if (J <= I) {
 #pragma unroll
@@ -701,7 +719,7 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(BwdArgs a) {
         for (int e = 0; e < 4; ++e) {
             const int r = rowof(e);
             const float dm = s < r ? -m[e] : 0.f;
-            dbr[e] += dm * Areg[J][e];
+            dbr[e] += dm * Areg[Ji][e];
             sm.dPb[r * PC + s] = (bf16)(sm.beta[r] * dm);
         }
     }
@@ -714,11 +732,12 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(BwdArgs a) {
 
     // ---- 15. dKt += dA Kb;  dKb += dA^T Kt
 #pragma unroll
-    for (int cb = 0; cb < NB; ++cb) {
+    for (int cbi = 0; cbi < NBH; ++cbi) {
+        const int cb = cb0 + cbi;
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-            dKt[cb] = mfma32(frag_rows(sm.dPb, PC, 16 * I, 32 * kk, lane), frag_cols(sm.Kb, PD, 32 * kk, 16 * cb, lane), dKt[cb]);
-            dKb[cb] = mfma32(frag_cols(sm.dPb, PC, 32 * kk, 16 * I, lane), frag_cols(sm.Kt, PD, 32 * kk, 16 * cb, lane), dKb[cb]);
+            dKt[cbi] = mfma32(frag_rows(sm.dPb, PC, 16 * I, 32 * kk, lane), frag_cols(sm.Kb, PD, 32 * kk, 16 * cb, lane), dKt[cbi]);
+            dKb[cbi] = mfma32(frag_cols(sm.dPb, PC, 32 * kk, 16 * I, lane), frag_cols(sm.Kt, PD, 32 * kk, 16 * cb, lane), dKb[cbi]);
         }
     }
     __syncthreads();                           // gated operands no longer read
@@ -735,7 +754,8 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(BwdArgs a) {
     static_assert(sizeof(sm.Qt) + sizeof(sm.Kt) >= sizeof(float) * C * D, "E overlay");
     float rowacc[4] = {0.f, 0.f, 0.f, 0.f}, hacc[4] = {0.f, 0.f, 0.f, 0.f};   // scalar gate
 #pragma unroll
-    for (int cb = 0; cb < NB; ++cb) {
+    for (int cbi = 0; cbi < NBH; ++cbi) {
+        const int cb = cb0 + cbi;
         const int j = 16 * cb + l15;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -743,8 +763,8 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(BwdArgs a) {
             const float qt = (float)sm.Qt[r * PD + j];
             const float kt = (float)sm.Kt[r * PD + j];
             const float kb = (float)sm.Kb[r * PD + j];
-            const float rowsum = dQt[cb][e] * qt + dKt[cb][e] * kt - dKb[cb][e] * kb;
-            const float hsum = dKbh[cb][e] * kb;
+            const float rowsum = dQt[cbi][e] * qt + dKt[cbi][e] * kt - dKb[cbi][e] * kb;
+            const float hsum = dKbh[cbi][e] * kb;
             if (CH) {
                 dbf[r * D + j] = rowsum;
                 hf[r * D + j] = hsum;
@@ -766,11 +786,12 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(BwdArgs a) {
         }
     }
     __syncthreads();                           // Qt, Kt no longer read
-    float *ptot = reinterpret_cast<float *>(sm.R.stage) + C * D;   // 512 floats past db
-    static_assert(sizeof(sm.R) >= sizeof(float) * (C * D + 512), "part sums");
-    if constexpr (CH) gate_running_sums<D>(Ef, ptot, gg, gstr, Cc, tid);   // b, over Qt and Kt
+    float *ptot = reinterpret_cast<float *>(sm.R.stage) + C * D;   // 2 NT floats past db
+    static_assert(sizeof(sm.R) >= sizeof(float) * (C * D + 2 * NT), "part sums");
+    if constexpr (CH) gate_running_sums<D, NT>(Ef, ptot, gg, gstr, Cc, tid);   // b, over Qt and Kt
 #pragma unroll
-    for (int cb = 0; cb < NB; ++cb) {
+    for (int cbi = 0; cbi < NBH; ++cbi) {
+        const int cb = cb0 + cbi;
         const int j = 16 * cb + l15;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -779,17 +800,17 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(BwdArgs a) {
             const float Ei = __builtin_amdgcn_rcpf(E);
             if (r < Cc) {
                 const size_t o = ((tok0 + r) * a.H + h) * D + j;
-                a.dq[o] = dQt[cb][e] * E;
-                a.dk[o] = dKt[cb][e] * E + (dKb[cb][e] + dKbh[cb][e]) * Ei;
+                a.dq[o] = dQt[cbi][e] * E;
+                a.dk[o] = dKt[cbi][e] * E + (dKb[cbi][e] + dKbh[cbi][e]) * Ei;
             }
         }
     }
     __syncthreads();
     if (CH) {
-        // dg_s = sum_{r >= s} db_r + db_C + sum_{r < s} h_r per channel: 256 / D
+        // dg_s = sum_{r >= s} db_r + db_C + sum_{r < s} h_r per channel: NT / D
         // parts of the rows per channel, each taken by one thread, with the
         // sums of the other parts as offsets
-        constexpr int NH = 256 / D, RH = C / NH;
+        constexpr int NH = NT / D, RH = C / NH;
         const int j = tid % D, part = tid / D;
         float hs = 0.f, ds = 0.f;
 #pragma unroll
@@ -1039,19 +1060,19 @@ hipError_t launch_backward(int D, const BwdArgs &a, hipStream_t s) {
     const long long chain_blocks = ((heads + 7) / 8) * 8 * (D / BVA);
     const long long chunk_blocks = a.chunks * a.H;
     if (chain_blocks >= (1LL << 31) || chunk_blocks >= (1LL << 31)) return hipErrorInvalidValue;
-    dim3 gr((unsigned)chain_blocks), gc((unsigned)chunk_blocks), blk(256);
+    dim3 gr((unsigned)chain_blocks), gc((unsigned)chunk_blocks), blk(256), blk8(512);
     if (D == 128) {
-        if (a.channel_gate) hipLaunchKernelGGL((chunk_grad_kernel<128, true, true>), gc, blk, 0, s, a);
-        else                hipLaunchKernelGGL((chunk_grad_kernel<128, false, true>), gc, blk, 0, s, a);
+        if (a.channel_gate) hipLaunchKernelGGL((chunk_grad_kernel<128, true, true>), gc, blk8, 0, s, a);
+        else                hipLaunchKernelGGL((chunk_grad_kernel<128, false, true>), gc, blk8, 0, s, a);
         hipLaunchKernelGGL(adjoint_chain_kernel<128>, gr, blk, 0, s, a);
-        if (a.channel_gate) hipLaunchKernelGGL((chunk_grad_kernel<128, true, false>), gc, blk, 0, s, a);
-        else                hipLaunchKernelGGL((chunk_grad_kernel<128, false, false>), gc, blk, 0, s, a);
+        if (a.channel_gate) hipLaunchKernelGGL((chunk_grad_kernel<128, true, false>), gc, blk8, 0, s, a);
+        else                hipLaunchKernelGGL((chunk_grad_kernel<128, false, false>), gc, blk8, 0, s, a);
     } else {
-        if (a.channel_gate) hipLaunchKernelGGL((chunk_grad_kernel<64, true, true>), gc, blk, 0, s, a);
-        else                hipLaunchKernelGGL((chunk_grad_kernel<64, false, true>), gc, blk, 0, s, a);
+        if (a.channel_gate) hipLaunchKernelGGL((chunk_grad_kernel<64, true, true>), gc, blk8, 0, s, a);
+        else                hipLaunchKernelGGL((chunk_grad_kernel<64, false, true>), gc, blk8, 0, s, a);
         hipLaunchKernelGGL(adjoint_chain_kernel<64>, gr, blk, 0, s, a);
-        if (a.channel_gate) hipLaunchKernelGGL((chunk_grad_kernel<64, true, false>), gc, blk, 0, s, a);
-        else                hipLaunchKernelGGL((chunk_grad_kernel<64, false, false>), gc, blk, 0, s, a);
+        if (a.channel_gate) hipLaunchKernelGGL((chunk_grad_kernel<64, true, false>), gc, blk8, 0, s, a);
+        else                hipLaunchKernelGGL((chunk_grad_kernel<64, false, false>), gc, blk8, 0, s, a);
     }
     return hipGetLastError();
 }
