@@ -170,16 +170,18 @@ template <int D> struct ChainRec {
 // the rows per channel are summed by one thread each and offset by the
 // parts above (tot: NT floats of LDS).  Ends with a barrier.
 template <int D, int NT>
-__device__ inline void gate_running_sums(float *gs, float *tot, const float *gg, size_t gstr, int Cc, int tid) {
-    constexpr int NG = C * D / 4 / NT;
-    f32x4 gv[NG];
+__device__ inline void gate_load(f32x4 (&gv)[C * D / 4 / NT], const float *gg, size_t gstr, int Cc,
+                                 int tid) {
 #pragma unroll
-    for (int it = 0; it < NG; ++it) {
+    for (int it = 0; it < C * D / 4 / NT; ++it) {
         const int p = it * NT + tid, r = p / (D / 4), j = 4 * (p % (D / 4));
         gv[it] = r < Cc ? *reinterpret_cast<const f32x4 *>(gg + (size_t)r * gstr + j) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
+}
+template <int D, int NT>
+__device__ inline void gate_sums_from(float *gs, float *tot, const f32x4 (&gv)[C * D / 4 / NT], int tid) {
 #pragma unroll
-    for (int it = 0; it < NG; ++it) {
+    for (int it = 0; it < C * D / 4 / NT; ++it) {
         const int p = it * NT + tid, r = p / (D / 4), j = 4 * (p % (D / 4));
         *reinterpret_cast<f32x4 *>(gs + r * D + j) = gv[it];
     }
@@ -199,6 +201,12 @@ __device__ inline void gate_running_sums(float *gs, float *tot, const float *gg,
 #pragma unroll
     for (int u = 0; u < RH; ++u) gs[(part * RH + u) * D + j] = rs[u] + off;
     __syncthreads();
+}
+template <int D, int NT>
+__device__ inline void gate_running_sums(float *gs, float *tot, const float *gg, size_t gstr, int Cc, int tid) {
+    f32x4 gv[C * D / 4 / NT];
+    gate_load<D, NT>(gv, gg, gstr, Cc, tid);
+    gate_sums_from<D, NT>(gs, tot, gv, tid);
 }
 
 // The chunks of all sequences are numbered one after the other: sequence n's
@@ -642,6 +650,9 @@ __global__ __launch_bounds__(512) void chunk_grad_kernel(BwdArgs a) {
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) atomicAdd(&sm.dbC[jc + u], dbc[u]);
+    // the channel gate again, for E in the last step: loads issued here
+    f32x4 gpre[CH ? C * D / 4 / NT : 1];
+    if constexpr (CH) gate_load<D, NT>(gpre, gg, gstr, Cc, tid);
 
     // ---- 8, 11. dP = scale lower(dO U^T) (its diagonal's rounding kept);
     //         dT = lower(dU X^T): dbeta_s += sum_r dT_rs N_rs, dN = dT diag(beta)
@@ -788,7 +799,7 @@ __global__ __launch_bounds__(512) void chunk_grad_kernel(BwdArgs a) {
     __syncthreads();                           // Qt, Kt no longer read
     float *ptot = reinterpret_cast<float *>(sm.R.stage) + C * D;   // 2 NT floats past db
     static_assert(sizeof(sm.R) >= sizeof(float) * (C * D + 2 * NT), "part sums");
-    if constexpr (CH) gate_running_sums<D, NT>(Ef, ptot, gg, gstr, Cc, tid);   // b, over Qt and Kt
+    if constexpr (CH) gate_sums_from<D, NT>(Ef, ptot, gpre, tid);   // b, over Qt and Kt
 #pragma unroll
     for (int cbi = 0; cbi < NBH; ++cbi) {
         const int cb = cb0 + cbi;
