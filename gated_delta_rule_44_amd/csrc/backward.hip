@@ -348,7 +348,6 @@ __global__ __launch_bounds__(512) void chunk_grad_kernel(BwdArgs a) {
     auto rowof = [&](int e) { return 16 * I + 4 * q4 + e; };
 
     // ---- 2. A = strict_lower(Kt Kb^T), P = lower(Qt Kb^T); L = diag(beta) A
-    f32x4 Areg[2];                             // blocks J = 2 half + Ji
 #pragma unroll
     for (int Ji = 0; Ji < 2; ++Ji) {
         const int J = 2 * half + Ji;
@@ -372,7 +371,6 @@ __global__ __launch_bounds__(512) void chunk_grad_kernel(BwdArgs a) {
             if (J < I) sm.R.inv.L[(I * (I - 1) / 2 + J) * 256 + (4 * q4 + e) * 16 + l15] = lv;
             sm.Pb[r * PC + s] = (bf16)pv[e];
         }
-        Areg[Ji] = av;
     }
     __syncthreads();
 
@@ -719,18 +717,21 @@ __global__ __launch_bounds__(512) void chunk_grad_kernel(BwdArgs a) {
 #pragma unroll
     for (int Ji = 0; Ji < 2; ++Ji) {
         const int J = 2 * half + Ji;
-        f32x4 m = zero4();
+        f32x4 m = zero4(), av = zero4();      // A formed again (as in step 2) from Kt, Kb
         if (J <= I) {
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
                 m = mfma32(frag_cols(sm.Nb, PC, 32 * kk, 16 * I, lane), frag_cols(sm.Tb, PC, 32 * kk, 16 * J, lane), m);
+#pragma unroll
+            for (int kk = 0; kk < KD; ++kk)
+                av = mfma32(frag_rows(sm.Kt, PD, 16 * I, 32 * kk, lane), frag_rows(sm.Kb, PD, 16 * J, 32 * kk, lane), av);
         }
         const int s = 16 * J + l15;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int r = rowof(e);
             const float dm = s < r ? -m[e] : 0.f;
-            dbr[e] += dm * Areg[Ji][e];
+            dbr[e] += dm * av[e];
             sm.dPb[r * PC + s] = (bf16)(sm.beta[r] * dm);
         }
     }
