@@ -99,23 +99,32 @@ gdr_status check_workspace(const char *what, const void *ws, size_t ws_bytes, si
 }
 
 // Workspace of one prefill call: the varlen schedule (N int32), the first
-// chunk of each packed sequence (N+1 int32) and, for the bf16 scalar-gate
-// chunked path, one kTileBytes record per (chunk, head).  Chunk records are
-// counted as tokens / 64 + N, which bounds sum_n ceil(len_n / 64).
+// chunk of each packed sequence (N+1 int32), for the bf16 channel-gate path
+// one int32 per (sequence, head) (the pairs the plain pass leaves to the
+// reference pass) and, for the bf16 scalar-gate path, one kTileBytes
+// record per (chunk, head).  Chunk records are counted as tokens / 64 + N,
+// which bounds sum_n ceil(len_n / 64).
 struct WsLayout {
-    size_t order, chunk_base, tiles, total;
+    size_t order, chunk_base, units, tiles, total;
     long long max_chunks;
 };
-WsLayout ws_layout(bool tiles, int N, long long tokens, int H, size_t rec = gdr::kTileBytes) {
+WsLayout ws_layout(bool tiles, bool units, int N, long long tokens, int H,
+                   size_t rec = gdr::kTileBytes) {
     WsLayout w{};
     if (N <= 0 || tokens < 0 || H <= 0) return w;
     auto r256 = [](size_t x) { return (x + 255) / 256 * 256; };
     w.order = 0;
     w.chunk_base = r256((size_t)N * sizeof(int32_t));
-    w.tiles = w.chunk_base + r256((size_t)(N + 1) * sizeof(int32_t));
+    w.units = w.chunk_base + r256((size_t)(N + 1) * sizeof(int32_t));
+    w.tiles = w.units + (units ? r256((size_t)N * H * sizeof(int32_t)) : 0);
     w.max_chunks = tiles ? tokens / 64 + N : 0;
     w.total = w.tiles + (size_t)w.max_chunks * H * rec;
     return w;
+}
+// the layout of a prefill call in dtype dt with gate kind gk
+WsLayout prefill_layout(int dt, int gk, int N, long long tokens, int H, bool raw) {
+    return ws_layout(dt == GDR_BF16 && gk == GDR_GATE_SCALAR, dt == GDR_BF16 && gk == GDR_GATE_CHANNEL,
+                     N, tokens, H, raw ? gdr::kTileBytesRaw : gdr::kTileBytes);
 }
 
 // packed-batch prefill shared by the plain and the pool entry points
@@ -134,8 +143,6 @@ gdr_status prefill_fixed_impl(const char *what, int dt, int gk, int B, int T, in
                               float gate_scale, const float *h0, void *o, float *ht,
                               void *workspace, size_t ws_bytes, void *stream);
 
-size_t record_bytes(bool raw) { return raw ? gdr::kTileBytesRaw : gdr::kTileBytes; }
-
 gdr_status check_gate_scale(const char *what, float c) {
     if (!(c >= 0.f))   // also rejects NaN
         return fail(GDR_EINVAL, "%s: gate_scale = %g; it must be >= 0", what, (double)c);
@@ -152,13 +159,12 @@ const char *gdr_version(void) { return "gdr 0.1.0 (gfx950)"; }
 
 size_t gdr_prefill_workspace_bytes(enum gdr_dtype dt, enum gdr_gate gk, int N,
                                    long long tokens, int H) {
-    return ws_layout(dt == GDR_BF16 && gk == GDR_GATE_SCALAR, N, tokens, H).total;
+    return prefill_layout(dt, gk, N, tokens, H, false).total;
 }
 
 size_t gdr_prefill_fused_workspace_bytes(enum gdr_dtype dt, enum gdr_gate gk, int N,
                                          long long tokens, int H) {
-    return ws_layout(dt == GDR_BF16 && gk == GDR_GATE_SCALAR, N, tokens, H,
-                     gdr::kTileBytesRaw).total;
+    return prefill_layout(dt, gk, N, tokens, H, true).total;
 }
 
 gdr_status gdr_prefill_chunked(enum gdr_dtype dt, enum gdr_gate gk, int B, int T, int H,
@@ -215,8 +221,9 @@ gdr_status prefill_fixed_impl(const char *what, int dt, int gk, int B, int T, in
     }
     if (B == 0) return GDR_OK;
     const bool tiles = dt == GDR_BF16 && gk == GDR_GATE_SCALAR;
-    const WsLayout L = ws_layout(tiles, B, (long long)B * T, H, record_bytes(raw));
-    st = check_workspace(what, workspace, ws_bytes, tiles ? L.total : 0);
+    const bool units = dt == GDR_BF16 && gk == GDR_GATE_CHANNEL;
+    const WsLayout L = prefill_layout(dt, gk, B, (long long)B * T, H, raw);
+    st = check_workspace(what, workspace, ws_bytes, tiles || units ? L.total : 0);
     if (st != GDR_OK) return st;
     gdr::PrefillArgs a{};
     a.q = q; a.k = k; a.v = v; a.h0 = h0; a.o = o; a.ht = ht;
@@ -227,6 +234,7 @@ gdr_status prefill_fixed_impl(const char *what, int dt, int gk, int B, int T, in
     }
     a.cu_seqlens = nullptr; a.order = nullptr; a.chunk_base = nullptr;
     a.tiles = tiles ? static_cast<char *>(workspace) + L.tiles : nullptr;
+    a.unit_wide = units ? reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + L.units) : nullptr;
     a.max_chunks = tiles ? (long long)B * ((T + 63) / 64) : 0;
     a.N = B; a.T = T; a.H = H; a.scale = scale; a.channel_gate = gk == GDR_GATE_CHANNEL;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -317,7 +325,8 @@ gdr_status prefill_varlen_impl(const char *what, int dt, int gk, int N, int T_to
     st = check_prefill_ptrs(what, q, k, v, g, beta, h0, o, ht, T_total);
     if (st != GDR_OK) return st;
     const bool tiles = dt == GDR_BF16 && gk == GDR_GATE_SCALAR;
-    const WsLayout L = ws_layout(tiles, N, T_total, H, record_bytes(raw));
+    const bool units = dt == GDR_BF16 && gk == GDR_GATE_CHANNEL;
+    const WsLayout L = prefill_layout(dt, gk, N, T_total, H, raw);
     st = check_workspace(what, workspace, ws_bytes, L.total);
     if (st != GDR_OK) return st;
 
@@ -336,6 +345,7 @@ gdr_status prefill_varlen_impl(const char *what, int dt, int gk, int N, int T_to
     a.cu_seqlens = cu_seqlens; a.order = order;
     a.chunk_base = reinterpret_cast<int32_t *>(ws + L.chunk_base);
     a.tiles = tiles ? ws + L.tiles : nullptr;
+    a.unit_wide = units ? reinterpret_cast<int32_t *>(ws + L.units) : nullptr;
     a.max_chunks = L.max_chunks;
     a.N = N; a.T = 0; a.H = H; a.scale = scale; a.channel_gate = gk == GDR_GATE_CHANNEL;
     a.h0_slot = h0_slot; a.ht_slot = ht_slot; a.pool = pool;
@@ -589,7 +599,7 @@ BwdWs bwd_layout(int gk, int N, long long tokens, long long chunks, int H, int D
     w.dstates = st;
     w.o = 2 * st;
     w.fwd = w.o + r256((size_t)tokens * H * Dv * 2);
-    w.recs = w.fwd + r256(ws_layout(gk == GDR_GATE_SCALAR, N, tokens, H).total);
+    w.recs = w.fwd + r256(prefill_layout(GDR_BF16, gk, N, tokens, H, false).total);
     w.total = w.recs + (size_t)chunks * H * gdr::backward_record_bytes(Dk);
     return w;
 }
@@ -658,12 +668,13 @@ gdr_status gdr_backward_chunked(enum gdr_dtype dt, enum gdr_gate gk, int B, int 
     char *ws = static_cast<char *>(workspace);
     // 1. the forward, keeping the state that enters every chunk
     const bool tiles = gk == GDR_GATE_SCALAR;
-    const WsLayout FL = ws_layout(tiles, B, (long long)B * T, H);
+    const WsLayout FL = prefill_layout(GDR_BF16, gk, B, (long long)B * T, H, false);
     gdr::PrefillArgs f{};
     f.q = q; f.k = k; f.v = v; f.g = g; f.beta = beta; f.h0 = h0;
     f.o = ws + W.o; f.ht = nullptr;
     f.cu_seqlens = nullptr; f.order = nullptr; f.chunk_base = nullptr;
     f.tiles = tiles ? ws + W.fwd + FL.tiles : nullptr;
+    f.unit_wide = tiles ? nullptr : reinterpret_cast<int32_t *>(ws + W.fwd + FL.units);
     f.max_chunks = tiles ? (long long)B * ((T + 63) / 64) : 0;
     f.N = B; f.T = T; f.H = H; f.scale = scale; f.channel_gate = gk == GDR_GATE_CHANNEL;
     f.states = reinterpret_cast<float *>(ws + W.states);
@@ -742,7 +753,7 @@ gdr_status gdr_backward_chunked_varlen(enum gdr_dtype dt, enum gdr_gate gk, int 
     }
     char *ws = static_cast<char *>(workspace);
     const bool tiles = gk == GDR_GATE_SCALAR;
-    const WsLayout FL = ws_layout(tiles, N, T_total, H);
+    const WsLayout FL = prefill_layout(GDR_BF16, gk, N, T_total, H, false);
     int32_t *order = reinterpret_cast<int32_t *>(ws + W.fwd + FL.order);
     int32_t *cbase = reinterpret_cast<int32_t *>(ws + W.fwd + FL.chunk_base);
     // 1. the forward (longest sequences first), keeping the state that
@@ -755,6 +766,7 @@ gdr_status gdr_backward_chunked_varlen(enum gdr_dtype dt, enum gdr_gate gk, int 
     f.o = ws + W.o; f.ht = nullptr;
     f.cu_seqlens = cu_seqlens; f.order = order; f.chunk_base = cbase;
     f.tiles = tiles ? ws + W.fwd + FL.tiles : nullptr;
+    f.unit_wide = tiles ? nullptr : reinterpret_cast<int32_t *>(ws + W.fwd + FL.units);
     f.max_chunks = FL.max_chunks;
     f.N = N; f.T = 0; f.H = H; f.scale = scale; f.channel_gate = gk == GDR_GATE_CHANNEL;
     f.states = reinterpret_cast<float *>(ws + W.states);

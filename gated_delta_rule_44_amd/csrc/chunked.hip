@@ -9,19 +9,38 @@
 // Chunked form used here (an exact reorganisation; derivation below).  For a
 // chunk of C = 64 tokens starting from state S0 (Dv x Dk), with the
 // in-chunk cumulative log gate b_r = sum_{s<=r} g_s (per key channel):
-//     Qt = q (.) e^{b},  Kt = k (.) e^{b},  Kb = k (.) e^{-b},
-//     Kh = k (.) e^{b_C - b}                            (rows are tokens)
-//     A  = strict_lower(Kt Kb^T),  P = lower(Qt Kb^T)     (C x C)
+//     A[r][s] = sum_j k_rj k_sj e^{b_rj - b_sj}  (s < r)
+//     P[r][s] = sum_j q_rj k_sj e^{b_rj - b_sj}  (s <= r)         (C x C)
 //     T  = (I + diag(beta) A)^{-1} diag(beta)             (UT transform)
-//     X  = V - Kt S0^T,   U = T X                         (C x Dv)
-//     O  = scale (Qt S0^T + P U)
-//     S_C = S0 Diag(e^{b_C}) + U^T Kh
+//     X  = V - Kt S0^T,   U = T X,   Kt = k (.) e^{b}     (C x Dv)
+//     O  = scale (Qt S0^T + P U),    Qt = q (.) e^{b}
+//     S_C = S0 Diag(e^{b_C}) + U^T Kh,   Kh = k (.) e^{b_C - b}
 // Derivation: with u_r = beta_r (v_r - S_{r-1} Diag(a_r) k_r) the recurrence
 // is S_r = S_{r-1} Diag(a_r) + u_r k_r^T, so S_r = S0 Gamma_r
 // + sum_{s<=r} u_s (k_s (.) e^{b_r - b_s})^T with Gamma_r = Diag(e^{b_r}).
 // Substituting into u_r gives (I + diag(beta) A) U = diag(beta)(V - Kt S0^T);
 // o_r = S_r q_r gives O; S_C is the r = C case.  (The scalar gate takes the
 // two-kernel path of chunked_chain.hip.)
+//
+// Range.  The gate may be anything in [0, 1] (g in [-inf, 0]); g is first
+// raised to kGateFloor, which keeps every prefix sum finite.  A chunk whose
+// decay stays within e^{kChunkDecayMax} in every channel is factored from
+// its first row as above: Kt = k (.) e^{b} and Kb = k (.) e^{-b} stay within
+// the range of bf16 and fp32, and A = strict_lower(Kt Kb^T),
+// P = lower(Qt Kb^T), Kh = Kb (.) e^{b_C}.  A chunk that decays further in
+// some channel ("wide") never forms a factor larger than 1 from the chunk's
+// whole decay: with R_I the prefix sum at the end of 16-row block I - 1
+// (R_0 = 0, R_4 = b_C),
+//     QR = q (.) e^{b - R_I},  KR = k (.) e^{b - R_I}    (rows of block I)
+//     KE = k (.) e^{R_{I+1} - b}                          (rows of block I)
+// are all at most 1, and every product above is assembled from them:
+//     A_IJ = KR_I (KE_J (.) e^{R_I - R_{J+1}})^T          (I > J, factor <= 1)
+//     A_II = KR_I (KE_I (.) e^{R_I - R_{I+1}})^T          (factor >= 1)
+//     Kt S0^T = KR_I (S0 Diag(e^{R_I}))^T,   Kh_J = KE_J (.) e^{b_C - R_{J+1}}
+// The one factor above 1 is the decay of a single 16-row block.  Where some
+// channel's block decays by more than e^{kDiagDecayMax}, that diagonal block
+// of A and P is formed entry by entry instead, sum_j k_rj k_sj e^{c_rj - c_sj}
+// with c the prefix sums within the block (slow_diag below).
 //
 // Work split.  One workgroup (8 waves) owns one (sequence, head, 32-wide
 // slice of Dv) and walks its chunks in order; rows of S never mix, so the
@@ -35,8 +54,7 @@
 //      16x16x16 MFMA block substitution; waves 4-7: X = V - Kt S0^T and
 //      Qt S0^T on MFMA
 //   4  U = T X
-//   5  O = Qt S0^T + P U, and S^T <- e^{b_C} (.) (S^T + Kb^T U), which is
-//      e^{b_C} (.) S^T + Kh^T U without forming Kh
+//   5  O = Qt S0^T + P U, and S^T <- e^{b_C} (.) S^T + Kh^T U
 // All contractions use bf16 operands with fp32 accumulation; the state is
 // carried in fp32 registers and rounded to bf16 only as an MFMA operand.
 //
@@ -65,6 +83,15 @@ constexpr int PCT = C + 16; // C-wide bf16 rows read by transpose loads: a row
 constexpr int PY = 24;      // padded row length of the bf16 Y^T blocks (read by
                             // transpose loads: 4 consecutive rows on disjoint banks)
 constexpr int PV = BV + 8;  // padded LDS row length of the v tile
+// A chunk whose summed log-decay exceeds kChunkDecayMax in some channel
+// takes the block-reference form; in it, a 16-row diagonal block whose
+// summed log-decay exceeds kDiagDecayMax in some channel takes the
+// entry-by-entry form.  Below these, the factors stay under e^80 (e^70) and
+// their partners above e^-80 (e^-70) times k, inside the normal range.
+constexpr float kChunkDecayMax = 80.f;
+constexpr float kDiagDecayMax = 70.f;
+// flag bits of a chunk: 0..3 diagonal blocks formed entry by entry, 4 wide
+constexpr int kWide = 16;
 
 // Per-thread indices used by every phase.
 template <int D> struct LaneIds {
@@ -112,21 +139,35 @@ __device__ inline float group_scan(float x, int lane) {
 
 template <int D> struct Smem {
     static constexpr int PD = D + 8;   // padded row length for D-wide rows
-    alignas(16) bf16 Q[C * PD];        // q (.) e^b, [r][j]
-    alignas(16) bf16 K[C * PD];        // k (.) e^b, [r][j]
-    alignas(16) bf16 Kb[2][C * PD];    // k (.) e^-b, [r][j], by chunk parity
+    alignas(16) bf16 Q[C * PD];        // QR = q (.) e^{b - R_I}, [r][j]
+    alignas(16) bf16 K[C * PD];        // KR = k (.) e^{b - R_I}, [r][j]
+    alignas(16) bf16 Kb[2][C * PD];    // KE = k (.) e^{R_{I+1} - b}, [r][j], by chunk parity
     alignas(16) bf16 S[BV * PD];       // bf16 copy of the state slice, [i][j]
     alignas(16) bf16 TT[C * PCT];      // T^T, [s][r] (read back by transpose loads)
     alignas(16) bf16 PT[C * PCT];      // P^T, [s][r]
     alignas(16) bf16 XT[BV * PC];      // X^T, [i][s]
     alignas(16) bf16 UT[BV * PC];      // U^T, [i][s]
     alignas(16) bf16 V[C * PV];        // v tile, [r][i]
-    alignas(16) bf16 LTo[C * PCT];     // L^T = (diag(beta) A)^T below the diagonal blocks, [s][r]
+    alignas(16) bf16 LTo[6][16 * PY];  // blocks (I > J) of L^T = (diag(beta) A)^T, [ltri(I, J)][s][r]
     alignas(16) bf16 YT[4 * 16 * PY];  // inverted diagonal blocks, transposed: [b][c][r]
     alignas(16) float QS[8 * 64 * 4];  // Qt S0^T of the prep chunk, transposed, in
                                        // accumulator order: [4 jv + I][lane][e]
     alignas(16) float beta[C];
     alignas(16) float gam[2][D];       // e^{b_C} per channel, by chunk parity
+    // per-channel factors of a chunk, from its block ends R_1..R_3 and b_C:
+    //   FD (prep chunk only): e^{R_b - R_{b+1}}, b = 0..3, then e^{R_2 - R_1},
+    //      e^{R_3 - R_1}, e^{R_3 - R_2} for the blocks (2,0), (3,0), (3,1)
+    //   FX (by parity): e^{R_1}, e^{R_2}, e^{R_3}
+    //   FU (by parity): e^{b_C - R_1}, e^{b_C - R_2}, e^{b_C - R_3}
+    alignas(16) float FD[7][D];
+    alignas(16) float FX[2][3][D];
+    alignas(16) float FU[2][3][D];
+    // A (0) and P (1) of the diagonal blocks formed entry by entry, [b][r][s]
+    alignas(16) float dres[2][4][256];
+    alignas(16) float rnorm[2][2][C];  // RAW: 1/|q_r|, 1/|k_r| by chunk parity
+    int dflag[2][2];                   // reference pass, by chunk parity: per-wave parts of
+                                       // the chunk's diagonal blocks to form entry by entry
+    int wide_any;                      // plain pass: some chunk so far is wide
     // per chunk parity: the per-wave sums of the gate logs [w][j], turned in
     // place into their exclusive prefix over the waves, and the chunk total
     // b_C in row NW, all times log2(e)
@@ -157,7 +198,7 @@ template <int D> struct Smem {
 // gate logits are turned into -c softplus at the scan (zero for rows past the
 // sequence end, which must not decay the state), beta from its logit when
 // staged.
-template <int D, bool RAW>
+template <int D, bool RAW, bool REF>
 __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
     using Sm = Smem<D>;
     using LI = LaneIds<D>;
@@ -180,6 +221,9 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
     const int rank = unit / a.H;
     const int h = unit - rank * a.H;
     const int n = a.order ? a.order[rank] : rank;
+    // the reference pass redoes only the (sequence, head) pairs the plain
+    // pass left to it
+    if (REF && !a.unit_wide[(size_t)n * a.H + h]) return;
     long long t0, t1;
     if (a.cu_seqlens) {
         t0 = a.cu_seqlens[n];
@@ -205,6 +249,7 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
         sm.TT[e] = (bf16)0.f;
         sm.PT[e] = (bf16)0.f;
     }
+    if (tid0 == 0) sm.wide_any = 0;
 
     // ---- state S^T in registers of waves 4..7: wave w holds blocks
     //      (Jk, Jv) for Jk = SBK*(w-4) + kb, Jv = 0, 1, i.e. S^T[j][iv] with
@@ -329,7 +374,8 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
         for (int i = 0; i < RPT; ++i) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                run[e] += RAW ? rgf[i][e] : rgc[i][e >> 2][e & 3];
+                const float gv = RAW ? rgf[i][e] : rgc[i][e >> 2][e & 3];
+                run[e] += REF ? __builtin_fmaxf(gv, kGateFloor) : gv;
                 cum[par][i][e] = run[e];
             }
         }
@@ -350,37 +396,105 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
     };
 
     // per-wave totals -> exclusive prefix over the waves and chunk total, one
-    // thread per key channel (threads 64 .. 64+D-1, phase C)
+    // thread per key channel (threads 64 .. 64+D-1, phase C); and flags:
+    // the plain pass notes a chunk that some channel decays by more than
+    // e^{kChunkDecayMax} over the chunk (wide; also any gate of -inf, which
+    // the plain pass does not clamp), the reference pass the 16-row blocks
+    // (two waves each) that some channel decays by more than e^{kDiagDecayMax}
     auto prefix = [&](int par) {
         const int ch = tid0 - 64;
+        int fl = 0;
         if (ch >= 0 && ch < D) {
             float t[NW];
 #pragma unroll
             for (int ww = 0; ww < NW; ++ww) t[ww] = sm.pfx[par][ww * D + ch];
-            float acc = 0.f;
+            float acc = 0.f, rb = 0.f;
 #pragma unroll
             for (int ww = 0; ww < NW; ++ww) {
                 sm.pfx[par][ww * D + ch] = acc * kL2e;
                 acc += t[ww];
+                if (REF && (ww & 1)) {
+                    if (rb - acc > kDiagDecayMax) fl |= 1 << (ww >> 1);
+                    rb = acc;
+                }
             }
             sm.pfx[par][NW * D + ch] = acc * kL2e;
+            if (!REF && !(-acc <= kChunkDecayMax)) fl = kWide;
+        }
+        const int wv = __builtin_amdgcn_readfirstlane(tid0 >> 6);
+        if (wv == 1 || wv == 2) {
+            if (REF) {
+                int m = 0;
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+                    if (__ballot((fl >> b) & 1)) m |= 1 << b;
+                if ((tid0 & 63) == 0) sm.dflag[par][wv - 1] = m;
+            } else if (__ballot(fl != 0) && (tid0 & 63) == 0) {
+                sm.wide_any = 1;
+            }
         }
     };
+    // reference pass: the diagonal blocks to form entry by entry of the
+    // chunk whose prefix sums are in pfx[par], wave-uniform
+    auto chunk_flags = [&](int par) -> int {
+        return __builtin_amdgcn_readfirstlane(sm.dflag[par][0] | sm.dflag[par][1]);
+    };
 
-    // gated operands of one chunk (phase C): Qt, Kt, Kb into registers and
-    // e^{b_C} into its parity buffer
+    // gated operands of one chunk (phase C) into registers: Qt, Kt, Kb, or
+    // for a wide chunk QR, KR, KE (the same formulas with the references
+    // R_I, R_{I+1} in place of 0); e^{b_C}, for a wide chunk the factors,
+    // and (RAW) the row norms into their buffers
     auto gate = [&](const LI &L, auto par_tag) {
         constexpr int par = decltype(par_tag)::value;
-        const float *pw = &sm.pfx[par][L.w * D + 8 * L.cg];
-        const float *pc = &sm.pfx[par][NW * D + 8 * L.cg];
-        const f32x4 p0 = *reinterpret_cast<const f32x4 *>(pw);
-        const f32x4 p1 = *reinterpret_cast<const f32x4 *>(pw + 4);
-        const f32x4 c0 = *reinterpret_cast<const f32x4 *>(pc);
-        const f32x4 c1 = *reinterpret_cast<const f32x4 *>(pc + 4);
-        const float pre[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-        const float bC[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-        if (L.rg == 0) {
-            float gC[8];
+        constexpr bool wide = REF;
+        auto ld8f = [&](int row, float (&v)[8]) {
+            const float *p = &sm.pfx[par][row * D + 8 * L.cg];
+            const f32x4 x0 = *reinterpret_cast<const f32x4 *>(p);
+            const f32x4 x1 = *reinterpret_cast<const f32x4 *>(p + 4);
+            v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w;
+            v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
+        };
+        const int Ib = L.w >> 1;             // this wave's 16-row block
+        float pre[8], r0[8] = {}, r1[8] = {};
+        ld8f(L.w, pre);                      // prefix sum before this wave's rows
+        if (wide) {
+            ld8f(2 * Ib, r0);                // R_I
+            ld8f(2 * Ib + 2, r1);            // R_{I+1} (b_C for the last block)
+        }
+        if (wide) {
+            // the chunk's per-channel factors: NT / D threads per channel,
+            // 14 vectors between them
+            constexpr int G = NT / D;
+            const int ch = L.tid % D, grp = L.tid / D;
+            const float *pf = sm.pfx[par];
+            const float R1 = pf[2 * D + ch], R2 = pf[4 * D + ch], R3 = pf[6 * D + ch],
+                        bC = pf[NW * D + ch];
+#pragma unroll
+            for (int v = 0; v < 14; ++v) {
+                if (v % G != grp) continue;
+                float x;
+                float *dst;
+                switch (v) {
+                case 0: x = -R1; dst = &sm.FD[0][ch]; break;
+                case 1: x = R1 - R2; dst = &sm.FD[1][ch]; break;
+                case 2: x = R2 - R3; dst = &sm.FD[2][ch]; break;
+                case 3: x = R3 - bC; dst = &sm.FD[3][ch]; break;
+                case 4: x = R2 - R1; dst = &sm.FD[4][ch]; break;
+                case 5: x = R3 - R1; dst = &sm.FD[5][ch]; break;
+                case 6: x = R3 - R2; dst = &sm.FD[6][ch]; break;
+                case 7: x = R1; dst = &sm.FX[par][0][ch]; break;
+                case 8: x = R2; dst = &sm.FX[par][1][ch]; break;
+                case 9: x = R3; dst = &sm.FX[par][2][ch]; break;
+                case 10: x = bC - R1; dst = &sm.FU[par][0][ch]; break;
+                case 11: x = bC - R2; dst = &sm.FU[par][1][ch]; break;
+                case 12: x = bC - R3; dst = &sm.FU[par][2][ch]; break;
+                default: x = bC; dst = &sm.gam[par][ch]; break;
+                }
+                *dst = __builtin_amdgcn_exp2f(x);
+            }
+        } else if (L.rg == 0) {
+            float bC[8], gC[8];
+            ld8f(NW, bC);
 #pragma unroll
             for (int e = 0; e < 8; ++e) gC[e] = __builtin_amdgcn_exp2f(bC[e]);
             *reinterpret_cast<f32x4 *>(&sm.gam[par][8 * L.cg]) = f32x4{gC[0], gC[1], gC[2], gC[3]};
@@ -403,15 +517,26 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
                 sk = sum_stride<RPW>(sk);
                 nq = inv_norm(sq);
                 nk = inv_norm(sk);
+                if (L.cg == 0) {
+                    sm.rnorm[par][0][L.rg * RPT + i] = nq;
+                    sm.rnorm[par][1][L.rg * RPT + i] = nk;
+                }
             }
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float eb = __builtin_amdgcn_exp2f(__builtin_fmaf(cum[par][i][e], kL2e, pre[e]));
-                const float ebi = __builtin_amdgcn_rcpf(eb);
+                const float b2 = __builtin_fmaf(cum[par][i][e], kL2e, pre[e]);
+                float er, ee;
+                if (REF) {
+                    er = __builtin_amdgcn_exp2f(b2 - r0[e]);          // e^{b - R_I}
+                    ee = __builtin_amdgcn_exp2f(r1[e] - b2);          // e^{R_{I+1} - b}
+                } else {
+                    er = __builtin_amdgcn_exp2f(b2);                  // e^{b}
+                    ee = __builtin_amdgcn_rcpf(er);                   // e^{-b}
+                }
                 const float kv = RAW ? (float)rk[i][e] * nk : (float)rk[i][e];
-                qt[e] = (RAW ? (float)rq[i][e] * nq : (float)rq[i][e]) * eb;
-                kt[e] = kv * eb;
-                kb[e] = kv * ebi;
+                qt[e] = (RAW ? (float)rq[i][e] * nq : (float)rq[i][e]) * er;
+                kt[e] = kv * er;
+                kb[e] = kv * ee;
             }
             gq[i] = cvt8(qt);
             gk[i] = cvt8(kt);
@@ -432,6 +557,100 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
         if (L.tid < C) sm.beta[L.tid] = RAW ? logistic(rb[par]) : rb[par];
     };
 
+    // Diagonal 16x16 blocks of A and P entry by entry, for the blocks of
+    // chunk j set in fl (all threads, a block at a time; ends with a
+    // barrier):  A[r][s] = sum_j k_rj k_sj 2^{c_rj - c_sj} (s < r) and
+    // P[r][s] = sum_j q_rj k_sj 2^{c_rj - c_sj} (s <= r), with c the prefix
+    // sums of the block's gate logs (log2 units), so every factor is at most
+    // 1 whatever the decay.  The block's rows of g, k and q come from global
+    // memory into buffers that are free at this point: c in TT, k in XT, q
+    // in LTo (TT is zeroed again afterwards, as its upper blocks must stay
+    // zero).  Four threads share a pair (r, s), a quarter of the channels
+    // each.
+    auto slow_diag = [&](const LI &L, long long j, int fl, int par) {
+        float *cs = reinterpret_cast<float *>(sm.TT);
+        bf16 *ks = sm.XT;
+        bf16 *qs = &sm.LTo[0][0];
+        static_assert(16 * D * 4 <= sizeof(sm.TT) && 16 * D * 2 <= sizeof(sm.XT) &&
+                      16 * D * 2 <= sizeof(sm.LTo), "entry-by-entry scratch");
+        const long long tc = t0 + j * C;
+        const int Cc = valid_rows(j);
+        const unsigned rowb = (unsigned)(tokstride * 2);
+        for (int b = 0; b < 4; ++b) {
+            if (!((fl >> b) & 1)) continue;
+            const int nr = Cc - 16 * b <= 0 ? 0 : (Cc - 16 * b > 16 ? 16 : Cc - 16 * b);
+            const size_t tb = (size_t)(tc + 16 * b);   // first token of the block
+            if (L.tid < D) {
+                const int ch = L.tid;
+                const unsigned rowx = (unsigned)(a.H * D * (RAW ? 2 : 4));
+                const rsrc_t rs = RAW ? make_rsrc(static_cast<const bf16 *>(a.xg) + (tb * a.H + h) * D,
+                                                  nr ? (nr - 1) * rowx + D * 2 : 0u)
+                                      : make_rsrc(a.g + (tb * a.H + h) * D, nr ? (nr - 1) * rowx + D * 4 : 0u);
+                float run = 0.f;
+#pragma unroll 1
+                for (int r4 = 0; r4 < 16; r4 += 4) {
+                    float gv[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int r = r4 + u;
+                        if (RAW) {
+                            const float x = bf16_bits_to_float(bload2(rs, r * rowx + 2 * ch));
+                            gv[u] = r < nr ? neg_softplus(x, a.gate_scale) : 0.f;
+                        } else {
+                            gv[u] = bload4(rs, r * rowx + 4 * ch);
+                        }
+                    }
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        run += __builtin_fmaxf(gv[u], kGateFloor);
+                        cs[(r4 + u) * D + ch] = run * kL2e;
+                    }
+                }
+            }
+            constexpr int NP = 16 * D / 8;           // 16-byte pieces of a block of rows
+            const rsrc_t rkb = make_rsrc(kg + tb * tokstride, nr ? (nr - 1) * rowb + D * 2 : 0u);
+            const rsrc_t rqb = make_rsrc(qg + tb * tokstride, nr ? (nr - 1) * rowb + D * 2 : 0u);
+            for (int p = L.tid; p < 2 * NP; p += NT) {
+                const int which = __builtin_amdgcn_readfirstlane(p / NP);   // whole waves
+                const int pp = p % NP, r = pp / (D / 8), c8 = pp % (D / 8);
+                const bf16x8 v = bload16(which ? rqb : rkb, r * rowb + 16 * c8);
+                *reinterpret_cast<bf16x8 *>((which ? qs : ks) + r * D + 8 * c8) = v;
+            }
+            __syncthreads();
+            for (int p = L.tid >> 2; p < 136; p += NT / 4) {
+                int r = 0;
+                while ((r + 1) * (r + 2) / 2 <= p) ++r;
+                const int s2 = p - r * (r + 1) / 2;
+                const int qq = L.tid & 3;
+                float aa = 0.f, pp = 0.f;
+#pragma unroll 2
+                for (int u = 0; u < D / 4; ++u) {
+                    const int ch = 4 * u + qq;
+                    const float e = __builtin_amdgcn_exp2f(cs[r * D + ch] - cs[s2 * D + ch]);
+                    const float kse = (float)ks[s2 * D + ch] * e;
+                    aa = __builtin_fmaf((float)ks[r * D + ch], kse, aa);
+                    pp = __builtin_fmaf((float)qs[r * D + ch], kse, pp);
+                }
+                aa += dpp_f<0xB1>(aa);
+                aa += dpp_f<0x4E>(aa);
+                pp += dpp_f<0xB1>(pp);
+                pp += dpp_f<0x4E>(pp);
+                if (qq == 0) {
+                    if (RAW) {
+                        const float nks = sm.rnorm[par][1][16 * b + s2];
+                        aa *= sm.rnorm[par][1][16 * b + r] * nks;
+                        pp *= sm.rnorm[par][0][16 * b + r] * nks;
+                    }
+                    sm.dres[0][b][r * 16 + s2] = aa;
+                    sm.dres[1][b][r * 16 + s2] = pp;
+                }
+            }
+            __syncthreads();
+        }
+        for (int e = L.tid; e < C * PCT; e += NT) sm.TT[e] = (bf16)0.f;
+        __syncthreads();
+    };
+
     // ---- one pipeline iteration; PAR = parity of the prep chunk j
     auto iteration = [&](auto par_tag, auto s_tag, auto p_tag, long long j) {
         constexpr int PAR = decltype(par_tag)::value;
@@ -441,11 +660,21 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
         constexpr bool hasP = decltype(p_tag)::value;   // j < nch
         const bool hasG = j + 1 < nch;
 
+        // fragment entries times per-channel factors f_j (LDS), for the
+        // channels a fragment lane holds (32 kk + 8 (lane >> 4) .. +7)
+        auto scale_frag = [&](bf16x8 &fr, int kk, const float *f) {
+            const int c0 = 32 * kk + 8 * (lane >> 4);
+            const f32x4 f0 = *reinterpret_cast<const f32x4 *>(f + c0);
+            const f32x4 f1 = *reinterpret_cast<const f32x4 *>(f + c0 + 4);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) fr[u] = (bf16)((float)fr[u] * (u < 4 ? f0[u] : f1[u - 4]));
+        };
         auto frags = [&](const bf16 *M, int blk, bf16x8 (&f)[KD]) {
 #pragma unroll
             for (int kk = 0; kk < KD; ++kk) f[kk] = frag_rows(M, PD, 16 * blk, 32 * kk, lane);
         };
-        // A and P block (I, J): Kt and Qt rows of block I against Kb rows of J
+        // A and P block (I, J): KR and QR rows of block I against KE rows of J
+        // (their fragments kf, qf, bf)
         auto gram = [&](const bf16x8 (&kf)[KD], const bf16x8 (&qf)[KD], const bf16x8 (&bf)[KD],
                         f32x4 &av, f32x4 &pv) {
             av = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -458,10 +687,9 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
         };
         // L^T[s][r] = beta_r A[r][s] of a block below the diagonal (I > J)
         auto putL = [&](int I, int J, f32x4 av) {
-            const int s = 16 * J + l15;
             const int r0 = 16 * I + 4 * l4;
             const f32x4 br = *reinterpret_cast<const f32x4 *>(&sm.beta[r0]);
-            *reinterpret_cast<bf16x4 *>(&sm.LTo[s * PCT + r0]) = cvt4(av * br);
+            *reinterpret_cast<bf16x4 *>(&sm.LTo[I * (I - 1) / 2 + J][l15 * PY + 4 * l4]) = cvt4(av * br);
         };
         // P^T[s][r] = P[r][s] for s <= r
         auto putP = [&](int I, int J, f32x4 pv) {
@@ -474,6 +702,10 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
         };
         // P blocks of chunk j computed in phase B, written in phase C
         f32x4 pdiag = {0.f, 0.f, 0.f, 0.f}, poff = pdiag;
+
+        // reference pass: the diagonal blocks of chunk j to form entry by
+        // entry (read now, used after phase A)
+        const int flP = (REF && hasP) ? chunk_flags(PAR) : 0;
 
         // ================= phase A ========================================
         if (hasS && w < 4) {   // U = T X of chunk j-1; wave w: row block w
@@ -494,6 +726,10 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
         __syncthreads();
 
         // ================= phase B ========================================
+        // diagonal blocks of a wide chunk that decay too fast for the
+        // reference of their first row: entry by entry, before the rest of
+        // the phase
+        if (REF && flP) slow_diag(L, j, flP, PAR);
         if (w < 4) {
             if (hasP) {
                 // diagonal block (b, b) and, for b >= 1, block (b, b-1): the
@@ -502,11 +738,26 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
                 bf16x8 kf[KD], qf[KD], bf[KD];
                 frags(sm.K, b, kf);
                 frags(sm.Q, b, qf);
-                frags(sm.Kb[PAR], b, bf);
                 f32x4 ad, adT = {0.f, 0.f, 0.f, 0.f};
-                gram(kf, qf, bf, ad, pdiag);
+                if (REF && ((flP >> b) & 1)) {
+                    const float *Ar = sm.dres[0][b], *Pr = sm.dres[1][b];
 #pragma unroll
-                for (int kk = 0; kk < KD; ++kk) adT = mfma32(bf[kk], kf[kk], adT);   // A_bb^T
+                    for (int e = 0; e < 4; ++e) {
+                        ad[e] = Ar[(4 * l4 + e) * 16 + l15];
+                        adT[e] = Ar[l15 * 16 + 4 * l4 + e];
+                        pdiag[e] = Pr[(4 * l4 + e) * 16 + l15];
+                    }
+                } else {
+                    // wide: against KE_b (.) e^{R_b - R_{b+1}} (at most e^{kDiagDecayMax})
+                    frags(sm.Kb[PAR], b, bf);
+                    if (REF) {
+#pragma unroll
+                        for (int kk = 0; kk < KD; ++kk) scale_frag(bf[kk], kk, sm.FD[b]);
+                    }
+                    gram(kf, qf, bf, ad, pdiag);
+#pragma unroll
+                    for (int kk = 0; kk < KD; ++kk) adT = mfma32(bf[kk], kf[kk], adT);   // A_bb^T
+                }
                 f32x4 aoff = {0.f, 0.f, 0.f, 0.f};
                 if (b >= 1) {
                     frags(sm.Kb[PAR], b - 1, bf);
@@ -573,19 +824,38 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
                     uf[jv][0] = frag_rows(sm.UT, PC, 16 * jv, 0, lane);
                     uf[jv][1] = frag_rows(sm.UT, PC, 16 * jv, 32, lane);
                 }
-                // S^T <- e^{b_C} (.) (S^T + Kb^T U)  (chunk j-1: parity 1 - PAR),
-                // which equals e^{b_C} (.) S^T + Kh^T U
+                // S^T <- e^{b_C} (.) S^T + Kh^T U  (chunk j-1: parity 1 - PAR):
+                // e^{b_C} (.) (S^T + Kb^T U), or for a wide chunk with
+                // Kh_J = KE_J (.) e^{b_C - R_{J+1}} (the lane's channel is
+                // 16 Jk + l15 and its tokens lie in blocks lane >> 5 (first
+                // fragment) and 2 + (lane >> 5) (second))
 #pragma unroll
                 for (int kb = 0; kb < SBK; ++kb) {
                     const int Jk = SBK * I + kb;
                     const int jc = 16 * Jk + 4 * l4;
                     const f32x4 gm = *reinterpret_cast<const f32x4 *>(&sm.gam[1 - PAR][jc]);
-                    const bf16x8 k0f = frag_cols(sm.Kb[1 - PAR], PD, 0, 16 * Jk, lane);
-                    const bf16x8 k1f = frag_cols(sm.Kb[1 - PAR], PD, 32, 16 * Jk, lane);
+                    bf16x8 k0f = frag_cols(sm.Kb[1 - PAR], PD, 0, 16 * Jk, lane);
+                    bf16x8 k1f = frag_cols(sm.Kb[1 - PAR], PD, 32, 16 * Jk, lane);
+                    if (REF) {
+                        const int chn = 16 * Jk + l15;
+                        const float f0 = sm.FU[1 - PAR][lane >> 5][chn];
+                        const float f1 = (lane >> 5) ? 1.f : sm.FU[1 - PAR][2][chn];
+#pragma unroll
+                        for (int u = 0; u < 8; ++u) {
+                            k0f[u] = (bf16)((float)k0f[u] * f0);
+                            k1f[u] = (bf16)((float)k1f[u] * f1);
+                        }
+                    }
 #pragma unroll
                     for (int jv = 0; jv < 2; ++jv) {
-                        f32x4 sv = mfma32(k0f, uf[jv][0], St[kb][jv]);
-                        sv = mfma32(k1f, uf[jv][1], sv) * gm;
+                        f32x4 sv;
+                        if (REF) {
+                            sv = mfma32(k0f, uf[jv][0], St[kb][jv] * gm);
+                            sv = mfma32(k1f, uf[jv][1], sv);
+                        } else {
+                            sv = mfma32(k0f, uf[jv][0], St[kb][jv]);
+                            sv = mfma32(k1f, uf[jv][1], sv) * gm;
+                        }
                         St[kb][jv] = sv;
                         *reinterpret_cast<bf16x4 *>(&sm.S[(16 * jv + l15) * PD + jc]) = cvt4(sv);
                         if (a.states && j < nch)   // the state entering chunk j
@@ -597,10 +867,15 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
             if (hasP && w < 7) {
                 // blocks (2,0), (3,0), (3,1) of A and P
                 const int I = w == 4 ? 2 : 3, J = w == 6 ? 1 : 0;
+                // wide: against KE_J (.) e^{R_I - R_{J+1}} (at most 1)
                 bf16x8 kf[KD], qf[KD], bf[KD];
                 frags(sm.K, I, kf);
                 frags(sm.Q, I, qf);
                 frags(sm.Kb[PAR], J, bf);
+                if (REF) {
+#pragma unroll
+                    for (int kk = 0; kk < KD; ++kk) scale_frag(bf[kk], kk, sm.FD[I == 2 ? 4 : (J == 0 ? 5 : 6)]);
+                }
                 f32x4 aoff;
                 gram(kf, qf, bf, aoff, poff);
                 putL(I, J, aoff);
@@ -616,8 +891,8 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
                 // off-diagonal blocks of T:  Y_ij = -Y_ii sum_{k=j}^{i-1} L_ik Y_kj
                 // on 16x16x16 MFMAs (A operand: row l15, cols 4*l4..+3;
                 // B operand: rows 4*l4..+3, col l15 == the accumulator layout)
-                auto opL = [&](int bi, int bk) -> bf16x4 {   // L_ik[l15][4*l4..] = L^T[16bk+4*l4..][16bi+l15]
-                    return frag_col4(sm.LTo, PCT, 16 * bk, 16 * bi, lane);
+                auto opL = [&](int bi, int bk) -> bf16x4 {   // L_ik[l15][4*l4..] = L^T_ik[4*l4..][l15]
+                    return frag_col4(sm.LTo[bi * (bi - 1) / 2 + bk], PY, 0, 0, lane);
                 };
                 auto opYA = [&](int bi) -> bf16x4 {   // Y_ii[l15][4*l4..] = Y^T[4*l4..][l15]
                     return frag_col4(sm.YT, PY, 16 * bi, 0, lane);
@@ -651,7 +926,8 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
                 putT(3, 0, Y30, bt0);
             } else if (w >= 4) {
                 // Qt S0^T (for the outputs, transposed, to LDS) and
-                // X = V - Kt S0^T, row block w-4
+                // X = V - Kt S0^T, row block w-4: Kt = KR (.) e^{R_I},
+                // Qt = QR (.) e^{R_I}
                 const int I = w - 4;
                 const int r0 = 16 * I + 4 * l4;
                 bf16x8 kf[KD], qf[KD];
@@ -659,6 +935,13 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
                 for (int kk = 0; kk < KD; ++kk) {
                     kf[kk] = frag_rows(sm.K, PD, 16 * I, 32 * kk, lane);
                     qf[kk] = frag_rows(sm.Q, PD, 16 * I, 32 * kk, lane);
+                }
+                if (REF && I > 0) {
+#pragma unroll
+                    for (int kk = 0; kk < KD; ++kk) {
+                        scale_frag(kf[kk], kk, sm.FX[PAR][I - 1]);
+                        scale_frag(qf[kk], kk, sm.FX[PAR][I - 1]);
+                    }
                 }
 #pragma unroll
                 for (int jv = 0; jv < 2; ++jv) {
@@ -736,6 +1019,14 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
         if (j & 1) iteration(O{}, std::true_type{}, std::false_type{}, j);
         else       iteration(E{}, std::true_type{}, std::false_type{}, j);
     }
+    // The plain pass ran every chunk; if one of them was wide its results
+    // are void, and the reference pass redoes the pair from its start (all
+    // outputs, states and the final state)
+    if (!REF) {
+        const bool wide_hit = __builtin_amdgcn_readfirstlane(sm.wide_any) != 0;
+        if (tile == 0 && tid0 == 0) a.unit_wide[(size_t)n * a.H + h] = wide_hit ? 1 : 0;
+        if (wide_hit) return;
+    }
 
     if (float *htp = seq_ht<D>(a, n, h)) {
         const LI L(tid0);
@@ -776,12 +1067,23 @@ hipError_t launch_prefill_chunked(int D, const PrefillArgs &a, hipStream_t s) {
     const int ntile = D / BV;
     const long long blocks = ((units + 7) / 8) * 8 * ntile;
     dim3 grid((unsigned)blocks), block(NT);
+    // the plain pass, then the reference pass over the pairs it marked
+    if (!a.unit_wide) return hipErrorInvalidValue;
     if (a.xg) {
-        if (D == 128) hipLaunchKernelGGL((chunked_kernel<128, true>), grid, block, 0, s, a);
-        else          hipLaunchKernelGGL((chunked_kernel<64, true>), grid, block, 0, s, a);
+        if (D == 128) hipLaunchKernelGGL((chunked_kernel<128, true, false>), grid, block, 0, s, a);
+        else          hipLaunchKernelGGL((chunked_kernel<64, true, false>), grid, block, 0, s, a);
     } else {
-        if (D == 128) hipLaunchKernelGGL((chunked_kernel<128, false>), grid, block, 0, s, a);
-        else          hipLaunchKernelGGL((chunked_kernel<64, false>), grid, block, 0, s, a);
+        if (D == 128) hipLaunchKernelGGL((chunked_kernel<128, false, false>), grid, block, 0, s, a);
+        else          hipLaunchKernelGGL((chunked_kernel<64, false, false>), grid, block, 0, s, a);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (a.xg) {
+        if (D == 128) hipLaunchKernelGGL((chunked_kernel<128, true, true>), grid, block, 0, s, a);
+        else          hipLaunchKernelGGL((chunked_kernel<64, true, true>), grid, block, 0, s, a);
+    } else {
+        if (D == 128) hipLaunchKernelGGL((chunked_kernel<128, false, true>), grid, block, 0, s, a);
+        else          hipLaunchKernelGGL((chunked_kernel<64, false, true>), grid, block, 0, s, a);
     }
     return hipGetLastError();
 }

@@ -69,8 +69,10 @@ template <int D> struct PrepSmem {
 
 // RAW (fused preprocessing): gate and beta from their logits, the Gram
 // blocks scaled by the inverse key norms 1/|k_r| 1/|k_s|, and a 6 KiB
-// record whose factor rows are e^{b_r}, e^{b_C - b_r}/|k_r|, e^{b_r}/|k_r|
-// and e^{-b_r}/|k_r| (the chain kernel applies 1/|q_r| itself).
+// record whose rows are b_r log2(e), e^{b_C - b_r}/|k_r|, e^{b_r}/|k_r|
+// and 1/|k_r| (the chain kernel applies 1/|q_r| itself).
+// Every gate log is raised to kGateFloor first, so that the prefix sums and
+// their differences stay finite for any gate a in [0, 1].
 template <int D, bool RAW>
 __global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a) {
     using Sm = PrepSmem<D>;
@@ -143,6 +145,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a) {
                 gv = bload4(make_rsrc(a.g + gb, gext), lane * hb);
                 bv = bload4(make_rsrc(a.beta + gb, gext), lane * hb);
             }
+            gv = __builtin_fmaxf(gv, kGateFloor);
         }
         if (RAW) {
             // |k_r|^2 over the CG consecutive lanes that hold row r
@@ -293,9 +296,10 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a) {
     //      one 16-byte piece.  The four pairs (1,0), (2,0), (3,0), (3,1) are
     //      stored whole (1 KB each); the pairs (0,0) and (2,1), whose second
     //      block lies above the diagonal, as their first block only (512
-    //      bytes).  Then two rows of 64 fp32 decay factors from b_r, the
-    //      in-chunk inclusive prefix sums of the gate logs: e^{b_r} and
-    //      e^{b_C - b_r}.
+    //      bytes).  Then two rows of 64 fp32 values from b_r, the in-chunk
+    //      inclusive prefix sums of the gate logs: b_r log2(e) itself (the
+    //      recurrence forms e^{b_r} and e^{b_r - b_s}, s <= r, from it, so
+    //      no factor ever exceeds 1) and e^{b_C - b_r}.
     {
         const size_t rec = (size_t)(ci * a.H + h) * REC;
         char *dst = static_cast<char *>(a.tiles) + rec;
@@ -313,12 +317,12 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a) {
             const int r = tid - 2 * 64;
             float *f = reinterpret_cast<float *>(dst + 5120);
             const float b = sm.fb[r];
-            f[r] = ex(b);
+            f[r] = b * kLog2e;
             if (RAW) {
                 const float nk = sm.frk[r];
                 f[C + r] = ex(sm.fb[C - 1] - b) * nk;
                 f[2 * C + r] = ex(b) * nk;
-                f[3 * C + r] = ex(-b) * nk;
+                f[3 * C + r] = nk;
             } else {
                 f[C + r] = ex(sm.fb[C - 1] - b);
             }
@@ -333,16 +337,16 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a) {
 template <bool RAW> struct TRecT {
     bf16x8 pairs[4][64];            // T operand pairs (1,0), (2,0), (3,0), (3,1)
     bf16x4 halves[2][64];           // first blocks of the pairs (0,0), (2,1)
-    float eb[C];                    // e^{b_r}
+    float lb[C];                    // b_r log2(e)
     float hs[C];                    // e^{b_C - b_r}
 };
 template <> struct TRecT<true> {
     bf16x8 pairs[4][64];
     bf16x4 halves[2][64];
-    float eb[C];                    // e^{b_r}
+    float lb[C];                    // b_r log2(e)
     float hs[C];                    // e^{b_C - b_r} / |k_r|
     float ek[C];                    // e^{b_r} / |k_r|
-    float nk[C];                    // e^{-b_r} / |k_r|
+    float rk[C];                    // 1 / |k_r|
 };
 
 template <int D, bool RAW> struct ChainSmem {
@@ -483,14 +487,19 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
 #pragma unroll
                 for (int kk = 0; kk < KD; ++kk) Kf[rb][kk] = frag_rows(Kc, PD, 16 * rb, 32 * kk, lane);
                 vv[rb] = frag_col4(Vc, PV, 16 * rb, 16 * ib, lane);
-                if constexpr (RAW) eb[rb] = *reinterpret_cast<const f32x4 *>(&R.ek[16 * rb + 4 * q4]);
-                else               eb[rb] = *reinterpret_cast<const f32x4 *>(&R.eb[16 * rb + 4 * q4]);
+                if constexpr (RAW) {
+                    eb[rb] = *reinterpret_cast<const f32x4 *>(&R.ek[16 * rb + 4 * q4]);
+                } else {
+                    const f32x4 lb = *reinterpret_cast<const f32x4 *>(&R.lb[16 * rb + 4 * q4]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) eb[rb][e] = __builtin_amdgcn_exp2f(lb[e]);
+                }
                 hs[rb] = *reinterpret_cast<const f32x4 *>(&R.hs[16 * rb + 4 * q4]);
                 Ta[rb][0] = rb == 0 ? cat8(R.halves[0][lane], bf16x4{}) : R.pairs[rb - 1][lane];
                 Ta[rb][1] = rb == 2 ? cat8(R.halves[1][lane], bf16x4{})
                           : (rb == 3 ? R.pairs[3][lane] : bf16x8{});
             }
-            gC = R.eb[C - 1];
+            gC = __builtin_amdgcn_exp2f(R.lb[C - 1]);
         };
         publish_state(0);
         __syncthreads();                      // chunks 0 and 1 staged
@@ -685,7 +694,7 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
             constexpr int r = decltype(S)::value;
             const bf16 *Kc = sm.K[m3];
             bf16x8 As[2][KD], Kj[RB + 1][KD];
-            f32x4 nebJ[RB + 1];
+            f32x4 lbJ[RB + 1], rkJ[RB + 1];
 #pragma unroll
             for (int ob = 0; ob < 2; ++ob)
 #pragma unroll
@@ -694,15 +703,11 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
             for (int J = 0; J <= RB; ++J) {
 #pragma unroll
                 for (int kk = 0; kk < KD; ++kk) Kj[J][kk] = frag_rows(Kc, PD, 16 * J, 32 * kk, lane);
-                if constexpr (RAW) {
-                    nebJ[J] = *reinterpret_cast<const f32x4 *>(&sm.TR[m3].nk[16 * J + 4 * q4]);
-                } else {
-                    const f32x4 ebJ = *reinterpret_cast<const f32x4 *>(&sm.TR[m3].eb[16 * J + 4 * q4]);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) nebJ[J][e] = __builtin_amdgcn_rcpf(ebJ[e]);   // e^{-b_s}
-                }
+                lbJ[J] = *reinterpret_cast<const f32x4 *>(&sm.TR[m3].lb[16 * J + 4 * q4]);
+                if constexpr (RAW) rkJ[J] = *reinterpret_cast<const f32x4 *>(&sm.TR[m3].rk[16 * J + 4 * q4]);
             }
-            float ebr = sm.TR[m3].eb[16 * RB + l15];
+            const float lbr = sm.TR[m3].lb[16 * RB + l15];
+            float ebr = __builtin_amdgcn_exp2f(lbr), iq = 1.f;
             if constexpr (RAW) {
                 // 1/|q_r| for the lane's row: its 8 KD values, then the four
                 // lanes (q4) that share the row
@@ -712,7 +717,8 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
 #pragma unroll
                     for (int u = 0; u < 8; ++u) ss = __builtin_fmaf((float)Qr[r][kk][u], (float)Qr[r][kk][u], ss);
                 ss = swap_sum32(swap_sum16(ss));
-                ebr *= inv_norm(ss);
+                iq = inv_norm(ss);
+                ebr *= iq;
             }
             // diag(e^b) Q S^T (S entering chunk c)
 #pragma unroll
@@ -723,7 +729,9 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
                 QSp[ob] = x * ebr;
             }
             // P: K_J Q_RB^T gives lane s = 16 J + 4 q4 + e, r = 16 RB + l15,
-            // and P[r][s] = e^{b_r} e^{-b_s} q_r.k_s for s <= r
+            // and P[r][s] = e^{b_r - b_s} q_r.k_s for s <= r (the factor is
+            // formed from the difference, so it is at most 1; the entries
+            // above the diagonal are selected away, not multiplied)
             f32x4 pv[RB + 2];
 #pragma unroll
             for (int J = 0; J <= RB; ++J) {
@@ -732,7 +740,8 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
                 for (int kk = 0; kk < KD; ++kk) p = mfma32(Kj[J][kk], Qr[r][kk], p);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float v = ebr * nebJ[J][e] * p[e];
+                    float v = __builtin_amdgcn_exp2f(lbr - lbJ[J][e]) * p[e];
+                    if constexpr (RAW) v *= rkJ[J][e] * iq;
                     pv[J][e] = (J < RB || 4 * q4 + e <= l15) ? v : 0.f;
                 }
             }

@@ -45,6 +45,15 @@ constexpr float kNormEps = 1e-6f;
 constexpr float kLog2eF = 1.4426950408889634f;
 constexpr float kLn2F = 0.6931471805599453f;
 
+// Floor on the gate log in the chunked forms.  The chunked forms take
+// differences of in-chunk prefix sums of g, which need finite terms: a gate
+// a = 0 (g = -inf) would make them -inf - (-inf).  Raising every g below
+// the floor to it replaces a < e^{-30} (about 9.4e-14) by e^{-30}, which
+// changes each state by at most that fraction of its previous value -- far
+// below fp32 rounding -- and keeps the prefix sums of a 64-token chunk above
+// -1920, where fp32 differences of them are good to about 1e-4.
+constexpr float kGateFloor = -30.f;
+
 __device__ inline float logistic(float x) {
     return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-x * kLog2eF));
 }
@@ -115,6 +124,10 @@ struct PrefillArgs {
     const int32_t *order;         // schedule [N] or nullptr (identity)
     int32_t *chunk_base;          // varlen: first chunk of each sequence [N+1] (written)
     void *tiles;                  // scalar gate: one kTileBytes record per (chunk, head)
+    // channel gate, bf16: one int32 per (sequence, head) [N, H], written by
+    // the plain pass (1: a chunk decays too far for it) and read by the
+    // reference pass, which redoes those pairs
+    int32_t *unit_wide;
     long long max_chunks;         // chunk records per head in tiles
     int N, T, H;                  // T used only when cu_seqlens == nullptr
     float scale;
@@ -158,8 +171,9 @@ __device__ inline float *seq_ht(const PrefillArgs &a, int n, int h) {
 }
 
 // Per (chunk, head) record of the scalar-gate chunked prefill's workspace:
-// T as MFMA operands of its 16x16 blocks (bf16, 5 KiB), then two
-// rows of the chunk's 64 decay factors (fp32).
+// T as MFMA operands of its 16x16 blocks (bf16, 5 KiB), then two fp32 rows
+// over the chunk's 64 tokens: the gate prefix sums b_r log2(e) and the
+// decay factors e^{b_C - b_r}.
 constexpr size_t kTileBytes = 5 * 1024 + 2 * 64 * 4;
 // With fused preprocessing the record carries the key norms folded into
 // two more factor rows (6 KiB).

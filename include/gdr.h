@@ -69,11 +69,13 @@ enum gdr_mixer { GDR_FA = 0, GDR_SWA = 1, GDR_GDN = 2, GDR_KDA = 3 };
  * tokens in all (B and B*T for gdr_prefill_chunked, N and T_total for
  * gdr_prefill_chunked_varlen) and H heads needs with this dtype and gate
  * kind: the varlen schedule and chunk offsets (N and N+1 int32, each rounded
- * up to 256 bytes) and, for bf16 with the scalar gate, a record of every
- * chunk and head (the chunk-local inverse T and the chunk's decay
- * factors, 5632 bytes) for tokens / 64 + N chunks, an upper bound.
- * Returns 0 for N <= 0, tokens < 0 or H <= 0.  A buffer of this size
- * serves either call with these sizes.
+ * up to 256 bytes); for bf16 with the channel gate, one int32 per (sequence,
+ * head) (rounded up to 256 bytes: the pairs that the second pass redoes,
+ * see gdr_prefill_chunked); for bf16 with the scalar gate, a record of
+ * every chunk and head (the chunk-local inverse T, the gate's prefix sums
+ * and the chunk's decay factors, 5632 bytes) for tokens / 64 + N chunks, an
+ * upper bound.  Returns 0 for N <= 0, tokens < 0 or H <= 0.  A buffer of
+ * this size serves either call with these sizes.
  */
 size_t gdr_prefill_workspace_bytes(enum gdr_dtype dt, enum gdr_gate gk, int N,
                                    long long tokens, int H);
@@ -98,9 +100,9 @@ size_t gdr_prefill_workspace_bytes(enum gdr_dtype dt, enum gdr_gate gk, int N,
  *               ht == h0 is allowed (in-place resume); no other aliasing.
  *   workspace   device buffer, 16-byte aligned, of at least
  *               gdr_prefill_workspace_bytes(dt, gk, B, B*T, H) bytes, used
- *               only for bf16 with the scalar gate (otherwise ignored and may
- *               be NULL); scratch for the duration of the call, not to be
- *               shared with a concurrent call
+ *               for bf16 inputs (fp32 inputs need none: it is ignored and
+ *               may be NULL); scratch for the duration of the call, not to
+ *               be shared with a concurrent call
  *   ws_bytes    its size
  *   stream      hipStream_t
  *
@@ -108,9 +110,17 @@ size_t gdr_prefill_workspace_bytes(enum gdr_dtype dt, enum gdr_gate gk, int N,
  * transform inside the chunk, state carried between chunks in fp32).  fp32
  * inputs run the recurrent form token by token in fp32 on the vector ALUs.
  * With T == 0 nothing is written to o and ht = h0 (zeros if h0 is NULL).
- * The chunked form forms exp(+-cumulative log-gate) inside a chunk; it is
- * accurate while the per-channel sum of g over any 64 consecutive tokens of
- * a chunk stays above -80.
+ * Every gate g in [-inf, 0] is taken, for both gate kinds: the chunked
+ * form never forms a decay factor from a difference of infinite prefix sums
+ * or a factor above 1 from the chunk's whole decay.  It raises g below -30
+ * to -30 (a gate under 9.4e-14 becomes 9.4e-14, a change far below fp32
+ * rounding of the states).  The scalar gate forms each in-chunk factor as
+ * e^{b_r - b_s}, s <= r.  The channel gate runs two passes: the first
+ * factors each chunk from its first token, which is exact while no channel
+ * decays by more than e^80 over the chunk, and marks any (sequence, head)
+ * where one does; the second redoes only the marked pairs with references at
+ * every 16th token (all factors at most 1), and forms a 16-token diagonal
+ * block entry by entry where a channel decays by more than e^70 inside it.
  */
 gdr_status gdr_prefill_chunked(enum gdr_dtype dt, enum gdr_gate gk, int B, int T,
                                int H, int Dk, int Dv, int chunk, float scale,

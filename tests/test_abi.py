@@ -55,8 +55,11 @@ def test_version_and_workspace(lib):
     # schedule and chunk offsets: N and N+1 int32, each rounded up to 256 bytes
     assert gdr.workspace_bytes(f32, False, 0, 0, 4) == 0
     assert gdr.workspace_bytes(f32, False, 1, 100, 4) == 512
-    assert gdr.workspace_bytes(bf, True, 64, 100, 4) == 256 + 512
     assert gdr.workspace_bytes(f32, True, 65, 100, 4) == 512 + 512
+    # bf16, channel gate: + one int32 per (sequence, head), rounded up to 256
+    # bytes (the pairs the plain pass leaves to the reference pass)
+    assert gdr.workspace_bytes(bf, True, 64, 100, 4) == 256 + 512 + 1024
+    assert gdr.workspace_bytes(bf, True, 2, 2 * 8192, 32) == 256 + 256 + 256
     assert gdr.workspace_bytes(f32, False, 2, 100, 0) == 0
     # bf16, scalar gate: + 5632 bytes (T and decay factors) per (chunk, head), for
     # tokens // 64 + N chunks
@@ -262,7 +265,8 @@ def test_backward_rejects(lib):
     o = (2 * 100 * 3 * 128 * 2 + 255) // 256 * 256
     rec = 2 * 3 * 2 * (3 * 64 * 128 * 2 + 64 * 64 * 2 + 128 * 4)
     fwd_gdn = (512 + (200 // 64 + 2) * 3 * 5632 + 255) // 256 * 256
-    assert lib.gdr_backward_workspace_bytes(1, 2, 100, 3, 128, 128) == 2 * st + o + 512 + rec
+    # channel gate: the forward's workspace holds one int32 per (sequence, head) more
+    assert lib.gdr_backward_workspace_bytes(1, 2, 100, 3, 128, 128) == 2 * st + o + 512 + 256 + rec
     assert lib.gdr_backward_workspace_bytes(0, 2, 100, 3, 128, 128) == 2 * st + o + fwd_gdn + rec
     assert lib.gdr_backward_workspace_bytes(1, 2, 0, 3, 128, 128) == 0
 
@@ -287,7 +291,7 @@ def test_backward_varlen_rejects(lib):
     o = (100 * 3 * 128 * 2 + 255) // 256 * 256
     rec = chunks * 3 * (3 * 64 * 128 * 2 + 64 * 64 * 2 + 128 * 4)
     fwd_gdn = (512 + chunks * 3 * 5632 + 255) // 256 * 256
-    assert lib.gdr_backward_varlen_workspace_bytes(1, 2, 100, 3, 128, 128) == 2 * st + o + 512 + rec
+    assert lib.gdr_backward_varlen_workspace_bytes(1, 2, 100, 3, 128, 128) == 2 * st + o + 512 + 256 + rec
     assert lib.gdr_backward_varlen_workspace_bytes(0, 2, 100, 3, 128, 128) == \
         2 * st + o + fwd_gdn + rec
     assert lib.gdr_backward_varlen_workspace_bytes(1, 2, 0, 3, 128, 128) == 0

@@ -191,19 +191,30 @@ def test_prefill_guard_bands():
     pad = 4096
     n_o = x["v"].numel()
     n_h = x["h0"].numel()
+    need = gdr.workspace_bytes(torch.bfloat16, True, 1, 100, 2)
     o_buf = torch.full((n_o + 2 * pad,), 3.0, device=DEV, dtype=torch.bfloat16)
     h_buf = torch.full((n_h + 2 * pad,), 5.0, device=DEV, dtype=torch.float32)
+    w_buf = torch.full((need + 2 * pad,), 0xA5, device=DEV, dtype=torch.uint8)
     lib = gdr._load()
+    rc = lib.gdr_prefill_chunked(
+        1, 1, 1, 100, 2, 128, 128, 64, ctypes.c_float(1.0),
+        x["q"].data_ptr(), x["k"].data_ptr(), x["v"].data_ptr(), x["g"].data_ptr(),
+        x["beta"].data_ptr(), x["h0"].data_ptr(), o_buf.data_ptr() + 2 * pad,
+        h_buf.data_ptr() + 4 * pad, w_buf.data_ptr() + pad, need,
+        ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert rc == 0, lib.gdr_last_error()
+    sync()
+    assert bool((o_buf[:pad] == 3.0).all()) and bool((o_buf[pad + n_o:] == 3.0).all())
+    assert bool((h_buf[:pad] == 5.0).all()) and bool((h_buf[pad + n_h:] == 5.0).all())
+    assert bool((w_buf[:pad] == 0xA5).all()) and bool((w_buf[pad + need:] == 0xA5).all())
+    # without the workspace the call is refused before anything is launched
     rc = lib.gdr_prefill_chunked(
         1, 1, 1, 100, 2, 128, 128, 64, ctypes.c_float(1.0),
         x["q"].data_ptr(), x["k"].data_ptr(), x["v"].data_ptr(), x["g"].data_ptr(),
         x["beta"].data_ptr(), x["h0"].data_ptr(), o_buf.data_ptr() + 2 * pad,
         h_buf.data_ptr() + 4 * pad, None, 0,
         ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
-    assert rc == 0, lib.gdr_last_error()
-    sync()
-    assert bool((o_buf[:pad] == 3.0).all()) and bool((o_buf[pad + n_o:] == 3.0).all())
-    assert bool((h_buf[:pad] == 5.0).all()) and bool((h_buf[pad + n_h:] == 5.0).all())
+    assert rc != 0 and b"workspace" in lib.gdr_last_error()
     o_ref, ht_ref = oracle.forward(x["q"], x["k"], x["v"], x["g"], x["beta"], h0=x["h0"])
     assert_close(o_buf[pad:pad + n_o].view(x["v"].shape), o_ref, torch.bfloat16, "o")
 
@@ -223,9 +234,10 @@ def test_prefill_strong_decay(gate):
 @pytest.mark.parametrize("gate", ["scalar", "channel"])
 def test_prefill_decay_at_the_documented_limit(gate):
     """A constant gate of -75/64 per token puts the cumulative log decay of
-    every full chunk at -75, inside the bound the header states (-80): the
-    chunk's e^{+-b} factors span 65 orders of magnitude and the outputs must
-    still meet the bf16 bar."""
+    every full chunk at -75, just inside the range where the channel gate's
+    first pass factors a chunk from its first token (e^80): the chunk's
+    e^{+-b} factors span 65 orders of magnitude and the outputs must still
+    meet the bf16 bar."""
     x = synthetic.prefill_inputs(1, 200, 2, 128, torch.bfloat16, gate, seed=23, device=DEV)
     x["g"] = torch.full_like(x["g"], -75.0 / 64.0)
     announce("decay at the limit %s: gate sum per chunk %.1f"
