@@ -58,6 +58,9 @@ def _load():
     lib.gdr_prefill_chunked.restype = I
     lib.gdr_prefill_chunked.argtypes = [I, I, I, I, I, I, I, I, F,
                                         P, P, P, P, P, P, P, P, P, Z, P]
+    lib.gdr_prefill_chunked_noalloc.restype = I
+    lib.gdr_prefill_chunked_noalloc.argtypes = [I, I, I, I, I, I, I, I, F,
+                                                P, P, P, P, P, P, P, P, P]
     lib.gdr_prefill_chunked_varlen.restype = I
     lib.gdr_prefill_chunked_varlen.argtypes = [I, I, I, I, I, I, I, I, F, P, P,
                                                P, P, P, P, P, P, P, P, P, Z, P]
@@ -199,6 +202,42 @@ def prefill(q, k, v, g, beta, h0=None, scale: float = 1.0,
         _dt(q), gk, B, T, H, D, D, 64, float(scale), _ptr(q), _ptr(k), _ptr(v),
         _ptr(g), _ptr(beta), _ptr(h0), _ptr(o), _ptr(ht), _ptr(workspace), nbytes,
         _stream(dev)))
+    return o, ht
+
+
+# the library's own per-GPU workspace for prefill_noalloc (include/gdr.h,
+# GDR_NOALLOC_MAX_BYTES)
+NOALLOC_MAX_BYTES = 32 << 20
+
+
+def prefill_noalloc(q, k, v, g, beta, o, h0=None, ht=None, scale: float = 1.0):
+    """prefill() through gdr_prefill_chunked_noalloc, which takes no
+    workspace (the library keeps one array of NOALLOC_MAX_BYTES per GPU) and
+    allocates nothing; o [B,T,H,D] and ht [B,H,D,D] fp32 (or None) are the
+    caller's, so this call allocates nothing either.  Calls that overlap on
+    one GPU race on that array."""
+    B, T, H, D = q.shape
+    dev = q.device
+    for n, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        _dense(n, t, q.dtype, dev)
+    _dense("g", g, torch.float32, dev)
+    _dense("beta", beta, torch.float32, dev)
+    _need(k.shape == q.shape and v.shape == q.shape and o.shape == q.shape,
+          "q, k, v, o shapes differ")
+    _need(beta.shape == (B, T, H), "beta must be [B,T,H]")
+    if g.dim() == 4:
+        _need(g.shape == (B, T, H, D), "channel gate must be [B,T,H,D]")
+        gk = _CHANNEL
+    else:
+        _need(g.shape == (B, T, H), "scalar gate must be [B,T,H]")
+        gk = _SCALAR
+    for n, t in (("h0", h0), ("ht", ht)):
+        if t is not None:
+            _dense(n, t, torch.float32, dev)
+            _need(t.shape == (B, H, D, D), "%s must be [B,H,D,D]" % n)
+    _check(_load().gdr_prefill_chunked_noalloc(
+        _dt(q), gk, B, T, H, D, D, 64, float(scale), _ptr(q), _ptr(k), _ptr(v),
+        _ptr(g), _ptr(beta), _ptr(h0), _ptr(o), _ptr(ht), _stream(dev)))
     return o, ht
 
 

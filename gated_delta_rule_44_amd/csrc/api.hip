@@ -7,6 +7,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/gdr.h"
 #include "gdr_internal.h"
 
@@ -243,7 +245,69 @@ gdr_status prefill_fixed_impl(const char *what, int dt, int gk, int B, int T, in
     return finish(e, s, what);
 }
 
+// The library's own workspace for gdr_prefill_chunked_noalloc: one array per
+// GPU, held from the library's first use on that GPU until the process
+// ends.  Host code never passes the array's name to a kernel (in host code
+// it names a host-side stand-in); it passes the device address that
+// hipGetSymbolAddress returns, taken once per device with that device
+// current.
+constexpr size_t kScratchBytes = GDR_NOALLOC_MAX_BYTES;
+static __device__ __align__(256) char scratch[kScratchBytes];
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+gdr_status scratch_of_current_device(const char *what, void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return fail(GDR_EHIP, "%s: hipGetDevice failed: %s", what, hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(GDR_EUNSUPPORTED, "%s: device %d is beyond the %d the library tracks", what,
+                    dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(GDR_EHIP, "%s: hipGetSymbolAddress(scratch) on device %d failed: %s",
+                        what, dev, hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return GDR_OK;
+}
+
 }  // namespace
+
+extern "C" {
+
+gdr_status gdr_prefill_chunked_noalloc(enum gdr_dtype dt, enum gdr_gate gk, int B, int T, int H,
+                                       int Dk, int Dv, int chunk, float scale, const void *q,
+                                       const void *k, const void *v, const float *g,
+                                       const float *beta, const float *h0, void *o, float *ht,
+                                       void *stream) {
+    const char *what = "gdr_prefill_chunked_noalloc";
+    gdr_status st = check_common(dt, gk, Dk, Dv, what);
+    if (st != GDR_OK) return st;
+    if (B < 0 || T < 0 || H <= 0)
+        return fail(GDR_EINVAL, "%s: bad sizes B=%d T=%d H=%d", what, B, T, H);
+    const size_t need = prefill_layout(dt, gk, B, (long long)B * T, H, false).total;
+    if (need > kScratchBytes)
+        return fail(GDR_EUNSUPPORTED,
+                    "%s: this call needs %zu bytes of workspace, beyond the library's own %zu "
+                    "(use gdr_prefill_chunked with a workspace of that size)",
+                    what, need, kScratchBytes);
+    void *ws = nullptr;
+    if (need > 0) {
+        st = scratch_of_current_device(what, &ws);
+        if (st != GDR_OK) return st;
+    }
+    return prefill_fixed_impl(what, dt, gk, B, T, H, Dk, Dv, chunk, scale, q, k, v, g, beta,
+                              false, 0.f, h0, o, ht, ws, need > 0 ? kScratchBytes : 0, stream);
+}
+
+}  // extern "C"
 
 extern "C" {
 

@@ -130,6 +130,31 @@ gdr_status gdr_prefill_chunked(enum gdr_dtype dt, enum gdr_gate gk, int B, int T
                                void *stream);
 
 /*
+ * gdr_prefill_chunked without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The library keeps its own workspace:
+ * one array of GDR_NOALLOC_MAX_BYTES per GPU, held from the first call on
+ * that GPU until the process ends.  The call allocates and frees nothing.
+ *
+ *   all arguments as gdr_prefill_chunked, without workspace and ws_bytes
+ *
+ * Calls whose workspace (gdr_prefill_workspace_bytes(dt, gk, B, B*T, H))
+ * would exceed GDR_NOALLOC_MAX_BYTES return GDR_EUNSUPPORTED and launch
+ * nothing; GDN B=4 H=16 T=4096 needs 23 MB.  Every call on one GPU uses that
+ * GPU's one array: calls that overlap on one GPU (two streams, two threads)
+ * race and must be ordered by the caller.  Nothing in the array needs
+ * clearing between calls: each call writes every byte it reads.  The device
+ * address of the array is taken once per GPU, on the call's current device,
+ * which must be the device of `stream`.
+ */
+#define GDR_NOALLOC_MAX_BYTES ((size_t)32 << 20)
+gdr_status gdr_prefill_chunked_noalloc(enum gdr_dtype dt, enum gdr_gate gk, int B, int T,
+                                       int H, int Dk, int Dv, int chunk, float scale,
+                                       const void *q, const void *k, const void *v,
+                                       const float *g, const float *beta, const float *h0,
+                                       void *o, float *ht, void *stream);
+
+/*
  * Chunked prefill over a packed variable-length batch.  Sequence n owns
  * tokens [cu_seqlens[n], cu_seqlens[n+1]) of the packed axis; its state
  * starts at h0[n] (zeros if h0 is NULL) and nothing crosses a boundary.

@@ -32,6 +32,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == sorted(["gdr_prefill_workspace_bytes", "gdr_prefill_chunked",
+                            "gdr_prefill_chunked_noalloc",
                             "gdr_prefill_chunked_varlen", "gdr_decode_step",
                             "gdr_decode_placement", "gdr_prefill_varlen_pool",
                             "gdr_decode_tokens", "gdr_decode_commit",
@@ -314,6 +315,28 @@ def test_backward_varlen_rejects(lib):
     assert call(do=None) == EINVAL and "do is NULL" in err()
     assert call(ws_bytes=100) == EINVAL and "workspace" in err()
     assert call(N=0) == 0
+
+
+def test_prefill_noalloc_rejects(lib):
+    """The no-allocation prefill refuses, before any HIP call, a call whose
+    workspace would not fit the library's own array, and bad arguments."""
+    hdr = open(HEADER).read()
+    m = re.search(r"#define GDR_NOALLOC_MAX_BYTES \(\(size_t\)(\d+) << (\d+)\)", hdr)
+    assert m and int(m.group(1)) << int(m.group(2)) == gdr.NOALLOC_MAX_BYTES
+    err = lambda: lib.gdr_last_error().decode()  # noqa: E731
+
+    def call(dt=1, gk=0, B=1, T=64, H=1, D=128, chunk=64):
+        return lib.gdr_prefill_chunked_noalloc(dt, gk, B, T, H, D, D, chunk, F(1.0), FAKE,
+                                               FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None)
+    # GDN: 5632 bytes per (chunk, head); 4 x 4096 tokens x 64 heads is 92 MB
+    need = gdr.workspace_bytes(torch.bfloat16, False, 4, 4 * 4096, 64)
+    assert need > gdr.NOALLOC_MAX_BYTES
+    assert call(B=4, T=4096, H=64) == EUNSUPPORTED and "beyond the library's own" in err()
+    assert call(dt=7) == EINVAL and "dtype" in err()
+    assert call(H=0) == EINVAL and "bad sizes" in err()
+    assert call(D=96) == EUNSUPPORTED
+    # the headline GDN workload fits
+    assert gdr.workspace_bytes(torch.bfloat16, False, 4, 4 * 4096, 16) <= gdr.NOALLOC_MAX_BYTES
 
 
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
