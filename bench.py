@@ -29,9 +29,15 @@ The same line carries:
                 backward of the GDN and KDA prefill workloads and of the
                 packed KDA workload.
 
+Times: each step is bracketed by HIP events on the launch stream; `value`
+and `ms_per_step` come from the median step, `roofline.achieved` from the
+mean (the average call time, as rocprofv3 reports kernel averages).
 Defaults: 100 warmup steps and 200 timed steps (a fifth of each for the
 decode and varlen workloads): the GPU reaches its steady clock only after
 about a hundred prefill calls, so shorter warm-ups time part of the ramp.
+The secondary list also carries the latency of one fp32 call on the GDN
+recurrent workload (B=1 H=1 T=64 d=64), and the oracle's rate on the other
+workloads in full beside the GPU's.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
                        [--only-headline] [--no-cpu-baseline]
@@ -92,19 +98,26 @@ def decode_bytes(head_steps, gate_bytes):
     return head_steps * (2 * D * D * 4 + 3 * D * 2 + D * 2 + 4) + gate_bytes
 
 
+LAST_MEAN_MS = [0.0]
+
+
 def timed(fn, steps, warmup, stream):
+    """Median ms per step over `steps` timed steps, each bracketed by HIP
+    events on the launch stream (the mean is kept in LAST_MEAN_MS[0])."""
     import torch
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(stream)
     for i in range(steps):
         fn(i)
-    end.record(stream)
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
-    return start.elapsed_time(end) / steps   # ms per step
+    per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    LAST_MEAN_MS[0] = ev[0].elapsed_time(ev[steps]) / steps
+    mid = steps // 2
+    return per[mid] if steps % 2 else 0.5 * (per[mid - 1] + per[mid])
 
 
 def bench_prefill(gdr, synthetic, torch, dev, B, T, H, gate, seed, steps, warmup,
@@ -134,6 +147,28 @@ def bench_prefill(gdr, synthetic, torch, dev, B, T, H, gate, seed, steps, warmup
     ms = timed(step, steps, warmup, stream)
     del xs, outs, ws
     return ms
+
+
+def bench_recurrent(gdr, synthetic, torch, dev, steps, warmup):
+    """One fp32 call on the GDN recurrent workload (B=1, H=1, T=64, d=64,
+    zero initial state): its latency."""
+    x = synthetic.prefill_inputs(1, 64, 1, 64, torch.float32, "scalar", seed=1000, h0=False,
+                                 device=dev)
+    o = torch.empty_like(x["v"])
+    ht = torch.empty((1, 1, 64, 64), device=dev, dtype=torch.float32)
+    lib = gdr._load()
+    import ctypes
+    stream = torch.cuda.current_stream(dev)
+    P = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    args = [0, 0, 1, 64, 1, 64, 64, C, ctypes.c_float(1.0)] + \
+        [P(t) for t in (x["q"], x["k"], x["v"], x["g"], x["beta"], None, o, ht)] + \
+        [None, ctypes.c_size_t(0), ctypes.c_void_p(stream.cuda_stream)]
+
+    def step(i):
+        rc = lib.gdr_prefill_chunked(*args)
+        if rc:
+            raise RuntimeError(lib.gdr_last_error().decode())
+    return timed(step, steps, warmup, stream)
 
 
 def bench_fused(gdr, synthetic, torch, dev, B, T, H, gate, seed, steps, warmup, h0=True,
@@ -318,36 +353,87 @@ def bench_varlen_pool(gdr, synthetic, torch, dev, steps, warmup):
     return ms, sum(lens)
 
 
-def cpu_baseline(synthetic, torch, target_s=12.0):
-    """fp64 oracle on the host cores over the GDN prefill workload (all 64
-    sequence-heads, 4096 tokens each), repeated until about target_s seconds
-    of wall time have accumulated (or truncated to fewer tokens per sequence
-    if one pass would take much longer)."""
-    import oracle
-    B, T, H = 4, 4096, 16
-    x = synthetic.prefill_inputs(B, T, H, D, torch.bfloat16, "scalar", seed=1001,
-                                 device="cpu")
-    threads = oracle.max_threads()
+def host_threads():
+    """(threads the oracle runs on, CPUs in this process's affinity mask):
+    the affinity mask, capped by OMP_NUM_THREADS when that is set."""
+    aff = len(os.sched_getaffinity(0))
+    try:
+        omp = int(os.environ.get("OMP_NUM_THREADS", "0"))
+    except ValueError:
+        omp = 0
+    return (min(aff, omp) if omp > 0 else aff), aff
 
-    def run(ts):
-        sl = {n: x[n][:, :ts].contiguous() for n in ("q", "k", "v", "g", "beta")}
+
+def cpu_baseline(synthetic, torch, target_s=3.0):
+    """The fp64 oracle as it stands on the host cores, on the workloads'
+    inputs drawn on the host: the GDN prefill in full (the headline's;
+    repeated until about target_s seconds have passed), the KDA prefill in
+    full, one step of the placement decode over all its recurrent layers,
+    and the packed KDA prefill at 8 of its 32 heads (its rate scaled to all
+    of them).  Returns (the headline's baseline, entries for the other
+    workloads)."""
+    import numpy as np
+    import oracle
+    threads, aff = host_threads()
+
+    def prefill_s(B, T, H, gate, seed, h0):
+        x = synthetic.prefill_inputs(B, T, H, D, torch.bfloat16, gate, seed=seed, h0=h0,
+                                     device="cpu")
         t0 = time.perf_counter()
-        oracle.forward(sl["q"], sl["k"], sl["v"], sl["g"], sl["beta"], h0=x["h0"])
+        oracle.forward(x["q"], x["k"], x["v"], x["g"], x["beta"], h0=x["h0"], threads=threads)
         return time.perf_counter() - t0
 
-    cal = 64
-    dt = run(cal)
-    ts = int(min(T, max(cal, cal * target_s / max(dt, 1e-6))))
-    total_t, total_tok, reps = 0.0, 0, 0
-    while total_t < target_s * 0.8 or reps == 0:
-        total_t += run(ts)
-        total_tok += B * ts
+    total_t, reps = 0.0, 0
+    while total_t < target_s or reps == 0:
+        total_t += prefill_s(4, 4096, 16, "scalar", 1001, True)
         reps += 1
-    return {"value": total_tok / total_t, "unit": "tokens/s", "cores": threads,
-            "kind": "oracle",
-            "sample": "GDN prefill B=4 H=16 d=128, first %d of 4096 tokens of every "
-                      "sequence (all 64 sequence-heads), fp64 token-by-token, %d pass(es), "
-                      "%.1f s" % (ts, reps, total_t)}
+    head = {"value": reps * 4 * 4096 / total_t, "unit": "tokens/s", "cores": threads,
+            "host_cores": aff, "kind": "oracle",
+            "sample": "GDN prefill B=4 H=16 T=4096 d=128 in full (all 64 sequence-heads), "
+                      "fp64 token by token, %d pass(es), %.1f s" % (reps, total_t)}
+    out = []
+    t2 = prefill_s(2, 8192, 32, "channel", 1002, False)
+    out.append({"workload": "kda_prefill_B2_H32_T8192_d128_bf16", "value": 2 * 8192 / t2,
+                "unit": "tokens/s", "seconds": t2, "sample": "in full"})
+    # placement decode: every recurrent layer of one step
+    place = synthetic.placement(0, 48)
+    rec = [l for l in range(48) if place[l] in (synthetic.GDN, synthetic.KDA)]
+    gen = torch.Generator().manual_seed(1003)
+    t3 = 0.0
+    for l in rec:
+        q = torch.randn((256, 32, D), generator=gen)
+        q = (q / q.norm(dim=-1, keepdim=True)).to(torch.bfloat16)
+        k = torch.randn((256, 32, D), generator=gen)
+        k = (k / k.norm(dim=-1, keepdim=True)).to(torch.bfloat16)
+        v = torch.randn((256, 32, D), generator=gen).to(torch.bfloat16)
+        beta = torch.sigmoid(torch.randn((256, 32), generator=gen))
+        c = 0.1 if place[l] == synthetic.GDN else 0.05
+        g = -torch.nn.functional.softplus(torch.randn((256, 32, D), generator=gen)) * c
+        if place[l] == synthetic.GDN:
+            g = g[..., 0].contiguous()
+        st = torch.randn((256, 32, D, D), generator=gen) * 0.02
+        t0 = time.perf_counter()
+        oracle.decode(q, k, v, g, beta, st, threads=threads)
+        t3 += time.perf_counter() - t0
+    out.append({"workload": "placement_decode_L48_B256_H32_d128_bf16",
+                "value": 256 / t3, "unit": "tokens/s", "head_steps_per_s": len(rec) * 256 * 32 / t3,
+                "seconds": t3, "sample": "one step over the %d recurrent layers (inputs of the "
+                                         "same law, host-drawn)" % len(rec)})
+    # packed KDA: all 16 sequences in full, 8 of the 32 heads (the work per
+    # head is the same), scaled to the whole workload's tokens/s
+    lens = synthetic.varlen_lengths(943)
+    x = synthetic.varlen_inputs(lens, 8, D, torch.bfloat16, "channel", seed=1004, device="cpu")
+    t0 = time.perf_counter()
+    oracle.forward(x["q"], x["k"], x["v"], x["g"], x["beta"], h0=x["h0"],
+                   cu_seqlens=x["cu_seqlens_host"], threads=threads)
+    t4 = time.perf_counter() - t0
+    out.append({"workload": "kda_varlen_N16_H32_d128_bf16", "value": int(np.sum(lens)) * 8 / 32 / t4,
+                "unit": "tokens/s", "seconds": t4,
+                "sample": "all 16 sequences (%d tokens) at 8 of the 32 heads, rate scaled to "
+                          "32 heads" % int(np.sum(lens))})
+    for e in out:
+        e.update({"cores": threads, "host_cores": aff, "kind": "oracle"})
+    return head, out
 
 
 def main():
@@ -426,11 +512,14 @@ def main():
     B, T, H = 4, 4096, 16
     ms = bench_prefill(gdr, synthetic, torch, dev, B, T, H, "scalar", 1001,
                        args.steps, args.warmup)
+    ms_mean = LAST_MEAN_MS[0]
     tokens = B * T
     th = tokens * H
     nbytes = prefill_bytes(th, B * H, "scalar")
     flops = prefill_flops(th)
-    achieved = nbytes / (ms * 1e-3) / 1e9
+    # the roofline takes the average call time (the rocprofv3 kernel
+    # averages are averages too); value and ms_per_step the median
+    achieved = nbytes / (ms_mean * 1e-3) / 1e9
     line = {
         "metric": METRIC,
         "value": tokens / (ms * 1e-3),
@@ -439,6 +528,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms,
+        "ms_per_step_mean": ms_mean,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -452,12 +542,18 @@ def main():
                      "traffic": measured_traffic(),
                      "kernel": "prep_kernel<128> + chain_kernel<128> (one gdr_prefill_chunked call)",
                      "algorithmic_bytes_per_launch": nbytes,
-                     "mfma_tflops_alg": flops / (ms * 1e-3) / 1e12,
-                     "mfma_frac_alg": flops / (ms * 1e-3) / 1e12 / MFMA_BF16_TFLOPS},
+                     "mfma_tflops_alg": flops / (ms_mean * 1e-3) / 1e12,
+                     "mfma_frac_alg": flops / (ms_mean * 1e-3) / 1e12 / MFMA_BF16_TFLOPS},
     }
 
     if not args.only_headline:
         sec = []
+        # the fp32 recurrent GDN workload (B=1 H=1 T=64 d=64): the latency of
+        # one call
+        ms0 = bench_recurrent(gdr, synthetic, torch, dev, args.steps, args.warmup)
+        sec.append({"workload": "gdn_recurrent_B1_H1_T64_d64_fp32", "latency_us": ms0 * 1e3,
+                    "latency_us_mean": LAST_MEAN_MS[0] * 1e3,
+                    "tokens_per_s": 64 / (ms0 * 1e-3)})
         ms2 = bench_prefill(gdr, synthetic, torch, dev, 2, 8192, 32, "channel", 1002,
                             args.steps, args.warmup, h0=False, sets=3)
         th2 = 2 * 8192 * 32
@@ -539,7 +635,12 @@ def main():
         line["secondary"] = sec
 
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(synthetic, torch)
+        head, others = cpu_baseline(synthetic, torch)
+        line["cpu_baseline"] = head
+        for e in others:
+            for s_ in line.get("secondary", []):
+                if s_["workload"] == e["workload"]:
+                    s_["cpu_baseline"] = {k: v for k, v in e.items() if k != "workload"}
     print(json.dumps(line), flush=True)
 
 

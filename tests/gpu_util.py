@@ -71,3 +71,23 @@ def assert_close(x, ref, dtype, what="", rows=True):
 
 def announce(msg):
     print(msg, flush=True)
+
+
+def assert_pairs_close(x, ref, what=""):
+    """bf16 bar per (sequence, head): x and ref are [pairs, ...] (one entry
+    per pair, any trailing shape); each pair's relative Frobenius error must
+    meet the bar on its own.  Returns the largest."""
+    x, ref = to_np(x), to_np(ref)
+    worst = 0.0
+    for i in range(ref.shape[0]):
+        e = rel_fro(x[i], ref[i])
+        assert e <= BF16_REL_FRO, "%s: pair %d rel-Frobenius %.3e > %.0e" % (what, i, e, BF16_REL_FRO)
+        worst = max(worst, e)
+    return worst
+
+
+def heads_first(t):
+    """[B, T, H, ...] -> [B * H, T, ...] (one entry per (sequence, head))."""
+    t = to_np(t)
+    B, T, H = t.shape[:3]
+    return np.moveaxis(t, 2, 1).reshape(B * H, T, *t.shape[3:])

@@ -11,7 +11,7 @@ import gated_delta_rule_44_amd as gdr
 import oracle
 from gated_delta_rule_44_amd import synthetic
 from tests.conftest import gpu_available
-from tests.gpu_util import announce, assert_close
+from tests.gpu_util import announce, assert_close, assert_pairs_close, heads_first
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
@@ -103,27 +103,25 @@ def test_decode_tokens_fused(dt, gate, D):
     announce("  err o=%.2e ckpt=%.2e" % (eo, ec))
 
 
-def _sampled_fused(B, T, H, gate, seed, pairs):
+def _full_fused(B, T, H, gate, seed):
     x = synthetic.raw_prefill_inputs(B, T, H, 128, torch.bfloat16, gate, seed=seed,
                                      h0=gate == "scalar", device=DEV)
     o, ht = gdr.prefill_fused(*[x[n] for n in RAW], x["gate_scale"], h0=x["h0"])
     sync()
-    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(ht).all())
-    for b, h in pairs:
-        sl = {n: x[n][b:b + 1, :, h:h + 1].contiguous() for n in RAW}
-        sl["gate_scale"] = x["gate_scale"]
-        h0 = None if x["h0"] is None else x["h0"][b:b + 1, h:h + 1].contiguous()
-        o_ref, ht_ref = oracle.forward(*_ref_inputs(sl), h0=h0)
-        eo = assert_close(o[b:b + 1, :, h:h + 1], o_ref, torch.bfloat16, "o[%d,:,%d]" % (b, h))
-        eh = assert_close(ht[b:b + 1, h:h + 1], ht_ref, torch.bfloat16, "ht[%d,%d]" % (b, h))
-        announce("  (b=%d,h=%d) rel-fro o=%.2e ht=%.2e" % (b, h, eo, eh))
+    announce("  kernels done; fp64 oracle over all %d (sequence, head) pairs" % (B * H))
+    o_ref, ht_ref = oracle.forward(*_ref_inputs(x), h0=x["h0"])
+    eo = assert_close(o, o_ref, torch.bfloat16, "o")
+    eh = assert_close(ht, ht_ref, torch.bfloat16, "ht")
+    po = assert_pairs_close(heads_first(o), heads_first(o_ref), "o")
+    ph = assert_pairs_close(ht.reshape(B * H, 128, 128), ht_ref.reshape(B * H, 128, 128), "ht")
+    announce("  rel-fro o=%.2e ht=%.2e; worst pair o=%.2e ht=%.2e" % (eo, eh, po, ph))
 
 
 def test_fused_gdn_prefill_B4_H16_T4096():
     announce("fused GDN prefill B=4 H=16 T=4096 (raw projections)")
-    _sampled_fused(4, 4096, 16, "scalar", 1011, [(0, 0), (2, 9), (3, 15)])
+    _full_fused(4, 4096, 16, "scalar", 1011)
 
 
 def test_fused_kda_prefill_B2_H32_T8192():
     announce("fused KDA prefill B=2 H=32 T=8192 (raw projections)")
-    _sampled_fused(2, 8192, 32, "channel", 1012, [(0, 3), (1, 30)])
+    _full_fused(2, 8192, 32, "channel", 1012)

@@ -150,11 +150,35 @@ def test_prefill_inplace_resume(dt):
     assert_close(st, ht_ref, DTYPES[dt], "ht split")
 
 
-def test_prefill_deterministic():
-    x = synthetic.prefill_inputs(2, 300, 4, 128, torch.bfloat16, "channel", seed=8, device=DEV)
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
+@pytest.mark.parametrize("wide", [False, True])
+def test_prefill_deterministic(gate, wide):
+    """Run to run, bit for bit: a race on LDS or a reordered reduction would
+    show here.  Scalar gate: the chunk-local kernel and the recurrence;
+    channel gate: the plain pass, and (wide) the reference pass as well."""
+    x = synthetic.prefill_inputs(2, 300, 4, 128, torch.bfloat16, gate, seed=8, device=DEV)
+    if wide:
+        x["g"][:, 100:120] = -9.0
     o1, h1 = run_prefill(x)
-    o2, h2 = run_prefill(x)
-    assert torch.equal(o1, o2) and torch.equal(h1, h2)
+    for _ in range(3):
+        o2, h2 = run_prefill(x)
+        assert torch.equal(o1, o2) and torch.equal(h1, h2)
+
+
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
+def test_prefill_varlen_deterministic(gate):
+    """The packed form (longest-first schedule, chunk offsets on the device)
+    bit for bit from run to run, at the packed workload's length mix."""
+    lens = synthetic.varlen_lengths(943)
+    lens = [max(1, l // 16) for l in lens]          # the same mix, 1/16 of the tokens
+    x = synthetic.varlen_inputs(lens, 4, 128, torch.bfloat16, gate, seed=10, device=DEV)
+    runs = []
+    for _ in range(3):
+        runs.append(gdr.prefill_varlen(x["q"], x["k"], x["v"], x["g"], x["beta"], x["cu_seqlens"],
+                                       h0=x["h0"], cu_seqlens_host=x["cu_seqlens_host"]))
+        sync()
+    for o, h in runs[1:]:
+        assert torch.equal(runs[0][0], o) and torch.equal(runs[0][1], h)
 
 
 def test_prefill_equal_channel_gates_match_scalar_gate():
