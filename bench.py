@@ -59,24 +59,30 @@ METRIC = "GDN/KDA prefill tokens/s + decode state-update GB/s (% of HBM peak), 1
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_TFLOPS = 2500.0
 D, C = 128, 64
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "chunked_prefill_gdn_B4_H16_T4096_traffic.json")
-KERNEL_SRC = os.path.join(ROOT, "gated_delta_rule_44_amd", "csrc", "chunked_chain.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_DIR = os.path.join(ROOT, "gated_delta_rule_44_amd", "csrc")
 
 
-def measured_traffic():
-    """HBM bytes per headline prefill call (its two kernels) from rocprofv3
-    FETCH_SIZE / WRITE_SIZE counters (scaled by the factors a plain copy of
-    known size gives), or None when they were taken on another version of
-    the kernel source."""
+def measured_traffic(workload):
+    """HBM bytes per call of a workload (all its kernels) from rocprofv3
+    FETCH_SIZE / WRITE_SIZE counters, scaled by the factors a plain copy of
+    known size gives (profiles/traffic.json), and their ratio to the
+    algorithmic bytes; None when the counters were taken on another version
+    of the kernel sources."""
+    import glob
     import hashlib
     try:
         rec = json.load(open(TRAFFIC_FILE))
-        src = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+        h = hashlib.sha256()
+        for f in sorted(glob.glob(os.path.join(KERNEL_DIR, "*"))):
+            h.update(open(f, "rb").read())
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_sha256") != src:
+    w = rec.get("workloads", {}).get(workload)
+    if rec.get("kernel_sources_sha256") != h.hexdigest() or not w or "bytes_per_call" not in w:
         return None
-    return rec["bytes_per_launch"]
+    return {"bytes_per_call": w["bytes_per_call"],
+            "over_algorithmic": w["traffic_over_algorithmic"]}
 
 
 def prefill_bytes(tokens_heads, units, gate):
@@ -442,9 +448,10 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--only-headline", action="store_true")
-    ap.add_argument("--only", choices=["kda_prefill", "decode", "varlen", "draft", "varlen_pool",
-                                       "fused_gdn", "fused_kda", "backward_gdn", "backward_kda",
-                                       "backward_kda_varlen"],
+    ap.add_argument("--only", choices=["gdn_prefill", "kda_prefill", "decode", "varlen", "draft",
+                                       "varlen_pool", "fused_gdn", "fused_kda", "backward_gdn",
+                                       "backward_kda", "backward_kda_varlen", "recurrent",
+                                       "hbm_copy"],
                     default=None,
                     help="time one secondary workload alone (for profiling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -460,6 +467,27 @@ def main():
     from gated_delta_rule_44_amd import synthetic
     dev = torch.device("cuda:0")
 
+    if args.only == "gdn_prefill":
+        ms = bench_prefill(gdr, synthetic, torch, dev, 4, 4096, 16, "scalar", 1001,
+                           args.steps, args.warmup)
+        print(json.dumps({"workload": "gdn_prefill_B4_H16_T4096_d128_bf16", "ms_per_step": ms,
+                          "ms_per_step_mean": LAST_MEAN_MS[0]}))
+        return
+    if args.only == "recurrent":
+        ms = bench_recurrent(gdr, synthetic, torch, dev, args.steps, args.warmup)
+        print(json.dumps({"workload": "gdn_recurrent_B1_H1_T64_d64_fp32", "latency_us": ms * 1e3}))
+        return
+    if args.only == "hbm_copy":
+        # a plain device-to-device copy of 1 GiB: what the memory system
+        # reaches for a pure stream, and the known byte count that the HBM
+        # counters are calibrated against
+        src = torch.empty(1 << 28, device=dev, dtype=torch.float32).normal_()
+        dst = torch.empty_like(src)
+        ms = timed(lambda i: dst.copy_(src), args.steps, args.warmup, torch.cuda.current_stream(dev))
+        nb = 2 * src.numel() * 4
+        print(json.dumps({"workload": "hbm_copy_1GiB", "ms_per_step": ms, "bytes_per_step": nb,
+                          "GB_per_s": nb / (ms * 1e-3) / 1e9, "frac_hbm": nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}))
+        return
     if args.only == "kda_prefill":
         ms = bench_prefill(gdr, synthetic, torch, dev, 2, 8192, 32, "channel", 1002,
                            args.steps, args.warmup, h0=False)
@@ -539,7 +567,7 @@ def main():
                    "state": "fp32, h0 and ht", "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(),
+                     "traffic": (measured_traffic("gdn_prefill") or {}).get("bytes_per_call"),
                      "kernel": "prep_kernel<128> + chain_kernel<128> (one gdr_prefill_chunked call)",
                      "algorithmic_bytes_per_launch": nbytes,
                      "mfma_tflops_alg": flops / (ms_mean * 1e-3) / 1e12,
@@ -632,6 +660,18 @@ def main():
                     "ms_per_step": msv, "tokens_per_s": tokv / (msv * 1e-3),
                     "GB_per_s": bb / (msv * 1e-3) / 1e9,
                     "frac_hbm": bb / (msv * 1e-3) / 1e9 / HBM_PEAK_GBS})
+        keys = {"kda_prefill_B2_H32_T8192_d128_bf16": "kda_prefill",
+                "placement_decode_L48_B256_H32_d128_bf16": "decode",
+                "kda_varlen_N16_H32_d128_bf16": "varlen",
+                "gdn_draft_decode_B256_n4_H32_d128_bf16": "draft",
+                "fused_gdn_prefill_B4_H16_T4096_d128_bf16": "fused_gdn",
+                "fused_kda_prefill_B2_H32_T8192_d128_bf16": "fused_kda",
+                "backward_gdn_B4_H16_T4096_d128_bf16": "backward_gdn",
+                "backward_kda_B2_H32_T8192_d128_bf16": "backward_kda",
+                "gdn_recurrent_B1_H1_T64_d64_fp32": "recurrent"}
+        for e in sec:
+            if e["workload"] in keys:
+                e["traffic"] = measured_traffic(keys[e["workload"]])
         line["secondary"] = sec
 
     if not args.no_cpu_baseline:
