@@ -663,7 +663,7 @@ BwdWs bwd_layout(int gk, int N, long long tokens, long long chunks, int H, int D
     w.dstates = st;
     w.o = 2 * st;
     w.fwd = w.o + r256((size_t)tokens * H * Dv * 2);
-    w.recs = w.fwd + r256(prefill_layout(GDR_BF16, gk, N, tokens, H, false).total);
+    w.recs = w.fwd + r256(ws_layout(gk == GDR_GATE_SCALAR, true, N, tokens, H).total);
     w.total = w.recs + (size_t)chunks * H * gdr::backward_record_bytes(Dk);
     return w;
 }
@@ -732,13 +732,13 @@ gdr_status gdr_backward_chunked(enum gdr_dtype dt, enum gdr_gate gk, int B, int 
     char *ws = static_cast<char *>(workspace);
     // 1. the forward, keeping the state that enters every chunk
     const bool tiles = gk == GDR_GATE_SCALAR;
-    const WsLayout FL = prefill_layout(GDR_BF16, gk, B, (long long)B * T, H, false);
+    const WsLayout FL = ws_layout(tiles, true, B, (long long)B * T, H);
     gdr::PrefillArgs f{};
     f.q = q; f.k = k; f.v = v; f.g = g; f.beta = beta; f.h0 = h0;
     f.o = ws + W.o; f.ht = nullptr;
     f.cu_seqlens = nullptr; f.order = nullptr; f.chunk_base = nullptr;
     f.tiles = tiles ? ws + W.fwd + FL.tiles : nullptr;
-    f.unit_wide = tiles ? nullptr : reinterpret_cast<int32_t *>(ws + W.fwd + FL.units);
+    f.unit_wide = reinterpret_cast<int32_t *>(ws + W.fwd + FL.units);
     f.max_chunks = tiles ? (long long)B * ((T + 63) / 64) : 0;
     f.N = B; f.T = T; f.H = H; f.scale = scale; f.channel_gate = gk == GDR_GATE_CHANNEL;
     f.states = reinterpret_cast<float *>(ws + W.states);
@@ -751,6 +751,7 @@ gdr_status gdr_backward_chunked(enum gdr_dtype dt, enum gdr_gate gk, int B, int 
     a.states = reinterpret_cast<float *>(ws + W.states);
     a.dstates = reinterpret_cast<float *>(ws + W.dstates);
     a.recs = ws + W.recs;
+    a.unit_wide = f.unit_wide;
     a.cu_seqlens = nullptr; a.chunk_base = nullptr; a.chunks = fixed_chunks(B, T);
     a.B = B; a.T = T; a.H = H; a.nc = (T + 63) / 64; a.scale = scale;
     a.channel_gate = gk == GDR_GATE_CHANNEL;
@@ -817,7 +818,7 @@ gdr_status gdr_backward_chunked_varlen(enum gdr_dtype dt, enum gdr_gate gk, int 
     }
     char *ws = static_cast<char *>(workspace);
     const bool tiles = gk == GDR_GATE_SCALAR;
-    const WsLayout FL = prefill_layout(GDR_BF16, gk, N, T_total, H, false);
+    const WsLayout FL = ws_layout(tiles, true, N, T_total, H);
     int32_t *order = reinterpret_cast<int32_t *>(ws + W.fwd + FL.order);
     int32_t *cbase = reinterpret_cast<int32_t *>(ws + W.fwd + FL.chunk_base);
     // 1. the forward (longest sequences first), keeping the state that
@@ -830,7 +831,7 @@ gdr_status gdr_backward_chunked_varlen(enum gdr_dtype dt, enum gdr_gate gk, int 
     f.o = ws + W.o; f.ht = nullptr;
     f.cu_seqlens = cu_seqlens; f.order = order; f.chunk_base = cbase;
     f.tiles = tiles ? ws + W.fwd + FL.tiles : nullptr;
-    f.unit_wide = tiles ? nullptr : reinterpret_cast<int32_t *>(ws + W.fwd + FL.units);
+    f.unit_wide = reinterpret_cast<int32_t *>(ws + W.fwd + FL.units);
     f.max_chunks = FL.max_chunks;
     f.N = N; f.T = 0; f.H = H; f.scale = scale; f.channel_gate = gk == GDR_GATE_CHANNEL;
     f.states = reinterpret_cast<float *>(ws + W.states);
@@ -843,6 +844,7 @@ gdr_status gdr_backward_chunked_varlen(enum gdr_dtype dt, enum gdr_gate gk, int 
     a.states = reinterpret_cast<float *>(ws + W.states);
     a.dstates = reinterpret_cast<float *>(ws + W.dstates);
     a.recs = ws + W.recs;
+    a.unit_wide = f.unit_wide;
     a.cu_seqlens = cu_seqlens; a.chunk_base = cbase; a.chunks = chunks;
     a.B = N; a.T = 0; a.H = H; a.nc = 0; a.scale = scale;
     a.channel_gate = gk == GDR_GATE_CHANNEL;

@@ -176,6 +176,8 @@ __device__ inline void gate_load(f32x4 (&gv)[C * D / 4 / NT], const float *gg, s
     for (int it = 0; it < C * D / 4 / NT; ++it) {
         const int p = it * NT + tid, r = p / (D / 4), j = 4 * (p % (D / 4));
         gv[it] = r < Cc ? *reinterpret_cast<const f32x4 *>(gg + (size_t)r * gstr + j) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) gv[it][u] = __builtin_fmaxf(gv[it][u], kGateFloor);   // as the forward
     }
 }
 template <int D, int NT>
@@ -283,7 +285,7 @@ __global__ __launch_bounds__(512) void chunk_grad_kernel(BwdArgs a) {
         sm.hrow[tid] = 0.f;
     }
     if (!CH && w == 0) {
-        const float gv = lane < Cc ? gg[(size_t)lane * gstr] : 0.f;
+        const float gv = lane < Cc ? __builtin_fmaxf(gg[(size_t)lane * gstr], kGateFloor) : 0.f;
         sm.bs[lane] = wave_prefix_sum(gv);
     }
     if (tid < D) sm.dbC[tid] = 0.f;
@@ -1066,6 +1068,45 @@ size_t backward_record_bytes(int D) {
     return D == 128 ? ChainRec<128>::BYTES : ChainRec<64>::BYTES;
 }
 
+// The chunk factorisation above (k e^{-b} inside a chunk) holds while no
+// channel decays by more than e^80 over a chunk.  The forward pass marks
+// the (sequence, head) pairs where one does (unit_wide); their gradients --
+// all of them, as the state gradient passes through the chunk to every
+// earlier one -- are set to NaN here rather than left wrong.  One
+// workgroup per (pair, part of its tokens).
+constexpr int kPoisonParts = 16;
+template <int D>
+__global__ __launch_bounds__(256) void poison_kernel(BwdArgs a) {
+    const long long unit = blockIdx.x / kPoisonParts;
+    const int part = blockIdx.x % kPoisonParts;
+    if (unit >= (long long)a.B * a.H || !a.unit_wide[unit]) return;
+    const int n = (int)(unit / a.H), h = (int)(unit % a.H);
+    long long t0, len;
+    if (a.cu_seqlens) {
+        t0 = a.cu_seqlens[n];
+        len = a.cu_seqlens[n + 1] - t0;
+    } else {
+        t0 = (long long)n * a.T;
+        len = a.T;
+    }
+    const float nan = __builtin_nanf("");
+    const long long per = (len + kPoisonParts - 1) / kPoisonParts;
+    const long long r0 = part * per, r1 = r0 + per < len ? r0 + per : len;
+    for (long long idx = r0 * D + threadIdx.x; idx < r1 * D; idx += 256) {
+        const long long t = t0 + idx / D;
+        const int j = (int)(idx % D);
+        const size_t o = ((size_t)t * a.H + h) * D + j;
+        a.dq[o] = nan;
+        a.dk[o] = nan;
+        a.dv[o] = nan;
+        if (a.channel_gate) a.dg[o] = nan;
+        else if (j == 0) a.dg[(size_t)t * a.H + h] = nan;
+        if (j == 0) a.dbeta[(size_t)t * a.H + h] = nan;
+    }
+    if (a.dh0 && part == 0)
+        for (int e = threadIdx.x; e < D * D; e += 256) a.dh0[(size_t)unit * D * D + e] = nan;
+}
+
 hipError_t launch_backward(int D, const BwdArgs &a, hipStream_t s) {
     const long long heads = (long long)a.B * a.H;
     if (heads <= 0 || a.chunks <= 0) return hipSuccess;
@@ -1085,6 +1126,12 @@ hipError_t launch_backward(int D, const BwdArgs &a, hipStream_t s) {
         hipLaunchKernelGGL(adjoint_chain_kernel<64>, gr, blk, 0, s, a);
         if (a.channel_gate) hipLaunchKernelGGL((chunk_grad_kernel<64, true, false>), gc, blk8, 0, s, a);
         else                hipLaunchKernelGGL((chunk_grad_kernel<64, false, false>), gc, blk8, 0, s, a);
+    }
+    if (a.unit_wide) {
+        if (heads * kPoisonParts >= (1LL << 31)) return hipErrorInvalidValue;
+        dim3 gp((unsigned)(heads * kPoisonParts));
+        if (D == 128) hipLaunchKernelGGL(poison_kernel<128>, gp, dim3(256), 0, s, a);
+        else          hipLaunchKernelGGL(poison_kernel<64>, gp, dim3(256), 0, s, a);
     }
     return hipGetLastError();
 }

@@ -375,7 +375,7 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float gv = RAW ? rgf[i][e] : rgc[i][e >> 2][e & 3];
-                run[e] += REF ? __builtin_fmaxf(gv, kGateFloor) : gv;
+                run[e] += __builtin_fmaxf(gv, kGateFloor);
                 cum[par][i][e] = run[e];
             }
         }
@@ -398,8 +398,7 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
     // per-wave totals -> exclusive prefix over the waves and chunk total, one
     // thread per key channel (threads 64 .. 64+D-1, phase C); and flags:
     // the plain pass notes a chunk that some channel decays by more than
-    // e^{kChunkDecayMax} over the chunk (wide; also any gate of -inf, which
-    // the plain pass does not clamp), the reference pass the 16-row blocks
+    // e^{kChunkDecayMax} over the chunk (wide), the reference pass the 16-row blocks
     // (two waves each) that some channel decays by more than e^{kDiagDecayMax}
     auto prefix = [&](int par) {
         const int ch = tid0 - 64;

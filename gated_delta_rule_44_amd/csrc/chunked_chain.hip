@@ -505,6 +505,7 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
         __syncthreads();                      // chunks 0 and 1 staged
         prefetch(0, 0);
         int m3 = 0;                           // c mod 3
+        bool wide = false;                    // a chunk decays by more than e^80
         for (long long c = 0; c < nch; ++c) {
             const int par = (int)(c & 1);
             const int n3 = m3 == 2 ? 0 : m3 + 1;
@@ -513,6 +514,7 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
 #pragma unroll
                 for (int jk = 0; jk < KS; ++jk) *reinterpret_cast<f32x4 *>(sp + srow(jk, 0)) = St[jk];
             }
+            wide |= !(gC >= 1.8e-35f);        // e^{b_C} < e^-80
             // ---- alpha: X = V - diag(e^b) K S^T, U = T X and the state
             //      update, all from registers
             f32x4 X[4];
@@ -567,6 +569,8 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
         }
         __syncthreads();                      // outputs of the last chunk
         __syncthreads();
+        if (a.unit_wide && tile == 0 && w == 0 && lane == 0)
+            a.unit_wide[(size_t)n * a.H + h] = wide ? 1 : 0;
         if (float *htp = seq_ht<D>(a, n, h)) {
 #pragma unroll
             for (int jk = 0; jk < KS; ++jk) *reinterpret_cast<f32x4 *>(htp + srow0 + srow(jk, 0)) = St[jk];

@@ -124,9 +124,11 @@ struct PrefillArgs {
     const int32_t *order;         // schedule [N] or nullptr (identity)
     int32_t *chunk_base;          // varlen: first chunk of each sequence [N+1] (written)
     void *tiles;                  // scalar gate: one kTileBytes record per (chunk, head)
-    // channel gate, bf16: one int32 per (sequence, head) [N, H], written by
-    // the plain pass (1: a chunk decays too far for it) and read by the
-    // reference pass, which redoes those pairs
+    // one int32 per (sequence, head) [N, H]: 1 where some chunk decays by
+    // more than e^80 in some channel.  Channel gate, bf16: written by the
+    // plain pass and read by the reference pass, which redoes those pairs;
+    // scalar gate: written by the recurrence kernel when set (the backward
+    // reads it), otherwise nullptr
     int32_t *unit_wide;
     long long max_chunks;         // chunk records per head in tiles
     int N, T, H;                  // T used only when cu_seqlens == nullptr
@@ -199,6 +201,9 @@ struct BwdArgs {
     const int32_t *cu_seqlens;    // [B+1] or nullptr (fixed length)
     const int32_t *chunk_base;    // [B+1] (packed batches)
     long long chunks;             // global chunks the grid covers (an upper bound when packed)
+    // [B, H]: pairs the forward marked (a chunk decays by more than e^80 in
+    // some channel); their gradients are set to NaN.  nullptr: none marked.
+    const int32_t *unit_wide;
     int B, T, H, nc;              // T, nc: fixed length only
     float scale;
     int channel_gate;

@@ -265,7 +265,9 @@ def test_backward_rejects(lib):
     st = 2 * 3 * 2 * 128 * 128 * 4
     o = (2 * 100 * 3 * 128 * 2 + 255) // 256 * 256
     rec = 2 * 3 * 2 * (3 * 64 * 128 * 2 + 64 * 64 * 2 + 128 * 4)
-    fwd_gdn = (512 + (200 // 64 + 2) * 3 * 5632 + 255) // 256 * 256
+    # the forward's workspace: schedule, chunk offsets, one int32 per (sequence, head)
+    # (rounded to 256 bytes), the records
+    fwd_gdn = (512 + 256 + (200 // 64 + 2) * 3 * 5632 + 255) // 256 * 256
     # channel gate: the forward's workspace holds one int32 per (sequence, head) more
     assert lib.gdr_backward_workspace_bytes(1, 2, 100, 3, 128, 128) == 2 * st + o + 512 + 256 + rec
     assert lib.gdr_backward_workspace_bytes(0, 2, 100, 3, 128, 128) == 2 * st + o + fwd_gdn + rec
@@ -291,7 +293,7 @@ def test_backward_varlen_rejects(lib):
     st = chunks * 3 * 128 * 128 * 4
     o = (100 * 3 * 128 * 2 + 255) // 256 * 256
     rec = chunks * 3 * (3 * 64 * 128 * 2 + 64 * 64 * 2 + 128 * 4)
-    fwd_gdn = (512 + chunks * 3 * 5632 + 255) // 256 * 256
+    fwd_gdn = (512 + 256 + chunks * 3 * 5632 + 255) // 256 * 256
     assert lib.gdr_backward_varlen_workspace_bytes(1, 2, 100, 3, 128, 128) == 2 * st + o + 512 + 256 + rec
     assert lib.gdr_backward_varlen_workspace_bytes(0, 2, 100, 3, 128, 128) == \
         2 * st + o + fwd_gdn + rec

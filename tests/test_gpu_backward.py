@@ -72,6 +72,35 @@ def test_backward_strong_decay(gate):
     _check(got, ref, "strong decay %s" % gate)
 
 
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
+def test_backward_beyond_its_range_is_nan(gate):
+    """The backward factors each chunk from its first token, which holds while
+    no channel decays by more than e^80 over a chunk.  A (sequence, head)
+    where one does gets NaN for all its gradients (never silently wrong
+    ones); the other pairs are exact, including one with a gate of zero at a
+    single token (g = -inf, which the kernels raise to -30 like the
+    forward)."""
+    announce("backward beyond its range %s" % gate)
+    B, T, H, D = 2, 150, 2, 128
+    x = synthetic.prefill_inputs(B, T, H, D, torch.bfloat16, gate, seed=73, device=DEV)
+    x["g"][0, 64:90, 1] = -6.0                 # pair (0, 1): chunk 1 decays by e^-156
+    x["g"][1, 10, 0] = float("-inf")           # pair (1, 0): one zero gate
+    do, dht = _upstream(B, T, H, D, 74)
+    got = gdr.backward(x["q"], x["k"], x["v"], x["g"], x["beta"], do, h0=x["h0"], dht=dht)
+    sync()
+    dq, dk, dv, dg, dbeta, dh0 = got
+    for t in (dq[0, :, 1], dk[0, :, 1], dv[0, :, 1], dg[0, :, 1], dbeta[0, :, 1], dh0[0, 1]):
+        assert bool(torch.isnan(t).all()), "the wide pair's gradients are not all NaN"
+    ref = oracle.backward(x["q"], x["k"], x["v"], x["g"], x["beta"], do, h0=x["h0"], dht=dht)
+    for b, h in ((0, 0), (1, 0), (1, 1)):
+        sel = lambda t, tok: t[b, :, h] if tok else t[b, h]  # noqa: E731
+        for n, gt, rf in zip(NAMES, got, ref):
+            tok = n != "dh0"
+            assert_close(sel(gt, tok), sel(torch.as_tensor(rf), tok) if not isinstance(rf, np.ndarray)
+                         else (rf[b, :, h] if tok else rf[b, h]), torch.bfloat16,
+                         "%s (b=%d, h=%d)" % (n, b, h))
+
+
 def _varlen_case(lens, H, D, gate, seed, scale=0.8):
     x = synthetic.varlen_inputs(lens, H, D, torch.bfloat16, gate, seed=seed, device=DEV)
     cu = x["cu_seqlens_host"]
