@@ -33,14 +33,19 @@
 // rows from global memory straight into registers and form P and O one
 // chunk behind.  Two staging waves (SIMDs 0 and 1, no MFMA work) bring the
 // k rows, the v slice and the chunk's record (T and the decay factors)
-// of chunk c+2 into LDS while chunk c runs, their global loads issued one
-// and a half iterations before the LDS stores.
-// Two barriers per chunk; iteration c:
-//   alpha: chain: X, U, state update (chunk c), from registers | output
-//          waves: O (c-1) | staging: chunk c+2 from registers into LDS
-//   beta:  chain: publish U, S^T; LDS operands of chunk c+1 into registers |
-//          output waves: diag(e^b) Q S^T and P (c), global loads of the q
-//          rows of c+2 | staging: global loads of chunk c+4
+// of chunk c+2 into LDS while chunk c runs, their global loads issued two
+// iterations before the LDS stores.
+// One barrier per chunk; between barriers c-1 and c (iteration c):
+//   chain:   X, U and the state update of chunk c from registers, then
+//            publish U (by chunk parity) and the new S^T, and read the LDS
+//            operands of chunk c+1 into registers
+//   output:  O of chunk c-1 (U of c-1 was published in iteration c-1), then
+//            diag(e^b) Q S^T and P of chunk c (S^T entering c likewise), and
+//            the global loads of the q rows of c+2
+//   staging: chunk c+2 from registers into LDS, global loads of chunk c+4
+// Every LDS value is written in one iteration and read in the next (U and
+// S^T are double-buffered by chunk parity, the staged chunks are held in
+// three slots), so the one barrier orders every producer before its reader.
 #include "gdr_internal.h"
 #include "device_util.h"
 
@@ -363,7 +368,7 @@ template <int D, bool RAW> struct ChainSmem {
     alignas(16) bf16 V[3][C * PV];      // by chunk mod 3
     alignas(16) TRec TR[3];             // by chunk mod 3
     alignas(16) bf16x8 SB[2][2][KD][64];// S^T entering a chunk (by parity), per chain wave
-    alignas(16) bf16x8 UB[2][2][64];    // U as operands, per chain wave
+    alignas(16) bf16x8 UB[2][2][2][64]; // U as operands (by parity), per chain wave
 };
 
 template <int D, bool RAW>
@@ -412,6 +417,14 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
     const bf16 *vg = static_cast<const bf16 *>(a.v) + (size_t)h * D + i0;
     bf16 *og = static_cast<bf16 *>(a.o) + (size_t)h * D + i0;
     const long long nch = (t1 - t0 + C - 1) / C;
+    // The output and staging waves run their loops in pairs of iterations
+    // (two register sets) with one exit test per pair, so that the compiler
+    // sees a single back edge and waits on each register set by the loads
+    // issued after it (an exit test between the two halves gives it a path
+    // on which the newest loads would be waited for at once).  All roles
+    // pass nhalf + 1 barriers: iterations 0 .. nch do work, the rest (at most
+    // one) find nothing to load or store.
+    const long long nhalf = (nch + 2) & ~1LL;
 
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -458,19 +471,48 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
 #pragma unroll
             for (int kk = 0; kk < KD; ++kk) sm.SB[spar][ib][kk][lane] = acc_pair(St[2 * kk], St[2 * kk + 1]);
         };
-        // operands of a chunk, read a phase ahead of their use: k row
-        // fragments, K^T, the v slice, T and the decay factors.  K^T comes
-        // from transpose loads of the k rows: lane j of each 16-lane group
-        // addresses k columns 32 (jk >> 1) + 8 (j & 3) + 4 (jk & 1) .. +3, so
-        // output lane i receives k = srow(jk, .) for row i of the block.
+        // operands of a chunk, read an iteration ahead of their use: k row
+        // fragments, K^T, the v slice, T and the decay factors
         bf16x8 Kf[4][KD], KT[KS][2], Ta[4][2];
         bf16x4 vv[4];
         f32x4 eb[4], hs[4];
         float gC = 0.f;
-        auto prefetch = [&](long long c, int m3) {
+        // operands of the chunk in slot m3 read while the previous chunk's
+        // state update runs: k row fragments, e^{b_C - b}, T and e^{b_C}
+        auto prefetch_rows = [&](int m3) {
+            const bf16 *Kc = sm.K[m3];
+            const typename Sm::TRec &R = sm.TR[m3];
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) {
+#pragma unroll
+                for (int kk = 0; kk < KD; ++kk) Kf[rb][kk] = frag_rows(Kc, PD, 16 * rb, 32 * kk, lane);
+                hs[rb] = *reinterpret_cast<const f32x4 *>(&R.hs[16 * rb + 4 * q4]);
+                Ta[rb][0] = rb == 0 ? cat8(R.halves[0][lane], bf16x4{}) : R.pairs[rb - 1][lane];
+                Ta[rb][1] = rb == 2 ? cat8(R.halves[1][lane], bf16x4{})
+                          : (rb == 3 ? R.pairs[3][lane] : bf16x8{});
+            }
+            gC = __builtin_amdgcn_exp2f(R.lb[C - 1]);
+        };
+        // the rest, after the update: the v slice, e^b, and K^T of the chunk
+        // in slot m3 by transpose loads: lane j of each
+        // 16-lane group addresses k columns 32 (jk >> 1) + 8 (j & 3) +
+        // 4 (jk & 1) .. +3, so output lane i receives k = srow(jk, .) for
+        // row i of the block
+        auto prefetch_kt = [&](int m3) {
             const bf16 *Kc = sm.K[m3];
             const bf16 *Vc = sm.V[m3];
             const typename Sm::TRec &R = sm.TR[m3];
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) {
+                vv[rb] = frag_col4(Vc, PV, 16 * rb, 16 * ib, lane);
+                if constexpr (RAW) {
+                    eb[rb] = *reinterpret_cast<const f32x4 *>(&R.ek[16 * rb + 4 * q4]);
+                } else {
+                    const f32x4 lb = *reinterpret_cast<const f32x4 *>(&R.lb[16 * rb + 4 * q4]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) eb[rb][e] = __builtin_amdgcn_exp2f(lb[e]);
+                }
+            }
 #pragma unroll
             for (int jk = 0; jk < KS; ++jk) {
                 const int pc = 32 * (jk >> 1) + 8 * (l15 & 3) + 4 * (jk & 1);
@@ -482,28 +524,11 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
                     KT[jk][kk] = cat8(__builtin_bit_cast(bf16x4, lo), __builtin_bit_cast(bf16x4, hi));
                 }
             }
-#pragma unroll
-            for (int rb = 0; rb < 4; ++rb) {
-#pragma unroll
-                for (int kk = 0; kk < KD; ++kk) Kf[rb][kk] = frag_rows(Kc, PD, 16 * rb, 32 * kk, lane);
-                vv[rb] = frag_col4(Vc, PV, 16 * rb, 16 * ib, lane);
-                if constexpr (RAW) {
-                    eb[rb] = *reinterpret_cast<const f32x4 *>(&R.ek[16 * rb + 4 * q4]);
-                } else {
-                    const f32x4 lb = *reinterpret_cast<const f32x4 *>(&R.lb[16 * rb + 4 * q4]);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) eb[rb][e] = __builtin_amdgcn_exp2f(lb[e]);
-                }
-                hs[rb] = *reinterpret_cast<const f32x4 *>(&R.hs[16 * rb + 4 * q4]);
-                Ta[rb][0] = rb == 0 ? cat8(R.halves[0][lane], bf16x4{}) : R.pairs[rb - 1][lane];
-                Ta[rb][1] = rb == 2 ? cat8(R.halves[1][lane], bf16x4{})
-                          : (rb == 3 ? R.pairs[3][lane] : bf16x8{});
-            }
-            gC = __builtin_amdgcn_exp2f(R.lb[C - 1]);
         };
         publish_state(0);
         __syncthreads();                      // chunks 0 and 1 staged
-        prefetch(0, 0);
+        prefetch_rows(0);
+        prefetch_kt(0);
         int m3 = 0;                           // c mod 3
         bool wide = false;                    // a chunk decays by more than e^80
         for (long long c = 0; c < nch; ++c) {
@@ -514,8 +539,9 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
 #pragma unroll
                 for (int jk = 0; jk < KS; ++jk) *reinterpret_cast<f32x4 *>(sp + srow(jk, 0)) = St[jk];
             }
-            wide |= !(gC >= 1.8e-35f);        // e^{b_C} < e^-80
-            // ---- alpha: X = V - diag(e^b) K S^T, U = T X and the state
+            const float gCc = gC;             // e^{b_C} of chunk c
+            wide |= !(gCc >= 1.8e-35f);       // e^{b_C} < e^-80
+            // ---- X = V - diag(e^b) K S^T, U = T X and the state
             //      update, all from registers
             f32x4 X[4];
             {
@@ -550,25 +576,27 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
 #pragma unroll
                 for (int sb = 0; sb < 4; ++sb) Uh[sb] = U[sb] * hs[sb];
                 const bf16x8 Bh[2] = {acc_pair(Uh[0], Uh[1]), acc_pair(Uh[2], Uh[3])};
+                // the next chunk's operands but K^T, in flight during the update
+                __builtin_amdgcn_sched_barrier(0);
+                prefetch_rows(n3);
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int jk = 0; jk < KS; ++jk) {
-                    f32x4 sv = St[jk] * gC;
+                    f32x4 sv = St[jk] * gCc;
                     sv = mfma32(KT[jk][0], Bh[0], sv);
                     sv = mfma32(KT[jk][1], Bh[1], sv);
                     St[jk] = sv;
                 }
             }
-            __syncthreads();
-            // ---- beta: publish U and S^T; operands of the next chunk
-            sm.UB[ib][0][lane] = Ub[0];
-            sm.UB[ib][1][lane] = Ub[1];
+            // publish U and S^T; the rest of the next chunk's operands
+            sm.UB[par][ib][0][lane] = Ub[0];
+            sm.UB[par][ib][1][lane] = Ub[1];
             publish_state(par ^ 1);
-            prefetch(c + 1, n3);
+            prefetch_kt(n3);
             __syncthreads();
             m3 = n3;
         }
-        __syncthreads();                      // outputs of the last chunk
-        __syncthreads();
+        for (long long c = nch; c < nhalf; ++c) __syncthreads();   // outputs of the last chunk
         if (a.unit_wide && tile == 0 && w == 0 && lane == 0)
             a.unit_wide[(size_t)n * a.H + h] = wide ? 1 : 0;
         if (float *htp = seq_ht<D>(a, n, h)) {
@@ -581,8 +609,8 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
     if (w >= 4 && w < 6) {
         // =================================================================
         // staging waves: k rows, the v slice and the record (T, factors) of
-        // chunk c+2 into LDS during alpha of iteration c, from registers
-        // loaded during beta of iteration c-2 (two register sets)
+        // chunk c+2 into LDS in iteration c, from registers loaded in
+        // iteration c-2 (two register sets)
         // =================================================================
         const int tl = tid - 256;
         bf16x8 rs[2][NI];
@@ -629,23 +657,22 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
         st_store(0, R0);
         st_load(1, R0);
         st_store(1, R0);
+        // chunk 2 strictly before chunk 3: the loop waits for each register
+        // set by the number of loads issued after it, which assumes this order
         st_load(2, R0);
+        __builtin_amdgcn_sched_barrier(0);
         st_load(3, R1);
         __syncthreads();
         int m3 = 2;                           // (c + 2) mod 3
-        for (long long c = 0;; c += 2) {
+        for (long long c = 0; c < nhalf; c += 2) {
             st_store(m3, R0);
             m3 = m3 == 2 ? 0 : m3 + 1;
-            __syncthreads();
             st_load(c + 4, R0);
             __syncthreads();
-            if (c + 1 > nch) break;
             st_store(m3, R1);
             m3 = m3 == 2 ? 0 : m3 + 1;
-            __syncthreads();
             st_load(c + 5, R1);
             __syncthreads();
-            if (c + 2 > nch) break;
         }
         return;
     }
@@ -657,11 +684,11 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
     // ends up with four adjacent columns of one output row: the published
     // S^T and U serve as A operands, the q rows and P^T as B operands.  P^T
     // is formed in accumulator registers, so it feeds the MFMA directly.
-    // Iteration c, alpha: O of chunk c-1 (U of chunk c-1 was published during
-    // beta of c-1); beta: QS and P of chunk c (S^T entering chunk c was
-    // published during beta of c-1, and chunk c's k rows stay in LDS until
-    // alpha of c+1), then the q rows of chunk c+2, from global memory
-    // straight into registers.
+    // Iteration c: O of chunk c-1 (U of chunk c-1 was published in iteration
+    // c-1), then QS and P of chunk c (S^T entering chunk c was published in
+    // iteration c-1, and chunk c's k rows stay in their LDS slot until
+    // iteration c+1 refills it), then the q rows of chunk c+2, from global
+    // memory straight into registers.
     // =====================================================================
     auto out_loop = [&](auto RBc) {
         constexpr int RB = decltype(RBc)::value;
@@ -679,10 +706,11 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
         // O of chunk c-1
         auto o_step = [&](long long c) {
             bf16x8 Au[2][NP2];
+            const int up = (int)((c - 1) & 1);
 #pragma unroll
             for (int ob = 0; ob < 2; ++ob)
 #pragma unroll
-                for (int k2 = 0; k2 < NP2; ++k2) Au[ob][k2] = sm.UB[ob][k2][lane];
+                for (int k2 = 0; k2 < NP2; ++k2) Au[ob][k2] = sm.UB[up][ob][k2][lane];
             const rsrc_t ro = make_rsrc(og + (size_t)chunk_tok(c - 1) * tokstride, extent(c - 1, BV * 2));
             const unsigned voff = l15 * rowb + 8 * q4;
 #pragma unroll
@@ -754,27 +782,24 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
             for (int k2 = 0; k2 < NP2; ++k2) Pp[k2] = acc_pair(pv[2 * k2], pv[2 * k2 + 1]);
         };
         q_load(0, R0);
+        __builtin_amdgcn_sched_barrier(0);    // chunk 0 strictly before chunk 1, as in the loop
         q_load(1, R1);
         QSp[0] = QSp[1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int k2 = 0; k2 < NP2; ++k2) Pp[k2] = bf16x8{};
         __syncthreads();
         int m3 = 0;                           // c mod 3
-        for (long long c = 0;; c += 2) {
+        for (long long c = 0; c < nhalf; c += 2) {
             o_step(c);
-            __syncthreads();
             qp_step(c, m3, R0);
             q_load(c + 2, R0);
             m3 = m3 == 2 ? 0 : m3 + 1;
             __syncthreads();
-            if (c + 1 > nch) break;
             o_step(c + 1);
-            __syncthreads();
             qp_step(c + 1, m3, R1);
             q_load(c + 3, R1);
             m3 = m3 == 2 ? 0 : m3 + 1;
             __syncthreads();
-            if (c + 2 > nch) break;
         }
     };
     if (w == 2)      out_loop(std::integral_constant<int, 0>{});
