@@ -648,11 +648,11 @@ namespace {
 // Backward workspace for N sequences, `tokens` tokens and `chunks` chunk
 // slots (fixed length: N ceil(T / 64); packed: the bound tokens / 64 + N):
 // the chunk-entering states and the chunk state gradients ([chunks, H, Dv,
-// Dk] fp32 each), the forward's outputs (bf16, unused), the forward's own
-// workspace (its schedule and chunk_base are reused) and the adjoint
-// chain's per-chunk records.
+// Dk] fp32 each), the forward's own workspace (its schedule and chunk_base
+// are reused) and the adjoint chain's per-chunk records.  The forward runs
+// without storing its outputs.
 struct BwdWs {
-    size_t states, dstates, o, fwd, recs, total;
+    size_t states, dstates, fwd, recs, total;
 };
 BwdWs bwd_layout(int gk, int N, long long tokens, long long chunks, int H, int Dk, int Dv) {
     BwdWs w{};
@@ -661,8 +661,7 @@ BwdWs bwd_layout(int gk, int N, long long tokens, long long chunks, int H, int D
     const size_t st = (size_t)chunks * H * Dv * Dk * sizeof(float);
     w.states = 0;
     w.dstates = st;
-    w.o = 2 * st;
-    w.fwd = w.o + r256((size_t)tokens * H * Dv * 2);
+    w.fwd = 2 * st;
     w.recs = w.fwd + r256(ws_layout(gk == GDR_GATE_SCALAR, true, N, tokens, H).total);
     w.total = w.recs + (size_t)chunks * H * gdr::backward_record_bytes(Dk);
     return w;
@@ -735,7 +734,7 @@ gdr_status gdr_backward_chunked(enum gdr_dtype dt, enum gdr_gate gk, int B, int 
     const WsLayout FL = ws_layout(tiles, true, B, (long long)B * T, H);
     gdr::PrefillArgs f{};
     f.q = q; f.k = k; f.v = v; f.g = g; f.beta = beta; f.h0 = h0;
-    f.o = ws + W.o; f.ht = nullptr;
+    f.o = nullptr; f.ht = nullptr;
     f.cu_seqlens = nullptr; f.order = nullptr; f.chunk_base = nullptr;
     f.tiles = tiles ? ws + W.fwd + FL.tiles : nullptr;
     f.unit_wide = reinterpret_cast<int32_t *>(ws + W.fwd + FL.units);
@@ -828,7 +827,7 @@ gdr_status gdr_backward_chunked_varlen(enum gdr_dtype dt, enum gdr_gate gk, int 
     if (e != hipSuccess) return finish(e, s, what);
     gdr::PrefillArgs f{};
     f.q = q; f.k = k; f.v = v; f.g = g; f.beta = beta; f.h0 = h0;
-    f.o = ws + W.o; f.ht = nullptr;
+    f.o = nullptr; f.ht = nullptr;
     f.cu_seqlens = cu_seqlens; f.order = order; f.chunk_base = cbase;
     f.tiles = tiles ? ws + W.fwd + FL.tiles : nullptr;
     f.unit_wide = reinterpret_cast<int32_t *>(ws + W.fwd + FL.units);

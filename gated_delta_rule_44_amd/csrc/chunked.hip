@@ -179,7 +179,7 @@ template <int D> struct Smem {
 // once, with three workgroup barriers:
 //   chunk j-1 ("state"):  U = T X, then O = Qt S0^T + P U and the state update
 //   chunk j   ("prep"):   gated operands -> LDS, A -> L, T (diagonal blocks by
-//                         the MFMA series, the rest by block substitution), P,
+//                         doubling, the rest by block substitution), P,
 //                         X, Qt S0^T
 //   chunk j+1 ("gate"):   gated operands in registers
 //   chunk j+2 ("scan"):   prefix sums of the gate logs
@@ -547,12 +547,12 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
     auto store_gate = [&](const LI &L, int par) {
 #pragma unroll
         for (int i = 0; i < RPT; ++i) {
-            const int r = L.rg * RPT + i;
-            *reinterpret_cast<bf16x8 *>(&sm.Q[r * PD + 8 * L.cg]) = gq[i];
-            *reinterpret_cast<bf16x8 *>(&sm.K[r * PD + 8 * L.cg]) = gk[i];
-            *reinterpret_cast<bf16x8 *>(&sm.Kb[par][r * PD + 8 * L.cg]) = gkb[i];
+            const unsigned e = (unsigned)((L.rg * RPT + i) * PD + 8 * L.cg);
+            *reinterpret_cast<bf16x8 *>(sm.Q + e) = gq[i];
+            *reinterpret_cast<bf16x8 *>(sm.K + e) = gk[i];
+            *reinterpret_cast<bf16x8 *>(sm.Kb[par] + e) = gkb[i];
         }
-        *reinterpret_cast<bf16x4 *>(&sm.V[L.vr * PV + L.vc]) = rv[par];
+        *reinterpret_cast<bf16x4 *>(sm.V + (unsigned)(L.vr * PV + L.vc)) = rv[par];
         if (L.tid < C) sm.beta[L.tid] = RAW ? logistic(rb[par]) : rb[par];
     };
 
@@ -763,27 +763,48 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
                     gram(kf, qf, bf, aoff, poff);
                 }
                 // M = L_bb = strict_lower(diag(beta) A_bb) as acc(M) and
-                // acc(M^T); Y = (I + M)^{-1} = (I - M)(I + M^2)(I + M^4)(I + M^8)
-                // (M^16 = 0).  An MFMA with A operand acc(X^T) and B operand
-                // acc(Z) yields acc(X Z).
+                // acc(M^T) (lane holds M[4 l4 + e][l15], M^T[4 l4 + e][l15]).
+                // Y = (I + M)^{-1} by doubling: with Y_k the inverse of the
+                // part of I + M inside the diagonal blocks of size 2^k and E_k
+                // the part of M joining the two halves of each block of size
+                // 2^{k+1}, Y_{k+1} = Y_k - Y_k E_k Y_k exactly (E_k Y_k E_k = 0),
+                // from Y_0 = I to Y_4 = Y.  Every term is an entry of a true
+                // inverse times entries of M, so the bf16 operands never carry
+                // the large, cancelling terms of a power series in M.  An
+                // MFMA with A operand acc(X^T) and B operand acc(Z) yields
+                // acc(X Z); Y and Y^T are carried side by side.
                 const float bl = sm.beta[16 * b + l15];
                 const f32x4 br4 = *reinterpret_cast<const f32x4 *>(&sm.beta[16 * b + 4 * l4]);
-                f32x4 MT, Mn, I4;
+                f32x4 MT, Mn;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int sl = 4 * l4 + e;
                     MT[e] = sl < l15 ? bl * adT[e] : 0.f;
                     Mn[e] = sl > l15 ? br4[e] * ad[e] : 0.f;
-                    I4[e] = sl == l15 ? 1.f : 0.f;
                 }
-                const f32x4 M2 = mfma16z(cvt4(MT), cvt4(Mn));
-                const f32x4 M2T = mfma16z(cvt4(Mn), cvt4(MT));
-                const f32x4 Z1 = mfma16(cvt4(M2T), cvt4(I4 - Mn), I4 - Mn);
-                const f32x4 M4 = mfma16z(cvt4(M2T), cvt4(M2));
-                const f32x4 M4T = mfma16z(cvt4(M2), cvt4(M2T));
-                const f32x4 Z2 = mfma16(cvt4(M4T), cvt4(Z1), Z1);
-                const f32x4 M8T = mfma16z(cvt4(M4), cvt4(M4T));
-                const f32x4 Y = mfma16(cvt4(M8T), cvt4(Z2), Z2);
+                // entry (r, s) of E_k: r, s in one block of 2^{k+1}, r in its
+                // lower and s in its upper half
+                auto joins = [](int k, int r, int sc) {
+                    return (r >> k) == (sc >> k) + 1 && (r >> (k + 1)) == (sc >> (k + 1));
+                };
+                f32x4 Y, YT;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int sl = 4 * l4 + e;
+                    const float id = sl == l15 ? 1.f : 0.f;
+                    Y[e] = id - (joins(0, sl, l15) ? Mn[e] : 0.f);    // Y_1 = I - E_0
+                    YT[e] = id - (joins(0, l15, sl) ? MT[e] : 0.f);
+                }
+#pragma unroll
+                for (int k = 1; k < 4; ++k) {
+                    f32x4 ET;   // acc(E_k^T)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) ET[e] = joins(k, l15, 4 * l4 + e) ? MT[e] : 0.f;
+                    const f32x4 P = mfma16z(cvt4(ET), cvt4(Y));     // E_k Y_k
+                    const f32x4 Yn = mfma16(cvt4(-YT), cvt4(P), Y); // Y_k - Y_k P
+                    YT = mfma16(cvt4(-P), cvt4(YT), YT);            // Y_k^T - P^T Y_k^T
+                    Y = Yn;
+                }
                 // acc(Y): Y[4 l4 + e][l15] -> T^T[s = l15][r] = Y[r][s] beta_s and
                 // Y^T[b][c = l15][r]
                 *reinterpret_cast<bf16x4 *>(&sm.TT[(16 * b + l15) * PCT + 16 * b + 4 * l4]) = cvt4(Y * bl);
@@ -808,7 +829,7 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
                 const long long tc = t0 + (j - 1) * C;
                 const int Cc = valid_rows(j - 1);
                 const unsigned rowb = (unsigned)(tokstride * 2);
-                const rsrc_t ro = make_rsrc(og + (size_t)tc * tokstride, (Cc - 1) * rowb + BV * 2);
+                const rsrc_t ro = make_rsrc(og + (size_t)tc * tokstride, a.o ? (Cc - 1) * rowb + BV * 2 : 0u);
 #pragma unroll
                 for (int jv = 0; jv < 2; ++jv)
                     bstore8s(ro, (16 * I + l15) * rowb + 2 * (16 * jv + 4 * l4), 0u, cvt4(ov[jv]));
@@ -1006,6 +1027,10 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(PrefillArgs a) {
         using E = std::integral_constant<int, 0>;
         using O = std::integral_constant<int, 1>;
         iteration(E{}, std::false_type{}, std::true_type{}, 0);
+        // no loads in flight on entry (vmcnt(0), other counters left as
+        // they are): the loop's waits then follow from its own body alone,
+        // whatever registers the peeled iteration loaded
+        __builtin_amdgcn_s_waitcnt(0x0F70);
         long long j = 1;
         for (; j + 1 < nch; j += 2) {
             iteration(O{}, std::true_type{}, std::true_type{}, j);

@@ -13,15 +13,19 @@
 //     O = scale (diag(e^b) Q S^T + P U)
 //     S^T <- e^{b_C} S^T + K^T diag(e^{b_C - b}) U
 //
-// prep_kernel (one workgroup per chunk and head) forms T, which does not
-// depend on the state, and writes it with the chunk's decay factors to a
-// record in the workspace, laid out as the MFMA A operands of U = T X (one
-// 16-byte piece per lane and operand).  Each diagonal block
-// Y_bb = (I + L_bb)^{-1} is the finite series (I - M)(I + M^2)(I + M^4)(I + M^8)
-// of its strictly lower 16x16 block M (M^16 = 0), on 16x16x16 MFMAs computed
-// in both orientations because an MFMA takes its A operand transposed
-// relative to the accumulator layout.  Off the diagonal, block forward
-// substitution Y_ij = -Y_ii sum_{k=j}^{i-1} L_ik Y_kj; T = Y diag(beta).
+// prep_kernel (one workgroup per chunk and head) forms what U needs that
+// does not depend on the state, and writes it with the chunk's decay factors
+// to a record in the workspace, laid out as MFMA A operands (one 8- or
+// 16-byte piece per lane and operand): the diagonal 16x16 blocks of
+// T = N diag(beta), N = (I + L)^{-1}, and the blocks A_IJ (I > J) of A
+// negated.  The recurrence kernel then solves (I + L) U = diag(beta) X by
+// block forward substitution,
+//     U_I = T_II (X_I - sum_{J<I} A_IJ U_J),
+// whose terms are bounded by |A| <= 1 and |U|, rather than applying the full
+// T, whose entries can grow large and cancel when beta A nears 1 (keys close
+// to one direction).  Each N_II is formed in fp32 by forward substitution,
+// one column per lane, and rounded once; a finite series in the nilpotent
+// part would add terms that grow like binomial coefficients there.
 //
 // chain_kernel (one workgroup per sequence, head and 32-wide slice of Dv)
 // walks the chunks in order.  The only dependency from chunk to chunk is the
@@ -64,9 +68,11 @@ __device__ inline int ltri(int i, int j) { return i * (i - 1) / 2 + j; }  // blo
 template <int D> struct PrepSmem {
     static constexpr int PD = D + 16;   // conflict-free 16-byte row fragments
     alignas(16) bf16 K[C * PD];
-    alignas(16) bf16 TT[10 * 256];      // T_ij^T, i >= j
-    alignas(16) bf16 LT[6 * 256];       // L_ij^T, i > j
-    alignas(16) bf16 YD[4][2][256];     // Y_bb, Y_bb^T
+    alignas(16) float MT[4][256];       // L_bb^T, [s][r] (strictly lower L_bb)
+    alignas(16) float Nd[4][256];       // N_bb, [r][s]
+    // the record's operands as tiles (lane l: row l & 15, columns 4 (l >> 4)
+    // .. +3): T_00, T_11, T_22, T_33, -A_10, -A_32, -A_20, -A_21, -A_30, -A_31
+    alignas(16) bf16 TT[10 * 256];
     alignas(16) float fb[C];            // b_r
     alignas(16) float fbeta[C];         // beta_r
     alignas(16) float frk[C];           // 1 / |k_r| (fused preprocessing)
@@ -194,132 +200,106 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a) {
         const f32x4 ns = *reinterpret_cast<const f32x4 *>(&sm.frk[16 * J + 4 * q4]);
         return g * ns * nr;
     };
-    // off-diagonal block (I > J) of L, as L_IJ^T
-    auto put_L = [&](int I, int J, f32x4 g) {
-        const float br = sm.fb[16 * I + l15], betar = sm.fbeta[16 * I + l15];
+    // block (I, J) of the chunk: I == J: L_II = strict_lower(diag(beta) A_II)
+    // in fp32, transposed, for the substitution; I > J: -A_IJ as a tile.
+    // A[r][s] = e^{b_r - b_s} k_r.k_s (s < r, so the factor is at most 1)
+    auto put_A = [&](int I, int J, int tile, f32x4 g) {
+        const float br = sm.fb[16 * I + l15];
         const f32x4 bs = *reinterpret_cast<const f32x4 *>(&sm.fb[16 * J + 4 * q4]);
         g = knorm(I, J, g);
-        f32x4 lv;
+        f32x4 av;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) lv[e] = betar * ex(br - bs[e]) * g[e];
-        tile_st(sm.LT + ltri(I, J) * 256, lane, lv);
+        for (int e = 0; e < 4; ++e) av[e] = ex(br - bs[e]) * g[e];
+        if (I == J) {
+            const float betar = sm.fbeta[16 * I + l15];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int sl = 4 * q4 + e;
+                sm.MT[I][16 * sl + l15] = sl < l15 ? betar * av[e] : 0.f;
+            }
+        } else {
+            tile_st(sm.TT + tile * 256, lane, -av);
+        }
     };
 
-    // ---- wave w: diagonal block w of T by the series, and the
-    //      off-diagonal blocks of L  w0: (1,0), (3,0)  w1: (2,1), (3,1)
-    //      w2: (2,0)  w3: (3,2)
+    // ---- wave w: blocks (w, w) and, below the diagonal, w0: (1,0), (3,0)
+    //      w1: (2,1), (3,1)  w2: (2,0)  w3: (3,2)
     {
         const int b = w;
         bf16x8 kd[KD];
         frags(b, kd);
-        const f32x4 g = knorm(b, b, gram(kd, kd));
-        // M = L_bb as acc(M^T) and acc(M): the Gram block is symmetric, so
-        // both come from the one product
-        const float br = sm.fb[16 * b + l15], betar = sm.fbeta[16 * b + l15];
-        const f32x4 bs = *reinterpret_cast<const f32x4 *>(&sm.fb[16 * b + 4 * q4]);
-        const f32x4 betas = *reinterpret_cast<const f32x4 *>(&sm.fbeta[16 * b + 4 * q4]);
-        f32x4 MT, Mn, I4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int sl = 4 * q4 + e;
-            const float d = br - bs[e];
-            const float f = ex(sl <= l15 ? d : -d);
-            MT[e] = sl < l15 ? betar * f * g[e] : 0.f;
-            Mn[e] = sl > l15 ? betas[e] * f * g[e] : 0.f;
-            I4[e] = sl == l15 ? 1.f : 0.f;
-        }
-        // Y = (I + M)^{-1} = (I - M)(I + M^2)(I + M^4)(I + M^8) and Y^T; an
-        // MFMA with A operand acc(X^T) and B operand acc(Y) yields acc(X Y)
-        const f32x4 IMn = I4 - Mn, IMT = I4 - MT;
-        const f32x4 M2 = mfma16z(cvt4(MT), cvt4(Mn));
-        const f32x4 M2T = mfma16z(cvt4(Mn), cvt4(MT));
-        const f32x4 Z1 = mfma16(cvt4(M2T), cvt4(IMn), IMn);
-        const f32x4 Z1T = mfma16(cvt4(M2), cvt4(IMT), IMT);
-        const f32x4 M4 = mfma16z(cvt4(M2T), cvt4(M2));
-        const f32x4 M4T = mfma16z(cvt4(M2), cvt4(M2T));
-        const f32x4 Z2 = mfma16(cvt4(M4T), cvt4(Z1), Z1);
-        const f32x4 Z2T = mfma16(cvt4(M4), cvt4(Z1T), Z1T);
-        const f32x4 M8 = mfma16z(cvt4(M4T), cvt4(M4));
-        const f32x4 M8T = mfma16z(cvt4(M4), cvt4(M4T));
-        const f32x4 Y = mfma16(cvt4(M8T), cvt4(Z2), Z2);
-        const f32x4 YT = mfma16(cvt4(M8), cvt4(Z2T), Z2T);
-        tile_st(sm.YD[b][0], lane, Y);
-        tile_st(sm.YD[b][1], lane, YT);
-        tile_st(sm.TT + tri(b, b) * 256, lane, YT * betas);   // T_bb^T = diag(beta) Y_bb^T
-
+        put_A(b, b, 0, gram(kd, kd));
+        // tiles: (1,0) 4, (3,2) 5, (2,0) 6, (2,1) 7, (3,0) 8, (3,1) 9
         const int J = b < 2 ? b : (b == 2 ? 0 : 2);
         const int I0 = b < 2 ? b + 1 : (b == 2 ? 2 : 3);
+        const int t0 = b == 0 ? 4 : (b == 1 ? 7 : (b == 2 ? 6 : 5));
         bf16x8 kj[KD], ki[KD];
         frags(J, kj);
         frags(I0, ki);
-        put_L(I0, J, gram(kj, ki));
+        put_A(I0, J, t0, gram(kj, ki));
         if (b < 2) {
             frags(3, ki);
-            put_L(3, J, gram(kj, ki));
+            put_A(3, J, b == 0 ? 8 : 9, gram(kj, ki));
         }
     }
     __syncthreads();
 
-    // ---- T off the diagonal: waves 0, 1, 2 take block columns 0, 1, 2
-    if (w < 3) {
-        auto LTb = [&](int i, int j) { return tile_ld(sm.LT + ltri(i, j) * 256, lane); };
-        auto YB = [&](int j) { return tile_ld(sm.YD[j][0], lane); };   // B operand Y_jj
-        auto fin = [&](int i, f32x4 v) -> f32x4 {                      // -Y_ii v
-            return -mfma16z(tile_ld(sm.YD[i][1], lane), cvt4(v));
-        };
-        // T_ij = Y_ij diag(beta_j), stored as T_ij^T in accumulator order:
-        // element (4 q4 + e, l15) of Y_ij goes to lane 16 (l15 >> 2) + 4 q4 + e
-        const float bj = sm.fbeta[16 * w + l15];
-        auto putT = [&](int i, int j, f32x4 y) {
-            bf16 *t = sm.TT + tri(i, j) * 256;
-            const int dl = 16 * (l15 >> 2) + 4 * q4;
+    // ---- N_bb = (I + L_bb)^{-1} in fp32 by forward substitution, lane
+    //      16 b + c of wave 0 taking column c of block b: once entry m of the
+    //      column is final, column m of L_bb updates the entries below it
+    if (w == 0) {
+        const int b = lane >> 4, c = lane & 15;
+        const float *Lt = sm.MT[b];
+        float n[16];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) t[4 * (dl + e) + (l15 & 3)] = (bf16)(y[e] * bj);
+        for (int r = 0; r < 16; ++r) n[r] = r == c ? 1.f : 0.f;
+        auto lcol = [&](int m, f32x4 (&R)[4]) {   // column m: four reads, one address per block
+#pragma unroll
+            for (int v = 0; v < 4; ++v) R[v] = *reinterpret_cast<const f32x4 *>(&Lt[16 * m + 4 * v]);
         };
-        if (w == 0) {
-            const f32x4 y10 = fin(1, mfma16z(LTb(1, 0), YB(0)));
-            const f32x4 y20 = fin(2, mfma16(LTb(2, 1), cvt4(y10), mfma16z(LTb(2, 0), YB(0))));
-            const f32x4 y30 = fin(3, mfma16(LTb(3, 2), cvt4(y20),
-                                            mfma16(LTb(3, 1), cvt4(y10), mfma16z(LTb(3, 0), YB(0)))));
-            putT(1, 0, y10);
-            putT(2, 0, y20);
-            putT(3, 0, y30);
-        } else if (w == 1) {
-            const f32x4 y21 = fin(2, mfma16z(LTb(2, 1), YB(1)));
-            const f32x4 y31 = fin(3, mfma16(LTb(3, 2), cvt4(y21), mfma16z(LTb(3, 1), YB(1))));
-            putT(2, 1, y21);
-            putT(3, 1, y31);
-        } else {
-            putT(3, 2, fin(3, mfma16z(LTb(3, 2), YB(2))));
+        f32x4 Lc[4], Ln[4];
+        lcol(0, Lc);
+#pragma unroll
+        for (int m = 0; m < 15; ++m) {
+            if (m + 1 < 15) lcol(m + 1, Ln);
+#pragma unroll
+            for (int r = m + 1; r < 16; ++r) n[r] -= Lc[r >> 2][r & 3] * n[m];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) Lc[v] = Ln[v];
         }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sm.Nd[b][16 * r + c] = n[r];
+    }
+    __syncthreads();
+    // ---- T_bb = N_bb diag(beta_b) as tiles, rounded to bf16 once
+    {
+        const int b = w;
+        const f32x4 nv = *reinterpret_cast<const f32x4 *>(&sm.Nd[b][16 * l15 + 4 * q4]);
+        const f32x4 bv = *reinterpret_cast<const f32x4 *>(&sm.fbeta[16 * b + 4 * q4]);
+        tile_st(sm.TT + b * 256, lane, nv * bv);
     }
     __syncthreads();
 
-    // ---- the chunk's record in the workspace.  T as MFMA A operands of
-    //      U = T X: for row block sb and token blocks (2kk, 2kk+1), lane l
-    //      reads its values of the two 16x16 blocks (sb, 2kk), (sb, 2kk+1) as
-    //      one 16-byte piece.  The four pairs (1,0), (2,0), (3,0), (3,1) are
-    //      stored whole (1 KB each); the pairs (0,0) and (2,1), whose second
-    //      block lies above the diagonal, as their first block only (512
-    //      bytes).  Then two rows of 64 fp32 values from b_r, the in-chunk
+    // ---- the chunk's record in the workspace: the pairs (-A_20 | -A_21) and
+    //      (-A_30 | -A_31), a 16-byte piece per lane (the A operands of a
+    //      16x16x32 MFMA over the tokens of blocks 0 and 1), then T_00 ..
+    //      T_33, -A_10 and -A_32, 8 bytes per lane (16x16x16 MFMA A
+    //      operands).  Then two rows of 64 fp32 values from b_r, the in-chunk
     //      inclusive prefix sums of the gate logs: b_r log2(e) itself (the
     //      recurrence forms e^{b_r} and e^{b_r - b_s}, s <= r, from it, so
     //      no factor ever exceeds 1) and e^{b_C - b_r}.
     {
         const size_t rec = (size_t)(ci * a.H + h) * REC;
         char *dst = static_cast<char *>(a.tiles) + rec;
-        for (int i = tid; i < 4 * 64; i += 256) {
-            const int pr = i >> 6, l = i & 63;          // pairs (1,0) (2,0) (3,0) (3,1)
-            const int sb = pr == 0 ? 1 : (pr == 1 ? 2 : 3);
-            const int kk = pr == 3 ? 1 : 0;
-            reinterpret_cast<bf16x8 *>(dst)[i] = cat8(tile_ld(sm.TT + tri(sb, 2 * kk) * 256, l),
-                                                      tile_ld(sm.TT + tri(sb, 2 * kk + 1) * 256, l));
+        if (tid < 2 * 64) {
+            const int pr = tid >> 6, l = tid & 63;
+            reinterpret_cast<bf16x8 *>(dst)[tid] = cat8(tile_ld(sm.TT + (6 + 2 * pr) * 256, l),
+                                                        tile_ld(sm.TT + (7 + 2 * pr) * 256, l));
         }
-        if (tid < 2 * 64) {                             // first blocks of (0,0), (2,1)
-            const int l = tid & 63;
-            reinterpret_cast<bf16x4 *>(dst + 4096)[tid] = tile_ld(sm.TT + (tid < 64 ? tri(0, 0) : tri(2, 2)) * 256, l);
-        } else if (tid < 2 * 64 + C) {
-            const int r = tid - 2 * 64;
+        for (int i = tid; i < 6 * 64; i += 256)
+            reinterpret_cast<bf16x4 *>(dst + 2048)[i] = tile_ld(sm.TT + (i >> 6) * 256, i & 63);
+        if (tid >= 128 && tid < 128 + C) {
+            const int r = tid - 128;
             float *f = reinterpret_cast<float *>(dst + 5120);
             const float b = sm.fb[r];
             f[r] = b * kLog2e;
@@ -340,14 +320,14 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a) {
 // ===========================================================================
 // the chunk's workspace record as the prep kernel writes it
 template <bool RAW> struct TRecT {
-    bf16x8 pairs[4][64];            // T operand pairs (1,0), (2,0), (3,0), (3,1)
-    bf16x4 halves[2][64];           // first blocks of the pairs (0,0), (2,1)
+    bf16x8 pairs[2][64];            // (-A_20 | -A_21), (-A_30 | -A_31)
+    bf16x4 halves[6][64];           // T_00, T_11, T_22, T_33, -A_10, -A_32
     float lb[C];                    // b_r log2(e)
     float hs[C];                    // e^{b_C - b_r}
 };
 template <> struct TRecT<true> {
-    bf16x8 pairs[4][64];
-    bf16x4 halves[2][64];
+    bf16x8 pairs[2][64];
+    bf16x4 halves[6][64];
     float lb[C];                    // b_r log2(e)
     float hs[C];                    // e^{b_C - b_r} / |k_r|
     float ek[C];                    // e^{b_r} / |k_r|
@@ -473,12 +453,14 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
         };
         // operands of a chunk, read an iteration ahead of their use: k row
         // fragments, K^T, the v slice, T and the decay factors
-        bf16x8 Kf[4][KD], KT[KS][2], Ta[4][2];
+        bf16x8 Kf[4][KD], KT[KS][2], Ap[2];
+        bf16x4 Td[4], A10, A32;
         bf16x4 vv[4];
         f32x4 eb[4], hs[4];
         float gC = 0.f;
         // operands of the chunk in slot m3 read while the previous chunk's
-        // state update runs: k row fragments, e^{b_C - b}, T and e^{b_C}
+        // state update runs: k row fragments, e^{b_C - b}, the diagonal
+        // blocks of T and the blocks of -A below them, and e^{b_C}
         auto prefetch_rows = [&](int m3) {
             const bf16 *Kc = sm.K[m3];
             const typename Sm::TRec &R = sm.TR[m3];
@@ -487,10 +469,12 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
 #pragma unroll
                 for (int kk = 0; kk < KD; ++kk) Kf[rb][kk] = frag_rows(Kc, PD, 16 * rb, 32 * kk, lane);
                 hs[rb] = *reinterpret_cast<const f32x4 *>(&R.hs[16 * rb + 4 * q4]);
-                Ta[rb][0] = rb == 0 ? cat8(R.halves[0][lane], bf16x4{}) : R.pairs[rb - 1][lane];
-                Ta[rb][1] = rb == 2 ? cat8(R.halves[1][lane], bf16x4{})
-                          : (rb == 3 ? R.pairs[3][lane] : bf16x8{});
+                Td[rb] = R.halves[rb][lane];
             }
+            A10 = R.halves[4][lane];
+            A32 = R.halves[5][lane];
+            Ap[0] = R.pairs[0][lane];
+            Ap[1] = R.pairs[1][lane];
             gC = __builtin_amdgcn_exp2f(R.lb[C - 1]);
         };
         // the rest, after the update: the v slice, e^b, and K^T of the chunk
@@ -560,16 +544,17 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) X[rb][e] = (float)vv[rb][e] - eb[rb][e] * xk[rb][e];
             }
-            // U = T X, S^T <- e^{b_C} S^T + K^T diag(e^{b_C - b}) U
+            // (I + L) U = diag(beta) X by block forward substitution,
+            // U_I = T_II (X_I - sum_{J<I} A_IJ U_J), then
+            // S^T <- e^{b_C} S^T + K^T diag(e^{b_C - b}) U
             bf16x8 Ub[2];
             {
-                const bf16x8 Bx[2] = {acc_pair(X[0], X[1]), acc_pair(X[2], X[3])};
                 f32x4 U[4];
-#pragma unroll
-                for (int sb = 0; sb < 4; ++sb) {
-                    U[sb] = mfma32z(Ta[sb][0], Bx[0]);
-                    if (sb >= 2) U[sb] = mfma32(Ta[sb][1], Bx[1], U[sb]);
-                }
+                U[0] = mfma16z(Td[0], cvt4(X[0]));
+                U[1] = mfma16z(Td[1], cvt4(mfma16(A10, cvt4(U[0]), X[1])));
+                const bf16x8 U01 = acc_pair(U[0], U[1]);
+                U[2] = mfma16z(Td[2], cvt4(mfma32(Ap[0], U01, X[2])));
+                U[3] = mfma16z(Td[3], cvt4(mfma16(A32, cvt4(U[2]), mfma32(Ap[1], U01, X[3]))));
                 Ub[0] = acc_pair(U[0], U[1]);
                 Ub[1] = acc_pair(U[2], U[3]);
                 f32x4 Uh[4];
@@ -711,7 +696,7 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
             for (int ob = 0; ob < 2; ++ob)
 #pragma unroll
                 for (int k2 = 0; k2 < NP2; ++k2) Au[ob][k2] = sm.UB[up][ob][k2][lane];
-            const rsrc_t ro = make_rsrc(og + (size_t)chunk_tok(c - 1) * tokstride, extent(c - 1, BV * 2));
+            const rsrc_t ro = make_rsrc(og + (size_t)chunk_tok(c - 1) * tokstride, a.o ? extent(c - 1, BV * 2) : 0u);
             const unsigned voff = l15 * rowb + 8 * q4;
 #pragma unroll
             for (int ob = 0; ob < 2; ++ob) {

@@ -118,7 +118,7 @@ struct PrefillArgs {
     const float *g;               // [tokens, H] or [tokens, H, D]
     const float *beta;            // [tokens, H]
     const float *h0;              // [N, H, D, D] or nullptr
-    void *o;                      // [tokens, H, D] dt
+    void *o;                      // [tokens, H, D] dt; bf16 chunked forms: nullptr = not stored
     float *ht;                    // [N, H, D, D] or nullptr
     const int32_t *cu_seqlens;    // [N+1] or nullptr (fixed length)
     const int32_t *order;         // schedule [N] or nullptr (identity)

@@ -373,9 +373,10 @@ gdr_status gdr_decode_tokens_fused(enum gdr_dtype dt, enum gdr_gate gk, int B, i
  *   dh0          [B, H, Dv, Dk] fp32 (written) or NULL
  *   workspace    device buffer of gdr_backward_workspace_bytes(gk, B, T, H,
  *                Dk, Dv) bytes (the state entering and the state gradient
- *                leaving every chunk of 64 tokens in fp32, the forward's own
- *                outputs and workspace, and per chunk the bf16 matrices of
- *                the state gradient's recurrence), 16-byte aligned
+ *                leaving every chunk of 64 tokens in fp32, the forward's
+ *                workspace -- the forward stores no outputs -- and per chunk
+ *                the bf16 matrices of the state gradient's recurrence),
+ *                16-byte aligned
  *
  * Three stages: the chunked forward storing the state that enters every
  * chunk; the state gradient's recurrence over chunks in reverse (its

@@ -258,19 +258,18 @@ def test_fused_rejects(lib):
 
 def test_backward_rejects(lib):
     err = lambda: lib.gdr_last_error().decode()  # noqa: E731
-    # chunk states and state gradients, the forward's outputs (bf16, rounded
-    # to 256 bytes) and its workspace (for the scalar gate: 5632-byte records)
-    # and per (b, h, chunk) a record of Qt, Kb, W (bf16 64 x 128), P (bf16
-    # 64 x 64) and e^{b_C} (fp32 128)
+    # chunk states and state gradients, the forward's workspace (for the
+    # scalar gate: 5632-byte records; the forward stores no outputs) and per
+    # (b, h, chunk) a record of Qt, Kb, W (bf16 64 x 128), P (bf16 64 x 64)
+    # and e^{b_C} (fp32 128)
     st = 2 * 3 * 2 * 128 * 128 * 4
-    o = (2 * 100 * 3 * 128 * 2 + 255) // 256 * 256
     rec = 2 * 3 * 2 * (3 * 64 * 128 * 2 + 64 * 64 * 2 + 128 * 4)
     # the forward's workspace: schedule, chunk offsets, one int32 per (sequence, head)
     # (rounded to 256 bytes), the records
     fwd_gdn = (512 + 256 + (200 // 64 + 2) * 3 * 5632 + 255) // 256 * 256
     # channel gate: the forward's workspace holds one int32 per (sequence, head) more
-    assert lib.gdr_backward_workspace_bytes(1, 2, 100, 3, 128, 128) == 2 * st + o + 512 + 256 + rec
-    assert lib.gdr_backward_workspace_bytes(0, 2, 100, 3, 128, 128) == 2 * st + o + fwd_gdn + rec
+    assert lib.gdr_backward_workspace_bytes(1, 2, 100, 3, 128, 128) == 2 * st + 512 + 256 + rec
+    assert lib.gdr_backward_workspace_bytes(0, 2, 100, 3, 128, 128) == 2 * st + fwd_gdn + rec
     assert lib.gdr_backward_workspace_bytes(1, 2, 0, 3, 128, 128) == 0
 
     def call(dt=1, ws_bytes=1 << 30, T=100, **kw):
@@ -291,12 +290,11 @@ def test_backward_varlen_rejects(lib):
     # sequences, 100 tokens, H = 3)
     chunks = 100 // 64 + 2
     st = chunks * 3 * 128 * 128 * 4
-    o = (100 * 3 * 128 * 2 + 255) // 256 * 256
     rec = chunks * 3 * (3 * 64 * 128 * 2 + 64 * 64 * 2 + 128 * 4)
     fwd_gdn = (512 + 256 + chunks * 3 * 5632 + 255) // 256 * 256
-    assert lib.gdr_backward_varlen_workspace_bytes(1, 2, 100, 3, 128, 128) == 2 * st + o + 512 + 256 + rec
+    assert lib.gdr_backward_varlen_workspace_bytes(1, 2, 100, 3, 128, 128) == 2 * st + 512 + 256 + rec
     assert lib.gdr_backward_varlen_workspace_bytes(0, 2, 100, 3, 128, 128) == \
-        2 * st + o + fwd_gdn + rec
+        2 * st + fwd_gdn + rec
     assert lib.gdr_backward_varlen_workspace_bytes(1, 2, 0, 3, 128, 128) == 0
 
     def call(dt=1, N=2, T_total=100, ws_bytes=1 << 30, cu=FAKE, host=None, **kw):

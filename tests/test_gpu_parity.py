@@ -272,6 +272,32 @@ def test_prefill_decay_at_the_documented_limit(gate):
     announce("  rel-fro o=%.2e ht=%.2e" % (eo, eh))
 
 
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
+@pytest.mark.parametrize("spread", [0.0, 0.03, 0.3])
+def test_prefill_unit_beta_collinear_keys(gate, spread):
+    """The in-chunk inverse (I + diag(beta) A)^{-1} at its least favourable
+    inputs: beta = 1, no decay (a = 1) and unit keys that all lie within
+    `spread` of one direction, so the strictly lower part of diag(beta) A
+    has entries up to 1 (exactly 1 for spread 0, where the inverse is
+    bidiagonal and each token overwrites the previous one's value).  The
+    kernels form the inverse from bf16 operands; the outputs must still meet
+    the bf16 bar against the fp64 oracle, row by row."""
+    announce("unit beta, collinear keys %s spread=%g" % (gate, spread))
+    B, T, H, D = 1, 200, 2, 128
+    x = synthetic.prefill_inputs(B, T, H, D, torch.bfloat16, gate, seed=27, device=DEV)
+    gen = torch.Generator().manual_seed(28)
+    u = torch.randn(H, D, generator=gen, dtype=torch.float64)
+    k = u[None, None] + spread * torch.randn(B, T, H, D, generator=gen, dtype=torch.float64)
+    k = k / k.norm(dim=-1, keepdim=True)
+    x["k"] = k.to(torch.bfloat16).to(DEV)
+    x["beta"] = torch.ones_like(x["beta"])
+    x["g"] = torch.zeros_like(x["g"])
+    o, ht = run_prefill(x)
+    assert bool(torch.isfinite(o.float()).all()) and bool(torch.isfinite(ht).all())
+    eo, eh = check_prefill(x, o, ht, torch.bfloat16)
+    announce("  rel-fro o=%.2e ht=%.2e" % (eo, eh))
+
+
 def test_prefill_guard_bands_scalar_gate_workspace():
     """Scalar gate (prep and recurrence kernels): canaries around o, ht and
     the exactly sized workspace stay untouched."""
