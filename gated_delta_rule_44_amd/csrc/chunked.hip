@@ -49,7 +49,7 @@
 //   1  prefix sums of the gate logs (two chunks ahead) and the gated
 //      operands (one chunk ahead, in registers)
 //   2  A (for L = diag(beta) A) and P by 16x16 blocks on MFMA; the four
-//      diagonal blocks of (I + L)^{-1} by forward substitution in fp32
+//      diagonal blocks of (I + L)^{-1} by doubling on 16x16x16 MFMAs
 //   3  wave 0: the off-diagonal blocks of T = (I + L)^{-1} diag(beta) by
 //      16x16x16 MFMA block substitution; waves 4-7: X = V - Kt S0^T and
 //      Qt S0^T on MFMA
