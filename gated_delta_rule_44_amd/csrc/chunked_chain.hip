@@ -40,9 +40,11 @@
 // of chunk c+2 into LDS while chunk c runs, their global loads issued two
 // iterations before the LDS stores.
 // One barrier per chunk; between barriers c-1 and c (iteration c):
-//   chain:   X, U and the state update of chunk c from registers, then
-//            publish U (by chunk parity) and the new S^T, and read the LDS
-//            operands of chunk c+1 into registers
+//   chain:   X, U and the state update of chunk c from registers, with
+//            the LDS operands of chunk c+1 read into registers while the
+//            update's MFMAs run (each K^T block right after its last use),
+//            then publish U (by chunk parity) and the new S^T (kept as the
+//            next X's operand), and read the v slice and e^b of chunk c+1
 //   output:  O of chunk c-1 (U of c-1 was published in iteration c-1), then
 //            diag(e^b) Q S^T and P of chunk c (S^T entering c likewise), and
 //            the global loads of the q rows of c+2
@@ -92,13 +94,21 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a) {
     constexpr int CG = D / 8;           // 16-byte pieces per row
     constexpr int NPC = C * CG / 256;
     static_assert(NPC >= 1 && (C * CG) % 256 == 0, "staging layout");
-    static_assert(kTileBytes == 5 * 1024 + 2 * C * 4, "tile record: T operands, two factor rows");
+    static_assert(kTileBytes == 5 * 1024 + 3 * C * 4, "tile record: T operands, three factor rows");
     constexpr size_t REC = RAW ? kTileBytesRaw : kTileBytes;
     __shared__ Sm sm;
 
-    // ---- which chunk: ci counts chunks over all sequences
-    const int h = blockIdx.x % a.H;
-    const long long ci = blockIdx.x / a.H;
+    // ---- which chunk: ci counts chunks over all sequences.  Workgroups are
+    //      handed to the eight XCDs in turn; each XCD takes a contiguous run
+    //      of (chunk, head) units, so the heads of one chunk share an XCD and
+    //      the lines of g and beta they read ([token, head] rows) are
+    //      fetched into one L2 only
+    const long long units = a.max_chunks * a.H;
+    const long long per_xcd = (units + 7) / 8;
+    const long long unit = (long long)(blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+    if (unit >= units) return;
+    const int h = (int)(unit % a.H);
+    const long long ci = unit / a.H;
     long long t0, t1, c;
     if (a.cu_seqlens) {
         if (ci >= a.chunk_base[a.N]) return;
@@ -310,6 +320,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a) {
                 f[3 * C + r] = nk;
             } else {
                 f[C + r] = ex(sm.fb[C - 1] - b);
+                f[2 * C + r] = ex(b);
             }
         }
     }
@@ -324,6 +335,7 @@ template <bool RAW> struct TRecT {
     bf16x4 halves[6][64];           // T_00, T_11, T_22, T_33, -A_10, -A_32
     float lb[C];                    // b_r log2(e)
     float hs[C];                    // e^{b_C - b_r}
+    float ek[C];                    // e^{b_r}
 };
 template <> struct TRecT<true> {
     bf16x8 pairs[2][64];
@@ -447,12 +459,19 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
         for (int jk = 0; jk < KS; ++jk)
             St[jk] = h0p ? *reinterpret_cast<const f32x4 *>(h0p + srow0 + srow(jk, 0))
                          : f32x4{0.f, 0.f, 0.f, 0.f};
-        auto publish_state = [&](int spar) {   // S^T entering a chunk of parity spar
+        // S^T entering the next chunk as bf16 operands: kept for its X and
+        // published for the output waves (by chunk parity spar)
+        bf16x8 Bs[KD];
+        auto publish_state = [&](int spar) {
 #pragma unroll
-            for (int kk = 0; kk < KD; ++kk) sm.SB[spar][ib][kk][lane] = acc_pair(St[2 * kk], St[2 * kk + 1]);
+            for (int kk = 0; kk < KD; ++kk) {
+                Bs[kk] = acc_pair(St[2 * kk], St[2 * kk + 1]);
+                sm.SB[spar][ib][kk][lane] = Bs[kk];
+            }
         };
         // operands of a chunk, read an iteration ahead of their use: k row
-        // fragments, K^T, the v slice, T and the decay factors
+        // fragments, K^T, the v slice, T and the decay factors (e^b from the
+        // record, e^{b_C} formed from b_C)
         bf16x8 Kf[4][KD], KT[KS][2], Ap[2];
         bf16x4 Td[4], A10, A32;
         bf16x4 vv[4];
@@ -460,7 +479,7 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
         float gC = 0.f;
         // operands of the chunk in slot m3 read while the previous chunk's
         // state update runs: k row fragments, e^{b_C - b}, the diagonal
-        // blocks of T and the blocks of -A below them, and e^{b_C}
+        // blocks of T and the blocks of -A below them
         auto prefetch_rows = [&](int m3) {
             const bf16 *Kc = sm.K[m3];
             const typename Sm::TRec &R = sm.TR[m3];
@@ -475,39 +494,38 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
             A32 = R.halves[5][lane];
             Ap[0] = R.pairs[0][lane];
             Ap[1] = R.pairs[1][lane];
-            gC = __builtin_amdgcn_exp2f(R.lb[C - 1]);
         };
-        // the rest, after the update: the v slice, e^b, and K^T of the chunk
-        // in slot m3 by transpose loads: lane j of each
-        // 16-lane group addresses k columns 32 (jk >> 1) + 8 (j & 3) +
-        // 4 (jk & 1) .. +3, so output lane i receives k = srow(jk, .) for
-        // row i of the block
-        auto prefetch_kt = [&](int m3) {
-            const bf16 *Kc = sm.K[m3];
+        // the v slice, e^b (RAW: e^b / |k|) and e^{b_C} of the chunk in slot m3
+        auto prefetch_veb = [&](int m3) {
             const bf16 *Vc = sm.V[m3];
             const typename Sm::TRec &R = sm.TR[m3];
+            const float lbC = R.lb[C - 1];
 #pragma unroll
             for (int rb = 0; rb < 4; ++rb) {
                 vv[rb] = frag_col4(Vc, PV, 16 * rb, 16 * ib, lane);
-                if constexpr (RAW) {
-                    eb[rb] = *reinterpret_cast<const f32x4 *>(&R.ek[16 * rb + 4 * q4]);
-                } else {
-                    const f32x4 lb = *reinterpret_cast<const f32x4 *>(&R.lb[16 * rb + 4 * q4]);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) eb[rb][e] = __builtin_amdgcn_exp2f(lb[e]);
-                }
+                eb[rb] = *reinterpret_cast<const f32x4 *>(&R.ek[16 * rb + 4 * q4]);
             }
+            gC = __builtin_amdgcn_exp2f(lbC);
+        };
+        // K^T row block jk of the chunk in slot m3, by transpose loads: lane
+        // j of each 16-lane group addresses k columns 32 (jk >> 1) + 8 (j & 3)
+        // + 4 (jk & 1) .. +3, so output lane i receives k = srow(jk, .) for
+        // row i of the block
+        auto kt_load = [&](int m3, int jk) {
+            const bf16 *Kc = sm.K[m3];
+            const int pc = 32 * (jk >> 1) + 8 * (l15 & 3) + 4 * (jk & 1);
 #pragma unroll
-            for (int jk = 0; jk < KS; ++jk) {
-                const int pc = 32 * (jk >> 1) + 8 * (l15 & 3) + 4 * (jk & 1);
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    const bf16 *p = Kc + (32 * kk + 4 * q4 + (l15 >> 2)) * PD + pc;
-                    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p));
-                    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p + 16 * PD));
-                    KT[jk][kk] = cat8(__builtin_bit_cast(bf16x4, lo), __builtin_bit_cast(bf16x4, hi));
-                }
+            for (int kk = 0; kk < 2; ++kk) {
+                const bf16 *p = Kc + (32 * kk + 4 * q4 + (l15 >> 2)) * PD + pc;
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p));
+                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p + 16 * PD));
+                KT[jk][kk] = cat8(__builtin_bit_cast(bf16x4, lo), __builtin_bit_cast(bf16x4, hi));
             }
+        };
+        auto prefetch_kt = [&](int m3) {
+            prefetch_veb(m3);
+#pragma unroll
+            for (int jk = 0; jk < KS; ++jk) kt_load(m3, jk);
         };
         publish_state(0);
         __syncthreads();                      // chunks 0 and 1 staged
@@ -529,9 +547,6 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
             //      update, all from registers
             f32x4 X[4];
             {
-                bf16x8 Bs[KD];
-#pragma unroll
-                for (int kk = 0; kk < KD; ++kk) Bs[kk] = acc_pair(St[2 * kk], St[2 * kk + 1]);
                 f32x4 xk[4];
 #pragma unroll
                 for (int rb = 0; rb < 4; ++rb) {
@@ -571,13 +586,14 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
                     sv = mfma32(KT[jk][0], Bh[0], sv);
                     sv = mfma32(KT[jk][1], Bh[1], sv);
                     St[jk] = sv;
+                    kt_load(n3, jk);   // the next chunk's K^T block, in flight during the rest
                 }
             }
             // publish U and S^T; the rest of the next chunk's operands
             sm.UB[par][ib][0][lane] = Ub[0];
             sm.UB[par][ib][1][lane] = Ub[1];
             publish_state(par ^ 1);
-            prefetch_kt(n3);
+            prefetch_veb(n3);
             __syncthreads();
             m3 = n3;
         }
@@ -696,6 +712,7 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
             for (int ob = 0; ob < 2; ++ob)
 #pragma unroll
                 for (int k2 = 0; k2 < NP2; ++k2) Au[ob][k2] = sm.UB[up][ob][k2][lane];
+            __builtin_amdgcn_sched_barrier(0);
             const rsrc_t ro = make_rsrc(og + (size_t)chunk_tok(c - 1) * tokstride, a.o ? extent(c - 1, BV * 2) : 0u);
             const unsigned voff = l15 * rowb + 8 * q4;
 #pragma unroll
@@ -724,6 +741,7 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
                 if constexpr (RAW) rkJ[J] = *reinterpret_cast<const f32x4 *>(&sm.TR[m3].rk[16 * J + 4 * q4]);
             }
             const float lbr = sm.TR[m3].lb[16 * RB + l15];
+            __builtin_amdgcn_sched_barrier(0);   // every LDS read of the step in flight at once
             float ebr = __builtin_amdgcn_exp2f(lbr), iq = 1.f;
             if constexpr (RAW) {
                 // 1/|q_r| for the lane's row: its 8 KD values, then the four
@@ -838,9 +856,9 @@ hipError_t launch_prefill_chain(int D, const PrefillArgs &a, hipStream_t s) {
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    const long long prep_blocks = a.max_chunks * a.H;
-    if (prep_blocks > 0) {
-        dim3 grid((unsigned)prep_blocks), block(256);
+    const long long prep_units = a.max_chunks * a.H;
+    if (prep_units > 0) {
+        dim3 grid((unsigned)((prep_units + 7) / 8 * 8)), block(256);
         if (a.xg) {
             if (D == 128) hipLaunchKernelGGL((prep_kernel<128, true>), grid, block, 0, s, a);
             else          hipLaunchKernelGGL((prep_kernel<64, true>), grid, block, 0, s, a);

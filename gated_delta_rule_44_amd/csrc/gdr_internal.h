@@ -173,13 +173,13 @@ __device__ inline float *seq_ht(const PrefillArgs &a, int n, int h) {
 }
 
 // Per (chunk, head) record of the scalar-gate chunked prefill's workspace:
-// T as MFMA operands of its 16x16 blocks (bf16, 5 KiB), then two fp32 rows
+// T as MFMA operands of its 16x16 blocks (bf16, 5 KiB), then three fp32 rows
 // over the chunk's 64 tokens: the gate prefix sums b_r log2(e) and the
-// decay factors e^{b_C - b_r}.
-constexpr size_t kTileBytes = 5 * 1024 + 2 * 64 * 4;
-// With fused preprocessing the record carries the key norms folded into
-// two more factor rows (6 KiB).
-constexpr size_t kTileBytesRaw = kTileBytes + 2 * 64 * 4;
+// decay factors e^{b_C - b_r} and e^{b_r}.
+constexpr size_t kTileBytes = 5 * 1024 + 3 * 64 * 4;
+// With fused preprocessing the record carries the key norms as one more
+// row and folds them into the last two (6 KiB).
+constexpr size_t kTileBytesRaw = kTileBytes + 64 * 4;
 
 // Backward of the chunked prefill (bf16 q/k/v/do), a fixed-length batch
 // (cu_seqlens == nullptr: B sequences of T tokens, nc = ceil(T / 64) chunks

@@ -73,7 +73,7 @@ enum gdr_mixer { GDR_FA = 0, GDR_SWA = 1, GDR_GDN = 2, GDR_KDA = 3 };
  * head) (rounded up to 256 bytes: the pairs that the second pass redoes,
  * see gdr_prefill_chunked); for bf16 with the scalar gate, a record of
  * every chunk and head (the chunk-local inverse T, the gate's prefix sums
- * and the chunk's decay factors, 5632 bytes) for tokens / 64 + N chunks, an
+ * and the chunk's decay factors, 5888 bytes) for tokens / 64 + N chunks, an
  * upper bound.  Returns 0 for N <= 0, tokens < 0 or H <= 0.  A buffer of
  * this size serves either call with these sizes.
  */

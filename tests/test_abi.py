@@ -62,10 +62,10 @@ def test_version_and_workspace(lib):
     assert gdr.workspace_bytes(bf, True, 64, 100, 4) == 256 + 512 + 1024
     assert gdr.workspace_bytes(bf, True, 2, 2 * 8192, 32) == 256 + 256 + 256
     assert gdr.workspace_bytes(f32, False, 2, 100, 0) == 0
-    # bf16, scalar gate: + 5632 bytes (T and decay factors) per (chunk, head), for
+    # bf16, scalar gate: + 5888 bytes (T and decay factors) per (chunk, head), for
     # tokens // 64 + N chunks
-    assert gdr.workspace_bytes(bf, False, 1, 64, 1) == 512 + 2 * 5632
-    assert gdr.workspace_bytes(bf, False, 4, 4 * 4096, 16) == 512 + (256 + 4) * 16 * 5632
+    assert gdr.workspace_bytes(bf, False, 1, 64, 1) == 512 + 2 * 5888
+    assert gdr.workspace_bytes(bf, False, 4, 4 * 4096, 16) == 512 + (256 + 4) * 16 * 5888
 
 
 F = ctypes.c_float
@@ -95,8 +95,8 @@ def prefill(lib, dt=1, gk=0, B=1, T=64, H=1, Dk=128, Dv=128, chunk=64, q=FAKE,
     (dict(o=None), EINVAL, "o is NULL"),
     (dict(h0=MIS), EINVAL, "h0 is not 16-byte aligned"),
     (dict(h0=FAKE, ht=FAKE + 256), EINVAL, "overlap"),
-    (dict(ws=None), EINVAL, "workspace of 11776 bytes needed, 0 given"),
-    (dict(ws_bytes=11775), EINVAL, "workspace of 11776 bytes needed"),
+    (dict(ws=None), EINVAL, "workspace of 12288 bytes needed, 0 given"),
+    (dict(ws_bytes=12287), EINVAL, "workspace of 12288 bytes needed"),
     (dict(ws=MIS), EINVAL, "workspace is not 16-byte aligned"),
 ])
 def test_prefill_rejects(lib, kw, code, msg):
@@ -259,14 +259,14 @@ def test_fused_rejects(lib):
 def test_backward_rejects(lib):
     err = lambda: lib.gdr_last_error().decode()  # noqa: E731
     # chunk states and state gradients, the forward's workspace (for the
-    # scalar gate: 5632-byte records; the forward stores no outputs) and per
+    # scalar gate: 5888-byte records; the forward stores no outputs) and per
     # (b, h, chunk) a record of Qt, Kb, W (bf16 64 x 128), P (bf16 64 x 64)
     # and e^{b_C} (fp32 128)
     st = 2 * 3 * 2 * 128 * 128 * 4
     rec = 2 * 3 * 2 * (3 * 64 * 128 * 2 + 64 * 64 * 2 + 128 * 4)
     # the forward's workspace: schedule, chunk offsets, one int32 per (sequence, head)
     # (rounded to 256 bytes), the records
-    fwd_gdn = (512 + 256 + (200 // 64 + 2) * 3 * 5632 + 255) // 256 * 256
+    fwd_gdn = (512 + 256 + (200 // 64 + 2) * 3 * 5888 + 255) // 256 * 256
     # channel gate: the forward's workspace holds one int32 per (sequence, head) more
     assert lib.gdr_backward_workspace_bytes(1, 2, 100, 3, 128, 128) == 2 * st + 512 + 256 + rec
     assert lib.gdr_backward_workspace_bytes(0, 2, 100, 3, 128, 128) == 2 * st + fwd_gdn + rec
@@ -291,7 +291,7 @@ def test_backward_varlen_rejects(lib):
     chunks = 100 // 64 + 2
     st = chunks * 3 * 128 * 128 * 4
     rec = chunks * 3 * (3 * 64 * 128 * 2 + 64 * 64 * 2 + 128 * 4)
-    fwd_gdn = (512 + 256 + chunks * 3 * 5632 + 255) // 256 * 256
+    fwd_gdn = (512 + 256 + chunks * 3 * 5888 + 255) // 256 * 256
     assert lib.gdr_backward_varlen_workspace_bytes(1, 2, 100, 3, 128, 128) == 2 * st + 512 + 256 + rec
     assert lib.gdr_backward_varlen_workspace_bytes(0, 2, 100, 3, 128, 128) == \
         2 * st + fwd_gdn + rec
@@ -328,7 +328,7 @@ def test_prefill_noalloc_rejects(lib):
     def call(dt=1, gk=0, B=1, T=64, H=1, D=128, chunk=64):
         return lib.gdr_prefill_chunked_noalloc(dt, gk, B, T, H, D, D, chunk, F(1.0), FAKE,
                                                FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None)
-    # GDN: 5632 bytes per (chunk, head); 4 x 4096 tokens x 64 heads is 92 MB
+    # GDN: 5888 bytes per (chunk, head); 4 x 4096 tokens x 64 heads is 98 MB
     need = gdr.workspace_bytes(torch.bfloat16, False, 4, 4 * 4096, 64)
     assert need > gdr.NOALLOC_MAX_BYTES
     assert call(B=4, T=4096, H=64) == EUNSUPPORTED and "beyond the library's own" in err()
