@@ -668,7 +668,9 @@ def main():
                 "fused_kda_prefill_B2_H32_T8192_d128_bf16": "fused_kda",
                 "backward_gdn_B4_H16_T4096_d128_bf16": "backward_gdn",
                 "backward_kda_B2_H32_T8192_d128_bf16": "backward_kda",
-                "gdn_recurrent_B1_H1_T64_d64_fp32": "recurrent"}
+                "gdn_recurrent_B1_H1_T64_d64_fp32": "recurrent",
+                "kda_varlen_pool_N16_H32_d128_bf16": "varlen_pool",
+                "backward_kda_varlen_N16_H32_d128_bf16": "backward_kda_varlen"}
         for e in sec:
             if e["workload"] in keys:
                 e["traffic"] = measured_traffic(keys[e["workload"]])
