@@ -33,12 +33,12 @@
 // each own 16 of the 32 value columns and keep their slice of S^T (Dk x 16,
 // fp32) in accumulator registers for the whole sequence; they do nothing but
 // X, U and the update, and publish S^T and U as bf16 MFMA operands.  Four
-// output waves (SIMDs 2 and 3) each own a 16-row block: they load their q
-// rows from global memory straight into registers and form P and O one
+// output waves (SIMDs 2 and 3) each own a 16-row block and form P and O one
 // chunk behind.  Two staging waves (SIMDs 0 and 1, no MFMA work) bring the
 // k rows, the v slice and the chunk's record (T and the decay factors)
-// of chunk c+2 into LDS while chunk c runs, their global loads issued two
-// iterations before the LDS stores.
+// of chunk c+2, and the q rows of chunk c+1, into LDS while chunk c runs,
+// their global loads (whole 128-byte lines) issued two iterations before
+// the LDS stores.
 // One barrier per chunk; between barriers c-1 and c (iteration c):
 //   chain:   X, U and the state update of chunk c from registers, with
 //            the LDS operands of chunk c+1 read into registers while the
@@ -46,12 +46,14 @@
 //            then publish U (by chunk parity) and the new S^T (kept as the
 //            next X's operand), and read the v slice and e^b of chunk c+1
 //   output:  O of chunk c-1 (U of c-1 was published in iteration c-1), then
-//            diag(e^b) Q S^T and P of chunk c (S^T entering c likewise), and
-//            the global loads of the q rows of c+2
-//   staging: chunk c+2 from registers into LDS, global loads of chunk c+4
-// Every LDS value is written in one iteration and read in the next (U and
-// S^T are double-buffered by chunk parity, the staged chunks are held in
-// three slots), so the one barrier orders every producer before its reader.
+//            diag(e^b) Q S^T and P of chunk c (S^T entering c likewise)
+//   staging: chunk c+2 (k, v, record) and the q rows of chunk c+1 from
+//            registers into LDS, global loads of chunk c+4 and of the q rows
+//            of chunk c+3
+// Every LDS value is written in one iteration and read in the next (U, S^T
+// and the q rows are double-buffered by chunk parity, the other staged data
+// are held in three slots), so the one barrier orders every producer before
+// its reader.
 #include "gdr_internal.h"
 #include "device_util.h"
 
@@ -357,6 +359,7 @@ template <int D, bool RAW> struct ChainSmem {
     static constexpr int PV = BV + 16;
     using TRec = TRecT<RAW>;
     alignas(16) bf16 K[3][C * PD];      // by chunk mod 3
+    alignas(16) bf16 Q[2][C * PD];      // by chunk parity
     alignas(16) bf16 V[3][C * PV];      // by chunk mod 3
     alignas(16) TRec TR[3];             // by chunk mod 3
     alignas(16) bf16x8 SB[2][2][KD][64];// S^T entering a chunk (by parity), per chain wave
@@ -615,6 +618,25 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
         // =================================================================
         const int tl = tid - 256;
         bf16x8 rs[2][NI];
+        constexpr int NQ = NKP / 128;         // q pieces per staging thread
+        bf16x8 qs[2][NQ];
+        auto q_load = [&](long long c, auto S) {
+            constexpr int r = decltype(S)::value;
+            const rsrc_t rq = make_rsrc(qg + (size_t)chunk_tok(c) * tokstride, extent(c, D * 2));
+#pragma unroll
+            for (int i = 0; i < NQ; ++i) {
+                const int p = i * 128 + tl;
+                qs[r][i] = bload16(rq, (p / CG) * rowb + 16 * (p % CG));
+            }
+        };
+        auto q_store = [&](int slot, auto S) {
+            constexpr int r = decltype(S)::value;
+#pragma unroll
+            for (int i = 0; i < NQ; ++i) {
+                const int p = i * 128 + tl;
+                *reinterpret_cast<bf16x8 *>(&sm.Q[slot][(p / CG) * PD + 8 * (p % CG)]) = qs[r][i];
+            }
+        };
         auto st_load = [&](long long c, auto S) {
             constexpr int r = decltype(S)::value;
             const size_t base = (size_t)chunk_tok(c) * tokstride;
@@ -654,25 +676,35 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
                 }
             }
         };
+        // q rows go one chunk behind the rest: chunk c+1 into q slot
+        // (c+1) mod 2 in iteration c, from registers loaded in iteration c-2
         st_load(0, R0);
+        q_load(0, R0);
         st_store(0, R0);
+        q_store(0, R0);
         st_load(1, R0);
         st_store(1, R0);
-        // chunk 2 strictly before chunk 3: the loop waits for each register
-        // set by the number of loads issued after it, which assumes this order
+        // loads strictly in this order: the loop waits for each register set
+        // by the number of loads issued after it, which assumes it
         st_load(2, R0);
+        q_load(1, R1);
+        q_load(2, R0);
         __builtin_amdgcn_sched_barrier(0);
         st_load(3, R1);
         __syncthreads();
         int m3 = 2;                           // (c + 2) mod 3
         for (long long c = 0; c < nhalf; c += 2) {
             st_store(m3, R0);
+            q_store(1, R1);                   // chunk c + 1
             m3 = m3 == 2 ? 0 : m3 + 1;
             st_load(c + 4, R0);
+            q_load(c + 3, R1);
             __syncthreads();
             st_store(m3, R1);
+            q_store(0, R0);                   // chunk c + 2
             m3 = m3 == 2 ? 0 : m3 + 1;
             st_load(c + 5, R1);
+            q_load(c + 4, R0);
             __syncthreads();
         }
         return;
@@ -687,23 +719,14 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
     // is formed in accumulator registers, so it feeds the MFMA directly.
     // Iteration c: O of chunk c-1 (U of chunk c-1 was published in iteration
     // c-1), then QS and P of chunk c (S^T entering chunk c was published in
-    // iteration c-1, and chunk c's k rows stay in their LDS slot until
-    // iteration c+1 refills it), then the q rows of chunk c+2, from global
-    // memory straight into registers.
+    // iteration c-1, chunk c's k rows stay in their LDS slot until iteration
+    // c+1 refills it, and its q rows were staged in iteration c-1).
     // =====================================================================
     auto out_loop = [&](auto RBc) {
         constexpr int RB = decltype(RBc)::value;
         constexpr int NP2 = (RB + 2) / 2;   // pairs of 16-token blocks J <= RB
-        bf16x8 Qr[2][KD];                   // q rows 16 RB + l15, two chunks
         bf16x8 Pp[NP2];                     // P^T of the previous chunk, as B operand pairs
         f32x4 QSp[2];                       // (Q S^T)^T[16 ob + 4 q4 + e][16 RB + l15], scaled by e^b
-        auto q_load = [&](long long c, auto S) {
-            constexpr int r = decltype(S)::value;
-            const rsrc_t rq = make_rsrc(qg + (size_t)chunk_tok(c) * tokstride, extent(c, D * 2));
-            const unsigned off = (16 * RB + l15) * rowb + 16 * q4;
-#pragma unroll
-            for (int kk = 0; kk < KD; ++kk) Qr[r][kk] = bload16(rq, off + 64 * kk);
-        };
         // O of chunk c-1
         auto o_step = [&](long long c) {
             bf16x8 Au[2][NP2];
@@ -724,15 +747,17 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
             }
         };
         // QS and P of chunk c (m3 = c mod 3)
-        auto qp_step = [&](long long c, int m3, auto S) {
-            constexpr int r = decltype(S)::value;
+        auto qp_step = [&](long long c, int m3) {
             const bf16 *Kc = sm.K[m3];
-            bf16x8 As[2][KD], Kj[RB + 1][KD];
+            const bf16 *Qc = sm.Q[(int)(c & 1)];
+            bf16x8 As[2][KD], Kj[RB + 1][KD], Qr[KD];   // Qr: q rows 16 RB + l15
             f32x4 lbJ[RB + 1], rkJ[RB + 1];
 #pragma unroll
             for (int ob = 0; ob < 2; ++ob)
 #pragma unroll
                 for (int kk = 0; kk < KD; ++kk) As[ob][kk] = sm.SB[(int)(c & 1)][ob][kk][lane];
+#pragma unroll
+            for (int kk = 0; kk < KD; ++kk) Qr[kk] = frag_rows(Qc, PD, 16 * RB, 32 * kk, lane);
 #pragma unroll
             for (int J = 0; J <= RB; ++J) {
 #pragma unroll
@@ -750,7 +775,7 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
 #pragma unroll
                 for (int kk = 0; kk < KD; ++kk)
 #pragma unroll
-                    for (int u = 0; u < 8; ++u) ss = __builtin_fmaf((float)Qr[r][kk][u], (float)Qr[r][kk][u], ss);
+                    for (int u = 0; u < 8; ++u) ss = __builtin_fmaf((float)Qr[kk][u], (float)Qr[kk][u], ss);
                 ss = swap_sum32(swap_sum16(ss));
                 iq = inv_norm(ss);
                 ebr *= iq;
@@ -760,7 +785,7 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
             for (int ob = 0; ob < 2; ++ob) {
                 f32x4 x = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kk = 0; kk < KD; ++kk) x = mfma32(As[ob][kk], Qr[r][kk], x);
+                for (int kk = 0; kk < KD; ++kk) x = mfma32(As[ob][kk], Qr[kk], x);
                 QSp[ob] = x * ebr;
             }
             // P: K_J Q_RB^T gives lane s = 16 J + 4 q4 + e, r = 16 RB + l15,
@@ -772,7 +797,7 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
             for (int J = 0; J <= RB; ++J) {
                 f32x4 p = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kk = 0; kk < KD; ++kk) p = mfma32(Kj[J][kk], Qr[r][kk], p);
+                for (int kk = 0; kk < KD; ++kk) p = mfma32(Kj[J][kk], Qr[kk], p);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     float v = __builtin_amdgcn_exp2f(lbr - lbJ[J][e]) * p[e];
@@ -784,9 +809,6 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
 #pragma unroll
             for (int k2 = 0; k2 < NP2; ++k2) Pp[k2] = acc_pair(pv[2 * k2], pv[2 * k2 + 1]);
         };
-        q_load(0, R0);
-        __builtin_amdgcn_sched_barrier(0);    // chunk 0 strictly before chunk 1, as in the loop
-        q_load(1, R1);
         QSp[0] = QSp[1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int k2 = 0; k2 < NP2; ++k2) Pp[k2] = bf16x8{};
@@ -794,13 +816,11 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
         int m3 = 0;                           // c mod 3
         for (long long c = 0; c < nhalf; c += 2) {
             o_step(c);
-            qp_step(c, m3, R0);
-            q_load(c + 2, R0);
+            qp_step(c, m3);
             m3 = m3 == 2 ? 0 : m3 + 1;
             __syncthreads();
             o_step(c + 1);
-            qp_step(c + 1, m3, R1);
-            q_load(c + 3, R1);
+            qp_step(c + 1, m3);
             m3 = m3 == 2 ? 0 : m3 + 1;
             __syncthreads();
         }
