@@ -447,16 +447,20 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
     auto srow = [&](int jk, int e) -> int { return 32 * (jk >> 1) + 8 * q4 + 4 * (jk & 1) + e; };
     const std::integral_constant<int, 0> R0;
     const std::integral_constant<int, 1> R1;
+    // Value column (within the slice) of local column m of chain wave ib:
+    // the two waves take alternate groups of four, so that an output lane's
+    // four columns from each wave are eight adjacent ones (one 16-byte store)
+    auto vcol = [](int ib, int m) -> int { return 8 * (m >> 2) + 4 * ib + (m & 3); };
 
     if (w < 2) {
         // =================================================================
-        // chain waves: value columns 16 ib .. 16 ib + 15 of the slice
+        // chain waves: value columns vcol(ib, 0..15) of the slice
         // =================================================================
         const int ib = w;
-        // S^T[srow(jk, e)][16 ib + l15] (fp32); the four rows e of a block are
-        // adjacent columns of S, so they move as one 16-byte access
+        // S^T[srow(jk, e)][vcol(ib, l15)] (fp32); the four rows e of a block
+        // are adjacent columns of S, so they move as one 16-byte access
         f32x4 St[KS];
-        const size_t srow0 = (size_t)(i0 + 16 * ib + l15) * D;
+        const size_t srow0 = (size_t)(i0 + vcol(ib, l15)) * D;
         const float *h0p = seq_h0<D>(a, n, h);
 #pragma unroll
         for (int jk = 0; jk < KS; ++jk)
@@ -505,7 +509,11 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
             const float lbC = R.lb[C - 1];
 #pragma unroll
             for (int rb = 0; rb < 4; ++rb) {
-                vv[rb] = frag_col4(Vc, PV, 16 * rb, 16 * ib, lane);
+                // rows 16 rb + 4 q4 .. +3 of column vcol(ib, l15), by one
+                // transpose load: lane j of each 16-lane group addresses row
+                // j >> 2 and the four columns vcol(ib, 4 (j & 3)) .. +3
+                const bf16 *pv = Vc + (16 * rb + 4 * q4 + (l15 >> 2)) * PV + 8 * (l15 & 3) + 4 * ib;
+                vv[rb] = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)pv));
                 eb[rb] = *reinterpret_cast<const f32x4 *>(&R.ek[16 * rb + 4 * q4]);
             }
             gC = __builtin_amdgcn_exp2f(lbC);
@@ -713,8 +721,9 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
     // =====================================================================
     // output waves: row block RB of the chunk (waves 2, 3, 7, 6 take 0, 1, 2,
     // 3, so each of SIMDs 2 and 3 carries 1 + 4 or 2 + 3 blocks of P), both
-    // value blocks.  O^T = scale (S Q^T diag(e^b) + U^T P^T) so that a lane
-    // ends up with four adjacent columns of one output row: the published
+    // value blocks (the columns of the two chain waves).  O^T = scale (S Q^T
+    // diag(e^b) + U^T P^T) so that a lane ends up with four columns of one
+    // output row per block, eight adjacent ones in all (vcol): the published
     // S^T and U serve as A operands, the q rows and P^T as B operands.  P^T
     // is formed in accumulator registers, so it feeds the MFMA directly.
     // Iteration c: O of chunk c-1 (U of chunk c-1 was published in iteration
@@ -726,7 +735,7 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
         constexpr int RB = decltype(RBc)::value;
         constexpr int NP2 = (RB + 2) / 2;   // pairs of 16-token blocks J <= RB
         bf16x8 Pp[NP2];                     // P^T of the previous chunk, as B operand pairs
-        f32x4 QSp[2];                       // (Q S^T)^T[16 ob + 4 q4 + e][16 RB + l15], scaled by e^b
+        f32x4 QSp[2];                       // (Q S^T)^T[vcol(ob, 4 q4 + e)][16 RB + l15], scaled by e^b
         // O of chunk c-1
         auto o_step = [&](long long c) {
             bf16x8 Au[2][NP2];
@@ -737,14 +746,17 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(PrefillArgs a) {
                 for (int k2 = 0; k2 < NP2; ++k2) Au[ob][k2] = sm.UB[up][ob][k2][lane];
             __builtin_amdgcn_sched_barrier(0);
             const rsrc_t ro = make_rsrc(og + (size_t)chunk_tok(c - 1) * tokstride, a.o ? extent(c - 1, BV * 2) : 0u);
-            const unsigned voff = l15 * rowb + 8 * q4;
+            // lane (q4, l15): columns vcol(ob, 4 q4 + e) = 8 q4 + 4 ob + e of
+            // row 16 RB + l15, eight adjacent columns over the two blocks
+            f32x4 o[2];
 #pragma unroll
             for (int ob = 0; ob < 2; ++ob) {
-                f32x4 o = QSp[ob];
+                o[ob] = QSp[ob];
 #pragma unroll
-                for (int k2 = 0; k2 < NP2; ++k2) o = mfma32(Au[ob][k2], Pp[k2], o);
-                bstore8s(ro, voff + 32 * ob, 16 * RB * rowb, cvt4(o * a.scale));
+                for (int k2 = 0; k2 < NP2; ++k2) o[ob] = mfma32(Au[ob][k2], Pp[k2], o[ob]);
             }
+            bstore16s(ro, l15 * rowb + 16 * q4, 16 * RB * rowb,
+                      cat8(cvt4(o[0] * a.scale), cvt4(o[1] * a.scale)));
         };
         // QS and P of chunk c (m3 = c mod 3)
         auto qp_step = [&](long long c, int m3) {

@@ -104,6 +104,10 @@ __device__ inline void bstore8s(rsrc_t r, unsigned voff, unsigned soff, bf16x4 v
     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, v),
                                           r, voff, (int)__builtin_amdgcn_readfirstlane(soff), 0);
 }
+__device__ inline void bstore16s(rsrc_t r, unsigned voff, unsigned soff, bf16x8 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, v),
+                                           r, voff, (int)__builtin_amdgcn_readfirstlane(soff), 0);
+}
 // same with a wave-uniform part of the offset in a scalar register
 __device__ inline void bstore2s(rsrc_t r, unsigned voff, unsigned soff, bf16 v) {
     __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, v), r, voff,
