@@ -69,17 +69,20 @@ __device__ inline int ltri(int i, int j) { return i * (i - 1) / 2 + j; }  // blo
 // ===========================================================================
 // prep_kernel: T of one (chunk, head)
 // ===========================================================================
-template <int D> struct PrepSmem {
-    static constexpr int PD = D + 16;   // conflict-free 16-byte row fragments
-    alignas(16) bf16 K[C * PD];
+// 27,136 bytes for the scalar gate, so that six workgroups fit a CU's LDS
+template <int D, bool RAW> struct PrepSmem {
+    static constexpr int PD = D + 8;    // rows padded by 16 bytes
+    union alignas(16) {
+        bf16 K[C * PD];                 // k rows, read by the Gram blocks
+        float Nd[4][256];               // then N_bb, [r][s]
+    };
     alignas(16) float MT[4][256];       // L_bb^T, [s][r] (strictly lower L_bb)
-    alignas(16) float Nd[4][256];       // N_bb, [r][s]
     // the record's operands as tiles (lane l: row l & 15, columns 4 (l >> 4)
     // .. +3): T_00, T_11, T_22, T_33, -A_10, -A_32, -A_20, -A_21, -A_30, -A_31
     alignas(16) bf16 TT[10 * 256];
     alignas(16) float fb[C];            // b_r
     alignas(16) float fbeta[C];         // beta_r
-    alignas(16) float frk[C];           // 1 / |k_r| (fused preprocessing)
+    alignas(16) float frk[RAW ? C : 1]; // 1 / |k_r| (fused preprocessing)
 };
 
 // RAW (fused preprocessing): gate and beta from their logits, the Gram
@@ -90,7 +93,7 @@ template <int D> struct PrepSmem {
 // their differences stay finite for any gate a in [0, 1].
 template <int D, bool RAW>
 __global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a) {
-    using Sm = PrepSmem<D>;
+    using Sm = PrepSmem<D, RAW>;
     constexpr int PD = Sm::PD;
     constexpr int KD = D / 32;
     constexpr int CG = D / 8;           // 16-byte pieces per row
