@@ -20,6 +20,7 @@
 // and S'q) by a recursive-halving exchange across the LPR lanes of a row,
 // which leaves one finished dot product per lane.
 #include "gdr_internal.h"
+#include "device_util.h"
 
 #ifndef GDR_DECODE_PASSES
 #define GDR_DECODE_PASSES 2   // 16 rows (8 KiB of state) per workgroup at D = 128
@@ -45,49 +46,118 @@ __device__ inline float dot4(f32x4 a, f32x4 b) {
     return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
 }
 
-// One token's update of the state slice S held by this thread.  qp, kp, vp
-// point at the head's D-vector for this token, gp at its gate logs (D values
-// for a channel gate, one for a scalar gate; fp32).  The output is written
-// to op.  RAW (fused preprocessing): gp points at gate logits of type T and
-// beta is a logit; q and k are normalised over the LPR lanes of the row.
+// One token's inputs as this thread needs them: k and q at its four columns,
+// the gate logs there (a scalar gate: its one value four times), v at the
+// row whose dot products the thread finishes, and beta.  RAW (fused
+// preprocessing): the gate and beta logits instead, and q and k not yet
+// normalised.
+struct StepIn {
+    f32x4 kv, qv, lg;
+    float vrow, beta;
+};
+
+// Row of the result a thread finishes in head_step (see there)
+template <int D>
+__device__ inline int result_row(int lane, int w) {
+    using G = Geom<D>;
+    const int idx = (lane % G::LPR) >> G::SHIFT;
+    return (idx % G::M) * G::RPI + w * G::RPW + lane / G::LPR;
+}
+
+// qp, kp, vp point at the head's D-vector for the token, gp at its gate logs
+// (D values for a channel gate, one for a scalar gate; fp32, or type T
+// logits with RAW), bp at its beta (RAW: a type T logit)
 template <typename T, int D, bool RAW>
-__device__ inline void head_step(f32x4 (&S)[Geom<D>::M], const T *qp, const T *kp,
-                                 const T *vp, const void *gp, bool channel,
-                                 float beta, float scale, float gate_scale, T *op, int lane,
-                                 int w) {
+__device__ inline StepIn step_load(const T *qp, const T *kp, const T *vp, const void *gp,
+                                   const void *bp, bool channel, int lane, int w) {
     using G = Geom<D>;
     const int c0 = (lane % G::LPR) * 4;
-    const int sub = lane / G::LPR;
-    f32x4 kv = Elem<T>::load4(kp + c0);
-    f32x4 qv = Elem<T>::load4(qp + c0);
-    f32x4 lg;
+    StepIn x;
+    x.kv = Elem<T>::load4(kp + c0);
+    x.qv = Elem<T>::load4(qp + c0);
     if (RAW) {
         const T *xg = static_cast<const T *>(gp);
         if (channel) {
-            lg = Elem<T>::load4(xg + c0);
+            x.lg = Elem<T>::load4(xg + c0);
         } else {
             const float s = Elem<T>::load(xg);
-            lg = f32x4{s, s, s, s};
+            x.lg = f32x4{s, s, s, s};
         }
+        x.beta = Elem<T>::load(static_cast<const T *>(bp));
+    } else {
+        const float *g = static_cast<const float *>(gp);
+        if (channel) {
+            x.lg = *reinterpret_cast<const f32x4 *>(g + c0);
+        } else {
+            const float s = g[0];
+            x.lg = f32x4{s, s, s, s};
+        }
+        x.beta = *static_cast<const float *>(bp);
+    }
+    x.vrow = Elem<T>::load(vp + result_row<D>(lane, w));
+    return x;
+}
+
+// Cross-lane steps of head_step when a state row is one 16-lane DPP row
+// (D = 64): VALU data-parallel moves instead of LDS permutes.  Recursive
+// halving needs, at the level of lane bit b, a partner with bit b flipped
+// and the higher bits kept (it holds the same part of the list); row_mirror
+// (lane i <-> 15 - i), row_half_mirror (i <-> i ^ 7 within each 8) and the
+// quad permutes xor 2, xor 1 are such partners for b = 8, 4, 2, 1, and the
+// lane keeps the part its own bit selects, so every lane ends with the sum
+// over all 16 lanes of the result its bits name.
+template <int MASK, int CTRL, int NV>
+__device__ inline void halving_step(float (&val)[NV], int &n, int lane) {
+    if (n > 1) {
+        const int half = n / 2;
+        const bool upper = (lane & MASK) != 0;
+#pragma unroll
+        for (int i = 0; i < half; ++i) {
+            const float keep = upper ? val[half + i] : val[i];
+            const float give = upper ? val[i] : val[half + i];
+            val[i] = keep + dpp_f<CTRL>(give);
+        }
+        n = half;
+    } else {
+        val[0] += dpp_f<CTRL>(val[0]);
+    }
+}
+// u of lane 2 m of each 16-lane row (row_newbcast), for the M rows m
+template <int M, int SHIFT, int m = 0>
+__device__ inline void bcast_rows(float u, float (&um)[M]) {
+    if constexpr (m < M) {
+        um[m] = dpp_f<0x150 + (m << SHIFT)>(u);
+        bcast_rows<M, SHIFT, m + 1>(u, um);
+    }
+}
+
+// One token's update of the state slice S held by this thread, from the
+// token's inputs; the output is written to op.
+template <typename T, int D, bool RAW>
+__device__ inline void head_step(f32x4 (&S)[Geom<D>::M], StepIn in, float scale,
+                                 float gate_scale, T *op, int lane, int w) {
+    using G = Geom<D>;
+    constexpr bool kDpp = G::LPR == 16;          // a state row is one DPP row
+    const int sub = lane / G::LPR;
+    f32x4 kv = in.kv, qv = in.qv, lg = in.lg;
+    float beta = in.beta;
+    if (RAW) {
         lg = f32x4{neg_softplus(lg.x, gate_scale), neg_softplus(lg.y, gate_scale),
                    neg_softplus(lg.z, gate_scale), neg_softplus(lg.w, gate_scale)};
         beta = logistic(beta);
         float sk = dot4(kv, kv), sq = dot4(qv, qv);
+        if constexpr (kDpp) {
+            sk = sum_group<16>(sk);
+            sq = sum_group<16>(sq);
+        } else {
 #pragma unroll
-        for (int mask = G::LPR / 2; mask >= 1; mask >>= 1) {
-            sk += __shfl_xor(sk, mask);
-            sq += __shfl_xor(sq, mask);
+            for (int mask = G::LPR / 2; mask >= 1; mask >>= 1) {
+                sk += __shfl_xor(sk, mask);
+                sq += __shfl_xor(sq, mask);
+            }
         }
         kv = kv * inv_norm(sk);
         qv = qv * inv_norm(sq);
-    } else {
-        const float *g = static_cast<const float *>(gp);
-        if (channel) {
-            lg = *reinterpret_cast<const f32x4 *>(g + c0);
-        } else {
-            const float s = g[0];
-            lg = f32x4{s, s, s, s};
-        }
     }
     constexpr float kLog2e = 1.4426950408889634f;
     const f32x4 a = f32x4{__builtin_amdgcn_exp2f(lg.x * kLog2e),
@@ -99,9 +169,13 @@ __device__ inline void head_step(f32x4 (&S)[Geom<D>::M], const T *qp, const T *k
 
     // k.q over the full row: all-reduce across the LPR lanes of the row
     float kq = dot4(kv, qv);
+    if constexpr (kDpp) {
+        kq = sum_group<16>(kq);
+    } else {
 #pragma unroll
-    for (int mask = G::LPR / 2; mask >= 1; mask >>= 1)
-        kq += __shfl_xor(kq, mask);
+        for (int mask = G::LPR / 2; mask >= 1; mask >>= 1)
+            kq += __shfl_xor(kq, mask);
+    }
 
     // partial (S'k)_row and (S'q)_row over this thread's 4 columns
     float val[G::NV];
@@ -113,40 +187,56 @@ __device__ inline void head_step(f32x4 (&S)[Geom<D>::M], const T *qp, const T *k
     // recursive halving: after step with mask b the lane keeps the half of
     // the list selected by its lane bit b, summed with the partner's copy
     int n = G::NV;
+    if constexpr (kDpp) {
+        halving_step<8, 0x140>(val, n, lane);   // row_mirror
+        halving_step<4, 0x141>(val, n, lane);   // row_half_mirror
+        halving_step<2, 0x4E>(val, n, lane);    // quad_perm [2,3,0,1]
+        halving_step<1, 0xB1>(val, n, lane);    // quad_perm [1,0,3,2]
+    } else {
 #pragma unroll
-    for (int mask = G::LPR / 2; mask >= 1; mask >>= 1) {
-        if (n > 1) {
-            const int half = n / 2;
-            const bool upper = (lane & mask) != 0;
+        for (int mask = G::LPR / 2; mask >= 1; mask >>= 1) {
+            if (n > 1) {
+                const int half = n / 2;
+                const bool upper = (lane & mask) != 0;
 #pragma unroll
-            for (int i = 0; i < half; ++i) {
-                const float keep = upper ? val[half + i] : val[i];
-                const float give = upper ? val[i] : val[half + i];
-                val[i] = keep + __shfl_xor(give, mask);
+                for (int i = 0; i < half; ++i) {
+                    const float keep = upper ? val[half + i] : val[i];
+                    const float give = upper ? val[i] : val[half + i];
+                    val[i] = keep + __shfl_xor(give, mask);
+                }
+                n = half;
+            } else {
+                val[0] += __shfl_xor(val[0], mask);
             }
-            n = half;
-        } else {
-            val[0] += __shfl_xor(val[0], mask);
         }
     }
     // this lane now holds result index idx: which = idx / M, row slot idx % M
+    // (row result_row(lane, w))
     const int idx = (lane % G::LPR) >> G::SHIFT;
     const bool is_q = idx >= G::M;
-    const int mrow = idx % G::M;
-    const int row = mrow * G::RPI + w * G::RPW + sub;
+    const int row = result_row<D>(lane, w);
 
-    const float vrow = Elem<T>::load(vp + row);
-    const float u = beta * (vrow - val[0]);              // valid where !is_q
-    const float u_pair = __shfl_xor(u, G::M << G::SHIFT);   // for is_q lanes
+    const float u = beta * (in.vrow - val[0]);           // valid where !is_q
+    float u_pair;                                        // for is_q lanes
+    if constexpr (kDpp) {
+        static_assert((G::M << G::SHIFT) == 8, "partner of the k result: lane ^ 8");
+        u_pair = dpp_f<0x128>(u);                        // row_ror:8 = lane ^ 8 in a row
+    } else {
+        u_pair = __shfl_xor(u, G::M << G::SHIFT);
+    }
     if (is_q && (lane & ((1 << G::SHIFT) - 1)) == 0)
         Elem<T>::store(op + row, scale * (val[0] + u_pair * kq));
 
     // rank-1 update: every lane needs u for each of its M rows
+    float um[G::M];
+    if constexpr (kDpp) {
+        bcast_rows<G::M, G::SHIFT>(u, um);
+    } else {
 #pragma unroll
-    for (int m = 0; m < G::M; ++m) {
-        const float um = __shfl(u, sub * G::LPR + (m << G::SHIFT));
-        S[m] = S[m] * a + um * kv;
+        for (int m = 0; m < G::M; ++m) um[m] = __shfl(u, sub * G::LPR + (m << G::SHIFT));
     }
+#pragma unroll
+    for (int m = 0; m < G::M; ++m) S[m] = S[m] * a + um[m] * kv;
 }
 
 // Consecutive workgroups go to the eight XCDs in turn, each with its own L2.
@@ -348,10 +438,15 @@ __global__ __launch_bounds__(256) void decode_tokens_kernel(TokensArgs a) {
             // |k|^2 and |q|^2 over the LPR lanes of the row, then the
             // normalised vectors, beta and the gate logs from their logits
             float sk = dot4(cur.k, cur.k), sq = dot4(cur.q, cur.q);
+            if constexpr (G::LPR == 16) {
+                sk = sum_group<16>(sk);
+                sq = sum_group<16>(sq);
+            } else {
 #pragma unroll
-            for (int mask = G::LPR / 2; mask >= 1; mask >>= 1) {
-                sk += __shfl_xor(sk, mask);
-                sq += __shfl_xor(sq, mask);
+                for (int mask = G::LPR / 2; mask >= 1; mask >>= 1) {
+                    sk += __shfl_xor(sk, mask);
+                    sq += __shfl_xor(sq, mask);
+                }
             }
             cur.k = cur.k * inv_norm(sk);
             cur.q = cur.q * inv_norm(sq);
@@ -364,19 +459,35 @@ __global__ __launch_bounds__(256) void decode_tokens_kernel(TokensArgs a) {
         const f32x4 ak = av * cur.k;
         const f32x4 aq = av * cur.q;
         float kq = dot4(cur.k, cur.q);
+        // a state row is one 16-lane DPP row at D = 64: VALU moves (row_ror:8
+        // is lane ^ 8 within the row; quad permutes and row_half_mirror sum
+        // each half) instead of LDS permutes
+        constexpr bool kDpp = G::LPR == 16;
+        if constexpr (kDpp) {
+            kq = sum_group<16>(kq);
+        } else {
 #pragma unroll
-        for (int mask = G::LPR / 2; mask >= 1; mask >>= 1) kq += __shfl_xor(kq, mask);
+            for (int mask = G::LPR / 2; mask >= 1; mask >>= 1) kq += __shfl_xor(kq, mask);
+        }
         T *op = static_cast<T *>(a.o) + bth * D;
 #pragma unroll
         for (int p = 0; p < PASSES; ++p) {
             const float yk = dot4(S[p], ak);
             const float yq = dot4(S[p], aq);
             const bool upper = (lane & (G::LPR / 2)) != 0;
-            float val = (upper ? yq : yk) + __shfl_xor(upper ? yk : yq, G::LPR / 2);
+            float val, u_lo, u;
+            if constexpr (kDpp) {
+                val = (upper ? yq : yk) + dpp_f<0x128>(upper ? yk : yq);
+                val = sum_group<8>(val);
+                u_lo = cur.beta * (cur.v[p] - val);
+                u = dpp_f<0x128>(u_lo);
+            } else {
+                val = (upper ? yq : yk) + __shfl_xor(upper ? yk : yq, G::LPR / 2);
 #pragma unroll
-            for (int mask = G::LPR / 4; mask >= 1; mask >>= 1) val += __shfl_xor(val, mask);
-            const float u_lo = cur.beta * (cur.v[p] - val);
-            const float u = __shfl_xor(u_lo, G::LPR / 2);
+                for (int mask = G::LPR / 4; mask >= 1; mask >>= 1) val += __shfl_xor(val, mask);
+                u_lo = cur.beta * (cur.v[p] - val);
+                u = __shfl_xor(u_lo, G::LPR / 2);
+            }
             const float um = upper ? u : u_lo;
             if (upper && (lane % (G::LPR / 2)) == 0) Elem<T>::store(op + row[p], a.scale * (val + um * kq));
             S[p] = S[p] * av + um * cur.k;
@@ -461,17 +572,40 @@ __global__ __launch_bounds__(256) void prefill_recurrent_kernel(PrefillArgs a) {
     const T *k = static_cast<const T *>(a.k) + h * D;
     const T *v = static_cast<const T *>(a.v) + h * D;
     T *o = static_cast<T *>(a.o) + h * D;
-    for (long long t = t0; t < t1; ++t) {
-        if (RAW) {
-            const T *xg = static_cast<const T *>(a.xg) + t * gtok + goff;
-            const float xb = Elem<T>::load(static_cast<const T *>(a.xb) + t * a.H + h);
-            head_step<T, D, true>(S, q + t * tok, k + t * tok, v + t * tok, xg,
-                                  a.channel_gate != 0, xb, a.scale, a.gate_scale, o + t * tok,
-                                  lane, w);
-        } else {
-            head_step<T, D, false>(S, q + t * tok, k + t * tok, v + t * tok,
-                                   a.g + t * gtok + goff, a.channel_gate != 0,
-                                   a.beta[t * a.H + h], a.scale, 0.f, o + t * tok, lane, w);
+    // token t's inputs, loaded P tokens ahead of their step (a ring of P
+    // register sets, so that the load latency is paid once, not per token)
+    auto load = [&](long long t) -> StepIn {
+        if (RAW)
+            return step_load<T, D, true>(q + t * tok, k + t * tok, v + t * tok,
+                                         static_cast<const T *>(a.xg) + t * gtok + goff,
+                                         static_cast<const T *>(a.xb) + t * a.H + h,
+                                         a.channel_gate != 0, lane, w);
+        return step_load<T, D, false>(q + t * tok, k + t * tok, v + t * tok,
+                                      a.g + t * gtok + goff, a.beta + t * a.H + h,
+                                      a.channel_gate != 0, lane, w);
+    };
+    constexpr int P = 4;
+    StepIn in[P];
+#pragma unroll
+    for (int i = 0; i < P; ++i)
+        if (t0 + i < t1) in[i] = load(t0 + i);
+    long long t = t0;
+    // every load of the main loop is in range (t + 2P - 1 < t1), so none is
+    // conditional there
+    for (; t + 2 * P <= t1; t += P) {
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
+            head_step<T, D, RAW>(S, in[i], a.scale, a.gate_scale, o + (t + i) * tok, lane, w);
+            in[i] = load(t + i + P);
+        }
+    }
+    for (; t < t1; t += P) {
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
+            if (t + i < t1) {
+                head_step<T, D, RAW>(S, in[i], a.scale, a.gate_scale, o + (t + i) * tok, lane, w);
+                if (t + i + P < t1) in[i] = load(t + i + P);
+            }
         }
     }
     if (float *htp = seq_ht<D>(a, n, h)) {
@@ -544,6 +678,34 @@ hipError_t launch_prefill_recurrent(bool bf16_io, int D, const PrefillArgs &a,
                                     hipStream_t s) {
     const long long blocks = (long long)a.N * a.H;
     if (blocks <= 0) return hipSuccess;
+    // A fixed-length batch whose final state is wanted runs as the tokens of
+    // a decode over its T tokens, in place on ht (h0 copied there first):
+    // the rows of a state split over D / RPI workgroups (one pass each), so
+    // a thread carries a quarter (D = 64) or a sixteenth (D = 128) of the
+    // state the one-workgroup kernel below gives it, and a token's step is
+    // that much shorter -- the latency of a short sequence.
+    if (!a.cu_seqlens && !a.h0_slot && !a.ht_slot && a.ht && a.T > 0) {
+        hipError_t e = launch_copy_or_zero(a.ht, a.h0, (size_t)a.N * a.H * D * D, s);
+        if (e != hipSuccess) return e;
+        TokensArgs t{};
+        t.q = a.q; t.k = a.k; t.v = a.v; t.g = a.g; t.beta = a.beta;
+        t.slot = nullptr; t.pool = a.N; t.state = a.ht; t.ckpt = nullptr; t.o = a.o;
+        t.B = a.N; t.n = a.T; t.H = a.H; t.scale = a.scale; t.channel_gate = a.channel_gate;
+        t.xg = a.xg; t.xb = a.xb; t.gate_scale = a.gate_scale;
+        const long long tb = blocks * (D == 128 ? 128 / Geom<128>::RPI : 64 / Geom<64>::RPI);
+        if (tb >= (1LL << 31)) return hipErrorInvalidValue;
+        dim3 tgrid((unsigned)tb), tblock(256);
+#define GDR_TOKENS1(TT, DD, RR) hipLaunchKernelGGL((decode_tokens_kernel<TT, DD, 1, RR>), tgrid, tblock, 0, s, t)
+        if (a.xg) {
+            if (bf16_io) { if (D == 128) GDR_TOKENS1(bf16, 128, true);  else GDR_TOKENS1(bf16, 64, true); }
+            else         { if (D == 128) GDR_TOKENS1(float, 128, true); else GDR_TOKENS1(float, 64, true); }
+        } else {
+            if (bf16_io) { if (D == 128) GDR_TOKENS1(bf16, 128, false);  else GDR_TOKENS1(bf16, 64, false); }
+            else         { if (D == 128) GDR_TOKENS1(float, 128, false); else GDR_TOKENS1(float, 64, false); }
+        }
+#undef GDR_TOKENS1
+        return hipGetLastError();
+    }
     dim3 grid((unsigned)blocks), block(256);
     if (a.xg) {
         if (bf16_io) {
