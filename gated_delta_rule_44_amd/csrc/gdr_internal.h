@@ -104,6 +104,11 @@ struct TokensArgs {
     // and beta; q and k are normalised in the kernel
     const void *xg, *xb;
     float gate_scale;
+    // prefill form: sequence b starts from init[b] ([B, H, D, D]) instead of
+    // its pool slot, or from zeros when init_zero is set; the final state
+    // still goes to the slot
+    const float *init;
+    int init_zero;
 };
 
 hipError_t launch_decode_tokens(bool bf16_io, int D, const TokensArgs &a, hipStream_t s,

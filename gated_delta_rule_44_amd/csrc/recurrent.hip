@@ -423,17 +423,21 @@ __global__ __launch_bounds__(256) void decode_tokens_kernel(TokensArgs a) {
     for (int p = 0; p < PASSES; ++p) row[p] = rb * ROWS + p * RPP + w * G::RPW + sub;
 
     float *st = a.state + ((size_t)slot * a.H + h) * D * D;
+    const float *s0 = a.init ? a.init + ((size_t)b * a.H + h) * D * D : st;
     f32x4 S[PASSES];
 #pragma unroll
     for (int p = 0; p < PASSES; ++p)
-        S[p] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(st + (size_t)row[p] * D + c0));
+        S[p] = a.init_zero ? f32x4{0.f, 0.f, 0.f, 0.f}
+                           : __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(s0 + (size_t)row[p] * D + c0));
 
     const size_t bh0 = (size_t)b * a.n * a.H + h;        // (b, token 0, h)
     TokIn<PASSES> cur = load_token<T, D, PASSES, RAW>(a, bh0, c0, row);
+    // the inputs of the next two tokens in flight while a token is worked on
+    TokIn<PASSES> nx1 = a.n > 1 ? load_token<T, D, PASSES, RAW>(a, bh0 + a.H, c0, row) : cur;
     constexpr float kLog2e = 1.4426950408889634f;
     for (int t = 0; t < a.n; ++t) {
         const size_t bth = bh0 + (size_t)t * a.H;
-        const TokIn<PASSES> nxt = t + 1 < a.n ? load_token<T, D, PASSES, RAW>(a, bth + a.H, c0, row) : cur;
+        const TokIn<PASSES> nx2 = t + 2 < a.n ? load_token<T, D, PASSES, RAW>(a, bth + 2 * a.H, c0, row) : nx1;
         if (RAW) {
             // |k|^2 and |q|^2 over the LPR lanes of the row, then the
             // normalised vectors, beta and the gate logs from their logits
@@ -498,7 +502,8 @@ __global__ __launch_bounds__(256) void decode_tokens_kernel(TokensArgs a) {
             for (int p = 0; p < PASSES; ++p)
                 __builtin_nontemporal_store(S[p], reinterpret_cast<f32x4 *>(cp + (size_t)row[p] * D + c0));
         }
-        cur = nxt;
+        cur = nx1;
+        nx1 = nx2;
     }
     if (!a.ckpt) {
 #pragma unroll
@@ -679,15 +684,15 @@ hipError_t launch_prefill_recurrent(bool bf16_io, int D, const PrefillArgs &a,
     const long long blocks = (long long)a.N * a.H;
     if (blocks <= 0) return hipSuccess;
     // A fixed-length batch whose final state is wanted runs as the tokens of
-    // a decode over its T tokens, in place on ht (h0 copied there first):
-    // the rows of a state split over D / RPI workgroups (one pass each), so
-    // a thread carries a quarter (D = 64) or a sixteenth (D = 128) of the
-    // state the one-workgroup kernel below gives it, and a token's step is
-    // that much shorter -- the latency of a short sequence.
+    // a decode over its T tokens, from h0 (or zeros) into ht: the rows of a
+    // state split over D / RPI workgroups (one pass each), so a thread
+    // carries a quarter (D = 64) or a sixteenth (D = 128) of the state the
+    // one-workgroup kernel below gives it, and a token's step is that much
+    // shorter -- the latency of a short sequence.
     if (!a.cu_seqlens && !a.h0_slot && !a.ht_slot && a.ht && a.T > 0) {
-        hipError_t e = launch_copy_or_zero(a.ht, a.h0, (size_t)a.N * a.H * D * D, s);
-        if (e != hipSuccess) return e;
         TokensArgs t{};
+        t.init = a.h0;
+        t.init_zero = a.h0 ? 0 : 1;
         t.q = a.q; t.k = a.k; t.v = a.v; t.g = a.g; t.beta = a.beta;
         t.slot = nullptr; t.pool = a.N; t.state = a.ht; t.ckpt = nullptr; t.o = a.o;
         t.B = a.N; t.n = a.T; t.H = a.H; t.scale = a.scale; t.channel_gate = a.channel_gate;
