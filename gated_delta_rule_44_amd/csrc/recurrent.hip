@@ -432,12 +432,18 @@ __global__ __launch_bounds__(256) void decode_tokens_kernel(TokensArgs a) {
 
     const size_t bh0 = (size_t)b * a.n * a.H + h;        // (b, token 0, h)
     TokIn<PASSES> cur = load_token<T, D, PASSES, RAW>(a, bh0, c0, row);
-    // the inputs of the next two tokens in flight while a token is worked on
-    TokIn<PASSES> nx1 = a.n > 1 ? load_token<T, D, PASSES, RAW>(a, bh0 + a.H, c0, row) : cur;
+    // the next token's inputs in flight while a token is worked on; with one
+    // pass per workgroup (the recurrent prefill: few registers, a short
+    // step) the next two tokens' -- with two passes (the decode) the second
+    // set would cost two waves per SIMD
+    constexpr bool kTwoAhead = PASSES == 1;
+    TokIn<PASSES> nx1 = (kTwoAhead && a.n > 1) ? load_token<T, D, PASSES, RAW>(a, bh0 + a.H, c0, row) : cur;
     constexpr float kLog2e = 1.4426950408889634f;
     for (int t = 0; t < a.n; ++t) {
         const size_t bth = bh0 + (size_t)t * a.H;
-        const TokIn<PASSES> nx2 = t + 2 < a.n ? load_token<T, D, PASSES, RAW>(a, bth + 2 * a.H, c0, row) : nx1;
+        TokIn<PASSES> nx2;
+        if constexpr (kTwoAhead) nx2 = t + 2 < a.n ? load_token<T, D, PASSES, RAW>(a, bth + 2 * a.H, c0, row) : nx1;
+        else                     nx2 = t + 1 < a.n ? load_token<T, D, PASSES, RAW>(a, bth + a.H, c0, row) : cur;
         if (RAW) {
             // |k|^2 and |q|^2 over the LPR lanes of the row, then the
             // normalised vectors, beta and the gate logs from their logits
@@ -502,8 +508,12 @@ __global__ __launch_bounds__(256) void decode_tokens_kernel(TokensArgs a) {
             for (int p = 0; p < PASSES; ++p)
                 __builtin_nontemporal_store(S[p], reinterpret_cast<f32x4 *>(cp + (size_t)row[p] * D + c0));
         }
-        cur = nx1;
-        nx1 = nx2;
+        if constexpr (kTwoAhead) {
+            cur = nx1;
+            nx1 = nx2;
+        } else {
+            cur = nx2;
+        }
     }
     if (!a.ckpt) {
 #pragma unroll

@@ -102,6 +102,25 @@ def test_prefill_recurrent_fp32(gate, D, T):
 
 
 @pytest.mark.parametrize("gate", ["scalar", "channel"])
+@pytest.mark.parametrize("D,T", [(64, 3), (64, 70), (128, 9), (128, 33)])
+def test_prefill_recurrent_fp32_without_final_state(gate, D, T):
+    """Without a final state the fp32 prefill runs the one-workgroup kernel
+    (inputs loaded four tokens ahead; T < 4 and T not a multiple of 4 take
+    its tail loop), with a final state the token kernel: both against the
+    oracle, and their outputs against each other."""
+    announce("prefill fp32 %s D=%d T=%d, no final state" % (gate, D, T))
+    x = synthetic.prefill_inputs(2, T, 3, D, torch.float32, gate, seed=23, device=DEV)
+    o, ht = gdr.prefill(x["q"], x["k"], x["v"], x["g"], x["beta"], h0=x["h0"], scale=0.5,
+                        output_final_state=False)
+    sync()
+    assert ht is None
+    o_ref, _ = oracle.forward(x["q"], x["k"], x["v"], x["g"], x["beta"], h0=x["h0"], scale=0.5)
+    assert_close(o, o_ref, torch.float32, "o")
+    o2, _ = run_prefill(x, scale=0.5)
+    assert_close(o, o2, torch.float32, "o, the two kernels")
+
+
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("T", [1, 17, 64, 65, 200, 320])
 def test_prefill_chunked_bf16(gate, D, T):
