@@ -366,8 +366,10 @@ struct TokIn {
     float v[PASSES];
 };
 
-// RAW: the gate and beta slots hold the logits, still to be transformed
-template <typename T, int D, int PASSES, bool RAW>
+// RAW: the gate and beta slots hold the logits, still to be transformed.
+// CH: a channel gate (four values per lane), else a scalar gate (in lg.x,
+// broadcast where it is used, so that no copy waits for the load)
+template <typename T, int D, int PASSES, bool RAW, bool CH>
 __device__ __forceinline__ TokIn<PASSES> load_token(const TokensArgs &a, size_t bth, int c0,
                                                     const int (&row)[PASSES]) {
     TokIn<PASSES> x;
@@ -378,20 +380,12 @@ __device__ __forceinline__ TokIn<PASSES> load_token(const TokensArgs &a, size_t 
     x.q = Elem<T>::load4(qp + c0);
     if (RAW) {
         const T *xg = static_cast<const T *>(a.xg);
-        if (a.channel_gate) {
-            x.lg = Elem<T>::load4(xg + bth * D + c0);
-        } else {
-            const float s = Elem<T>::load(xg + bth);
-            x.lg = f32x4{s, s, s, s};
-        }
+        if constexpr (CH) x.lg = Elem<T>::load4(xg + bth * D + c0);
+        else              x.lg.x = Elem<T>::load(xg + bth);
         x.beta = Elem<T>::load(static_cast<const T *>(a.xb) + bth);
     } else {
-        if (a.channel_gate) {
-            x.lg = *reinterpret_cast<const f32x4 *>(a.g + bth * D + c0);
-        } else {
-            const float s = a.g[bth];
-            x.lg = f32x4{s, s, s, s};
-        }
+        if constexpr (CH) x.lg = *reinterpret_cast<const f32x4 *>(a.g + bth * D + c0);
+        else              x.lg.x = a.g[bth];
         x.beta = a.beta[bth];
     }
 #pragma unroll
@@ -399,7 +393,7 @@ __device__ __forceinline__ TokIn<PASSES> load_token(const TokensArgs &a, size_t 
     return x;
 }
 
-template <typename T, int D, int PASSES, bool RAW>
+template <typename T, int D, int PASSES, bool RAW, bool CH>
 __global__ __launch_bounds__(256) void decode_tokens_kernel(TokensArgs a) {
     using G = Geom<D>;
     constexpr int RPP = G::RPI;
@@ -431,24 +425,19 @@ __global__ __launch_bounds__(256) void decode_tokens_kernel(TokensArgs a) {
                            : __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(s0 + (size_t)row[p] * D + c0));
 
     const size_t bh0 = (size_t)b * a.n * a.H + h;        // (b, token 0, h)
-    TokIn<PASSES> cur = load_token<T, D, PASSES, RAW>(a, bh0, c0, row);
-    // the next token's inputs in flight while a token is worked on; with one
-    // pass per workgroup (the recurrent prefill: few registers, a short
-    // step) the next two tokens' -- with two passes (the decode) the second
-    // set would cost two waves per SIMD
-    constexpr bool kTwoAhead = PASSES == 1;
-    TokIn<PASSES> nx1 = (kTwoAhead && a.n > 1) ? load_token<T, D, PASSES, RAW>(a, bh0 + a.H, c0, row) : cur;
     constexpr float kLog2e = 1.4426950408889634f;
-    for (int t = 0; t < a.n; ++t) {
+    // a state row is one 16-lane DPP row at D = 64: VALU moves (row_ror:8
+    // is lane ^ 8 within the row; quad permutes and row_half_mirror sum each
+    // half) instead of LDS permutes
+    constexpr bool kDpp = G::LPR == 16;
+    auto step = [&](TokIn<PASSES> cur, int t) {
         const size_t bth = bh0 + (size_t)t * a.H;
-        TokIn<PASSES> nx2;
-        if constexpr (kTwoAhead) nx2 = t + 2 < a.n ? load_token<T, D, PASSES, RAW>(a, bth + 2 * a.H, c0, row) : nx1;
-        else                     nx2 = t + 1 < a.n ? load_token<T, D, PASSES, RAW>(a, bth + a.H, c0, row) : cur;
+        f32x4 lg = cur.lg;
         if (RAW) {
             // |k|^2 and |q|^2 over the LPR lanes of the row, then the
             // normalised vectors, beta and the gate logs from their logits
             float sk = dot4(cur.k, cur.k), sq = dot4(cur.q, cur.q);
-            if constexpr (G::LPR == 16) {
+            if constexpr (kDpp) {
                 sk = sum_group<16>(sk);
                 sq = sum_group<16>(sq);
             } else {
@@ -461,18 +450,18 @@ __global__ __launch_bounds__(256) void decode_tokens_kernel(TokensArgs a) {
             cur.k = cur.k * inv_norm(sk);
             cur.q = cur.q * inv_norm(sq);
             cur.beta = logistic(cur.beta);
-            cur.lg = f32x4{neg_softplus(cur.lg.x, a.gate_scale), neg_softplus(cur.lg.y, a.gate_scale),
-                           neg_softplus(cur.lg.z, a.gate_scale), neg_softplus(cur.lg.w, a.gate_scale)};
+            if constexpr (CH)
+                lg = f32x4{neg_softplus(lg.x, a.gate_scale), neg_softplus(lg.y, a.gate_scale),
+                           neg_softplus(lg.z, a.gate_scale), neg_softplus(lg.w, a.gate_scale)};
+            else
+                lg.x = neg_softplus(lg.x, a.gate_scale);
         }
-        const f32x4 av = f32x4{__builtin_amdgcn_exp2f(cur.lg.x * kLog2e), __builtin_amdgcn_exp2f(cur.lg.y * kLog2e),
-                               __builtin_amdgcn_exp2f(cur.lg.z * kLog2e), __builtin_amdgcn_exp2f(cur.lg.w * kLog2e)};
+        if constexpr (!CH) lg = f32x4{lg.x, lg.x, lg.x, lg.x};
+        const f32x4 av = f32x4{__builtin_amdgcn_exp2f(lg.x * kLog2e), __builtin_amdgcn_exp2f(lg.y * kLog2e),
+                               __builtin_amdgcn_exp2f(lg.z * kLog2e), __builtin_amdgcn_exp2f(lg.w * kLog2e)};
         const f32x4 ak = av * cur.k;
         const f32x4 aq = av * cur.q;
         float kq = dot4(cur.k, cur.q);
-        // a state row is one 16-lane DPP row at D = 64: VALU moves (row_ror:8
-        // is lane ^ 8 within the row; quad permutes and row_half_mirror sum
-        // each half) instead of LDS permutes
-        constexpr bool kDpp = G::LPR == 16;
         if constexpr (kDpp) {
             kq = sum_group<16>(kq);
         } else {
@@ -508,11 +497,44 @@ __global__ __launch_bounds__(256) void decode_tokens_kernel(TokensArgs a) {
             for (int p = 0; p < PASSES; ++p)
                 __builtin_nontemporal_store(S[p], reinterpret_cast<f32x4 *>(cp + (size_t)row[p] * D + c0));
         }
-        if constexpr (kTwoAhead) {
-            cur = nx1;
-            nx1 = nx2;
-        } else {
-            cur = nx2;
+    };
+    auto load = [&](int t) { return load_token<T, D, PASSES, RAW, CH>(a, bh0 + (size_t)t * a.H, c0, row); };
+    if constexpr (PASSES == 1) {
+        // the recurrent prefill's form (few registers, a short step): token
+        // t + 2's inputs are loaded while token t is worked on, into three
+        // register sets taken in turn -- token u lives in set u mod 3 -- so
+        // that no set is copied while its loads are in flight
+        constexpr int AH = 2, NS = 3;
+        TokIn<PASSES> in[NS];
+#pragma unroll
+        for (int i = 0; i < AH; ++i)
+            if (i < a.n) in[i] = load(i);
+        int t = 0;
+        // every load of a trip is in range here, so none is conditional
+        for (; t + AH + NS <= a.n; t += NS) {
+#pragma unroll
+            for (int i = 0; i < NS; ++i) {
+                in[(i + AH) % NS] = load(t + i + AH);
+                step(in[i], t + i);
+            }
+        }
+        for (; t < a.n; t += NS) {
+#pragma unroll
+            for (int i = 0; i < NS; ++i) {
+                if (t + i < a.n) {
+                    if (t + i + AH < a.n) in[(i + AH) % NS] = load(t + i + AH);
+                    step(in[i], t + i);
+                }
+            }
+        }
+    } else {
+        // the decode (two passes of rows): the next token's inputs in flight
+        // while a token is worked on; more sets would cost waves per SIMD
+        TokIn<PASSES> cur = load(0);
+        for (int t = 0; t < a.n; ++t) {
+            const TokIn<PASSES> nxt = t + 1 < a.n ? load(t + 1) : cur;
+            step(cur, t);
+            cur = nxt;
         }
     }
     if (!a.ckpt) {
@@ -652,16 +674,26 @@ hipError_t launch_decode(bool bf16_io, int D, const DecodeArgs &a,
     return hipGetLastError();
 }
 
-template <bool RAW>
-void launch_tokens(bool bf16_io, int D, const TokensArgs &a, dim3 grid, hipStream_t s) {
-    constexpr int P = GDR_DECODE_PASSES;
+// the token kernel for a dtype, D, gate kind and raw flag, P passes of rows
+template <int P, bool RAW, bool CH>
+void launch_tokens_p(bool bf16_io, int D, const TokensArgs &a, dim3 grid, hipStream_t s) {
     dim3 block(256);
     if (bf16_io) {
-        if (D == 128) hipLaunchKernelGGL((decode_tokens_kernel<bf16, 128, P, RAW>), grid, block, 0, s, a);
-        else          hipLaunchKernelGGL((decode_tokens_kernel<bf16, 64, P, RAW>), grid, block, 0, s, a);
+        if (D == 128) hipLaunchKernelGGL((decode_tokens_kernel<bf16, 128, P, RAW, CH>), grid, block, 0, s, a);
+        else          hipLaunchKernelGGL((decode_tokens_kernel<bf16, 64, P, RAW, CH>), grid, block, 0, s, a);
     } else {
-        if (D == 128) hipLaunchKernelGGL((decode_tokens_kernel<float, 128, P, RAW>), grid, block, 0, s, a);
-        else          hipLaunchKernelGGL((decode_tokens_kernel<float, 64, P, RAW>), grid, block, 0, s, a);
+        if (D == 128) hipLaunchKernelGGL((decode_tokens_kernel<float, 128, P, RAW, CH>), grid, block, 0, s, a);
+        else          hipLaunchKernelGGL((decode_tokens_kernel<float, 64, P, RAW, CH>), grid, block, 0, s, a);
+    }
+}
+template <int P>
+void launch_tokens_any(bool bf16_io, int D, const TokensArgs &a, dim3 grid, hipStream_t s, bool raw) {
+    if (raw) {
+        if (a.channel_gate) launch_tokens_p<P, true, true>(bf16_io, D, a, grid, s);
+        else                launch_tokens_p<P, true, false>(bf16_io, D, a, grid, s);
+    } else {
+        if (a.channel_gate) launch_tokens_p<P, false, true>(bf16_io, D, a, grid, s);
+        else                launch_tokens_p<P, false, false>(bf16_io, D, a, grid, s);
     }
 }
 
@@ -673,8 +705,7 @@ hipError_t launch_decode_tokens(bool bf16_io, int D, const TokensArgs &a, hipStr
     const long long blocks = (long long)a.B * a.H * per_head;
     if (blocks >= (1LL << 31)) return hipErrorInvalidValue;
     dim3 grid((unsigned)blocks);
-    if (raw) launch_tokens<true>(bf16_io, D, a, grid, s);
-    else     launch_tokens<false>(bf16_io, D, a, grid, s);
+    launch_tokens_any<P>(bf16_io, D, a, grid, s, raw);
     return hipGetLastError();
 }
 
@@ -709,16 +740,7 @@ hipError_t launch_prefill_recurrent(bool bf16_io, int D, const PrefillArgs &a,
         t.xg = a.xg; t.xb = a.xb; t.gate_scale = a.gate_scale;
         const long long tb = blocks * (D == 128 ? 128 / Geom<128>::RPI : 64 / Geom<64>::RPI);
         if (tb >= (1LL << 31)) return hipErrorInvalidValue;
-        dim3 tgrid((unsigned)tb), tblock(256);
-#define GDR_TOKENS1(TT, DD, RR) hipLaunchKernelGGL((decode_tokens_kernel<TT, DD, 1, RR>), tgrid, tblock, 0, s, t)
-        if (a.xg) {
-            if (bf16_io) { if (D == 128) GDR_TOKENS1(bf16, 128, true);  else GDR_TOKENS1(bf16, 64, true); }
-            else         { if (D == 128) GDR_TOKENS1(float, 128, true); else GDR_TOKENS1(float, 64, true); }
-        } else {
-            if (bf16_io) { if (D == 128) GDR_TOKENS1(bf16, 128, false);  else GDR_TOKENS1(bf16, 64, false); }
-            else         { if (D == 128) GDR_TOKENS1(float, 128, false); else GDR_TOKENS1(float, 64, false); }
-        }
-#undef GDR_TOKENS1
+        launch_tokens_any<1>(bf16_io, D, t, dim3((unsigned)tb), s, a.xg != nullptr);
         return hipGetLastError();
     }
     dim3 grid((unsigned)blocks), block(256);
