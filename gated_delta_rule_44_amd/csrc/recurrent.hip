@@ -67,31 +67,25 @@ __device__ inline int result_row(int lane, int w) {
 // qp, kp, vp point at the head's D-vector for the token, gp at its gate logs
 // (D values for a channel gate, one for a scalar gate; fp32, or type T
 // logits with RAW), bp at its beta (RAW: a type T logit)
-template <typename T, int D, bool RAW>
+template <typename T, int D, bool RAW, bool CH>
 __device__ inline StepIn step_load(const T *qp, const T *kp, const T *vp, const void *gp,
-                                   const void *bp, bool channel, int lane, int w) {
+                                   const void *bp, int lane, int w) {
     using G = Geom<D>;
     const int c0 = (lane % G::LPR) * 4;
     StepIn x;
     x.kv = Elem<T>::load4(kp + c0);
     x.qv = Elem<T>::load4(qp + c0);
+    // a scalar gate (CH false) is loaded into lg.x alone and broadcast
+    // where it is used, so that no copy waits for the load
     if (RAW) {
         const T *xg = static_cast<const T *>(gp);
-        if (channel) {
-            x.lg = Elem<T>::load4(xg + c0);
-        } else {
-            const float s = Elem<T>::load(xg);
-            x.lg = f32x4{s, s, s, s};
-        }
+        if constexpr (CH) x.lg = Elem<T>::load4(xg + c0);
+        else              x.lg.x = Elem<T>::load(xg);
         x.beta = Elem<T>::load(static_cast<const T *>(bp));
     } else {
         const float *g = static_cast<const float *>(gp);
-        if (channel) {
-            x.lg = *reinterpret_cast<const f32x4 *>(g + c0);
-        } else {
-            const float s = g[0];
-            x.lg = f32x4{s, s, s, s};
-        }
+        if constexpr (CH) x.lg = *reinterpret_cast<const f32x4 *>(g + c0);
+        else              x.lg.x = g[0];
         x.beta = *static_cast<const float *>(bp);
     }
     x.vrow = Elem<T>::load(vp + result_row<D>(lane, w));
@@ -133,7 +127,7 @@ __device__ inline void bcast_rows(float u, float (&um)[M]) {
 
 // One token's update of the state slice S held by this thread, from the
 // token's inputs; the output is written to op.
-template <typename T, int D, bool RAW>
+template <typename T, int D, bool RAW, bool CH>
 __device__ inline void head_step(f32x4 (&S)[Geom<D>::M], StepIn in, float scale,
                                  float gate_scale, T *op, int lane, int w) {
     using G = Geom<D>;
@@ -142,8 +136,11 @@ __device__ inline void head_step(f32x4 (&S)[Geom<D>::M], StepIn in, float scale,
     f32x4 kv = in.kv, qv = in.qv, lg = in.lg;
     float beta = in.beta;
     if (RAW) {
-        lg = f32x4{neg_softplus(lg.x, gate_scale), neg_softplus(lg.y, gate_scale),
-                   neg_softplus(lg.z, gate_scale), neg_softplus(lg.w, gate_scale)};
+        if constexpr (CH)
+            lg = f32x4{neg_softplus(lg.x, gate_scale), neg_softplus(lg.y, gate_scale),
+                       neg_softplus(lg.z, gate_scale), neg_softplus(lg.w, gate_scale)};
+        else
+            lg.x = neg_softplus(lg.x, gate_scale);
         beta = logistic(beta);
         float sk = dot4(kv, kv), sq = dot4(qv, qv);
         if constexpr (kDpp) {
@@ -159,6 +156,7 @@ __device__ inline void head_step(f32x4 (&S)[Geom<D>::M], StepIn in, float scale,
         kv = kv * inv_norm(sk);
         qv = qv * inv_norm(sq);
     }
+    if constexpr (!CH) lg = f32x4{lg.x, lg.x, lg.x, lg.x};
     constexpr float kLog2e = 1.4426950408889634f;
     const f32x4 a = f32x4{__builtin_amdgcn_exp2f(lg.x * kLog2e),
                           __builtin_amdgcn_exp2f(lg.y * kLog2e),
@@ -578,7 +576,7 @@ __global__ __launch_bounds__(256) void commit_kernel(TokensArgs a, const int32_t
 // ---------------------------------------------------------------------------
 // Prefill in the recurrent form: one workgroup per (sequence, head) walks
 // its tokens in order with the state resident in registers.
-template <typename T, int D, bool RAW>
+template <typename T, int D, bool RAW, bool CH>
 __global__ __launch_bounds__(256) void prefill_recurrent_kernel(PrefillArgs a) {
     using G = Geom<D>;
     const int lane = threadIdx.x & 63;
@@ -603,8 +601,8 @@ __global__ __launch_bounds__(256) void prefill_recurrent_kernel(PrefillArgs a) {
                    : f32x4{0.f, 0.f, 0.f, 0.f};
 
     const size_t tok = (size_t)a.H * D;                 // q/k/v/o token stride
-    const size_t gtok = a.channel_gate ? tok : (size_t)a.H;
-    const size_t goff = a.channel_gate ? (size_t)h * D : (size_t)h;
+    const size_t gtok = CH ? tok : (size_t)a.H;
+    const size_t goff = CH ? (size_t)h * D : (size_t)h;
     const T *q = static_cast<const T *>(a.q) + h * D;
     const T *k = static_cast<const T *>(a.k) + h * D;
     const T *v = static_cast<const T *>(a.v) + h * D;
@@ -613,13 +611,13 @@ __global__ __launch_bounds__(256) void prefill_recurrent_kernel(PrefillArgs a) {
     // register sets, so that the load latency is paid once, not per token)
     auto load = [&](long long t) -> StepIn {
         if (RAW)
-            return step_load<T, D, true>(q + t * tok, k + t * tok, v + t * tok,
+            return step_load<T, D, true, CH>(q + t * tok, k + t * tok, v + t * tok,
                                          static_cast<const T *>(a.xg) + t * gtok + goff,
                                          static_cast<const T *>(a.xb) + t * a.H + h,
-                                         a.channel_gate != 0, lane, w);
-        return step_load<T, D, false>(q + t * tok, k + t * tok, v + t * tok,
+                                         lane, w);
+        return step_load<T, D, false, CH>(q + t * tok, k + t * tok, v + t * tok,
                                       a.g + t * gtok + goff, a.beta + t * a.H + h,
-                                      a.channel_gate != 0, lane, w);
+                                      lane, w);
     };
     constexpr int P = 4;
     StepIn in[P];
@@ -632,7 +630,7 @@ __global__ __launch_bounds__(256) void prefill_recurrent_kernel(PrefillArgs a) {
     for (; t + 2 * P <= t1; t += P) {
 #pragma unroll
         for (int i = 0; i < P; ++i) {
-            head_step<T, D, RAW>(S, in[i], a.scale, a.gate_scale, o + (t + i) * tok, lane, w);
+            head_step<T, D, RAW, CH>(S, in[i], a.scale, a.gate_scale, o + (t + i) * tok, lane, w);
             in[i] = load(t + i + P);
         }
     }
@@ -640,7 +638,7 @@ __global__ __launch_bounds__(256) void prefill_recurrent_kernel(PrefillArgs a) {
 #pragma unroll
         for (int i = 0; i < P; ++i) {
             if (t + i < t1) {
-                head_step<T, D, RAW>(S, in[i], a.scale, a.gate_scale, o + (t + i) * tok, lane, w);
+                head_step<T, D, RAW, CH>(S, in[i], a.scale, a.gate_scale, o + (t + i) * tok, lane, w);
                 if (t + i + P < t1) in[i] = load(t + i + P);
             }
         }
@@ -744,23 +742,19 @@ hipError_t launch_prefill_recurrent(bool bf16_io, int D, const PrefillArgs &a,
         return hipGetLastError();
     }
     dim3 grid((unsigned)blocks), block(256);
+#define GDR_REC(TT, DD, RR)                                                                   \
+    do {                                                                                      \
+        if (a.channel_gate) hipLaunchKernelGGL((prefill_recurrent_kernel<TT, DD, RR, true>), grid, block, 0, s, a); \
+        else                hipLaunchKernelGGL((prefill_recurrent_kernel<TT, DD, RR, false>), grid, block, 0, s, a); \
+    } while (0)
     if (a.xg) {
-        if (bf16_io) {
-            if (D == 128) hipLaunchKernelGGL((prefill_recurrent_kernel<bf16, 128, true>), grid, block, 0, s, a);
-            else          hipLaunchKernelGGL((prefill_recurrent_kernel<bf16, 64, true>), grid, block, 0, s, a);
-        } else {
-            if (D == 128) hipLaunchKernelGGL((prefill_recurrent_kernel<float, 128, true>), grid, block, 0, s, a);
-            else          hipLaunchKernelGGL((prefill_recurrent_kernel<float, 64, true>), grid, block, 0, s, a);
-        }
+        if (bf16_io) { if (D == 128) GDR_REC(bf16, 128, true);  else GDR_REC(bf16, 64, true); }
+        else         { if (D == 128) GDR_REC(float, 128, true); else GDR_REC(float, 64, true); }
     } else {
-        if (bf16_io) {
-            if (D == 128) hipLaunchKernelGGL((prefill_recurrent_kernel<bf16, 128, false>), grid, block, 0, s, a);
-            else          hipLaunchKernelGGL((prefill_recurrent_kernel<bf16, 64, false>), grid, block, 0, s, a);
-        } else {
-            if (D == 128) hipLaunchKernelGGL((prefill_recurrent_kernel<float, 128, false>), grid, block, 0, s, a);
-            else          hipLaunchKernelGGL((prefill_recurrent_kernel<float, 64, false>), grid, block, 0, s, a);
-        }
+        if (bf16_io) { if (D == 128) GDR_REC(bf16, 128, false);  else GDR_REC(bf16, 64, false); }
+        else         { if (D == 128) GDR_REC(float, 128, false); else GDR_REC(float, 64, false); }
     }
+#undef GDR_REC
     return hipGetLastError();
 }
 
