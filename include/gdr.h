@@ -140,7 +140,7 @@ gdr_status gdr_prefill_chunked(enum gdr_dtype dt, enum gdr_gate gk, int B, int T
  *
  * Calls whose workspace (gdr_prefill_workspace_bytes(dt, gk, B, B*T, H))
  * would exceed GDR_NOALLOC_MAX_BYTES return GDR_EUNSUPPORTED and launch
- * nothing; GDN B=4 H=16 T=4096 needs 23 MB.  Every call on one GPU uses that
+ * nothing; GDN B=4 H=16 T=4096 needs 25 MB.  Every call on one GPU uses that
  * GPU's one array: calls that overlap on one GPU (two streams, two threads)
  * race and must be ordered by the caller.  Nothing in the array needs
  * clearing between calls: each call writes every byte it reads.  The device
