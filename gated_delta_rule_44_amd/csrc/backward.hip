@@ -1068,17 +1068,95 @@ size_t backward_record_bytes(int D) {
     return D == 128 ? ChainRec<128>::BYTES : ChainRec<64>::BYTES;
 }
 
-// The chunk factorisation above (k e^{-b} inside a chunk) holds while no
-// channel decays by more than e^80 over a chunk.  The forward pass marks
-// the (sequence, head) pairs where one does (unit_wide); their gradients --
-// all of them, as the state gradient passes through the chunk to every
-// earlier one -- are set to NaN here rather than left wrong.  One
-// workgroup per (pair, part of its tokens).
-constexpr int kPoisonParts = 16;
-template <int D>
-__global__ __launch_bounds__(256) void poison_kernel(BwdArgs a) {
-    const long long unit = blockIdx.x / kPoisonParts;
-    const int part = blockIdx.x % kPoisonParts;
+// ===========================================================================
+// Pairs beyond the chunk factorisation
+// ===========================================================================
+// The chunk-local gradients factor each chunk from its first token
+// (k e^{-b} inside a chunk), which holds while no channel decays by more
+// than e^80 over a chunk.  The forward pass marks the (sequence, head) pairs
+// where one does (unit_wide); every gradient of such a pair is recomputed
+// here, exactly, by the adjoint of the token recurrence in fp32, from the
+// chunk-entering states the forward stored (the chunked forward itself is
+// exact for every gate).  Per value row i of the state (rows never mix),
+// with s = s_{t-1}, u = a_t (.) s, e = v_ti - u.k_t,
+// s_t = u + beta_t e k_t and o_ti = scale s_t.q_t, and G the gradient of
+// s_t through everything after token t:
+//     G' = G + scale do_ti q_t           dq_t += scale do_ti s_t
+//     dv_ti = beta_t (G'.k_t)            dbeta_t += e (G'.k_t)
+//     dk_t += beta_t e G' - beta_t (G'.k_t) u
+//     du = G' - beta_t (G'.k_t) k_t      dg_t += du (.) u   (summed over
+//     G <- a_t (.) du                    channels for the scalar gate)
+// so dq, dk, dg and dbeta are sums over the rows and dv, dh0 are row-local.
+// A workgroup (16 waves) takes 64 rows of one pair, 16 lanes to a row with
+// D/16 columns each; a chunk is walked backwards in sub-blocks of kWideSub
+// tokens, each sub-block's entering state recomputed forward from the
+// chunk's stored state (kWideSub token states stay in registers).  The
+// column sums over the 64 rows go through LDS; at D = 128 the two
+// workgroups of a pair add theirs into outputs the zeroing kernel cleared
+// -- two fp32 additions onto zero, whose result does not depend on their
+// order, so the gradients are the same on every run.
+constexpr int kWideSub = 4;
+
+template <int D, bool CH> struct WideSmem {
+    static constexpr int NA = CH ? D : 1;
+    static constexpr int NV = CH ? 3 : 2;          // column sums: dq, dk (, dg)
+    alignas(16) float a[C * NA];                    // e^g per token (and channel)
+    alignas(16) bf16 k[C * D], q[C * D];
+    alignas(16) float v[C * 64], dout[C * 64];      // the workgroup's 64 value rows
+    alignas(16) float beta[C];
+    alignas(16) float red[2][16][NV * D];           // per-wave column sums, two tokens
+    alignas(16) float reds[2][16][2];               // per-wave dbeta (, scalar dg)
+};
+
+template <int VPL>
+__device__ inline void lds_row(const bf16 *p, float (&x)[VPL]) {
+    if constexpr (VPL == 8) {
+        const bf16x8 r = *reinterpret_cast<const bf16x8 *>(p);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = (float)r[j];
+    } else {
+        const bf16x4 r = *reinterpret_cast<const bf16x4 *>(p);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[j] = (float)r[j];
+    }
+}
+
+template <int D, bool CH>
+__device__ inline void wide_gate(const WideSmem<D, CH> &sm, int t, int j0, float (&at)[D / 16]) {
+#pragma unroll
+    for (int j = 0; j < D / 16; ++j) at[j] = CH ? sm.a[t * D + j0 + j] : sm.a[t];
+}
+
+// one token forward on a lane's part of a row: s <- s_t; returns e
+template <int D, bool CH>
+__device__ inline float wide_fwd(const WideSmem<D, CH> &sm, float (&s)[D / 16], int t, int rl,
+                                 int j0) {
+    constexpr int VPL = D / 16;
+    float kk[VPL], at[VPL];
+    lds_row<VPL>(sm.k + t * D + j0, kk);
+    wide_gate<D, CH>(sm, t, j0, at);
+    float kd = 0.f;
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+        s[j] *= at[j];
+        kd += s[j] * kk[j];
+    }
+    kd = sum_group<16>(kd);
+    const float e = sm.v[t * 64 + rl] - kd;
+    const float be = sm.beta[t] * e;
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) s[j] += be * kk[j];
+    return e;
+}
+
+template <int D, bool CH>
+__global__ __launch_bounds__(1024) void wide_backward_kernel(BwdArgs a) {
+    constexpr int P = D / 64;
+    constexpr int VPL = D / 16;
+    constexpr int NV = WideSmem<D, CH>::NV;
+    __shared__ WideSmem<D, CH> sm;
+    const long long unit = blockIdx.x / P;
+    const int part = blockIdx.x % P;
     if (unit >= (long long)a.B * a.H || !a.unit_wide[unit]) return;
     const int n = (int)(unit / a.H), h = (int)(unit % a.H);
     long long t0, len;
@@ -1089,22 +1167,186 @@ __global__ __launch_bounds__(256) void poison_kernel(BwdArgs a) {
         t0 = (long long)n * a.T;
         len = a.T;
     }
-    const float nan = __builtin_nanf("");
-    const long long per = (len + kPoisonParts - 1) / kPoisonParts;
+    const long long cb = a.cu_seqlens ? (long long)a.chunk_base[n] : (long long)n * a.nc;
+    const int nch = (int)((len + C - 1) / C);
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const int rl = 4 * w + (lane >> 4);            // row within the workgroup's 64
+    const int r = 64 * part + rl;                  // value row of the state
+    const int j0 = VPL * (lane & 15);
+    const size_t DD = (size_t)D * D;
+    const bf16 *qg = static_cast<const bf16 *>(a.q), *kg = static_cast<const bf16 *>(a.k);
+    const bf16 *vg = static_cast<const bf16 *>(a.v), *dog = static_cast<const bf16 *>(a.dout);
+    float G[VPL];
+#pragma unroll
+    for (int j = 0; j < VPL; ++j)
+        G[j] = a.dht ? a.dht[(size_t)unit * DD + (size_t)r * D + j0 + j] : 0.f;
+    int par = 0;
+    for (int c = nch - 1; c >= 0; --c) {
+        const int L = (int)(len - (long long)C * c < C ? len - (long long)C * c : C);
+        const long long tc = t0 + (long long)C * c;
+        __syncthreads();                           // the previous chunk's reads are done
+        // stage the chunk: k, q rows (bf16), e^g, this workgroup's v and do
+        // columns (fp32), beta; tokens past L as zeros
+        for (int x = tid; x < C * D / 8; x += 1024) {
+            const int t = x / (D / 8), c8 = x % (D / 8);
+            bf16x8 kv = {}, qv = {};
+            if (t < L) {
+                const size_t o = ((size_t)(tc + t) * a.H + h) * D + 8 * c8;
+                kv = *reinterpret_cast<const bf16x8 *>(kg + o);
+                qv = *reinterpret_cast<const bf16x8 *>(qg + o);
+            }
+            *reinterpret_cast<bf16x8 *>(sm.k + t * D + 8 * c8) = kv;
+            *reinterpret_cast<bf16x8 *>(sm.q + t * D + 8 * c8) = qv;
+        }
+        if (CH) {
+            for (int x = tid; x < C * D / 4; x += 1024) {
+                const int t = x / (D / 4), c4 = x % (D / 4);
+                f32x4 gv = {0.f, 0.f, 0.f, 0.f};
+                if (t < L)
+                    gv = *reinterpret_cast<const f32x4 *>(a.g + ((size_t)(tc + t) * a.H + h) * D + 4 * c4);
+                f32x4 av;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) av[u] = ex(__builtin_fmaxf(gv[u], kGateFloor));
+                *reinterpret_cast<f32x4 *>(sm.a + t * D + 4 * c4) = av;
+            }
+        } else if (tid < C) {
+            sm.a[tid] = tid < L ? ex(__builtin_fmaxf(a.g[(size_t)(tc + tid) * a.H + h], kGateFloor)) : 1.f;
+        }
+        for (int x = tid; x < C * 8; x += 1024) {  // 64 rows = 8 pieces of 8 per token
+            const int t = x >> 3, c8 = x & 7;
+            bf16x8 vv = {}, dv = {};
+            if (t < L) {
+                const size_t o = ((size_t)(tc + t) * a.H + h) * D + 64 * part + 8 * c8;
+                vv = *reinterpret_cast<const bf16x8 *>(vg + o);
+                dv = *reinterpret_cast<const bf16x8 *>(dog + o);
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                sm.v[t * 64 + 8 * c8 + u] = (float)vv[u];
+                sm.dout[t * 64 + 8 * c8 + u] = (float)dv[u] * a.scale;
+            }
+        }
+        if (tid < C) sm.beta[tid] = tid < L ? a.beta[(size_t)(tc + tid) * a.H + h] : 0.f;
+        __syncthreads();
+        float S0[VPL];
+        {
+            const float *sp = a.states + ((size_t)(cb + c) * a.H + h) * DD + (size_t)r * D + j0;
+#pragma unroll
+            for (int j = 0; j < VPL; ++j) S0[j] = sp[j];
+        }
+        for (int sb = (L - 1) / kWideSub; sb >= 0; --sb) {
+            float s[VPL];
+#pragma unroll
+            for (int j = 0; j < VPL; ++j) s[j] = S0[j];
+            for (int t = 0; t < kWideSub * sb; ++t) wide_fwd<D, CH>(sm, s, t, rl, j0);
+            const int nt = L - kWideSub * sb < kWideSub ? L - kWideSub * sb : kWideSub;
+            float st[kWideSub][VPL], e[kWideSub];
+#pragma unroll
+            for (int u = 0; u < kWideSub; ++u) {
+                if (u < nt) {
+#pragma unroll
+                    for (int j = 0; j < VPL; ++j) st[u][j] = s[j];
+                    e[u] = wide_fwd<D, CH>(sm, s, kWideSub * sb + u, rl, j0);
+                }
+            }
+#pragma unroll
+            for (int u = kWideSub - 1; u >= 0; --u) {
+                if (u >= nt) continue;
+                const int t = kWideSub * sb + u;
+                const size_t row = (size_t)(tc + t) * a.H + h;
+                float kk[VPL], qq[VPL], at[VPL];
+                lds_row<VPL>(sm.k + t * D + j0, kk);
+                lds_row<VPL>(sm.q + t * D + j0, qq);
+                wide_gate<D, CH>(sm, t, j0, at);
+                const float b = sm.beta[t], dor = sm.dout[t * 64 + rl], eu = e[u];
+                // each column sum is taken over the wave's four rows and
+                // stored as soon as it is formed (few values live at once)
+                float uu[VPL], gk = 0.f;
+#pragma unroll
+                for (int j = 0; j < VPL; ++j) {
+                    uu[j] = at[j] * st[u][j];
+                    const float pq = swap_sum32(swap_sum16(dor * (uu[j] + b * eu * kk[j])));
+                    if (lane < 16) sm.red[par][w][j0 + j] = pq;       // scale do_ti s_t
+                    G[j] += dor * qq[j];
+                    gk += G[j] * kk[j];
+                }
+                gk = sum_group<16>(gk);
+                if ((lane & 15) == 0) a.dv[row * D + r] = b * gk;
+                const float de = b * gk, be = b * eu;
+                float pgs = 0.f;
+#pragma unroll
+                for (int j = 0; j < VPL; ++j) {
+                    const float pk = swap_sum32(swap_sum16(be * G[j] - de * uu[j]));
+                    if (lane < 16) sm.red[par][w][D + j0 + j] = pk;
+                    const float du = G[j] - de * kk[j];
+                    if (CH) {
+                        const float pg = swap_sum32(swap_sum16(du * uu[j]));
+                        if (lane < 16) sm.red[par][w][2 * D + j0 + j] = pg;
+                    } else {
+                        pgs += du * uu[j];
+                    }
+                    G[j] = at[j] * du;
+                }
+                const float pb = swap_sum32(swap_sum16(eu * gk));
+                if (!CH) pgs = swap_sum32(swap_sum16(sum_group<16>(pgs)));
+                if (lane == 0) {
+                    sm.reds[par][w][0] = pb;
+                    sm.reds[par][w][1] = pgs;
+                }
+                __syncthreads();
+                if (tid < NV * D) {
+                    const int comp = tid / D, j = tid % D;
+                    float sum = 0.f;
+#pragma unroll
+                    for (int x = 0; x < 16; ++x) sum += sm.red[par][x][tid];
+                    float *dst = comp == 0 ? a.dq : comp == 1 ? a.dk : a.dg;
+                    atomicAdd(dst + row * D + j, sum);
+                } else if (tid < NV * D + (CH ? 1 : 2)) {
+                    const int comp = tid - NV * D;
+                    float sum = 0.f;
+#pragma unroll
+                    for (int x = 0; x < 16; ++x) sum += sm.reds[par][x][comp];
+                    atomicAdd(comp == 0 ? a.dbeta + row : a.dg + row, sum);
+                }
+                par ^= 1;
+            }
+        }
+    }
+    if (a.dh0) {
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) a.dh0[(size_t)unit * DD + (size_t)r * D + j0 + j] = G[j];
+    }
+}
+
+// Clears dq, dk, dg and dbeta of the marked pairs (the wide kernel adds into
+// them).  One workgroup per (pair, part of its tokens).
+constexpr int kZeroParts = 16;
+template <int D>
+__global__ __launch_bounds__(256) void wide_zero_kernel(BwdArgs a) {
+    const long long unit = blockIdx.x / kZeroParts;
+    const int part = blockIdx.x % kZeroParts;
+    if (unit >= (long long)a.B * a.H || !a.unit_wide[unit]) return;
+    const int n = (int)(unit / a.H), h = (int)(unit % a.H);
+    long long t0, len;
+    if (a.cu_seqlens) {
+        t0 = a.cu_seqlens[n];
+        len = a.cu_seqlens[n + 1] - t0;
+    } else {
+        t0 = (long long)n * a.T;
+        len = a.T;
+    }
+    const long long per = (len + kZeroParts - 1) / kZeroParts;
     const long long r0 = part * per, r1 = r0 + per < len ? r0 + per : len;
     for (long long idx = r0 * D + threadIdx.x; idx < r1 * D; idx += 256) {
         const long long t = t0 + idx / D;
         const int j = (int)(idx % D);
         const size_t o = ((size_t)t * a.H + h) * D + j;
-        a.dq[o] = nan;
-        a.dk[o] = nan;
-        a.dv[o] = nan;
-        if (a.channel_gate) a.dg[o] = nan;
-        else if (j == 0) a.dg[(size_t)t * a.H + h] = nan;
-        if (j == 0) a.dbeta[(size_t)t * a.H + h] = nan;
+        a.dq[o] = 0.f;
+        a.dk[o] = 0.f;
+        if (a.channel_gate) a.dg[o] = 0.f;
+        else if (j == 0) a.dg[(size_t)t * a.H + h] = 0.f;
+        if (j == 0) a.dbeta[(size_t)t * a.H + h] = 0.f;
     }
-    if (a.dh0 && part == 0)
-        for (int e = threadIdx.x; e < D * D; e += 256) a.dh0[(size_t)unit * D * D + e] = nan;
 }
 
 hipError_t launch_backward(int D, const BwdArgs &a, hipStream_t s) {
@@ -1128,10 +1370,20 @@ hipError_t launch_backward(int D, const BwdArgs &a, hipStream_t s) {
         else                hipLaunchKernelGGL((chunk_grad_kernel<64, false, false>), gc, blk8, 0, s, a);
     }
     if (a.unit_wide) {
-        if (heads * kPoisonParts >= (1LL << 31)) return hipErrorInvalidValue;
-        dim3 gp((unsigned)(heads * kPoisonParts));
-        if (D == 128) hipLaunchKernelGGL(poison_kernel<128>, gp, dim3(256), 0, s, a);
-        else          hipLaunchKernelGGL(poison_kernel<64>, gp, dim3(256), 0, s, a);
+        // the marked pairs again, exactly: their sums cleared, then the
+        // token-level adjoint
+        if (heads * kZeroParts >= (1LL << 31) || heads * (D / 64) >= (1LL << 31))
+            return hipErrorInvalidValue;
+        dim3 gz((unsigned)(heads * kZeroParts)), gw((unsigned)(heads * (D / 64)));
+        if (D == 128) {
+            hipLaunchKernelGGL(wide_zero_kernel<128>, gz, dim3(256), 0, s, a);
+            if (a.channel_gate) hipLaunchKernelGGL((wide_backward_kernel<128, true>), gw, dim3(1024), 0, s, a);
+            else                hipLaunchKernelGGL((wide_backward_kernel<128, false>), gw, dim3(1024), 0, s, a);
+        } else {
+            hipLaunchKernelGGL(wide_zero_kernel<64>, gz, dim3(256), 0, s, a);
+            if (a.channel_gate) hipLaunchKernelGGL((wide_backward_kernel<64, true>), gw, dim3(1024), 0, s, a);
+            else                hipLaunchKernelGGL((wide_backward_kernel<64, false>), gw, dim3(1024), 0, s, a);
+        }
     }
     return hipGetLastError();
 }

@@ -384,12 +384,15 @@ gdr_status gdr_decode_tokens_fused(enum gdr_dtype dt, enum gdr_gate gk, int B, i
  * state gradient and dh0; and one MFMA workgroup per (chunk, head) for the
  * chunk-local gradients.  fp32 inputs are GDR_EUNSUPPORTED.
  * Numerics: bf16 operands with fp32 accumulation, as the forward.
- * Range: g is raised to -30 as in the forward, so gates of zero are
- * allowed.  The chunk-local gradients factor each chunk from its first
- * token, which holds while every gate channel decays by at most e^80 over
- * the chunk; a (sequence, head) with a chunk that decays further gets NaN in
- * all its gradients (its token rows of dq, dk, dv, dg, dbeta and its dh0),
- * never wrong finite values.  The other pairs are unaffected.
+ * Range: every gate g in [-inf, 0]; g is raised to -30 as in the forward.
+ * The chunk-local gradients factor each chunk from its first token, which
+ * holds while every gate channel decays by at most e^80 over the chunk; the
+ * forward marks each (sequence, head) with a chunk that decays further, and
+ * all gradients of the marked pairs are then recomputed by the adjoint of
+ * the token recurrence in fp32 from the stored chunk-entering states (about
+ * 15 times the in-range cost for a batch where every pair is marked).  The
+ * results are the same bits on every run except dg and dbeta of in-range
+ * pairs, which are summed in LDS float atomics (equal to fp32 rounding).
  */
 size_t gdr_backward_workspace_bytes(enum gdr_gate gk, int B, int T, int H, int Dk, int Dv);
 
