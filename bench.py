@@ -33,13 +33,17 @@ Times: each step is bracketed by HIP events on the launch stream; `value`
 and `ms_per_step` come from the median step, `roofline.achieved` from the
 mean (the average call time, as rocprofv3 reports kernel averages).
 Defaults: 100 warmup steps and 200 timed steps (a fifth of each for the
-decode and varlen workloads): the GPU reaches its steady clock only after
-about a hundred prefill calls, so shorter warm-ups time part of the ramp.
+decode and varlen workloads).  The GPU reaches its steady clock only after
+about a hundred prefill calls (with 5 warm-up steps the headline's median
+is about 6 % slower), so `--settle` (default 100) untimed headline calls
+run before the warm-up steps; the line reports them as
+`clock_settle_calls`.  The workloads after the headline find the clock
+settled.
 The secondary list also carries the latency of one fp32 call on the GDN
 recurrent workload (B=1 H=1 T=64 d=64), and the oracle's rate on the other
 workloads in full beside the GPU's.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle N]
                        [--only-headline] [--no-cpu-baseline]
                        [--only {kda_prefill,decode,varlen,draft,varlen_pool,fused_gdn,fused_kda,
                                 backward_gdn,backward_kda,backward_kda_varlen}]
@@ -63,23 +67,30 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_DIR = os.path.join(ROOT, "gated_delta_rule_44_amd", "csrc")
 
 
+def sources_sha256(names):
+    """sha256 over the named kernel source files, in the order given."""
+    import hashlib
+    h = hashlib.sha256()
+    for n in names:
+        h.update(open(os.path.join(KERNEL_DIR, n), "rb").read())
+    return h.hexdigest()
+
+
 def measured_traffic(workload):
     """HBM bytes per call of a workload (all its kernels) from rocprofv3
     FETCH_SIZE / WRITE_SIZE counters, scaled by the factors a plain copy of
     known size gives (profiles/traffic.json), and their ratio to the
     algorithmic bytes; None when the counters were taken on another version
-    of the kernel sources."""
-    import glob
-    import hashlib
+    of the sources the workload's kernels are built from (each entry names
+    them and their hash)."""
     try:
         rec = json.load(open(TRAFFIC_FILE))
-        h = hashlib.sha256()
-        for f in sorted(glob.glob(os.path.join(KERNEL_DIR, "*"))):
-            h.update(open(f, "rb").read())
+        w = rec.get("workloads", {}).get(workload)
+        if not w or "bytes_per_call" not in w or "sources" not in w:
+            return None
+        if sources_sha256(w["sources"]) != w.get("sources_sha256"):
+            return None
     except (OSError, ValueError):
-        return None
-    w = rec.get("workloads", {}).get(workload)
-    if rec.get("kernel_sources_sha256") != h.hexdigest() or not w or "bytes_per_call" not in w:
         return None
     return {"bytes_per_call": w["bytes_per_call"],
             "over_algorithmic": w["traffic_over_algorithmic"]}
@@ -107,10 +118,13 @@ def decode_bytes(head_steps, gate_bytes):
 LAST_MEAN_MS = [0.0]
 
 
-def timed(fn, steps, warmup, stream):
+def timed(fn, steps, warmup, stream, settle=0):
     """Median ms per step over `steps` timed steps, each bracketed by HIP
-    events on the launch stream (the mean is kept in LAST_MEAN_MS[0])."""
+    events on the launch stream (the mean is kept in LAST_MEAN_MS[0]).
+    `settle` untimed calls come before the `warmup` ones (the clock ramp)."""
     import torch
+    for i in range(settle):
+        fn(i)
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
@@ -127,7 +141,7 @@ def timed(fn, steps, warmup, stream):
 
 
 def bench_prefill(gdr, synthetic, torch, dev, B, T, H, gate, seed, steps, warmup,
-                  h0=True, sets=3):
+                  h0=True, sets=3, settle=0):
     xs = [synthetic.prefill_inputs(B, T, H, D, torch.bfloat16, gate, seed=seed + i,
                                    h0=h0, device=dev) for i in range(sets)]
     outs = [(torch.empty_like(x["v"]), torch.empty((B, H, D, D), device=dev,
@@ -150,7 +164,7 @@ def bench_prefill(gdr, synthetic, torch, dev, B, T, H, gate, seed, steps, warmup
         rc = lib.gdr_prefill_chunked(*args[i % sets])
         if rc:
             raise RuntimeError(lib.gdr_last_error().decode())
-    ms = timed(step, steps, warmup, stream)
+    ms = timed(step, steps, warmup, stream, settle)
     del xs, outs, ws
     return ms
 
@@ -447,6 +461,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--settle", type=int, default=100,
+                    help="untimed headline calls before the warm-up ones, so that the "
+                         "GPU is at its steady clock when timing starts")
     ap.add_argument("--only-headline", action="store_true")
     ap.add_argument("--only", choices=["gdn_prefill", "kda_prefill", "decode", "varlen", "draft",
                                        "varlen_pool", "fused_gdn", "fused_kda", "backward_gdn",
@@ -539,7 +556,7 @@ def main():
 
     B, T, H = 4, 4096, 16
     ms = bench_prefill(gdr, synthetic, torch, dev, B, T, H, "scalar", 1001,
-                       args.steps, args.warmup)
+                       args.steps, args.warmup, settle=max(0, args.settle))
     ms_mean = LAST_MEAN_MS[0]
     tokens = B * T
     th = tokens * H
@@ -555,6 +572,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "clock_settle_calls": max(0, args.settle),
         "ms_per_step": ms,
         "ms_per_step_mean": ms_mean,
         "higher_is_better": True,
