@@ -47,6 +47,11 @@ def _bind(lib):
                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+    b = lib.gdr_oracle_backward
+    b.restype = ctypes.c_int
+    b.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                  ctypes.c_int, ctypes.c_int, ctypes.c_double] + [ctypes.c_void_p] * 14 + [
+                  ctypes.c_int]
     lib.gdr_oracle_max_threads.restype = ctypes.c_int
     return lib
 
@@ -117,6 +122,40 @@ def forward(q, k, v, g, beta, h0=None, cu_seqlens=None, scale: float = 1.0,
     if rc != 0:
         raise RuntimeError("gdr_oracle_forward failed with code %d" % rc)
     return o, ht
+
+
+def backward_c(q, k, v, g, beta, do, h0=None, dht=None, cu_seqlens=None,
+               scale: float = 1.0, threads: int | None = None, lib=None):
+    """Gradients (dq, dk, dv, dg, dbeta, dh0) of sum(o * do) + sum(S_T * dht)
+    by the C oracle's hand-written fp64 vector-Jacobian product (one token at
+    a time, states recomputed from checkpoints), for the large cases the
+    autograd form ``backward`` cannot hold in memory.  Layouts as
+    ``forward`` (fixed or packed); do like v, dht like h0.  Float64 arrays
+    shaped like q, k, v, g, beta and [N, H, Dv, Dk]."""
+    lib = lib or load()
+    qf, kf, vf, gf, bf, df = (_f32(x) for x in (q, k, v, g, beta, do))
+    channel = gf.ndim == qf.ndim
+    if cu_seqlens is None:
+        B, T, H, Dk = qf.shape
+        cu = np.arange(B + 1, dtype=np.int64) * T
+    else:
+        cu = np.ascontiguousarray(np.asarray(
+            cu_seqlens.cpu() if hasattr(cu_seqlens, "cpu") else cu_seqlens,
+            dtype=np.int64))
+        _, H, Dk = qf.shape
+    Dv = vf.shape[-1]
+    N = len(cu) - 1
+    hf = None if h0 is None else _f32(h0)
+    dtf = None if dht is None else _f32(dht)
+    out = [np.zeros(x.shape, dtype=np.float64) for x in (qf, kf, vf, gf, bf)]
+    dh0 = np.zeros((N, H, Dv, Dk), dtype=np.float64)
+    rc = lib.gdr_oracle_backward(
+        N, _ptr(cu), H, Dk, Dv, int(channel), float(scale),
+        _ptr(qf), _ptr(kf), _ptr(vf), _ptr(gf), _ptr(bf), _ptr(hf), _ptr(df), _ptr(dtf),
+        *(_ptr(x) for x in out), _ptr(dh0), int(threads or 0))
+    if rc != 0:
+        raise RuntimeError("gdr_oracle_backward failed with code %d" % rc)
+    return tuple(out) + (dh0,)
 
 
 def decode(q, k, v, g, beta, state, scale: float = 1.0, threads=None, lib=None):

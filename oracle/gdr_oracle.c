@@ -187,3 +187,205 @@ int gdr_oracle_max_threads(void)
     return 1;
 #endif
 }
+
+/*
+ * Backward: the vector-Jacobian product of the recurrence above, for
+ * upstream gradients dO of the outputs and dS_T of the final state (the
+ * gradients a training step of the mixers needs; the summary's section 2a
+ * recurrence differentiated by hand, one token at a time, in fp64).
+ *
+ * Write one token as  P = S_{t-1} Diag(a_t),  e = v_t - P k_t,
+ * S_t = P + beta_t e k_t^T,  o_t = scale S_t q_t.  With R the gradient of
+ * the loss with respect to S_t through everything after token t, the
+ * gradient with respect to S_t in total is  R' = R + scale do_t q_t^T, and
+ *   dq_t    = scale S_t^T do_t
+ *   dv_t    = beta_t R' k_t
+ *   dbeta_t = e . (R' k_t)
+ *   dk_t    = beta_t (R'^T e - P^T (R' k_t))
+ *   dP      = R' - beta_t (R' k_t) k_t^T
+ *   dg_t[j] = sum_i dP[i][j] P[i][j]     (summed over j for a scalar gate,
+ *                                         since da/dg = a)
+ *   R      <- dP Diag(a_t)               (the gradient w.r.t. S_{t-1})
+ * starting from R = dS_T after the last token; dS_0 is R after the first.
+ * The states S_{t-1} are recomputed forward from checkpoints taken every
+ * kBlock tokens, the block's states kept while it is walked backwards.
+ */
+enum { kBlock = 64 };
+
+/* S <- S Diag(a); S += beta (v - S k) k^T; e (Dv) receives v - S' k */
+static void fwd_token(int Dk, int Dv, const double *a, const double *kt, double bt,
+                      const float *vrow, double *S, double *e)
+{
+    for (int i = 0; i < Dv; ++i) {
+        double *Si = S + (size_t)i * Dk;
+        double y = 0.0;
+        for (int j = 0; j < Dk; ++j) {
+            Si[j] *= a[j];
+            y += Si[j] * kt[j];
+        }
+        e[i] = (double)vrow[i] - y;
+        for (int j = 0; j < Dk; ++j)
+            Si[j] += bt * e[i] * kt[j];
+    }
+}
+
+static void token_inputs(int Dk, int channel_gate, const float *krow, const float *grow,
+                         double *a, double *kt)
+{
+    for (int j = 0; j < Dk; ++j) {
+        kt[j] = (double)krow[j];
+        a[j] = exp((double)(channel_gate ? grow[j] : grow[0]));
+    }
+}
+
+/*
+ * Packed-batch backward.  Layouts as gdr_oracle_forward; do_ like v,
+ * dht like h0 (NULL: zero).  Outputs (double, written): dq, dk like q,
+ * dv like v, dg like g, dbeta like beta, dh0 [N, H, Dv, Dk] (or NULL).
+ * Returns 0, -1 on bad arguments, -2 if scratch allocation failed.
+ */
+int gdr_oracle_backward(int N, const int64_t *cu_seqlens, int H, int Dk, int Dv,
+                        int channel_gate, double scale,
+                        const float *q, const float *k, const float *v,
+                        const float *g, const float *beta, const float *h0,
+                        const float *do_, const float *dht,
+                        double *dq, double *dk, double *dv, double *dg, double *dbeta,
+                        double *dh0, int num_threads)
+{
+    if (N < 0 || H <= 0 || Dk <= 0 || Dv <= 0 || !cu_seqlens)
+        return -1;
+    int64_t Tmax = 0;
+    for (int n = 0; n < N; ++n) {
+        if (cu_seqlens[n + 1] < cu_seqlens[n])
+            return -1;
+        if (cu_seqlens[n + 1] - cu_seqlens[n] > Tmax)
+            Tmax = cu_seqlens[n + 1] - cu_seqlens[n];
+    }
+    const size_t qk_stride = (size_t)H * Dk;
+    const size_t v_stride = (size_t)H * Dv;
+    const size_t g_stride = channel_gate ? (size_t)H * Dk : (size_t)H;
+    const size_t SS = (size_t)Dv * Dk;
+    const size_t nblk_max = (size_t)((Tmax + kBlock - 1) / kBlock);
+    const long pairs = (long)N * H;
+    int failed = 0;
+
+#ifdef _OPENMP
+    if (num_threads > 0)
+        omp_set_num_threads(num_threads);
+#else
+    (void)num_threads;
+#endif
+
+#pragma omp parallel
+    {
+        double *ck = (double *)malloc(sizeof(double) * SS * (nblk_max ? nblk_max : 1));
+        double *Sb = (double *)malloc(sizeof(double) * SS * (kBlock + 1));
+        double *R = (double *)malloc(sizeof(double) * SS);
+        double *e = (double *)malloc(sizeof(double) * (size_t)Dv);
+        double *rk = (double *)malloc(sizeof(double) * (size_t)Dv);
+        double *a = (double *)malloc(sizeof(double) * (size_t)Dk);
+        double *kt = (double *)malloc(sizeof(double) * (size_t)Dk);
+        if (!ck || !Sb || !R || !e || !rk || !a || !kt) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (long p = 0; p < pairs; ++p) {
+                const int n = (int)(p / H);
+                const int h = (int)(p % H);
+                const int64_t t0 = cu_seqlens[n];
+                const int T = (int)(cu_seqlens[n + 1] - t0);
+                const int nblk = (T + kBlock - 1) / kBlock;
+                const size_t pair_off = ((size_t)n * H + h) * SS;
+#define ROWQK(base, t) ((base) + (size_t)(t0 + (t)) * qk_stride + (size_t)h * Dk)
+#define ROWV(base, t) ((base) + (size_t)(t0 + (t)) * v_stride + (size_t)h * Dv)
+#define ROWG(base, t) ((base) + (size_t)(t0 + (t)) * g_stride + (size_t)h * (channel_gate ? Dk : 1))
+#define AT(base, t) ((base) + (size_t)(t0 + (t)) * H + h)
+                /* forward, keeping the state that enters every block */
+                double *S = Sb;
+                for (size_t x = 0; x < SS; ++x)
+                    S[x] = h0 ? (double)h0[pair_off + x] : 0.0;
+                for (int t = 0; t < T; ++t) {
+                    if (t % kBlock == 0)
+                        memcpy(ck + (size_t)(t / kBlock) * SS, S, sizeof(double) * SS);
+                    token_inputs(Dk, channel_gate, ROWQK(k, t), ROWG(g, t), a, kt);
+                    fwd_token(Dk, Dv, a, kt, (double)*AT(beta, t), ROWV(v, t), S, e);
+                }
+                for (size_t x = 0; x < SS; ++x)
+                    R[x] = dht ? (double)dht[pair_off + x] : 0.0;
+                for (int c = nblk - 1; c >= 0; --c) {
+                    const int tb = c * kBlock;
+                    const int L = T - tb < kBlock ? T - tb : kBlock;
+                    /* the block's states: Sb[u] enters token tb + u */
+                    memcpy(Sb, ck + (size_t)c * SS, sizeof(double) * SS);
+                    for (int u = 0; u < L; ++u) {
+                        memcpy(Sb + (size_t)(u + 1) * SS, Sb + (size_t)u * SS, sizeof(double) * SS);
+                        token_inputs(Dk, channel_gate, ROWQK(k, tb + u), ROWG(g, tb + u), a, kt);
+                        fwd_token(Dk, Dv, a, kt, (double)*AT(beta, tb + u), ROWV(v, tb + u),
+                                  Sb + (size_t)(u + 1) * SS, e);
+                    }
+                    for (int u = L - 1; u >= 0; --u) {
+                        const int t = tb + u;
+                        const double *Sp = Sb + (size_t)u * SS;       /* S_{t-1} */
+                        const double *St = Sb + (size_t)(u + 1) * SS; /* S_t */
+                        const float *qrow = ROWQK(q, t), *vrow = ROWV(v, t), *dorow = ROWV(do_, t);
+                        const double bt = (double)*AT(beta, t);
+                        token_inputs(Dk, channel_gate, ROWQK(k, t), ROWG(g, t), a, kt);
+                        double *dqr = ROWQK(dq, t), *dkr = ROWQK(dk, t), *dvr = ROWV(dv, t);
+                        double *dgr = ROWG(dg, t);
+                        for (int j = 0; j < Dk; ++j) {
+                            dqr[j] = 0.0;
+                            dkr[j] = 0.0;
+                        }
+                        for (int j = 0; j < (channel_gate ? Dk : 1); ++j)
+                            dgr[j] = 0.0;
+                        double db = 0.0;
+                        for (int i = 0; i < Dv; ++i) {
+                            const double doi = (double)dorow[i];
+                            double *Ri = R + (size_t)i * Dk;
+                            const double *Pi_src = Sp + (size_t)i * Dk;
+                            const double *Sti = St + (size_t)i * Dk;
+                            double y = 0.0, r = 0.0;
+                            for (int j = 0; j < Dk; ++j) {
+                                Ri[j] += scale * doi * (double)qrow[j];   /* R' */
+                                dqr[j] += scale * doi * Sti[j];
+                                y += a[j] * Pi_src[j] * kt[j];
+                                r += Ri[j] * kt[j];
+                            }
+                            e[i] = (double)vrow[i] - y;
+                            rk[i] = r;
+                            dvr[i] = bt * r;
+                            db += e[i] * r;
+                        }
+                        *AT(dbeta, t) = db;
+                        for (int i = 0; i < Dv; ++i) {
+                            double *Ri = R + (size_t)i * Dk;
+                            const double *Pi_src = Sp + (size_t)i * Dk;
+                            for (int j = 0; j < Dk; ++j) {
+                                const double P = a[j] * Pi_src[j];
+                                dkr[j] += bt * (e[i] * Ri[j] - rk[i] * P);
+                                const double dP = Ri[j] - bt * rk[i] * kt[j];
+                                dgr[channel_gate ? j : 0] += dP * P;
+                                Ri[j] = dP * a[j];
+                            }
+                        }
+                    }
+                }
+                if (dh0)
+                    memcpy(dh0 + pair_off, R, sizeof(double) * SS);
+#undef ROWQK
+#undef ROWV
+#undef ROWG
+#undef AT
+            }
+        }
+        free(ck);
+        free(Sb);
+        free(R);
+        free(e);
+        free(rk);
+        free(a);
+        free(kt);
+    }
+    return failed ? -2 : 0;
+}

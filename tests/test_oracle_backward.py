@@ -88,3 +88,45 @@ def test_backward_closed_form_without_writes(channel):
                                    atol=1e-11)
         dgt = np.einsum("bhij,bhij->bhj", dSt, h0)
         np.testing.assert_allclose(dg[:, t], dgt if channel else dgt.sum(-1), atol=1e-11)
+
+
+# The C oracle's hand-written backward (oracle.backward_c), used where the
+# autograd form cannot hold a long sequence's graph in memory, pinned to the
+# autograd form above (itself pinned to finite differences and closed forms)
+# on fixed and packed batches with both gate kinds, zero gates included.
+@pytest.mark.parametrize("channel", [False, True])
+def test_c_backward_equals_autograd(channel, oracle_lib):
+    q, k, v, g, beta, h0, do, dht = _case(np.random.default_rng(41), 2, 150, 2, 8, channel)
+    g[0, 70, 1] = -np.inf                      # a zero gate mid-sequence
+    g[1, 5:9] = -7.0                           # a strong decay
+    ref = oracle.backward(q, k, v, g, beta, do, h0=h0, dht=dht, scale=0.6)
+    got = oracle.backward_c(q, k, v, g, beta, do, h0=h0, dht=dht, scale=0.6, lib=oracle_lib)
+    for name, x, r in zip(("dq", "dk", "dv", "dg", "dbeta", "dh0"), got, ref):
+        assert x.shape == r.shape, name
+        np.testing.assert_allclose(x, r, rtol=1e-9, atol=1e-11, err_msg=name)
+
+
+@pytest.mark.parametrize("channel", [False, True])
+def test_c_backward_packed_equals_per_sequence(channel, oracle_lib):
+    """A packed batch (an empty sequence, one token, ragged lengths across
+    the checkpoint blocks) equals the autograd form run sequence by
+    sequence; without h0 or dht both start from zeros."""
+    rng = np.random.default_rng(42)
+    lens = [70, 0, 1, 129]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    Tt, H, D = int(cu[-1]), 2, 5
+    q, k, v, g, beta, h0, do, dht = _case(rng, 1, Tt, H, D, channel)
+    q, k, v, g, beta, do = (x[0] for x in (q, k, v, g, beta, do))
+    h0 = 0.5 * rng.standard_normal((len(lens), H, D, D)).astype(np.float32)
+    got = oracle.backward_c(q, k, v, g, beta, do, h0=h0, cu_seqlens=cu, scale=0.9,
+                            lib=oracle_lib)
+    for n, L in enumerate(lens):
+        a, b = int(cu[n]), int(cu[n + 1])
+        if L == 0:
+            assert np.all(got[5][n] == 0)
+            continue
+        ref = oracle.backward(*(x[a:b][None] for x in (q, k, v, g, beta, do)),
+                              h0=h0[n:n + 1], scale=0.9)
+        for i in range(5):
+            np.testing.assert_allclose(got[i][a:b], ref[i][0], rtol=1e-9, atol=1e-11)
+        np.testing.assert_allclose(got[5][n], ref[5][0], rtol=1e-9, atol=1e-11)
