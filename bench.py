@@ -33,17 +33,16 @@ Times: each step is bracketed by HIP events on the launch stream; `value`
 and `ms_per_step` come from the median step, `roofline.achieved` from the
 mean (the average call time, as rocprofv3 reports kernel averages).
 Defaults: 100 warmup steps and 200 timed steps (a fifth of each for the
-decode and varlen workloads).  The GPU reaches its steady clock only after
-about a hundred prefill calls (with 5 warm-up steps the headline's median
-is about 6 % slower), so `--settle` (default 100) untimed headline calls
-run before the warm-up steps; the line reports them as
-`clock_settle_calls`.  The workloads after the headline find the clock
-settled.
+decode and varlen workloads).  The GPU clock ramps up over the first ~25 ms
+of sustained load (headline calls 0-100 take 126-133 us, calls past 200
+117 us), so before each workload's W warm-up calls come untimed calls
+filling `--settle-ms` (default 40) ms of GPU time; the line reports the
+headline's as `clock_settle_calls`.
 The secondary list also carries the latency of one fp32 call on the GDN
 recurrent workload (B=1 H=1 T=64 d=64), and the oracle's rate on the other
 workloads in full beside the GPU's.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle N]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle-ms MS]
                        [--only-headline] [--no-cpu-baseline]
                        [--only {kda_prefill,decode,varlen,draft,varlen_pool,fused_gdn,fused_kda,
                                 backward_gdn,backward_kda,backward_kda_varlen}]
@@ -116,15 +115,31 @@ def decode_bytes(head_steps, gate_bytes):
 
 
 LAST_MEAN_MS = [0.0]
+SETTLE_MS = [40.0]          # untimed GPU time before each workload's warm-up
+LAST_SETTLE_CALLS = [0]
 
 
-def timed(fn, steps, warmup, stream, settle=0):
+def timed(fn, steps, warmup, stream):
     """Median ms per step over `steps` timed steps, each bracketed by HIP
     events on the launch stream (the mean is kept in LAST_MEAN_MS[0]).
-    `settle` untimed calls come before the `warmup` ones (the clock ramp)."""
+    Before the `warmup` calls, untimed calls fill about SETTLE_MS[0] ms of
+    GPU time (their count is kept in LAST_SETTLE_CALLS[0]): the GPU clock
+    ramps up over the first ~25 ms of sustained load."""
+    import time
     import torch
-    for i in range(settle):
-        fn(i)
+    n, batch = 0, 1
+    if SETTLE_MS[0] > 0:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        while n < 20000:
+            for _ in range(batch):
+                fn(n)
+                n += 1
+            torch.cuda.synchronize()
+            if time.perf_counter() - t0 >= SETTLE_MS[0] * 1e-3:
+                break
+            batch = min(2 * batch, 64)
+    LAST_SETTLE_CALLS[0] = n
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
@@ -141,7 +156,7 @@ def timed(fn, steps, warmup, stream, settle=0):
 
 
 def bench_prefill(gdr, synthetic, torch, dev, B, T, H, gate, seed, steps, warmup,
-                  h0=True, sets=3, settle=0):
+                  h0=True, sets=3):
     xs = [synthetic.prefill_inputs(B, T, H, D, torch.bfloat16, gate, seed=seed + i,
                                    h0=h0, device=dev) for i in range(sets)]
     outs = [(torch.empty_like(x["v"]), torch.empty((B, H, D, D), device=dev,
@@ -164,7 +179,7 @@ def bench_prefill(gdr, synthetic, torch, dev, B, T, H, gate, seed, steps, warmup
         rc = lib.gdr_prefill_chunked(*args[i % sets])
         if rc:
             raise RuntimeError(lib.gdr_last_error().decode())
-    ms = timed(step, steps, warmup, stream, settle)
+    ms = timed(step, steps, warmup, stream)
     del xs, outs, ws
     return ms
 
@@ -461,9 +476,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--settle", type=int, default=100,
-                    help="untimed headline calls before the warm-up ones, so that the "
-                         "GPU is at its steady clock when timing starts")
+    ap.add_argument("--settle-ms", type=float, default=40.0,
+                    help="untimed GPU time (ms) before each workload's warm-up calls, so "
+                         "that the GPU is at its steady clock when timing starts")
     ap.add_argument("--only-headline", action="store_true")
     ap.add_argument("--only", choices=["gdn_prefill", "kda_prefill", "decode", "varlen", "draft",
                                        "varlen_pool", "fused_gdn", "fused_kda", "backward_gdn",
@@ -473,6 +488,7 @@ def main():
                     help="time one secondary workload alone (for profiling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
+    SETTLE_MS[0] = max(0.0, args.settle_ms)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(each GPU would run its own share of sequences/heads independently).",
@@ -556,8 +572,9 @@ def main():
 
     B, T, H = 4, 4096, 16
     ms = bench_prefill(gdr, synthetic, torch, dev, B, T, H, "scalar", 1001,
-                       args.steps, args.warmup, settle=max(0, args.settle))
+                       args.steps, args.warmup)
     ms_mean = LAST_MEAN_MS[0]
+    settle_calls = LAST_SETTLE_CALLS[0]
     tokens = B * T
     th = tokens * H
     nbytes = prefill_bytes(th, B * H, "scalar")
@@ -572,7 +589,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "clock_settle_calls": max(0, args.settle),
+        "clock_settle_calls": settle_calls,
         "ms_per_step": ms,
         "ms_per_step_mean": ms_mean,
         "higher_is_better": True,
