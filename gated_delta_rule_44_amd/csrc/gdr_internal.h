@@ -207,7 +207,8 @@ struct BwdArgs {
     const int32_t *chunk_base;    // [B+1] (packed batches)
     long long chunks;             // global chunks the grid covers (an upper bound when packed)
     // [B, H]: pairs the forward marked (a chunk decays by more than e^80 in
-    // some channel); their gradients are set to NaN.  nullptr: none marked.
+    // some channel); their gradients are recomputed by the token-level
+    // adjoint.  nullptr: none marked.
     const int32_t *unit_wide;
     int B, T, H, nc;              // T, nc: fixed length only
     float scale;
