@@ -1088,14 +1088,16 @@ size_t backward_record_bytes(int D) {
 //     G <- a_t (.) du                    channels for the scalar gate)
 // so dq, dk, dg and dbeta are sums over the rows and dv, dh0 are row-local.
 // A workgroup (16 waves) takes 64 rows of one pair, 16 lanes to a row with
-// D/16 columns each; a chunk is walked backwards in sub-blocks of kWideSub
-// tokens, each sub-block's entering state recomputed forward from the
-// chunk's stored state (kWideSub token states stay in registers).  The
+// D/16 columns each; a chunk is walked backwards in blocks of kWideBlk
+// tokens and those in sub-blocks of kWideSub, the block's entering state
+// recomputed forward from the chunk's stored state and each sub-block's
+// from the block's (kWideSub token states stay in registers).  The
 // column sums over the 64 rows go through LDS; at D = 128 the two
 // workgroups of a pair add theirs into outputs the zeroing kernel cleared
 // -- two fp32 additions onto zero, whose result does not depend on their
 // order, so the gradients are the same on every run.
-constexpr int kWideSub = 4;
+constexpr int kWideSub = 4;    // token states a lane keeps at once
+constexpr int kWideBlk = 16;   // tokens whose entering state is kept
 
 template <int D, bool CH> struct WideSmem {
     static constexpr int NA = CH ? D : 1;
@@ -1228,31 +1230,36 @@ __global__ __launch_bounds__(1024) void wide_backward_kernel(BwdArgs a) {
         }
         if (tid < C) sm.beta[tid] = tid < L ? a.beta[(size_t)(tc + tid) * a.H + h] : 0.f;
         __syncthreads();
-        float S0[VPL];
-        {
-            const float *sp = a.states + ((size_t)(cb + c) * a.H + h) * DD + (size_t)r * D + j0;
+        // the chunk in blocks of kWideBlk tokens, last first: a block's
+        // entering state forward from the chunk's stored one, then the
+        // block in sub-blocks of kWideSub, each entered from the block's
+        // state (the same steps in the same order as from the chunk start)
+        const float *sc = a.states + ((size_t)(cb + c) * a.H + h) * DD;   // uniform
+        for (int tb = (L - 1) / kWideBlk * kWideBlk; tb >= 0; tb -= kWideBlk) {
+          float sbk[VPL];
 #pragma unroll
-            for (int j = 0; j < VPL; ++j) S0[j] = sp[j];
-        }
-        for (int sb = (L - 1) / kWideSub; sb >= 0; --sb) {
+          for (int j = 0; j < VPL; ++j) sbk[j] = sc[r * D + j0 + j];
+          for (int t = 0; t < tb; ++t) wide_fwd<D, CH>(sm, sbk, t, rl, j0);
+          const int Lb = L - tb < kWideBlk ? L - tb : kWideBlk;
+          for (int sb = (Lb - 1) / kWideSub; sb >= 0; --sb) {
             float s[VPL];
 #pragma unroll
-            for (int j = 0; j < VPL; ++j) s[j] = S0[j];
-            for (int t = 0; t < kWideSub * sb; ++t) wide_fwd<D, CH>(sm, s, t, rl, j0);
-            const int nt = L - kWideSub * sb < kWideSub ? L - kWideSub * sb : kWideSub;
+            for (int j = 0; j < VPL; ++j) s[j] = sbk[j];
+            for (int t = tb; t < tb + kWideSub * sb; ++t) wide_fwd<D, CH>(sm, s, t, rl, j0);
+            const int nt = Lb - kWideSub * sb < kWideSub ? Lb - kWideSub * sb : kWideSub;
             float st[kWideSub][VPL], e[kWideSub];
 #pragma unroll
             for (int u = 0; u < kWideSub; ++u) {
                 if (u < nt) {
 #pragma unroll
                     for (int j = 0; j < VPL; ++j) st[u][j] = s[j];
-                    e[u] = wide_fwd<D, CH>(sm, s, kWideSub * sb + u, rl, j0);
+                    e[u] = wide_fwd<D, CH>(sm, s, tb + kWideSub * sb + u, rl, j0);
                 }
             }
 #pragma unroll
             for (int u = kWideSub - 1; u >= 0; --u) {
                 if (u >= nt) continue;
-                const int t = kWideSub * sb + u;
+                const int t = tb + kWideSub * sb + u;
                 const size_t row = (size_t)(tc + t) * a.H + h;
                 float kk[VPL], qq[VPL], at[VPL];
                 lds_row<VPL>(sm.k + t * D + j0, kk);
@@ -1310,6 +1317,7 @@ __global__ __launch_bounds__(1024) void wide_backward_kernel(BwdArgs a) {
                 }
                 par ^= 1;
             }
+          }
         }
     }
     if (a.dh0) {

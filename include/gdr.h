@@ -390,7 +390,7 @@ gdr_status gdr_decode_tokens_fused(enum gdr_dtype dt, enum gdr_gate gk, int B, i
  * forward marks each (sequence, head) with a chunk that decays further, and
  * all gradients of the marked pairs are then recomputed by the adjoint of
  * the token recurrence in fp32 from the stored chunk-entering states (about
- * 15 times the in-range cost for a batch where every pair is marked).  The
+ * 11 to 12 times the in-range cost for a batch where every pair is marked).  The
  * results are the same bits on every run except dg and dbeta of in-range
  * pairs, which are summed in LDS float atomics (equal to fp32 rounding).
  */
