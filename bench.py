@@ -27,7 +27,9 @@ The same line carries:
                 the GDN and KDA prefill on raw projections (fused q/k
                 normalisation, beta and gate from bf16 logits), and the
                 backward of the GDN and KDA prefill workloads and of the
-                packed KDA workload.
+                packed KDA workload, and the GDN backward with every
+                (sequence, head) past the chunk form's range (g = -4 per
+                token: the exact token-level path).
 
 Times: each step is bracketed by HIP events on the launch stream; `value`
 and `ms_per_step` come from the median step, `roofline.achieved` from the
@@ -226,10 +228,15 @@ def bench_fused(gdr, synthetic, torch, dev, B, T, H, gate, seed, steps, warmup, 
     return ms
 
 
-def bench_backward(gdr, synthetic, torch, dev, B, T, H, gate, seed, steps, warmup, h0=True):
+def bench_backward(gdr, synthetic, torch, dev, B, T, H, gate, seed, steps, warmup, h0=True,
+                   gate_fill=None):
     """Gradients of the chunked prefill (gdr_backward_chunked): all inputs and
-    the upstream gradients resident, outputs and workspace preallocated."""
+    the upstream gradients resident, outputs and workspace preallocated.
+    gate_fill: every gate log set to this value (e.g. -4: every chunk decays
+    by e^-256, so every pair takes the token-level path)."""
     x = synthetic.prefill_inputs(B, T, H, D, torch.bfloat16, gate, seed=seed, h0=h0, device=dev)
+    if gate_fill is not None:
+        x["g"].fill_(gate_fill)
     gen = torch.Generator(device=dev)
     gen.manual_seed(seed + 50)
     do = torch.randn((B, T, H, D), generator=gen, device=dev).to(torch.bfloat16)
@@ -688,6 +695,17 @@ def main():
                         "tokens_per_s": B_ * T_ / (msb * 1e-3),
                         "GB_per_s": bb / (msb * 1e-3) / 1e9,
                         "frac_hbm": bb / (msb * 1e-3) / 1e9 / HBM_PEAK_GBS})
+        # the same GDN backward with g = -4 per token everywhere: every
+        # (sequence, head) has chunks decaying by e^-256 and takes the exact
+        # token-level path
+        msw = bench_backward(gdr, synthetic, torch, dev, 4, 4096, 16, "scalar", 1001,
+                             max(3, args.steps // 10), max(1, args.warmup // 10), gate_fill=-4.0)
+        bb = backward_bytes(4 * 4096 * 16, 64, "scalar", True)
+        sec.append({"workload": "backward_gdn_B4_H16_T4096_d128_bf16_all_pairs_past_chunk_range",
+                    "gate": "g = -4 per token (every pair on the token-level path)",
+                    "ms_per_step": msw, "tokens_per_s": 4 * 4096 / (msw * 1e-3),
+                    "GB_per_s": bb / (msw * 1e-3) / 1e9,
+                    "frac_hbm": bb / (msw * 1e-3) / 1e9 / HBM_PEAK_GBS})
         msv, tokv, nv = bench_backward_varlen(gdr, synthetic, torch, dev,
                                               max(3, args.steps // 40), max(1, args.warmup // 50))
         bb = backward_bytes(tokv * 32, nv * 32, "channel", True)
